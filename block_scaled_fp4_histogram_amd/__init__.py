@@ -1,1 +1,198 @@
-"""Routed mixture-of-experts with block-scaled 4-bit expert weights on MI355X (gfx950)."""
+"""Routed mixture-of-experts with block-scaled 4-bit expert weights on MI355X (gfx950).
+
+Python front end of the C ABI in include/moe.h. PyTorch supplies device memory
+and streams; the library's HIP kernels do every step of the layer:
+
+    plan = Plan(E, K, N, top_k, swiglu_limit=7.0, act_format=A_MXFP8, max_tokens=4096)
+    experts = Experts(plan, W_MXFP4, E, w13, s13, w2, s2)      # in-place repack
+    run(plan, [experts], x, topk_ids, topk_weights, out, deterministic=False)
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+from typing import Optional, Sequence
+
+from . import _lib
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOTPREPARED, MOE_ESCRATCH, MOE_EHIP = 0, -1, -2, -3, -4, -5
+W_MXFP4, W_NVFP4, W_NF3 = 1, 2, 3
+A_MXFP8, A_BF16 = 1, 2
+W13_UP_GATE, W13_GATE_UP = 0, 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"moe error {code}: {msg}")
+        self.code = code
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        raise MoeError(rc, _lib.load().moe_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t, name, dtype, device=True):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+class Plan:
+    """One layer geometry (moe_plan)."""
+
+    def __init__(self, E: int, K: int, N: int, top_k: int, swiglu_limit: Optional[float] = None,
+                 act_format: int = A_MXFP8, w13_layout: int = W13_UP_GATE, max_tokens: int = 4096):
+        L = _lib.load()
+        h = C.c_void_p()
+        lim = math.nan if swiglu_limit is None else float(swiglu_limit)
+        _check(L.moe_plan(E, K, N, top_k, lim, act_format, w13_layout, max_tokens, C.byref(h)))
+        self.handle = h
+        self.E, self.K, self.N, self.top_k = E, K, N, top_k
+        self.act_format, self.max_tokens = act_format, max_tokens
+
+    def scratch_bytes(self, T: int, deterministic: bool = False) -> int:
+        return _lib.load().moe_scratch_bytes(self.handle, T, int(bool(deterministic)))
+
+    def capacity(self, T: int):
+        rows = C.c_int(0)
+        cap = _lib.load().moe_plan_capacity(self.handle, T, C.byref(rows))
+        return cap, rows.value
+
+    def close(self):
+        if self.handle:
+            _lib.load().moe_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Experts:
+    """One layer's (or tier's) experts, repacked in place (moe_prepare_weights).
+
+    The tensors are borrowed: they hold the tile layout until unpack()."""
+
+    def __init__(self, plan: Plan, weight_format: int, num_experts: int, w13, s13, w2, s2, g13=None, g2=None,
+                 stream=None):
+        import torch
+        for name, t in (("w13", w13), ("s13", s13), ("w2", w2), ("s2", s2)):
+            _need(t, name, torch.uint8)
+        for name, t in (("g13", g13), ("g2", g2)):
+            if t is not None:
+                _need(t, name, torch.float32)
+        h = C.c_void_p()
+        _check(_lib.load().moe_prepare_weights(plan.handle, weight_format, num_experts, _ptr(w13), _ptr(s13),
+                                               _ptr(g13), _ptr(w2), _ptr(s2), _ptr(g2), _stream(stream),
+                                               C.byref(h)))
+        self.handle = h
+        self.plan = plan
+        self.weight_format, self.num_experts = weight_format, num_experts
+        self.tensors = (w13, s13, w2, s2, g13, g2)
+
+    def unpack(self, stream=None):
+        _check(_lib.load().moe_unpack_weights(self.handle, _stream(stream)))
+
+    def close(self):
+        if self.handle:
+            _lib.load().moe_experts_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _tiers(tiers):
+    arr = (_lib.MoeTier * len(tiers))()
+    keep = []
+    for i, t in enumerate(tiers):
+        ex, emap = (t if isinstance(t, (tuple, list)) else (t, None))
+        if emap is not None:
+            import torch
+            _need(emap, "expert_map", torch.int32)
+        keep.append(emap)
+        arr[i] = _lib.MoeTier(ex.handle.value, _ptr(emap))
+    return arr, keep
+
+
+def scratch_for(plan: Plan, T: int, deterministic: bool = False, device="cuda"):
+    """A scratch tensor large enough for moe_run of T tokens."""
+    import torch
+    return torch.empty(max(plan.scratch_bytes(T, deterministic), 256), dtype=torch.uint8, device=device)
+
+
+def run(plan: Plan, tiers: Sequence, x, topk_ids, topk_weights, out=None, deterministic: bool = False,
+        scratch=None, stream=None):
+    """The layer (moe_run). tiers: Experts, or (Experts, expert_map int32 [E]) pairs."""
+    import torch
+    _need(x, "x", torch.bfloat16)
+    _need(topk_ids, "topk_ids", torch.int32)
+    _need(topk_weights, "topk_weights", torch.float32)
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", torch.bfloat16)
+    if scratch is None:
+        scratch = scratch_for(plan, T, deterministic, x.device)
+    arr, keep = _tiers(tiers)
+    _check(_lib.load().moe_run(plan.handle, arr, len(tiers), _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
+                               _ptr(out), T, int(bool(deterministic)), _ptr(scratch), scratch.numel(),
+                               _stream(stream)))
+    return out
+
+
+def debug_route(plan: Plan, tiers: Sequence, topk_ids, scratch=None, stream=None):
+    """Route planner alone. Returns (cnt [U], off [U+1], perm [off[U]], inv [T*k]) device tensors."""
+    import torch
+    _need(topk_ids, "topk_ids", torch.int32)
+    T, k = topk_ids.shape
+    U = sum((t[0] if isinstance(t, (tuple, list)) else t).num_experts for t in tiers)
+    dev = topk_ids.device
+    if scratch is None:
+        scratch = scratch_for(plan, T, True, dev)
+    cnt = torch.empty(U, dtype=torch.int32, device=dev)
+    off = torch.empty(U + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    arr, keep = _tiers(tiers)
+    _check(_lib.load().moe_debug_route(plan.handle, arr, len(tiers), _ptr(topk_ids), T, _ptr(scratch),
+                                       scratch.numel(), _ptr(cnt), _ptr(off), _ptr(perm), _ptr(inv),
+                                       _stream(stream)))
+    torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+    return cnt, off, perm[: int(off[-1].item())], inv
+
+
+def debug_quant_mxfp8(v, stream=None):
+    """MXFP8 quantiser alone on a [rows, cols] bf16 or fp32 device tensor -> (codes, scales)."""
+    import torch
+    if v.dtype not in (torch.bfloat16, torch.float32) or not v.is_contiguous():
+        raise TypeError("expected a contiguous bf16 or fp32 tensor")
+    rows, cols = v.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=v.device)
+    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=v.device)
+    fn = _lib.load().moe_debug_quant_mxfp8_bf16 if v.dtype == torch.bfloat16 else _lib.load().moe_debug_quant_mxfp8_f32
+    _check(fn(_ptr(v), rows, cols, _ptr(q), _ptr(s), _stream(stream)))
+    return q, s

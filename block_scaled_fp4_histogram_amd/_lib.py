@@ -1,0 +1,52 @@
+"""ctypes binding of libmoe_gfx950.so (the C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_gfx950.so")
+
+# Every function include/moe.h declares, with (restype, argtypes).
+_vp, _i, _f, _sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+SIGNATURES = {
+    "moe_plan": (_i, [_i, _i, _i, _i, _f, _i, _i, _i, C.POINTER(_vp)]),
+    "moe_plan_destroy": (None, [_vp]),
+    "moe_scratch_bytes": (_sz, [_vp, _i, _i]),
+    "moe_prepare_weights": (_i, [_vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.POINTER(_vp)]),
+    "moe_unpack_weights": (_i, [_vp, _vp]),
+    "moe_experts_destroy": (None, [_vp]),
+    "moe_run": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]),
+    "moe_last_error": (C.c_char_p, []),
+    "moe_plan_capacity": (_i, [_vp, _i, C.POINTER(_i)]),
+    "moe_debug_route": (_i, [_vp, _vp, _i, _vp, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp]),
+    "moe_debug_quant_mxfp8_bf16": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "moe_debug_quant_mxfp8_f32": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+}
+
+
+class MoeTier(C.Structure):
+    _fields_ = [("experts", C.c_void_p), ("expert_map", C.c_void_p)]
+
+
+_lib = None
+
+
+def load():
+    """Load the library once. Raises ImportError when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with block_scaled_fp4_histogram_amd/build.py "
+                              "(or __graft_entry__.build())")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib

@@ -1,0 +1,482 @@
+// C ABI of the routed MoE layer (declared in include/moe.h): plans, the
+// capacity ladder, scratch carving, argument validation, in-place weight
+// preparation and the launch sequence of one layer.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "moe.h"
+#include "moe_common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(MOE_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr uint32_t kPlanMagic = 0x4D4F4550u;     // "MOEP"
+constexpr uint32_t kExpertsMagic = 0x4D4F4558u;  // "MOEX"
+
+// Capacity ladder rungs (tokens per launch): exact small decode batches, then
+// powers of two up to the plan's max_tokens (sglang moe_b12x_next.py: exact
+// decode/verify capacities plus a bounded prefill ladder; a batch runs at the
+// smallest capacity >= its size, larger batches in chunks of the top one).
+const int kLadder[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16, 24, 32, 48, 64, 96, 128, 256, 512, 1024, 2048,
+                       4096, 8192, 16384};
+
+}  // namespace
+
+struct moe_plan_s {
+  uint32_t magic;
+  int E, K, N, topk;
+  float limit;
+  int has_limit;
+  int afmt, w13_layout, max_tokens;
+  std::vector<int> caps;  // ascending; caps.back() == chunk
+};
+
+struct moe_experts_s {
+  uint32_t magic;
+  int K, N, w13_layout;   // geometry the buffers were prepared for
+  int wfmt, E;
+  uint8_t *w13, *s13, *w2, *s2;
+  const float *g13, *g2;
+  int prepared;
+};
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool plan_ok(const moe_plan_s *p) { return p && p->magic == kPlanMagic; }
+
+int cap_for(const moe_plan_s *p, int T) {
+  for (int c : p->caps)
+    if (c >= T) return c;
+  return p->caps.back();
+}
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Carving of the scratch arena for one chunk of `cap` tokens.
+struct Layout {
+  size_t ru, lrank, inv, perm, cnt, off, chunk_hist, tile_u, tile_row0, tier_tiles;
+  size_t xq, xs, hq, hs, hb, acc, rb;
+  size_t total;
+  int R, G, max_tiles;
+};
+
+Layout layout(const moe_plan_s *p, int cap, int deterministic) {
+  Layout L;
+  memset(&L, 0, sizeof L);
+  const size_t R = (size_t)cap * p->topk;
+  const int U = moe::kMaxExperts;
+  L.R = (int)R;
+  L.G = (int)((R + moe::kRouteChunk - 1) / moe::kRouteChunk);
+  L.max_tiles = (int)((R + moe::kTileRows - 1) / moe::kTileRows + std::min<size_t>(U, R));
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = al256(o + bytes);
+    return at;
+  };
+  L.ru = take(4 * R);
+  L.lrank = take(4 * R);
+  L.inv = take(4 * R);
+  L.perm = take(4 * R);
+  L.cnt = take(4 * (size_t)U);
+  L.off = take(4 * (size_t)(U + 1));
+  L.chunk_hist = take(4 * (size_t)L.G * U);
+  L.tile_u = take(4 * (size_t)L.max_tiles);
+  L.tile_row0 = take(4 * (size_t)L.max_tiles);
+  L.tier_tiles = take(4 * 2 * moe::kMaxTiers);
+  if (p->afmt == MOE_A_MXFP8) {
+    L.xq = take((size_t)cap * p->K);
+    L.xs = take((size_t)cap * (p->K / 32));
+    L.hq = take(R * p->N);
+    L.hs = take(R * (p->N / 32));
+  } else {
+    L.hb = take(2 * R * p->N);
+  }
+  if (deterministic) L.rb = take(2 * R * p->K);
+  else L.acc = take(4 * (size_t)cap * p->K);
+  L.total = o;
+  return L;
+}
+
+int check_tiers(const moe_plan_s *p, const moe_tier *tiers, int n_tiers) {
+  if (!tiers || n_tiers < 1 || n_tiers > moe::kMaxTiers) return fail(MOE_EINVAL, "n_tiers must be 1 or 2");
+  int U = 0;
+  for (int i = 0; i < n_tiers; i++) {
+    const moe_experts_s *x = tiers[i].experts;
+    if (!x || x->magic != kExpertsMagic) return fail(MOE_EINVAL, "tier %d: null or invalid experts handle", i);
+    if (!x->prepared) return fail(MOE_ENOTPREPARED, "tier %d: experts are not prepared (checkpoint layout)", i);
+    if (x->K != p->K || x->N != p->N || x->w13_layout != p->w13_layout)
+      return fail(MOE_ENOTPREPARED, "tier %d: experts prepared for K=%d N=%d layout=%d, plan has K=%d N=%d layout=%d",
+                  i, x->K, x->N, x->w13_layout, p->K, p->N, p->w13_layout);
+    const int want_a = (x->wfmt == MOE_W_MXFP4) ? MOE_A_MXFP8 : MOE_A_BF16;
+    if (want_a != p->afmt) return fail(MOE_EUNSUPPORTED, "tier %d: weight format %d does not run with activation format %d", i, x->wfmt, p->afmt);
+    if (tiers[i].expert_map && !aligned(tiers[i].expert_map, 4)) return fail(MOE_EINVAL, "tier %d: misaligned expert_map", i);
+    if (!tiers[i].expert_map && x->E > p->E) return fail(MOE_EINVAL, "tier %d: %d experts exceed the id range %d without a map", i, x->E, p->E);
+    U += x->E;
+  }
+  if (U > moe::kMaxExperts) return fail(MOE_EUNSUPPORTED, "tiers hold %d experts; at most %d", U, moe::kMaxExperts);
+  return MOE_OK;
+}
+
+// Everything one chunk needs after validation.
+int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uint16_t *x, const int32_t *ids,
+              const float *wts, uint16_t *out, int T, int deterministic, const Layout &L, uint8_t *scratch,
+              hipStream_t s, bool route_only) {
+  const int R = T * p->topk;
+  auto I32 = [&](size_t o) { return (int32_t *)(scratch + o); };
+  moe::RouteArgs ra;
+  memset(&ra, 0, sizeof ra);
+  ra.ids = ids;
+  ra.R = R;
+  ra.topk = p->topk;
+  ra.E = p->E;
+  ra.n_tiers = n_tiers;
+  ra.emap0 = tiers[0].expert_map;
+  ra.E0 = tiers[0].experts->E;
+  ra.emap1 = n_tiers > 1 ? tiers[1].expert_map : nullptr;
+  ra.E1 = n_tiers > 1 ? tiers[1].experts->E : 0;
+  ra.G = (R + moe::kRouteChunk - 1) / moe::kRouteChunk;
+  ra.max_tiles = L.max_tiles;
+  ra.ru = I32(L.ru);
+  ra.lrank = I32(L.lrank);
+  ra.chunk_hist = I32(L.chunk_hist);
+  ra.cnt = I32(L.cnt);
+  ra.off = I32(L.off);
+  ra.perm = I32(L.perm);
+  ra.inv = I32(L.inv);
+  ra.tile_u = I32(L.tile_u);
+  ra.tile_row0 = I32(L.tile_row0);
+  ra.tier_tiles = I32(L.tier_tiles);
+  ra.x = x;
+  ra.T = T;
+  ra.K = p->K;
+  long side_work = 0;
+  if (!route_only) {
+    if (p->afmt == MOE_A_MXFP8) {
+      ra.xq = scratch + L.xq;
+      ra.xs = scratch + L.xs;
+      side_work = std::max(side_work, (long)T * (p->K / 32));
+    }
+    if (!deterministic) {
+      ra.zero_buf = (float *)(scratch + L.acc);
+      ra.zero_n = (long)T * p->K;
+      side_work = std::max(side_work, ra.zero_n / 4);
+    }
+  }
+  ra.side_blocks = (int)std::min<long>((side_work + 255) / 256, 2048);
+  HIP_TRY(moe::launch_route(ra, s));
+  if (route_only) return MOE_OK;
+
+  moe::GemmArgs ga;
+  memset(&ga, 0, sizeof ga);
+  ga.tile_u = I32(L.tile_u);
+  ga.tile_row0 = I32(L.tile_row0);
+  ga.tier_tiles = I32(L.tier_tiles);
+  ga.off = I32(L.off);
+  ga.perm = I32(L.perm);
+  ga.topk = p->topk;
+  ga.K = p->K;
+  ga.N = p->N;
+  ga.xq = scratch + L.xq;
+  ga.xs = scratch + L.xs;
+  ga.xb = x;
+  ga.hq = scratch + L.hq;
+  ga.hs = scratch + L.hs;
+  ga.hb = (uint16_t *)(scratch + L.hb);
+  ga.limit = p->limit;
+  ga.has_limit = p->has_limit;
+  ga.topk_w = wts;
+  ga.out_acc = (float *)(scratch + L.acc);
+  ga.rb = (uint16_t *)(scratch + L.rb);
+  ga.deterministic = deterministic;
+  const int row_tiles = (R + moe::kTileRows - 1) / moe::kTileRows;
+  int u_base = 0;
+  for (int i = 0; i < n_tiers; i++) {
+    const moe_experts_s *xp = tiers[i].experts;
+    ga.tier = i;
+    ga.u_base = u_base;
+    ga.w13 = xp->w13;
+    ga.s13 = xp->s13;
+    ga.w2 = xp->w2;
+    ga.s2 = xp->s2;
+    ga.g13 = xp->g13;
+    ga.g2 = xp->g2;
+    const int grid_tiles = row_tiles + std::min(xp->E, R);
+    HIP_TRY(moe::launch_gemm1(xp->wfmt, ga, grid_tiles, s));
+    u_base += xp->E;
+  }
+  u_base = 0;
+  for (int i = 0; i < n_tiers; i++) {
+    const moe_experts_s *xp = tiers[i].experts;
+    ga.tier = i;
+    ga.u_base = u_base;
+    ga.w13 = xp->w13;
+    ga.s13 = xp->s13;
+    ga.w2 = xp->w2;
+    ga.s2 = xp->s2;
+    ga.g13 = xp->g13;
+    ga.g2 = xp->g2;
+    const int grid_tiles = row_tiles + std::min(xp->E, R);
+    HIP_TRY(moe::launch_gemm2(xp->wfmt, ga, grid_tiles, s));
+    u_base += xp->E;
+  }
+  HIP_TRY(moe::launch_finalize(deterministic, ga.out_acc, ga.rb, I32(L.inv), T, p->K, p->topk, out, s));
+  return MOE_OK;
+}
+
+// Bytes per (row, 32-column group) of the data and scale tensors of a format.
+void fmt_units(int wfmt, int *unit, int *sunit) {
+  *unit = (wfmt == MOE_W_NF3) ? 12 : 16;
+  *sunit = (wfmt == MOE_W_NVFP4) ? 2 : 1;
+}
+
+// Rewrite the four tensors between checkpoint and tile layout, a batch of
+// experts at a time through a temporary device buffer.
+int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
+  int unit, sunit;
+  fmt_units(x->wfmt, &unit, &sunit);
+  struct T {
+    uint8_t *buf;
+    int unit, rows, groups, pair;
+  } tensors[4] = {{x->w13, unit, 2 * x->N, x->K / 32, 1},
+                  {x->s13, sunit, 2 * x->N, x->K / 32, 1},
+                  {x->w2, unit, x->K, x->N / 32, 0},
+                  {x->s2, sunit, x->K, x->N / 32, 0}};
+  size_t max_exp = 0;
+  for (auto &t : tensors) max_exp = std::max(max_exp, (size_t)t.rows * t.groups * t.unit);
+  const size_t budget = (size_t)256 << 20;
+  const long batch = std::max<long>(1, std::min<long>(x->E, (long)(budget / max_exp)));
+  uint8_t *tmp = nullptr;
+  HIP_TRY(hipMalloc(&tmp, batch * max_exp));
+  int rc = MOE_OK;
+  for (auto &t : tensors) {
+    const size_t exp_bytes = (size_t)t.rows * t.groups * t.unit;
+    for (long e0 = 0; e0 < x->E && rc == MOE_OK; e0 += batch) {
+      const long ne = std::min<long>(batch, x->E - e0);
+      uint8_t *base = t.buf + e0 * exp_bytes;
+      hipError_t e = hipMemcpyAsync(tmp, base, ne * exp_bytes, hipMemcpyDeviceToDevice, s);
+      if (e == hipSuccess)
+        e = moe::launch_permute(tmp, base, ne, t.unit, t.rows, t.groups, t.pair, x->w13_layout == MOE_W13_GATE_UP,
+                                to_tiles, s);
+      if (e != hipSuccess) rc = fail(MOE_EHIP, "weight permute: %s", hipGetErrorString(e));
+    }
+  }
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess && rc == MOE_OK) rc = fail(MOE_EHIP, "weight permute sync: %s", hipGetErrorString(e));
+  (void)hipFree(tmp);
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_plan(int E, int K, int N, int top_k, float swiglu_limit, int act_format, int w13_layout, int max_tokens,
+             moe_plan_t *out) {
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (E < 1 || E > moe::kMaxExperts) return fail(MOE_EUNSUPPORTED, "E=%d outside [1, %d]", E, moe::kMaxExperts);
+  if (K < 256 || K % 256) return fail(MOE_EUNSUPPORTED, "K=%d must be a positive multiple of 256", K);
+  if (N < 32 || N % 32) return fail(MOE_EUNSUPPORTED, "N=%d must be a positive multiple of 32", N);
+  if (top_k < 1 || top_k > 16) return fail(MOE_EINVAL, "top_k=%d outside [1, 16]", top_k);
+  if (act_format != MOE_A_MXFP8 && act_format != MOE_A_BF16) return fail(MOE_EUNSUPPORTED, "act_format=%d", act_format);
+  if (w13_layout != MOE_W13_UP_GATE && w13_layout != MOE_W13_GATE_UP) return fail(MOE_EINVAL, "w13_layout=%d", w13_layout);
+  if (max_tokens < 1 || (long)max_tokens * top_k > (1L << 24)) return fail(MOE_EINVAL, "max_tokens=%d", max_tokens);
+  moe_plan_s *p = new moe_plan_s();
+  p->magic = kPlanMagic;
+  p->E = E;
+  p->K = K;
+  p->N = N;
+  p->topk = top_k;
+  p->has_limit = !(isnan(swiglu_limit) || swiglu_limit <= 0.f);
+  p->limit = p->has_limit ? swiglu_limit : 0.f;
+  p->afmt = act_format;
+  p->w13_layout = w13_layout;
+  p->max_tokens = max_tokens;
+  for (int c : kLadder)
+    if (c < max_tokens) p->caps.push_back(c);
+  p->caps.push_back(max_tokens);
+  *out = p;
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan_t plan) {
+  if (plan && plan->magic == kPlanMagic) {
+    plan->magic = 0;
+    delete plan;
+  }
+}
+
+int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows) {
+  if (!plan_ok(plan) || T < 0) return 0;
+  if (tile_rows) *tile_rows = moe::kTileRows;
+  return cap_for(plan, std::max(T, 1));
+}
+
+size_t moe_scratch_bytes(moe_plan_t plan, int tokens, int deterministic) {
+  if (!plan_ok(plan) || tokens < 0) return 0;
+  const int cap = cap_for(plan, std::max(1, std::min(tokens, plan->max_tokens)));
+  return layout(plan, cap, deterministic ? 1 : 0).total;
+}
+
+int moe_prepare_weights(moe_plan_t plan, int weight_format, int num_experts, void *w13, void *s13, const float *g13,
+                        void *w2, void *s2, const float *g2, void *stream, moe_experts_t *out) {
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
+  if (weight_format != MOE_W_MXFP4 && weight_format != MOE_W_NVFP4 && weight_format != MOE_W_NF3)
+    return fail(MOE_EUNSUPPORTED, "weight_format=%d", weight_format);
+  const int want_a = (weight_format == MOE_W_MXFP4) ? MOE_A_MXFP8 : MOE_A_BF16;
+  if (want_a != plan->afmt)
+    return fail(MOE_EUNSUPPORTED, "weight format %d needs activation format %d, plan has %d", weight_format, want_a,
+                plan->afmt);
+  if (num_experts < 1 || num_experts > moe::kMaxExperts) return fail(MOE_EINVAL, "num_experts=%d", num_experts);
+  if (!w13 || !s13 || !w2 || !s2) return fail(MOE_EINVAL, "null weight pointer");
+  if (!aligned(w13, 16) || !aligned(w2, 16) || !aligned(s13, 4) || !aligned(s2, 4))
+    return fail(MOE_EINVAL, "weights must be 16-byte aligned, scales 4-byte aligned");
+  if ((g13 && !aligned(g13, 4)) || (g2 && !aligned(g2, 4))) return fail(MOE_EINVAL, "misaligned global scales");
+  if (weight_format != MOE_W_NVFP4 && (g13 || g2)) return fail(MOE_EINVAL, "global scales are NVFP4-only");
+  moe_experts_s *x = new moe_experts_s();
+  x->magic = kExpertsMagic;
+  x->K = plan->K;
+  x->N = plan->N;
+  x->w13_layout = plan->w13_layout;
+  x->wfmt = weight_format;
+  x->E = num_experts;
+  x->w13 = (uint8_t *)w13;
+  x->s13 = (uint8_t *)s13;
+  x->w2 = (uint8_t *)w2;
+  x->s2 = (uint8_t *)s2;
+  x->g13 = g13;
+  x->g2 = g2;
+  x->prepared = 0;
+  const int rc = permute_all(x, 1, (hipStream_t)stream);
+  if (rc != MOE_OK) {
+    x->magic = 0;
+    delete x;
+    return rc;
+  }
+  x->prepared = 1;
+  *out = x;
+  return MOE_OK;
+}
+
+int moe_unpack_weights(moe_experts_t x, void *stream) {
+  if (!x || x->magic != kExpertsMagic) return fail(MOE_EINVAL, "invalid experts handle");
+  if (!x->prepared) return fail(MOE_ENOTPREPARED, "experts are already in checkpoint layout");
+  const int rc = permute_all(x, 0, (hipStream_t)stream);
+  if (rc == MOE_OK) x->prepared = 0;
+  return rc;
+}
+
+void moe_experts_destroy(moe_experts_t x) {
+  if (x && x->magic == kExpertsMagic) {
+    x->magic = 0;
+    delete x;
+  }
+}
+
+static int check_run_args(moe_plan_t p, const moe_tier *tiers, int n_tiers, const void *x, const int32_t *ids,
+                          const float *wts, void *out, int T, void *scratch) {
+  if (!plan_ok(p)) return fail(MOE_EINVAL, "invalid plan");
+  if (T < 0) return fail(MOE_EINVAL, "T=%d", T);
+  int rc = check_tiers(p, tiers, n_tiers);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !ids || !wts || !out || !scratch) return fail(MOE_EINVAL, "null tensor pointer");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ids, 4) || !aligned(wts, 4) || !aligned(scratch, 256))
+    return fail(MOE_EINVAL, "x/out need 16-byte, ids/weights 4-byte, scratch 256-byte alignment");
+  return MOE_OK;
+}
+
+int moe_run(moe_plan_t p, const moe_tier *tiers, int n_tiers, const void *x, const int32_t *ids,
+            const float *wts, void *out, int T, int deterministic, void *scratch, size_t scratch_bytes,
+            void *stream) {
+  int rc = check_run_args(p, tiers, n_tiers, x, ids, wts, out, T, scratch);
+  if (rc != MOE_OK || T == 0) return rc;
+  deterministic = deterministic ? 1 : 0;
+  const int chunk = p->caps.back();
+  const int cap = cap_for(p, std::min(T, chunk));
+  const Layout L = layout(p, cap, deterministic);
+  if (scratch_bytes < L.total)
+    return fail(MOE_ESCRATCH, "scratch of %zu bytes; %zu needed for %d tokens", scratch_bytes, L.total, T);
+  hipStream_t s = (hipStream_t)stream;
+  for (int t0 = 0; t0 < T; t0 += cap) {
+    const int tc = std::min(cap, T - t0);
+    rc = run_chunk(p, tiers, n_tiers, (const uint16_t *)x + (size_t)t0 * p->K, ids + (size_t)t0 * p->topk,
+                   wts + (size_t)t0 * p->topk, (uint16_t *)out + (size_t)t0 * p->K, tc, deterministic, L,
+                   (uint8_t *)scratch, s, false);
+    if (rc != MOE_OK) return rc;
+  }
+  return MOE_OK;
+}
+
+int moe_debug_route(moe_plan_t p, const moe_tier *tiers, int n_tiers, const int32_t *ids, int T, void *scratch,
+                    size_t scratch_bytes, int32_t *cnt, int32_t *off, int32_t *perm, int32_t *inv, void *stream) {
+  if (!plan_ok(p)) return fail(MOE_EINVAL, "invalid plan");
+  int rc = check_tiers(p, tiers, n_tiers);
+  if (rc != MOE_OK) return rc;
+  if (T < 1 || T > p->max_tokens) return fail(MOE_EINVAL, "T=%d outside [1, max_tokens=%d]", T, p->max_tokens);
+  if (!ids || !scratch || !cnt || !off || !perm || !inv) return fail(MOE_EINVAL, "null pointer");
+  if (!aligned(scratch, 256)) return fail(MOE_EINVAL, "scratch needs 256-byte alignment");
+  const int cap = cap_for(p, T);
+  const Layout L = layout(p, cap, 1);
+  if (scratch_bytes < L.total) return fail(MOE_ESCRATCH, "scratch of %zu bytes; %zu needed", scratch_bytes, L.total);
+  hipStream_t s = (hipStream_t)stream;
+  rc = run_chunk(p, tiers, n_tiers, nullptr, ids, nullptr, nullptr, T, 1, L, (uint8_t *)scratch, s, true);
+  if (rc != MOE_OK) return rc;
+  int U = 0;
+  for (int i = 0; i < n_tiers; i++) U += tiers[i].experts->E;
+  const size_t R = (size_t)T * p->topk;
+  uint8_t *sc = (uint8_t *)scratch;
+  HIP_TRY(hipMemcpyAsync(cnt, sc + L.cnt, 4 * (size_t)U, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(off, sc + L.off, 4 * (size_t)(U + 1), hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(perm, sc + L.perm, 4 * R, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(inv, sc + L.inv, 4 * R, hipMemcpyDeviceToDevice, s));
+  return MOE_OK;
+}
+
+int moe_debug_quant_mxfp8_bf16(const void *x, int rows, int cols, uint8_t *q, uint8_t *scales, void *stream) {
+  if (rows < 0 || cols < 32 || cols % 32) return fail(MOE_EINVAL, "cols must be a positive multiple of 32");
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scales || !aligned(x, 16) || !aligned(q, 16)) return fail(MOE_EINVAL, "null or misaligned pointer");
+  HIP_TRY(moe::launch_quant_bf16((const uint16_t *)x, rows, cols, q, scales, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_debug_quant_mxfp8_f32(const float *h, int rows, int cols, uint8_t *q, uint8_t *scales, void *stream) {
+  if (rows < 0 || cols < 32 || cols % 32) return fail(MOE_EINVAL, "cols must be a positive multiple of 32");
+  if (rows == 0) return MOE_OK;
+  if (!h || !q || !scales || !aligned(h, 16) || !aligned(q, 16)) return fail(MOE_EINVAL, "null or misaligned pointer");
+  HIP_TRY(moe::launch_quant_f32(h, rows, cols, q, scales, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+}  // extern "C"

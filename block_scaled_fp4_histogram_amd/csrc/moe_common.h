@@ -1,0 +1,76 @@
+// Internal declarations shared by the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kTileRows = 16;        // token rows of one GEMM tile (MFMA N dimension)
+constexpr int kRouteChunk = 2048;    // routes handled by one route-planner block
+constexpr int kMaxExperts = 1024;    // experts of all tiers together (LDS histogram size)
+constexpr int kMaxTiers = 2;
+
+enum WFmt { W_MXFP4 = 1, W_NVFP4 = 2, W_NF3 = 3 };
+
+// Route planner: ids -> per-expert counts, offsets, stable permutation, tile table.
+struct RouteArgs {
+  const int32_t *ids;
+  int R, topk, E;                    // routes, slots per token, global id range
+  int n_tiers;
+  const int32_t *emap0, *emap1;      // NULL = identity
+  int E0, E1;                        // experts per tier; U = E0 + E1
+  int G;                             // route blocks (ceil(R / kRouteChunk))
+  int max_tiles;
+  int32_t *ru, *lrank, *chunk_hist;  // per-route expert / in-chunk rank; [G][U] counts
+  int32_t *cnt, *off, *perm, *inv;
+  int32_t *tile_u, *tile_row0, *tier_tiles;
+  // work fused into the same launch by extra blocks
+  const uint16_t *x;                 // bf16 [T, K] (MXFP8 quantisation when xq != NULL)
+  int T, K;
+  uint8_t *xq, *xs;
+  float *zero_buf;                   // fp32 accumulator to clear (atomic combine)
+  long zero_n;
+  int side_blocks;
+};
+
+// GEMM launches (one tier at a time).
+struct GemmArgs {
+  const int32_t *tile_u, *tile_row0, *tier_tiles;
+  int tier, u_base;
+  const int32_t *off, *perm;
+  int topk, K, N;
+  const uint8_t *w13, *s13, *w2, *s2;
+  const float *g13, *g2;
+  const uint8_t *xq, *xs;            // MXFP8 activations (A8)
+  const uint16_t *xb;                // bf16 activations (A16)
+  uint8_t *hq, *hs;                  // MXFP8 intermediate (A8), [Rcap, N] / [Rcap, N/32]
+  uint16_t *hb;                      // bf16 intermediate (A16), [Rcap, N]
+  float limit;
+  int has_limit;
+  const float *topk_w;
+  float *out_acc;                    // fp32 [T, K] (atomic combine)
+  uint16_t *rb;                      // bf16 [R, K] route buffer (deterministic combine)
+  int deterministic;
+};
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_gemm1(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s);
+hipError_t launch_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s);
+hipError_t launch_finalize(int deterministic, const float *out_acc, const uint16_t *rb, const int32_t *inv,
+                           int T, int K, int topk, uint16_t *out, hipStream_t s);
+hipError_t launch_quant_bf16(const uint16_t *x, long rows, int cols, uint8_t *q, uint8_t *sc, hipStream_t s);
+hipError_t launch_quant_f32(const float *h, long rows, int cols, uint8_t *q, uint8_t *sc, hipStream_t s);
+
+// In-place layout change of one weight tensor, experts [e0, e0+ne) staged in tmp.
+//   unit   bytes per (row, 32-column group): 16 (fp4 data), 12 (NF3 data),
+//          1 (E8M0 / E4M3-per-32 scales), 2 (E4M3-per-16 scales)
+//   rows   rows per expert (2N for w13, K for w2); groups = columns / 32
+//   pair   1 for w13: row tiles interleave up and gate halves
+//   gate_up 1 when the checkpoint stacks w13 as [gate; up]
+//   to_tiles 1 = checkpoint -> tile layout, 0 = back
+hipError_t launch_permute(const uint8_t *tmp, uint8_t *dst, long ne, int unit, int rows, int groups, int pair,
+                          int gate_up, int to_tiles, hipStream_t s);
+
+}  // namespace moe

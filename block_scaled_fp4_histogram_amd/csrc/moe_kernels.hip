@@ -1,0 +1,861 @@
+// gfx950 kernels of the routed MoE layer with block-scaled 4-bit expert weights.
+//
+// Data flow of one launch sequence (one chunk of T tokens, R = T * top_k routes):
+//   k_route      expert histogram, prefix offsets, stable route permutation and
+//                the tile table (one block when R <= kRouteChunk; otherwise
+//                count -> scan -> scatter); extra blocks quantise x to MXFP8 and
+//                clear the fp32 accumulator.
+//   k_gemm1_*    per (tile of 16 routes of one expert, 32 intermediate columns):
+//                up and gate GEMMs over K, clamped SwiGLU, requantisation of h
+//                (MXFP8 for W4A8, bf16 for W4A16/W3A16).
+//   k_gemm2_*    per (tile, 64 output columns): down GEMM over N, router weight,
+//                then fp32 atomics (atomic combine) or a bf16 per-slot route
+//                buffer (deterministic combine).
+//   k_cast / k_topk_sum   fp32 accumulator -> bf16, or fixed slot-order sum.
+//
+// Operand layouts of the block-scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4
+// (A = 16 weight rows x 128 k, FP4; B = 128 k x 16 routes, FP8 E4M3), as
+// measured on gfx950: an FP4 operand lane l holds row (l % 16) and the 32
+// consecutive k of block (l / 16), element 2i in the low nibble of byte i; an
+// FP8 operand lane l holds column (l % 16), bytes 0..15 at k = 16*(l/16) + j and
+// bytes 16..31 at k = 64 + 16*(l/16) + j; lane l supplies the E8M0 scale of
+// (row or column l % 16, 32-block l / 16); the accumulator lane l holds column
+// l % 16, rows 4*(l/16) .. +3.
+#include "moe_common.h"
+
+namespace moe {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ numerics
+
+// Nearest E4M3 (fn) code to v, ties to even, magnitudes >= 448 saturate.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {            // |v| >= 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {      // |v| < 2^-6: subnormal grid m * 2^-9
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {                           // keep 3 mantissa bits, round to nearest even
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    r &= 0xFFF00000u;
+    code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+  }
+  return s | code;
+}
+
+// Shared exponent of an MXFP8 block: E = floor(log2 amax) - 8, clamped to
+// [-127, 127]; returns the E8M0 byte E + 127 and the multiplier 2^-E.
+__device__ __forceinline__ uint32_t mx_scale(float amax, float *inv_scale) {
+  const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFFu);   // amax >= 0
+  const int E = max(ex - 135, -127);
+  *inv_scale = __uint_as_float((uint32_t)(127 - E) << 23);
+  return (uint32_t)(E + 127);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// E2M1 code (4 bits) -> fp32.
+__device__ __forceinline__ float e2m1_f32(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const uint32_t bits = (m < 2u) ? (m * 0x3F000000u) : ((m + 252u) << 22);
+  return __uint_as_float(bits | ((c & 8u) << 28));
+}
+
+// E4M3 (fn) byte -> fp32 (NaN codes are out of contract).
+__device__ __forceinline__ float e4m3_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (b & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ float silu_clamped(float gate, float up, float limit, int has_limit) {
+  if (has_limit) {
+    gate = fminf(gate, limit);
+    up = fminf(fmaxf(up, -limit), limit);
+  }
+  return gate / (1.0f + __expf(-gate)) * up;
+}
+
+// Quantise 32 fp32 values to MXFP8 (codes packed 4 per dword).
+__device__ __forceinline__ uint32_t quant_block32(const float *v, uint32_t *codes) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
+  float inv;
+  const uint32_t sb = mx_scale(amax, &inv);
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+    codes[i] = e4m3_rne_sat(v[4 * i] * inv) | (e4m3_rne_sat(v[4 * i + 1] * inv) << 8) |
+               (e4m3_rne_sat(v[4 * i + 2] * inv) << 16) | (e4m3_rne_sat(v[4 * i + 3] * inv) << 24);
+  return sb;
+}
+
+// ------------------------------------------------------------ route planner
+
+__device__ __forceinline__ int resolve_u(int id, const RouteArgs &a) {
+  if (id < 0 || id >= a.E) return -1;
+  const int e0 = a.emap0 ? a.emap0[id] : id;
+  if (e0 >= 0 && e0 < a.E0) return e0;
+  if (a.n_tiers > 1) {
+    const int e1 = a.emap1 ? a.emap1[id] : id;
+    if (e1 >= 0 && e1 < a.E1) return a.E0 + e1;
+  }
+  return -1;
+}
+
+// Exclusive scan of v[0..n) (LDS, n <= kMaxExperts) by a 256-thread block.
+// Returns the total.  tmp: LDS [256].
+__device__ int block_excl_scan(int *v, int n, int *tmp) {
+  const int tid = threadIdx.x;
+  const int per = (n + 255) / 256;
+  const int b = tid * per;
+  int s = 0;
+  for (int i = 0; i < per; i++)
+    if (b + i < n) s += v[b + i];
+  tmp[tid] = s;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int add = (tid >= d) ? tmp[tid - d] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  int run = tmp[tid] - s;   // exclusive prefix of this thread's run
+  for (int i = 0; i < per; i++)
+    if (b + i < n) {
+      const int x = v[b + i];
+      v[b + i] = run;
+      run += x;
+    }
+  const int total = tmp[255];
+  __syncthreads();
+  return total;
+}
+
+// Offsets and tile table from per-expert counts held in LDS cnt[U].
+// Leaves the exclusive offsets in LDS off[U+1].
+__device__ void finish_plan(const RouteArgs &a, int U, int *cnt, int *off, int *ntile, int *tmp) {
+  const int tid = threadIdx.x;
+  for (int u = tid; u < U; u += 256) {
+    off[u] = cnt[u];
+    ntile[u] = (cnt[u] + kTileRows - 1) / kTileRows;
+    a.cnt[u] = cnt[u];
+  }
+  __syncthreads();
+  const int total = block_excl_scan(off, U, tmp);
+  const int ntiles = block_excl_scan(ntile, U, tmp);
+  if (tid == 0) {
+    off[U] = total;
+    ntile[U] = ntiles;
+  }
+  __syncthreads();
+  for (int u = tid; u <= U; u += 256) a.off[u] = off[u];
+  for (int u = tid; u < U; u += 256) {
+    const int tb = ntile[u];
+    for (int i = 0; i * kTileRows < cnt[u]; i++) {
+      a.tile_u[tb + i] = u;
+      a.tile_row0[tb + i] = i * kTileRows;
+    }
+  }
+  if (tid == 0) {
+    a.tier_tiles[0] = 0;
+    a.tier_tiles[1] = ntile[a.E0];
+    a.tier_tiles[2] = ntile[a.E0];
+    a.tier_tiles[3] = ntiles;
+  }
+}
+
+// Work fused into the route launch: MXFP8 quantisation of x (one thread per
+// 32-element block) and clearing of the fp32 accumulator.
+__device__ void route_side_work(const RouteArgs &a, int sb) {
+  const long stride = (long)a.side_blocks * 256;
+  const long i0 = (long)sb * 256 + threadIdx.x;
+  if (a.xq) {
+    const long nblk = (long)a.T * (a.K / 32);
+    for (long i = i0; i < nblk; i += stride) {
+      const v4i *src = (const v4i *)(a.x + i * 32);
+      float v[32];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const v4i w = src[q];
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+          v[8 * q + 2 * d] = bf16_to_f32((uint32_t)w[d] & 0xFFFFu);
+          v[8 * q + 2 * d + 1] = bf16_to_f32((uint32_t)w[d] >> 16);
+        }
+      }
+      uint32_t codes[8];
+      const uint32_t s = quant_block32(v, codes);
+      v4i *dst = (v4i *)(a.xq + i * 32);
+      dst[0] = v4i{(int)codes[0], (int)codes[1], (int)codes[2], (int)codes[3]};
+      dst[1] = v4i{(int)codes[4], (int)codes[5], (int)codes[6], (int)codes[7]};
+      a.xs[i] = (uint8_t)s;
+    }
+  }
+  if (a.zero_buf) {
+    const long n4 = a.zero_n / 4;
+    for (long i = i0; i < n4; i += stride) ((v4f *)a.zero_buf)[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// One block per chunk of kRouteChunk routes (4 waves x 8 rounds of 64).  Each
+// route's rank among the routes of its expert with a smaller index is found
+// with wave ballots, so the permutation is a stable counting sort.
+// SINGLE: the grid has one route block, which also scans and scatters.
+template <bool SINGLE>
+__global__ __launch_bounds__(256) void k_route(RouteArgs a) {
+  if ((int)blockIdx.x >= a.G) {
+    route_side_work(a, blockIdx.x - a.G);
+    return;
+  }
+  __shared__ int whist[4][kMaxExperts];
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int ntile[kMaxExperts + 1];
+  __shared__ int tmp[256];
+  const int U = a.E0 + a.E1;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 4 * kMaxExperts; i += 256) (&whist[0][0])[i] = 0;
+  __syncthreads();
+  const int b = blockIdx.x;
+  const int r0 = b * kRouteChunk + w * (kRouteChunk / 4);
+  const unsigned long long ltmask = (1ull << lane) - 1ull;
+  int us[8], rk[8];
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    const int r = r0 + s * 64 + lane;
+    const int u = (r < a.R) ? resolve_u(a.ids[r], a) : -1;
+    int myrank = 0;
+    unsigned long long rem = __ballot(u >= 0);
+    while (rem) {
+      const int leader = __ffsll((unsigned long long)rem) - 1;
+      const int lu = __shfl(u, leader);
+      const unsigned long long m = __ballot(u == lu);
+      const int base = whist[w][lu];
+      if (u == lu) myrank = base + __popcll(m & ltmask);
+      if (lane == leader) whist[w][lu] = base + __popcll(m);
+      rem &= ~m;
+    }
+    us[s] = u;
+    rk[s] = myrank;
+  }
+  __syncthreads();
+  // wave prefixes within the chunk; chunk totals
+  for (int u = tid; u < U; u += 256) {
+    const int s0 = whist[0][u], s1 = whist[1][u], s2 = whist[2][u], s3 = whist[3][u];
+    whist[0][u] = 0;
+    whist[1][u] = s0;
+    whist[2][u] = s0 + s1;
+    whist[3][u] = s0 + s1 + s2;
+    if (SINGLE) cnt[u] = s0 + s1 + s2 + s3;
+    else a.chunk_hist[b * U + u] = s0 + s1 + s2 + s3;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 8; s++)
+    if (us[s] >= 0) rk[s] += whist[w][us[s]];
+  if (!SINGLE) {
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      const int r = r0 + s * 64 + lane;
+      if (r < a.R) {
+        a.ru[r] = us[s];
+        a.lrank[r] = rk[s];
+      }
+    }
+    return;
+  }
+  // single chunk: the chunk totals are the expert counts
+  finish_plan(a, U, cnt, off, ntile, tmp);
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    const int r = r0 + s * 64 + lane;
+    if (r < a.R) {
+      if (us[s] >= 0) {
+        const int pos = off[us[s]] + rk[s];
+        a.perm[pos] = r;
+        a.inv[r] = pos;
+      } else {
+        a.inv[r] = -1;
+      }
+    }
+  }
+}
+
+// Multi-chunk: per-expert scan over chunks, offsets, tile table.
+__global__ __launch_bounds__(256) void k_route_scan(RouteArgs a) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int ntile[kMaxExperts + 1];
+  __shared__ int tmp[256];
+  const int U = a.E0 + a.E1;
+  for (int u = threadIdx.x; u < U; u += 256) {
+    int run = 0;
+    for (int b = 0; b < a.G; b++) {
+      const int v = a.chunk_hist[b * U + u];
+      a.chunk_hist[b * U + u] = run;
+      run += v;
+    }
+    cnt[u] = run;
+  }
+  __syncthreads();
+  finish_plan(a, U, cnt, off, ntile, tmp);
+  __syncthreads();
+  for (int u = threadIdx.x; u < U; u += 256)
+    for (int b = 0; b < a.G; b++) a.chunk_hist[b * U + u] += off[u];
+}
+
+__global__ __launch_bounds__(256) void k_route_scatter(RouteArgs a) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.R) return;
+  const int U = a.E0 + a.E1;
+  const int u = a.ru[r];
+  if (u < 0) {
+    a.inv[r] = -1;
+    return;
+  }
+  const int pos = a.chunk_hist[(r / kRouteChunk) * U + u] + a.lrank[r];
+  a.perm[pos] = r;
+  a.inv[r] = pos;
+}
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
+  if (a.G == 1) {
+    hipLaunchKernelGGL(k_route<true>, dim3(1 + a.side_blocks), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_route<false>, dim3(a.G + a.side_blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_route_scatter, dim3((a.R + 255) / 256), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ quantisers
+
+__global__ __launch_bounds__(256) void k_quant_bf16(const uint16_t *x, long nblk, uint8_t *q, uint8_t *sc) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nblk) return;
+  float v[32];
+  for (int j = 0; j < 32; j++) v[j] = bf16_to_f32(x[i * 32 + j]);
+  uint32_t codes[8];
+  sc[i] = (uint8_t)quant_block32(v, codes);
+  for (int j = 0; j < 8; j++) ((uint32_t *)(q + i * 32))[j] = codes[j];
+}
+
+__global__ __launch_bounds__(256) void k_quant_f32(const float *h, long nblk, uint8_t *q, uint8_t *sc) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nblk) return;
+  float v[32];
+  for (int j = 0; j < 32; j++) v[j] = h[i * 32 + j];
+  uint32_t codes[8];
+  sc[i] = (uint8_t)quant_block32(v, codes);
+  for (int j = 0; j < 8; j++) ((uint32_t *)(q + i * 32))[j] = codes[j];
+}
+
+hipError_t launch_quant_bf16(const uint16_t *x, long rows, int cols, uint8_t *q, uint8_t *sc, hipStream_t s) {
+  const long nblk = rows * (cols / 32);
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quant_bf16, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, x, nblk, q, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_f32(const float *h, long rows, int cols, uint8_t *q, uint8_t *sc, hipStream_t s) {
+  const long nblk = rows * (cols / 32);
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quant_f32, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, h, nblk, q, sc);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ tile schedule
+
+struct TileInfo {
+  int valid, e, p0, rows;
+};
+
+__device__ __forceinline__ TileInfo tile_info(const GemmArgs &a) {
+  TileInfo ti;
+  const int tbeg = a.tier_tiles[2 * a.tier], tend = a.tier_tiles[2 * a.tier + 1];
+  const int tile = tbeg + (int)blockIdx.y;
+  ti.valid = tile < tend;
+  if (!ti.valid) return ti;
+  const int u = a.tile_u[tile];
+  ti.e = u - a.u_base;
+  ti.p0 = a.off[u] + a.tile_row0[tile];
+  ti.rows = min(kTileRows, a.off[u + 1] - ti.p0);
+  return ti;
+}
+
+// -------------------------------------------------- W4A8 (MXFP4 x MXFP8)
+
+// Weight tile layout (per expert, per matrix of R rows x Kd columns): row tiles
+// of 16 rows; within a row tile, k-tiles of 128 columns, each stored lane-major
+// (lane l = row + 16*q holds the 32 columns 128*kt + 32*q .. +31 of its row),
+// 16 bytes per lane for FP4.  The last k-tile of a row tile may hold fewer
+// 32-column groups (only its first 16*nq lanes exist).  Scales likewise, one
+// byte per lane.  w13 row tiles interleave up and gate: tile 2j = up rows
+// 16j..16j+15, tile 2j+1 = gate rows 16j..16j+15.
+
+__device__ __forceinline__ v8i fp4_operand(v4i a) { return v8i{a[0], a[1], a[2], a[3], 0, 0, 0, 0}; }
+
+__device__ __forceinline__ v4f mfma_fp4_fp8(v4i a, v8i b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(a), b, c, 4, 0, 0, sa, 0, sb);
+}
+
+// grid: x = N/32 (intermediate column blocks), y = tiles; 4 waves split K.
+__global__ __launch_bounds__(256) void k_gemm1_a8(GemmArgs a) {
+  const TileInfo ti = tile_info(a);
+  if (!ti.valid) return;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, g = l >> 4;
+  const int K = a.K, N = a.N, nkt = K / 128;
+  const int hb = blockIdx.x;
+  int t = -1;
+  if (c < ti.rows) t = a.perm[ti.p0 + c] / a.topk;
+  const uint8_t *xrow = a.xq + (size_t)(t < 0 ? 0 : t) * K;
+  const uint8_t *xsrow = a.xs + (size_t)(t < 0 ? 0 : t) * (K / 32);
+  const size_t rt_bytes = (size_t)16 * (K / 2);
+  const size_t rt_scales = (size_t)16 * (K / 32);
+  const uint8_t *wt = a.w13 + (size_t)ti.e * (2 * N) * (K / 2) + (size_t)(4 * hb) * rt_bytes + l * 16;
+  const uint8_t *st = a.s13 + (size_t)ti.e * (2 * N) * (K / 32) + (size_t)(4 * hb) * rt_scales + l;
+  v4f acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int kt = w; kt < nkt; kt += 4) {
+    v4i A[4];
+    int sa[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      A[q] = *(const v4i *)(wt + q * rt_bytes + (size_t)kt * 1024);
+      sa[q] = st[q * rt_scales + kt * 64];
+    }
+    v4i B0 = v4i{0, 0, 0, 0}, B1 = v4i{0, 0, 0, 0};
+    int sb = 0;
+    if (t >= 0) {
+      B0 = *(const v4i *)(xrow + kt * 128 + 16 * g);
+      B1 = *(const v4i *)(xrow + kt * 128 + 64 + 16 * g);
+      sb = xsrow[kt * 4 + g];
+    }
+    const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
+#pragma unroll
+    for (int q = 0; q < 4; q++) acc[q] = mfma_fp4_fp8(A[q], bop, acc[q], sa[q], sb);
+  }
+  __shared__ float red[4][16][64];
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) red[w][q * 4 + i][l] = acc[q][i];
+  __syncthreads();
+  if (w != 0) return;
+  float h[8];
+#pragma unroll
+  for (int s = 0; s < 2; s++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int iu = (2 * s) * 4 + i, ig = (2 * s + 1) * 4 + i;
+      const float up = red[0][iu][l] + red[1][iu][l] + red[2][iu][l] + red[3][iu][l];
+      const float gate = red[0][ig][l] + red[1][ig][l] + red[2][ig][l] + red[3][ig][l];
+      h[s * 4 + i] = silu_clamped(gate, up, a.limit, a.has_limit);
+    }
+  // MXFP8 block of 32 intermediate columns of route c: 8 values here x 4 lanes
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(h[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  float inv;
+  const uint32_t sbyte = mx_scale(amax, &inv);
+  if (c < ti.rows) {
+    const size_t p = (size_t)(ti.p0 + c);
+    const int n0 = hb * 32;
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      const uint32_t word = e4m3_rne_sat(h[s * 4] * inv) | (e4m3_rne_sat(h[s * 4 + 1] * inv) << 8) |
+                            (e4m3_rne_sat(h[s * 4 + 2] * inv) << 16) | (e4m3_rne_sat(h[s * 4 + 3] * inv) << 24);
+      *(uint32_t *)(a.hq + p * N + n0 + 16 * s + 4 * g) = word;
+    }
+    if (g == 0) a.hs[p * (N / 32) + hb] = (uint8_t)sbyte;
+  }
+}
+
+// Combine epilogue shared by the GEMM2 kernels: acc holds 4 output columns
+// (f0 .. f0+3) of route column c.
+__device__ __forceinline__ void combine_store(const GemmArgs &a, const TileInfo &ti, int c, int f0, v4f acc,
+                                              float gscale) {
+  if (c >= ti.rows) return;
+  const int r = a.perm[ti.p0 + c];
+  const float wgt = a.topk_w[r] * gscale;
+  if (a.deterministic) {
+    uint2 v;
+    v.x = pack_bf16x2(wgt * acc[0], wgt * acc[1]);
+    v.y = pack_bf16x2(wgt * acc[2], wgt * acc[3]);
+    *(uint2 *)(a.rb + (size_t)r * a.K + f0) = v;
+  } else {
+    float *o = a.out_acc + (size_t)(r / a.topk) * a.K + f0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) atomicAdd(o + i, wgt * acc[i]);
+  }
+}
+
+// grid: x = K/64 (output column blocks), y = tiles; wave w owns 16 columns.
+__global__ __launch_bounds__(256) void k_gemm2_a8(GemmArgs a) {
+  const TileInfo ti = tile_info(a);
+  if (!ti.valid) return;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, g = l >> 4;
+  const int K = a.K, N = a.N, nkt = (N + 127) / 128;
+  const int rt = blockIdx.x * 4 + w;
+  const size_t rt_bytes = (size_t)16 * (N / 2);
+  const size_t rt_scales = (size_t)16 * (N / 32);
+  const uint8_t *wt = a.w2 + (size_t)ti.e * K * (N / 2) + (size_t)rt * rt_bytes + l * 16;
+  const uint8_t *st = a.s2 + (size_t)ti.e * K * (N / 32) + (size_t)rt * rt_scales + l;
+  const bool have = c < ti.rows;
+  const uint8_t *hrow = a.hq + (size_t)(ti.p0 + (have ? c : 0)) * N;
+  const uint8_t *hsrow = a.hs + (size_t)(ti.p0 + (have ? c : 0)) * (N / 32);
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < nkt; kt++) {
+    const int kb = kt * 128;
+    v4i A = v4i{0, 0, 0, 0};
+    int sa = 0;
+    if (kb + 32 * g < N) {
+      A = *(const v4i *)(wt + (size_t)kt * 1024);
+      sa = st[kt * 64];
+    }
+    v4i B0 = v4i{0, 0, 0, 0}, B1 = v4i{0, 0, 0, 0};
+    int sb = 0;
+    if (have) {
+      if (kb + 16 * g < N) B0 = *(const v4i *)(hrow + kb + 16 * g);
+      if (kb + 64 + 16 * g < N) B1 = *(const v4i *)(hrow + kb + 64 + 16 * g);
+      if (kb + 32 * g < N) sb = hsrow[kb / 32 + g];
+    }
+    const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
+    acc = mfma_fp4_fp8(A, bop, acc, sa, sb);
+  }
+  combine_store(a, ti, c, rt * 16 + 4 * g, acc, 1.0f);
+}
+
+// ------------------------------------------- W4A16 (NVFP4) / W3A16 (NF3)
+
+// Weight tiles as for MXFP4 (lane l = row + 16*q holds 32 consecutive columns of
+// its row; 16 bytes for NVFP4, 12 bytes = four 3-byte NF3 groups), scales 2
+// bytes per lane (NVFP4, E4M3 per 16) or 1 byte (NF3, E4M3 per 32).  The bf16
+// MFMA v_mfma_f32_16x16x32_bf16 takes 8 consecutive k per lane group; lane l
+// feeds its 32 columns in 4 steps of 8, and the activation operand walks the
+// same columns, so each step pairs the same k on both sides.
+
+// 8 fp4 codes (one dword) x scale -> 8 bf16 (exact: E2M1 x E4M3 fits bf16).
+__device__ __forceinline__ v8bf nvfp4_step(uint32_t w, float sc) {
+  v4i r;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const uint32_t byte = (w >> (8 * m)) & 0xFFu;
+    const float lo = e2m1_f32(byte & 15u) * sc, hi = e2m1_f32(byte >> 4) * sc;
+    r[m] = (int)__builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  }
+  return __builtin_bit_cast(v8bf, r);
+}
+
+// NF3 magnitudes |codebook| ascending; code c >= 4 is +mag[c-4], c < 4 is -mag[3-c].
+__device__ __forceinline__ float nf3_val(uint32_t c, float m0, float m1, float m2, float m3) {
+  const uint32_t mi = (c & 4u) ? (c & 3u) : (3u - (c & 3u));
+  const float v = (mi & 2u) ? ((mi & 1u) ? m3 : m2) : ((mi & 1u) ? m1 : m0);
+  return (c & 4u) ? v : -v;
+}
+
+// 8 NF3 codes (one 24-bit group) -> 8 bf16 (codebook x scale, rounded to bf16).
+__device__ __forceinline__ v8bf nf3_step(uint32_t w24, float m0, float m1, float m2, float m3) {
+  v4i r;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const float lo = nf3_val((w24 >> (6 * m)) & 7u, m0, m1, m2, m3);
+    const float hi = nf3_val((w24 >> (6 * m + 3)) & 7u, m0, m1, m2, m3);
+    r[m] = (int)pack_bf16x2(lo, hi);
+  }
+  return __builtin_bit_cast(v8bf, r);
+}
+
+// Dequantised operand of one lane for k-step s (0..3) of a 128-column k-tile.
+template <int WF>
+struct A16Tile {
+  uint32_t d[4];   // NVFP4: 4 dwords of codes; NF3: 3 dwords (12 bytes)
+  uint32_t sc;     // scale byte(s)
+  __device__ __forceinline__ void load(const uint8_t *data, const uint8_t *scales) {
+    if (WF == W_NVFP4) {
+      const v4i v = *(const v4i *)data;
+      d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+      sc = *(const uint16_t *)scales;
+    } else {
+      const uint32_t *p = (const uint32_t *)data;
+      d[0] = p[0]; d[1] = p[1]; d[2] = p[2]; d[3] = 0;
+      sc = *scales;
+    }
+  }
+  __device__ __forceinline__ void zero() { d[0] = d[1] = d[2] = d[3] = 0; sc = 0; }
+  __device__ __forceinline__ v8bf step(int s) const {
+    if (WF == W_NVFP4) {
+      return nvfp4_step(d[s], e4m3_f32(s < 2 ? (sc & 0xFFu) : (sc >> 8)));
+    } else {
+      const float f = e4m3_f32(sc);
+      // group s of 24 bits starts at bit 24*s of the 96-bit lane word
+      const uint64_t lo = (uint64_t)d[0] | ((uint64_t)d[1] << 32);
+      uint32_t w24;
+      if (s == 0) w24 = (uint32_t)lo & 0xFFFFFFu;
+      else if (s == 1) w24 = (uint32_t)(lo >> 24) & 0xFFFFFFu;
+      else if (s == 2) w24 = (uint32_t)((lo >> 48) | ((uint64_t)d[2] << 16)) & 0xFFFFFFu;
+      else w24 = d[2] >> 8;
+      return nf3_step(w24, 0.1275f * f, 0.3563f * f, 0.6047f * f, f);
+    }
+  }
+};
+
+template <int WF>
+struct FmtGeom {
+  static constexpr int unit = (WF == W_NF3) ? 12 : 16;   // data bytes per (row, 32-col group)
+  static constexpr int sunit = (WF == W_NVFP4) ? 2 : 1;  // scale bytes per (row, 32-col group)
+};
+
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int WF>
+__global__ __launch_bounds__(256) void k_gemm1_a16(GemmArgs a) {
+  const TileInfo ti = tile_info(a);
+  if (!ti.valid) return;
+  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, g = l >> 4;
+  const int K = a.K, N = a.N, nkt = K / 128, groups = K / 32;
+  const int hb = blockIdx.x;
+  int t = -1;
+  if (c < ti.rows) t = a.perm[ti.p0 + c] / a.topk;
+  const uint16_t *xrow = a.xb + (size_t)(t < 0 ? 0 : t) * K;
+  const size_t rt_bytes = (size_t)16 * groups * U;
+  const size_t rt_scales = (size_t)16 * groups * SU;
+  const uint8_t *wt = a.w13 + (size_t)ti.e * (2 * N) * groups * U + (size_t)(4 * hb) * rt_bytes + l * U;
+  const uint8_t *st = a.s13 + (size_t)ti.e * (2 * N) * groups * SU + (size_t)(4 * hb) * rt_scales + l * SU;
+  v4f acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int kt = w; kt < nkt; kt += 4) {
+    A16Tile<WF> A[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) A[q].load(wt + q * rt_bytes + (size_t)kt * 64 * U, st + q * rt_scales + kt * 64 * SU);
+    v4i B[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++) B[s] = v4i{0, 0, 0, 0};
+    if (t >= 0) {
+      const v4i *xp = (const v4i *)(xrow + kt * 128 + 32 * g);
+#pragma unroll
+      for (int s = 0; s < 4; s++) B[s] = xp[s];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const v8bf b = __builtin_bit_cast(v8bf, B[s]);
+#pragma unroll
+      for (int q = 0; q < 4; q++) acc[q] = mfma_bf16(A[q].step(s), b, acc[q]);
+    }
+  }
+  __shared__ float red[4][16][64];
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) red[w][q * 4 + i][l] = acc[q][i];
+  __syncthreads();
+  if (w != 0) return;
+  const float gs = a.g13 ? a.g13[ti.e] : 1.0f;
+  if (c < ti.rows) {
+    const size_t p = (size_t)(ti.p0 + c);
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      float h[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int iu = (2 * s) * 4 + i, ig = (2 * s + 1) * 4 + i;
+        const float up = (red[0][iu][l] + red[1][iu][l] + red[2][iu][l] + red[3][iu][l]) * gs;
+        const float gate = (red[0][ig][l] + red[1][ig][l] + red[2][ig][l] + red[3][ig][l]) * gs;
+        h[i] = silu_clamped(gate, up, a.limit, a.has_limit);
+      }
+      uint2 v;
+      v.x = pack_bf16x2(h[0], h[1]);
+      v.y = pack_bf16x2(h[2], h[3]);
+      *(uint2 *)(a.hb + p * N + hb * 32 + 16 * s + 4 * g) = v;
+    }
+  }
+}
+
+template <int WF>
+__global__ __launch_bounds__(256) void k_gemm2_a16(GemmArgs a) {
+  const TileInfo ti = tile_info(a);
+  if (!ti.valid) return;
+  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, g = l >> 4;
+  const int K = a.K, N = a.N, nkt = (N + 127) / 128, groups = N / 32;
+  const int rt = blockIdx.x * 4 + w;
+  const size_t rt_bytes = (size_t)16 * groups * U;
+  const size_t rt_scales = (size_t)16 * groups * SU;
+  const uint8_t *wt = a.w2 + (size_t)ti.e * K * groups * U + (size_t)rt * rt_bytes + l * U;
+  const uint8_t *st = a.s2 + (size_t)ti.e * K * groups * SU + (size_t)rt * rt_scales + l * SU;
+  const bool have = c < ti.rows;
+  const uint16_t *hrow = a.hb + (size_t)(ti.p0 + (have ? c : 0)) * N;
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < nkt; kt++) {
+    const int kb = kt * 128;
+    const bool inb = kb + 32 * g < N;
+    A16Tile<WF> A;
+    if (inb) A.load(wt + (size_t)kt * 64 * U, st + kt * 64 * SU);
+    else A.zero();
+    v4i B[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++) B[s] = v4i{0, 0, 0, 0};
+    if (have && inb) {
+      const v4i *hp = (const v4i *)(hrow + kb + 32 * g);
+#pragma unroll
+      for (int s = 0; s < 4; s++) B[s] = hp[s];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; s++) acc = mfma_bf16(A.step(s), __builtin_bit_cast(v8bf, B[s]), acc);
+  }
+  combine_store(a, ti, c, rt * 16 + 4 * g, acc, a.g2 ? a.g2[ti.e] : 1.0f);
+}
+
+hipError_t launch_gemm1(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s) {
+  if (grid_tiles <= 0) return hipSuccess;
+  const dim3 grid(a.N / 32, grid_tiles), block(256);
+  if (wfmt == W_MXFP4) hipLaunchKernelGGL(k_gemm1_a8, grid, block, 0, s, a);
+  else if (wfmt == W_NVFP4) hipLaunchKernelGGL(k_gemm1_a16<W_NVFP4>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_gemm1_a16<W_NF3>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s) {
+  if (grid_tiles <= 0) return hipSuccess;
+  const dim3 grid(a.K / 64, grid_tiles), block(256);
+  if (wfmt == W_MXFP4) hipLaunchKernelGGL(k_gemm2_a8, grid, block, 0, s, a);
+  else if (wfmt == W_NVFP4) hipLaunchKernelGGL(k_gemm2_a16<W_NVFP4>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_gemm2_a16<W_NF3>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ combine
+
+// fp32 accumulator -> bf16, 8 values per thread.
+__global__ __launch_bounds__(256) void k_cast(const float *acc, long n8, uint16_t *out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const v4f a = ((const v4f *)acc)[2 * i], b = ((const v4f *)acc)[2 * i + 1];
+  uint4 o;
+  o.x = pack_bf16x2(a[0], a[1]);
+  o.y = pack_bf16x2(a[2], a[3]);
+  o.z = pack_bf16x2(b[0], b[1]);
+  o.w = pack_bf16x2(b[2], b[3]);
+  ((uint4 *)out)[i] = o;
+}
+
+// out[t] = bf16(sum over valid slots j, in slot order, of rb[t*topk + j]); 8 columns per thread.
+__global__ __launch_bounds__(256) void k_topk_sum(const uint16_t *rb, const int32_t *inv, int T, int K, int topk,
+                                                  uint16_t *out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long per_row = K / 8;
+  if (i >= (long)T * per_row) return;
+  const long t = i / per_row, c8 = i % per_row;
+  float s[8];
+#pragma unroll
+  for (int m = 0; m < 8; m++) s[m] = 0.f;
+  for (int j = 0; j < topk; j++) {
+    const long r = t * topk + j;
+    if (inv[r] < 0) continue;
+    const uint4 v = *(const uint4 *)(rb + r * K + c8 * 8);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      s[2 * m] += bf16_to_f32(wv[m] & 0xFFFFu);
+      s[2 * m + 1] += bf16_to_f32(wv[m] >> 16);
+    }
+  }
+  uint4 o;
+  o.x = pack_bf16x2(s[0], s[1]);
+  o.y = pack_bf16x2(s[2], s[3]);
+  o.z = pack_bf16x2(s[4], s[5]);
+  o.w = pack_bf16x2(s[6], s[7]);
+  *(uint4 *)(out + t * K + c8 * 8) = o;
+}
+
+hipError_t launch_finalize(int deterministic, const float *out_acc, const uint16_t *rb, const int32_t *inv, int T,
+                           int K, int topk, uint16_t *out, hipStream_t s) {
+  const long n8 = (long)T * K / 8;
+  if (n8 == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
+  if (deterministic) hipLaunchKernelGGL(k_topk_sum, grid, block, 0, s, rb, inv, T, K, topk, out);
+  else hipLaunchKernelGGL(k_cast, grid, block, 0, s, out_acc, n8, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ repacker
+
+// Position, in the checkpoint layout, of byte `o` of the tile layout (both
+// within one expert).  See the weight tile layout above.
+__device__ __forceinline__ long ckpt_offset(long o, int unit, int rows, int groups, int pair, int gate_up) {
+  const long rt_size = (long)16 * groups * unit;
+  const long rt = o / rt_size;
+  const long in_rt = o % rt_size;
+  const long kt = in_rt / (64L * unit);
+  const long rem = in_rt % (64L * unit);
+  const int lane = (int)(rem / unit), b = (int)(rem % unit);
+  const int r = lane & 15, q = lane >> 4;
+  long row;
+  if (pair) {
+    const long j = rt >> 1;
+    const int half = (int)(rt & 1);  // 0 = up, 1 = gate
+    const long half_rows = rows / 2;
+    const long start = (half == 0) == (gate_up == 0) ? 0 : half_rows;
+    row = start + 16 * j + r;
+  } else {
+    row = 16 * rt + r;
+  }
+  return row * ((long)groups * unit) + (kt * 4 + q) * unit + b;
+}
+
+template <typename Word>
+__global__ __launch_bounds__(256) void k_permute(const uint8_t *tmp, uint8_t *dst, long total_words, long exp_bytes,
+                                                 int unit, int rows, int groups, int pair, int gate_up,
+                                                 int to_tiles) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total_words) return;
+  const long o = i * (long)sizeof(Word);
+  const long e = o / exp_bytes, in_e = o % exp_bytes;
+  const long ck = e * exp_bytes + ckpt_offset(in_e, unit, rows, groups, pair, gate_up);
+  if (to_tiles) *(Word *)(dst + o) = *(const Word *)(tmp + ck);
+  else *(Word *)(dst + ck) = *(const Word *)(tmp + o);
+}
+
+hipError_t launch_permute(const uint8_t *tmp, uint8_t *dst, long ne, int unit, int rows, int groups, int pair,
+                          int gate_up, int to_tiles, hipStream_t s) {
+  const long exp_bytes = (long)rows * groups * unit;
+  const long bytes = ne * exp_bytes;
+  if (bytes == 0) return hipSuccess;
+  if (unit % 4 == 0) {
+    const long words = bytes / 4;
+    hipLaunchKernelGGL(k_permute<uint32_t>, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, tmp, dst, words,
+                       exp_bytes, unit, rows, groups, pair, gate_up, to_tiles);
+  } else {
+    hipLaunchKernelGGL(k_permute<uint8_t>, dim3((unsigned)((bytes + 255) / 256)), dim3(256), 0, s, tmp, dst, bytes,
+                       exp_bytes, unit, rows, groups, pair, gate_up, to_tiles);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,173 @@
+/*
+ * moe.h -- C ABI of the routed mixture-of-experts layer with block-scaled
+ * 4-bit expert weights, for AMD MI355X (gfx950).
+ *
+ * What the layer computes (vLLM "hybrid_loader.py", _apply_ref; sglang
+ * "moe_b12x_next.py", module docstring): for each token t and each of its
+ * top_k slots j whose expert id e = topk_ids[t,j] lies in [0, E),
+ *     z   = W13[e] . x_t                 (w13 stacked [up; gate])
+ *     h   = silu(min(gate, L)) * clamp(up, -L, L)   (L = swiglu_limit)
+ *     y   = W2[e] . h
+ *     out[t] += topk_weights[t,j] * y
+ * Ids outside [0, E), including the CUDA-graph padding id -1, contribute
+ * nothing; a row with no valid slot is written as zeros (moe_b12x_next.py,
+ * module docstring on direct ids).
+ *
+ * Weight formats (checkpoint layouts, all row-major and contiguous):
+ *   MOE_W_MXFP4: w13 u8 [E, 2N, K/2] (two E2M1 codes per byte, element 2i in
+ *                the low nibble), s13 E8M0 [E, 2N, K/32], w2 u8 [E, K, N/2],
+ *                s2 E8M0 [E, K, N/32]   (moe_b12x_next.py, _convert_layer).
+ *                Activations are quantised to MXFP8 (E4M3 + E8M0 per 32) in
+ *                the layer, before each GEMM (W4A8).
+ *   MOE_W_NVFP4: as MXFP4 but E4M3 scales per 16 (s13 [E, 2N, K/16], s2
+ *                [E, K, N/16]) and one fp32 global per expert per tensor
+ *                (g13 [E], g2 [E]) (hybrid_loader.py, create_weights, _deq_nv).
+ *                bf16 activations (W4A16).
+ *   MOE_W_NF3:   3-bit indices into {-1, -0.6047, -0.3563, -0.1275, 0.1275,
+ *                0.3563, 0.6047, 1}, 8 codes per 3 little-endian bytes
+ *                (w13 [E, 2N, K/8*3], w2 [E, K, N/8*3]), E4M3 scales per 32
+ *                (hybrid_loader.py, _NF3_VALS, _unpack_nf3). bf16 activations.
+ *
+ * Conventions.  Every tensor pointer passed to moe_prepare_weights, moe_run
+ * and the moe_debug_* calls is a DEVICE pointer.  Streams are hipStream_t
+ * passed as void* (NULL = the null stream).  moe_run is stream-ordered: it
+ * does not allocate, free or synchronise, so it may be captured in a HIP
+ * graph once plan and weights are prepared.  Functions return a moe_status;
+ * nothing throws.  moe_last_error() gives a message for the calling thread's
+ * most recent failure.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,          /* null / misaligned pointer, bad size or argument */
+  MOE_EUNSUPPORTED = -2,    /* shape or format combination the kernels do not cover */
+  MOE_ENOTPREPARED = -3,    /* experts not prepared, or prepared for another plan */
+  MOE_ESCRATCH = -4,        /* scratch buffer smaller than moe_scratch_bytes() */
+  MOE_EHIP = -5             /* a HIP runtime call failed */
+} moe_status;
+
+typedef enum { MOE_W_MXFP4 = 1, MOE_W_NVFP4 = 2, MOE_W_NF3 = 3 } moe_wfmt;
+typedef enum { MOE_A_MXFP8 = 1, MOE_A_BF16 = 2 } moe_afmt;
+typedef enum { MOE_W13_UP_GATE = 0, MOE_W13_GATE_UP = 1 } moe_w13_layout;
+
+typedef struct moe_plan_s *moe_plan_t;       /* one layer geometry (host memory only) */
+typedef struct moe_experts_s *moe_experts_t; /* one layer's (or tier's) prepared weights */
+
+/* One group of experts taking part in a moe_run.  expert_map (device, int32
+ * [E], may be NULL = identity) maps a global expert id to this tier's local
+ * id, or -1 when the id belongs elsewhere (hybrid_loader.py: per-tier expert
+ * maps, "translates global->local + drops -1").  A global id is served by the
+ * first tier whose map accepts it. */
+typedef struct {
+  moe_experts_t experts;
+  const int32_t *expert_map;
+} moe_tier;
+
+/*
+ * moe_plan -- plan one layer geometry (sglang moe_b12x_next.py: plans are per
+ * geometry (experts, K, N, top-k, swiglu limit) and shared by every layer of
+ * that geometry).
+ *   E            global expert id range [0, E) of topk_ids (1 .. 4096)
+ *   K            hidden size (GEMM1 reduction, output width); multiple of 256
+ *   N            intermediate size of this rank's slice; multiple of 32
+ *   top_k        slots per token (1 .. 16)
+ *   swiglu_limit clamp L of the SwiGLU; NaN or <= 0 = no clamp
+ *   act_format   MOE_A_MXFP8 (for MXFP4 experts) or MOE_A_BF16 (NVFP4 / NF3)
+ *   w13_layout   MOE_W13_UP_GATE (default) or MOE_W13_GATE_UP
+ *   max_tokens   largest T one launch handles; larger batches run in chunks
+ *                of the largest capacity (moe_b12x_next.py, _Geometry.forward)
+ * Host only.  *out receives a plan owned by the caller (moe_plan_destroy).
+ */
+int moe_plan(int E, int K, int N, int top_k, float swiglu_limit, int act_format, int w13_layout,
+             int max_tokens, moe_plan_t *out);
+void moe_plan_destroy(moe_plan_t plan);
+
+/* Bytes of device scratch one moe_run of `tokens` tokens needs under `plan`
+ * (tokens above the top capacity are sized for one chunk).  The arena is
+ * carved into 256-byte aligned pieces.  Host only; 0 on a bad plan. */
+size_t moe_scratch_bytes(moe_plan_t plan, int tokens, int deterministic);
+
+/*
+ * moe_prepare_weights -- repack one layer's checkpoint tensors IN PLACE into
+ * the tile layout the kernels stream (moe_b12x_next.py, _convert_layer: the
+ * checkpoint storage is reused, a second copy would double expert memory).
+ *   weight_format  MOE_W_MXFP4 / MOE_W_NVFP4 / MOE_W_NF3 (must fit the plan's
+ *                  act_format)
+ *   num_experts    experts held in these tensors (this tier's local ids)
+ *   w13,s13,w2,s2  device buffers in the checkpoint layout above; they are
+ *                  rewritten in place and afterwards hold the tile layout
+ *   g13, g2        device fp32 [num_experts] globals (NVFP4; NULL = 1.0)
+ * The returned handle borrows the buffers (the caller keeps ownership and must
+ * keep them alive); moe_experts_destroy releases only the handle.  Prepare
+ * allocates a temporary device buffer and synchronises `stream`; it is not
+ * for graph capture.
+ */
+int moe_prepare_weights(moe_plan_t plan, int weight_format, int num_experts, void *w13, void *s13,
+                        const float *g13, void *w2, void *s2, const float *g2, void *stream,
+                        moe_experts_t *out);
+/* Undo moe_prepare_weights: rewrite the buffers back to the checkpoint layout
+ * in place.  The handle becomes unprepared (moe_run refuses it). */
+int moe_unpack_weights(moe_experts_t experts, void *stream);
+void moe_experts_destroy(moe_experts_t experts);
+
+/*
+ * moe_run -- the layer.
+ *   tiers, n_tiers  1 or 2 groups of prepared experts (2 = hybrid: NVFP4 and
+ *                   NF3 tiers, both through the bf16 path)
+ *   x               bf16 [T, K] row-major
+ *   topk_ids        int32 [T, top_k]; ids outside [0, E) are skipped
+ *   topk_weights    fp32 [T, top_k]
+ *   out             bf16 [T, K], fully overwritten
+ *   T               tokens (0 = no-op)
+ *   deterministic   0: per-route results are added into an fp32 accumulator
+ *                   with atomics (run-to-run order may vary);
+ *                   1: per-slot route buffer + fixed-order top-k sum,
+ *                   bit-stable run to run (moe_b12x_next.py, DETERMINISTIC)
+ *   scratch         device buffer of >= moe_scratch_bytes(plan, T, deterministic)
+ * Stream-ordered, no allocation, no synchronisation.
+ */
+int moe_run(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const void *x, const int32_t *topk_ids,
+            const float *topk_weights, void *out, int T, int deterministic, void *scratch,
+            size_t scratch_bytes, void *stream);
+
+/* Message of the calling thread's most recent failure ("" if none). */
+const char *moe_last_error(void);
+
+/* Capacity the plan runs a batch of T tokens at, and the token rows of that
+ * capacity's tile (0 on a bad plan).  Host only; used by tests and benches. */
+int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows);
+
+/* ---- stage entry points, for the bit-exact stage tests ---------------- */
+
+/*
+ * moe_debug_route -- the route planner alone (expert histogram, prefix-sum
+ * offsets, stable token permutation).  Experts of all tiers form one index
+ * space u = (experts of earlier tiers) + local id.
+ *   cnt  int32 [U], off int32 [U+1], perm int32 [T*top_k] (first off[U]
+ *   entries are the valid route indices r = t*top_k + j sorted by (u, r)),
+ *   inv  int32 [T*top_k] (position of r in perm, or -1 for a skipped slot).
+ * Uses `scratch` like moe_run (capacity of T tokens, T <= max_tokens).
+ */
+int moe_debug_route(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const int32_t *topk_ids, int T,
+                    void *scratch, size_t scratch_bytes, int32_t *cnt, int32_t *off, int32_t *perm,
+                    int32_t *inv, void *stream);
+
+/* MXFP8 quantiser alone: rows x cols (cols % 32 == 0) of bf16 or fp32 ->
+ * E4M3 codes u8 [rows, cols] + E8M0 scales u8 [rows, cols/32]. */
+int moe_debug_quant_mxfp8_bf16(const void *x, int rows, int cols, uint8_t *q, uint8_t *scales, void *stream);
+int moe_debug_quant_mxfp8_f32(const float *h, int rows, int cols, uint8_t *q, uint8_t *scales, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,168 @@
+"""Layer parity on the GPU (through the C ABI) against the CPU oracle, per row:
+rel-L2 <= 1e-2 and rel max-abs <= 2e-2 against the oracle's float64
+accumulator; rows with no valid slot exactly zero; deterministic mode bit-stable.
+Small configurations are compared on every row, full-size ones on sampled rows."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_histogram_amd as M
+import oracle as O
+from block_scaled_fp4_histogram_amd import inputs as I
+
+from gpu_util import DeviceLayer, assert_rows_match, dev
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def layer(name, **kw):
+    key = (name, tuple(sorted(kw.items())))
+    if key not in _CACHE:
+        if name in I.CONFIGS:
+            prob = I.make_problem(name)
+        else:
+            prob = SMALL[name]()
+        _CACHE.clear()   # keep at most one large layer resident
+        _CACHE[key] = DeviceLayer(prob, **kw)
+    return _CACHE[key]
+
+
+SMALL = {
+    # ragged T and N with a partial last k-tile in the down GEMM (N % 128 == 96)
+    "mxfp4_ragged": lambda: I.make_problem(I.Config("mxfp4_ragged", T=37, E=12, K=512, N=224, topk=3, limit=7.0,
+                                                    fmt=I.FMT_MXFP4, e8m0_exp=(-6, -2)), seed=3),
+    "nvfp4_small": lambda: I.make_problem(I.Config("nvfp4_small", T=21, E=16, K=256, N=160, topk=4, limit=None,
+                                                   fmt=I.FMT_NVFP4), seed=4),
+    "nf3_small": lambda: I.make_problem(I.Config("nf3_small", T=19, E=10, K=512, N=96, topk=2, limit=None,
+                                                 fmt=I.FMT_NF3), seed=5),
+    "hybrid_small": lambda: I.make_problem(I.Config("hybrid_small", T=29, E=24, K=256, N=128, topk=5, limit=None,
+                                                    fmt=I.FMT_NVFP4, hybrid_nvfp4=8), seed=6),
+    "nvfp4_clamped": lambda: I.make_problem(I.Config("nvfp4_clamped", T=9, E=6, K=256, N=64, topk=2, limit=30.0,
+                                                     fmt=I.FMT_NVFP4), seed=7),
+}
+
+
+def _sample_rows(prob, n, seed=0):
+    """Rows to compare at full size: spread over the batch, plus every padding row and
+    rows routed to the most loaded expert."""
+    T = prob.cfg.T
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    ids = prob.ids
+    valid = ids[(ids >= 0) & (ids < prob.cfg.E)]
+    if valid.size:
+        top = np.bincount(valid, minlength=prob.cfg.E).argmax()
+        rows |= set(np.flatnonzero((ids == top).any(axis=1))[:4].tolist())
+    rows |= set(np.flatnonzero(~((ids >= 0) & (ids < prob.cfg.E)).any(axis=1))[:2].tolist())
+    return np.array(sorted(rows), dtype=np.int32)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mxfp4_ragged", "nvfp4_small", "nf3_small", "hybrid_small",
+                                  "nvfp4_clamped"])
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_small_layers_all_rows(name, deterministic):
+    L = layer(name)
+    out = L.run(deterministic=deterministic)
+    acc, _ = O.moe_problem(L.prob)
+    assert_rows_match(out, acc, label=f"{name} det={deterministic}")
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_decode_all_rows(deterministic):
+    L = layer("decode")
+    out = L.run(deterministic=deterministic)
+    acc, _ = O.moe_problem(L.prob)
+    assert_rows_match(out, acc, label=f"decode det={deterministic}")
+    assert torch.all(out[6:].view(torch.int16) == 0)   # the two padding rows
+
+
+@pytest.mark.parametrize("name,nrows", [("prefill", 20), ("nvfp4_decode", 8), ("nvfp4_prefill", 16),
+                                        ("hybrid", 16)])
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_full_size_sampled_rows(name, nrows, deterministic):
+    L = layer(name)
+    out = L.run(deterministic=deterministic)
+    rows = _sample_rows(L.prob, nrows)
+    acc, _ = O.moe_problem(L.prob, rows=rows)
+    assert_rows_match(out, acc, rows=rows, label=f"{name} det={deterministic}")
+
+
+@pytest.mark.parametrize("name", ["decode", "hybrid_small", "prefill"])
+def test_deterministic_bit_stable(name):
+    L = layer(name)
+    outs = [L.run(deterministic=True).view(torch.int16).clone() for _ in range(3)]
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_chunked_batch_matches_single_launch():
+    """T above the plan's max_tokens runs in chunks of the top capacity."""
+    prob = SMALL["mxfp4_ragged"]()
+    big = DeviceLayer(prob)
+    ref = big.run(deterministic=True)
+    small = DeviceLayer(SMALL["mxfp4_ragged"](), max_tokens=8)
+    out = small.run(deterministic=True)
+    assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
+    acc, _ = O.moe_problem(prob)
+    assert_rows_match(small.run(deterministic=False), acc, label="chunked atomic")
+
+
+def test_invalid_ids_and_zero_weights():
+    L = layer("mxfp4_ragged")
+    p = L.prob
+    E = p.cfg.E
+    ids = p.ids.copy()
+    wts = p.wts.copy()
+    ids[:, 1] = np.array([-1, E, E + 7, np.iinfo(np.int32).min, np.iinfo(np.int32).max] * 8)[: p.cfg.T]
+    ids[3, :] = -1                 # a row with no valid slot
+    wts[4, 0] = 0.0                # a zero-weight slot
+    for det in (False, True):
+        out = L.run(ids=dev(ids), wts=dev(wts), deterministic=det)
+        q = I.Problem(p.cfg, p.x, ids, wts, p.tiers)
+        acc, _ = O.moe_problem(q)
+        assert_rows_match(out, acc, label=f"invalid ids det={det}")
+        assert torch.all(out[3].view(torch.int16) == 0)
+
+
+def test_duplicate_ids_in_a_row():
+    L = layer("nvfp4_small")
+    p = L.prob
+    ids = np.repeat(p.ids[:, :1], p.cfg.topk, axis=1).copy()
+    out = L.run(ids=dev(ids), deterministic=True)
+    acc, _ = O.moe_problem(I.Problem(p.cfg, p.x, ids, p.wts, p.tiers))
+    assert_rows_match(out, acc, label="duplicate ids")
+
+
+def test_zero_tokens_is_noop_and_all_padding_batch():
+    L = layer("tiny")
+    c = L.prob.cfg
+    x = torch.zeros((0, c.K), dtype=torch.bfloat16, device="cuda")
+    ids = torch.zeros((0, c.topk), dtype=torch.int32, device="cuda")
+    wts = torch.zeros((0, c.topk), dtype=torch.float32, device="cuda")
+    out = M.run(L.plan, L.tiers, x, ids, wts, scratch=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    assert out.shape == (0, c.K)
+    ids = torch.full((c.T, c.topk), -1, dtype=torch.int32, device="cuda")
+    for det in (False, True):
+        out = L.run(ids=ids, deterministic=det)
+        assert torch.all(out.view(torch.int16) == 0)
+
+
+def test_scratch_too_small_is_refused():
+    L = layer("tiny")
+    c = L.prob.cfg
+    need = L.plan.scratch_bytes(c.T, False)
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(M.MoeError) as ei:
+        L.run(scratch=small)
+    assert ei.value.code == M.MOE_ESCRATCH
+
+
+def test_gate_up_layout_flag():
+    prob = SMALL["mxfp4_ragged"]()
+    L = DeviceLayer(prob, gate_up=True)
+    out = L.run()
+    acc, _ = O.moe_problem(prob, gate_up=True)
+    assert_rows_match(out, acc, label="gate_up")
