@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE layer on one MI355X.
+
+One step = one moe_run (route planner, MXFP8 quantiser, GEMM1 + SwiGLU +
+requantiser, GEMM2 + combine) over one batch, inputs already resident in HBM.
+Steps cycle through --layers independent copies of the expert weights so the
+decode working set (about 0.22 GB of distinct experts per layer) cannot be
+served from the 256 MB last-level cache, as in a real stack of layers.
+
+Prints ONE JSON line. `value` is tokens/s per layer (live tokens / layer time);
+`roofline` is for the dominant kernel, timed live with HIP events recorded by
+the library on the launch stream; `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_scaled_fp4_histogram_amd import inputs as I  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+METRIC = "routed-MoE tokens/s per layer + % HBM peak (decode) / % MFMA peak (prefill)"
+STAGES = ("route", "gemm1", "gemm2", "combine")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def expert_bytes(fmt, K, N):
+    """(w13+s13, w2+s2) bytes of one expert in the checkpoint format."""
+    if fmt == I.FMT_MXFP4:
+        per = lambda rows, cols: rows * cols // 2 + rows * cols // 32
+    elif fmt == I.FMT_NVFP4:
+        per = lambda rows, cols: rows * cols // 2 + rows * cols // 16
+    else:
+        per = lambda rows, cols: rows * cols // 8 * 3 + rows * cols // 32
+    return per(2 * N, K), per(K, N)
+
+
+def algorithmic(prob):
+    """Algorithmic bytes and flops of one layer and of each GEMM kernel: weights of the
+    distinct experts touched (each read once), activations in, results out."""
+    c = prob.cfg
+    ids = prob.ids
+    valid = (ids >= 0) & (ids < c.E)
+    live = int(valid.any(axis=1).sum())
+    routes = int(valid.sum())
+    distinct = np.unique(ids[valid])
+    w1 = w2 = 0
+    for g in distinct:
+        for t in prob.tiers:
+            e = int(g) if t.emap is None else int(t.emap[g])
+            if 0 <= e < t.E:
+                a, b = expert_bytes(t.fmt, c.K, c.N)
+                w1 += a
+                w2 += b
+                break
+    a8 = prob.tiers[0].fmt == I.FMT_MXFP4
+    x_in = live * c.K * ((1 + 1 / 32) if a8 else 2)        # activation operand as GEMM1 reads it
+    h_bytes = routes * c.N * ((1 + 1 / 32) if a8 else 2)   # intermediate written by GEMM1, read by GEMM2
+    out_bytes = live * c.K * 2                              # bf16 output rows
+    flops1 = 2.0 * routes * 2 * c.N * c.K
+    flops2 = 2.0 * routes * c.K * c.N
+    return dict(live=live, routes=routes, distinct=int(len(distinct)),
+                layer_bytes=w1 + w2 + live * c.K * 2 + out_bytes,
+                gemm1_bytes=w1 + x_in + h_bytes, gemm2_bytes=w2 + h_bytes + out_bytes,
+                gemm1_flops=flops1, gemm2_flops=flops2, layer_flops=flops1 + flops2)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("moe_kernels.hip", "moe_common.h"):
+        with open(os.path.join(ROOT, "block_scaled_fp4_histogram_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel, per_launch_units):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(prob, seconds, live_rows):
+    """The oracle, as it stands, on a bounded sample of the workload's rows."""
+    import oracle as O
+    O.lib()
+    rows = live_rows
+    t0 = time.perf_counter()
+    done = 0
+    reps = 0
+    while True:
+        O.moe_problem(prob, rows=rows)
+        done += len(rows)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    return done / el, O.num_threads(), reps, el
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="decode", choices=sorted(I.CONFIGS))
+    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--layers", type=int, default=8, help="independent weight copies cycled per step")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle budget (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=16, help="token rows in the CPU oracle sample")
+    ap.add_argument("--timing-runs", type=int, default=200, help="runs with per-stage HIP events")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer shards by "
+              "tensor-parallel N-slices plus one all-reduce, which is not built here).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_fp4_histogram_amd as M
+
+    cfg = I.CONFIGS[args.config]
+    log(f"config {cfg.name}: generating inputs")
+    prob = I.make_problem(cfg.name)
+    alg = algorithmic(prob)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    a8 = prob.tiers[0].fmt == I.FMT_MXFP4
+    plan = M.Plan(cfg.E, cfg.K, cfg.N, cfg.topk, cfg.limit, M.A_MXFP8 if a8 else M.A_BF16, max_tokens=cfg.T)
+
+    def upload(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    host = []
+    for t in prob.tiers:
+        w = t.weights
+        host.append(({k: upload(w[k]) for k in ("w13", "s13", "w2", "s2")},
+                     None if w["g13"] is None else upload(w["g13"]),
+                     None if w["g2"] is None else upload(w["g2"]),
+                     None if t.emap is None else upload(t.emap), t))
+    layers = []
+    for li in range(args.layers):
+        tiers = []
+        for ws, g13, g2, emap, t in host:
+            ts = {k: (v if li == 0 else v.clone()) for k, v in ws.items()}
+            tiers.append((ts, M.Experts(plan, t.fmt, t.E, ts["w13"], ts["s13"], ts["w2"], ts["s2"], g13, g2), emap))
+        layers.append(tiers)
+        log(f"layer copy {li + 1}/{args.layers} prepared")
+    x = upload(prob.x).view(torch.bfloat16)
+    ids = upload(prob.ids)
+    wts = upload(prob.wts)
+    out = torch.empty_like(x)
+    scratch = M.scratch_for(plan, cfg.T, args.deterministic, dev)
+    run_tiers = [[(ex, emap) for _, ex, emap in tiers] for tiers in layers]
+
+    def step(i):
+        M.run(plan, run_tiers[i % len(run_tiers)], x, ids, wts, out, args.deterministic, scratch)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    log(f"timed: {ms_step * 1000:.1f} us per layer")
+
+    # per-stage durations with events the library records on the launch stream
+    nrec = min(args.timing_runs, args.steps)
+    plan.enable_stage_timing(nrec)
+    for i in range(nrec):
+        step(i)
+    stage_ms, runs = plan.stage_times()
+    plan.enable_stage_timing(0)
+    stage_us = {s: 1000.0 * v / max(runs, 1) for s, v in zip(STAGES, stage_ms)}
+    log("stages (us): " + ", ".join(f"{k} {v:.1f}" for k, v in stage_us.items()))
+
+    dominant = max(("gemm1", "gemm2"), key=lambda s: stage_us[s])
+    dom_s = stage_us[dominant] * 1e-6
+    decode_like = alg["live"] <= 64
+    if decode_like:
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+        achieved = alg[f"{dominant}_bytes"] / dom_s / 1e9
+    else:
+        bound, unit = "mfma", "TFLOP/s"
+        peak = MFMA_PEAK_TFLOPS["fp8" if a8 else "bf16"]
+        achieved = alg[f"{dominant}_flops"] / dom_s / 1e12
+    traffic = measured_traffic(cfg.name + ("_det" if args.deterministic else ""), dominant, 1)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        valid_rows = np.flatnonzero(((prob.ids >= 0) & (prob.ids < cfg.E)).any(axis=1))
+        rng = np.random.default_rng(0)
+        rows = valid_rows if len(valid_rows) <= args.cpu_rows else np.sort(rng.choice(valid_rows, args.cpu_rows, replace=False))
+        log(f"cpu oracle on {len(rows)} rows, budget {args.cpu_seconds}s")
+        tps, cores, reps, el = cpu_baseline(prob, args.cpu_seconds, rows.astype(np.int32))
+        cpu = {"value": round(tps, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"{len(rows)} live token rows of the {cfg.name} batch x {reps} repetitions "
+                         f"({el:.1f} s, float64 CPU oracle, OpenMP over rows)"}
+
+    us_layer = ms_step * 1000.0
+    tokens_s = alg["live"] / (ms_step * 1e-3)
+    workload = (f"{cfg.name}: T={cfg.T} ({alg['live']} live), E={cfg.E}, K={cfg.K}, N={cfg.N}, top-{cfg.topk}, "
+                f"{'MXFP4 W4A8' if a8 else ('NVFP4+NF3 hybrid' if cfg.hybrid_nvfp4 else 'NVFP4 W4A16')}, "
+                f"{'deterministic' if args.deterministic else 'atomic'} combine")
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4*mxfp8->f32" if a8 else "bf16(dequant nvfp4/nf3)*bf16->f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "tokens": cfg.T, "live_tokens": alg["live"], "experts": cfg.E,
+                   "hidden": cfg.K, "intermediate": cfg.N, "top_k": cfg.topk,
+                   "distinct_experts": alg["distinct"], "layer_copies_cycled": args.layers,
+                   "us_per_layer": round(us_layer, 2),
+                   "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+                   "layer_hbm_frac": round(alg["layer_bytes"] / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "layer_mfma_frac": round(alg["layer_flops"] / (us_layer * 1e-6) / 1e12 /
+                                            MFMA_PEAK_TFLOPS["fp8" if a8 else "bf16"], 4)},
+        "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -76,6 +76,17 @@ class Plan:
         cap = _lib.load().moe_plan_capacity(self.handle, T, C.byref(rows))
         return cap, rows.value
 
+    def enable_stage_timing(self, max_runs: int):
+        """Record HIP events between the layer's stages for the next max_runs runs."""
+        _check(_lib.load().moe_plan_enable_stage_timing(self.handle, max_runs))
+
+    def stage_times(self):
+        """Summed ms of (route, gemm1, gemm2, combine) over the recorded runs, and the run count."""
+        ms = (C.c_float * 4)()
+        runs = C.c_int(0)
+        _check(_lib.load().moe_plan_stage_times(self.handle, ms, 4, C.byref(runs)))
+        return [float(v) for v in ms], runs.value
+
     def close(self):
         if self.handle:
             _lib.load().moe_plan_destroy(self.handle)

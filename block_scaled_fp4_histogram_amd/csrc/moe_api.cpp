@@ -33,6 +33,7 @@ int fail(int code, const char *fmt, ...) {
     if (e_ != hipSuccess) return fail(MOE_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
+constexpr int kStageEvents = 5;  // before route, after route / gemm1 / gemm2 / combine
 constexpr uint32_t kPlanMagic = 0x4D4F4550u;     // "MOEP"
 constexpr uint32_t kExpertsMagic = 0x4D4F4558u;  // "MOEX"
 
@@ -52,6 +53,9 @@ struct moe_plan_s {
   int has_limit;
   int afmt, w13_layout, max_tokens;
   std::vector<int> caps;  // ascending; caps.back() == chunk
+  // optional stage timing: kStageEvents events per recorded run
+  std::vector<hipEvent_t> events;
+  int timing_runs_max = 0, timing_runs = 0;
 };
 
 struct moe_experts_s {
@@ -146,7 +150,8 @@ int check_tiers(const moe_plan_s *p, const moe_tier *tiers, int n_tiers) {
 // Everything one chunk needs after validation.
 int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uint16_t *x, const int32_t *ids,
               const float *wts, uint16_t *out, int T, int deterministic, const Layout &L, uint8_t *scratch,
-              hipStream_t s, bool route_only) {
+              hipStream_t s, bool route_only, const hipEvent_t *ev = nullptr) {
+  if (ev) HIP_TRY(hipEventRecord(ev[0], s));
   const int R = T * p->topk;
   auto I32 = [&](size_t o) { return (int32_t *)(scratch + o); };
   moe::RouteArgs ra;
@@ -191,6 +196,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ra.side_blocks = (int)std::min<long>((side_work + 255) / 256, 2048);
   HIP_TRY(moe::launch_route(ra, s));
   if (route_only) return MOE_OK;
+  if (ev) HIP_TRY(hipEventRecord(ev[1], s));
 
   moe::GemmArgs ga;
   memset(&ga, 0, sizeof ga);
@@ -230,6 +236,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     HIP_TRY(moe::launch_gemm1(xp->wfmt, ga, grid_tiles, s));
     u_base += xp->E;
   }
+  if (ev) HIP_TRY(hipEventRecord(ev[2], s));
   u_base = 0;
   for (int i = 0; i < n_tiers; i++) {
     const moe_experts_s *xp = tiers[i].experts;
@@ -245,7 +252,9 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     HIP_TRY(moe::launch_gemm2(xp->wfmt, ga, grid_tiles, s));
     u_base += xp->E;
   }
+  if (ev) HIP_TRY(hipEventRecord(ev[3], s));
   HIP_TRY(moe::launch_finalize(deterministic, ga.out_acc, ga.rb, I32(L.inv), T, p->K, p->topk, out, s));
+  if (ev) HIP_TRY(hipEventRecord(ev[4], s));
   return MOE_OK;
 }
 
@@ -329,9 +338,43 @@ int moe_plan(int E, int K, int N, int top_k, float swiglu_limit, int act_format,
 
 void moe_plan_destroy(moe_plan_t plan) {
   if (plan && plan->magic == kPlanMagic) {
+    for (hipEvent_t e : plan->events) (void)hipEventDestroy(e);
     plan->magic = 0;
     delete plan;
   }
+}
+
+int moe_plan_enable_stage_timing(moe_plan_t plan, int max_runs) {
+  if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
+  if (max_runs < 0 || max_runs > 100000) return fail(MOE_EINVAL, "max_runs=%d", max_runs);
+  for (hipEvent_t e : plan->events) (void)hipEventDestroy(e);
+  plan->events.clear();
+  plan->timing_runs = plan->timing_runs_max = 0;
+  for (long i = 0; i < (long)max_runs * kStageEvents; i++) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e));
+    plan->events.push_back(e);
+  }
+  plan->timing_runs_max = max_runs;
+  return MOE_OK;
+}
+
+int moe_plan_stage_times(moe_plan_t plan, float *ms, int n, int *runs) {
+  if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
+  if (!ms || n < kStageEvents - 1) return fail(MOE_EINVAL, "need room for %d stages", kStageEvents - 1);
+  for (int i = 0; i < n; i++) ms[i] = 0.f;
+  for (int r = 0; r < plan->timing_runs; r++) {
+    const hipEvent_t *ev = &plan->events[(size_t)r * kStageEvents];
+    HIP_TRY(hipEventSynchronize(ev[kStageEvents - 1]));
+    for (int i = 0; i + 1 < kStageEvents; i++) {
+      float t = 0.f;
+      HIP_TRY(hipEventElapsedTime(&t, ev[i], ev[i + 1]));
+      ms[i] += t;
+    }
+  }
+  if (runs) *runs = plan->timing_runs;
+  plan->timing_runs = 0;
+  return MOE_OK;
 }
 
 int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows) {
@@ -428,11 +471,17 @@ int moe_run(moe_plan_t p, const moe_tier *tiers, int n_tiers, const void *x, con
   if (scratch_bytes < L.total)
     return fail(MOE_ESCRATCH, "scratch of %zu bytes; %zu needed for %d tokens", scratch_bytes, L.total, T);
   hipStream_t s = (hipStream_t)stream;
+  // stage timing covers single-chunk runs only
+  const hipEvent_t *ev = nullptr;
+  if (p->timing_runs < p->timing_runs_max && T <= cap) {
+    ev = &p->events[(size_t)p->timing_runs * kStageEvents];
+    p->timing_runs++;
+  }
   for (int t0 = 0; t0 < T; t0 += cap) {
     const int tc = std::min(cap, T - t0);
     rc = run_chunk(p, tiers, n_tiers, (const uint16_t *)x + (size_t)t0 * p->K, ids + (size_t)t0 * p->topk,
                    wts + (size_t)t0 * p->topk, (uint16_t *)out + (size_t)t0 * p->K, tc, deterministic, L,
-                   (uint8_t *)scratch, s, false);
+                   (uint8_t *)scratch, s, false, ev);
     if (rc != MOE_OK) return rc;
   }
   return MOE_OK;

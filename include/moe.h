@@ -76,7 +76,8 @@ typedef struct {
  * moe_plan -- plan one layer geometry (sglang moe_b12x_next.py: plans are per
  * geometry (experts, K, N, top-k, swiglu limit) and shared by every layer of
  * that geometry).
- *   E            global expert id range [0, E) of topk_ids (1 .. 4096)
+ *   E            global expert id range [0, E) of topk_ids (1 .. 1024; all tiers together
+ *                hold at most 1024 experts)
  *   K            hidden size (GEMM1 reduction, output width); multiple of 256
  *   N            intermediate size of this rank's slice; multiple of 32
  *   top_k        slots per token (1 .. 16)
@@ -145,6 +146,19 @@ const char *moe_last_error(void);
 /* Capacity the plan runs a batch of T tokens at, and the token rows of that
  * capacity's tile (0 on a bad plan).  Host only; used by tests and benches. */
 int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows);
+
+/* ---- instrumentation ------------------------------------------------- */
+
+/* Stage timing for benchmarks: after this call, each moe_run under `plan`
+ * records a HIP event on its stream before the route planner and after each
+ * stage (route, gemm1, gemm2, combine), for up to max_runs runs (later runs
+ * record nothing).  Events are created here, not in moe_run.  max_runs = 0
+ * turns timing off and frees the events.  Returns a moe_status. */
+int moe_plan_enable_stage_timing(moe_plan_t plan, int max_runs);
+/* Waits for the recorded runs and writes the summed milliseconds of each
+ * stage (ms[0] route, ms[1] gemm1, ms[2] gemm2, ms[3] combine; n >= 4) over
+ * the recorded runs; *runs receives their count.  Resets the run counter. */
+int moe_plan_stage_times(moe_plan_t plan, float *ms, int n, int *runs);
 
 /* ---- stage entry points, for the bit-exact stage tests ---------------- */
 
