@@ -127,6 +127,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle budget (0 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=16, help="token rows in the CPU oracle sample")
     ap.add_argument("--timing-runs", type=int, default=200, help="runs with per-stage HIP events")
+    ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
+                    help="replay the layer from a captured HIP graph (auto: batches of <= 64 tokens, "
+                         "as decode steps run in serving)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the layer shards by "
@@ -159,7 +162,9 @@ def main():
     for li in range(args.layers):
         tiers = []
         for ws, g13, g2, emap, t in host:
-            ts = {k: (v if li == 0 else v.clone()) for k, v in ws.items()}
+            # every copy but the last is cloned from the checkpoint-layout upload before any
+            # copy is repacked in place; the last copy repacks the upload itself
+            ts = {k: (v if li == args.layers - 1 else v.clone()) for k, v in ws.items()}
             tiers.append((ts, M.Experts(plan, t.fmt, t.E, ts["w13"], ts["s13"], ts["w2"], ts["s2"], g13, g2), emap))
         layers.append(tiers)
         log(f"layer copy {li + 1}/{args.layers} prepared")
@@ -176,19 +181,42 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+    use_graph = args.graph == "on" or (args.graph == "auto" and cfg.T <= 64)
+    nl = len(run_tiers)
+    if use_graph:
+        # one graph holds one run per layer copy; it is replayed steps / copies times
+        args.steps = max(nl, (args.steps + nl - 1) // nl * nl)
+        graph = torch.cuda.CUDAGraph()
+        cap_stream = torch.cuda.Stream()
+        cap_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap_stream):
+            for i in range(nl):   # warm the capture stream once outside the graph
+                step(i)
+        torch.cuda.current_stream().wait_stream(cap_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for i in range(nl):
+                step(i)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps ({'graph replay' if use_graph else 'eager'})")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for i in range(args.steps):
-        step(i)
+    if use_graph:
+        for _ in range(args.steps // nl):
+            graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     e1.record()
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
     log(f"timed: {ms_step * 1000:.1f} us per layer")
 
-    # per-stage durations with events the library records on the launch stream
+    # per-stage durations with events the library records on the launch stream (eager runs)
     nrec = min(args.timing_runs, args.steps)
     plan.enable_stage_timing(nrec)
     for i in range(nrec):
@@ -242,6 +270,7 @@ def main():
         "config": {"workload": workload, "tokens": cfg.T, "live_tokens": alg["live"], "experts": cfg.E,
                    "hidden": cfg.K, "intermediate": cfg.N, "top_k": cfg.topk,
                    "distinct_experts": alg["distinct"], "layer_copies_cycled": args.layers,
+                   "launch": "hipGraph replay" if use_graph else "eager",
                    "us_per_layer": round(us_layer, 2),
                    "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
                    "layer_hbm_frac": round(alg["layer_bytes"] / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

@@ -119,55 +119,46 @@ __device__ __forceinline__ int resolve_u(int id, const RouteArgs &a) {
   return -1;
 }
 
-// Exclusive scan of v[0..n) (LDS, n <= kMaxExperts) by a 256-thread block.
-// Returns the total.  tmp: LDS [256].
-__device__ int block_excl_scan(int *v, int n, int *tmp) {
+// Offsets and tile table from per-expert counts held in LDS cnt[U].  Wave 0
+// scans (each lane owns a run of consecutive experts, runs combined with a
+// wave prefix sum); leaves the exclusive offsets in LDS off[U+1].
+__device__ void finish_plan(const RouteArgs &a, int U, const int *cnt, int *off, int *tbeg) {
   const int tid = threadIdx.x;
-  const int per = (n + 255) / 256;
-  const int b = tid * per;
-  int s = 0;
-  for (int i = 0; i < per; i++)
-    if (b + i < n) s += v[b + i];
-  tmp[tid] = s;
-  __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {
-    const int add = (tid >= d) ? tmp[tid - d] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
-  }
-  int run = tmp[tid] - s;   // exclusive prefix of this thread's run
-  for (int i = 0; i < per; i++)
-    if (b + i < n) {
-      const int x = v[b + i];
-      v[b + i] = run;
-      run += x;
+  if (tid < 64) {
+    const int per = (U + 63) / 64, b = tid * per;
+    int s = 0, nt = 0;
+    for (int i = 0; i < per; i++)
+      if (b + i < U) {
+        s += cnt[b + i];
+        nt += (cnt[b + i] + kTileRows - 1) / kTileRows;
+      }
+    int is = s, it = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int vs = __shfl_up(is, d), vt = __shfl_up(it, d);
+      if (tid >= d) {
+        is += vs;
+        it += vt;
+      }
     }
-  const int total = tmp[255];
-  __syncthreads();
-  return total;
-}
-
-// Offsets and tile table from per-expert counts held in LDS cnt[U].
-// Leaves the exclusive offsets in LDS off[U+1].
-__device__ void finish_plan(const RouteArgs &a, int U, int *cnt, int *off, int *ntile, int *tmp) {
-  const int tid = threadIdx.x;
-  for (int u = tid; u < U; u += 256) {
-    off[u] = cnt[u];
-    ntile[u] = (cnt[u] + kTileRows - 1) / kTileRows;
-    a.cnt[u] = cnt[u];
-  }
-  __syncthreads();
-  const int total = block_excl_scan(off, U, tmp);
-  const int ntiles = block_excl_scan(ntile, U, tmp);
-  if (tid == 0) {
-    off[U] = total;
-    ntile[U] = ntiles;
+    int rs = is - s, rt = it - nt;
+    for (int i = 0; i < per; i++)
+      if (b + i < U) {
+        off[b + i] = rs;
+        tbeg[b + i] = rt;
+        rs += cnt[b + i];
+        rt += (cnt[b + i] + kTileRows - 1) / kTileRows;
+      }
+    if (tid == 63) {
+      off[U] = is;
+      tbeg[U] = it;
+    }
   }
   __syncthreads();
   for (int u = tid; u <= U; u += 256) a.off[u] = off[u];
   for (int u = tid; u < U; u += 256) {
-    const int tb = ntile[u];
+    a.cnt[u] = cnt[u];
+    const int tb = tbeg[u];
     for (int i = 0; i * kTileRows < cnt[u]; i++) {
       a.tile_u[tb + i] = u;
       a.tile_row0[tb + i] = i * kTileRows;
@@ -175,9 +166,9 @@ __device__ void finish_plan(const RouteArgs &a, int U, int *cnt, int *off, int *
   }
   if (tid == 0) {
     a.tier_tiles[0] = 0;
-    a.tier_tiles[1] = ntile[a.E0];
-    a.tier_tiles[2] = ntile[a.E0];
-    a.tier_tiles[3] = ntiles;
+    a.tier_tiles[1] = tbeg[a.E0];
+    a.tier_tiles[2] = tbeg[a.E0];
+    a.tier_tiles[3] = tbeg[U];
   }
 }
 
@@ -227,8 +218,7 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
   __shared__ int whist[4][kMaxExperts];
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
-  __shared__ int ntile[kMaxExperts + 1];
-  __shared__ int tmp[256];
+  __shared__ int tbeg[kMaxExperts + 1];
   const int U = a.E0 + a.E1;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   for (int i = tid; i < 4 * kMaxExperts; i += 256) (&whist[0][0])[i] = 0;
@@ -282,7 +272,7 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
     return;
   }
   // single chunk: the chunk totals are the expert counts
-  finish_plan(a, U, cnt, off, ntile, tmp);
+  finish_plan(a, U, cnt, off, tbeg);
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < 8; s++) {
@@ -303,8 +293,7 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
 __global__ __launch_bounds__(256) void k_route_scan(RouteArgs a) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
-  __shared__ int ntile[kMaxExperts + 1];
-  __shared__ int tmp[256];
+  __shared__ int tbeg[kMaxExperts + 1];
   const int U = a.E0 + a.E1;
   for (int u = threadIdx.x; u < U; u += 256) {
     int run = 0;
@@ -316,7 +305,7 @@ __global__ __launch_bounds__(256) void k_route_scan(RouteArgs a) {
     cnt[u] = run;
   }
   __syncthreads();
-  finish_plan(a, U, cnt, off, ntile, tmp);
+  finish_plan(a, U, cnt, off, tbeg);
   __syncthreads();
   for (int u = threadIdx.x; u < U; u += 256)
     for (int b = 0; b < a.G; b++) a.chunk_hist[b * U + u] += off[u];
@@ -418,7 +407,43 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(v4i a, v8i b, v4f c, int sa, int sb)
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(a), b, c, 4, 0, 0, sa, 0, sb);
 }
 
-// grid: x = N/32 (intermediate column blocks), y = tiles; 4 waves split K.
+// Operands of one 128-column k-tile of GEMM1 for one lane: the up and gate
+// row tiles of two adjacent 16-column intermediate blocks, and the token's
+// MXFP8 activation slice.
+struct A8G1Stage {
+  v4i A[4];
+  int sa[4];
+  v4i B0, B1;
+  int sb;
+};
+
+__device__ __forceinline__ void a8g1_load(A8G1Stage &st, const uint8_t *wt, const uint8_t *sp, size_t rt_bytes,
+                                          size_t rt_scales, int kt, const uint8_t *xrow, const uint8_t *xsrow,
+                                          bool have, int g) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    st.A[q] = *(const v4i *)(wt + q * rt_bytes + (size_t)kt * 1024);
+    st.sa[q] = sp[q * rt_scales + kt * 64];
+  }
+  if (have) {
+    st.B0 = *(const v4i *)(xrow + kt * 128 + 16 * g);
+    st.B1 = *(const v4i *)(xrow + kt * 128 + 64 + 16 * g);
+    st.sb = xsrow[kt * 4 + g];
+  } else {
+    st.B0 = v4i{0, 0, 0, 0};
+    st.B1 = v4i{0, 0, 0, 0};
+    st.sb = 0;
+  }
+}
+
+__device__ __forceinline__ void a8g1_compute(const A8G1Stage &st, v4f *acc) {
+  const v8i bop = v8i{st.B0[0], st.B0[1], st.B0[2], st.B0[3], st.B1[0], st.B1[1], st.B1[2], st.B1[3]};
+#pragma unroll
+  for (int q = 0; q < 4; q++) acc[q] = mfma_fp4_fp8(st.A[q], bop, acc[q], st.sa[q], st.sb);
+}
+
+// grid: x = N/32 (intermediate column blocks), y = tiles; 4 waves split K
+// (wave w takes k-tiles w, w+4, ...), loads double-buffered in registers.
 __global__ __launch_bounds__(256) void k_gemm1_a8(GemmArgs a) {
   const TileInfo ti = tile_info(a);
   if (!ti.valid) return;
@@ -427,8 +452,9 @@ __global__ __launch_bounds__(256) void k_gemm1_a8(GemmArgs a) {
   const int hb = blockIdx.x;
   int t = -1;
   if (c < ti.rows) t = a.perm[ti.p0 + c] / a.topk;
-  const uint8_t *xrow = a.xq + (size_t)(t < 0 ? 0 : t) * K;
-  const uint8_t *xsrow = a.xs + (size_t)(t < 0 ? 0 : t) * (K / 32);
+  const bool have = t >= 0;
+  const uint8_t *xrow = a.xq + (size_t)(have ? t : 0) * K;
+  const uint8_t *xsrow = a.xs + (size_t)(have ? t : 0) * (K / 32);
   const size_t rt_bytes = (size_t)16 * (K / 2);
   const size_t rt_scales = (size_t)16 * (K / 32);
   const uint8_t *wt = a.w13 + (size_t)ti.e * (2 * N) * (K / 2) + (size_t)(4 * hb) * rt_bytes + l * 16;
@@ -436,24 +462,13 @@ __global__ __launch_bounds__(256) void k_gemm1_a8(GemmArgs a) {
   v4f acc[4];
 #pragma unroll
   for (int q = 0; q < 4; q++) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int kt = w; kt < nkt; kt += 4) {
-    v4i A[4];
-    int sa[4];
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      A[q] = *(const v4i *)(wt + q * rt_bytes + (size_t)kt * 1024);
-      sa[q] = st[q * rt_scales + kt * 64];
-    }
-    v4i B0 = v4i{0, 0, 0, 0}, B1 = v4i{0, 0, 0, 0};
-    int sb = 0;
-    if (t >= 0) {
-      B0 = *(const v4i *)(xrow + kt * 128 + 16 * g);
-      B1 = *(const v4i *)(xrow + kt * 128 + 64 + 16 * g);
-      sb = xsrow[kt * 4 + g];
-    }
-    const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
-#pragma unroll
-    for (int q = 0; q < 4; q++) acc[q] = mfma_fp4_fp8(A[q], bop, acc[q], sa[q], sb);
+  A8G1Stage s0, s1;
+  if (w < nkt) a8g1_load(s0, wt, st, rt_bytes, rt_scales, w, xrow, xsrow, have, g);
+  for (int kt = w; kt < nkt; kt += 8) {
+    if (kt + 4 < nkt) a8g1_load(s1, wt, st, rt_bytes, rt_scales, kt + 4, xrow, xsrow, have, g);
+    a8g1_compute(s0, acc);
+    if (kt + 8 < nkt) a8g1_load(s0, wt, st, rt_bytes, rt_scales, kt + 8, xrow, xsrow, have, g);
+    if (kt + 4 < nkt) a8g1_compute(s1, acc);
   }
   __shared__ float red[4][16][64];
 #pragma unroll
@@ -513,6 +528,8 @@ __device__ __forceinline__ void combine_store(const GemmArgs &a, const TileInfo 
 }
 
 // grid: x = K/64 (output column blocks), y = tiles; wave w owns 16 columns.
+// The reduction over N runs in batches of 4 k-tiles whose loads are all issued
+// before the batch's MFMAs.
 __global__ __launch_bounds__(256) void k_gemm2_a8(GemmArgs a) {
   const TileInfo ti = tile_info(a);
   if (!ti.valid) return;
@@ -527,23 +544,29 @@ __global__ __launch_bounds__(256) void k_gemm2_a8(GemmArgs a) {
   const uint8_t *hrow = a.hq + (size_t)(ti.p0 + (have ? c : 0)) * N;
   const uint8_t *hsrow = a.hs + (size_t)(ti.p0 + (have ? c : 0)) * (N / 32);
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int kt = 0; kt < nkt; kt++) {
-    const int kb = kt * 128;
-    v4i A = v4i{0, 0, 0, 0};
-    int sa = 0;
-    if (kb + 32 * g < N) {
-      A = *(const v4i *)(wt + (size_t)kt * 1024);
-      sa = st[kt * 64];
+  for (int kt0 = 0; kt0 < nkt; kt0 += 4) {
+    v4i A[4], B0[4], B1[4];
+    int sa[4], sb[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int kt = kt0 + j, kb = kt * 128;
+      A[j] = B0[j] = B1[j] = v4i{0, 0, 0, 0};
+      sa[j] = sb[j] = 0;
+      if (kt < nkt && kb + 32 * g < N) {
+        A[j] = *(const v4i *)(wt + (size_t)kt * 1024);
+        sa[j] = st[kt * 64];
+      }
+      if (have && kt < nkt) {
+        if (kb + 16 * g < N) B0[j] = *(const v4i *)(hrow + kb + 16 * g);
+        if (kb + 64 + 16 * g < N) B1[j] = *(const v4i *)(hrow + kb + 64 + 16 * g);
+        if (kb + 32 * g < N) sb[j] = hsrow[kb / 32 + g];
+      }
     }
-    v4i B0 = v4i{0, 0, 0, 0}, B1 = v4i{0, 0, 0, 0};
-    int sb = 0;
-    if (have) {
-      if (kb + 16 * g < N) B0 = *(const v4i *)(hrow + kb + 16 * g);
-      if (kb + 64 + 16 * g < N) B1 = *(const v4i *)(hrow + kb + 64 + 16 * g);
-      if (kb + 32 * g < N) sb = hsrow[kb / 32 + g];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const v8i bop = v8i{B0[j][0], B0[j][1], B0[j][2], B0[j][3], B1[j][0], B1[j][1], B1[j][2], B1[j][3]};
+      acc = mfma_fp4_fp8(A[j], bop, acc, sa[j], sb[j]);
     }
-    const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
-    acc = mfma_fp4_fp8(A, bop, acc, sa, sb);
   }
   combine_store(a, ti, c, rt * 16 + 4 * g, acc, 1.0f);
 }
@@ -633,6 +656,38 @@ __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
 }
 
 template <int WF>
+struct A16G1Stage {
+  A16Tile<WF> A[4];
+  v4i B[4];
+};
+
+template <int WF>
+__device__ __forceinline__ void a16g1_load(A16G1Stage<WF> &st, const uint8_t *wt, const uint8_t *sp, size_t rt_bytes,
+                                           size_t rt_scales, int kt, const uint16_t *xrow, bool have, int g) {
+  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+#pragma unroll
+  for (int q = 0; q < 4; q++) st.A[q].load(wt + q * rt_bytes + (size_t)kt * 64 * U, sp + q * rt_scales + kt * 64 * SU);
+  if (have) {
+    const v4i *xp = (const v4i *)(xrow + kt * 128 + 32 * g);
+#pragma unroll
+    for (int s = 0; s < 4; s++) st.B[s] = xp[s];
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; s++) st.B[s] = v4i{0, 0, 0, 0};
+  }
+}
+
+template <int WF>
+__device__ __forceinline__ void a16g1_compute(const A16G1Stage<WF> &st, v4f *acc) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const v8bf b = __builtin_bit_cast(v8bf, st.B[s]);
+#pragma unroll
+    for (int q = 0; q < 4; q++) acc[q] = mfma_bf16(st.A[q].step(s), b, acc[q]);
+  }
+}
+
+template <int WF>
 __global__ __launch_bounds__(256) void k_gemm1_a16(GemmArgs a) {
   const TileInfo ti = tile_info(a);
   if (!ti.valid) return;
@@ -642,7 +697,8 @@ __global__ __launch_bounds__(256) void k_gemm1_a16(GemmArgs a) {
   const int hb = blockIdx.x;
   int t = -1;
   if (c < ti.rows) t = a.perm[ti.p0 + c] / a.topk;
-  const uint16_t *xrow = a.xb + (size_t)(t < 0 ? 0 : t) * K;
+  const bool have = t >= 0;
+  const uint16_t *xrow = a.xb + (size_t)(have ? t : 0) * K;
   const size_t rt_bytes = (size_t)16 * groups * U;
   const size_t rt_scales = (size_t)16 * groups * SU;
   const uint8_t *wt = a.w13 + (size_t)ti.e * (2 * N) * groups * U + (size_t)(4 * hb) * rt_bytes + l * U;
@@ -650,24 +706,13 @@ __global__ __launch_bounds__(256) void k_gemm1_a16(GemmArgs a) {
   v4f acc[4];
 #pragma unroll
   for (int q = 0; q < 4; q++) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int kt = w; kt < nkt; kt += 4) {
-    A16Tile<WF> A[4];
-#pragma unroll
-    for (int q = 0; q < 4; q++) A[q].load(wt + q * rt_bytes + (size_t)kt * 64 * U, st + q * rt_scales + kt * 64 * SU);
-    v4i B[4];
-#pragma unroll
-    for (int s = 0; s < 4; s++) B[s] = v4i{0, 0, 0, 0};
-    if (t >= 0) {
-      const v4i *xp = (const v4i *)(xrow + kt * 128 + 32 * g);
-#pragma unroll
-      for (int s = 0; s < 4; s++) B[s] = xp[s];
-    }
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-      const v8bf b = __builtin_bit_cast(v8bf, B[s]);
-#pragma unroll
-      for (int q = 0; q < 4; q++) acc[q] = mfma_bf16(A[q].step(s), b, acc[q]);
-    }
+  A16G1Stage<WF> s0, s1;
+  if (w < nkt) a16g1_load(s0, wt, st, rt_bytes, rt_scales, w, xrow, have, g);
+  for (int kt = w; kt < nkt; kt += 8) {
+    if (kt + 4 < nkt) a16g1_load(s1, wt, st, rt_bytes, rt_scales, kt + 4, xrow, have, g);
+    a16g1_compute(s0, acc);
+    if (kt + 8 < nkt) a16g1_load(s0, wt, st, rt_bytes, rt_scales, kt + 8, xrow, have, g);
+    if (kt + 4 < nkt) a16g1_compute(s1, acc);
   }
   __shared__ float red[4][16][64];
 #pragma unroll
@@ -712,22 +757,27 @@ __global__ __launch_bounds__(256) void k_gemm2_a16(GemmArgs a) {
   const bool have = c < ti.rows;
   const uint16_t *hrow = a.hb + (size_t)(ti.p0 + (have ? c : 0)) * N;
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int kt = 0; kt < nkt; kt++) {
-    const int kb = kt * 128;
-    const bool inb = kb + 32 * g < N;
-    A16Tile<WF> A;
-    if (inb) A.load(wt + (size_t)kt * 64 * U, st + kt * 64 * SU);
-    else A.zero();
-    v4i B[4];
+  for (int kt0 = 0; kt0 < nkt; kt0 += 2) {
+    A16Tile<WF> A[2];
+    v4i B[2][4];
 #pragma unroll
-    for (int s = 0; s < 4; s++) B[s] = v4i{0, 0, 0, 0};
-    if (have && inb) {
-      const v4i *hp = (const v4i *)(hrow + kb + 32 * g);
+    for (int j = 0; j < 2; j++) {
+      const int kt = kt0 + j, kb = kt * 128;
+      const bool inb = kt < nkt && kb + 32 * g < N;
+      if (inb) A[j].load(wt + (size_t)kt * 64 * U, st + kt * 64 * SU);
+      else A[j].zero();
 #pragma unroll
-      for (int s = 0; s < 4; s++) B[s] = hp[s];
+      for (int s = 0; s < 4; s++) B[j][s] = v4i{0, 0, 0, 0};
+      if (have && inb) {
+        const v4i *hp = (const v4i *)(hrow + kb + 32 * g);
+#pragma unroll
+        for (int s = 0; s < 4; s++) B[j][s] = hp[s];
+      }
     }
 #pragma unroll
-    for (int s = 0; s < 4; s++) acc = mfma_bf16(A.step(s), __builtin_bit_cast(v8bf, B[s]), acc);
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int s = 0; s < 4; s++) acc = mfma_bf16(A[j].step(s), __builtin_bit_cast(v8bf, B[j][s]), acc);
   }
   combine_store(a, ti, c, rt * 16 + 4 * g, acc, a.g2 ? a.g2[ti.e] : 1.0f);
 }

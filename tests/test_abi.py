@@ -1,0 +1,104 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/moe.h
+declares, and its host-side validation returns the documented codes. No call
+here launches GPU work."""
+import ctypes as C
+import math
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_histogram_amd as M
+from block_scaled_fp4_histogram_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    L = _lib.load()
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_plan_validation_codes():
+    ok = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
+    assert ok.scratch_bytes(8) > 0
+    bad = [((384, 7000, 576, 6), M.MOE_EUNSUPPORTED),   # K % 256
+           ((384, 7168, 570, 6), M.MOE_EUNSUPPORTED),   # N % 32
+           ((0, 7168, 576, 6), M.MOE_EUNSUPPORTED),
+           ((2000, 7168, 576, 6), M.MOE_EUNSUPPORTED),
+           ((384, 7168, 576, 0), M.MOE_EINVAL),
+           ((384, 7168, 576, 17), M.MOE_EINVAL)]
+    for args, code in bad:
+        with pytest.raises(M.MoeError) as ei:
+            M.Plan(*args)
+        assert ei.value.code == code, args
+        assert str(ei.value)  # carries the library's message
+    with pytest.raises(M.MoeError) as ei:
+        M.Plan(8, 256, 128, 2, None, act_format=7)
+    assert ei.value.code == M.MOE_EUNSUPPORTED
+    with pytest.raises(M.MoeError) as ei:
+        M.Plan(8, 256, 128, 2, None, w13_layout=5)
+    assert ei.value.code == M.MOE_EINVAL
+
+
+def test_capacity_ladder_and_scratch_sizes():
+    p = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
+    assert p.capacity(1)[0] == 1
+    assert p.capacity(6)[0] == 6
+    assert p.capacity(9)[0] == 10
+    assert p.capacity(100)[0] == 128
+    assert p.capacity(4096)[0] == 4096
+    assert p.capacity(10000)[0] == 4096          # chunks of the top rung
+    sizes = [p.scratch_bytes(t) for t in (1, 8, 64, 512, 4096)]
+    assert sizes == sorted(sizes)
+    assert p.scratch_bytes(10000) == p.scratch_bytes(4096)
+    assert p.scratch_bytes(4096, True) > p.scratch_bytes(4096, False)   # route buffer vs accumulator
+    assert p.scratch_bytes(8) % 256 == 0
+    L = _lib.load()
+    assert L.moe_scratch_bytes(None, 8, 0) == 0
+
+
+def test_null_and_bad_handles_are_refused_on_the_host():
+    L = _lib.load()
+    p = M.Plan(8, 256, 128, 2, 7.0, M.A_MXFP8, max_tokens=16)
+    h = C.c_void_p()
+    # weight format that does not fit the plan's activation format
+    rc = L.moe_prepare_weights(p.handle, M.W_NVFP4, 8, 16, 16, None, 16, 16, None, None, C.byref(h))
+    assert rc == M.MOE_EUNSUPPORTED
+    rc = L.moe_prepare_weights(p.handle, 9, 8, 16, 16, None, 16, 16, None, None, C.byref(h))
+    assert rc == M.MOE_EUNSUPPORTED
+    rc = L.moe_prepare_weights(p.handle, M.W_MXFP4, 8, None, 16, None, 16, 16, None, None, C.byref(h))
+    assert rc == M.MOE_EINVAL
+    rc = L.moe_prepare_weights(p.handle, M.W_MXFP4, 8, 17, 16, None, 16, 16, None, None, C.byref(h))
+    assert rc == M.MOE_EINVAL                                       # misaligned
+    rc = L.moe_prepare_weights(None, M.W_MXFP4, 8, 16, 16, None, 16, 16, None, None, C.byref(h))
+    assert rc == M.MOE_EINVAL
+    # moe_run with no tiers / a null experts handle
+    tiers = (_lib.MoeTier * 1)()
+    rc = L.moe_run(p.handle, tiers, 1, 256, 256, 256, 256, 4, 0, 256, 1 << 20, None)
+    assert rc == M.MOE_EINVAL
+    rc = L.moe_run(p.handle, tiers, 0, 256, 256, 256, 256, 4, 0, 256, 1 << 20, None)
+    assert rc == M.MOE_EINVAL
+    rc = L.moe_run(None, tiers, 1, 256, 256, 256, 256, 4, 0, 256, 1 << 20, None)
+    assert rc == M.MOE_EINVAL
+    assert L.moe_last_error().decode() != ""
+    # stage timing on a bad plan; debug quantiser shape checks
+    assert L.moe_plan_enable_stage_timing(None, 4) == M.MOE_EINVAL
+    assert L.moe_debug_quant_mxfp8_f32(16, 4, 33, 16, 16, None) == M.MOE_EINVAL
+    assert L.moe_debug_quant_mxfp8_f32(16, 0, 32, 16, 16, None) == M.MOE_OK   # empty is a no-op
+
+
+def test_destroy_is_safe_on_null():
+    L = _lib.load()
+    L.moe_plan_destroy(None)
+    L.moe_experts_destroy(None)
