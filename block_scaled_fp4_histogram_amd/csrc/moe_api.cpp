@@ -147,6 +147,59 @@ int check_tiers(const moe_plan_s *p, const moe_tier *tiers, int n_tiers) {
   return MOE_OK;
 }
 
+// Decode-size batch: the two-launch path (routing inside each workgroup).
+int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uint16_t *x, const int32_t *ids,
+               const float *wts, uint16_t *out, int T, const Layout &L, uint8_t *scratch, hipStream_t s,
+               const hipEvent_t *ev) {
+  moe::DecArgs da;
+  memset(&da, 0, sizeof da);
+  da.ids = ids;
+  da.topk_w = wts;
+  da.x = x;
+  da.T = T;
+  da.R = T * p->topk;
+  da.topk = p->topk;
+  da.E = p->E;
+  da.K = p->K;
+  da.N = p->N;
+  da.n_tiers = n_tiers;
+  for (int i = 0; i < n_tiers; i++) {
+    const moe_experts_s *xp = tiers[i].experts;
+    da.tier[i].w13 = xp->w13;
+    da.tier[i].s13 = xp->s13;
+    da.tier[i].w2 = xp->w2;
+    da.tier[i].s2 = xp->s2;
+    da.tier[i].g13 = xp->g13;
+    da.tier[i].g2 = xp->g2;
+    da.tier[i].emap = tiers[i].expert_map;
+    da.tier[i].fmt = xp->wfmt;
+    da.tier[i].E = xp->E;
+  }
+  da.limit = p->limit;
+  da.has_limit = p->has_limit;
+  da.cpass = moe::decode_cpass(p->K);
+  da.hq = scratch + L.hq;
+  da.hs = scratch + L.hs;
+  da.hb = (uint16_t *)(scratch + L.hb);
+  da.out = out;
+  if (ev) {
+    HIP_TRY(hipEventRecord(ev[0], s));
+    HIP_TRY(hipEventRecord(ev[1], s));
+  }
+  HIP_TRY(moe::launch_decode(p->afmt == MOE_A_MXFP8, da, s, ev ? ev[2] : nullptr));
+  if (ev) {
+    HIP_TRY(hipEventRecord(ev[3], s));
+    HIP_TRY(hipEventRecord(ev[4], s));
+  }
+  return MOE_OK;
+}
+
+bool use_decode(const moe_plan_s *p, int T) {
+  // the W4A8 decode GEMM1 stages at least one MXFP8 token row in 60 KB of LDS
+  const bool lds_ok = p->afmt != MOE_A_MXFP8 || (long)p->K + 16 + p->K / 32 <= 61440;
+  return T <= moe::kDecodeMaxT && T * p->topk <= moe::kDecodeMaxRoutes && lds_ok;
+}
+
 // Everything one chunk needs after validation.
 int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uint16_t *x, const int32_t *ids,
               const float *wts, uint16_t *out, int T, int deterministic, const Layout &L, uint8_t *scratch,
@@ -479,9 +532,14 @@ int moe_run(moe_plan_t p, const moe_tier *tiers, int n_tiers, const void *x, con
   }
   for (int t0 = 0; t0 < T; t0 += cap) {
     const int tc = std::min(cap, T - t0);
-    rc = run_chunk(p, tiers, n_tiers, (const uint16_t *)x + (size_t)t0 * p->K, ids + (size_t)t0 * p->topk,
-                   wts + (size_t)t0 * p->topk, (uint16_t *)out + (size_t)t0 * p->K, tc, deterministic, L,
-                   (uint8_t *)scratch, s, false, ev);
+    const uint16_t *xc = (const uint16_t *)x + (size_t)t0 * p->K;
+    const int32_t *idc = ids + (size_t)t0 * p->topk;
+    const float *wc = wts + (size_t)t0 * p->topk;
+    uint16_t *oc = (uint16_t *)out + (size_t)t0 * p->K;
+    if (use_decode(p, tc))
+      rc = run_decode(p, tiers, n_tiers, xc, idc, wc, oc, tc, L, (uint8_t *)scratch, s, ev);
+    else
+      rc = run_chunk(p, tiers, n_tiers, xc, idc, wc, oc, tc, deterministic, L, (uint8_t *)scratch, s, false, ev);
     if (rc != MOE_OK) return rc;
   }
   return MOE_OK;

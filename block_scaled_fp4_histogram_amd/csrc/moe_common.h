@@ -55,6 +55,36 @@ struct GemmArgs {
   int deterministic;
 };
 
+// Decode-size batches (T <= kDecodeMaxT tokens, T * top_k <= 64 routes): two
+// launches, routing recomputed in each workgroup from the ids.
+constexpr int kDecodeMaxT = 16;
+constexpr int kDecodeMaxRoutes = 64;
+
+struct DecTier {
+  const uint8_t *w13, *s13, *w2, *s2;
+  const float *g13, *g2;
+  const int32_t *emap;
+  int fmt, E;
+};
+
+struct DecArgs {
+  const int32_t *ids;
+  const float *topk_w;
+  const uint16_t *x;                 // bf16 [T, K]
+  int T, R, topk, E, K, N, n_tiers;
+  DecTier tier[kMaxTiers];
+  float limit;
+  int has_limit;
+  int cpass;                         // token rows per LDS staging pass (MXFP8 x)
+  uint8_t *hq, *hs;                  // MXFP8 intermediate per route r: [R, N], [R, N/32]
+  uint16_t *hb;                      // bf16 intermediate per route r: [R, N]
+  uint16_t *out;                     // bf16 [T, K]
+};
+
+int decode_cpass(int K);
+size_t decode_gemm1_lds(int K, int cpass);
+hipError_t launch_decode(int a8, const DecArgs &a, hipStream_t s, hipEvent_t ev_mid);
+
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_gemm1(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s);
 hipError_t launch_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s);

@@ -43,6 +43,14 @@ SMALL = {
                                                     fmt=I.FMT_NVFP4, hybrid_nvfp4=8), seed=6),
     "nvfp4_clamped": lambda: I.make_problem(I.Config("nvfp4_clamped", T=9, E=6, K=256, N=64, topk=2, limit=30.0,
                                                      fmt=I.FMT_NVFP4), seed=7),
+    # decode-size batches (T <= 16, T * top_k <= 64): the two-launch path
+    "hybrid_decode": lambda: I.make_problem(I.Config("hybrid_decode", T=8, E=256, K=1024, N=512, topk=8, limit=None,
+                                                     fmt=I.FMT_NVFP4, hybrid_nvfp4=64), seed=8),
+    # ~16 routes per expert at K=7168: the MXFP8 rows are staged through LDS in two passes
+    "decode_many_routes": lambda: I.make_problem(I.Config("decode_many_routes", T=16, E=4, K=7168, N=64, topk=4,
+                                                          limit=7.0, fmt=I.FMT_MXFP4, e8m0_exp=(-9, -5)), seed=9),
+    "nf3_decode": lambda: I.make_problem(I.Config("nf3_decode", T=5, E=40, K=512, N=96, topk=7, limit=None,
+                                                  fmt=I.FMT_NF3), seed=10),
 }
 
 
@@ -62,7 +70,7 @@ def _sample_rows(prob, n, seed=0):
 
 
 @pytest.mark.parametrize("name", ["tiny", "mxfp4_ragged", "nvfp4_small", "nf3_small", "hybrid_small",
-                                  "nvfp4_clamped"])
+                                  "nvfp4_clamped", "hybrid_decode", "decode_many_routes", "nf3_decode"])
 @pytest.mark.parametrize("deterministic", [False, True])
 def test_small_layers_all_rows(name, deterministic):
     L = layer(name)
@@ -91,7 +99,7 @@ def test_full_size_sampled_rows(name, nrows, deterministic):
     assert_rows_match(out, acc, rows=rows, label=f"{name} det={deterministic}")
 
 
-@pytest.mark.parametrize("name", ["decode", "hybrid_small", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "hybrid_small", "prefill", "hybrid_decode"])
 def test_deterministic_bit_stable(name):
     L = layer(name)
     outs = [L.run(deterministic=True).view(torch.int16).clone() for _ in range(3)]
@@ -99,41 +107,51 @@ def test_deterministic_bit_stable(name):
 
 
 def test_chunked_batch_matches_single_launch():
-    """T above the plan's max_tokens runs in chunks of the top capacity."""
-    prob = SMALL["mxfp4_ragged"]()
+    """T above the plan's max_tokens runs in chunks of the top capacity; chunks of the
+    same kernel path give the bit-identical deterministic result of one launch."""
+    prob = SMALL["mxfp4_ragged"]()   # T = 37
     big = DeviceLayer(prob)
     ref = big.run(deterministic=True)
-    small = DeviceLayer(SMALL["mxfp4_ragged"](), max_tokens=8)
-    out = small.run(deterministic=True)
+    chunked = DeviceLayer(SMALL["mxfp4_ragged"](), max_tokens=20)   # chunks of 20 + 17 tokens
+    out = chunked.run(deterministic=True)
     assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
     acc, _ = O.moe_problem(prob)
-    assert_rows_match(small.run(deterministic=False), acc, label="chunked atomic")
+    assert_rows_match(chunked.run(deterministic=False), acc, label="chunked atomic")
+    # chunks small enough for the decode path (8 tokens x 3 slots)
+    dec = DeviceLayer(SMALL["mxfp4_ragged"](), max_tokens=8)
+    for det in (False, True):
+        assert_rows_match(dec.run(deterministic=det), acc, label=f"decode-size chunks det={det}")
 
 
-def test_invalid_ids_and_zero_weights():
-    L = layer("mxfp4_ragged")
+@pytest.mark.parametrize("name", ["mxfp4_ragged", "decode"])
+def test_invalid_ids_and_zero_weights(name):
+    L = layer(name)
     p = L.prob
     E = p.cfg.E
     ids = p.ids.copy()
     wts = p.wts.copy()
     ids[:, 1] = np.array([-1, E, E + 7, np.iinfo(np.int32).min, np.iinfo(np.int32).max] * 8)[: p.cfg.T]
     ids[3, :] = -1                 # a row with no valid slot
+    ids[5 % p.cfg.T, 2] = ids[5 % p.cfg.T, 0]   # a duplicate
     wts[4, 0] = 0.0                # a zero-weight slot
     for det in (False, True):
         out = L.run(ids=dev(ids), wts=dev(wts), deterministic=det)
         q = I.Problem(p.cfg, p.x, ids, wts, p.tiers)
         acc, _ = O.moe_problem(q)
-        assert_rows_match(out, acc, label=f"invalid ids det={det}")
+        assert_rows_match(out, acc, label=f"{name} invalid ids det={det}")
         assert torch.all(out[3].view(torch.int16) == 0)
 
 
-def test_duplicate_ids_in_a_row():
-    L = layer("nvfp4_small")
+@pytest.mark.parametrize("name", ["nvfp4_small", "decode", "hybrid_decode"])
+def test_duplicate_ids_in_a_row(name):
+    L = layer(name)
     p = L.prob
     ids = np.repeat(p.ids[:, :1], p.cfg.topk, axis=1).copy()
-    out = L.run(ids=dev(ids), deterministic=True)
-    acc, _ = O.moe_problem(I.Problem(p.cfg, p.x, ids, p.wts, p.tiers))
-    assert_rows_match(out, acc, label="duplicate ids")
+    ids[:, -1] = p.ids[:, -1]
+    for det in (False, True):
+        out = L.run(ids=dev(ids), deterministic=det)
+        acc, _ = O.moe_problem(I.Problem(p.cfg, p.x, ids, p.wts, p.tiers))
+        assert_rows_match(out, acc, label=f"{name} duplicate ids det={det}")
 
 
 def test_zero_tokens_is_noop_and_all_padding_batch():
@@ -144,10 +162,13 @@ def test_zero_tokens_is_noop_and_all_padding_batch():
     wts = torch.zeros((0, c.topk), dtype=torch.float32, device="cuda")
     out = M.run(L.plan, L.tiers, x, ids, wts, scratch=torch.empty(256, dtype=torch.uint8, device="cuda"))
     assert out.shape == (0, c.K)
-    ids = torch.full((c.T, c.topk), -1, dtype=torch.int32, device="cuda")
-    for det in (False, True):
-        out = L.run(ids=ids, deterministic=det)
-        assert torch.all(out.view(torch.int16) == 0)
+    for name in ("tiny", "mxfp4_ragged"):   # decode-size and general paths
+        L = layer(name)
+        c = L.prob.cfg
+        ids = torch.full((c.T, c.topk), -1, dtype=torch.int32, device="cuda")
+        for det in (False, True):
+            out = L.run(ids=ids, deterministic=det)
+            assert torch.all(out.view(torch.int16) == 0)
 
 
 def test_scratch_too_small_is_refused():
