@@ -9,7 +9,8 @@ import ctypes as C
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_gfx950.so")
+# MOE_LIB_PATH points at another build of the same library (e.g. a variant being measured)
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe_gfx950.so")
 
 # Every function include/moe.h declares, with (restype, argtypes).
 _vp, _i, _f, _sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t

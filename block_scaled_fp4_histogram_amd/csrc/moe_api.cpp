@@ -177,7 +177,7 @@ int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const ui
   }
   da.limit = p->limit;
   da.has_limit = p->has_limit;
-  da.cpass = moe::decode_cpass(p->K);
+  da.cpass = moe::decode_cpass(p->K, p->afmt == MOE_A_MXFP8);
   da.hq = scratch + L.hq;
   da.hs = scratch + L.hs;
   da.hb = (uint16_t *)(scratch + L.hb);
@@ -195,8 +195,12 @@ int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const ui
 }
 
 bool use_decode(const moe_plan_s *p, int T) {
-  // the W4A8 decode GEMM1 stages at least one MXFP8 token row in 60 KB of LDS
-  const bool lds_ok = p->afmt != MOE_A_MXFP8 || (long)p->K + 16 + p->K / 32 <= 61440;
+  // the decode GEMM1 stages at least one token row in its 32 KB of LDS, and the
+  // W4A8 GEMM2 all routes' MXFP8 rows of the intermediate
+  const bool a8 = p->afmt == MOE_A_MXFP8;
+  const long row = a8 ? (long)p->K + 16 + p->K / 32 : 2L * (p->K + 8);
+  const long lds2 = a8 ? (long)T * p->topk * (p->N + 16 + p->N / 32) : 0;
+  const bool lds_ok = row <= 32768 && lds2 <= 49152;
   return T <= moe::kDecodeMaxT && T * p->topk <= moe::kDecodeMaxRoutes && lds_ok;
 }
 

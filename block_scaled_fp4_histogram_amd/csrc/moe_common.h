@@ -81,8 +81,8 @@ struct DecArgs {
   uint16_t *out;                     // bf16 [T, K]
 };
 
-int decode_cpass(int K);
-size_t decode_gemm1_lds(int K, int cpass);
+int decode_cpass(int K, int a8);
+size_t decode_gemm1_lds(int K, int cpass, int a8);
 hipError_t launch_decode(int a8, const DecArgs &a, hipStream_t s, hipEvent_t ev_mid);
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);

@@ -16,6 +16,8 @@
 //                columns and folds the router-weighted results into per-token
 //                fp32 accumulators; the 8 waves are summed in a fixed order and
 //                the bf16 output written.  No atomics: bit-stable run to run.
+#include <type_traits>
+
 #include "moe_device.h"
 
 namespace moe {
@@ -34,6 +36,11 @@ __device__ __forceinline__ int dec_route_u(const DecArgs &a, int lane) {
   return -1;
 }
 
+__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 // Group d, in order of first occurrence, of the routes sharing one expert:
 // its expert and the mask of its routes (bit r = route r).  Wave-uniform.
 __device__ __forceinline__ bool dec_group(int u, int d, int *gu, unsigned long long *gm) {
@@ -43,8 +50,9 @@ __device__ __forceinline__ bool dec_group(int u, int d, int *gu, unsigned long l
     const int lu = __shfl(u, leader);
     const unsigned long long m = __ballot(u == lu);
     if (i == d) {
-      *gu = lu;
-      *gm = m;
+      // wave-uniform values: keep them (and every pointer derived from them) scalar
+      *gu = __builtin_amdgcn_readfirstlane(lu);
+      *gm = uniform_u64(m);
       return true;
     }
     rem &= ~m;
@@ -79,9 +87,10 @@ __device__ __forceinline__ DecExpert dec_expert(const DecArgs &a, int u) {
   return x;
 }
 
-// Fixed-order sum over the 8 waves of the 16 GEMM1 accumulators, clamped
+// Fixed-order sum over the NW waves of the 16 GEMM1 accumulators, clamped
 // SwiGLU; returns the 8 intermediate values of lane (route column c, group g):
 // columns 32*hb + 16*s + 4*g + i for s, i.
+template <int NW>
 __device__ __forceinline__ void dec_swiglu(const float *red, int l, float gs, float limit, int has_limit, float *h) {
 #pragma unroll
   for (int s = 0; s < 2; s++)
@@ -89,8 +98,8 @@ __device__ __forceinline__ void dec_swiglu(const float *red, int l, float gs, fl
     for (int i = 0; i < 4; i++) {
       const int iu = (2 * s) * 4 + i, ig = (2 * s + 1) * 4 + i;
       float up = 0.f, gate = 0.f;
-#pragma unroll
-      for (int w = 0; w < 8; w++) {
+#pragma unroll 2
+      for (int w = 0; w < NW; w++) {
         up += red[(w * 16 + iu) * 64 + l];
         gate += red[(w * 16 + ig) * 64 + l];
       }
@@ -98,76 +107,163 @@ __device__ __forceinline__ void dec_swiglu(const float *red, int l, float gs, fl
     }
 }
 
-// ---------------------------------------------------------------- GEMM1, W4A8
-__global__ __launch_bounds__(512) void k_dec_gemm1_a8(DecArgs a) {
-  extern __shared__ __align__(16) uint8_t dsm[];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
-  int ud;
-  unsigned long long md;
-  if (!dec_group(dec_route_u(a, l), blockIdx.y, &ud, &md)) return;
-  const DecExpert X = dec_expert(a, ud);
-  const int K = a.K, N = a.N, nkt = K / 128, hb = blockIdx.x, kb32 = K / 32;
-  const size_t rt_bytes = (size_t)16 * (K / 2), rt_scales = (size_t)16 * kb32;
-  const uint8_t *wt = X.w13 + (size_t)X.e * (2 * N) * (K / 2) + (size_t)(4 * hb) * rt_bytes + l * 16;
-  const uint8_t *st = X.s13 + (size_t)X.e * (2 * N) * kb32 + (size_t)(4 * hb) * rt_scales + l;
-  const int xstride = K + 16;   // LDS row stride: rows land on different banks
-  uint8_t *xq = dsm;
-  uint8_t *xsc = dsm + (size_t)a.cpass * xstride;
-  float *red = (float *)dsm;    // reused after the k-loop: [8 waves][16][64]
-  const int ncols = __popcll(md);
-  for (int p0 = 0; p0 < ncols; p0 += a.cpass) {
-    const int ncol = min(a.cpass, ncols - p0);
-    // first weight stage in flight while the token rows are quantised
-    A8G1Stage s0, s1;
-    const bool have = c < ncol;
-    if (w < nkt) {
+// ---------------------------------------------------------------- GEMM1
+//
+// One k-tile of weights for one lane: the up and gate row tiles of two
+// adjacent 16-column intermediate blocks.  Activations are read from LDS at
+// MFMA time, so only weights travel through registers and two k-tiles of them
+// are kept in flight per wave.
+struct A8W {
+  v4i A[4];
+  int sa[4];
+};
+
+// The expert's w13 data and scales as buffer resources; row tile q of the
+// block starts at wave-uniform offsets w0 + q * wstep, s0 + q * sstep.
+struct RowTiles {
+  Buf wb, sb;
+  uint32_t w0, wstep, s0, sstep;
+};
+
+__device__ __forceinline__ void a8w_load(A8W &st, const RowTiles &rt, uint32_t l, int kt) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        s0.A[q] = *(const v4i *)(wt + q * rt_bytes + (size_t)w * 1024);
-        s0.sa[q] = st[q * rt_scales + w * 64];
-      }
-    }
-    for (int i = tid; i < ncol * kb32; i += 512) {
+  for (int q = 0; q < 4; q++) {
+    st.A[q] = buf_load16(rt.wb, (uint32_t)kt * 1024u + l * 16u, rt.w0 + q * rt.wstep);
+    st.sa[q] = buf_load1(rt.sb, (uint32_t)kt * 64u + l, rt.s0 + q * rt.sstep);
+  }
+}
+
+// MXFP8 activations of route column c (LDS row xrow, scales xsrow) for k-tile kt.
+__device__ __forceinline__ void a8w_mfma(const A8W &st, const uint8_t *xrow, const uint8_t *xsrow, bool have, int g,
+                                         int kt, v4f *acc) {
+  v4i B0 = v4i{0, 0, 0, 0}, B1 = v4i{0, 0, 0, 0};
+  int sb = 0;
+  if (have) {
+    B0 = *(const v4i *)(xrow + kt * 128 + 16 * g);
+    B1 = *(const v4i *)(xrow + kt * 128 + 64 + 16 * g);
+    sb = xsrow[kt * 4 + g];
+  }
+  const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
+#pragma unroll
+  for (int q = 0; q < 4; q++) acc[q] = mfma_fp4_fp8(st.A[q], bop, acc[q], st.sa[q], sb);
+}
+
+template <int WF>
+struct A16W {
+  A16Tile<WF> A[4];
+};
+
+template <int WF>
+__device__ __forceinline__ void a16w_load(A16W<WF> &st, const RowTiles &rt, uint32_t l, int kt) {
+  constexpr uint32_t U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+    st.A[q].load(rt.wb, (uint32_t)kt * 64u * U + l * U, rt.w0 + q * rt.wstep, rt.sb, (uint32_t)kt * 64u * SU + l * SU,
+                 rt.s0 + q * rt.sstep);
+}
+
+// bf16 activations of route column c (LDS row xrow) for k-tile kt.
+template <int WF>
+__device__ __forceinline__ void a16w_mfma(const A16W<WF> &st, const uint16_t *xrow, bool have, int g, int kt,
+                                          v4f *acc) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    v4i b = v4i{0, 0, 0, 0};
+    if (have) b = *(const v4i *)(xrow + kt * 128 + 32 * g + 8 * s);
+    const v8bf bb = __builtin_bit_cast(v8bf, b);
+#pragma unroll
+    for (int q = 0; q < 4; q++) acc[q] = mfma_bf16(st.A[q].step(s), bb, acc[q]);
+  }
+}
+
+// Stage the activation rows of the pass's route columns into LDS: MXFP8 codes
+// and scales (W4A8), or the bf16 rows as they are (W4A16).
+template <bool A8, int NW>
+__device__ __forceinline__ void dec_stage_x(const DecArgs &a, unsigned long long md, int p0, int ncol, uint8_t *dsm) {
+  const int K = a.K, kb32 = K / 32, tid = threadIdx.x;
+  if (A8) {
+    const int xstride = K + 16;
+    uint8_t *xq = dsm, *xsc = dsm + (size_t)a.cpass * xstride;
+#pragma unroll 1
+    for (int i = tid; i < ncol * kb32; i += NW * 64) {
       const int col = i / kb32, blk = i - col * kb32;
       const int t = nth_bit(md, p0 + col) / a.topk;
       const v4i *src = (const v4i *)(a.x + (size_t)t * K + blk * 32);
-      float v[32];
+      v4i x4[4];
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const v4i x4 = src[q];
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-          v[8 * q + 2 * d] = bf16_to_f32((uint32_t)x4[d] & 0xFFFFu);
-          v[8 * q + 2 * d + 1] = bf16_to_f32((uint32_t)x4[d] >> 16);
-        }
-      }
+      for (int q = 0; q < 4; q++) x4[q] = src[q];
       uint32_t codes[8];
-      xsc[col * kb32 + blk] = (uint8_t)quant_block32(v, codes);
+      xsc[col * kb32 + blk] = (uint8_t)quant_block32_bf16(x4, codes);
       v4i *dst = (v4i *)(xq + col * xstride + blk * 32);
       dst[0] = v4i{(int)codes[0], (int)codes[1], (int)codes[2], (int)codes[3]};
       dst[1] = v4i{(int)codes[4], (int)codes[5], (int)codes[6], (int)codes[7]};
     }
-    __syncthreads();
-    const uint8_t *xrow = xq + (have ? c : 0) * xstride;
-    const uint8_t *xsrow = xsc + (have ? c : 0) * kb32;
-    if (w < nkt) {
-      if (have) {
-        s0.B0 = *(const v4i *)(xrow + w * 128 + 16 * g);
-        s0.B1 = *(const v4i *)(xrow + w * 128 + 64 + 16 * g);
-        s0.sb = xsrow[w * 4 + g];
-      } else {
-        s0.B0 = s0.B1 = v4i{0, 0, 0, 0};
-        s0.sb = 0;
-      }
+  } else {
+    const int xstride = K + 8;   // bf16 elements
+    uint16_t *xb = (uint16_t *)dsm;
+    for (int i = tid; i < ncol * (K / 8); i += NW * 64) {
+      const int col = i / (K / 8), c8 = i - col * (K / 8);
+      const int t = nth_bit(md, p0 + col) / a.topk;
+      *(v4i *)(xb + col * xstride + c8 * 8) = *(const v4i *)(a.x + (size_t)t * K + c8 * 8);
     }
+  }
+}
+
+template <bool A8, int WF, int NW>
+__device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert &X, unsigned long long md,
+                                               uint8_t *dsm) {
+  constexpr int U = A8 ? 16 : FmtGeom<WF>::unit, SU = A8 ? 1 : FmtGeom<WF>::sunit;
+  typedef typename std::conditional<A8, A8W, A16W<WF>>::type Stage;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int K = a.K, N = a.N, nkt = K / 128, groups = K / 32, hb = blockIdx.x;
+  const size_t rt_bytes = (size_t)16 * groups * U, rt_scales = (size_t)16 * groups * SU;
+  RowTiles rt;
+  rt.wb = make_buf(X.w13 + (size_t)X.e * (2 * N) * groups * U, (uint32_t)((size_t)(2 * N) * groups * U));
+  rt.sb = make_buf(X.s13 + (size_t)X.e * (2 * N) * groups * SU, (uint32_t)((size_t)(2 * N) * groups * SU));
+  rt.w0 = (uint32_t)((size_t)(4 * hb) * rt_bytes);
+  rt.wstep = (uint32_t)rt_bytes;
+  rt.s0 = (uint32_t)((size_t)(4 * hb) * rt_scales);
+  rt.sstep = (uint32_t)rt_scales;
+  const uint32_t lu = (uint32_t)l;
+  float *red = (float *)dsm;   // after the k-loop: [NW waves][16][64]
+  const int ncols = __popcll(md);
+  for (int p0 = 0; p0 < ncols; p0 += a.cpass) {
+    const int ncol = min(a.cpass, ncols - p0);
+    const bool have = c < ncol;
+    // three k-tiles of weights in flight per wave: tiles w, w + NW, w + 2 NW, ...
+    Stage s0, s1, s2;
+    auto load = [&](Stage &st, int kt) {
+      if constexpr (A8) a8w_load(st, rt, lu, kt);
+      else a16w_load<WF>(st, rt, lu, kt);
+    };
+    if (w < nkt) load(s0, w);
+    if (w + NW < nkt) load(s1, w + NW);
+    dec_stage_x<A8, NW>(a, md, p0, ncol, dsm);
+    __syncthreads();
     v4f acc[4];
 #pragma unroll
     for (int q = 0; q < 4; q++) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int kt = w; kt < nkt; kt += 16) {
-      if (kt + 8 < nkt) a8g1_load(s1, wt, st, rt_bytes, rt_scales, kt + 8, xrow, xsrow, have, g);
-      a8g1_compute(s0, acc);
-      if (kt + 16 < nkt) a8g1_load(s0, wt, st, rt_bytes, rt_scales, kt + 16, xrow, xsrow, have, g);
-      if (kt + 8 < nkt) a8g1_compute(s1, acc);
+    const int cc = have ? c : 0;
+    auto mfma = [&](const Stage &st, int kt) {
+      if constexpr (A8) {
+        const uint8_t *xrow = dsm + cc * (K + 16);
+        const uint8_t *xsrow = dsm + (size_t)a.cpass * (K + 16) + cc * (K / 32);
+        a8w_mfma(st, xrow, xsrow, have, g, kt, acc);
+      } else {
+        a16w_mfma<WF>(st, (const uint16_t *)dsm + cc * (K + 8), have, g, kt, acc);
+      }
+    };
+    for (int kt = w; kt < nkt; kt += 3 * NW) {
+      if (kt + 2 * NW < nkt) load(s2, kt + 2 * NW);
+      mfma(s0, kt);
+      if (kt + NW < nkt) {
+        if (kt + 3 * NW < nkt) load(s0, kt + 3 * NW);
+        mfma(s1, kt + NW);
+      }
+      if (kt + 2 * NW < nkt) {
+        if (kt + 4 * NW < nkt) load(s1, kt + 4 * NW);
+        mfma(s2, kt + 2 * NW);
+      }
     }
     __syncthreads();   // the staged rows are dead; LDS becomes the reduction buffer
 #pragma unroll
@@ -177,81 +273,57 @@ __global__ __launch_bounds__(512) void k_dec_gemm1_a8(DecArgs a) {
     __syncthreads();
     if (w == 0) {
       float h[8];
-      dec_swiglu(red, l, 1.0f, a.limit, a.has_limit, h);
-      float amax = 0.f;
+      dec_swiglu<NW>(red, l, X.g13, a.limit, a.has_limit, h);
+      if (A8) {
+        float amax = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(h[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      float inv;
-      const uint32_t sbyte = mx_scale(amax, &inv);
-      if (have) {
+        for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(h[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        float inv;
+        const uint32_t sbyte = mx_scale(amax, &inv);
+        if (have) {
+          const size_t r = (size_t)nth_bit(md, p0 + c);
+#pragma unroll
+          for (int s = 0; s < 2; s++)
+            *(uint32_t *)(a.hq + r * N + hb * 32 + 16 * s + 4 * g) =
+                e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
+          if (g == 0) a.hs[r * (N / 32) + hb] = (uint8_t)sbyte;
+        }
+      } else if (have) {
         const size_t r = (size_t)nth_bit(md, p0 + c);
 #pragma unroll
-        for (int s = 0; s < 2; s++)
-          *(uint32_t *)(a.hq + r * N + hb * 32 + 16 * s + 4 * g) =
-              e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
-        if (g == 0) a.hs[r * (N / 32) + hb] = (uint8_t)sbyte;
+        for (int s = 0; s < 2; s++) {
+          uint2 v;
+          v.x = pack_bf16x2(h[s * 4], h[s * 4 + 1]);
+          v.y = pack_bf16x2(h[s * 4 + 2], h[s * 4 + 3]);
+          *(uint2 *)(a.hb + r * N + hb * 32 + 16 * s + 4 * g) = v;
+        }
       }
     }
     __syncthreads();   // LDS is restaged by the next pass
   }
 }
 
-// ---------------------------------------------------- GEMM1, W4A16 / W3A16
-template <int WF>
-__device__ __forceinline__ void dec_gemm1_a16_body(const DecArgs &a, const DecExpert &X, unsigned long long md,
-                                                   float *red) {
-  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
-  const int K = a.K, N = a.N, nkt = K / 128, groups = K / 32, hb = blockIdx.x;
-  const size_t rt_bytes = (size_t)16 * groups * U, rt_scales = (size_t)16 * groups * SU;
-  const uint8_t *wt = X.w13 + (size_t)X.e * (2 * N) * groups * U + (size_t)(4 * hb) * rt_bytes + l * U;
-  const uint8_t *st = X.s13 + (size_t)X.e * (2 * N) * groups * SU + (size_t)(4 * hb) * rt_scales + l * SU;
-  const int ncols = __popcll(md);
-  for (int p0 = 0; p0 < ncols; p0 += 16) {
-    const int r = (p0 + c < ncols) ? nth_bit(md, p0 + c) : -1;
-    const bool have = r >= 0;
-    const uint16_t *xrow = a.x + (size_t)(have ? r / a.topk : 0) * K;
-    v4f acc[4];
-#pragma unroll
-    for (int q = 0; q < 4; q++) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-    A16G1Stage<WF> s0, s1;
-    if (w < nkt) a16g1_load(s0, wt, st, rt_bytes, rt_scales, w, xrow, have, g);
-    for (int kt = w; kt < nkt; kt += 16) {
-      if (kt + 8 < nkt) a16g1_load(s1, wt, st, rt_bytes, rt_scales, kt + 8, xrow, have, g);
-      a16g1_compute(s0, acc);
-      if (kt + 16 < nkt) a16g1_load(s0, wt, st, rt_bytes, rt_scales, kt + 16, xrow, have, g);
-      if (kt + 8 < nkt) a16g1_compute(s1, acc);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; q++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) red[(w * 16 + q * 4 + i) * 64 + l] = acc[q][i];
-    __syncthreads();
-    if (w == 0 && have) {
-      float h[8];
-      dec_swiglu(red, l, X.g13, a.limit, a.has_limit, h);
-#pragma unroll
-      for (int s = 0; s < 2; s++) {
-        uint2 v;
-        v.x = pack_bf16x2(h[s * 4], h[s * 4 + 1]);
-        v.y = pack_bf16x2(h[s * 4 + 2], h[s * 4 + 3]);
-        *(uint2 *)(a.hb + (size_t)r * N + hb * 32 + 16 * s + 4 * g) = v;
-      }
-    }
-    __syncthreads();
-  }
+// grid (N/32 intermediate blocks, expert slots); the block's 4 waves split K.
+// At decode sizes (~35 experts x N/32 blocks) every block is resident at once
+// with up to 128 VGPRs per lane, so no block waits for a second round.
+__global__ __launch_bounds__(256, 4) void k_dec_gemm1_a8(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t dsm[];
+  int ud;
+  unsigned long long md;
+  if (!dec_group(dec_route_u(a, threadIdx.x & 63), blockIdx.y, &ud, &md)) return;
+  dec_gemm1_body<true, W_MXFP4, 4>(a, dec_expert(a, ud), md, dsm);
 }
 
-__global__ __launch_bounds__(512) void k_dec_gemm1_a16(DecArgs a) {
-  __shared__ float red[8 * 16 * 64];
+__global__ __launch_bounds__(256, 4) void k_dec_gemm1_a16(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t dsm[];
   int ud;
   unsigned long long md;
   if (!dec_group(dec_route_u(a, threadIdx.x & 63), blockIdx.y, &ud, &md)) return;
   const DecExpert X = dec_expert(a, ud);
-  if (X.fmt == W_NVFP4) dec_gemm1_a16_body<W_NVFP4>(a, X, md, red);
-  else dec_gemm1_a16_body<W_NF3>(a, X, md, red);
+  if (X.fmt == W_NVFP4) dec_gemm1_body<false, W_NVFP4, 4>(a, X, md, dsm);
+  else dec_gemm1_body<false, W_NF3, 4>(a, X, md, dsm);
 }
 
 // ---------------------------------------------------------------- GEMM2
@@ -284,98 +356,121 @@ __device__ __forceinline__ void dec_fold(const DecArgs &a, unsigned long long md
   }
 }
 
-__device__ __forceinline__ void dec_gemm2_a8_expert(const DecArgs &a, const DecExpert &X, unsigned long long md,
-                                                    int rt, int l, float *tok) {
-  const int c = l & 15, g = l >> 4, K = a.K, N = a.N, nkt = (N + 127) / 128;
-  const size_t rt_bytes = (size_t)16 * (N / 2), rt_scales = (size_t)16 * (N / 32);
-  const uint8_t *wt = X.w2 + (size_t)X.e * K * (N / 2) + (size_t)rt * rt_bytes + l * 16;
-  const uint8_t *st = X.s2 + (size_t)X.e * K * (N / 32) + (size_t)rt * rt_scales + l;
-  const int ncols = __popcll(md);
-  for (int p0 = 0; p0 < ncols; p0 += 16) {
-    const int r = (p0 + c < ncols) ? nth_bit(md, p0 + c) : -1;
-    const bool have = r >= 0;
-    const uint8_t *hrow = a.hq + (size_t)(have ? r : 0) * N;
-    const uint8_t *hsrow = a.hs + (size_t)(have ? r : 0) * (N / 32);
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int kt0 = 0; kt0 < nkt; kt0 += 8) {
-      v4i A[8], B0[8], B1[8];
-      int sa[8], sb[8];
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int kt = kt0 + j, kb = kt * 128;
-        A[j] = B0[j] = B1[j] = v4i{0, 0, 0, 0};
-        sa[j] = sb[j] = 0;
-        if (kt < nkt && kb + 32 * g < N) {
-          A[j] = *(const v4i *)(wt + (size_t)kt * 1024);
-          sa[j] = st[kt * 64];
-        }
-        if (have && kt < nkt) {
-          if (kb + 16 * g < N) B0[j] = *(const v4i *)(hrow + kb + 16 * g);
-          if (kb + 64 + 16 * g < N) B1[j] = *(const v4i *)(hrow + kb + 64 + 16 * g);
-          if (kb + 32 * g < N) sb[j] = hsrow[kb / 32 + g];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        if (kt0 + j < nkt) {
-          const v8i bop = v8i{B0[j][0], B0[j][1], B0[j][2], B0[j][3], B1[j][0], B1[j][1], B1[j][2], B1[j][3]};
-          acc = mfma_fp4_fp8(A[j], bop, acc, sa[j], sb[j]);
-        }
-      }
-    }
-    dec_fold(a, md, p0, c, g, acc, have ? a.topk_w[r] * X.g2 : 0.f, tok);
-  }
-}
+// One w2 row tile of one expert: buffer resources of the expert's data and
+// scales and the row tile's wave-uniform offsets.
+struct W2Tile {
+  Buf wb, sb;
+  uint32_t w0, s0;
+  float g2;
+};
 
-template <int WF>
-__device__ __forceinline__ void dec_gemm2_a16_expert(const DecArgs &a, const DecExpert &X, unsigned long long md,
-                                                     int rt, int l, float *tok) {
-  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
-  const int c = l & 15, g = l >> 4, K = a.K, N = a.N, nkt = (N + 127) / 128, groups = N / 32;
-  const size_t rt_bytes = (size_t)16 * groups * U, rt_scales = (size_t)16 * groups * SU;
-  const uint8_t *wt = X.w2 + (size_t)X.e * K * groups * U + (size_t)rt * rt_bytes + l * U;
-  const uint8_t *st = X.s2 + (size_t)X.e * K * groups * SU + (size_t)rt * rt_scales + l * SU;
-  const int ncols = __popcll(md);
-  for (int p0 = 0; p0 < ncols; p0 += 16) {
-    const int r = (p0 + c < ncols) ? nth_bit(md, p0 + c) : -1;
-    const bool have = r >= 0;
-    const uint16_t *hrow = a.hb + (size_t)(have ? r : 0) * N;
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int kt0 = 0; kt0 < nkt; kt0 += 4) {
-      A16Tile<WF> A[4];
-      v4i B[4][4];
+// k-tiles of the down GEMM loaded in one burst: all of them when N <= 640
+// (W4A8); two at a time for W4A16, whose bf16 activations also sit in registers
+constexpr int kW2MaxTiles = 5;
+constexpr int kW2MaxTilesA16 = 2;
+constexpr int kDecG2Waves = 16;
+
+// Down GEMM of one expert for one row tile and up to 16 of its route columns:
+// every k-tile of weights (and, for W4A16, of activations) is requested before
+// the first MFMA, so one memory round trip covers the expert.
+template <bool A8, int WF>
+__device__ __forceinline__ v4f w2_expert(const DecArgs &a, const W2Tile &t, const uint8_t *hq_s, const uint8_t *hs_s,
+                                         int r, int g, uint32_t l, float *wr) {
+  constexpr uint32_t U = A8 ? 16 : FmtGeom<WF>::unit, SU = A8 ? 1 : FmtGeom<WF>::sunit;
+  typedef typename std::conditional<A8, v4i, A16Tile<WF>>::type T;
+  constexpr int NB = A8 ? kW2MaxTiles : kW2MaxTilesA16;
+  const int N = a.N, nkt = (N + 127) / 128;
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  *wr = r >= 0 ? a.topk_w[r] : 0.f;   // in flight with the weight burst
+  for (int kt0 = 0; kt0 < nkt; kt0 += NB) {
+    T A[NB];
+    int sa[NB];
+    v4i B[A8 ? 1 : NB][4];
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int kt = kt0 + j, kb = kt * 128;
-        const bool inb = kt < nkt && kb + 32 * g < N;
-        if (inb) A[j].load(wt + (size_t)kt * 64 * U, st + kt * 64 * SU);
+    for (int j = 0; j < NB; j++) {
+      const int kt = kt0 + j, kb = kt * 128;
+      const bool inb = kt < nkt && kb + 32 * g < N;
+      if constexpr (A8) {
+        A[j] = v4i{0, 0, 0, 0};
+        sa[j] = 0;
+        if (inb) {
+          A[j] = buf_load16(t.wb, (uint32_t)kt * 1024u + l * 16u, t.w0);
+          sa[j] = buf_load1(t.sb, (uint32_t)kt * 64u + l, t.s0);
+        }
+      } else {
+        if (inb) A[j].load(t.wb, (uint32_t)kt * 64u * U + l * U, t.w0, t.sb, (uint32_t)kt * 64u * SU + l * SU, t.s0);
         else A[j].zero();
 #pragma unroll
         for (int s = 0; s < 4; s++) B[j][s] = v4i{0, 0, 0, 0};
-        if (have && inb) {
-          const v4i *hp = (const v4i *)(hrow + kb + 32 * g);
+        if (r >= 0 && inb) {
+          const v4i *hp = (const v4i *)(a.hb + (size_t)r * N + kb + 32 * g);
 #pragma unroll
           for (int s = 0; s < 4; s++) B[j][s] = hp[s];
         }
       }
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        if (kt0 + j < nkt) {
-#pragma unroll
-          for (int s = 0; s < 4; s++) acc = mfma_bf16(A[j].step(s), __builtin_bit_cast(v8bf, B[j][s]), acc);
-        }
     }
-    dec_fold(a, md, p0, c, g, acc, have ? a.topk_w[r] * X.g2 : 0.f, tok);
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+      const int kt = kt0 + j, kb = kt * 128;
+      if (kt >= nkt) break;
+      if constexpr (A8) {
+        v4i B0 = v4i{0, 0, 0, 0}, B1 = v4i{0, 0, 0, 0};
+        int sb = 0;
+        if (r >= 0) {   // MXFP8 rows of every route are staged in LDS
+          const uint8_t *hrow = hq_s + r * (N + 16);
+          if (kb + 16 * g < N) B0 = *(const v4i *)(hrow + kb + 16 * g);
+          if (kb + 64 + 16 * g < N) B1 = *(const v4i *)(hrow + kb + 64 + 16 * g);
+          if (kb + 32 * g < N) sb = hs_s[r * (N / 32) + kb / 32 + g];
+        }
+        const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
+        acc = mfma_fp4_fp8(A[j], bop, acc, sa[j], sb);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; s++) acc = mfma_bf16(A[j].step(s), __builtin_bit_cast(v8bf, B[j][s]), acc);
+      }
+    }
+  }
+  return acc;
+}
+
+// One wave's share of the experts (gi = w, w + kDecG2Waves, ...) of format WF
+// for output row tile rt.
+template <bool A8, int WF>
+__device__ __forceinline__ void dec_gemm2_wave(const DecArgs &a, const int *gu_s, const unsigned long long *gm_s,
+                                               int ng, const uint8_t *hq_s, const uint8_t *hs_s, float *tok) {
+  constexpr int U = A8 ? 16 : FmtGeom<WF>::unit, SU = A8 ? 1 : FmtGeom<WF>::sunit;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, g = l >> 4;
+  const int K = a.K, N = a.N, groups = N / 32, rt = blockIdx.x;
+  const size_t rt_bytes = (size_t)16 * groups * U, rt_scales = (size_t)16 * groups * SU;
+  for (int gi = w; gi < ng; gi += kDecG2Waves) {
+    const DecExpert X = dec_expert(a, __builtin_amdgcn_readfirstlane(gu_s[gi]));
+    if (!A8 && X.fmt != WF) continue;
+    W2Tile t;
+    t.wb = make_buf(X.w2 + (size_t)X.e * K * groups * U, (uint32_t)((size_t)K * groups * U));
+    t.sb = make_buf(X.s2 + (size_t)X.e * K * groups * SU, (uint32_t)((size_t)K * groups * SU));
+    t.w0 = (uint32_t)((size_t)rt * rt_bytes);
+    t.s0 = (uint32_t)((size_t)rt * rt_scales);
+    const unsigned long long md = uniform_u64(gm_s[gi]);
+    const int ncols = __popcll(md);
+    for (int p0 = 0; p0 < ncols; p0 += 16) {   // one pass unless the expert holds > 16 routes
+      const int r = (p0 + c < ncols) ? nth_bit(md, p0 + c) : -1;
+      float wr;
+      const v4f acc = w2_expert<A8, WF>(a, t, hq_s, hs_s, r, g, (uint32_t)l, &wr);
+      dec_fold(a, md, p0, c, g, acc, wr * X.g2, tok);
+    }
   }
 }
 
+// grid (K/16 output row tiles); the block's waves split the experts.
 template <bool A8>
-__global__ __launch_bounds__(512) void k_dec_gemm2(DecArgs a) {
+__global__ __launch_bounds__(kDecG2Waves * 64) void k_dec_gemm2(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t dsm2[];
   __shared__ int gu_s[kDecodeMaxRoutes];
   __shared__ unsigned long long gm_s[kDecodeMaxRoutes];
   __shared__ int ng_s;
-  __shared__ float tred[8][4][64];
+  __shared__ float tred[kDecG2Waves][4][64];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int N = a.N;
   if (w == 0) {
     const int u = dec_route_u(a, l);
     unsigned long long rem = __ballot(u >= 0);
@@ -393,15 +488,39 @@ __global__ __launch_bounds__(512) void k_dec_gemm2(DecArgs a) {
     }
     if (l == 0) ng_s = n;
   }
+  uint8_t *hq_s = dsm2, *hs_s = dsm2 + (size_t)a.R * (N + 16);
+  if (A8) {   // MXFP8 intermediate rows of every route -> LDS, loads issued first
+    // the host takes this path only when R * (N + 16 + N/32) <= 48 KB, so
+    // R * N / 16 <= 3072 sixteen-byte chunks: three per thread
+    constexpr int kMaxPer = 3;
+    const int nchunk = a.R * (N / 16);
+    v4i tmp[kMaxPer];
+    uint32_t sv = 0;
+    const int nsc = a.R * (N / 32);
+#pragma unroll
+    for (int j = 0; j < kMaxPer; j++) {
+      const int i = tid + j * kDecG2Waves * 64;
+      if (i < nchunk) tmp[j] = *(const v4i *)(a.hq + (size_t)i * 16);
+    }
+    if (tid * 4 < nsc) sv = *(const uint32_t *)(a.hs + tid * 4);   // R*N/32 <= 4 * 1024 bytes
+#pragma unroll
+    for (int j = 0; j < kMaxPer; j++) {
+      const int i = tid + j * kDecG2Waves * 64;
+      if (i < nchunk) {
+        const int r = i / (N / 16), c16 = i - r * (N / 16);
+        *(v4i *)(hq_s + r * (N + 16) + c16 * 16) = tmp[j];
+      }
+    }
+    if (tid * 4 < nsc)
+      for (int b = 0; b < 4 && tid * 4 + b < nsc; b++) hs_s[tid * 4 + b] = (uint8_t)(sv >> (8 * b));
+  }
   __syncthreads();
-  const int ng = ng_s, rt = blockIdx.x;
   float tok[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int gi = w; gi < ng; gi += 8) {
-    const DecExpert X = dec_expert(a, gu_s[gi]);
-    const unsigned long long md = gm_s[gi];
-    if (A8) dec_gemm2_a8_expert(a, X, md, rt, l, tok);
-    else if (X.fmt == W_NVFP4) dec_gemm2_a16_expert<W_NVFP4>(a, X, md, rt, l, tok);
-    else dec_gemm2_a16_expert<W_NF3>(a, X, md, rt, l, tok);
+  if (A8) {
+    dec_gemm2_wave<true, W_MXFP4>(a, gu_s, gm_s, ng_s, hq_s, hs_s, tok);
+  } else {
+    dec_gemm2_wave<false, W_NVFP4>(a, gu_s, gm_s, ng_s, hq_s, hs_s, tok);
+    dec_gemm2_wave<false, W_NF3>(a, gu_s, gm_s, ng_s, hq_s, hs_s, tok);
   }
 #pragma unroll
   for (int i = 0; i < 4; i++) tred[w][i][l] = tok[i];
@@ -412,40 +531,42 @@ __global__ __launch_bounds__(512) void k_dec_gemm2(DecArgs a) {
     for (int i = 0; i < 4; i++) {
       s[i] = 0.f;
 #pragma unroll
-      for (int v = 0; v < 8; v++) s[i] += tred[v][i][l];
+      for (int v = 0; v < kDecG2Waves; v++) s[i] += tred[v][i][l];
     }
     uint2 o;
     o.x = pack_bf16x2(s[0], s[1]);
     o.y = pack_bf16x2(s[2], s[3]);
-    *(uint2 *)(a.out + (size_t)c * a.K + rt * 16 + 4 * g) = o;
+    *(uint2 *)(a.out + (size_t)c * a.K + blockIdx.x * 16 + 4 * g) = o;
   }
 }
 
-int decode_cpass(int K) { return max(1, min(kDecodeMaxT, 61440 / (K + 16 + K / 32))); }
+int decode_cpass(int K, int a8) {
+  const int row = a8 ? K + 16 + K / 32 : 2 * (K + 8);
+  return max(1, min(kDecodeMaxT, 32768 / row));
+}
 
-size_t decode_gemm1_lds(int K, int cpass) {
-  const size_t stage = (size_t)cpass * (K + 16) + (size_t)cpass * (K / 32);
-  const size_t red = (size_t)8 * 16 * 64 * sizeof(float);
+size_t decode_gemm1_lds(int K, int cpass, int a8) {
+  const size_t stage = a8 ? (size_t)cpass * (K + 16) + (size_t)cpass * (K / 32) : (size_t)cpass * 2 * (K + 8);
+  const size_t red = (size_t)4 * 16 * 64 * sizeof(float);
   return ((stage > red ? stage : red) + 15) & ~(size_t)15;
 }
 
 hipError_t launch_decode(int a8, const DecArgs &a, hipStream_t s, hipEvent_t ev_mid) {
   if (a.R == 0) return hipSuccess;
   int U = a.tier[0].E + (a.n_tiers > 1 ? a.tier[1].E : 0);
-  const dim3 g1(a.N / 32, (unsigned)min(a.R, U)), g2(a.K / 16), block(512);
-  if (a8) {
-    hipLaunchKernelGGL(k_dec_gemm1_a8, g1, block, decode_gemm1_lds(a.K, a.cpass), s, a);
-  } else {
-    hipLaunchKernelGGL(k_dec_gemm1_a16, g1, block, 0, s, a);
-  }
+  const dim3 g1(a.N / 32, (unsigned)min(a.R, U)), g2(a.K / 16);
+  const size_t lds1 = decode_gemm1_lds(a.K, a.cpass, a8);
+  if (a8) hipLaunchKernelGGL(k_dec_gemm1_a8, g1, dim3(256), lds1, s, a);
+  else hipLaunchKernelGGL(k_dec_gemm1_a16, g1, dim3(256), lds1, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_mid) {
     e = hipEventRecord(ev_mid, s);
     if (e != hipSuccess) return e;
   }
-  if (a8) hipLaunchKernelGGL(k_dec_gemm2<true>, g2, block, 0, s, a);
-  else hipLaunchKernelGGL(k_dec_gemm2<false>, g2, block, 0, s, a);
+  const size_t lds2 = a8 ? (size_t)a.R * (a.N + 16) + (size_t)a.R * (a.N / 32) : 0;
+  if (a8) hipLaunchKernelGGL(k_dec_gemm2<true>, g2, dim3(kDecG2Waves * 64), lds2, s, a);
+  else hipLaunchKernelGGL(k_dec_gemm2<false>, g2, dim3(kDecG2Waves * 64), lds2, s, a);
   return hipGetLastError();
 }
 

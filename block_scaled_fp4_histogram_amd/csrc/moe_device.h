@@ -11,6 +11,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ numerics
 
@@ -32,13 +33,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-}
-
-// E2M1 code (4 bits) -> fp32.
-__device__ __forceinline__ float e2m1_f32(uint32_t c) {
-  const uint32_t m = c & 7u;
-  const uint32_t bits = (m < 2u) ? (m * 0x3F000000u) : ((m + 252u) << 22);
-  return __uint_as_float(bits | ((c & 8u) << 28));
 }
 
 // E4M3 (fn) byte -> fp32 (NaN codes are out of contract).
@@ -83,6 +77,74 @@ __device__ __forceinline__ uint32_t quant_block32(const float *v, uint32_t *code
   return sb;
 }
 
+// Quantise 32 bf16 values (4 x 16 bytes, element order) to MXFP8 without
+// unpacking them first: the block maximum is the integer maximum of the bf16
+// magnitude bits (same order as the values), then pairs are converted in place.
+__device__ __forceinline__ uint32_t quant_block32_bf16(const v4i *x, uint32_t *codes) {
+  uint32_t mbits = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      const uint32_t w = (uint32_t)x[q][d];
+      mbits = max(mbits, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
+    }
+  float inv;
+  const uint32_t sb = mx_scale(__uint_as_float(mbits << 16), &inv);
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+#pragma unroll
+    for (int d = 0; d < 4; d += 2) {
+      const uint32_t w0 = (uint32_t)x[q][d], w1 = (uint32_t)x[q][d + 1];
+      codes[2 * q + d / 2] = e4m3x4(bf16_to_f32(w0 & 0xFFFFu), bf16_to_f32(w0 >> 16), bf16_to_f32(w1 & 0xFFFFu),
+                                    bf16_to_f32(w1 >> 16), inv);
+    }
+  return sb;
+}
+
+// ------------------------------------------------------------ buffer loads
+//
+// Weight streams go through raw buffer loads: a wave-uniform 128-bit resource
+// (base address, byte range) in scalar registers plus a 32-bit offset per lane,
+// so no 64-bit per-lane address is formed.  Loads beyond the range return 0.
+typedef int v3i __attribute__((ext_vector_type(3)));
+extern "C" __device__ v4i moe_raw_buffer_load_v4i32(v4i rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.v4i32");
+extern "C" __device__ v3i moe_raw_buffer_load_v3i32(v4i rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.v3i32");
+extern "C" __device__ unsigned short moe_raw_buffer_load_i16(v4i rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.i16");
+extern "C" __device__ unsigned char moe_raw_buffer_load_i8(v4i rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.i8");
+
+struct Buf {
+  v4i r;
+};
+
+// Resource over [base, base + bytes); word 3 is the gfx9 default data format.
+__device__ __forceinline__ Buf make_buf(const void *base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  Buf b;
+  b.r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  b.r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  b.r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  b.r[3] = 0x00020000;
+  return b;
+}
+
+__device__ __forceinline__ v4i buf_load16(const Buf &b, uint32_t voff, uint32_t soff) {
+  return moe_raw_buffer_load_v4i32(b.r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ v3i buf_load12(const Buf &b, uint32_t voff, uint32_t soff) {
+  return moe_raw_buffer_load_v3i32(b.r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_load2(const Buf &b, uint32_t voff, uint32_t soff) {
+  return moe_raw_buffer_load_i16(b.r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_load1(const Buf &b, uint32_t voff, uint32_t soff) {
+  return moe_raw_buffer_load_i8(b.r, (int)voff, (int)soff, 0);
+}
+
 // MFMA operand of an FP4 weight tile (16 bytes per lane in the low 4 VGPRs).
 __device__ __forceinline__ v8i fp4_operand(v4i a) { return v8i{a[0], a[1], a[2], a[3], 0, 0, 0, 0}; }
 
@@ -100,13 +162,22 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(v4i a, v8i b, v4f c, int sa, int sb)
 // feeds its 32 columns in 4 steps of 8, and the activation operand walks the
 // same columns, so each step pairs the same k on both sides.
 
-// 8 fp4 codes (one dword) x scale -> 8 bf16 (exact: E2M1 x E4M3 fits bf16).
+// 8 fp4 codes (one dword, element 2i in the low nibble of byte i) x scale -> 8
+// bf16, exact (an E2M1 value times an E4M3 scale has at most 5 significant
+// bits, so the fp32 product's upper half is the bf16 value).
+// v_cvt_scalef32_pk_f32_fp4 decodes the two codes of one byte; its scale
+// operand only contributes a power of two, so it is 1 here and the E4M3 scale
+// is applied with an fp32 multiply.
 __device__ __forceinline__ v8bf nvfp4_step(uint32_t w, float sc) {
   v4i r;
 #pragma unroll
   for (int m = 0; m < 4; m++) {
-    const uint32_t byte = (w >> (8 * m)) & 0xFFu;
-    const float lo = e2m1_f32(byte & 15u) * sc, hi = e2m1_f32(byte >> 4) * sc;
+    v2f f;
+    if (m == 0) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    else if (m == 1) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    else if (m == 2) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    else f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    const float lo = f[0] * sc, hi = f[1] * sc;
     r[m] = (int)__builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
   }
   return __builtin_bit_cast(v8bf, r);
@@ -145,6 +216,20 @@ struct A16Tile {
       const uint32_t *p = (const uint32_t *)data;
       d[0] = p[0]; d[1] = p[1]; d[2] = p[2]; d[3] = 0;
       sc = *scales;
+    }
+  }
+  // the same from buffer resources (data wb, scales sb) at lane offsets vd, vs
+  // plus wave-uniform offsets sd, ss
+  __device__ __forceinline__ void load(const Buf &wb, uint32_t vd, uint32_t sd, const Buf &sb, uint32_t vs,
+                                       uint32_t ss) {
+    if (WF == W_NVFP4) {
+      const v4i v = buf_load16(wb, vd, sd);
+      d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+      sc = buf_load2(sb, vs, ss);
+    } else {
+      const v3i v = buf_load12(wb, vd, sd);
+      d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = 0;
+      sc = buf_load1(sb, vs, ss);
     }
   }
   __device__ __forceinline__ void zero() { d[0] = d[1] = d[2] = d[3] = 0; sc = 0; }
