@@ -79,7 +79,7 @@ def algorithmic(prob):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("moe_kernels.hip", "moe_decode.hip", "moe_device.h", "moe_common.h"):
+    for f in ("moe_kernels.hip", "moe_decode.hip", "moe_prefill.hip", "moe_device.h", "moe_common.h"):
         with open(os.path.join(ROOT, "block_scaled_fp4_histogram_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -117,7 +117,7 @@ Layout layout(const moe_plan_s *p, int cap, int deterministic) {
     L.xq = take((size_t)cap * p->K);
     L.xs = take((size_t)cap * (p->K / 32));
     L.hq = take(R * p->N);
-    L.hs = take(R * (p->N / 32));
+    L.hs = take(R * moe::hs_stride(p->N));
   } else {
     L.hb = take(2 * R * p->N);
   }
@@ -199,7 +199,7 @@ bool use_decode(const moe_plan_s *p, int T) {
   // W4A8 GEMM2 all routes' MXFP8 rows of the intermediate
   const bool a8 = p->afmt == MOE_A_MXFP8;
   const long row = a8 ? (long)p->K + 16 + p->K / 32 : 2L * (p->K + 8);
-  const long lds2 = a8 ? (long)T * p->topk * (p->N + 16 + p->N / 32) : 0;
+  const long lds2 = a8 ? (long)T * p->topk * (p->N + 16 + moe::hs_stride(p->N)) : 0;
   const bool lds_ok = row <= 32768 && lds2 <= 49152;
   return T <= moe::kDecodeMaxT && T * p->topk <= moe::kDecodeMaxRoutes && lds_ok;
 }
@@ -224,6 +224,10 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ra.E1 = n_tiers > 1 ? tiers[1].experts->E : 0;
   ra.G = (R + moe::kRouteChunk - 1) / moe::kRouteChunk;
   ra.max_tiles = L.max_tiles;
+  // prefill kernels: W4A8 experts only, N % 64 == 0, batches of a prefill rung
+  bool prefill = p->afmt == MOE_A_MXFP8 && p->N % 64 == 0 && T >= moe::kPrefillMinT;
+  for (int i = 0; i < n_tiers; i++) prefill = prefill && tiers[i].experts->wfmt == MOE_W_MXFP4;
+  ra.tile_rows = prefill ? moe::kPfTileRows : moe::kTileRows;
   ra.ru = I32(L.ru);
   ra.lrank = I32(L.lrank);
   ra.chunk_hist = I32(L.chunk_hist);
@@ -257,6 +261,8 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
 
   moe::GemmArgs ga;
   memset(&ga, 0, sizeof ga);
+  ga.tile_rows = ra.tile_rows;
+  ga.T = T;
   ga.tile_u = I32(L.tile_u);
   ga.tile_row0 = I32(L.tile_row0);
   ga.tier_tiles = I32(L.tier_tiles);
@@ -277,7 +283,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ga.out_acc = (float *)(scratch + L.acc);
   ga.rb = (uint16_t *)(scratch + L.rb);
   ga.deterministic = deterministic;
-  const int row_tiles = (R + moe::kTileRows - 1) / moe::kTileRows;
+  const int row_tiles = (R + ra.tile_rows - 1) / ra.tile_rows;
   int u_base = 0;
   for (int i = 0; i < n_tiers; i++) {
     const moe_experts_s *xp = tiers[i].experts;
@@ -290,7 +296,8 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     ga.g13 = xp->g13;
     ga.g2 = xp->g2;
     const int grid_tiles = row_tiles + std::min(xp->E, R);
-    HIP_TRY(moe::launch_gemm1(xp->wfmt, ga, grid_tiles, s));
+    if (prefill) HIP_TRY(moe::launch_pf_gemm1(ga, grid_tiles, s));
+    else HIP_TRY(moe::launch_gemm1(xp->wfmt, ga, grid_tiles, s));
     u_base += xp->E;
   }
   if (ev) HIP_TRY(hipEventRecord(ev[2], s));
@@ -306,7 +313,8 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     ga.g13 = xp->g13;
     ga.g2 = xp->g2;
     const int grid_tiles = row_tiles + std::min(xp->E, R);
-    HIP_TRY(moe::launch_gemm2(xp->wfmt, ga, grid_tiles, s));
+    if (prefill) HIP_TRY(moe::launch_pf_gemm2(ga, grid_tiles, s));
+    else HIP_TRY(moe::launch_gemm2(xp->wfmt, ga, grid_tiles, s));
     u_base += xp->E;
   }
   if (ev) HIP_TRY(hipEventRecord(ev[3], s));

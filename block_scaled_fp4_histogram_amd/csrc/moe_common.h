@@ -7,12 +7,18 @@
 
 namespace moe {
 
-constexpr int kTileRows = 16;        // token rows of one GEMM tile (MFMA N dimension)
+constexpr int kTileRows = 16;        // routes of one tile of the general GEMM kernels
+constexpr int kPfTileRows = 64;      // routes of one tile of the prefill kernels
+constexpr int kPrefillMinT = 128;    // smallest batch run with the prefill kernels
 constexpr int kRouteChunk = 2048;    // routes handled by one route-planner block
 constexpr int kMaxExperts = 1024;    // experts of all tiers together (LDS histogram size)
 constexpr int kMaxTiers = 2;
 
 enum WFmt { W_MXFP4 = 1, W_NVFP4 = 2, W_NF3 = 3 };
+
+// Bytes per row of the MXFP8 intermediate's scales: N/32 rounded up to a
+// multiple of 4, so every row starts 4-byte aligned.
+__host__ __device__ constexpr int hs_stride(int N) { return (N / 32 + 3) & ~3; }
 
 // Route planner: ids -> per-expert counts, offsets, stable permutation, tile table.
 struct RouteArgs {
@@ -22,6 +28,7 @@ struct RouteArgs {
   const int32_t *emap0, *emap1;      // NULL = identity
   int E0, E1;                        // experts per tier; U = E0 + E1
   int G;                             // route blocks (ceil(R / kRouteChunk))
+  int tile_rows;                     // routes per GEMM tile
   int max_tiles;
   int32_t *ru, *lrank, *chunk_hist;  // per-route expert / in-chunk rank; [G][U] counts
   int32_t *cnt, *off, *perm, *inv;
@@ -38,7 +45,7 @@ struct RouteArgs {
 // GEMM launches (one tier at a time).
 struct GemmArgs {
   const int32_t *tile_u, *tile_row0, *tier_tiles;
-  int tier, u_base;
+  int tier, u_base, tile_rows;
   const int32_t *off, *perm;
   int topk, K, N;
   const uint8_t *w13, *s13, *w2, *s2;
@@ -53,6 +60,7 @@ struct GemmArgs {
   float *out_acc;                    // fp32 [T, K] (atomic combine)
   uint16_t *rb;                      // bf16 [R, K] route buffer (deterministic combine)
   int deterministic;
+  int T;                             // tokens of the chunk (rows of x / the accumulator)
 };
 
 // Decode-size batches (T <= kDecodeMaxT tokens, T * top_k <= 64 routes): two
@@ -88,6 +96,9 @@ hipError_t launch_decode(int a8, const DecArgs &a, hipStream_t s, hipEvent_t ev_
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_gemm1(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s);
 hipError_t launch_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s);
+// Prefill kernels (64-route tiles, LDS-staged operands); W4A8 and N % 64 == 0.
+hipError_t launch_pf_gemm1(const GemmArgs &a, int grid_tiles, hipStream_t s);
+hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s);
 hipError_t launch_finalize(int deterministic, const float *out_acc, const uint16_t *rb, const int32_t *inv,
                            int T, int K, int topk, uint16_t *out, hipStream_t s);
 hipError_t launch_quant_bf16(const uint16_t *x, long rows, int cols, uint8_t *q, uint8_t *sc, hipStream_t s);

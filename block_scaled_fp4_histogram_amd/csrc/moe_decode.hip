@@ -288,7 +288,7 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
           for (int s = 0; s < 2; s++)
             *(uint32_t *)(a.hq + r * N + hb * 32 + 16 * s + 4 * g) =
                 e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
-          if (g == 0) a.hs[r * (N / 32) + hb] = (uint8_t)sbyte;
+          if (g == 0) a.hs[r * hs_stride(N) + hb] = (uint8_t)sbyte;
         }
       } else if (have) {
         const size_t r = (size_t)nth_bit(md, p0 + c);
@@ -420,7 +420,7 @@ __device__ __forceinline__ v4f w2_expert(const DecArgs &a, const W2Tile &t, cons
           const uint8_t *hrow = hq_s + r * (N + 16);
           if (kb + 16 * g < N) B0 = *(const v4i *)(hrow + kb + 16 * g);
           if (kb + 64 + 16 * g < N) B1 = *(const v4i *)(hrow + kb + 64 + 16 * g);
-          if (kb + 32 * g < N) sb = hs_s[r * (N / 32) + kb / 32 + g];
+          if (kb + 32 * g < N) sb = hs_s[r * hs_stride(N) + kb / 32 + g];
         }
         const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
         acc = mfma_fp4_fp8(A[j], bop, acc, sa[j], sb);
@@ -496,13 +496,13 @@ __global__ __launch_bounds__(kDecG2Waves * 64) void k_dec_gemm2(DecArgs a) {
     const int nchunk = a.R * (N / 16);
     v4i tmp[kMaxPer];
     uint32_t sv = 0;
-    const int nsc = a.R * (N / 32);
+    const int nsc = a.R * hs_stride(N);
 #pragma unroll
     for (int j = 0; j < kMaxPer; j++) {
       const int i = tid + j * kDecG2Waves * 64;
       if (i < nchunk) tmp[j] = *(const v4i *)(a.hq + (size_t)i * 16);
     }
-    if (tid * 4 < nsc) sv = *(const uint32_t *)(a.hs + tid * 4);   // R*N/32 <= 4 * 1024 bytes
+    if (tid * 4 < nsc) sv = *(const uint32_t *)(a.hs + tid * 4);   // R * hs_stride(N) <= 4 * 1024 bytes
 #pragma unroll
     for (int j = 0; j < kMaxPer; j++) {
       const int i = tid + j * kDecG2Waves * 64;
@@ -564,7 +564,7 @@ hipError_t launch_decode(int a8, const DecArgs &a, hipStream_t s, hipEvent_t ev_
     e = hipEventRecord(ev_mid, s);
     if (e != hipSuccess) return e;
   }
-  const size_t lds2 = a8 ? (size_t)a.R * (a.N + 16) + (size_t)a.R * (a.N / 32) : 0;
+  const size_t lds2 = a8 ? (size_t)a.R * (a.N + 16) + (size_t)a.R * hs_stride(a.N) : 0;
   if (a8) hipLaunchKernelGGL(k_dec_gemm2<true>, g2, dim3(kDecG2Waves * 64), lds2, s, a);
   else hipLaunchKernelGGL(k_dec_gemm2<false>, g2, dim3(kDecG2Waves * 64), lds2, s, a);
   return hipGetLastError();

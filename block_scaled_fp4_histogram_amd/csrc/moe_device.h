@@ -112,6 +112,8 @@ extern "C" __device__ v4i moe_raw_buffer_load_v4i32(v4i rsrc, int voffset, int s
     "llvm.amdgcn.raw.buffer.load.v4i32");
 extern "C" __device__ v3i moe_raw_buffer_load_v3i32(v4i rsrc, int voffset, int soffset, int aux) __asm(
     "llvm.amdgcn.raw.buffer.load.v3i32");
+extern "C" __device__ unsigned int moe_raw_buffer_load_i32(v4i rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.i32");
 extern "C" __device__ unsigned short moe_raw_buffer_load_i16(v4i rsrc, int voffset, int soffset, int aux) __asm(
     "llvm.amdgcn.raw.buffer.load.i16");
 extern "C" __device__ unsigned char moe_raw_buffer_load_i8(v4i rsrc, int voffset, int soffset, int aux) __asm(
@@ -137,6 +139,9 @@ __device__ __forceinline__ v4i buf_load16(const Buf &b, uint32_t voff, uint32_t 
 }
 __device__ __forceinline__ v3i buf_load12(const Buf &b, uint32_t voff, uint32_t soff) {
   return moe_raw_buffer_load_v3i32(b.r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(const Buf &b, uint32_t voff, uint32_t soff) {
+  return moe_raw_buffer_load_i32(b.r, (int)voff, (int)soff, 0);
 }
 __device__ __forceinline__ uint32_t buf_load2(const Buf &b, uint32_t voff, uint32_t soff) {
   return moe_raw_buffer_load_i16(b.r, (int)voff, (int)soff, 0);
@@ -260,6 +265,25 @@ __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+
+// ------------------------------------------------ tile schedule
+
+struct TileInfo {
+  int valid, e, p0, rows;
+};
+
+__device__ __forceinline__ TileInfo tile_info(const GemmArgs &a) {
+  TileInfo ti;
+  const int tbeg = a.tier_tiles[2 * a.tier], tend = a.tier_tiles[2 * a.tier + 1];
+  const int tile = tbeg + (int)blockIdx.y;
+  ti.valid = tile < tend;
+  if (!ti.valid) return ti;
+  const int u = a.tile_u[tile];
+  ti.e = u - a.u_base;
+  ti.p0 = a.off[u] + a.tile_row0[tile];
+  ti.rows = min(a.tile_rows, a.off[u + 1] - ti.p0);
+  return ti;
+}
 
 // ------------------------------------------------ GEMM1 k-tile stages
 

@@ -49,7 +49,7 @@ __device__ void finish_plan(const RouteArgs &a, int U, const int *cnt, int *off,
     for (int i = 0; i < per; i++)
       if (b + i < U) {
         s += cnt[b + i];
-        nt += (cnt[b + i] + kTileRows - 1) / kTileRows;
+        nt += (cnt[b + i] + a.tile_rows - 1) / a.tile_rows;
       }
     int is = s, it = nt;
 #pragma unroll
@@ -66,7 +66,7 @@ __device__ void finish_plan(const RouteArgs &a, int U, const int *cnt, int *off,
         off[b + i] = rs;
         tbeg[b + i] = rt;
         rs += cnt[b + i];
-        rt += (cnt[b + i] + kTileRows - 1) / kTileRows;
+        rt += (cnt[b + i] + a.tile_rows - 1) / a.tile_rows;
       }
     if (tid == 63) {
       off[U] = is;
@@ -78,9 +78,9 @@ __device__ void finish_plan(const RouteArgs &a, int U, const int *cnt, int *off,
   for (int u = tid; u < U; u += 256) {
     a.cnt[u] = cnt[u];
     const int tb = tbeg[u];
-    for (int i = 0; i * kTileRows < cnt[u]; i++) {
+    for (int i = 0; i * a.tile_rows < cnt[u]; i++) {
       a.tile_u[tb + i] = u;
-      a.tile_row0[tb + i] = i * kTileRows;
+      a.tile_row0[tb + i] = i * a.tile_rows;
     }
   }
   if (tid == 0) {
@@ -293,23 +293,6 @@ hipError_t launch_quant_f32(const float *h, long rows, int cols, uint8_t *q, uin
 
 // ------------------------------------------------------------ tile schedule
 
-struct TileInfo {
-  int valid, e, p0, rows;
-};
-
-__device__ __forceinline__ TileInfo tile_info(const GemmArgs &a) {
-  TileInfo ti;
-  const int tbeg = a.tier_tiles[2 * a.tier], tend = a.tier_tiles[2 * a.tier + 1];
-  const int tile = tbeg + (int)blockIdx.y;
-  ti.valid = tile < tend;
-  if (!ti.valid) return ti;
-  const int u = a.tile_u[tile];
-  ti.e = u - a.u_base;
-  ti.p0 = a.off[u] + a.tile_row0[tile];
-  ti.rows = min(kTileRows, a.off[u + 1] - ti.p0);
-  return ti;
-}
-
 // -------------------------------------------------- W4A8 (MXFP4 x MXFP8)
 
 // Weight tile layout (per expert, per matrix of R rows x Kd columns): row tiles
@@ -379,7 +362,7 @@ __global__ __launch_bounds__(256) void k_gemm1_a8(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; s++)
       *(uint32_t *)(a.hq + p * N + n0 + 16 * s + 4 * g) = e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
-    if (g == 0) a.hs[p * (N / 32) + hb] = (uint8_t)sbyte;
+    if (g == 0) a.hs[p * hs_stride(N) + hb] = (uint8_t)sbyte;
   }
 }
 
@@ -417,7 +400,7 @@ __global__ __launch_bounds__(256) void k_gemm2_a8(GemmArgs a) {
   const uint8_t *st = a.s2 + (size_t)ti.e * K * (N / 32) + (size_t)rt * rt_scales + l;
   const bool have = c < ti.rows;
   const uint8_t *hrow = a.hq + (size_t)(ti.p0 + (have ? c : 0)) * N;
-  const uint8_t *hsrow = a.hs + (size_t)(ti.p0 + (have ? c : 0)) * (N / 32);
+  const uint8_t *hsrow = a.hs + (size_t)(ti.p0 + (have ? c : 0)) * hs_stride(N);
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
   for (int kt0 = 0; kt0 < nkt; kt0 += 4) {
     v4i A[4], B0[4], B1[4];
