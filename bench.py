@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
                     help="replay the layer from a captured HIP graph (auto: batches of <= 64 tokens, "
                          "as decode steps run in serving)")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (the reference kernel that "
+                         "scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the layer shards by "
@@ -138,6 +141,16 @@ def main():
 
     import torch
     import block_scaled_fp4_histogram_amd as M
+
+    if args.copy_calib:
+        n = args.copy_calib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n}), flush=True)
+        return
 
     cfg = I.CONFIGS[args.config]
     log(f"config {cfg.name}: generating inputs")

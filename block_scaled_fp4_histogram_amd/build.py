@@ -14,6 +14,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-munsafe-fp-atomics",
+    # MFMA accumulators in VGPRs: in-place accumulation, no AGPR copies in pipelined loops
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

@@ -1,177 +1,283 @@
-// Prefill-size W4A8 GEMMs: tiles of 64 routes of one expert, operands staged
-// through LDS and shared by a 2 x 2 grid of waves.
+// Prefill-size W4A8 GEMMs: tiles of 64 routes of one expert, operands streamed
+// into an LDS ring by direct global-to-LDS loads and shared by a 2 x 2 grid of
+// waves.
 //
-// Per 128-column k-tile a block stages 8 weight row tiles (8 x 1 KB of FP4 in
-// MFMA lane order + 8 x 64 E8M0 bytes) and the 64 routes' MXFP8 activation
-// slices (64 x 128 bytes + 64 x 4 scale bytes) into one of two LDS buffers
-// while the waves multiply the other.  Wave (wr, wc) owns row tiles 4*wr..+3
-// and routes 32*wc..+31: 8 block-scaled MFMAs per k-tile from 4 weight and 2
-// activation operands.  Each weight byte is read from memory once per 64
-// routes, each activation byte once per 64 (GEMM1) or 128 (GEMM2) outputs.
+// One ring stage holds one 128-column k-tile: 8 weight row tiles (8 x 1 KB of
+// FP4 in MFMA lane order), the 64 routes' MXFP8 activation slices (8 blocks of
+// 8 rows x 128 bytes, 16-byte chunks XOR-swizzled so that MFMA operand reads
+// spread over the LDS banks) and the scales of both (As: 8 x 64 bytes, Bs:
+// 64 x 4 bytes).  Every wave issues the same five loads per stage (two weight
+// tiles, two activation blocks, one 256-byte scale chunk), so "all but the
+// newest n stages have landed" is one s_waitcnt vmcnt(5 n) per wave followed
+// by a barrier.  Each wave reads its operands of k-tile kt+1 from LDS while its
+// MFMAs of k-tile kt run, and the ring keeps its other stages in flight.
 //
-//   k_pf_gemm1_a8  grid (N/64 intermediate blocks, tiles): up/gate GEMMs over K,
-//                  clamped SwiGLU and MXFP8 requantisation of 64 intermediate
+// Wave (wr, wc) owns row tiles 4 wr .. +3 and routes 32 wc .. +31: 8 block-
+// scaled MFMAs per k-tile.
+//
+// Blocks are numbered XCD-major: the hardware hands workgroup b to XCD b % 8,
+// so logical work item (b % 8) * per + b / 8 puts a contiguous run of
+// (tile, column block) items on each XCD, in order.  The up/gate GEMM orders
+// items column-block-major: all tiles of a hot expert then run at once on one
+// XCD against the same weight slab, which is read once, while the activations
+// (tens of MB, re-read once per column block) stay in the last-level cache.
+// The down GEMM orders them tile-major: the 56-odd column blocks of a tile
+// share its activation rows in L2, and one expert's w2 (2 MB) stays in L2
+// across its consecutive tiles.
+//
+//   k_pf_gemm1_a8  items (tile, 64-column intermediate block): up/gate GEMMs over
+//                  K, clamped SwiGLU and MXFP8 requantisation of 64 intermediate
 //                  columns of 64 routes.
-//   k_pf_gemm2_a8  grid (K/128 output blocks, tiles): down GEMM over N; the
-//                  accumulators are transposed through LDS so each combine
-//                  store (fp32 atomic or bf16 route-buffer write) covers
-//                  consecutive output columns of one route.
+//   k_pf_gemm2_a8  items (tile, 128-column output block): down GEMM over N with
+//                  the activations as the MFMA's A operand, so each lane holds
+//                  16 consecutive output columns' worth of one route per
+//                  instruction; combine straight from the accumulators (fp32
+//                  atomics, or bf16 route-buffer rows).
 #include "moe_device.h"
 
 namespace moe {
 
 constexpr int kPfRowTiles = 8;   // weight row tiles per block
-constexpr int kPfBStride = 144;  // LDS bytes per activation row (128 + 16: rows on different banks)
+constexpr int kPfStages1 = 4;    // LDS ring depth (k-tiles), up/gate GEMM
+constexpr int kPfStages2 = 3;    // down GEMM: short k-loops, more blocks per CU
+constexpr int kPfLoadsPerStage = 5;
 
 struct PfStage {
-  uint8_t A[kPfRowTiles][1024];
-  uint8_t As[kPfRowTiles][64];
-  uint8_t B[kPfTileRows][kPfBStride];
-  uint8_t Bs[kPfTileRows][4];
+  uint8_t A[kPfRowTiles][1024];   // weight row tiles, MFMA lane order
+  uint8_t B[8][1024];             // activation rows 8b .. 8b+7 of block b, swizzled 16-byte chunks
+  uint8_t S[1024];                // As [8][64] | Bs [64][4] | spare
 };
 
-union PfLds {
-  PfStage st[2];
-  float tr[kPfTileRows][132];   // GEMM2 epilogue: [route][128 columns + pad]
+template <int ST>
+struct __attribute__((aligned(16))) PfLds {
+  PfStage st[ST];
 };
 
-// Registers of one thread's share of a stage: 2 weight chunks, 1 scale dword,
-// 2 activation chunks, 1 activation-scale dword.
-struct PfRegs {
-  v4i a[2], b[2];
-  uint32_t as, bs;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS loads: lane i of the wave writes lds + i * bytes.
+__device__ __forceinline__ void dma16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `stages` ring stages issued by this wave are in flight.
+__device__ __forceinline__ void wait_stages(int stages) {
+  if (stages >= 3) wait_vm<3 * kPfLoadsPerStage>();
+  else if (stages == 2) wait_vm<2 * kPfLoadsPerStage>();
+  else if (stages == 1) wait_vm<kPfLoadsPerStage>();
+  else wait_vm<0>();
+}
+
+// LDS chunk (0..63) of activation row r8 = row % 8, 16-byte part p, inside its block.
+__device__ __forceinline__ int pf_slot(int r8, int p) { return r8 * 8 + (p ^ r8); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// One block's work item: tile of the tier's tile table and column block.
+struct PfWork {
+  int valid, e, p0, rows, sub;
 };
 
-// Global -> registers.  Weight chunk q = tid + 256 j: row tile q / 64, lane q % 64.
-// Activation chunk q: route row q / 8, 16-byte part q % 8 (parts at or past
-// n_valid_parts of a partial k-tile are zero).
-__device__ __forceinline__ void pf_load(PfRegs &R, const Buf &wb, const Buf &sb, uint32_t w0, uint32_t wstep,
-                                        uint32_t s0, uint32_t sstep, int kt, const Buf &xb, const Buf &xsb,
-                                        const uint32_t *xrow_off, const uint32_t *xsrow_off, const bool *rvalid,
-                                        int kbytes, int kscales, int tid) {
+__device__ __forceinline__ PfWork pf_work(const GemmArgs &a, int nsub, bool sub_major) {
+  PfWork w;
+  const int tbeg = a.tier_tiles[2 * a.tier], tend = a.tier_tiles[2 * a.tier + 1];
+  const int items = (tend - tbeg) * nsub, per = (items + 7) >> 3;
+  const int b = blockIdx.x, slot = b >> 3, item = (b & 7) * per + slot;
+  w.valid = slot < per && item < items;
+  if (!w.valid) return w;
+  const int ntiles = tend - tbeg;
+  const int t = sub_major ? item % ntiles : item / nsub;
+  w.sub = sub_major ? item / ntiles : item - t * nsub;
+  const int u = a.tile_u[tbeg + t];
+  w.e = u - a.u_base;
+  w.p0 = a.off[u] + a.tile_row0[tbeg + t];
+  w.rows = min(a.tile_rows, a.off[u + 1] - w.p0);
+  return w;
+}
+
+struct PfSrc {
+  const uint8_t *wbase, *sbase;   // row tile rt, k-tile kt: wbase + rt * wstep + kt * 1024 (scales: 64 per k-tile)
+  size_t wstep, sstep;
+  const uint8_t *brow[2];         // this lane's activation rows of its two B blocks
+  const uint8_t *bsrow;           // activation scale row of route (lane)
+  int kbytes;                     // reduction length (bytes of one activation row)
+};
+
+// The five loads of wave w for k-tile kt into stage S.  Lanes whose data lies
+// past the reduction length (a partial last k-tile) load from a valid address
+// instead; the MFMA step zeroes those activation bytes and both scales there.
+__device__ __forceinline__ void pf_issue(PfStage &S, const PfSrc &src, int kt, int w, int l) {
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const uint32_t q = tid + 256 * j, rt = q >> 6, ln = q & 63;
-    // lanes of a 32-column group past the reduction length hold no data (partial k-tile)
-    const bool in = (uint32_t)kt * 128 + 32 * (ln >> 4) < (uint32_t)kbytes;
-    R.a[j] = in ? buf_load16(wb, (uint32_t)kt * 1024u + ln * 16u, w0 + rt * wstep) : v4i{0, 0, 0, 0};
-  }
-  if (tid < 128) {   // 8 row tiles x 64 scale bytes = 128 dwords (dword-aligned: K/2 and N/2 are multiples of 16)
-    const uint32_t rt = tid >> 4, d = tid & 15;
-    const bool in = (uint32_t)kt * 4 + (d >> 2) < (uint32_t)kscales;   // the 4 lanes of dword d share one group
-    R.as = in ? buf_load4(sb, (uint32_t)kt * 64u + 4 * d, s0 + rt * sstep) : 0u;
+  for (int j = 0; j < 2; j++) {   // weight row tiles 2w + j
+    const int rt = 2 * w + j;
+    const bool in = (kt * 4 + (l >> 4)) * 32 < src.kbytes;
+    dma16(src.wbase + rt * src.wstep + (in ? (size_t)kt * 1024 + l * 16 : 0), &S.A[rt][0]);
   }
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int q = tid + 256 * j, part = q & 7;   // row q / 8 is the row of xrow_off[j]
-    const bool in = rvalid[j] && kt * 128 + part * 16 < kbytes;
-    R.b[j] = in ? buf_load16(xb, xrow_off[j] + (uint32_t)(kt * 128 + part * 16), 0) : v4i{0, 0, 0, 0};
+  for (int j = 0; j < 2; j++) {   // activation blocks 2w + j: lane l -> row l / 8, its chunk slot l
+    const int r8 = l >> 3, part = (l & 7) ^ r8, off = kt * 128 + part * 16;
+    dma16(src.brow[j] + (off < src.kbytes ? off : 0), &S.B[2 * w + j][0]);
   }
-  if (tid < 64) {
-    uint32_t v = 0;
-    if (rvalid[2]) {
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        if (kt * 4 + j < kscales) v |= buf_load1(xsb, xsrow_off[0] + (uint32_t)(kt * 4 + j), 0) << (8 * j);
-    }
-    R.bs = v;
+  if (w < 2) {   // As row tiles 4w .. 4w+3: lane l -> row tile 4w + l / 16, dword l % 16
+    const int rt = 4 * w + (l >> 4), d = l & 15;
+    const bool in = (kt * 4 + (d >> 2)) * 32 < src.kbytes;
+    dma4(src.sbase + rt * src.sstep + (in ? (size_t)kt * 64 + 4 * d : 0), &S.S[256 * w]);
+  } else {       // Bs (wave 3 fills the spare slot to keep the per-wave load count equal)
+    dma4(src.bsrow + 4 * kt, &S.S[w == 2 ? 512 : 768]);
   }
 }
 
-__device__ __forceinline__ void pf_store(PfStage &S, const PfRegs &R, int tid) {
-#pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int q = tid + 256 * j;
-    *(v4i *)&S.A[q >> 6][(q & 63) * 16] = R.a[j];
-  }
-  if (tid < 128) *(uint32_t *)&S.As[tid >> 4][(tid & 15) * 4] = R.as;
-#pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int q = tid + 256 * j;
-    *(v4i *)&S.B[q >> 3][(q & 7) * 16] = R.b[j];
-  }
-  if (tid < 64) *(uint32_t *)&S.Bs[tid][0] = R.bs;
+// One wave's operands of a landed stage.  The LDS reads are issued by asm the
+// compiler cannot see into: seen, each would make it wait for every direct-to-
+// LDS load in flight (it cannot tell ring stages apart), emptying the ring at
+// every k-tile.  pf_read issues them; pf_wait waits for them and, taking the
+// registers as operands, keeps every use of them after the wait.
+struct PfOps {
+  v4i a[4];      // weight row tiles 4 wr + q
+  v4i b[4];      // activation chunks: [cb] = columns 16 g .. of route block cb, [2 + cb] = columns 64 + 16 g ..
+  int sa[4], sb[2];
+};
+
+__device__ __forceinline__ void pf_read(PfOps &o, const PfStage &S, int wr, int wc, int l) {
+  const int c = l & 15, g = l >> 4, r8 = c & 7;
+  const uint8_t *bblk = &S.B[4 * wc + (c >> 3)][0];
+  const uint32_t va = lds_addr(&S.A[4 * wr][l * 16]), vb0 = lds_addr(bblk + pf_slot(r8, g) * 16),
+                 vb1 = lds_addr(bblk + pf_slot(r8, 4 + g) * 16), vsa = lds_addr(&S.S[4 * wr * 64 + l]),
+                 vsb = lds_addr(&S.S[512 + (32 * wc + c) * 4 + g]);
+  asm volatile(
+      "ds_read_b128 %0, %14\n"
+      "ds_read_b128 %1, %14 offset:1024\n"
+      "ds_read_b128 %2, %14 offset:2048\n"
+      "ds_read_b128 %3, %14 offset:3072\n"
+      "ds_read_b128 %4, %15\n"
+      "ds_read_b128 %5, %15 offset:2048\n"
+      "ds_read_b128 %6, %16\n"
+      "ds_read_b128 %7, %16 offset:2048\n"
+      "ds_read_u8 %8, %17\n"
+      "ds_read_u8 %9, %17 offset:64\n"
+      "ds_read_u8 %10, %17 offset:128\n"
+      "ds_read_u8 %11, %17 offset:192\n"
+      "ds_read_u8 %12, %18\n"
+      "ds_read_u8 %13, %18 offset:64"
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.b[0]), "=&v"(o.b[1]), "=&v"(o.b[2]),
+        "=&v"(o.b[3]), "=&v"(o.sa[0]), "=&v"(o.sa[1]), "=&v"(o.sa[2]), "=&v"(o.sa[3]), "=&v"(o.sb[0]), "=&v"(o.sb[1])
+      : "v"(va), "v"(vb0), "v"(vb1), "v"(vsa), "v"(vsb)
+      : "memory");
 }
 
-// 8 MFMAs of wave (wr, wc) on one staged k-tile.
-__device__ __forceinline__ void pf_mfma(const PfStage &S, int wr, int wc, int l, v4f (*acc)[2]) {
-  const int c = l & 15, g = l >> 4;
+__device__ __forceinline__ void pf_wait(PfOps &o) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(o.a[0]), "+v"(o.a[1]), "+v"(o.a[2]), "+v"(o.a[3]), "+v"(o.b[0]), "+v"(o.b[1]), "+v"(o.b[2]),
+                 "+v"(o.b[3]), "+v"(o.sa[0]), "+v"(o.sa[1]), "+v"(o.sa[2]), "+v"(o.sa[3]), "+v"(o.sb[0]), "+v"(o.sb[1])
+               :
+               : "memory");
+}
+
+// 8 MFMAs of one k-tile.  Past the reduction length (a partial last k-tile)
+// the activation bytes are zeroed and both scales set to 2^-127, so the
+// products there are exact zeros whatever the stage held.  SWAP: activations
+// as the A operand (accumulator lane = output column, elements = 4 routes).
+template <bool SWAP>
+__device__ __forceinline__ void pf_mma(const PfOps &o, int kt, int kbytes, int l, v4f (*acc)[2]) {
+  const int g = l >> 4;
+  const bool in0 = kt * 128 + 16 * g < kbytes, in1 = kt * 128 + 64 + 16 * g < kbytes;
+  const bool gin = (kt * 4 + g) * 32 < kbytes;   // 32-column group g of this k-tile exists
   v8i bop[2];
-  int sb[2];
 #pragma unroll
   for (int cb = 0; cb < 2; cb++) {
-    const int row = 32 * wc + 16 * cb + c;
-    const v4i b0 = *(const v4i *)&S.B[row][16 * g];
-    const v4i b1 = *(const v4i *)&S.B[row][64 + 16 * g];
+    const v4i b0 = in0 ? o.b[cb] : v4i{0, 0, 0, 0};
+    const v4i b1 = in1 ? o.b[2 + cb] : v4i{0, 0, 0, 0};
     bop[cb] = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-    sb[cb] = S.Bs[row][g];
   }
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const v4i a = *(const v4i *)&S.A[4 * wr + q][l * 16];
-    const int sa = S.As[4 * wr + q][l];
+  for (int q = 0; q < 4; q++)
 #pragma unroll
-    for (int cb = 0; cb < 2; cb++) acc[q][cb] = mfma_fp4_fp8(a, bop[cb], acc[q][cb], sa, sb[cb]);
-  }
+    for (int cb = 0; cb < 2; cb++) {
+      const int sa = gin ? o.sa[q] : 0, sb = gin ? o.sb[cb] : 0;
+      if (SWAP)
+        acc[q][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bop[cb], fp4_operand(o.a[q]), acc[q][cb], 0, 4,
+                                                                      0, sb, 0, sa);
+      else
+        acc[q][cb] = mfma_fp4_fp8(o.a[q], bop[cb], acc[q][cb], sa, sb);
+    }
 }
 
-// The k-loop shared by both GEMMs: double-buffered LDS stages, one barrier per
-// k-tile.  kbytes / kscales: reduction length in bytes of activation / scales.
-__device__ __forceinline__ void pf_kloop(PfLds &L, const Buf &wb, const Buf &sb, uint32_t w0, uint32_t wstep,
-                                         uint32_t s0, uint32_t sstep, const Buf &xb, const Buf &xsb,
-                                         const uint32_t *xrow_off, const uint32_t *xsrow_off, const bool *rvalid,
-                                         int kbytes, int kscales, v4f (*acc)[2]) {
+// One k-tile: operands of kt are in `cur` (reads issued one k-tile earlier).
+template <bool SWAP, int ST>
+__device__ __forceinline__ void pf_step(PfLds<ST> &L, const PfSrc &src, int kt, int nkt, PfOps &cur, PfOps &nxt,
+                                        v4f (*acc)[2]) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wr = w >> 1, wc = w & 1;
-  const int nkt = (kbytes + 127) / 128;
-  PfRegs R;
-  pf_load(R, wb, sb, w0, wstep, s0, sstep, 0, xb, xsb, xrow_off, xsrow_off, rvalid, kbytes, kscales, tid);
-  pf_store(L.st[0], R, tid);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; kt++) {
-    const bool more = kt + 1 < nkt;
-    if (more) pf_load(R, wb, sb, w0, wstep, s0, sstep, kt + 1, xb, xsb, xrow_off, xsrow_off, rvalid, kbytes, kscales, tid);
-    pf_mfma(L.st[kt & 1], wr, wc, l, acc);
-    if (more) pf_store(L.st[(kt + 1) & 1], R, tid);
-    __syncthreads();
-  }
+  pf_wait(cur);
+  wait_stages(min(ST - 2, nkt - 2 - kt));   // stage kt + 1 has landed
+  __builtin_amdgcn_s_barrier();                   // ... for every wave, and no wave reads stage kt any more
+  if (kt + ST < nkt) pf_issue(L.st[kt % ST], src, kt + ST, w, l);
+  if (kt + 1 < nkt) pf_read(nxt, L.st[(kt + 1) % ST], wr, wc, l);
+  pf_mma<SWAP>(cur, kt, src.kbytes, l, acc);
 }
 
-// ---------------------------------------------------------------- GEMM1
-__global__ __launch_bounds__(256) void k_pf_gemm1_a8(GemmArgs a) {
-  __shared__ PfLds L;
-  const TileInfo ti = tile_info(a);
-  if (!ti.valid) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
-  const int K = a.K, N = a.N, hb = blockIdx.x;
-  const size_t rt_bytes = (size_t)16 * (K / 2), rt_scales = (size_t)16 * (K / 32);
-  const Buf wb = make_buf(a.w13 + (size_t)ti.e * (2 * N) * (K / 2), (uint32_t)((size_t)(2 * N) * (K / 2)));
-  const Buf sb = make_buf(a.s13 + (size_t)ti.e * (2 * N) * (K / 32), (uint32_t)((size_t)(2 * N) * (K / 32)));
-  // activation rows of this thread's staging chunks (rows tid/8 and tid/8 + 32) and scale row (tid < 64)
-  const int T = a.T;
-  const Buf xb = make_buf(a.xq, (uint32_t)((size_t)T * K));
-  const Buf xsb = make_buf(a.xs, (uint32_t)((size_t)T * (K / 32)));
-  uint32_t xrow_off[2], xsrow_off[1];
-  bool rvalid[3];
+// The k-loop of both GEMMs.
+template <bool SWAP, int ST>
+__device__ __forceinline__ void pf_kloop(PfLds<ST> &L, const PfSrc &src, v4f (*acc)[2]) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wr = w >> 1, wc = w & 1;
+  const int nkt = (src.kbytes + 127) / 128;
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int row = (tid + 256 * j) >> 3;
-    rvalid[j] = row < ti.rows;
-    const int t = rvalid[j] ? a.perm[ti.p0 + row] / a.topk : 0;
-    xrow_off[j] = (uint32_t)((size_t)t * K);
+  for (int s = 0; s < ST; s++)
+    if (s < nkt) pf_issue(L.st[s], src, s, w, l);
+  wait_stages(min(ST - 1, nkt - 1));   // stage 0 has landed
+  __builtin_amdgcn_s_barrier();
+  PfOps r0, r1;
+  pf_read(r0, L.st[0], wr, wc, l);
+  for (int kt = 0; kt + 1 < nkt; kt += 2) {
+    pf_step<SWAP, ST>(L, src, kt, nkt, r0, r1, acc);
+    pf_step<SWAP, ST>(L, src, kt + 1, nkt, r1, r0, acc);
   }
-  {
-    rvalid[2] = tid < 64 && tid < ti.rows;
-    const int t = rvalid[2] ? a.perm[ti.p0 + tid] / a.topk : 0;
-    xsrow_off[0] = (uint32_t)((size_t)t * (K / 32));
-  }
-  v4f acc[4][2];
+  if (nkt & 1) pf_step<SWAP, ST>(L, src, nkt - 1, nkt, r0, r1, acc);
+}
+
+__device__ __forceinline__ void zero_acc(v4f (*acc)[2]) {
 #pragma unroll
   for (int q = 0; q < 4; q++)
 #pragma unroll
     for (int cb = 0; cb < 2; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
-  pf_kloop(L, wb, sb, (uint32_t)((size_t)(8 * hb) * rt_bytes), (uint32_t)rt_bytes, (uint32_t)((size_t)(8 * hb) * rt_scales),
-           (uint32_t)rt_scales, xb, xsb, xrow_off, xsrow_off, rvalid, K, K / 32, acc);
+}
+
+// ---------------------------------------------------------------- GEMM1
+__global__ __launch_bounds__(256) void k_pf_gemm1_a8(GemmArgs a) {
+  __shared__ PfLds<kPfStages1> L;
+  const int K = a.K, N = a.N;
+  const PfWork wk = pf_work(a, N / 64, true);
+  if (!wk.valid) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
+  const int hb = wk.sub;
+  PfSrc src;
+  src.wstep = (size_t)16 * (K / 2);
+  src.sstep = (size_t)16 * (K / 32);
+  src.wbase = a.w13 + (size_t)wk.e * (2 * N) * (K / 2) + (size_t)(8 * hb) * src.wstep;
+  src.sbase = a.s13 + (size_t)wk.e * (2 * N) * (K / 32) + (size_t)(8 * hb) * src.sstep;
+  src.kbytes = K;
+  // rows past the tile read route p0's token; their results are never stored
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int row = 8 * (2 * w + j) + (l >> 3);
+    src.brow[j] = a.xq + (size_t)(a.perm[wk.p0 + (row < wk.rows ? row : 0)] / a.topk) * K;
+  }
+  src.bsrow = a.xs + (size_t)(a.perm[wk.p0 + (l < wk.rows ? l : 0)] / a.topk) * (K / 32);
+  v4f acc[4][2];
+  zero_acc(acc);
+  pf_kloop<false, kPfStages1>(L, src, acc);
   // epilogue: row tiles 4wr + {0,1,2,3} = up/gate of intermediate blocks 4hb + 2wr + {0,1}
+  const int hss = hs_stride(N);
 #pragma unroll
   for (int cb = 0; cb < 2; cb++) {
     float h[8];
@@ -187,91 +293,97 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a8(GemmArgs a) {
     float inv;
     const uint32_t sbyte = mx_scale(amax, &inv);
     const int row = 32 * wc + 16 * cb + c;
-    if (row < ti.rows) {
-      const size_t p = (size_t)(ti.p0 + row);
+    if (row < wk.rows) {
+      const size_t p = (size_t)(wk.p0 + row);
 #pragma unroll
       for (int s = 0; s < 2; s++)
         *(uint32_t *)(a.hq + p * N + 64 * hb + 32 * wr + 16 * s + 4 * g) =
             e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
-      if (g == 0) a.hs[p * hs_stride(N) + 2 * hb + wr] = (uint8_t)sbyte;
+      if (g == 0) a.hs[p * hss + 2 * hb + wr] = (uint8_t)sbyte;
     }
   }
 }
 
 // ---------------------------------------------------------------- GEMM2
 __global__ __launch_bounds__(256) void k_pf_gemm2_a8(GemmArgs a) {
-  __shared__ PfLds L;
-  const TileInfo ti = tile_info(a);
-  if (!ti.valid) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
-  const int K = a.K, N = a.N, ob = blockIdx.x;   // output columns 128 ob .. +127 = w2 row tiles 8 ob .. +7
-  const size_t rt_bytes = (size_t)16 * (N / 2), rt_scales = (size_t)16 * (N / 32);
-  const Buf wb = make_buf(a.w2 + (size_t)ti.e * K * (N / 2), (uint32_t)((size_t)K * (N / 2)));
-  const Buf sb = make_buf(a.s2 + (size_t)ti.e * K * (N / 32), (uint32_t)((size_t)K * (N / 32)));
-  const Buf hb = make_buf(a.hq, (uint32_t)((size_t)(ti.p0 + ti.rows) * N));
-  const Buf hsb = make_buf(a.hs, (uint32_t)((size_t)(ti.p0 + ti.rows) * hs_stride(N)));
-  uint32_t hrow_off[2], hsrow_off[1];
-  bool rvalid[3];
-#pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int row = (tid + 256 * j) >> 3;
-    rvalid[j] = row < ti.rows;
-    hrow_off[j] = (uint32_t)((size_t)(ti.p0 + row) * N);
-  }
-  rvalid[2] = tid < 64 && tid < ti.rows;
-  hsrow_off[0] = (uint32_t)((size_t)(ti.p0 + tid) * hs_stride(N));
-  v4f acc[4][2];
-#pragma unroll
-  for (int q = 0; q < 4; q++)
-#pragma unroll
-    for (int cb = 0; cb < 2; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
-  pf_kloop(L, wb, sb, (uint32_t)((size_t)(8 * ob) * rt_bytes), (uint32_t)rt_bytes, (uint32_t)((size_t)(8 * ob) * rt_scales),
-           (uint32_t)rt_scales, hb, hsb, hrow_off, hsrow_off, rvalid, N, N / 32, acc);
-  // per-row route, token and router weight
+  __shared__ PfLds<kPfStages2> L;
   __shared__ int s_r[kPfTileRows];
   __shared__ float s_w[kPfTileRows];
-  if (tid < ti.rows) {
-    const int r = a.perm[ti.p0 + tid];
+  const int K = a.K, N = a.N;
+  const PfWork wk = pf_work(a, K / 128, false);
+  if (!wk.valid) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
+  const int ob = wk.sub;   // output columns 128 ob .. +127 = w2 row tiles 8 ob .. +7
+  PfSrc src;
+  src.wstep = (size_t)16 * (N / 2);
+  src.sstep = (size_t)16 * (N / 32);
+  src.wbase = a.w2 + (size_t)wk.e * K * (N / 2) + (size_t)(8 * ob) * src.wstep;
+  src.sbase = a.s2 + (size_t)wk.e * K * (N / 32) + (size_t)(8 * ob) * src.sstep;
+  src.kbytes = N;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int row = 8 * (2 * w + j) + (l >> 3);
+    src.brow[j] = a.hq + (size_t)(wk.p0 + (row < wk.rows ? row : 0)) * N;
+  }
+  src.bsrow = a.hs + (size_t)(wk.p0 + (l < wk.rows ? l : 0)) * hs_stride(N);
+  if (tid < wk.rows) {
+    const int r = a.perm[wk.p0 + tid];
     s_r[tid] = r;
     s_w[tid] = a.topk_w[r];
   }
-  // transpose: wave (wr, wc), lane (c, g): columns 64 wr + 16 q + 4 g + i of route 32 wc + 16 cb + c
-#pragma unroll
-  for (int q = 0; q < 4; q++)
+  v4f acc[4][2];
+  zero_acc(acc);
+  pf_kloop<true, kPfStages2>(L, src, acc);
+  __syncthreads();   // s_r / s_w visible
+  // acc[q][cb][i]: route 32 wc + 16 cb + 4 g + i, output column 128 ob + 64 wr + 16 q + c
+  const size_t col = (size_t)128 * ob + 64 * wr + c;
+  if (a.deterministic) {
+    // bf16 route-buffer rows: lanes c, c ^ 1 swap one value so each writes two adjacent columns of one route
+    const bool odd = c & 1;
 #pragma unroll
     for (int cb = 0; cb < 2; cb++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) L.tr[32 * wc + 16 * cb + c][64 * wr + 16 * q + 4 * g + i] = acc[q][cb][i];
-  __syncthreads();
-  const size_t col0 = (size_t)128 * ob;
-  if (a.deterministic) {
-    // bf16 route buffer: 2 columns per thread, 64 routes x 64 column pairs
-    for (int idx = tid; idx < kPfTileRows * 64; idx += 256) {
-      const int row = idx >> 6, cp = idx & 63;
-      if (row >= ti.rows) break;
-      const int r = s_r[row];
-      const float wgt = s_w[row];
-      *(uint32_t *)(a.rb + (size_t)r * K + col0 + 2 * cp) = pack_bf16x2(wgt * L.tr[row][2 * cp], wgt * L.tr[row][2 * cp + 1]);
-    }
+      for (int ip = 0; ip < 2; ip++) {
+        const int row = 32 * wc + 16 * cb + 4 * g + 2 * ip + (odd ? 1 : 0);
+        const bool ok = row < wk.rows;
+        const int r = ok ? s_r[row] : 0;
+        const float wgt = ok ? s_w[row] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const float mine = acc[q][cb][2 * ip + (odd ? 1 : 0)], give = acc[q][cb][2 * ip + (odd ? 0 : 1)];
+          const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
+          const float lo = odd ? got : mine, hi = odd ? mine : got;
+          if (ok) *(uint32_t *)(a.rb + (size_t)r * K + col + 16 * q - (odd ? 1 : 0)) = pack_bf16x2(wgt * lo, wgt * hi);
+        }
+      }
   } else {
-    // fp32 atomics: each wave instruction adds 64 consecutive columns of one route
-    for (int idx = tid; idx < kPfTileRows * 128; idx += 256) {
-      const int row = idx >> 7, col = idx & 127;
-      if (row >= ti.rows) break;
-      atomicAdd(a.out_acc + (size_t)(s_r[row] / a.topk) * K + col0 + col, s_w[row] * L.tr[row][col]);
-    }
+    // fp32 atomics: per instruction 4 routes x 16 consecutive columns
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int row = 32 * wc + 16 * cb + 4 * g + i;
+        if (row < wk.rows) {
+          float *dst = a.out_acc + (size_t)(s_r[row] / a.topk) * K + col;
+          const float wgt = s_w[row];
+#pragma unroll
+          for (int q = 0; q < 4; q++) atomicAdd(dst + 16 * q, wgt * acc[q][cb][i]);
+        }
+      }
   }
 }
 
+static int pf_grid(int grid_tiles, int nsub) { return (grid_tiles * nsub + 7) / 8 * 8; }
+
 hipError_t launch_pf_gemm1(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pf_gemm1_a8, dim3(a.N / 64, grid_tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_pf_gemm1_a8, dim3(pf_grid(grid_tiles, a.N / 64)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pf_gemm2_a8, dim3(a.K / 128, grid_tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_pf_gemm2_a8, dim3(pf_grid(grid_tiles, a.K / 128)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -51,6 +51,15 @@ SMALL = {
                                                           limit=7.0, fmt=I.FMT_MXFP4, e8m0_exp=(-9, -5)), seed=9),
     "nf3_decode": lambda: I.make_problem(I.Config("nf3_decode", T=5, E=40, K=512, N=96, topk=7, limit=None,
                                                   fmt=I.FMT_NF3), seed=10),
+    # prefill-size W4A8 batches (T >= 128, N % 64 == 0): 64-route tiles streamed through
+    # the LDS ring; Zipf-skewed loads give full, ragged and single-tile experts, and
+    # N % 128 == 64 leaves a half k-tile in the down GEMM
+    "prefill_small": lambda: I.make_problem(I.Config("prefill_small", T=160, E=12, K=512, N=192, topk=4, limit=7.0,
+                                                     fmt=I.FMT_MXFP4, e8m0_exp=(-6, -2), zipf_s=1.1,
+                                                     pad_rows=3), seed=11),
+    # one k-tile in the down GEMM (N = 64), two in the up/gate GEMM (K = 256), no clamp
+    "prefill_narrow": lambda: I.make_problem(I.Config("prefill_narrow", T=130, E=3, K=256, N=64, topk=2,
+                                                      limit=None, fmt=I.FMT_MXFP4), seed=12),
 }
 
 
@@ -70,7 +79,8 @@ def _sample_rows(prob, n, seed=0):
 
 
 @pytest.mark.parametrize("name", ["tiny", "mxfp4_ragged", "nvfp4_small", "nf3_small", "hybrid_small",
-                                  "nvfp4_clamped", "hybrid_decode", "decode_many_routes", "nf3_decode"])
+                                  "nvfp4_clamped", "hybrid_decode", "decode_many_routes", "nf3_decode",
+                                  "prefill_small", "prefill_narrow"])
 @pytest.mark.parametrize("deterministic", [False, True])
 def test_small_layers_all_rows(name, deterministic):
     L = layer(name)
