@@ -199,7 +199,7 @@ bool use_decode(const moe_plan_s *p, int T) {
   // W4A8 GEMM2 all routes' MXFP8 rows of the intermediate
   const bool a8 = p->afmt == MOE_A_MXFP8;
   const long row = a8 ? (long)p->K + 16 + p->K / 32 : 2L * (p->K + 8);
-  const long lds2 = a8 ? (long)T * p->topk * (p->N + 16 + moe::hs_stride(p->N)) : 0;
+  const long lds2 = a8 ? (long)moe::dec2_hq_bytes(T * p->topk, p->N) + moe::dec2_hs_bytes(T * p->topk, p->N) : 0;
   const bool lds_ok = row <= 32768 && lds2 <= 49152;
   return T <= moe::kDecodeMaxT && T * p->topk <= moe::kDecodeMaxRoutes && lds_ok;
 }

@@ -20,6 +20,12 @@ enum WFmt { W_MXFP4 = 1, W_NVFP4 = 2, W_NF3 = 3 };
 // multiple of 4, so every row starts 4-byte aligned.
 __host__ __device__ constexpr int hs_stride(int N) { return (N / 32 + 3) & ~3; }
 
+// Dynamic LDS of the W4A8 decode down GEMM: every route's MXFP8 row (stride
+// N + 16) rounded up to whole 1 KB direct-load chunks, then the scale rows
+// (stride hs_stride(N)) rounded up to whole 256-byte chunks.
+__host__ __device__ constexpr int dec2_hq_bytes(int R, int N) { return (R * (N + 16) + 1023) & ~1023; }
+__host__ __device__ constexpr int dec2_hs_bytes(int R, int N) { return (R * hs_stride(N) + 255) & ~255; }
+
 // Route planner: ids -> per-expert counts, offsets, stable permutation, tile table.
 struct RouteArgs {
   const int32_t *ids;

@@ -11,11 +11,13 @@
 //                into LDS once per workgroup (W4A8) or read as bf16 (W4A16);
 //                up/gate GEMMs, clamped SwiGLU and requantisation of h, stored
 //                per route r = t*top_k + j.
-//   k_dec_gemm2  grid (K/16 output row tiles), 8 waves split the experts.
-//                Each wave runs the down GEMM of its experts for 16 output
+//   k_dec_gemm2  grid (K/16 output row tiles), the block's waves split the work.
+//                Each wave runs the down GEMM of its share for 16 output
 //                columns and folds the router-weighted results into per-token
-//                fp32 accumulators; the 8 waves are summed in a fixed order and
+//                fp32 accumulators; the waves are summed in a fixed order and
 //                the bf16 output written.  No atomics: bit-stable run to run.
+//                W4A8 splits (expert, k-tile) items evenly over the waves and
+//                requests every item's weights up front; W4A16 splits experts.
 #include <type_traits>
 
 #include "moe_device.h"
@@ -41,21 +43,34 @@ __device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) 
   return ((unsigned long long)hi << 32) | lo;
 }
 
+// Routes (lanes) whose expert equals this lane's, as a 64-bit mask (0 for a
+// route without one): the AND over the 10 bits of the unified expert index
+// (< kMaxExperts = 1024) of the lanes that agree on that bit.  Ten ballots, no
+// per-route loop.
+__device__ __forceinline__ unsigned long long dec_same(int u) {
+  unsigned long long s = __ballot(u >= 0);
+#pragma unroll
+  for (int b = 0; b < 10; b++) {
+    const bool bit = (u >> b) & 1;
+    const unsigned long long m = __ballot(bit);
+    s &= bit ? m : ~m;
+  }
+  return u >= 0 ? s : 0ull;
+}
+
 // Group d, in order of first occurrence, of the routes sharing one expert:
 // its expert and the mask of its routes (bit r = route r).  Wave-uniform.
 __device__ __forceinline__ bool dec_group(int u, int d, int *gu, unsigned long long *gm) {
-  unsigned long long rem = __ballot(u >= 0);
-  for (int i = 0; rem; i++) {
-    const int leader = __ffsll(rem) - 1;
-    const int lu = __shfl(u, leader);
-    const unsigned long long m = __ballot(u == lu);
+  const int l = threadIdx.x & 63;
+  const unsigned long long same = dec_same(u);
+  unsigned long long f = __ballot(same != 0 && __ffsll(same) - 1 == l);   // first route of each expert
+  for (int i = 0; f; i++, f &= f - 1) {
     if (i == d) {
-      // wave-uniform values: keep them (and every pointer derived from them) scalar
-      *gu = __builtin_amdgcn_readfirstlane(lu);
-      *gm = uniform_u64(m);
+      const int L = __ffsll(f) - 1;
+      *gu = __builtin_amdgcn_readlane(u, L);
+      *gm = __ballot(same != 0 && __ffsll(same) - 1 == L);
       return true;
     }
-    rem &= ~m;
   }
   return false;
 }
@@ -356,6 +371,26 @@ __device__ __forceinline__ void dec_fold(const DecArgs &a, unsigned long long md
   }
 }
 
+// The same fold through a per-wave 16 x 16 fp32 LDS tile: lane (route column
+// c, group g) stores its router-weighted outputs, then lane (token c, group g)
+// adds the rows of its token's routes, slots in order.
+__device__ __forceinline__ void dec_fold_lds(const DecArgs &a, unsigned long long md, int p0, int c, int g,
+                                             const v4f &acc, float wr, float *yb, float *tok) {
+  *(v4f *)(yb + c * 16 + 4 * g) = acc * wr;
+  if (c >= a.T) return;
+  for (int j = 0; j < a.topk; j++) {
+    const int rr = c * a.topk + j;
+    if (rr < 64 && ((md >> rr) & 1ull)) {
+      const int col = __popcll(md & ((1ull << rr) - 1ull)) - p0;
+      if (col >= 0 && col < 16) {
+        const v4f v = *(const v4f *)(yb + col * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; i++) tok[i] += v[i];
+      }
+    }
+  }
+}
+
 // One w2 row tile of one expert: buffer resources of the expert's data and
 // scales and the row tile's wave-uniform offsets.
 struct W2Tile {
@@ -461,67 +496,33 @@ __device__ __forceinline__ void dec_gemm2_wave(const DecArgs &a, const int *gu_s
   }
 }
 
-// grid (K/16 output row tiles); the block's waves split the experts.
-template <bool A8>
-__global__ __launch_bounds__(kDecG2Waves * 64) void k_dec_gemm2(DecArgs a) {
-  extern __shared__ __align__(16) uint8_t dsm2[];
+// W4A16 down GEMM, grid (K/16 output row tiles); the block's waves split the
+// experts (bf16 intermediate rows are read from global memory at MFMA time).
+__global__ __launch_bounds__(kDecG2Waves * 64) void k_dec_gemm2_a16(DecArgs a) {
   __shared__ int gu_s[kDecodeMaxRoutes];
   __shared__ unsigned long long gm_s[kDecodeMaxRoutes];
   __shared__ int ng_s;
   __shared__ float tred[kDecG2Waves][4][64];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
-  const int N = a.N;
   if (w == 0) {
     const int u = dec_route_u(a, l);
-    unsigned long long rem = __ballot(u >= 0);
+    const unsigned long long same = dec_same(u);
+    const int lead = same ? __ffsll(same) - 1 : -1;
     int n = 0;
-    while (rem) {
-      const int leader = __ffsll(rem) - 1;
-      const int lu = __shfl(u, leader);
-      const unsigned long long m = __ballot(u == lu);
+    for (unsigned long long f = __ballot(lead == l); f; f &= f - 1, n++) {
+      const int L = __ffsll(f) - 1;
+      const unsigned long long m = __ballot(lead == L);
       if (l == 0) {
-        gu_s[n] = lu;
+        gu_s[n] = __builtin_amdgcn_readlane(u, L);
         gm_s[n] = m;
       }
-      n++;
-      rem &= ~m;
     }
     if (l == 0) ng_s = n;
   }
-  uint8_t *hq_s = dsm2, *hs_s = dsm2 + (size_t)a.R * (N + 16);
-  if (A8) {   // MXFP8 intermediate rows of every route -> LDS, loads issued first
-    // the host takes this path only when R * (N + 16 + N/32) <= 48 KB, so
-    // R * N / 16 <= 3072 sixteen-byte chunks: three per thread
-    constexpr int kMaxPer = 3;
-    const int nchunk = a.R * (N / 16);
-    v4i tmp[kMaxPer];
-    uint32_t sv = 0;
-    const int nsc = a.R * hs_stride(N);
-#pragma unroll
-    for (int j = 0; j < kMaxPer; j++) {
-      const int i = tid + j * kDecG2Waves * 64;
-      if (i < nchunk) tmp[j] = *(const v4i *)(a.hq + (size_t)i * 16);
-    }
-    if (tid * 4 < nsc) sv = *(const uint32_t *)(a.hs + tid * 4);   // R * hs_stride(N) <= 4 * 1024 bytes
-#pragma unroll
-    for (int j = 0; j < kMaxPer; j++) {
-      const int i = tid + j * kDecG2Waves * 64;
-      if (i < nchunk) {
-        const int r = i / (N / 16), c16 = i - r * (N / 16);
-        *(v4i *)(hq_s + r * (N + 16) + c16 * 16) = tmp[j];
-      }
-    }
-    if (tid * 4 < nsc)
-      for (int b = 0; b < 4 && tid * 4 + b < nsc; b++) hs_s[tid * 4 + b] = (uint8_t)(sv >> (8 * b));
-  }
   __syncthreads();
   float tok[4] = {0.f, 0.f, 0.f, 0.f};
-  if (A8) {
-    dec_gemm2_wave<true, W_MXFP4>(a, gu_s, gm_s, ng_s, hq_s, hs_s, tok);
-  } else {
-    dec_gemm2_wave<false, W_NVFP4>(a, gu_s, gm_s, ng_s, hq_s, hs_s, tok);
-    dec_gemm2_wave<false, W_NF3>(a, gu_s, gm_s, ng_s, hq_s, hs_s, tok);
-  }
+  dec_gemm2_wave<false, W_NVFP4>(a, gu_s, gm_s, ng_s, nullptr, nullptr, tok);
+  dec_gemm2_wave<false, W_NF3>(a, gu_s, gm_s, ng_s, nullptr, nullptr, tok);
 #pragma unroll
   for (int i = 0; i < 4; i++) tred[w][i][l] = tok[i];
   __syncthreads();
@@ -537,6 +538,180 @@ __global__ __launch_bounds__(kDecG2Waves * 64) void k_dec_gemm2(DecArgs a) {
     o.x = pack_bf16x2(s[0], s[1]);
     o.y = pack_bf16x2(s[2], s[3]);
     *(uint2 *)(a.out + (size_t)c * a.K + blockIdx.x * 16 + 4 * g) = o;
+  }
+}
+
+// W4A8 down GEMM, grid (K/16 output row tiles).  The block's work is the list
+// of items (expert group, 16-route pass, k-tile of N) in group-major order; its
+// waves take equal contiguous slices.  A wave streams its items through a ring
+// of kG2Ring register slots: the weights of the next kG2Ring items are always
+// in flight, so every wave keeps its share of HBM busy from the first
+// instruction to the last.  A wave folds its accumulator into per-token sums
+// whenever a run of one (group, pass) ends; the waves' token sums are added in
+// wave order.  The partition depends only on the ids: bit-stable run to run.
+constexpr int kG2Ring = 6;
+constexpr int kDecG2WavesA8 = 8;
+
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane), hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Position in the item list; the expert's weight streams follow the group.
+struct G2Iter {
+  int item, grp, pass, kt, npass;
+  unsigned long long md;
+  Buf wb, sb;
+};
+
+__device__ __forceinline__ void g2_enter_group(G2Iter &it, const DecArgs &a, int gu, unsigned long long gm) {
+  it.md = readlane_u64(gm, it.grp);
+  it.npass = (__popcll(it.md) + 15) / 16;
+  const DecExpert X = dec_expert(a, __builtin_amdgcn_readlane(gu, it.grp));
+  const int groups = a.N / 32;
+  it.wb = make_buf(X.w2 + (size_t)X.e * a.K * groups * 16, (uint32_t)((size_t)a.K * groups * 16));
+  it.sb = make_buf(X.s2 + (size_t)X.e * a.K * groups, (uint32_t)((size_t)a.K * groups));
+}
+
+__device__ __forceinline__ void g2_start(G2Iter &it, const DecArgs &a, int item, int istart, int ng, int nkt, int gu,
+                                         unsigned long long gm) {
+  const int l = threadIdx.x & 63;
+  it.item = item;
+  it.grp = max(0, __popcll(__ballot(l < ng && istart <= item)) - 1);
+  const int rel = item - __builtin_amdgcn_readlane(istart, it.grp);
+  it.pass = rel / nkt;
+  it.kt = rel - it.pass * nkt;
+  g2_enter_group(it, a, gu, gm);
+}
+
+__device__ __forceinline__ void g2_next(G2Iter &it, const DecArgs &a, int ng, int nkt, int gu, unsigned long long gm) {
+  it.item++;
+  if (++it.kt < nkt) return;
+  it.kt = 0;
+  if (++it.pass < it.npass) return;
+  it.pass = 0;
+  if (++it.grp < ng) g2_enter_group(it, a, gu, gm);
+}
+
+__global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t dsm2[];
+  __shared__ float tred[kDecG2WavesA8][4][64];
+  __shared__ float wr_s[kDecodeMaxRoutes];
+  __shared__ __align__(16) float yb[kDecG2WavesA8][256];
+  // wave-uniform values are pinned to scalar registers: derived from them, the
+  // item bounds and weight descriptors stay scalar through the ring's branches
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
+  const int K = a.K, N = a.N, nkt = (N + 127) / 128, groups = N / 32, rt = blockIdx.x;
+  const uint32_t w0 = (uint32_t)((size_t)rt * 16 * groups * 16), s0 = (uint32_t)((size_t)rt * 16 * groups);
+  // group table, one group per lane, in order of first occurrence
+  const int u = dec_route_u(a, l);
+  const unsigned long long same = dec_same(u);
+  const unsigned long long F = __ballot(same != 0 && __ffsll(same) - 1 == l);
+  const int ng = __popcll(F);
+  int leader = 0;
+  {
+    unsigned long long f = F;
+    for (int i = 0; f; i++, f &= f - 1)
+      if (i == l) leader = __ffsll(f) - 1;
+  }
+  const int gu = __shfl(u, leader);
+  const unsigned long long gm = ((unsigned long long)(uint32_t)__shfl((int)(uint32_t)(same >> 32), leader) << 32) |
+                                (uint32_t)__shfl((int)(uint32_t)same, leader);
+  const int nitems = l < ng ? ((__popcll(gm) + 15) / 16) * nkt : 0;
+  int incl = nitems;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (l >= d) incl += v;
+  }
+  const int istart = incl - nitems;
+  const int NI = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  const int per = (NI + kDecG2WavesA8 - 1) / kDecG2WavesA8;
+  const int i0 = min(NI, w * per), i1 = min(NI, i0 + per);
+  // ring of weight k-tiles; items past the slice load out of the buffer's range
+  // (zero, no memory traffic) so every slot issues the same two loads
+  v4i A[kG2Ring];
+  int sa[kG2Ring];
+  G2Iter is;
+  if (i0 < i1) g2_start(is, a, i0, istart, ng, nkt, gu, gm);
+  else is.item = i1;
+  auto issue = [&](int s) {
+    const bool ok = is.item < i1 && is.kt * 128 + 32 * g < N;
+    A[s] = buf_load16(is.wb, ok ? (uint32_t)is.kt * 1024u + (uint32_t)l * 16u : 0x80000000u, w0);
+    sa[s] = buf_load1(is.sb, ok ? (uint32_t)is.kt * 64u + (uint32_t)l : 0x80000000u, s0);
+    if (is.item < i1) g2_next(is, a, ng, nkt, gu, gm);
+  };
+  if (i0 >= i1) {   // no items: the ring's loads still need valid descriptors
+    is.wb = make_buf(a.hq, 0);
+    is.sb = is.wb;
+  }
+#pragma unroll
+  for (int s = 0; s < kG2Ring; s++) issue(s);
+  // every route's MXFP8 intermediate row and scales -> LDS by direct loads
+  // issued behind the ring (1 KB / 256-byte chunks; bytes past the rows read
+  // a valid dummy address), router weights by plain loads
+  uint8_t *hq_s = dsm2, *hs_s = dsm2 + dec2_hq_bytes(a.R, N);
+  {
+    const int rs = N + 16, hss = hs_stride(N);
+    for (int ch = w; ch * 1024 < dec2_hq_bytes(a.R, N); ch += kDecG2WavesA8) {
+      const int pos = ch * 1024 + l * 16, row = pos / rs, col = pos - row * rs;
+      dma16(row < a.R && col < N ? a.hq + (size_t)row * N + col : a.hq, hq_s + ch * 1024);
+    }
+    for (int ch = w; ch * 256 < dec2_hs_bytes(a.R, N); ch += kDecG2WavesA8) {
+      const int pos = ch * 256 + l * 4;
+      dma4(pos < a.R * hss ? a.hs + pos : a.hs, hs_s + ch * 256);
+    }
+    if (tid < a.R) wr_s[tid] = a.topk_w[tid];
+  }
+  __syncthreads();
+  float tok[4] = {0.f, 0.f, 0.f, 0.f};
+  G2Iter ic;
+  if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkt, gu, gm);
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  int r = -1;
+  for (int base = i0; base < i1; base += kG2Ring) {
+#pragma unroll
+    for (int s = 0; s < kG2Ring; s++) {
+      if (base + s < i1) {
+        if (s == 0 || ic.kt == 0 || base + s == i0) {   // route column of this lane in the current run
+          const int col = ic.pass * 16 + c;
+          r = col < __popcll(ic.md) ? nth_bit(ic.md, col) : -1;
+        }
+        const int kb = ic.kt * 128;
+        v4i B0 = v4i{0, 0, 0, 0}, B1 = v4i{0, 0, 0, 0};
+        int sbv = 0;
+        if (r >= 0) {
+          const uint8_t *hrow = hq_s + r * (N + 16);
+          if (kb + 16 * g < N) B0 = *(const v4i *)(hrow + kb + 16 * g);
+          if (kb + 64 + 16 * g < N) B1 = *(const v4i *)(hrow + kb + 64 + 16 * g);
+          if (kb + 32 * g < N) sbv = hs_s[r * hs_stride(N) + kb / 32 + g];
+        }
+        const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
+        acc = mfma_fp4_fp8(A[s], bop, acc, sa[s], sbv);
+        if (ic.kt == nkt - 1 || base + s + 1 == i1) {
+          dec_fold_lds(a, ic.md, ic.pass * 16, c, g, acc, r >= 0 ? wr_s[r] : 0.f, &yb[w][0], tok);
+          acc = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        g2_next(ic, a, ng, nkt, gu, gm);
+      }
+      issue(s);   // the item kG2Ring ahead (out of range past the slice)
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; i++) tred[w][i][l] = tok[i];
+  __syncthreads();
+  if (w == 0 && c < a.T) {
+    float s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      s4[i] = 0.f;
+#pragma unroll
+      for (int v = 0; v < kDecG2WavesA8; v++) s4[i] += tred[v][i][l];
+    }
+    uint2 o;
+    o.x = pack_bf16x2(s4[0], s4[1]);
+    o.y = pack_bf16x2(s4[2], s4[3]);
+    *(uint2 *)(a.out + (size_t)c * K + rt * 16 + 4 * g) = o;
   }
 }
 
@@ -564,9 +739,9 @@ hipError_t launch_decode(int a8, const DecArgs &a, hipStream_t s, hipEvent_t ev_
     e = hipEventRecord(ev_mid, s);
     if (e != hipSuccess) return e;
   }
-  const size_t lds2 = a8 ? (size_t)a.R * (a.N + 16) + (size_t)a.R * hs_stride(a.N) : 0;
-  if (a8) hipLaunchKernelGGL(k_dec_gemm2<true>, g2, dim3(kDecG2Waves * 64), lds2, s, a);
-  else hipLaunchKernelGGL(k_dec_gemm2<false>, g2, dim3(kDecG2Waves * 64), lds2, s, a);
+  const size_t lds2 = a8 ? (size_t)dec2_hq_bytes(a.R, a.N) + dec2_hs_bytes(a.R, a.N) : 0;
+  if (a8) hipLaunchKernelGGL(k_dec_gemm2_a8, g2, dim3(kDecG2WavesA8 * 64), lds2, s, a);
+  else hipLaunchKernelGGL(k_dec_gemm2_a16, g2, dim3(kDecG2Waves * 64), 0, s, a);
   return hipGetLastError();
 }
 

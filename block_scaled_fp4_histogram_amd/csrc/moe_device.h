@@ -150,6 +150,22 @@ __device__ __forceinline__ uint32_t buf_load1(const Buf &b, uint32_t voff, uint3
   return moe_raw_buffer_load_i8(b.r, (int)voff, (int)soff, 0);
 }
 
+// Direct global -> LDS loads: lane i of the wave writes lds + i * bytes (the
+// LDS address is wave-uniform).  They count in vmcnt like any vector load.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void dma16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // MFMA operand of an FP4 weight tile (16 bytes per lane in the low 4 VGPRs).
 __device__ __forceinline__ v8i fp4_operand(v4i a) { return v8i{a[0], a[1], a[2], a[3], 0, 0, 0, 0}; }
 

@@ -53,21 +53,6 @@ struct __attribute__((aligned(16))) PfLds {
   PfStage st[ST];
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Direct global -> LDS loads: lane i of the wave writes lds + i * bytes.
-__device__ __forceinline__ void dma16(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0);
-}
-
-// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // Wait until at most `stages` ring stages issued by this wave are in flight.
 __device__ __forceinline__ void wait_stages(int stages) {
