@@ -20,6 +20,11 @@ enum WFmt { W_MXFP4 = 1, W_NVFP4 = 2, W_NF3 = 3 };
 // multiple of 4, so every row starts 4-byte aligned.
 __host__ __device__ constexpr int hs_stride(int N) { return (N / 32 + 3) & ~3; }
 
+// LDS budget of the decode up/gate GEMM's staged token rows: six MXFP8 rows
+// at K = 7168 (one pass for every expert of an 8-token batch at top-6), and
+// three blocks per CU.
+constexpr int kDecStageBytes = 45056;
+
 // Dynamic LDS of the W4A8 decode down GEMM: every route's MXFP8 row (stride
 // N + 16) rounded up to whole 1 KB direct-load chunks, then the scale rows
 // (stride hs_stride(N)) rounded up to whole 256-byte chunks.
@@ -81,6 +86,16 @@ struct DecTier {
   int fmt, E;
 };
 
+// Expert groups of a decode batch (routes sharing an expert, in order of first
+// occurrence) with the first item of each in the W4A8 down GEMM's item list;
+// written by the up/gate kernel, read by the down kernel.
+struct DecGroups {
+  int ng, nitems;
+  int gu[kDecodeMaxRoutes];
+  int istart[kDecodeMaxRoutes];
+  unsigned long long gm[kDecodeMaxRoutes];
+};
+
 struct DecArgs {
   const int32_t *ids;
   const float *topk_w;
@@ -93,6 +108,7 @@ struct DecArgs {
   uint8_t *hq, *hs;                  // MXFP8 intermediate per route r: [R, N], [R, N/32]
   uint16_t *hb;                      // bf16 intermediate per route r: [R, N]
   uint16_t *out;                     // bf16 [T, K]
+  DecGroups *groups;                 // scratch
 };
 
 int decode_cpass(int K, int a8);

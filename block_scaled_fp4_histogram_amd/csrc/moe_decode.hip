@@ -43,6 +43,11 @@ __device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) 
   return ((unsigned long long)hi << 32) | lo;
 }
 
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane), hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 // Routes (lanes) whose expert equals this lane's, as a 64-bit mask (0 for a
 // route without one): the AND over the 10 bits of the unified expert index
 // (< kMaxExperts = 1024) of the lanes that agree on that bit.  Ten ballots, no
@@ -64,15 +69,20 @@ __device__ __forceinline__ bool dec_group(int u, int d, int *gu, unsigned long l
   const int l = threadIdx.x & 63;
   const unsigned long long same = dec_same(u);
   unsigned long long f = __ballot(same != 0 && __ffsll(same) - 1 == l);   // first route of each expert
-  for (int i = 0; f; i++, f &= f - 1) {
-    if (i == d) {
-      const int L = __ffsll(f) - 1;
-      *gu = __builtin_amdgcn_readlane(u, L);
-      *gm = __ballot(same != 0 && __ffsll(same) - 1 == L);
-      return true;
+  if (d >= __popcll(f)) return false;
+  int L = 0;   // position of the d-th set bit of f, by halving
+#pragma unroll
+  for (int width = 32; width >= 1; width >>= 1) {
+    const int below = __popcll(f & ((1ull << width) - 1ull));
+    if (d >= below) {
+      d -= below;
+      f >>= width;
+      L += width;
     }
   }
-  return false;
+  *gu = __builtin_amdgcn_readlane(u, L);
+  *gm = readlane_u64(same, L);
+  return true;
 }
 
 // Index of the n-th set bit of m (n from 0), or -1.
@@ -323,11 +333,36 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
 // grid (N/32 intermediate blocks, expert slots); the block's 4 waves split K.
 // At decode sizes (~35 experts x N/32 blocks) every block is resident at once
 // with up to 128 VGPRs per lane, so no block waits for a second round.
+// The expert groups and the down GEMM's item offsets (passes of up to 16
+// routes times its k-tiles), for the down kernel.
+__device__ __forceinline__ void dec_write_groups(const DecArgs &a, int u) {
+  const int l = threadIdx.x & 63, nkt2 = (a.N + 127) / 128;
+  const unsigned long long same = dec_same(u);
+  const unsigned long long F = __ballot(same != 0 && __ffsll(same) - 1 == l);
+  int n = 0, items = 0;
+  for (unsigned long long f = F; f; f &= f - 1, n++) {
+    const int L = __ffsll(f) - 1;
+    const unsigned long long m = readlane_u64(same, L);
+    if (l == 0) {
+      a.groups->gu[n] = __builtin_amdgcn_readlane(u, L);
+      a.groups->gm[n] = m;
+      a.groups->istart[n] = items;
+    }
+    items += ((__popcll(m) + 15) / 16) * nkt2;
+  }
+  if (l == 0) {
+    a.groups->ng = n;
+    a.groups->nitems = items;
+  }
+}
+
 __global__ __launch_bounds__(256, 4) void k_dec_gemm1_a8(DecArgs a) {
   extern __shared__ __align__(16) uint8_t dsm[];
   int ud;
   unsigned long long md;
-  if (!dec_group(dec_route_u(a, threadIdx.x & 63), blockIdx.y, &ud, &md)) return;
+  const int u = dec_route_u(a, threadIdx.x & 63);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) dec_write_groups(a, u);
+  if (!dec_group(u, blockIdx.y, &ud, &md)) return;
   dec_gemm1_body<true, W_MXFP4, 4>(a, dec_expert(a, ud), md, dsm);
 }
 
@@ -552,11 +587,6 @@ __global__ __launch_bounds__(kDecG2Waves * 64) void k_dec_gemm2_a16(DecArgs a) {
 constexpr int kG2Ring = 6;
 constexpr int kDecG2WavesA8 = 8;
 
-__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane), hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
-  return ((unsigned long long)hi << 32) | lo;
-}
-
 // Position in the item list; the expert's weight streams follow the group.
 struct G2Iter {
   int item, grp, pass, kt, npass;
@@ -603,29 +633,18 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
   const int K = a.K, N = a.N, nkt = (N + 127) / 128, groups = N / 32, rt = blockIdx.x;
   const uint32_t w0 = (uint32_t)((size_t)rt * 16 * groups * 16), s0 = (uint32_t)((size_t)rt * 16 * groups);
-  // group table, one group per lane, in order of first occurrence
-  const int u = dec_route_u(a, l);
-  const unsigned long long same = dec_same(u);
-  const unsigned long long F = __ballot(same != 0 && __ffsll(same) - 1 == l);
-  const int ng = __popcll(F);
-  int leader = 0;
-  {
-    unsigned long long f = F;
-    for (int i = 0; f; i++, f &= f - 1)
-      if (i == l) leader = __ffsll(f) - 1;
-  }
-  const int gu = __shfl(u, leader);
-  const unsigned long long gm = ((unsigned long long)(uint32_t)__shfl((int)(uint32_t)(same >> 32), leader) << 32) |
-                                (uint32_t)__shfl((int)(uint32_t)same, leader);
-  const int nitems = l < ng ? ((__popcll(gm) + 15) / 16) * nkt : 0;
-  int incl = nitems;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d);
-    if (l >= d) incl += v;
-  }
-  const int istart = incl - nitems;
-  const int NI = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  // expert groups (one per lane) and item offsets, from the up/gate kernel
+  const DecGroups *G = a.groups;
+  const int ng = __builtin_amdgcn_readfirstlane(G->ng), NI = __builtin_amdgcn_readfirstlane(G->nitems);
+  int gu = G->gu[l], istart = G->istart[l];
+  uint32_t gm_lo = (uint32_t)G->gm[l], gm_hi = (uint32_t)(G->gm[l] >> 32);
+  float wv = tid < a.R ? a.topk_w[tid] : 0.f;
+  // the table and router weights are complete here; re-defined by an empty
+  // asm, their registers carry no pending load, so nothing after waits on them
+  wait_vm<0>();
+  asm volatile("" : "+v"(gu), "+v"(istart), "+v"(gm_lo), "+v"(gm_hi), "+v"(wv));
+  const unsigned long long gm = ((unsigned long long)gm_hi << 32) | gm_lo;
+  if (tid < a.R) wr_s[tid] = wv;
   const int per = (NI + kDecG2WavesA8 - 1) / kDecG2WavesA8;
   const int i0 = min(NI, w * per), i1 = min(NI, i0 + per);
   // ring of weight k-tiles; items past the slice load out of the buffer's range
@@ -645,11 +664,9 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
     is.wb = make_buf(a.hq, 0);
     is.sb = is.wb;
   }
-#pragma unroll
-  for (int s = 0; s < kG2Ring; s++) issue(s);
   // every route's MXFP8 intermediate row and scales -> LDS by direct loads
-  // issued behind the ring (1 KB / 256-byte chunks; bytes past the rows read
-  // a valid dummy address), router weights by plain loads
+  // (1 KB / 256-byte chunks; bytes past the rows read a valid dummy address),
+  // issued ahead of the ring
   uint8_t *hq_s = dsm2, *hs_s = dsm2 + dec2_hq_bytes(a.R, N);
   {
     const int rs = N + 16, hss = hs_stride(N);
@@ -661,9 +678,14 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
       const int pos = ch * 256 + l * 4;
       dma4(pos < a.R * hss ? a.hs + pos : a.hs, hs_s + ch * 256);
     }
-    if (tid < a.R) wr_s[tid] = a.topk_w[tid];
   }
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kG2Ring; s++) issue(s);
+  // the staged rows have landed once at most the ring's 2 kG2Ring loads are
+  // outstanding; LDS stores done; then every wave's share is visible
+  wait_vm<2 * kG2Ring>();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
   float tok[4] = {0.f, 0.f, 0.f, 0.f};
   G2Iter ic;
   if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkt, gu, gm);
@@ -717,7 +739,7 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
 
 int decode_cpass(int K, int a8) {
   const int row = a8 ? K + 16 + K / 32 : 2 * (K + 8);
-  return max(1, min(kDecodeMaxT, 32768 / row));
+  return max(1, min(kDecodeMaxT, kDecStageBytes / row));
 }
 
 size_t decode_gemm1_lds(int K, int cpass, int a8) {

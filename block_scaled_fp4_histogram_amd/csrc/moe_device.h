@@ -165,6 +165,8 @@ template <int n>
 __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+// s_waitcnt lgkmcnt(0), other counters untouched.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 
 // MFMA operand of an FP4 weight tile (16 bytes per lane in the low 4 VGPRs).
 __device__ __forceinline__ v8i fp4_operand(v4i a) { return v8i{a[0], a[1], a[2], a[3], 0, 0, 0, 0}; }
