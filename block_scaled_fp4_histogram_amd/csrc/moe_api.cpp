@@ -225,9 +225,8 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ra.E1 = n_tiers > 1 ? tiers[1].experts->E : 0;
   ra.G = (R + moe::kRouteChunk - 1) / moe::kRouteChunk;
   ra.max_tiles = L.max_tiles;
-  // prefill kernels: W4A8 experts only, N % 64 == 0, batches of a prefill rung
-  bool prefill = p->afmt == MOE_A_MXFP8 && p->N % 64 == 0 && T >= moe::kPrefillMinT;
-  for (int i = 0; i < n_tiers; i++) prefill = prefill && tiers[i].experts->wfmt == MOE_W_MXFP4;
+  // prefill kernels (64-route tiles): N % 64 == 0, batches of a prefill rung
+  const bool prefill = p->N % 64 == 0 && T >= moe::kPrefillMinT;
   ra.tile_rows = prefill ? moe::kPfTileRows : moe::kTileRows;
   ra.ru = I32(L.ru);
   ra.lrank = I32(L.lrank);
@@ -297,7 +296,8 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     ga.g13 = xp->g13;
     ga.g2 = xp->g2;
     const int grid_tiles = row_tiles + std::min(xp->E, R);
-    if (prefill) HIP_TRY(moe::launch_pf_gemm1(ga, grid_tiles, s));
+    if (prefill && xp->wfmt == MOE_W_MXFP4) HIP_TRY(moe::launch_pf_gemm1(ga, grid_tiles, s));
+    else if (prefill) HIP_TRY(moe::launch_pf16_gemm1(xp->wfmt, ga, grid_tiles, s));
     else HIP_TRY(moe::launch_gemm1(xp->wfmt, ga, grid_tiles, s));
     u_base += xp->E;
   }
@@ -314,7 +314,8 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     ga.g13 = xp->g13;
     ga.g2 = xp->g2;
     const int grid_tiles = row_tiles + std::min(xp->E, R);
-    if (prefill) HIP_TRY(moe::launch_pf_gemm2(ga, grid_tiles, s));
+    if (prefill && xp->wfmt == MOE_W_MXFP4) HIP_TRY(moe::launch_pf_gemm2(ga, grid_tiles, s));
+    else if (prefill) HIP_TRY(moe::launch_pf16_gemm2(xp->wfmt, ga, grid_tiles, s));
     else HIP_TRY(moe::launch_gemm2(xp->wfmt, ga, grid_tiles, s));
     u_base += xp->E;
   }

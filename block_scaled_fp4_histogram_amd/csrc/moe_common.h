@@ -121,6 +121,8 @@ hipError_t launch_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t
 // Prefill kernels (64-route tiles, LDS-staged operands); W4A8 and N % 64 == 0.
 hipError_t launch_pf_gemm1(const GemmArgs &a, int grid_tiles, hipStream_t s);
 hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s);
+hipError_t launch_pf16_gemm1(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s);
+hipError_t launch_pf16_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s);
 hipError_t launch_finalize(int deterministic, const float *out_acc, const uint16_t *rb, const int32_t *inv,
                            int T, int K, int topk, uint16_t *out, hipStream_t s);
 hipError_t launch_quant_bf16(const uint16_t *x, long rows, int cols, uint8_t *q, uint8_t *sc, hipStream_t s);

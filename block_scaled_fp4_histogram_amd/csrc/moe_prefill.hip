@@ -237,6 +237,50 @@ __device__ __forceinline__ void zero_acc(v4f (*acc)[2]) {
     for (int cb = 0; cb < 2; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
 }
 
+// Down-GEMM combine from accumulators in the swapped layout: acc[q][cb][i] is
+// route 32 wc + 16 cb + 4 g + i (tile row), output column col + 16 q; s_r, s_w
+// hold each tile row's route and its router weight (times the expert's global
+// scale).  Deterministic mode writes bf16 route-buffer rows (lanes c, c ^ 1
+// swap one value so each stores two adjacent columns of one route); atomic mode
+// adds fp32 into the token accumulator, 4 routes x 16 consecutive columns per
+// instruction.
+__device__ __forceinline__ void pf_combine(const GemmArgs &a, const PfWork &wk, v4f (*acc)[2], const int *s_r,
+                                           const float *s_w, size_t col, int wc, int c, int g) {
+  const int K = a.K;
+  if (a.deterministic) {
+    const bool odd = c & 1;
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+      for (int ip = 0; ip < 2; ip++) {
+        const int row = 32 * wc + 16 * cb + 4 * g + 2 * ip + (odd ? 1 : 0);
+        const bool ok = row < wk.rows;
+        const int r = ok ? s_r[row] : 0;
+        const float wgt = ok ? s_w[row] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const float mine = acc[q][cb][2 * ip + (odd ? 1 : 0)], give = acc[q][cb][2 * ip + (odd ? 0 : 1)];
+          const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
+          const float lo = odd ? got : mine, hi = odd ? mine : got;
+          if (ok) *(uint32_t *)(a.rb + (size_t)r * K + col + 16 * q - (odd ? 1 : 0)) = pack_bf16x2(wgt * lo, wgt * hi);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int row = 32 * wc + 16 * cb + 4 * g + i;
+        if (row < wk.rows) {
+          float *dst = a.out_acc + (size_t)(s_r[row] / a.topk) * K + col;
+          const float wgt = s_w[row];
+#pragma unroll
+          for (int q = 0; q < 4; q++) atomicAdd(dst + 16 * q, wgt * acc[q][cb][i]);
+        }
+      }
+  }
+}
+
 // ---------------------------------------------------------------- GEMM1
 __global__ __launch_bounds__(256) void k_pf_gemm1_a8(GemmArgs a) {
   __shared__ PfLds<kPfStages1> L;
@@ -320,42 +364,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a8(GemmArgs a) {
   zero_acc(acc);
   pf_kloop<true, kPfStages2>(L, src, acc);
   __syncthreads();   // s_r / s_w visible
-  // acc[q][cb][i]: route 32 wc + 16 cb + 4 g + i, output column 128 ob + 64 wr + 16 q + c
-  const size_t col = (size_t)128 * ob + 64 * wr + c;
-  if (a.deterministic) {
-    // bf16 route-buffer rows: lanes c, c ^ 1 swap one value so each writes two adjacent columns of one route
-    const bool odd = c & 1;
-#pragma unroll
-    for (int cb = 0; cb < 2; cb++)
-#pragma unroll
-      for (int ip = 0; ip < 2; ip++) {
-        const int row = 32 * wc + 16 * cb + 4 * g + 2 * ip + (odd ? 1 : 0);
-        const bool ok = row < wk.rows;
-        const int r = ok ? s_r[row] : 0;
-        const float wgt = ok ? s_w[row] : 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const float mine = acc[q][cb][2 * ip + (odd ? 1 : 0)], give = acc[q][cb][2 * ip + (odd ? 0 : 1)];
-          const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
-          const float lo = odd ? got : mine, hi = odd ? mine : got;
-          if (ok) *(uint32_t *)(a.rb + (size_t)r * K + col + 16 * q - (odd ? 1 : 0)) = pack_bf16x2(wgt * lo, wgt * hi);
-        }
-      }
-  } else {
-    // fp32 atomics: per instruction 4 routes x 16 consecutive columns
-#pragma unroll
-    for (int cb = 0; cb < 2; cb++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int row = 32 * wc + 16 * cb + 4 * g + i;
-        if (row < wk.rows) {
-          float *dst = a.out_acc + (size_t)(s_r[row] / a.topk) * K + col;
-          const float wgt = s_w[row];
-#pragma unroll
-          for (int q = 0; q < 4; q++) atomicAdd(dst + 16 * q, wgt * acc[q][cb][i]);
-        }
-      }
-  }
+  pf_combine(a, wk, acc, s_r, s_w, (size_t)128 * ob + 64 * wr + c, wc, c, g);
 }
 
 static int pf_grid(int grid_tiles, int nsub) { return (grid_tiles * nsub + 7) / 8 * 8; }
@@ -370,6 +379,393 @@ hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_pf_gemm2_a8, dim3(pf_grid(grid_tiles, a.K / 128)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+// ================================================================ W4A16 / W3A16
+//
+// The same 64-route tiles, 2 x 2 waves and LDS ring for NVFP4 and NF3 experts
+// with bf16 activations.  A ring stage holds 8 weight row tiles of one
+// 128-column k-tile in MFMA lane order (16 / 12 bytes and 2 / 1 scale bytes per
+// lane) and the 64 routes' bf16 activation slices (256 bytes each, 16-byte
+// chunks XOR-swizzled by row % 16).  Each wave dequantises its 4 row tiles one
+// 8-column step at a time (E2M1 x E4M3, or NF3 codebook x E4M3, to bf16; exact
+// for E2M1) and feeds bf16 MFMAs: 4 steps x 4 row tiles x 2 route blocks per
+// k-tile.  Every wave issues eight loads per stage.
+namespace {
+
+constexpr int kPf16Stages = 3;
+
+// Direct-to-LDS loads of one wave per stage: NVFP4 2 weight tiles (16 bytes a
+// lane) + 1 scale chunk + 4 activation chunks; NF3 6 dword loads for 2 weight
+// tiles (768 bytes each) + 1 scale chunk + 4 activation chunks.  Loads narrower
+// than a dword are not used: they would leave 4-byte lane slots in LDS.
+template <int WF>
+struct Pf16Loads {
+  static constexpr int n = (WF == W_NVFP4) ? 7 : 11;
+};
+
+template <int WF>
+struct Pf16Stage {
+  static constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  uint8_t A[kPfRowTiles][64 * U];
+  uint8_t AS[kPfRowTiles][64 * SU];
+  uint8_t spare[256];   // NF3: landing slot of the scale loads of waves 2, 3
+  uint8_t B[kPfTileRows][256];
+};
+
+template <int WF>
+struct __attribute__((aligned(16))) Pf16Lds {
+  Pf16Stage<WF> st[kPf16Stages];
+};
+
+template <int WF>
+__device__ __forceinline__ void wait16_stages(int stages) {
+  constexpr int n = Pf16Loads<WF>::n;
+  if (stages >= 2) wait_vm<2 * n>();
+  else if (stages == 1) wait_vm<n>();
+  else wait_vm<0>();
+}
+
+struct Pf16Src {
+  const uint8_t *wbase, *sbase;   // row tile rt, k-tile kt: wbase + rt * wstep + kt * 64 U (scales: 64 SU)
+  size_t wstep, sstep;
+  const uint16_t *brow[4];        // this lane's activation rows of its four B chunks
+  int kcols;                      // reduction length (columns)
+};
+
+// The loads of wave w for k-tile kt: weight row tiles 2w, 2w+1 (NVFP4: one
+// 16-byte load each; NF3: three dword loads of 256 bytes each), one dword load
+// of scales (NVFP4: row tiles 2w, 2w+1; NF3: waves 0, 1 row tiles 4w .. 4w+3,
+// waves 2, 3 a spare slot), activation chunks 4w .. 4w+3 (1 KB each: 4 routes x
+// 256 bytes; lane l -> route 4j + l/16, LDS slot l % 16 holding global chunk
+// slot ^ route%16).  Lanes past the reduction length load from a valid address.
+template <int WF>
+__device__ __forceinline__ void pf16_issue(Pf16Stage<WF> &S, const Pf16Src &src, int kt, int w, int l) {
+  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  if constexpr (WF == W_NVFP4) {
+    const bool in = kt * 128 + 32 * (l >> 4) < src.kcols;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int rt = 2 * w + j;
+      dma16(src.wbase + rt * src.wstep + (in ? (size_t)kt * 64 * U + l * U : 0), &S.A[rt][0]);
+    }
+    // dword d of row tile 2w + l/32 holds the scales of MFMA lanes 2d, 2d + 1
+    const int rt = 2 * w + (l >> 5), d = l & 31;
+    const bool ins = kt * 128 + 32 * ((2 * d) >> 4) < src.kcols;
+    dma4(src.sbase + rt * src.sstep + (ins ? (size_t)kt * 64 * SU + 4 * d : 0), &S.AS[2 * w][0]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int rt = 2 * w + j;
+#pragma unroll
+      for (int m = 0; m < 3; m++) {   // bytes 256 m + 4 l of the row tile's 768-byte k-tile: MFMA lane (256 m + 4 l) / 12
+        const int lane = (256 * m + 4 * l) / 12;
+        const bool in = kt * 128 + 32 * (lane >> 4) < src.kcols;
+        dma4(src.wbase + rt * src.wstep + (in ? (size_t)kt * 64 * U + 256 * m + 4 * l : 0), &S.A[rt][256 * m]);
+      }
+    }
+    if (w < 2) {   // dword d of row tile 4w + l/16 holds the scales of MFMA lanes 4d .. 4d + 3
+      const int rt = 4 * w + (l >> 4), d = l & 15;
+      const bool ins = kt * 128 + 32 * ((4 * d) >> 4) < src.kcols;
+      dma4(src.sbase + rt * src.sstep + (ins ? (size_t)kt * 64 * SU + 4 * d : 0), &S.AS[4 * w][0]);
+    } else {
+      dma4(src.sbase, &S.spare[0]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int r = 4 * (4 * w + j) + (l >> 4), cg = (l & 15) ^ (r & 15), col = kt * 128 + 8 * cg;
+    dma16(src.brow[j] + (col < src.kcols ? col : 0), &S.B[4 * (4 * w + j)][0]);
+  }
+}
+
+template <int WF>
+struct Pf16Ops {
+  uint32_t a[4][4];   // row tile q: NVFP4 4 dwords, NF3 3 dwords (+1 unused)
+  int sc[4];
+  v4i b[2][4];        // route block cb, step s
+};
+
+// LDS reads of one wave's operands (asm: invisible to the compiler's
+// direct-to-LDS bookkeeping, as for the W4A8 kernels); pf16_wait completes them.
+template <int WF>
+__device__ __forceinline__ void pf16_read(Pf16Ops<WF> &o, const Pf16Stage<WF> &S, int wr, int wc, int l) {
+  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  const int c = l & 15, g = l >> 4;
+  const uint32_t va = lds_addr(&S.A[4 * wr][l * U]), vs = lds_addr(&S.AS[4 * wr][l * SU]);
+  const uint8_t *brow = &S.B[32 * wc + c][0];   // + 16 rows for cb = 1
+  uint32_t vb[4];
+#pragma unroll
+  for (int s = 0; s < 4; s++) vb[s] = lds_addr(brow + 16 * ((4 * g + s) ^ c));
+  if constexpr (WF == W_NVFP4) {
+    v4i a0, a1, a2, a3;
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:1024\n"
+        "ds_read_b128 %2, %8 offset:2048\n"
+        "ds_read_b128 %3, %8 offset:3072\n"
+        "ds_read_u16 %4, %9\n"
+        "ds_read_u16 %5, %9 offset:128\n"
+        "ds_read_u16 %6, %9 offset:256\n"
+        "ds_read_u16 %7, %9 offset:384"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(o.sc[0]), "=&v"(o.sc[1]), "=&v"(o.sc[2]), "=&v"(o.sc[3])
+        : "v"(va), "v"(vs)
+        : "memory");
+    const v4i av[4] = {a0, a1, a2, a3};
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+#pragma unroll
+      for (int d = 0; d < 4; d++) o.a[q][d] = (uint32_t)av[q][d];
+  } else {
+    // 12-byte lanes are only 4-byte aligned: three dword reads per row tile
+    asm volatile(
+        "ds_read_b32 %0, %16\n"
+        "ds_read_b32 %1, %16 offset:4\n"
+        "ds_read_b32 %2, %16 offset:8\n"
+        "ds_read_b32 %3, %16 offset:768\n"
+        "ds_read_b32 %4, %16 offset:772\n"
+        "ds_read_b32 %5, %16 offset:776\n"
+        "ds_read_b32 %6, %16 offset:1536\n"
+        "ds_read_b32 %7, %16 offset:1540\n"
+        "ds_read_b32 %8, %16 offset:1544\n"
+        "ds_read_b32 %9, %16 offset:2304\n"
+        "ds_read_b32 %10, %16 offset:2308\n"
+        "ds_read_b32 %11, %16 offset:2312\n"
+        "ds_read_u8 %12, %17\n"
+        "ds_read_u8 %13, %17 offset:64\n"
+        "ds_read_u8 %14, %17 offset:128\n"
+        "ds_read_u8 %15, %17 offset:192"
+        : "=&v"(o.a[0][0]), "=&v"(o.a[0][1]), "=&v"(o.a[0][2]), "=&v"(o.a[1][0]), "=&v"(o.a[1][1]), "=&v"(o.a[1][2]),
+          "=&v"(o.a[2][0]), "=&v"(o.a[2][1]), "=&v"(o.a[2][2]), "=&v"(o.a[3][0]), "=&v"(o.a[3][1]), "=&v"(o.a[3][2]),
+          "=&v"(o.sc[0]), "=&v"(o.sc[1]), "=&v"(o.sc[2]), "=&v"(o.sc[3])
+        : "v"(va), "v"(vs)
+        : "memory");
+#pragma unroll
+    for (int q = 0; q < 4; q++) o.a[q][3] = 0;
+  }
+  asm volatile(
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %9\n"
+      "ds_read_b128 %2, %10\n"
+      "ds_read_b128 %3, %11\n"
+      "ds_read_b128 %4, %8 offset:4096\n"
+      "ds_read_b128 %5, %9 offset:4096\n"
+      "ds_read_b128 %6, %10 offset:4096\n"
+      "ds_read_b128 %7, %11 offset:4096"
+      : "=&v"(o.b[0][0]), "=&v"(o.b[0][1]), "=&v"(o.b[0][2]), "=&v"(o.b[0][3]), "=&v"(o.b[1][0]), "=&v"(o.b[1][1]),
+        "=&v"(o.b[1][2]), "=&v"(o.b[1][3])
+      : "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3])
+      : "memory");
+}
+
+template <int WF>
+__device__ __forceinline__ void pf16_wait(Pf16Ops<WF> &o) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(o.a[0][0]), "+v"(o.a[0][1]), "+v"(o.a[0][2]), "+v"(o.a[0][3]), "+v"(o.a[1][0]), "+v"(o.a[1][1]),
+                 "+v"(o.a[1][2]), "+v"(o.a[1][3]), "+v"(o.a[2][0]), "+v"(o.a[2][1]), "+v"(o.a[2][2]), "+v"(o.a[2][3]),
+                 "+v"(o.a[3][0]), "+v"(o.a[3][1]), "+v"(o.a[3][2]), "+v"(o.a[3][3])
+               :
+               : "memory");
+  asm volatile("" : "+v"(o.sc[0]), "+v"(o.sc[1]), "+v"(o.sc[2]), "+v"(o.sc[3]), "+v"(o.b[0][0]), "+v"(o.b[0][1]),
+                    "+v"(o.b[0][2]), "+v"(o.b[0][3]), "+v"(o.b[1][0]), "+v"(o.b[1][1]), "+v"(o.b[1][2]), "+v"(o.b[1][3]));
+}
+
+// 24-bit NF3 group (8 codes) -> 8 bf16 through a 4-entry table of the rounded
+// magnitudes (t01 = |v0| | |v1| << 16, t23 likewise): per code pair one byte
+// permute picks both magnitudes, then the sign bits are or-ed in.  A code c
+// stands for +mag[c - 4] (c >= 4) or -mag[3 - c]; the bits are worked on for
+// all eight codes at once.
+__device__ __forceinline__ v8bf nf3_step_lut(uint32_t w24, uint32_t t01, uint32_t t23) {
+  const uint32_t neg = (~w24 >> 2) & 0x249249u;             // bit 3e: code e is negative
+  const uint32_t idx = (w24 ^ (neg * 3u)) & 0x6DB6DBu;      // bits 3e, 3e + 1: magnitude index of code e
+  v4i r;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const uint32_t x = ((idx >> (6 * m)) & 3u) | (((idx >> (6 * m + 3)) & 3u) << 16);
+    const uint32_t sel = ((x | (x << 8)) << 1) + 0x01000100u;
+    const uint32_t sgn = (((neg >> (6 * m)) & 1u) << 15) | (((neg >> (6 * m + 3)) & 1u) << 31);
+    r[m] = (int)(__builtin_amdgcn_perm(t23, t01, sel) | sgn);
+  }
+  return __builtin_bit_cast(v8bf, r);
+}
+
+// 32 bf16 MFMAs of one k-tile.  Columns past the reduction length: scale 0
+// (weights 0) and activations 0.  SWAP: activations as the A operand.  Scale
+// decoding (and the NF3 magnitude table) is done once per row tile, not per
+// 8-column step.
+template <int WF, bool SWAP>
+__device__ __forceinline__ void pf16_mma(const Pf16Ops<WF> &o, int kt, int kcols, int l, v4f (*acc)[2]) {
+  const int g = l >> 4;
+  const bool gin = kt * 128 + 32 * g < kcols;
+  float slo[4], shi[4];
+  uint32_t t01[4], t23[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const uint32_t sc = gin ? (uint32_t)o.sc[q] : 0u;
+    if constexpr (WF == W_NVFP4) {
+      slo[q] = e4m3_f32(sc & 0xFFu);
+      shi[q] = e4m3_f32((sc >> 8) & 0xFFu);
+    } else {
+      const float f = e4m3_f32(sc & 0xFFu);
+      t01[q] = pack_bf16x2(0.1275f * f, 0.3563f * f);
+      t23[q] = pack_bf16x2(0.6047f * f, f);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    v8bf bop[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++) bop[cb] = __builtin_bit_cast(v8bf, gin ? o.b[cb][s] : v4i{0, 0, 0, 0});
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      v8bf aop;
+      if constexpr (WF == W_NVFP4) {
+        aop = nvfp4_step(o.a[q][s], s < 2 ? slo[q] : shi[q]);
+      } else {
+        // group s of 24 bits starts at bit 24 s of the lane's 96-bit word
+        const uint32_t d0 = o.a[q][0], d1 = o.a[q][1], d2 = o.a[q][2];
+        const uint32_t w24 = s == 0 ? (d0 & 0xFFFFFFu)
+                             : s == 1 ? ((d0 >> 24) | (d1 << 8)) & 0xFFFFFFu
+                             : s == 2 ? ((d1 >> 16) | (d2 << 16)) & 0xFFFFFFu
+                                      : d2 >> 8;
+        aop = nf3_step_lut(w24, t01[q], t23[q]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; cb++) acc[q][cb] = SWAP ? mfma_bf16(bop[cb], aop, acc[q][cb]) : mfma_bf16(aop, bop[cb], acc[q][cb]);
+    }
+  }
+}
+
+template <int WF, bool SWAP>
+__device__ __forceinline__ void pf16_step(Pf16Lds<WF> &L, const Pf16Src &src, int kt, int nkt, Pf16Ops<WF> &cur,
+                                          Pf16Ops<WF> &nxt, v4f (*acc)[2]) {
+  constexpr int ST = kPf16Stages;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wr = w >> 1, wc = w & 1;
+  pf16_wait(cur);
+  wait16_stages<WF>(min(ST - 2, nkt - 2 - kt));   // stage kt + 1 has landed
+  __builtin_amdgcn_s_barrier();              // ... for every wave, and no wave reads stage kt any more
+  if (kt + ST < nkt) pf16_issue<WF>(L.st[kt % ST], src, kt + ST, w, l);
+  if (kt + 1 < nkt) pf16_read<WF>(nxt, L.st[(kt + 1) % ST], wr, wc, l);
+  pf16_mma<WF, SWAP>(cur, kt, src.kcols, l, acc);
+}
+
+template <int WF, bool SWAP>
+__device__ __forceinline__ void pf16_kloop(Pf16Lds<WF> &L, const Pf16Src &src, v4f (*acc)[2]) {
+  constexpr int ST = kPf16Stages;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wr = w >> 1, wc = w & 1;
+  const int nkt = (src.kcols + 127) / 128;
+#pragma unroll
+  for (int s = 0; s < ST; s++)
+    if (s < nkt) pf16_issue<WF>(L.st[s], src, s, w, l);
+  wait16_stages<WF>(min(ST - 1, nkt - 1));   // stage 0 has landed
+  __builtin_amdgcn_s_barrier();
+  Pf16Ops<WF> r0, r1;
+  pf16_read<WF>(r0, L.st[0], wr, wc, l);
+  for (int kt = 0; kt + 1 < nkt; kt += 2) {
+    pf16_step<WF, SWAP>(L, src, kt, nkt, r0, r1, acc);
+    pf16_step<WF, SWAP>(L, src, kt + 1, nkt, r1, r0, acc);
+  }
+  if (nkt & 1) pf16_step<WF, SWAP>(L, src, nkt - 1, nkt, r0, r1, acc);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- GEMM1 (A16)
+template <int WF>
+__global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
+  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  __shared__ Pf16Lds<WF> L;
+  const int K = a.K, N = a.N;
+  const PfWork wk = pf_work(a, N / 64, true);
+  if (!wk.valid) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
+  const int hb = wk.sub, groups = K / 32;
+  Pf16Src src;
+  src.wstep = (size_t)16 * groups * U;
+  src.sstep = (size_t)16 * groups * SU;
+  src.wbase = a.w13 + (size_t)wk.e * (2 * N) * groups * U + (size_t)(8 * hb) * src.wstep;
+  src.sbase = a.s13 + (size_t)wk.e * (2 * N) * groups * SU + (size_t)(8 * hb) * src.sstep;
+  src.kcols = K;
+  // rows past the tile read route p0's token; their results are never stored
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int row = 4 * (4 * w + j) + (l >> 4);
+    src.brow[j] = a.xb + (size_t)(a.perm[wk.p0 + (row < wk.rows ? row : 0)] / a.topk) * K;
+  }
+  v4f acc[4][2];
+  zero_acc(acc);
+  pf16_kloop<WF, false>(L, src, acc);
+  // epilogue: row tiles 4wr + {0,1,2,3} = up/gate of intermediate blocks 4hb + 2wr + {0,1}
+  const float gs = a.g13 ? a.g13[wk.e] : 1.0f;
+#pragma unroll
+  for (int cb = 0; cb < 2; cb++) {
+    const int row = 32 * wc + 16 * cb + c;
+    if (row < wk.rows) {
+      const size_t p = (size_t)(wk.p0 + row);
+#pragma unroll
+      for (int s = 0; s < 2; s++) {
+        float h[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) h[i] = silu_clamped(acc[2 * s + 1][cb][i] * gs, acc[2 * s][cb][i] * gs, a.limit, a.has_limit);
+        uint2 v;
+        v.x = pack_bf16x2(h[0], h[1]);
+        v.y = pack_bf16x2(h[2], h[3]);
+        *(uint2 *)(a.hb + p * N + 64 * hb + 32 * wr + 16 * s + 4 * g) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- GEMM2 (A16)
+template <int WF>
+__global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
+  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  __shared__ Pf16Lds<WF> L;
+  __shared__ int s_r[kPfTileRows];
+  __shared__ float s_w[kPfTileRows];
+  const int K = a.K, N = a.N;
+  const PfWork wk = pf_work(a, K / 128, false);
+  if (!wk.valid) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
+  const int ob = wk.sub, groups = N / 32;   // output columns 128 ob .. +127 = w2 row tiles 8 ob .. +7
+  Pf16Src src;
+  src.wstep = (size_t)16 * groups * U;
+  src.sstep = (size_t)16 * groups * SU;
+  src.wbase = a.w2 + (size_t)wk.e * K * groups * U + (size_t)(8 * ob) * src.wstep;
+  src.sbase = a.s2 + (size_t)wk.e * K * groups * SU + (size_t)(8 * ob) * src.sstep;
+  src.kcols = N;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int row = 4 * (4 * w + j) + (l >> 4);
+    src.brow[j] = a.hb + (size_t)(wk.p0 + (row < wk.rows ? row : 0)) * N;
+  }
+  if (tid < wk.rows) {
+    const int r = a.perm[wk.p0 + tid];
+    s_r[tid] = r;
+    s_w[tid] = a.topk_w[r] * (a.g2 ? a.g2[wk.e] : 1.0f);
+  }
+  v4f acc[4][2];
+  zero_acc(acc);
+  pf16_kloop<WF, true>(L, src, acc);
+  __syncthreads();   // s_r / s_w visible
+  pf_combine(a, wk, acc, s_r, s_w, (size_t)128 * ob + 64 * wr + c, wc, c, g);
+}
+
+template <int WF>
+static hipError_t launch_pf_a16(const GemmArgs &a, int grid_tiles, hipStream_t s, bool second) {
+  if (second) hipLaunchKernelGGL(k_pf_gemm2_a16<WF>, dim3(pf_grid(grid_tiles, a.K / 128)), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_pf_gemm1_a16<WF>, dim3(pf_grid(grid_tiles, a.N / 64)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf16_gemm1(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s) {
+  if (grid_tiles <= 0) return hipSuccess;
+  return wfmt == W_NVFP4 ? launch_pf_a16<W_NVFP4>(a, grid_tiles, s, false) : launch_pf_a16<W_NF3>(a, grid_tiles, s, false);
+}
+
+hipError_t launch_pf16_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s) {
+  if (grid_tiles <= 0) return hipSuccess;
+  return wfmt == W_NVFP4 ? launch_pf_a16<W_NVFP4>(a, grid_tiles, s, true) : launch_pf_a16<W_NF3>(a, grid_tiles, s, true);
 }
 
 }  // namespace moe

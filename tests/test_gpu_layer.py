@@ -60,6 +60,16 @@ SMALL = {
     # one k-tile in the down GEMM (N = 64), two in the up/gate GEMM (K = 256), no clamp
     "prefill_narrow": lambda: I.make_problem(I.Config("prefill_narrow", T=130, E=3, K=256, N=64, topk=2,
                                                       limit=None, fmt=I.FMT_MXFP4), seed=12),
+    # the W4A16 / W3A16 prefill kernels: NVFP4 with a half k-tile in the down GEMM,
+    # NF3 with one down k-tile and the clamp, and both tiers in one batch
+    "nvfp4_prefill_small": lambda: I.make_problem(I.Config("nvfp4_prefill_small", T=150, E=8, K=256, N=192,
+                                                           topk=4, limit=None, fmt=I.FMT_NVFP4, pad_rows=2),
+                                                  seed=13),
+    "nf3_prefill_small": lambda: I.make_problem(I.Config("nf3_prefill_small", T=130, E=6, K=256, N=64, topk=2,
+                                                         limit=10.0, fmt=I.FMT_NF3), seed=14),
+    "hybrid_prefill_small": lambda: I.make_problem(I.Config("hybrid_prefill_small", T=140, E=12, K=512, N=128,
+                                                            topk=3, limit=None, fmt=I.FMT_NVFP4, hybrid_nvfp4=4),
+                                                   seed=15),
 }
 
 
@@ -80,7 +90,8 @@ def _sample_rows(prob, n, seed=0):
 
 @pytest.mark.parametrize("name", ["tiny", "mxfp4_ragged", "nvfp4_small", "nf3_small", "hybrid_small",
                                   "nvfp4_clamped", "hybrid_decode", "decode_many_routes", "nf3_decode",
-                                  "prefill_small", "prefill_narrow"])
+                                  "prefill_small", "prefill_narrow", "nvfp4_prefill_small", "nf3_prefill_small",
+                                  "hybrid_prefill_small"])
 @pytest.mark.parametrize("deterministic", [False, True])
 def test_small_layers_all_rows(name, deterministic):
     L = layer(name)
