@@ -37,27 +37,24 @@
 
 namespace moe {
 
-constexpr int kPfRowTiles = 8;   // weight row tiles per block
-constexpr int kPfStages1 = 4;    // LDS ring depth (k-tiles), up/gate GEMM
-constexpr int kPfStages2 = 3;    // down GEMM: short k-loops, more blocks per CU
-constexpr int kPfLoadsPerStage = 5;
+constexpr int kPfRT = 16;        // W4A8: weight row tiles per block (256 weight rows)
+constexpr int kPfQ = 8;          // W4A8: row tiles per wave
+constexpr int kPfStages = 3;     // W4A8: LDS ring depth (k-tiles)
+constexpr int kPfLoadsPerStage = 8;
 
 struct PfStage {
-  uint8_t A[kPfRowTiles][1024];   // weight row tiles, MFMA lane order
+  uint8_t A[kPfRT][1024];         // weight row tiles, MFMA lane order
   uint8_t B[8][1024];             // activation rows 8b .. 8b+7 of block b, swizzled 16-byte chunks
-  uint8_t S[1024];                // As [8][64] | Bs [64][4] | spare
+  uint8_t S[2048];                // As [16][64] | Bs [64][4] | 3 spare 256-byte slots
 };
 
-template <int ST>
 struct __attribute__((aligned(16))) PfLds {
-  PfStage st[ST];
+  PfStage st[kPfStages];
 };
-
 
 // Wait until at most `stages` ring stages issued by this wave are in flight.
 __device__ __forceinline__ void wait_stages(int stages) {
-  if (stages >= 3) wait_vm<3 * kPfLoadsPerStage>();
-  else if (stages == 2) wait_vm<2 * kPfLoadsPerStage>();
+  if (stages >= 2) wait_vm<2 * kPfLoadsPerStage>();
   else if (stages == 1) wait_vm<kPfLoadsPerStage>();
   else wait_vm<0>();
 }
@@ -94,33 +91,36 @@ __device__ __forceinline__ PfWork pf_work(const GemmArgs &a, int nsub, bool sub_
 struct PfSrc {
   const uint8_t *wbase, *sbase;   // row tile rt, k-tile kt: wbase + rt * wstep + kt * 1024 (scales: 64 per k-tile)
   size_t wstep, sstep;
+  int nrt;                        // row tiles of this block that exist (8 or 16); the rest repeat the last one
   const uint8_t *brow[2];         // this lane's activation rows of its two B blocks
   const uint8_t *bsrow;           // activation scale row of route (lane)
   int kbytes;                     // reduction length (bytes of one activation row)
 };
 
-// The five loads of wave w for k-tile kt into stage S.  Lanes whose data lies
-// past the reduction length (a partial last k-tile) load from a valid address
-// instead; the MFMA step zeroes those activation bytes and both scales there.
+// The eight loads of wave w for k-tile kt into stage S: weight row tiles 4w ..
+// 4w+3, activation blocks 2w, 2w+1, the scales of row tiles 4w .. 4w+3, and the
+// activation scales (wave 0; waves 1-3 fill spare slots to keep the per-wave
+// load count equal).  Lanes whose data lies past the reduction length (a
+// partial last k-tile) load from a valid address instead; the MFMA step zeroes
+// those activation bytes and both scales there.
 __device__ __forceinline__ void pf_issue(PfStage &S, const PfSrc &src, int kt, int w, int l) {
+  const bool in = (kt * 4 + (l >> 4)) * 32 < src.kbytes;
 #pragma unroll
-  for (int j = 0; j < 2; j++) {   // weight row tiles 2w + j
-    const int rt = 2 * w + j;
-    const bool in = (kt * 4 + (l >> 4)) * 32 < src.kbytes;
-    dma16(src.wbase + rt * src.wstep + (in ? (size_t)kt * 1024 + l * 16 : 0), &S.A[rt][0]);
+  for (int j = 0; j < 4; j++) {
+    const int rt = 4 * w + j, rs = min(rt, src.nrt - 1);
+    dma16(src.wbase + rs * src.wstep + (in ? (size_t)kt * 1024 + l * 16 : 0), &S.A[rt][0]);
   }
 #pragma unroll
   for (int j = 0; j < 2; j++) {   // activation blocks 2w + j: lane l -> row l / 8, its chunk slot l
     const int r8 = l >> 3, part = (l & 7) ^ r8, off = kt * 128 + part * 16;
     dma16(src.brow[j] + (off < src.kbytes ? off : 0), &S.B[2 * w + j][0]);
   }
-  if (w < 2) {   // As row tiles 4w .. 4w+3: lane l -> row tile 4w + l / 16, dword l % 16
-    const int rt = 4 * w + (l >> 4), d = l & 15;
-    const bool in = (kt * 4 + (d >> 2)) * 32 < src.kbytes;
-    dma4(src.sbase + rt * src.sstep + (in ? (size_t)kt * 64 + 4 * d : 0), &S.S[256 * w]);
-  } else {       // Bs (wave 3 fills the spare slot to keep the per-wave load count equal)
-    dma4(src.bsrow + 4 * kt, &S.S[w == 2 ? 512 : 768]);
+  {   // As row tiles 4w .. 4w+3: lane l -> row tile 4w + l / 16, dword l % 16
+    const int rs = min(4 * w + (l >> 4), src.nrt - 1), d = l & 15;
+    const bool ins = (kt * 4 + (d >> 2)) * 32 < src.kbytes;
+    dma4(src.sbase + rs * src.sstep + (ins ? (size_t)kt * 64 + 4 * d : 0), &S.S[256 * w]);
   }
+  dma4(src.bsrow + 4 * kt, &S.S[w == 0 ? 1024 : 1024 + 256 * w]);
 }
 
 // One wave's operands of a landed stage.  The LDS reads are issued by asm the
@@ -129,47 +129,59 @@ __device__ __forceinline__ void pf_issue(PfStage &S, const PfSrc &src, int kt, i
 // every k-tile.  pf_read issues them; pf_wait waits for them and, taking the
 // registers as operands, keeps every use of them after the wait.
 struct PfOps {
-  v4i a[4];      // weight row tiles 4 wr + q
+  v4i a[kPfQ];   // weight row tiles 8 wr + q
   v4i b[4];      // activation chunks: [cb] = columns 16 g .. of route block cb, [2 + cb] = columns 64 + 16 g ..
-  int sa[4], sb[2];
+  int sa[kPfQ], sb[2];
 };
 
 __device__ __forceinline__ void pf_read(PfOps &o, const PfStage &S, int wr, int wc, int l) {
   const int c = l & 15, g = l >> 4, r8 = c & 7;
   const uint8_t *bblk = &S.B[4 * wc + (c >> 3)][0];
-  const uint32_t va = lds_addr(&S.A[4 * wr][l * 16]), vb0 = lds_addr(bblk + pf_slot(r8, g) * 16),
-                 vb1 = lds_addr(bblk + pf_slot(r8, 4 + g) * 16), vsa = lds_addr(&S.S[4 * wr * 64 + l]),
-                 vsb = lds_addr(&S.S[512 + (32 * wc + c) * 4 + g]);
+  const uint32_t va = lds_addr(&S.A[kPfQ * wr][l * 16]), vb0 = lds_addr(bblk + pf_slot(r8, g) * 16),
+                 vb1 = lds_addr(bblk + pf_slot(r8, 4 + g) * 16), vsa = lds_addr(&S.S[kPfQ * wr * 64 + l]),
+                 vsb = lds_addr(&S.S[1024 + (32 * wc + c) * 4 + g]);
   asm volatile(
-      "ds_read_b128 %0, %14\n"
-      "ds_read_b128 %1, %14 offset:1024\n"
-      "ds_read_b128 %2, %14 offset:2048\n"
-      "ds_read_b128 %3, %14 offset:3072\n"
-      "ds_read_b128 %4, %15\n"
-      "ds_read_b128 %5, %15 offset:2048\n"
-      "ds_read_b128 %6, %16\n"
-      "ds_read_b128 %7, %16 offset:2048\n"
-      "ds_read_u8 %8, %17\n"
-      "ds_read_u8 %9, %17 offset:64\n"
-      "ds_read_u8 %10, %17 offset:128\n"
-      "ds_read_u8 %11, %17 offset:192\n"
-      "ds_read_u8 %12, %18\n"
-      "ds_read_u8 %13, %18 offset:64"
-      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.b[0]), "=&v"(o.b[1]), "=&v"(o.b[2]),
-        "=&v"(o.b[3]), "=&v"(o.sa[0]), "=&v"(o.sa[1]), "=&v"(o.sa[2]), "=&v"(o.sa[3]), "=&v"(o.sb[0]), "=&v"(o.sb[1])
+      "ds_read_b128 %0, %22\n"
+      "ds_read_b128 %1, %22 offset:1024\n"
+      "ds_read_b128 %2, %22 offset:2048\n"
+      "ds_read_b128 %3, %22 offset:3072\n"
+      "ds_read_b128 %4, %22 offset:4096\n"
+      "ds_read_b128 %5, %22 offset:5120\n"
+      "ds_read_b128 %6, %22 offset:6144\n"
+      "ds_read_b128 %7, %22 offset:7168\n"
+      "ds_read_b128 %8, %23\n"
+      "ds_read_b128 %9, %23 offset:2048\n"
+      "ds_read_b128 %10, %24\n"
+      "ds_read_b128 %11, %24 offset:2048\n"
+      "ds_read_u8 %12, %25\n"
+      "ds_read_u8 %13, %25 offset:64\n"
+      "ds_read_u8 %14, %25 offset:128\n"
+      "ds_read_u8 %15, %25 offset:192\n"
+      "ds_read_u8 %16, %25 offset:256\n"
+      "ds_read_u8 %17, %25 offset:320\n"
+      "ds_read_u8 %18, %25 offset:384\n"
+      "ds_read_u8 %19, %25 offset:448\n"
+      "ds_read_u8 %20, %26\n"
+      "ds_read_u8 %21, %26 offset:64"
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.a[4]), "=&v"(o.a[5]), "=&v"(o.a[6]),
+        "=&v"(o.a[7]), "=&v"(o.b[0]), "=&v"(o.b[1]), "=&v"(o.b[2]), "=&v"(o.b[3]), "=&v"(o.sa[0]), "=&v"(o.sa[1]),
+        "=&v"(o.sa[2]), "=&v"(o.sa[3]), "=&v"(o.sa[4]), "=&v"(o.sa[5]), "=&v"(o.sa[6]), "=&v"(o.sa[7]),
+        "=&v"(o.sb[0]), "=&v"(o.sb[1])
       : "v"(va), "v"(vb0), "v"(vb1), "v"(vsa), "v"(vsb)
       : "memory");
 }
 
 __device__ __forceinline__ void pf_wait(PfOps &o) {
   asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(o.a[0]), "+v"(o.a[1]), "+v"(o.a[2]), "+v"(o.a[3]), "+v"(o.b[0]), "+v"(o.b[1]), "+v"(o.b[2]),
-                 "+v"(o.b[3]), "+v"(o.sa[0]), "+v"(o.sa[1]), "+v"(o.sa[2]), "+v"(o.sa[3]), "+v"(o.sb[0]), "+v"(o.sb[1])
+               : "+v"(o.a[0]), "+v"(o.a[1]), "+v"(o.a[2]), "+v"(o.a[3]), "+v"(o.a[4]), "+v"(o.a[5]), "+v"(o.a[6]),
+                 "+v"(o.a[7]), "+v"(o.b[0]), "+v"(o.b[1]), "+v"(o.b[2]), "+v"(o.b[3])
                :
                : "memory");
+  asm volatile("" : "+v"(o.sa[0]), "+v"(o.sa[1]), "+v"(o.sa[2]), "+v"(o.sa[3]), "+v"(o.sa[4]), "+v"(o.sa[5]),
+                    "+v"(o.sa[6]), "+v"(o.sa[7]), "+v"(o.sb[0]), "+v"(o.sb[1]));
 }
 
-// 8 MFMAs of one k-tile.  Past the reduction length (a partial last k-tile)
+// 16 MFMAs of one k-tile.  Past the reduction length (a partial last k-tile)
 // the activation bytes are zeroed and both scales set to 2^-127, so the
 // products there are exact zeros whatever the stage held.  SWAP: activations
 // as the A operand (accumulator lane = output column, elements = 4 routes).
@@ -186,7 +198,7 @@ __device__ __forceinline__ void pf_mma(const PfOps &o, int kt, int kbytes, int l
     bop[cb] = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
   }
 #pragma unroll
-  for (int q = 0; q < 4; q++)
+  for (int q = 0; q < kPfQ; q++)
 #pragma unroll
     for (int cb = 0; cb < 2; cb++) {
       const int sa = gin ? o.sa[q] : 0, sb = gin ? o.sb[cb] : 0;
@@ -198,41 +210,38 @@ __device__ __forceinline__ void pf_mma(const PfOps &o, int kt, int kbytes, int l
     }
 }
 
-// One k-tile: operands of kt are in `cur` (reads issued one k-tile earlier).
-template <bool SWAP, int ST>
-__device__ __forceinline__ void pf_step(PfLds<ST> &L, const PfSrc &src, int kt, int nkt, PfOps &cur, PfOps &nxt,
-                                        v4f (*acc)[2]) {
+// One k-tile: wait until stage kt has landed for every wave (every wave is
+// then also done with stage kt - 1), read this wave's operands of stage kt,
+// refill stage kt - 1's slot with k-tile kt + kPfStages - 1, multiply.
+template <bool SWAP>
+__device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, int kt, int nkt, v4f (*acc)[2]) {
+  constexpr int ST = kPfStages;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wr = w >> 1, wc = w & 1;
-  pf_wait(cur);
-  wait_stages(min(ST - 2, nkt - 2 - kt));   // stage kt + 1 has landed
-  __builtin_amdgcn_s_barrier();                   // ... for every wave, and no wave reads stage kt any more
-  if (kt + ST < nkt) pf_issue(L.st[kt % ST], src, kt + ST, w, l);
-  if (kt + 1 < nkt) pf_read(nxt, L.st[(kt + 1) % ST], wr, wc, l);
-  pf_mma<SWAP>(cur, kt, src.kbytes, l, acc);
+  wait_stages(min(ST - 2, nkt - 1 - kt));   // stage kt has landed
+  __builtin_amdgcn_s_barrier();
+  PfOps o;
+  pf_read(o, L.st[kt % ST], wr, wc, l);
+  if (kt + ST - 1 < nkt) pf_issue(L.st[(kt + ST - 1) % ST], src, kt + ST - 1, w, l);
+  pf_wait(o);
+  pf_mma<SWAP>(o, kt, src.kbytes, l, acc);
 }
 
 // The k-loop of both GEMMs.
-template <bool SWAP, int ST>
-__device__ __forceinline__ void pf_kloop(PfLds<ST> &L, const PfSrc &src, v4f (*acc)[2]) {
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wr = w >> 1, wc = w & 1;
+template <bool SWAP>
+__device__ __forceinline__ void pf_kloop(PfLds &L, const PfSrc &src, v4f (*acc)[2]) {
+  constexpr int ST = kPfStages;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int nkt = (src.kbytes + 127) / 128;
 #pragma unroll
-  for (int s = 0; s < ST; s++)
+  for (int s = 0; s < ST - 1; s++)
     if (s < nkt) pf_issue(L.st[s], src, s, w, l);
-  wait_stages(min(ST - 1, nkt - 1));   // stage 0 has landed
-  __builtin_amdgcn_s_barrier();
-  PfOps r0, r1;
-  pf_read(r0, L.st[0], wr, wc, l);
-  for (int kt = 0; kt + 1 < nkt; kt += 2) {
-    pf_step<SWAP, ST>(L, src, kt, nkt, r0, r1, acc);
-    pf_step<SWAP, ST>(L, src, kt + 1, nkt, r1, r0, acc);
-  }
-  if (nkt & 1) pf_step<SWAP, ST>(L, src, nkt - 1, nkt, r0, r1, acc);
+  for (int kt = 0; kt < nkt; kt++) pf_step<SWAP>(L, src, kt, nkt, acc);
 }
 
+template <int Q>
 __device__ __forceinline__ void zero_acc(v4f (*acc)[2]) {
 #pragma unroll
-  for (int q = 0; q < 4; q++)
+  for (int q = 0; q < Q; q++)
 #pragma unroll
     for (int cb = 0; cb < 2; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
 }
@@ -244,6 +253,7 @@ __device__ __forceinline__ void zero_acc(v4f (*acc)[2]) {
 // swap one value so each stores two adjacent columns of one route); atomic mode
 // adds fp32 into the token accumulator, 4 routes x 16 consecutive columns per
 // instruction.
+template <int Q>
 __device__ __forceinline__ void pf_combine(const GemmArgs &a, const PfWork &wk, v4f (*acc)[2], const int *s_r,
                                            const float *s_w, size_t col, int wc, int c, int g) {
   const int K = a.K;
@@ -258,7 +268,7 @@ __device__ __forceinline__ void pf_combine(const GemmArgs &a, const PfWork &wk, 
         const int r = ok ? s_r[row] : 0;
         const float wgt = ok ? s_w[row] : 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
+        for (int q = 0; q < Q; q++) {
           const float mine = acc[q][cb][2 * ip + (odd ? 1 : 0)], give = acc[q][cb][2 * ip + (odd ? 0 : 1)];
           const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
           const float lo = odd ? got : mine, hi = odd ? mine : got;
@@ -275,25 +285,28 @@ __device__ __forceinline__ void pf_combine(const GemmArgs &a, const PfWork &wk, 
           float *dst = a.out_acc + (size_t)(s_r[row] / a.topk) * K + col;
           const float wgt = s_w[row];
 #pragma unroll
-          for (int q = 0; q < 4; q++) atomicAdd(dst + 16 * q, wgt * acc[q][cb][i]);
+          for (int q = 0; q < Q; q++) atomicAdd(dst + 16 * q, wgt * acc[q][cb][i]);
         }
       }
   }
 }
 
 // ---------------------------------------------------------------- GEMM1
+// Block: 16 row tiles of w13 = up and gate of 128 intermediate columns (the
+// last block of an N % 128 == 64 layer holds 8).
 __global__ __launch_bounds__(256) void k_pf_gemm1_a8(GemmArgs a) {
-  __shared__ PfLds<kPfStages1> L;
+  __shared__ PfLds L;
   const int K = a.K, N = a.N;
-  const PfWork wk = pf_work(a, N / 64, true);
+  const PfWork wk = pf_work(a, (N + 127) / 128, true);
   if (!wk.valid) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
   const int hb = wk.sub;
   PfSrc src;
   src.wstep = (size_t)16 * (K / 2);
   src.sstep = (size_t)16 * (K / 32);
-  src.wbase = a.w13 + (size_t)wk.e * (2 * N) * (K / 2) + (size_t)(8 * hb) * src.wstep;
-  src.sbase = a.s13 + (size_t)wk.e * (2 * N) * (K / 32) + (size_t)(8 * hb) * src.sstep;
+  src.wbase = a.w13 + (size_t)wk.e * (2 * N) * (K / 2) + (size_t)(kPfRT * hb) * src.wstep;
+  src.sbase = a.s13 + (size_t)wk.e * (2 * N) * (K / 32) + (size_t)(kPfRT * hb) * src.sstep;
+  src.nrt = min(kPfRT, N / 8 - kPfRT * hb);
   src.kbytes = K;
   // rows past the tile read route p0's token; their results are never stored
 #pragma unroll
@@ -302,52 +315,62 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a8(GemmArgs a) {
     src.brow[j] = a.xq + (size_t)(a.perm[wk.p0 + (row < wk.rows ? row : 0)] / a.topk) * K;
   }
   src.bsrow = a.xs + (size_t)(a.perm[wk.p0 + (l < wk.rows ? l : 0)] / a.topk) * (K / 32);
-  v4f acc[4][2];
-  zero_acc(acc);
-  pf_kloop<false, kPfStages1>(L, src, acc);
-  // epilogue: row tiles 4wr + {0,1,2,3} = up/gate of intermediate blocks 4hb + 2wr + {0,1}
+  v4f acc[kPfQ][2];
+  zero_acc<kPfQ>(acc);
+  pf_kloop<false>(L, src, acc);
+  if (kPfQ * wr >= src.nrt) return;   // the missing half of a partial block
+  // epilogue: row tiles 8 wr + q, q = 2 s + {0, 1}: up / gate of intermediate
+  // columns 128 hb + 64 wr + 16 s .. +15; MXFP8 groups of two 16-column blocks
   const int hss = hs_stride(N);
 #pragma unroll
   for (int cb = 0; cb < 2; cb++) {
-    float h[8];
-#pragma unroll
-    for (int s = 0; s < 2; s++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) h[s * 4 + i] = silu_clamped(acc[2 * s + 1][cb][i], acc[2 * s][cb][i], a.limit, a.has_limit);
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(h[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    float inv;
-    const uint32_t sbyte = mx_scale(amax, &inv);
     const int row = 32 * wc + 16 * cb + c;
-    if (row < wk.rows) {
-      const size_t p = (size_t)(wk.p0 + row);
+#pragma unroll
+    for (int pp = 0; pp < 2; pp++) {
+      float h[8];
 #pragma unroll
       for (int s = 0; s < 2; s++)
-        *(uint32_t *)(a.hq + p * N + 64 * hb + 32 * wr + 16 * s + 4 * g) =
-            e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
-      if (g == 0) a.hs[p * hss + 2 * hb + wr] = (uint8_t)sbyte;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int q = 2 * (2 * pp + s);
+          h[s * 4 + i] = silu_clamped(acc[q + 1][cb][i], acc[q][cb][i], a.limit, a.has_limit);
+        }
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(h[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      float inv;
+      const uint32_t sbyte = mx_scale(amax, &inv);
+      if (row < wk.rows) {
+        const size_t p = (size_t)(wk.p0 + row);
+        const size_t c0 = (size_t)128 * hb + 64 * wr + 32 * pp;
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+          *(uint32_t *)(a.hq + p * N + c0 + 16 * s + 4 * g) = e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
+        if (g == 0) a.hs[p * hss + c0 / 32] = (uint8_t)sbyte;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------- GEMM2
+// Block: 16 row tiles of w2 = 256 output columns.
 __global__ __launch_bounds__(256) void k_pf_gemm2_a8(GemmArgs a) {
-  __shared__ PfLds<kPfStages2> L;
+  __shared__ PfLds L;
   __shared__ int s_r[kPfTileRows];
   __shared__ float s_w[kPfTileRows];
   const int K = a.K, N = a.N;
-  const PfWork wk = pf_work(a, K / 128, false);
+  const PfWork wk = pf_work(a, K / 256, false);
   if (!wk.valid) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
-  const int ob = wk.sub;   // output columns 128 ob .. +127 = w2 row tiles 8 ob .. +7
+  const int ob = wk.sub;
   PfSrc src;
   src.wstep = (size_t)16 * (N / 2);
   src.sstep = (size_t)16 * (N / 32);
-  src.wbase = a.w2 + (size_t)wk.e * K * (N / 2) + (size_t)(8 * ob) * src.wstep;
-  src.sbase = a.s2 + (size_t)wk.e * K * (N / 32) + (size_t)(8 * ob) * src.sstep;
+  src.wbase = a.w2 + (size_t)wk.e * K * (N / 2) + (size_t)(kPfRT * ob) * src.wstep;
+  src.sbase = a.s2 + (size_t)wk.e * K * (N / 32) + (size_t)(kPfRT * ob) * src.sstep;
+  src.nrt = kPfRT;
   src.kbytes = N;
 #pragma unroll
   for (int j = 0; j < 2; j++) {
@@ -360,24 +383,24 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a8(GemmArgs a) {
     s_r[tid] = r;
     s_w[tid] = a.topk_w[r];
   }
-  v4f acc[4][2];
-  zero_acc(acc);
-  pf_kloop<true, kPfStages2>(L, src, acc);
+  v4f acc[kPfQ][2];
+  zero_acc<kPfQ>(acc);
+  pf_kloop<true>(L, src, acc);
   __syncthreads();   // s_r / s_w visible
-  pf_combine(a, wk, acc, s_r, s_w, (size_t)128 * ob + 64 * wr + c, wc, c, g);
+  pf_combine<kPfQ>(a, wk, acc, s_r, s_w, (size_t)256 * ob + 128 * wr + c, wc, c, g);
 }
 
 static int pf_grid(int grid_tiles, int nsub) { return (grid_tiles * nsub + 7) / 8 * 8; }
 
 hipError_t launch_pf_gemm1(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pf_gemm1_a8, dim3(pf_grid(grid_tiles, a.N / 64)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_pf_gemm1_a8, dim3(pf_grid(grid_tiles, (a.N + 127) / 128)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pf_gemm2_a8, dim3(pf_grid(grid_tiles, a.K / 128)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_pf_gemm2_a8, dim3(pf_grid(grid_tiles, a.K / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -407,8 +430,8 @@ struct Pf16Loads {
 template <int WF>
 struct Pf16Stage {
   static constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
-  uint8_t A[kPfRowTiles][64 * U];
-  uint8_t AS[kPfRowTiles][64 * SU];
+  uint8_t A[8][64 * U];
+  uint8_t AS[8][64 * SU];
   uint8_t spare[256];   // NF3: landing slot of the scale loads of waves 2, 3
   uint8_t B[kPfTileRows][256];
 };
@@ -693,7 +716,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
     src.brow[j] = a.xb + (size_t)(a.perm[wk.p0 + (row < wk.rows ? row : 0)] / a.topk) * K;
   }
   v4f acc[4][2];
-  zero_acc(acc);
+  zero_acc<4>(acc);
   pf16_kloop<WF, false>(L, src, acc);
   // epilogue: row tiles 4wr + {0,1,2,3} = up/gate of intermediate blocks 4hb + 2wr + {0,1}
   const float gs = a.g13 ? a.g13[wk.e] : 1.0f;
@@ -745,10 +768,10 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
     s_w[tid] = a.topk_w[r] * (a.g2 ? a.g2[wk.e] : 1.0f);
   }
   v4f acc[4][2];
-  zero_acc(acc);
+  zero_acc<4>(acc);
   pf16_kloop<WF, true>(L, src, acc);
   __syncthreads();   // s_r / s_w visible
-  pf_combine(a, wk, acc, s_r, s_w, (size_t)128 * ob + 64 * wr + c, wc, c, g);
+  pf_combine<4>(a, wk, acc, s_r, s_w, (size_t)128 * ob + 64 * wr + c, wc, c, g);
 }
 
 template <int WF>
