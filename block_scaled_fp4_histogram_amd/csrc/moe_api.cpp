@@ -197,11 +197,12 @@ int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const ui
 
 bool use_decode(const moe_plan_s *p, int T) {
   // the decode GEMM1 stages at least one token row in its LDS budget, and the
-  // W4A8 GEMM2 all routes' MXFP8 rows of the intermediate
+  // down GEMM all routes' rows of the intermediate
   const bool a8 = p->afmt == MOE_A_MXFP8;
   const long row = a8 ? (long)p->K + 16 + p->K / 32 : 2L * (p->K + 8);
-  const long lds2 = a8 ? (long)moe::dec2_hq_bytes(T * p->topk, p->N) + moe::dec2_hs_bytes(T * p->topk, p->N) : 0;
-  const bool lds_ok = row <= moe::kDecStageBytes && lds2 <= 49152;
+  const long lds2 = a8 ? (long)moe::dec2_hq_bytes(T * p->topk, p->N) + moe::dec2_hs_bytes(T * p->topk, p->N)
+                       : (long)moe::dec2_hb_bytes(T * p->topk, p->N);
+  const bool lds_ok = row <= moe::kDecStageBytes && lds2 <= moe::kDec2MaxLds;
   return T <= moe::kDecodeMaxT && T * p->topk <= moe::kDecodeMaxRoutes && lds_ok;
 }
 

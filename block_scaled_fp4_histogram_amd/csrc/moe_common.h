@@ -30,6 +30,9 @@ constexpr int kDecStageBytes = 45056;
 // (stride hs_stride(N)) rounded up to whole 256-byte chunks.
 __host__ __device__ constexpr int dec2_hq_bytes(int R, int N) { return (R * (N + 16) + 1023) & ~1023; }
 __host__ __device__ constexpr int dec2_hs_bytes(int R, int N) { return (R * hs_stride(N) + 255) & ~255; }
+// W4A16: every route's bf16 intermediate row (stride 2 N + 16 bytes) in whole 1 KB chunks.
+__host__ __device__ constexpr int dec2_hb_bytes(int R, int N) { return (R * (2 * N + 16) + 1023) & ~1023; }
+constexpr int kDec2MaxLds = 73728;   // dynamic LDS bound of the decode down GEMM (two blocks per CU)
 
 // Route planner: ids -> per-expert counts, offsets, stable permutation, tile table.
 struct RouteArgs {

@@ -370,7 +370,9 @@ __global__ __launch_bounds__(256, 4) void k_dec_gemm1_a16(DecArgs a) {
   extern __shared__ __align__(16) uint8_t dsm[];
   int ud;
   unsigned long long md;
-  if (!dec_group(dec_route_u(a, threadIdx.x & 63), blockIdx.y, &ud, &md)) return;
+  const int u = dec_route_u(a, threadIdx.x & 63);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) dec_write_groups(a, u);
+  if (!dec_group(u, blockIdx.y, &ud, &md)) return;
   const DecExpert X = dec_expert(a, ud);
   if (X.fmt == W_NVFP4) dec_gemm1_body<false, W_NVFP4, 4>(a, X, md, dsm);
   else dec_gemm1_body<false, W_NF3, 4>(a, X, md, dsm);
@@ -587,40 +589,55 @@ __global__ __launch_bounds__(kDecG2Waves * 64) void k_dec_gemm2_a16(DecArgs a) {
 constexpr int kG2Ring = 6;
 constexpr int kDecG2WavesA8 = 8;
 
-// Position in the item list; the expert's weight streams follow the group.
+// Position in the item list; the expert's weight streams (and format, global
+// scale and this block's row-tile offsets) follow the group.
 struct G2Iter {
-  int item, grp, pass, kt, npass;
+  int item, grp, pass, kt, npass, fmt;
+  float g2;
   unsigned long long md;
   Buf wb, sb;
+  uint32_t w0, s0;   // this block's output row tile within the expert's data / scales
 };
 
-__device__ __forceinline__ void g2_enter_group(G2Iter &it, const DecArgs &a, int gu, unsigned long long gm) {
+// g2v: the groups' global scales, one per lane (loaded up front: a load here
+// would be waited for behind the weight ring).
+__device__ __forceinline__ void g2_enter_group(G2Iter &it, const DecArgs &a, int gu, unsigned long long gm,
+                                               float g2v = 1.0f) {
   it.md = readlane_u64(gm, it.grp);
   it.npass = (__popcll(it.md) + 15) / 16;
-  const DecExpert X = dec_expert(a, __builtin_amdgcn_readlane(gu, it.grp));
+  const int u = __builtin_amdgcn_readlane(gu, it.grp);
+  const bool t1 = a.n_tiers > 1 && u >= a.tier[0].E;
+  const DecTier &T = t1 ? a.tier[1] : a.tier[0];
+  const int e = t1 ? u - a.tier[0].E : u;
   const int groups = a.N / 32;
-  it.wb = make_buf(X.w2 + (size_t)X.e * a.K * groups * 16, (uint32_t)((size_t)a.K * groups * 16));
-  it.sb = make_buf(X.s2 + (size_t)X.e * a.K * groups, (uint32_t)((size_t)a.K * groups));
+  it.fmt = __builtin_amdgcn_readfirstlane(T.fmt);
+  const uint32_t U = it.fmt == W_NF3 ? 12u : 16u, SU = it.fmt == W_NVFP4 ? 2u : 1u;
+  it.g2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2v), it.grp));
+  it.wb = make_buf(T.w2 + (size_t)e * a.K * groups * U, (uint32_t)((size_t)a.K * groups * U));
+  it.sb = make_buf(T.s2 + (size_t)e * a.K * groups * SU, (uint32_t)((size_t)a.K * groups * SU));
+  it.w0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 16u * (uint32_t)groups * U);
+  it.s0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 16u * (uint32_t)groups * SU);
 }
 
 __device__ __forceinline__ void g2_start(G2Iter &it, const DecArgs &a, int item, int istart, int ng, int nkt, int gu,
-                                         unsigned long long gm) {
+                                         unsigned long long gm, float g2v = 1.0f) {
   const int l = threadIdx.x & 63;
   it.item = item;
   it.grp = max(0, __popcll(__ballot(l < ng && istart <= item)) - 1);
   const int rel = item - __builtin_amdgcn_readlane(istart, it.grp);
   it.pass = rel / nkt;
   it.kt = rel - it.pass * nkt;
-  g2_enter_group(it, a, gu, gm);
+  g2_enter_group(it, a, gu, gm, g2v);
 }
 
-__device__ __forceinline__ void g2_next(G2Iter &it, const DecArgs &a, int ng, int nkt, int gu, unsigned long long gm) {
+__device__ __forceinline__ void g2_next(G2Iter &it, const DecArgs &a, int ng, int nkt, int gu, unsigned long long gm,
+                                        float g2v = 1.0f) {
   it.item++;
   if (++it.kt < nkt) return;
   it.kt = 0;
   if (++it.pass < it.npass) return;
   it.pass = 0;
-  if (++it.grp < ng) g2_enter_group(it, a, gu, gm);
+  if (++it.grp < ng) g2_enter_group(it, a, gu, gm, g2v);
 }
 
 __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) {
@@ -631,8 +648,7 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   // wave-uniform values are pinned to scalar registers: derived from them, the
   // item bounds and weight descriptors stay scalar through the ring's branches
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
-  const int K = a.K, N = a.N, nkt = (N + 127) / 128, groups = N / 32, rt = blockIdx.x;
-  const uint32_t w0 = (uint32_t)((size_t)rt * 16 * groups * 16), s0 = (uint32_t)((size_t)rt * 16 * groups);
+  const int K = a.K, N = a.N, nkt = (N + 127) / 128, rt = blockIdx.x;
   // expert groups (one per lane) and item offsets, from the up/gate kernel
   const DecGroups *G = a.groups;
   const int ng = __builtin_amdgcn_readfirstlane(G->ng), NI = __builtin_amdgcn_readfirstlane(G->nitems);
@@ -656,13 +672,14 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   else is.item = i1;
   auto issue = [&](int s) {
     const bool ok = is.item < i1 && is.kt * 128 + 32 * g < N;
-    A[s] = buf_load16(is.wb, ok ? (uint32_t)is.kt * 1024u + (uint32_t)l * 16u : 0x80000000u, w0);
-    sa[s] = buf_load1(is.sb, ok ? (uint32_t)is.kt * 64u + (uint32_t)l : 0x80000000u, s0);
+    A[s] = buf_load16(is.wb, ok ? (uint32_t)is.kt * 1024u + (uint32_t)l * 16u : 0x80000000u, is.w0);
+    sa[s] = buf_load1(is.sb, ok ? (uint32_t)is.kt * 64u + (uint32_t)l : 0x80000000u, is.s0);
     if (is.item < i1) g2_next(is, a, ng, nkt, gu, gm);
   };
   if (i0 >= i1) {   // no items: the ring's loads still need valid descriptors
     is.wb = make_buf(a.hq, 0);
     is.sb = is.wb;
+    is.w0 = is.s0 = 0;
   }
   // every route's MXFP8 intermediate row and scales -> LDS by direct loads
   // (1 KB / 256-byte chunks; bytes past the rows read a valid dummy address),
@@ -737,6 +754,144 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   }
 }
 
+// W4A16 / W3A16 down GEMM, grid (K/16 output row tiles): the same item list,
+// wave slices and weight ring as the W4A8 kernel (a slot: NVFP4 16 + 2 bytes
+// or NF3 12 + 1 bytes a lane, per the group's tier); every route's bf16
+// intermediate row is staged in LDS by direct loads.  Each item is four
+// dequantise-and-multiply steps of 8 columns (bf16 MFMA).
+constexpr int kG2RingA16 = 6;
+
+__global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t dsm2[];
+  __shared__ float wr_s[kDecodeMaxRoutes];
+  __shared__ __align__(16) float yb[kDecG2WavesA8][256];   // per-wave fold tile, then its token sums
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
+  const int K = a.K, N = a.N, nkt = (N + 127) / 128, rt = blockIdx.x;
+  const DecGroups *G = a.groups;
+  const int ng = __builtin_amdgcn_readfirstlane(G->ng), NI = __builtin_amdgcn_readfirstlane(G->nitems);
+  int gu = G->gu[l], istart = G->istart[l];
+  uint32_t gm_lo = (uint32_t)G->gm[l], gm_hi = (uint32_t)(G->gm[l] >> 32);
+  float wv = tid < a.R ? a.topk_w[tid] : 0.f;
+  float g2v = 1.0f;   // global scale of group l's expert
+  if (l < ng) {
+    const bool t1 = a.n_tiers > 1 && gu >= a.tier[0].E;
+    const float *g2p = t1 ? a.tier[1].g2 : a.tier[0].g2;
+    if (g2p) g2v = g2p[t1 ? gu - a.tier[0].E : gu];
+  }
+  // the table, router weights and scales are complete here; re-defined by an
+  // empty asm, their registers carry no pending load
+  wait_vm<0>();
+  asm volatile("" : "+v"(gu), "+v"(istart), "+v"(gm_lo), "+v"(gm_hi), "+v"(wv), "+v"(g2v));
+  const unsigned long long gm = ((unsigned long long)gm_hi << 32) | gm_lo;
+  if (tid < a.R) wr_s[tid] = wv;
+  const int per = (NI + kDecG2WavesA8 - 1) / kDecG2WavesA8;
+  const int i0 = min(NI, w * per), i1 = min(NI, i0 + per);
+  v3i A3[kG2RingA16];   // weight bytes 0..11 of the lane
+  uint32_t A4[kG2RingA16], sa[kG2RingA16];
+  G2Iter is;
+  if (i0 < i1) g2_start(is, a, i0, istart, ng, nkt, gu, gm, g2v);
+  else is.item = i1;
+  if (i0 >= i1) {   // no items: the ring's loads still need valid descriptors
+    is.wb = make_buf(a.hb, 0);
+    is.sb = is.wb;
+    is.w0 = is.s0 = 0;
+    is.fmt = W_NVFP4;
+    is.kt = 0;
+  }
+  // one instruction shape for both formats (no branch: a loaded value copied
+  // out of a branch would have to be waited for): 12 data bytes, the 4th
+  // dword (NVFP4 only; NF3 loads out of range), and an aligned 16-bit scale
+  // load (NVFP4: the lane's two E4M3 bytes; NF3: the pair holding its byte)
+  auto issue = [&](int s) {
+    const bool ok = is.item < i1 && is.kt * 128 + 32 * g < N;
+    const bool nv = is.fmt == W_NVFP4;
+    const uint32_t U = nv ? 16u : 12u;
+    const uint32_t dv = ok ? (uint32_t)is.kt * 64u * U + (uint32_t)l * U : 0x80000000u;
+    A3[s] = buf_load12(is.wb, dv, is.w0);
+    A4[s] = buf_load4(is.wb, nv && ok ? dv + 12u : 0x80000000u, is.w0);
+    sa[s] = buf_load2(is.sb, ok ? (nv ? (uint32_t)is.kt * 128u + (uint32_t)l * 2u : (uint32_t)is.kt * 64u + (uint32_t)(l & ~1))
+                                : 0x80000000u, is.s0);
+    if (is.item < i1) g2_next(is, a, ng, nkt, gu, gm, g2v);
+  };
+  // every route's bf16 intermediate row -> LDS (row stride N + 8 elements),
+  // 1 KB direct loads issued ahead of the ring
+  const uint16_t *hb_s = (const uint16_t *)dsm2;
+  {
+    const int rs = 2 * N + 16;
+    for (int ch = w; ch * 1024 < dec2_hb_bytes(a.R, N); ch += kDecG2WavesA8) {
+      const int pos = ch * 1024 + l * 16, row = pos / rs, col = pos - row * rs;
+      dma16(row < a.R && col < 2 * N ? (const uint8_t *)a.hb + (size_t)row * 2 * N + col : (const uint8_t *)a.hb,
+            dsm2 + ch * 1024);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kG2RingA16; s++) issue(s);
+  wait_vm<3 * kG2RingA16>();   // the staged rows have landed (the ring's 3 loads a slot may be in flight)
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  float tok[4] = {0.f, 0.f, 0.f, 0.f};
+  G2Iter ic;
+  if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkt, gu, gm, g2v);
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  int r = -1;
+  for (int base = i0; base < i1; base += kG2RingA16) {
+#pragma unroll
+    for (int s = 0; s < kG2RingA16; s++) {
+      if (base + s < i1) {
+        if (s == 0 || ic.kt == 0 || base + s == i0) {   // route column of this lane in the current run
+          const int col = ic.pass * 16 + c;
+          r = col < __popcll(ic.md) ? nth_bit(ic.md, col) : -1;
+        }
+        const int kb = ic.kt * 128 + 32 * g;
+        v4i B[4];
+#pragma unroll
+        for (int st = 0; st < 4; st++) B[st] = v4i{0, 0, 0, 0};
+        if (r >= 0 && kb < N) {
+          const v4i *hp = (const v4i *)(hb_s + r * (N + 8) + kb);
+#pragma unroll
+          for (int st = 0; st < 4; st++) B[st] = hp[st];
+        }
+        const uint32_t sc = sa[s], d[4] = {(uint32_t)A3[s][0], (uint32_t)A3[s][1], (uint32_t)A3[s][2], A4[s]};
+        if (ic.fmt == W_NVFP4) {
+          const float slo = e4m3_f32(sc & 0xFFu), shi = e4m3_f32((sc >> 8) & 0xFFu);
+#pragma unroll
+          for (int st = 0; st < 4; st++)
+            acc = mfma_bf16(nvfp4_step(d[st], st < 2 ? slo : shi), __builtin_bit_cast(v8bf, B[st]), acc);
+        } else {
+          const float f = e4m3_f32((l & 1) ? (sc >> 8) & 0xFFu : sc & 0xFFu);
+          const uint32_t t01 = pack_bf16x2(0.1275f * f, 0.3563f * f), t23 = pack_bf16x2(0.6047f * f, f);
+#pragma unroll
+          for (int st = 0; st < 4; st++)
+            acc = mfma_bf16(nf3_step_lut(nf3_group(d[0], d[1], d[2], st), t01, t23), __builtin_bit_cast(v8bf, B[st]), acc);
+        }
+        if (ic.kt == nkt - 1 || base + s + 1 == i1) {
+          dec_fold_lds(a, ic.md, ic.pass * 16, c, g, acc, r >= 0 ? wr_s[r] * ic.g2 : 0.f, &yb[w][0], tok);
+          acc = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        g2_next(ic, a, ng, nkt, gu, gm, g2v);
+      }
+      issue(s);   // the item kG2RingA16 ahead (out of range past the slice)
+    }
+  }
+  float *tw = &yb[w][0];   // this wave's token sums [4][64], in its own fold tile
+#pragma unroll
+  for (int i = 0; i < 4; i++) tw[i * 64 + l] = tok[i];
+  __syncthreads();
+  if (w == 0 && c < a.T) {
+    float s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      s4[i] = 0.f;
+#pragma unroll
+      for (int v = 0; v < kDecG2WavesA8; v++) s4[i] += yb[v][i * 64 + l];
+    }
+    uint2 o;
+    o.x = pack_bf16x2(s4[0], s4[1]);
+    o.y = pack_bf16x2(s4[2], s4[3]);
+    *(uint2 *)(a.out + (size_t)c * K + rt * 16 + 4 * g) = o;
+  }
+}
+
 int decode_cpass(int K, int a8) {
   const int row = a8 ? K + 16 + K / 32 : 2 * (K + 8);
   return max(1, min(kDecodeMaxT, kDecStageBytes / row));
@@ -763,7 +918,7 @@ hipError_t launch_decode(int a8, const DecArgs &a, hipStream_t s, hipEvent_t ev_
   }
   const size_t lds2 = a8 ? (size_t)dec2_hq_bytes(a.R, a.N) + dec2_hs_bytes(a.R, a.N) : 0;
   if (a8) hipLaunchKernelGGL(k_dec_gemm2_a8, g2, dim3(kDecG2WavesA8 * 64), lds2, s, a);
-  else hipLaunchKernelGGL(k_dec_gemm2_a16, g2, dim3(kDecG2Waves * 64), 0, s, a);
+  else hipLaunchKernelGGL(k_dec_gemm2_a16r, g2, dim3(kDecG2WavesA8 * 64), (size_t)dec2_hb_bytes(a.R, a.N), s, a);
   return hipGetLastError();
 }
 

@@ -225,6 +225,33 @@ __device__ __forceinline__ v8bf nf3_step(uint32_t w24, float m0, float m1, float
   return __builtin_bit_cast(v8bf, r);
 }
 
+// 24-bit NF3 group (8 codes) -> 8 bf16 through a 4-entry table of the rounded
+// magnitudes (t01 = |v0| | |v1| << 16, t23 likewise): per code pair one byte
+// permute picks both magnitudes, then the sign bits are or-ed in.  A code c
+// stands for +mag[c - 4] (c >= 4) or -mag[3 - c]; the bits are worked on for
+// all eight codes at once.
+__device__ __forceinline__ v8bf nf3_step_lut(uint32_t w24, uint32_t t01, uint32_t t23) {
+  const uint32_t neg = (~w24 >> 2) & 0x249249u;             // bit 3e: code e is negative
+  const uint32_t idx = (w24 ^ (neg * 3u)) & 0x6DB6DBu;      // bits 3e, 3e + 1: magnitude index of code e
+  v4i r;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const uint32_t x = ((idx >> (6 * m)) & 3u) | (((idx >> (6 * m + 3)) & 3u) << 16);
+    const uint32_t sel = ((x | (x << 8)) << 1) + 0x01000100u;
+    const uint32_t sgn = (((neg >> (6 * m)) & 1u) << 15) | (((neg >> (6 * m + 3)) & 1u) << 31);
+    r[m] = (int)(__builtin_amdgcn_perm(t23, t01, sel) | sgn);
+  }
+  return __builtin_bit_cast(v8bf, r);
+}
+
+// The 24-bit group s (codes 8 s .. 8 s + 7) of a lane's 12 NF3 bytes d0..d2.
+__device__ __forceinline__ uint32_t nf3_group(uint32_t d0, uint32_t d1, uint32_t d2, int s) {
+  return s == 0 ? (d0 & 0xFFFFFFu)
+       : s == 1 ? ((d0 >> 24) | (d1 << 8)) & 0xFFFFFFu
+       : s == 2 ? ((d1 >> 16) | (d2 << 16)) & 0xFFFFFFu
+                : d2 >> 8;
+}
+
 // Dequantised operand of one lane for k-step s (0..3) of a 128-column k-tile.
 template <int WF>
 struct A16Tile {

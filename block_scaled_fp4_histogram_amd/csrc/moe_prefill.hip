@@ -593,25 +593,6 @@ __device__ __forceinline__ void pf16_wait(Pf16Ops<WF> &o) {
                     "+v"(o.b[0][2]), "+v"(o.b[0][3]), "+v"(o.b[1][0]), "+v"(o.b[1][1]), "+v"(o.b[1][2]), "+v"(o.b[1][3]));
 }
 
-// 24-bit NF3 group (8 codes) -> 8 bf16 through a 4-entry table of the rounded
-// magnitudes (t01 = |v0| | |v1| << 16, t23 likewise): per code pair one byte
-// permute picks both magnitudes, then the sign bits are or-ed in.  A code c
-// stands for +mag[c - 4] (c >= 4) or -mag[3 - c]; the bits are worked on for
-// all eight codes at once.
-__device__ __forceinline__ v8bf nf3_step_lut(uint32_t w24, uint32_t t01, uint32_t t23) {
-  const uint32_t neg = (~w24 >> 2) & 0x249249u;             // bit 3e: code e is negative
-  const uint32_t idx = (w24 ^ (neg * 3u)) & 0x6DB6DBu;      // bits 3e, 3e + 1: magnitude index of code e
-  v4i r;
-#pragma unroll
-  for (int m = 0; m < 4; m++) {
-    const uint32_t x = ((idx >> (6 * m)) & 3u) | (((idx >> (6 * m + 3)) & 3u) << 16);
-    const uint32_t sel = ((x | (x << 8)) << 1) + 0x01000100u;
-    const uint32_t sgn = (((neg >> (6 * m)) & 1u) << 15) | (((neg >> (6 * m + 3)) & 1u) << 31);
-    r[m] = (int)(__builtin_amdgcn_perm(t23, t01, sel) | sgn);
-  }
-  return __builtin_bit_cast(v8bf, r);
-}
-
 // 32 bf16 MFMAs of one k-tile.  Columns past the reduction length: scale 0
 // (weights 0) and activations 0.  SWAP: activations as the A operand.  Scale
 // decoding (and the NF3 magnitude table) is done once per row tile, not per
@@ -645,13 +626,7 @@ __device__ __forceinline__ void pf16_mma(const Pf16Ops<WF> &o, int kt, int kcols
       if constexpr (WF == W_NVFP4) {
         aop = nvfp4_step(o.a[q][s], s < 2 ? slo[q] : shi[q]);
       } else {
-        // group s of 24 bits starts at bit 24 s of the lane's 96-bit word
-        const uint32_t d0 = o.a[q][0], d1 = o.a[q][1], d2 = o.a[q][2];
-        const uint32_t w24 = s == 0 ? (d0 & 0xFFFFFFu)
-                             : s == 1 ? ((d0 >> 24) | (d1 << 8)) & 0xFFFFFFu
-                             : s == 2 ? ((d1 >> 16) | (d2 << 16)) & 0xFFFFFFu
-                                      : d2 >> 8;
-        aop = nf3_step_lut(w24, t01[q], t23[q]);
+        aop = nf3_step_lut(nf3_group(o.a[q][0], o.a[q][1], o.a[q][2], s), t01[q], t23[q]);
       }
 #pragma unroll
       for (int cb = 0; cb < 2; cb++) acc[q][cb] = SWAP ? mfma_bf16(bop[cb], aop, acc[q][cb]) : mfma_bf16(aop, bop[cb], acc[q][cb]);
