@@ -247,20 +247,20 @@ __device__ __forceinline__ void zero_acc(v4f (*acc)[2]) {
 }
 
 // Down-GEMM combine from accumulators in the swapped layout: acc[q][cb][i] is
-// route 32 wc + 16 cb + 4 g + i (tile row), output column col + 16 q; s_r, s_w
+// route 32 wc + 16 cb + 4 g + i (tile row; cb < CB), output column col + 16 q; s_r, s_w
 // hold each tile row's route and its router weight (times the expert's global
 // scale).  Deterministic mode writes bf16 route-buffer rows (lanes c, c ^ 1
 // swap one value so each stores two adjacent columns of one route); atomic mode
 // adds fp32 into the token accumulator, 4 routes x 16 consecutive columns per
 // instruction.
-template <int Q>
-__device__ __forceinline__ void pf_combine(const GemmArgs &a, const PfWork &wk, v4f (*acc)[2], const int *s_r,
+template <int Q, int CB>
+__device__ __forceinline__ void pf_combine(const GemmArgs &a, const PfWork &wk, v4f (*acc)[CB], const int *s_r,
                                            const float *s_w, size_t col, int wc, int c, int g) {
   const int K = a.K;
   if (a.deterministic) {
     const bool odd = c & 1;
 #pragma unroll
-    for (int cb = 0; cb < 2; cb++)
+    for (int cb = 0; cb < CB; cb++)
 #pragma unroll
       for (int ip = 0; ip < 2; ip++) {
         const int row = 32 * wc + 16 * cb + 4 * g + 2 * ip + (odd ? 1 : 0);
@@ -277,7 +277,7 @@ __device__ __forceinline__ void pf_combine(const GemmArgs &a, const PfWork &wk, 
       }
   } else {
 #pragma unroll
-    for (int cb = 0; cb < 2; cb++)
+    for (int cb = 0; cb < CB; cb++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int row = 32 * wc + 16 * cb + 4 * g + i;
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a8(GemmArgs a) {
   zero_acc<kPfQ>(acc);
   pf_kloop<true>(L, src, acc);
   __syncthreads();   // s_r / s_w visible
-  pf_combine<kPfQ>(a, wk, acc, s_r, s_w, (size_t)256 * ob + 128 * wr + c, wc, c, g);
+  pf_combine<kPfQ, 2>(a, wk, acc, s_r, s_w, (size_t)256 * ob + 128 * wr + c, wc, c, g);
 }
 
 static int pf_grid(int grid_tiles, int nsub) { return (grid_tiles * nsub + 7) / 8 * 8; }
@@ -406,14 +406,14 @@ hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s) {
 
 // ================================================================ W4A16 / W3A16
 //
-// The same 64-route tiles, 2 x 2 waves and LDS ring for NVFP4 and NF3 experts
-// with bf16 activations.  A ring stage holds 8 weight row tiles of one
-// 128-column k-tile in MFMA lane order (16 / 12 bytes and 2 / 1 scale bytes per
-// lane) and the 64 routes' bf16 activation slices (256 bytes each, 16-byte
-// chunks XOR-swizzled by row % 16).  Each wave dequantises its 4 row tiles one
-// 8-column step at a time (E2M1 x E4M3, or NF3 codebook x E4M3, to bf16; exact
-// for E2M1) and feeds bf16 MFMAs: 4 steps x 4 row tiles x 2 route blocks per
-// k-tile.  Every wave issues eight loads per stage.
+// The same 64-route tiles and LDS ring for NVFP4 and NF3 experts with bf16
+// activations.  A ring stage holds 8 weight row tiles of one 128-column k-tile
+// in MFMA lane order (16 / 12 bytes and 2 / 1 scale bytes per lane) and the 64
+// routes' bf16 activation slices (256 bytes each, 16-byte chunks XOR-swizzled
+// by row % 16).  Wave w owns row tiles 2w, 2w + 1 against all 64 routes, so
+// each weight element is dequantised once per tile, one 8-column step at a
+// time (E2M1 x E4M3, or NF3 codebook x E4M3, to bf16; exact for E2M1), and
+// feeds 4 bf16 MFMAs: 4 steps x 2 row tiles x 4 route blocks per k-tile.
 namespace {
 
 constexpr int kPf16Stages = 3;
@@ -502,109 +502,124 @@ __device__ __forceinline__ void pf16_issue(Pf16Stage<WF> &S, const Pf16Src &src,
   }
 }
 
+// One wave's operands of a landed stage: its 2 weight row tiles (2w, 2w + 1)
+// and all 64 routes' activation chunks (4 steps x 4 route blocks).
 template <int WF>
 struct Pf16Ops {
-  uint32_t a[4][4];   // row tile q: NVFP4 4 dwords, NF3 3 dwords (+1 unused)
-  int sc[4];
-  v4i b[2][4];        // route block cb, step s
+  uint32_t a[2][4];   // row tile q: NVFP4 4 dwords, NF3 3 dwords (+1 unused)
+  int sc[2];
+  v4i b[4][4];        // step s, route block cb
 };
 
-// LDS reads of one wave's operands (asm: invisible to the compiler's
-// direct-to-LDS bookkeeping, as for the W4A8 kernels); pf16_wait completes them.
+// LDS reads of one wave's operands, weights first, then activations step by
+// step (asm: invisible to the compiler's direct-to-LDS bookkeeping, as for the
+// W4A8 kernels).  LDS reads return in order, so pf16_wait_step<s> waits for
+// the weights and the activations of steps 0 .. s only.
 template <int WF>
-__device__ __forceinline__ void pf16_read(Pf16Ops<WF> &o, const Pf16Stage<WF> &S, int wr, int wc, int l) {
+__device__ __forceinline__ void pf16_read(Pf16Ops<WF> &o, const Pf16Stage<WF> &S, int w, int l) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
   const int c = l & 15, g = l >> 4;
-  const uint32_t va = lds_addr(&S.A[4 * wr][l * U]), vs = lds_addr(&S.AS[4 * wr][l * SU]);
-  const uint8_t *brow = &S.B[32 * wc + c][0];   // + 16 rows for cb = 1
-  uint32_t vb[4];
-#pragma unroll
-  for (int s = 0; s < 4; s++) vb[s] = lds_addr(brow + 16 * ((4 * g + s) ^ c));
+  const uint32_t va = lds_addr(&S.A[2 * w][l * U]), vs = lds_addr(&S.AS[2 * w][l * SU]);
+  const uint8_t *brow = &S.B[c][0];   // + 16 rows (4096 bytes) per route block
   if constexpr (WF == W_NVFP4) {
-    v4i a0, a1, a2, a3;
+    v4i a0, a1;
     asm volatile(
-        "ds_read_b128 %0, %8\n"
-        "ds_read_b128 %1, %8 offset:1024\n"
-        "ds_read_b128 %2, %8 offset:2048\n"
-        "ds_read_b128 %3, %8 offset:3072\n"
-        "ds_read_u16 %4, %9\n"
-        "ds_read_u16 %5, %9 offset:128\n"
-        "ds_read_u16 %6, %9 offset:256\n"
-        "ds_read_u16 %7, %9 offset:384"
-        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(o.sc[0]), "=&v"(o.sc[1]), "=&v"(o.sc[2]), "=&v"(o.sc[3])
+        "ds_read_b128 %0, %4\n"
+        "ds_read_b128 %1, %4 offset:1024\n"
+        "ds_read_u16 %2, %5\n"
+        "ds_read_u16 %3, %5 offset:128"
+        : "=&v"(a0), "=&v"(a1), "=&v"(o.sc[0]), "=&v"(o.sc[1])
         : "v"(va), "v"(vs)
         : "memory");
-    const v4i av[4] = {a0, a1, a2, a3};
 #pragma unroll
-    for (int q = 0; q < 4; q++)
-#pragma unroll
-      for (int d = 0; d < 4; d++) o.a[q][d] = (uint32_t)av[q][d];
+    for (int d = 0; d < 4; d++) {
+      o.a[0][d] = (uint32_t)a0[d];
+      o.a[1][d] = (uint32_t)a1[d];
+    }
   } else {
     // 12-byte lanes are only 4-byte aligned: three dword reads per row tile
     asm volatile(
-        "ds_read_b32 %0, %16\n"
-        "ds_read_b32 %1, %16 offset:4\n"
-        "ds_read_b32 %2, %16 offset:8\n"
-        "ds_read_b32 %3, %16 offset:768\n"
-        "ds_read_b32 %4, %16 offset:772\n"
-        "ds_read_b32 %5, %16 offset:776\n"
-        "ds_read_b32 %6, %16 offset:1536\n"
-        "ds_read_b32 %7, %16 offset:1540\n"
-        "ds_read_b32 %8, %16 offset:1544\n"
-        "ds_read_b32 %9, %16 offset:2304\n"
-        "ds_read_b32 %10, %16 offset:2308\n"
-        "ds_read_b32 %11, %16 offset:2312\n"
-        "ds_read_u8 %12, %17\n"
-        "ds_read_u8 %13, %17 offset:64\n"
-        "ds_read_u8 %14, %17 offset:128\n"
-        "ds_read_u8 %15, %17 offset:192"
+        "ds_read_b32 %0, %8\n"
+        "ds_read_b32 %1, %8 offset:4\n"
+        "ds_read_b32 %2, %8 offset:8\n"
+        "ds_read_b32 %3, %8 offset:768\n"
+        "ds_read_b32 %4, %8 offset:772\n"
+        "ds_read_b32 %5, %8 offset:776\n"
+        "ds_read_u8 %6, %9\n"
+        "ds_read_u8 %7, %9 offset:64"
         : "=&v"(o.a[0][0]), "=&v"(o.a[0][1]), "=&v"(o.a[0][2]), "=&v"(o.a[1][0]), "=&v"(o.a[1][1]), "=&v"(o.a[1][2]),
-          "=&v"(o.a[2][0]), "=&v"(o.a[2][1]), "=&v"(o.a[2][2]), "=&v"(o.a[3][0]), "=&v"(o.a[3][1]), "=&v"(o.a[3][2]),
-          "=&v"(o.sc[0]), "=&v"(o.sc[1]), "=&v"(o.sc[2]), "=&v"(o.sc[3])
+          "=&v"(o.sc[0]), "=&v"(o.sc[1])
         : "v"(va), "v"(vs)
         : "memory");
-#pragma unroll
-    for (int q = 0; q < 4; q++) o.a[q][3] = 0;
+    o.a[0][3] = o.a[1][3] = 0;
   }
-  asm volatile(
-      "ds_read_b128 %0, %8\n"
-      "ds_read_b128 %1, %9\n"
-      "ds_read_b128 %2, %10\n"
-      "ds_read_b128 %3, %11\n"
-      "ds_read_b128 %4, %8 offset:4096\n"
-      "ds_read_b128 %5, %9 offset:4096\n"
-      "ds_read_b128 %6, %10 offset:4096\n"
-      "ds_read_b128 %7, %11 offset:4096"
-      : "=&v"(o.b[0][0]), "=&v"(o.b[0][1]), "=&v"(o.b[0][2]), "=&v"(o.b[0][3]), "=&v"(o.b[1][0]), "=&v"(o.b[1][1]),
-        "=&v"(o.b[1][2]), "=&v"(o.b[1][3])
-      : "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3])
-      : "memory");
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const uint32_t vb = lds_addr(brow + 16 * ((4 * g + s) ^ c));
+    asm volatile(
+        "ds_read_b128 %0, %4\n"
+        "ds_read_b128 %1, %4 offset:4096\n"
+        "ds_read_b128 %2, %4 offset:8192\n"
+        "ds_read_b128 %3, %4 offset:12288"
+        : "=&v"(o.b[s][0]), "=&v"(o.b[s][1]), "=&v"(o.b[s][2]), "=&v"(o.b[s][3])
+        : "v"(vb)
+        : "memory");
+  }
 }
 
-template <int WF>
-__device__ __forceinline__ void pf16_wait(Pf16Ops<WF> &o) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(o.a[0][0]), "+v"(o.a[0][1]), "+v"(o.a[0][2]), "+v"(o.a[0][3]), "+v"(o.a[1][0]), "+v"(o.a[1][1]),
-                 "+v"(o.a[1][2]), "+v"(o.a[1][3]), "+v"(o.a[2][0]), "+v"(o.a[2][1]), "+v"(o.a[2][2]), "+v"(o.a[2][3]),
-                 "+v"(o.a[3][0]), "+v"(o.a[3][1]), "+v"(o.a[3][2]), "+v"(o.a[3][3])
-               :
-               : "memory");
-  asm volatile("" : "+v"(o.sc[0]), "+v"(o.sc[1]), "+v"(o.sc[2]), "+v"(o.sc[3]), "+v"(o.b[0][0]), "+v"(o.b[0][1]),
-                    "+v"(o.b[0][2]), "+v"(o.b[0][3]), "+v"(o.b[1][0]), "+v"(o.b[1][1]), "+v"(o.b[1][2]), "+v"(o.b[1][3]));
+// Completes the reads up to the activations of step S (4 reads per later step
+// may stay in flight); the empty-looking register operands tie the wait to the
+// values it makes valid.
+template <int WF, int S>
+__device__ __forceinline__ void pf16_wait_step(Pf16Ops<WF> &o) {
+  if constexpr (S == 0) {
+    asm volatile("s_waitcnt lgkmcnt(12)"
+                 : "+v"(o.a[0][0]), "+v"(o.a[0][1]), "+v"(o.a[0][2]), "+v"(o.a[0][3]), "+v"(o.a[1][0]),
+                   "+v"(o.a[1][1]), "+v"(o.a[1][2]), "+v"(o.a[1][3]), "+v"(o.sc[0]), "+v"(o.sc[1]), "+v"(o.b[0][0]),
+                   "+v"(o.b[0][1]), "+v"(o.b[0][2]), "+v"(o.b[0][3])
+                 :
+                 : "memory");
+  } else if constexpr (S == 1) {
+    asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(o.b[1][0]), "+v"(o.b[1][1]), "+v"(o.b[1][2]), "+v"(o.b[1][3]) : : "memory");
+  } else if constexpr (S == 2) {
+    asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(o.b[2][0]), "+v"(o.b[2][1]), "+v"(o.b[2][2]), "+v"(o.b[2][3]) : : "memory");
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(o.b[3][0]), "+v"(o.b[3][1]), "+v"(o.b[3][2]), "+v"(o.b[3][3]) : : "memory");
+  }
 }
 
-// 32 bf16 MFMAs of one k-tile.  Columns past the reduction length: scale 0
-// (weights 0) and activations 0.  SWAP: activations as the A operand.  Scale
-// decoding (and the NF3 magnitude table) is done once per row tile, not per
-// 8-column step.
+// 8 bf16 MFMAs of step S of a k-tile (2 row tiles x 4 route blocks); each
+// dequantised weight operand feeds 4 MFMAs.  Columns past the reduction
+// length: scale 0 (weights 0) and activations 0.  SWAP: activations as the A
+// operand.
+template <int WF, bool SWAP, int S>
+__device__ __forceinline__ void pf16_mma_step(Pf16Ops<WF> &o, bool gin, const float (&slo)[2], const float (&shi)[2],
+                                              const uint32_t (&t01)[2], const uint32_t (&t23)[2], v4f (*acc)[4]) {
+  if constexpr (S > 0) pf16_wait_step<WF, S>(o);   // step 0: waited for by the caller
+  v8bf bop[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; cb++) bop[cb] = __builtin_bit_cast(v8bf, gin ? o.b[S][cb] : v4i{0, 0, 0, 0});
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    v8bf aop;
+    if constexpr (WF == W_NVFP4) aop = nvfp4_step(o.a[q][S], S < 2 ? slo[q] : shi[q]);
+    else aop = nf3_step_lut(nf3_group(o.a[q][0], o.a[q][1], o.a[q][2], S), t01[q], t23[q]);
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++) acc[q][cb] = SWAP ? mfma_bf16(bop[cb], aop, acc[q][cb]) : mfma_bf16(aop, bop[cb], acc[q][cb]);
+  }
+}
+
+// One k-tile: the scales are decoded once per row tile (NF3: its scaled
+// magnitude table) after the weights have arrived.
 template <int WF, bool SWAP>
-__device__ __forceinline__ void pf16_mma(const Pf16Ops<WF> &o, int kt, int kcols, int l, v4f (*acc)[2]) {
+__device__ __forceinline__ void pf16_mma(Pf16Ops<WF> &o, int kt, int kcols, int l, v4f (*acc)[4]) {
   const int g = l >> 4;
   const bool gin = kt * 128 + 32 * g < kcols;
-  float slo[4], shi[4];
-  uint32_t t01[4], t23[4];
+  pf16_wait_step<WF, 0>(o);
+  float slo[2] = {0.f, 0.f}, shi[2] = {0.f, 0.f};
+  uint32_t t01[2] = {0u, 0u}, t23[2] = {0u, 0u};
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
+  for (int q = 0; q < 2; q++) {
     const uint32_t sc = gin ? (uint32_t)o.sc[q] : 0u;
     if constexpr (WF == W_NVFP4) {
       slo[q] = e4m3_f32(sc & 0xFFu);
@@ -615,55 +630,36 @@ __device__ __forceinline__ void pf16_mma(const Pf16Ops<WF> &o, int kt, int kcols
       t23[q] = pack_bf16x2(0.6047f * f, f);
     }
   }
-#pragma unroll
-  for (int s = 0; s < 4; s++) {
-    v8bf bop[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; cb++) bop[cb] = __builtin_bit_cast(v8bf, gin ? o.b[cb][s] : v4i{0, 0, 0, 0});
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      v8bf aop;
-      if constexpr (WF == W_NVFP4) {
-        aop = nvfp4_step(o.a[q][s], s < 2 ? slo[q] : shi[q]);
-      } else {
-        aop = nf3_step_lut(nf3_group(o.a[q][0], o.a[q][1], o.a[q][2], s), t01[q], t23[q]);
-      }
-#pragma unroll
-      for (int cb = 0; cb < 2; cb++) acc[q][cb] = SWAP ? mfma_bf16(bop[cb], aop, acc[q][cb]) : mfma_bf16(aop, bop[cb], acc[q][cb]);
-    }
-  }
+  pf16_mma_step<WF, SWAP, 0>(o, gin, slo, shi, t01, t23, acc);
+  pf16_mma_step<WF, SWAP, 1>(o, gin, slo, shi, t01, t23, acc);
+  pf16_mma_step<WF, SWAP, 2>(o, gin, slo, shi, t01, t23, acc);
+  pf16_mma_step<WF, SWAP, 3>(o, gin, slo, shi, t01, t23, acc);
+}
+
+// One k-tile of the ring: stage kt is read straight after the barrier that
+// proves it landed for every wave (and that every wave is done with stage
+// kt - 1, whose slot then takes stage kt + ST - 1).
+template <int WF, bool SWAP>
+__device__ __forceinline__ void pf16_step(Pf16Lds<WF> &L, const Pf16Src &src, int kt, int nkt, v4f (*acc)[4]) {
+  constexpr int ST = kPf16Stages;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  wait16_stages<WF>(min(ST - 2, nkt - 1 - kt));   // stage kt has landed
+  __builtin_amdgcn_s_barrier();
+  Pf16Ops<WF> o;
+  pf16_read<WF>(o, L.st[kt % ST], w, l);
+  if (kt + ST - 1 < nkt) pf16_issue<WF>(L.st[(kt + ST - 1) % ST], src, kt + ST - 1, w, l);
+  pf16_mma<WF, SWAP>(o, kt, src.kcols, l, acc);
 }
 
 template <int WF, bool SWAP>
-__device__ __forceinline__ void pf16_step(Pf16Lds<WF> &L, const Pf16Src &src, int kt, int nkt, Pf16Ops<WF> &cur,
-                                          Pf16Ops<WF> &nxt, v4f (*acc)[2]) {
+__device__ __forceinline__ void pf16_kloop(Pf16Lds<WF> &L, const Pf16Src &src, v4f (*acc)[4]) {
   constexpr int ST = kPf16Stages;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wr = w >> 1, wc = w & 1;
-  pf16_wait(cur);
-  wait16_stages<WF>(min(ST - 2, nkt - 2 - kt));   // stage kt + 1 has landed
-  __builtin_amdgcn_s_barrier();              // ... for every wave, and no wave reads stage kt any more
-  if (kt + ST < nkt) pf16_issue<WF>(L.st[kt % ST], src, kt + ST, w, l);
-  if (kt + 1 < nkt) pf16_read<WF>(nxt, L.st[(kt + 1) % ST], wr, wc, l);
-  pf16_mma<WF, SWAP>(cur, kt, src.kcols, l, acc);
-}
-
-template <int WF, bool SWAP>
-__device__ __forceinline__ void pf16_kloop(Pf16Lds<WF> &L, const Pf16Src &src, v4f (*acc)[2]) {
-  constexpr int ST = kPf16Stages;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wr = w >> 1, wc = w & 1;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int nkt = (src.kcols + 127) / 128;
 #pragma unroll
-  for (int s = 0; s < ST; s++)
+  for (int s = 0; s < ST - 1; s++)
     if (s < nkt) pf16_issue<WF>(L.st[s], src, s, w, l);
-  wait16_stages<WF>(min(ST - 1, nkt - 1));   // stage 0 has landed
-  __builtin_amdgcn_s_barrier();
-  Pf16Ops<WF> r0, r1;
-  pf16_read<WF>(r0, L.st[0], wr, wc, l);
-  for (int kt = 0; kt + 1 < nkt; kt += 2) {
-    pf16_step<WF, SWAP>(L, src, kt, nkt, r0, r1, acc);
-    pf16_step<WF, SWAP>(L, src, kt + 1, nkt, r1, r0, acc);
-  }
-  if (nkt & 1) pf16_step<WF, SWAP>(L, src, nkt - 1, nkt, r0, r1, acc);
+  for (int kt = 0; kt < nkt; kt++) pf16_step<WF, SWAP>(L, src, kt, nkt, acc);
 }
 
 }  // namespace
@@ -676,7 +672,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
   const int K = a.K, N = a.N;
   const PfWork wk = pf_work(a, N / 64, true);
   if (!wk.valid) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
   const int hb = wk.sub, groups = K / 32;
   Pf16Src src;
   src.wstep = (size_t)16 * groups * U;
@@ -690,26 +686,26 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
     const int row = 4 * (4 * w + j) + (l >> 4);
     src.brow[j] = a.xb + (size_t)(a.perm[wk.p0 + (row < wk.rows ? row : 0)] / a.topk) * K;
   }
-  v4f acc[4][2];
-  zero_acc<4>(acc);
+  v4f acc[2][4];
+#pragma unroll
+  for (int q = 0; q < 2; q++)
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
   pf16_kloop<WF, false>(L, src, acc);
-  // epilogue: row tiles 4wr + {0,1,2,3} = up/gate of intermediate blocks 4hb + 2wr + {0,1}
+  // epilogue: row tiles 2w (up) and 2w + 1 (gate) = intermediate columns 64 hb + 16 w .. +15
   const float gs = a.g13 ? a.g13[wk.e] : 1.0f;
 #pragma unroll
-  for (int cb = 0; cb < 2; cb++) {
-    const int row = 32 * wc + 16 * cb + c;
+  for (int cb = 0; cb < 4; cb++) {
+    const int row = 16 * cb + c;
     if (row < wk.rows) {
       const size_t p = (size_t)(wk.p0 + row);
+      float h[4];
 #pragma unroll
-      for (int s = 0; s < 2; s++) {
-        float h[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) h[i] = silu_clamped(acc[2 * s + 1][cb][i] * gs, acc[2 * s][cb][i] * gs, a.limit, a.has_limit);
-        uint2 v;
-        v.x = pack_bf16x2(h[0], h[1]);
-        v.y = pack_bf16x2(h[2], h[3]);
-        *(uint2 *)(a.hb + p * N + 64 * hb + 32 * wr + 16 * s + 4 * g) = v;
-      }
+      for (int i = 0; i < 4; i++) h[i] = silu_clamped(acc[1][cb][i] * gs, acc[0][cb][i] * gs, a.limit, a.has_limit);
+      uint2 v;
+      v.x = pack_bf16x2(h[0], h[1]);
+      v.y = pack_bf16x2(h[2], h[3]);
+      *(uint2 *)(a.hb + p * N + 64 * hb + 16 * w + 4 * g) = v;
     }
   }
 }
@@ -724,7 +720,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
   const int K = a.K, N = a.N;
   const PfWork wk = pf_work(a, K / 128, false);
   if (!wk.valid) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
   const int ob = wk.sub, groups = N / 32;   // output columns 128 ob .. +127 = w2 row tiles 8 ob .. +7
   Pf16Src src;
   src.wstep = (size_t)16 * groups * U;
@@ -742,11 +738,15 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
     s_r[tid] = r;
     s_w[tid] = a.topk_w[r] * (a.g2 ? a.g2[wk.e] : 1.0f);
   }
-  v4f acc[4][2];
-  zero_acc<4>(acc);
+  v4f acc[2][4];
+#pragma unroll
+  for (int q = 0; q < 2; q++)
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
   pf16_kloop<WF, true>(L, src, acc);
   __syncthreads();   // s_r / s_w visible
-  pf_combine<4>(a, wk, acc, s_r, s_w, (size_t)128 * ob + 64 * wr + c, wc, c, g);
+  // acc[q][cb][i]: route 16 cb + 4 g + i, output column 128 ob + 32 w + 16 q + c
+  pf_combine<2, 4>(a, wk, acc, s_r, s_w, (size_t)128 * ob + 32 * w + c, 0, c, g);
 }
 
 template <int WF>
