@@ -255,7 +255,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
       side_work = std::max(side_work, ra.zero_n / 4);
     }
   }
-  ra.side_blocks = (int)std::min<long>((side_work + 255) / 256, 2048);
+  ra.side_blocks = (int)std::min<long>((side_work + 1023) / 1024, 512);   // blocks of 1024 threads
   HIP_TRY(moe::launch_route(ra, s));
   if (route_only) return MOE_OK;
   if (ev) HIP_TRY(hipEventRecord(ev[1], s));

@@ -74,8 +74,8 @@ __device__ void finish_plan(const RouteArgs &a, int U, const int *cnt, int *off,
     }
   }
   __syncthreads();
-  for (int u = tid; u <= U; u += 256) a.off[u] = off[u];
-  for (int u = tid; u < U; u += 256) {
+  for (int u = tid; u <= U; u += blockDim.x) a.off[u] = off[u];
+  for (int u = tid; u < U; u += blockDim.x) {
     a.cnt[u] = cnt[u];
     const int tb = tbeg[u];
     for (int i = 0; i * a.tile_rows < cnt[u]; i++) {
@@ -94,8 +94,8 @@ __device__ void finish_plan(const RouteArgs &a, int U, const int *cnt, int *off,
 // Work fused into the route launch: MXFP8 quantisation of x (one thread per
 // 32-element block) and clearing of the fp32 accumulator.
 __device__ void route_side_work(const RouteArgs &a, int sb) {
-  const long stride = (long)a.side_blocks * 256;
-  const long i0 = (long)sb * 256 + threadIdx.x;
+  const long stride = (long)a.side_blocks * blockDim.x;
+  const long i0 = (long)sb * blockDim.x + threadIdx.x;
   if (a.xq) {
     const long nblk = (long)a.T * (a.K / 32);
     for (long i = i0; i < nblk; i += stride) {
@@ -124,110 +124,119 @@ __device__ void route_side_work(const RouteArgs &a, int sb) {
   }
 }
 
-// One block per chunk of kRouteChunk routes (4 waves x 8 rounds of 64).  Each
-// route's rank among the routes of its expert with a smaller index is found
-// with wave ballots, so the permutation is a stable counting sort.
-// SINGLE: the grid has one route block, which also scans and scatters.
+// One block per chunk of kRouteChunk routes (16 waves x 64).  Each route's
+// rank among the routes of its expert with a smaller index is found with wave
+// ballots (the lanes of one expert are found together; no LDS round trip in
+// the loop), then the waves' counts are scanned per expert, so the permutation
+// is a stable counting sort.  SINGLE: the grid has one route block, which also
+// scans and scatters.
+constexpr int kRouteWaves = 16, kRouteRounds = kRouteChunk / (64 * kRouteWaves);
+static_assert(kRouteRounds == 1, "one 64-route round per wave");
+
 template <bool SINGLE>
-__global__ __launch_bounds__(256) void k_route(RouteArgs a) {
+__global__ __launch_bounds__(64 * kRouteWaves) void k_route(RouteArgs a) {
   if ((int)blockIdx.x >= a.G) {
     route_side_work(a, blockIdx.x - a.G);
     return;
   }
-  __shared__ int whist[4][kMaxExperts];
+  __shared__ uint16_t whist[kRouteWaves][kMaxExperts];   // per wave: count, then exclusive prefix
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int tbeg[kMaxExperts + 1];
   const int U = a.E0 + a.E1;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < 4 * kMaxExperts; i += 256) (&whist[0][0])[i] = 0;
+  for (int u = tid; u < U; u += 64 * kRouteWaves)
+#pragma unroll
+    for (int v = 0; v < kRouteWaves; v++) whist[v][u] = 0;
   __syncthreads();
   const int b = blockIdx.x;
-  const int r0 = b * kRouteChunk + w * (kRouteChunk / 4);
-  const unsigned long long ltmask = (1ull << lane) - 1ull;
-  int us[8], rk[8];
-#pragma unroll
-  for (int s = 0; s < 8; s++) {
-    const int r = r0 + s * 64 + lane;
-    const int u = (r < a.R) ? resolve_u(a.ids[r], a) : -1;
-    int myrank = 0;
+  const int r = b * kRouteChunk + w * 64 + lane;
+  const int u = (r < a.R) ? resolve_u(a.ids[r], a) : -1;
+  int rk = 0;
+  {
+    const unsigned long long ltmask = (1ull << lane) - 1ull;
     unsigned long long rem = __ballot(u >= 0);
     while (rem) {
       const int leader = __ffsll((unsigned long long)rem) - 1;
       const int lu = __shfl(u, leader);
       const unsigned long long m = __ballot(u == lu);
-      const int base = whist[w][lu];
-      if (u == lu) myrank = base + __popcll(m & ltmask);
-      if (lane == leader) whist[w][lu] = base + __popcll(m);
+      if (u == lu) rk = __popcll(m & ltmask);
+      if (lane == leader) whist[w][lu] = (uint16_t)__popcll(m);
       rem &= ~m;
     }
-    us[s] = u;
-    rk[s] = myrank;
   }
   __syncthreads();
   // wave prefixes within the chunk; chunk totals
-  for (int u = tid; u < U; u += 256) {
-    const int s0 = whist[0][u], s1 = whist[1][u], s2 = whist[2][u], s3 = whist[3][u];
-    whist[0][u] = 0;
-    whist[1][u] = s0;
-    whist[2][u] = s0 + s1;
-    whist[3][u] = s0 + s1 + s2;
-    if (SINGLE) cnt[u] = s0 + s1 + s2 + s3;
-    else a.chunk_hist[b * U + u] = s0 + s1 + s2 + s3;
+  for (int x = tid; x < U; x += 64 * kRouteWaves) {
+    int run = 0;
+#pragma unroll
+    for (int v = 0; v < kRouteWaves; v++) {
+      const int c = whist[v][x];
+      whist[v][x] = (uint16_t)run;
+      run += c;
+    }
+    if (SINGLE) cnt[x] = run;
+    else a.chunk_hist[b * U + x] = run;
   }
   __syncthreads();
-#pragma unroll
-  for (int s = 0; s < 8; s++)
-    if (us[s] >= 0) rk[s] += whist[w][us[s]];
+  if (u >= 0) rk += whist[w][u];
   if (!SINGLE) {
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      const int r = r0 + s * 64 + lane;
-      if (r < a.R) {
-        a.ru[r] = us[s];
-        a.lrank[r] = rk[s];
-      }
+    if (r < a.R) {
+      a.ru[r] = u;
+      a.lrank[r] = rk;
     }
     return;
   }
   // single chunk: the chunk totals are the expert counts
   finish_plan(a, U, cnt, off, tbeg);
   __syncthreads();
-#pragma unroll
-  for (int s = 0; s < 8; s++) {
-    const int r = r0 + s * 64 + lane;
-    if (r < a.R) {
-      if (us[s] >= 0) {
-        const int pos = off[us[s]] + rk[s];
-        a.perm[pos] = r;
-        a.inv[r] = pos;
-      } else {
-        a.inv[r] = -1;
-      }
+  if (r < a.R) {
+    if (u >= 0) {
+      const int pos = off[u] + rk;
+      a.perm[pos] = r;
+      a.inv[r] = pos;
+    } else {
+      a.inv[r] = -1;
     }
   }
 }
 
-// Multi-chunk: per-expert scan over chunks, offsets, tile table.
-__global__ __launch_bounds__(256) void k_route_scan(RouteArgs a) {
+// Multi-chunk: per-expert scan over chunks, offsets, tile table.  One thread
+// per expert; the chunk counts are read 8 at a time so the loads overlap.
+__global__ __launch_bounds__(1024) void k_route_scan(RouteArgs a) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int tbeg[kMaxExperts + 1];
-  const int U = a.E0 + a.E1;
-  for (int u = threadIdx.x; u < U; u += 256) {
+  const int U = a.E0 + a.E1, u = threadIdx.x;
+  constexpr int B = 8;
+  if (u < U) {
     int run = 0;
-    for (int b = 0; b < a.G; b++) {
-      const int v = a.chunk_hist[b * U + u];
-      a.chunk_hist[b * U + u] = run;
-      run += v;
+    for (int b0 = 0; b0 < a.G; b0 += B) {
+      int v[B];
+#pragma unroll
+      for (int j = 0; j < B; j++) v[j] = b0 + j < a.G ? a.chunk_hist[(b0 + j) * U + u] : 0;
+#pragma unroll
+      for (int j = 0; j < B; j++) run += v[j];
     }
     cnt[u] = run;
   }
   __syncthreads();
   finish_plan(a, U, cnt, off, tbeg);
   __syncthreads();
-  for (int u = threadIdx.x; u < U; u += 256)
-    for (int b = 0; b < a.G; b++) a.chunk_hist[b * U + u] += off[u];
+  if (u < U) {
+    int run = off[u];
+    for (int b0 = 0; b0 < a.G; b0 += B) {
+      int v[B];
+#pragma unroll
+      for (int j = 0; j < B; j++) v[j] = b0 + j < a.G ? a.chunk_hist[(b0 + j) * U + u] : 0;
+#pragma unroll
+      for (int j = 0; j < B; j++)
+        if (b0 + j < a.G) {
+          a.chunk_hist[(b0 + j) * U + u] = run;
+          run += v[j];
+        }
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void k_route_scatter(RouteArgs a) {
@@ -246,10 +255,10 @@ __global__ __launch_bounds__(256) void k_route_scatter(RouteArgs a) {
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
   if (a.G == 1) {
-    hipLaunchKernelGGL(k_route<true>, dim3(1 + a.side_blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_route<true>, dim3(1 + a.side_blocks), dim3(64 * kRouteWaves), 0, s, a);
   } else {
-    hipLaunchKernelGGL(k_route<false>, dim3(a.G + a.side_blocks), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_route<false>, dim3(a.G + a.side_blocks), dim3(64 * kRouteWaves), 0, s, a);
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(k_route_scatter, dim3((a.R + 255) / 256), dim3(256), 0, s, a);
   }
   return hipGetLastError();

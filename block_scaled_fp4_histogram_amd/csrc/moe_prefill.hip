@@ -103,8 +103,9 @@ struct PfSrc {
 // load count equal).  Lanes whose data lies past the reduction length (a
 // partial last k-tile) load from a valid address instead; the MFMA step zeroes
 // those activation bytes and both scales there.
+template <bool FULL>
 __device__ __forceinline__ void pf_issue(PfStage &S, const PfSrc &src, int kt, int w, int l) {
-  const bool in = (kt * 4 + (l >> 4)) * 32 < src.kbytes;
+  const bool in = FULL || (kt * 4 + (l >> 4)) * 32 < src.kbytes;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int rt = 4 * w + j, rs = min(rt, src.nrt - 1);
@@ -113,11 +114,11 @@ __device__ __forceinline__ void pf_issue(PfStage &S, const PfSrc &src, int kt, i
 #pragma unroll
   for (int j = 0; j < 2; j++) {   // activation blocks 2w + j: lane l -> row l / 8, its chunk slot l
     const int r8 = l >> 3, part = (l & 7) ^ r8, off = kt * 128 + part * 16;
-    dma16(src.brow[j] + (off < src.kbytes ? off : 0), &S.B[2 * w + j][0]);
+    dma16(src.brow[j] + (FULL || off < src.kbytes ? off : 0), &S.B[2 * w + j][0]);
   }
   {   // As row tiles 4w .. 4w+3: lane l -> row tile 4w + l / 16, dword l % 16
     const int rs = min(4 * w + (l >> 4), src.nrt - 1), d = l & 15;
-    const bool ins = (kt * 4 + (d >> 2)) * 32 < src.kbytes;
+    const bool ins = FULL || (kt * 4 + (d >> 2)) * 32 < src.kbytes;
     dma4(src.sbase + rs * src.sstep + (ins ? (size_t)kt * 64 + 4 * d : 0), &S.S[256 * w]);
   }
   dma4(src.bsrow + 4 * kt, &S.S[w == 0 ? 1024 : 1024 + 256 * w]);
@@ -126,8 +127,7 @@ __device__ __forceinline__ void pf_issue(PfStage &S, const PfSrc &src, int kt, i
 // One wave's operands of a landed stage.  The LDS reads are issued by asm the
 // compiler cannot see into: seen, each would make it wait for every direct-to-
 // LDS load in flight (it cannot tell ring stages apart), emptying the ring at
-// every k-tile.  pf_read issues them; pf_wait waits for them and, taking the
-// registers as operands, keeps every use of them after the wait.
+// every k-tile.  pf_read issues them and waits for them in one statement.
 struct PfOps {
   v4i a[kPfQ];   // weight row tiles 8 wr + q
   v4i b[4];      // activation chunks: [cb] = columns 16 g .. of route block cb, [2 + cb] = columns 64 + 16 g ..
@@ -140,19 +140,16 @@ __device__ __forceinline__ void pf_read(PfOps &o, const PfStage &S, int wr, int 
   const uint32_t va = lds_addr(&S.A[kPfQ * wr][l * 16]), vb0 = lds_addr(bblk + pf_slot(r8, g) * 16),
                  vb1 = lds_addr(bblk + pf_slot(r8, 4 + g) * 16), vsa = lds_addr(&S.S[kPfQ * wr * 64 + l]),
                  vsb = lds_addr(&S.S[1024 + (32 * wc + c) * 4 + g]);
+  // the wait is part of the same statement: between an LDS read and its wait
+  // the compiler could copy the register it loads (it cannot know the value
+  // is still in flight)
   asm volatile(
-      "ds_read_b128 %0, %22\n"
-      "ds_read_b128 %1, %22 offset:1024\n"
-      "ds_read_b128 %2, %22 offset:2048\n"
-      "ds_read_b128 %3, %22 offset:3072\n"
-      "ds_read_b128 %4, %22 offset:4096\n"
-      "ds_read_b128 %5, %22 offset:5120\n"
-      "ds_read_b128 %6, %22 offset:6144\n"
-      "ds_read_b128 %7, %22 offset:7168\n"
       "ds_read_b128 %8, %23\n"
       "ds_read_b128 %9, %23 offset:2048\n"
       "ds_read_b128 %10, %24\n"
       "ds_read_b128 %11, %24 offset:2048\n"
+      "ds_read_u8 %20, %26\n"
+      "ds_read_u8 %21, %26 offset:64\n"
       "ds_read_u8 %12, %25\n"
       "ds_read_u8 %13, %25 offset:64\n"
       "ds_read_u8 %14, %25 offset:128\n"
@@ -161,8 +158,15 @@ __device__ __forceinline__ void pf_read(PfOps &o, const PfStage &S, int wr, int 
       "ds_read_u8 %17, %25 offset:320\n"
       "ds_read_u8 %18, %25 offset:384\n"
       "ds_read_u8 %19, %25 offset:448\n"
-      "ds_read_u8 %20, %26\n"
-      "ds_read_u8 %21, %26 offset:64"
+      "ds_read_b128 %0, %22\n"
+      "ds_read_b128 %1, %22 offset:1024\n"
+      "ds_read_b128 %2, %22 offset:2048\n"
+      "ds_read_b128 %3, %22 offset:3072\n"
+      "ds_read_b128 %4, %22 offset:4096\n"
+      "ds_read_b128 %5, %22 offset:5120\n"
+      "ds_read_b128 %6, %22 offset:6144\n"
+      "ds_read_b128 %7, %22 offset:7168\n"
+      "s_waitcnt lgkmcnt(0)"
       : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.a[4]), "=&v"(o.a[5]), "=&v"(o.a[6]),
         "=&v"(o.a[7]), "=&v"(o.b[0]), "=&v"(o.b[1]), "=&v"(o.b[2]), "=&v"(o.b[3]), "=&v"(o.sa[0]), "=&v"(o.sa[1]),
         "=&v"(o.sa[2]), "=&v"(o.sa[3]), "=&v"(o.sa[4]), "=&v"(o.sa[5]), "=&v"(o.sa[6]), "=&v"(o.sa[7]),
@@ -171,25 +175,28 @@ __device__ __forceinline__ void pf_read(PfOps &o, const PfStage &S, int wr, int 
       : "memory");
 }
 
-__device__ __forceinline__ void pf_wait(PfOps &o) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(o.a[0]), "+v"(o.a[1]), "+v"(o.a[2]), "+v"(o.a[3]), "+v"(o.a[4]), "+v"(o.a[5]), "+v"(o.a[6]),
-                 "+v"(o.a[7]), "+v"(o.b[0]), "+v"(o.b[1]), "+v"(o.b[2]), "+v"(o.b[3])
-               :
-               : "memory");
-  asm volatile("" : "+v"(o.sa[0]), "+v"(o.sa[1]), "+v"(o.sa[2]), "+v"(o.sa[3]), "+v"(o.sa[4]), "+v"(o.sa[5]),
-                    "+v"(o.sa[6]), "+v"(o.sa[7]), "+v"(o.sb[0]), "+v"(o.sb[1]));
+// 16 MFMAs of one k-tile, two per weight row tile.  Past the reduction length (a partial last k-tile; FULL: none) the activation
+// bytes are zeroed and both scales set to 2^-127, so the products there are
+// exact zeros whatever the stage held.  SWAP: activations as the A operand
+// (accumulator lane = output column, elements = 4 routes).
+template <bool SWAP, bool FULL, int Q>
+__device__ __forceinline__ void pf_mma_q(const PfOps &o, bool gin, const v8i (&bop)[2], v4f (*acc)[2]) {
+#pragma unroll
+  for (int cb = 0; cb < 2; cb++) {
+    const int sa = (FULL || gin) ? o.sa[Q] : 0, sb = (FULL || gin) ? o.sb[cb] : 0;
+    if (SWAP)
+      acc[Q][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bop[cb], fp4_operand(o.a[Q]), acc[Q][cb], 0, 4, 0,
+                                                                    sb, 0, sa);
+    else
+      acc[Q][cb] = mfma_fp4_fp8(o.a[Q], bop[cb], acc[Q][cb], sa, sb);
+  }
 }
 
-// 16 MFMAs of one k-tile.  Past the reduction length (a partial last k-tile)
-// the activation bytes are zeroed and both scales set to 2^-127, so the
-// products there are exact zeros whatever the stage held.  SWAP: activations
-// as the A operand (accumulator lane = output column, elements = 4 routes).
-template <bool SWAP>
+template <bool SWAP, bool FULL>
 __device__ __forceinline__ void pf_mma(const PfOps &o, int kt, int kbytes, int l, v4f (*acc)[2]) {
   const int g = l >> 4;
-  const bool in0 = kt * 128 + 16 * g < kbytes, in1 = kt * 128 + 64 + 16 * g < kbytes;
-  const bool gin = (kt * 4 + g) * 32 < kbytes;   // 32-column group g of this k-tile exists
+  const bool in0 = FULL || kt * 128 + 16 * g < kbytes, in1 = FULL || kt * 128 + 64 + 16 * g < kbytes;
+  const bool gin = FULL || (kt * 4 + g) * 32 < kbytes;   // 32-column group g of this k-tile exists
   v8i bop[2];
 #pragma unroll
   for (int cb = 0; cb < 2; cb++) {
@@ -197,33 +204,34 @@ __device__ __forceinline__ void pf_mma(const PfOps &o, int kt, int kbytes, int l
     const v4i b1 = in1 ? o.b[2 + cb] : v4i{0, 0, 0, 0};
     bop[cb] = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
   }
-#pragma unroll
-  for (int q = 0; q < kPfQ; q++)
-#pragma unroll
-    for (int cb = 0; cb < 2; cb++) {
-      const int sa = gin ? o.sa[q] : 0, sb = gin ? o.sb[cb] : 0;
-      if (SWAP)
-        acc[q][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bop[cb], fp4_operand(o.a[q]), acc[q][cb], 0, 4,
-                                                                      0, sb, 0, sa);
-      else
-        acc[q][cb] = mfma_fp4_fp8(o.a[q], bop[cb], acc[q][cb], sa, sb);
-    }
+  pf_mma_q<SWAP, FULL, 0>(o, gin, bop, acc);
+  pf_mma_q<SWAP, FULL, 1>(o, gin, bop, acc);
+  pf_mma_q<SWAP, FULL, 2>(o, gin, bop, acc);
+  pf_mma_q<SWAP, FULL, 3>(o, gin, bop, acc);
+  pf_mma_q<SWAP, FULL, 4>(o, gin, bop, acc);
+  pf_mma_q<SWAP, FULL, 5>(o, gin, bop, acc);
+  pf_mma_q<SWAP, FULL, 6>(o, gin, bop, acc);
+  pf_mma_q<SWAP, FULL, 7>(o, gin, bop, acc);
 }
 
 // One k-tile: wait until stage kt has landed for every wave (every wave is
-// then also done with stage kt - 1), read this wave's operands of stage kt,
-// refill stage kt - 1's slot with k-tile kt + kPfStages - 1, multiply.
+// then also done with stage kt - 1), refill stage kt - 1's slot with k-tile
+// kt + kPfStages - 1, read this wave's operands of stage kt, multiply.
 template <bool SWAP>
 __device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, int kt, int nkt, v4f (*acc)[2]) {
   constexpr int ST = kPfStages;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wr = w >> 1, wc = w & 1;
   wait_stages(min(ST - 2, nkt - 1 - kt));   // stage kt has landed
   __builtin_amdgcn_s_barrier();
+  const int kn = kt + ST - 1;
+  if (kn < nkt) {
+    if ((kn + 1) * 128 <= src.kbytes) pf_issue<true>(L.st[kn % ST], src, kn, w, l);
+    else pf_issue<false>(L.st[kn % ST], src, kn, w, l);
+  }
   PfOps o;
   pf_read(o, L.st[kt % ST], wr, wc, l);
-  if (kt + ST - 1 < nkt) pf_issue(L.st[(kt + ST - 1) % ST], src, kt + ST - 1, w, l);
-  pf_wait(o);
-  pf_mma<SWAP>(o, kt, src.kbytes, l, acc);
+  if ((kt + 1) * 128 <= src.kbytes) pf_mma<SWAP, true>(o, kt, src.kbytes, l, acc);
+  else pf_mma<SWAP, false>(o, kt, src.kbytes, l, acc);
 }
 
 // The k-loop of both GEMMs.
@@ -234,7 +242,7 @@ __device__ __forceinline__ void pf_kloop(PfLds &L, const PfSrc &src, v4f (*acc)[
   const int nkt = (src.kbytes + 127) / 128;
 #pragma unroll
   for (int s = 0; s < ST - 1; s++)
-    if (s < nkt) pf_issue(L.st[s], src, s, w, l);
+    if (s < nkt) pf_issue<false>(L.st[s], src, s, w, l);
   for (int kt = 0; kt < nkt; kt++) pf_step<SWAP>(L, src, kt, nkt, acc);
 }
 
@@ -511,26 +519,51 @@ struct Pf16Ops {
   v4i b[4][4];        // step s, route block cb
 };
 
-// LDS reads of one wave's operands, weights first, then activations step by
-// step (asm: invisible to the compiler's direct-to-LDS bookkeeping, as for the
-// W4A8 kernels).  LDS reads return in order, so pf16_wait_step<s> waits for
-// the weights and the activations of steps 0 .. s only.
+// LDS reads of one wave's operands (asm: invisible to the compiler's
+// direct-to-LDS bookkeeping, as for the W4A8 kernels).  The wait is part of
+// each statement: between an LDS read and its wait the compiler could copy the
+// register it loads.
 template <int WF>
 __device__ __forceinline__ void pf16_read(Pf16Ops<WF> &o, const Pf16Stage<WF> &S, int w, int l) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
   const int c = l & 15, g = l >> 4;
   const uint32_t va = lds_addr(&S.A[2 * w][l * U]), vs = lds_addr(&S.AS[2 * w][l * SU]);
   const uint8_t *brow = &S.B[c][0];   // + 16 rows (4096 bytes) per route block
+  uint32_t vb[4];
+#pragma unroll
+  for (int s = 0; s < 4; s++) vb[s] = lds_addr(brow + 16 * ((4 * g + s) ^ c));
+#define PF16_READ_B                               \
+  "ds_read_b128 %0, %[b0]\n"                      \
+  "ds_read_b128 %1, %[b0] offset:4096\n"          \
+  "ds_read_b128 %2, %[b0] offset:8192\n"          \
+  "ds_read_b128 %3, %[b0] offset:12288\n"         \
+  "ds_read_b128 %4, %[b1]\n"                      \
+  "ds_read_b128 %5, %[b1] offset:4096\n"          \
+  "ds_read_b128 %6, %[b1] offset:8192\n"          \
+  "ds_read_b128 %7, %[b1] offset:12288\n"         \
+  "ds_read_b128 %8, %[b2]\n"                      \
+  "ds_read_b128 %9, %[b2] offset:4096\n"          \
+  "ds_read_b128 %10, %[b2] offset:8192\n"         \
+  "ds_read_b128 %11, %[b2] offset:12288\n"        \
+  "ds_read_b128 %12, %[b3]\n"                     \
+  "ds_read_b128 %13, %[b3] offset:4096\n"         \
+  "ds_read_b128 %14, %[b3] offset:8192\n"         \
+  "ds_read_b128 %15, %[b3] offset:12288\n"
+#define PF16_B_OUT                                                                                             \
+  "=&v"(o.b[0][0]), "=&v"(o.b[0][1]), "=&v"(o.b[0][2]), "=&v"(o.b[0][3]), "=&v"(o.b[1][0]), "=&v"(o.b[1][1]), \
+      "=&v"(o.b[1][2]), "=&v"(o.b[1][3]), "=&v"(o.b[2][0]), "=&v"(o.b[2][1]), "=&v"(o.b[2][2]),                 \
+      "=&v"(o.b[2][3]), "=&v"(o.b[3][0]), "=&v"(o.b[3][1]), "=&v"(o.b[3][2]), "=&v"(o.b[3][3])
   if constexpr (WF == W_NVFP4) {
     v4i a0, a1;
-    asm volatile(
-        "ds_read_b128 %0, %4\n"
-        "ds_read_b128 %1, %4 offset:1024\n"
-        "ds_read_u16 %2, %5\n"
-        "ds_read_u16 %3, %5 offset:128"
-        : "=&v"(a0), "=&v"(a1), "=&v"(o.sc[0]), "=&v"(o.sc[1])
-        : "v"(va), "v"(vs)
-        : "memory");
+    asm volatile(PF16_READ_B
+                 "ds_read_b128 %16, %[va]\n"
+                 "ds_read_b128 %17, %[va] offset:1024\n"
+                 "ds_read_u16 %18, %[vs]\n"
+                 "ds_read_u16 %19, %[vs] offset:128\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 : PF16_B_OUT, "=&v"(a0), "=&v"(a1), "=&v"(o.sc[0]), "=&v"(o.sc[1])
+                 : [b0] "v"(vb[0]), [b1] "v"(vb[1]), [b2] "v"(vb[2]), [b3] "v"(vb[3]), [va] "v"(va), [vs] "v"(vs)
+                 : "memory");
 #pragma unroll
     for (int d = 0; d < 4; d++) {
       o.a[0][d] = (uint32_t)a0[d];
@@ -538,54 +571,24 @@ __device__ __forceinline__ void pf16_read(Pf16Ops<WF> &o, const Pf16Stage<WF> &S
     }
   } else {
     // 12-byte lanes are only 4-byte aligned: three dword reads per row tile
-    asm volatile(
-        "ds_read_b32 %0, %8\n"
-        "ds_read_b32 %1, %8 offset:4\n"
-        "ds_read_b32 %2, %8 offset:8\n"
-        "ds_read_b32 %3, %8 offset:768\n"
-        "ds_read_b32 %4, %8 offset:772\n"
-        "ds_read_b32 %5, %8 offset:776\n"
-        "ds_read_u8 %6, %9\n"
-        "ds_read_u8 %7, %9 offset:64"
-        : "=&v"(o.a[0][0]), "=&v"(o.a[0][1]), "=&v"(o.a[0][2]), "=&v"(o.a[1][0]), "=&v"(o.a[1][1]), "=&v"(o.a[1][2]),
-          "=&v"(o.sc[0]), "=&v"(o.sc[1])
-        : "v"(va), "v"(vs)
-        : "memory");
+    asm volatile(PF16_READ_B
+                 "ds_read_b32 %16, %[va]\n"
+                 "ds_read_b32 %17, %[va] offset:4\n"
+                 "ds_read_b32 %18, %[va] offset:8\n"
+                 "ds_read_b32 %19, %[va] offset:768\n"
+                 "ds_read_b32 %20, %[va] offset:772\n"
+                 "ds_read_b32 %21, %[va] offset:776\n"
+                 "ds_read_u8 %22, %[vs]\n"
+                 "ds_read_u8 %23, %[vs] offset:64\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 : PF16_B_OUT, "=&v"(o.a[0][0]), "=&v"(o.a[0][1]), "=&v"(o.a[0][2]), "=&v"(o.a[1][0]),
+                   "=&v"(o.a[1][1]), "=&v"(o.a[1][2]), "=&v"(o.sc[0]), "=&v"(o.sc[1])
+                 : [b0] "v"(vb[0]), [b1] "v"(vb[1]), [b2] "v"(vb[2]), [b3] "v"(vb[3]), [va] "v"(va), [vs] "v"(vs)
+                 : "memory");
     o.a[0][3] = o.a[1][3] = 0;
   }
-#pragma unroll
-  for (int s = 0; s < 4; s++) {
-    const uint32_t vb = lds_addr(brow + 16 * ((4 * g + s) ^ c));
-    asm volatile(
-        "ds_read_b128 %0, %4\n"
-        "ds_read_b128 %1, %4 offset:4096\n"
-        "ds_read_b128 %2, %4 offset:8192\n"
-        "ds_read_b128 %3, %4 offset:12288"
-        : "=&v"(o.b[s][0]), "=&v"(o.b[s][1]), "=&v"(o.b[s][2]), "=&v"(o.b[s][3])
-        : "v"(vb)
-        : "memory");
-  }
-}
-
-// Completes the reads up to the activations of step S (4 reads per later step
-// may stay in flight); the empty-looking register operands tie the wait to the
-// values it makes valid.
-template <int WF, int S>
-__device__ __forceinline__ void pf16_wait_step(Pf16Ops<WF> &o) {
-  if constexpr (S == 0) {
-    asm volatile("s_waitcnt lgkmcnt(12)"
-                 : "+v"(o.a[0][0]), "+v"(o.a[0][1]), "+v"(o.a[0][2]), "+v"(o.a[0][3]), "+v"(o.a[1][0]),
-                   "+v"(o.a[1][1]), "+v"(o.a[1][2]), "+v"(o.a[1][3]), "+v"(o.sc[0]), "+v"(o.sc[1]), "+v"(o.b[0][0]),
-                   "+v"(o.b[0][1]), "+v"(o.b[0][2]), "+v"(o.b[0][3])
-                 :
-                 : "memory");
-  } else if constexpr (S == 1) {
-    asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(o.b[1][0]), "+v"(o.b[1][1]), "+v"(o.b[1][2]), "+v"(o.b[1][3]) : : "memory");
-  } else if constexpr (S == 2) {
-    asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(o.b[2][0]), "+v"(o.b[2][1]), "+v"(o.b[2][2]), "+v"(o.b[2][3]) : : "memory");
-  } else {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(o.b[3][0]), "+v"(o.b[3][1]), "+v"(o.b[3][2]), "+v"(o.b[3][3]) : : "memory");
-  }
+#undef PF16_READ_B
+#undef PF16_B_OUT
 }
 
 // 8 bf16 MFMAs of step S of a k-tile (2 row tiles x 4 route blocks); each
@@ -593,9 +596,8 @@ __device__ __forceinline__ void pf16_wait_step(Pf16Ops<WF> &o) {
 // length: scale 0 (weights 0) and activations 0.  SWAP: activations as the A
 // operand.
 template <int WF, bool SWAP, int S>
-__device__ __forceinline__ void pf16_mma_step(Pf16Ops<WF> &o, bool gin, const float (&slo)[2], const float (&shi)[2],
+__device__ __forceinline__ void pf16_mma_step(const Pf16Ops<WF> &o, bool gin, const float (&slo)[2], const float (&shi)[2],
                                               const uint32_t (&t01)[2], const uint32_t (&t23)[2], v4f (*acc)[4]) {
-  if constexpr (S > 0) pf16_wait_step<WF, S>(o);   // step 0: waited for by the caller
   v8bf bop[4];
 #pragma unroll
   for (int cb = 0; cb < 4; cb++) bop[cb] = __builtin_bit_cast(v8bf, gin ? o.b[S][cb] : v4i{0, 0, 0, 0});
@@ -610,12 +612,11 @@ __device__ __forceinline__ void pf16_mma_step(Pf16Ops<WF> &o, bool gin, const fl
 }
 
 // One k-tile: the scales are decoded once per row tile (NF3: its scaled
-// magnitude table) after the weights have arrived.
+// magnitude table).
 template <int WF, bool SWAP>
-__device__ __forceinline__ void pf16_mma(Pf16Ops<WF> &o, int kt, int kcols, int l, v4f (*acc)[4]) {
+__device__ __forceinline__ void pf16_mma(const Pf16Ops<WF> &o, int kt, int kcols, int l, v4f (*acc)[4]) {
   const int g = l >> 4;
   const bool gin = kt * 128 + 32 * g < kcols;
-  pf16_wait_step<WF, 0>(o);
   float slo[2] = {0.f, 0.f}, shi[2] = {0.f, 0.f};
   uint32_t t01[2] = {0u, 0u}, t23[2] = {0u, 0u};
 #pragma unroll
@@ -636,18 +637,18 @@ __device__ __forceinline__ void pf16_mma(Pf16Ops<WF> &o, int kt, int kcols, int 
   pf16_mma_step<WF, SWAP, 3>(o, gin, slo, shi, t01, t23, acc);
 }
 
-// One k-tile of the ring: stage kt is read straight after the barrier that
-// proves it landed for every wave (and that every wave is done with stage
-// kt - 1, whose slot then takes stage kt + ST - 1).
+// One k-tile of the ring: after the barrier that proves stage kt landed for
+// every wave (and that every wave is done with stage kt - 1, whose slot then
+// takes stage kt + ST - 1), stage kt is read.
 template <int WF, bool SWAP>
 __device__ __forceinline__ void pf16_step(Pf16Lds<WF> &L, const Pf16Src &src, int kt, int nkt, v4f (*acc)[4]) {
   constexpr int ST = kPf16Stages;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   wait16_stages<WF>(min(ST - 2, nkt - 1 - kt));   // stage kt has landed
   __builtin_amdgcn_s_barrier();
+  if (kt + ST - 1 < nkt) pf16_issue<WF>(L.st[(kt + ST - 1) % ST], src, kt + ST - 1, w, l);
   Pf16Ops<WF> o;
   pf16_read<WF>(o, L.st[kt % ST], w, l);
-  if (kt + ST - 1 < nkt) pf16_issue<WF>(L.st[(kt + ST - 1) % ST], src, kt + ST - 1, w, l);
   pf16_mma<WF, SWAP>(o, kt, src.kcols, l, acc);
 }
 

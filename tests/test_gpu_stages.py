@@ -73,10 +73,14 @@ def _route_case(name):
         ids[5] = -1
         cfg = I.Config("inv", T=333, E=E, K=256, N=64, topk=5, limit=None, fmt=I.FMT_MXFP4)
         return I.Problem(cfg, None, ids, None, [I.Tier(I.FMT_MXFP4, E, {})])
+    if name == "single_block":   # 1,020 routes: one planner block, its last wave ragged
+        cfg = I.Config("single", T=170, E=384, K=256, N=64, topk=6, limit=None, fmt=I.FMT_MXFP4)
+        ids, wts = I.make_routing(cfg.T, cfg.E, cfg.topk, 3, 1.1)
+        return I.Problem(cfg, None, ids, wts, [I.Tier(cfg.fmt, cfg.E, {})])
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "hybrid", "invalid_ids"])
+@pytest.mark.parametrize("name", ["decode", "single_block", "prefill", "hybrid", "invalid_ids"])
 def test_route_bitexact(name):
     prob = _route_case(name)
     c = prob.cfg
