@@ -98,6 +98,41 @@ def measured_traffic(workload, kernel, per_launch_units):
     return d.get("hbm_bytes_per_launch")
 
 
+def pmc_summary(args):
+    """HBM bytes per launch of one kernel from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE; counter_collection.csv each), scaled by what the same counters read for a
+    plain device copy of known size (bench.py --copy-calib) run under the same counters."""
+    import csv
+    fetch, write, cfetch, cwrite = args.pmc_csv
+
+    def kib(path, name_part):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if name_part in r["Kernel_Name"]:
+                key = r.get("Dispatch_Id") or r.get("Correlation_Id") or str(len(vals))
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no dispatch of {name_part!r} in {path}")
+        return sum(vals.values()) / len(vals), len(vals)
+
+    copy_bytes = args.copy_calib_bytes
+    f_copy, _ = kib(cfetch, "copyBuffer")
+    w_copy, _ = kib(cwrite, "copyBuffer")
+    f_scale = copy_bytes / (f_copy * 1024.0)
+    w_scale = copy_bytes / (w_copy * 1024.0)
+    f_k, n_f = kib(fetch, args.pmc_kernel)
+    w_k, n_w = kib(write, args.pmc_kernel)
+    read_b, write_b = f_k * 1024.0 * f_scale, w_k * 1024.0 * w_scale
+    return {"kernel": args.pmc_kernel, "workload": args.config + ("_det" if args.deterministic else ""),
+            "kernel_source_sha256_16": kernel_source_hash(),
+            "dispatches": [n_f, n_w], "fetch_kib_per_dispatch": round(f_k, 1),
+            "write_kib_per_dispatch": round(w_k, 1),
+            "copy_calibration": {"bytes": copy_bytes, "fetch_kib": round(f_copy, 1), "write_kib": round(w_copy, 1),
+                                 "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+            "hbm_read_bytes_per_launch": round(read_b), "hbm_write_bytes_per_launch": round(write_b),
+            "hbm_bytes_per_launch": round(read_b + write_b)}
+
+
 def cpu_baseline(prob, seconds, live_rows):
     """The oracle, as it stands, on a bounded sample of the workload's rows."""
     import oracle as O
@@ -133,7 +168,15 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference kernel that "
                          "scales HBM byte counters)")
+    ap.add_argument("--pmc-csv", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="only summarise rocprofv3 counter_collection.csv files of one kernel (with --pmc-kernel)"
+                         " into HBM bytes per launch, calibrated by the copy runs")
+    ap.add_argument("--pmc-kernel", default="k_dec_gemm1_a8", help="kernel name (substring) for --pmc-csv")
+    ap.add_argument("--copy-calib-bytes", type=int, default=1 << 30, help="bytes of the calibration copy")
     args = ap.parse_args()
+    if args.pmc_csv:
+        print(json.dumps(pmc_summary(args), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the layer shards by "
               "tensor-parallel N-slices plus one all-reduce, which is not built here).", file=sys.stderr)
@@ -241,13 +284,16 @@ def main():
 
     dominant = max(("gemm1", "gemm2"), key=lambda s: stage_us[s])
     dom_s = stage_us[dominant] * 1e-6
-    decode_like = alg["live"] <= 64
-    if decode_like:
+    # the binding roofline of the dominant kernel: the larger of its algorithmic
+    # bytes at peak HBM bandwidth and its flops at the peak MFMA rate of its dtype
+    mfma_peak = MFMA_PEAK_TFLOPS["fp8" if a8 else "bf16"]
+    t_hbm = alg[f"{dominant}_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = alg[f"{dominant}_flops"] / (mfma_peak * 1e12)
+    if t_hbm >= t_mfma:
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
         achieved = alg[f"{dominant}_bytes"] / dom_s / 1e9
     else:
-        bound, unit = "mfma", "TFLOP/s"
-        peak = MFMA_PEAK_TFLOPS["fp8" if a8 else "bf16"]
+        bound, unit, peak = "mfma", "TFLOP/s", mfma_peak
         achieved = alg[f"{dominant}_flops"] / dom_s / 1e12
     traffic = measured_traffic(cfg.name + ("_det" if args.deterministic else ""), dominant, 1)
 

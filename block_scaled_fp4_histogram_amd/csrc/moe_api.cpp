@@ -419,8 +419,10 @@ int moe_plan_enable_stage_timing(moe_plan_t plan, int max_runs) {
   plan->events.clear();
   plan->timing_runs = plan->timing_runs_max = 0;
   for (long i = 0; i < (long)max_runs * kStageEvents; i++) {
+    // timing only: no system-scope fence (cache write-back and invalidate) at
+    // each stage boundary, which would lengthen the stages it separates
     hipEvent_t e;
-    HIP_TRY(hipEventCreate(&e));
+    HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
     plan->events.push_back(e);
   }
   plan->timing_runs_max = max_runs;

@@ -470,11 +470,11 @@ struct Pf16Src {
 // waves 2, 3 a spare slot), activation chunks 4w .. 4w+3 (1 KB each: 4 routes x
 // 256 bytes; lane l -> route 4j + l/16, LDS slot l % 16 holding global chunk
 // slot ^ route%16).  Lanes past the reduction length load from a valid address.
-template <int WF>
+template <int WF, bool FULL>
 __device__ __forceinline__ void pf16_issue(Pf16Stage<WF> &S, const Pf16Src &src, int kt, int w, int l) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
   if constexpr (WF == W_NVFP4) {
-    const bool in = kt * 128 + 32 * (l >> 4) < src.kcols;
+    const bool in = FULL || kt * 128 + 32 * (l >> 4) < src.kcols;
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const int rt = 2 * w + j;
@@ -482,7 +482,7 @@ __device__ __forceinline__ void pf16_issue(Pf16Stage<WF> &S, const Pf16Src &src,
     }
     // dword d of row tile 2w + l/32 holds the scales of MFMA lanes 2d, 2d + 1
     const int rt = 2 * w + (l >> 5), d = l & 31;
-    const bool ins = kt * 128 + 32 * ((2 * d) >> 4) < src.kcols;
+    const bool ins = FULL || kt * 128 + 32 * ((2 * d) >> 4) < src.kcols;
     dma4(src.sbase + rt * src.sstep + (ins ? (size_t)kt * 64 * SU + 4 * d : 0), &S.AS[2 * w][0]);
   } else {
 #pragma unroll
@@ -491,13 +491,13 @@ __device__ __forceinline__ void pf16_issue(Pf16Stage<WF> &S, const Pf16Src &src,
 #pragma unroll
       for (int m = 0; m < 3; m++) {   // bytes 256 m + 4 l of the row tile's 768-byte k-tile: MFMA lane (256 m + 4 l) / 12
         const int lane = (256 * m + 4 * l) / 12;
-        const bool in = kt * 128 + 32 * (lane >> 4) < src.kcols;
+        const bool in = FULL || kt * 128 + 32 * (lane >> 4) < src.kcols;
         dma4(src.wbase + rt * src.wstep + (in ? (size_t)kt * 64 * U + 256 * m + 4 * l : 0), &S.A[rt][256 * m]);
       }
     }
     if (w < 2) {   // dword d of row tile 4w + l/16 holds the scales of MFMA lanes 4d .. 4d + 3
       const int rt = 4 * w + (l >> 4), d = l & 15;
-      const bool ins = kt * 128 + 32 * ((4 * d) >> 4) < src.kcols;
+      const bool ins = FULL || kt * 128 + 32 * ((4 * d) >> 4) < src.kcols;
       dma4(src.sbase + rt * src.sstep + (ins ? (size_t)kt * 64 * SU + 4 * d : 0), &S.AS[4 * w][0]);
     } else {
       dma4(src.sbase, &S.spare[0]);
@@ -506,7 +506,7 @@ __device__ __forceinline__ void pf16_issue(Pf16Stage<WF> &S, const Pf16Src &src,
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int r = 4 * (4 * w + j) + (l >> 4), cg = (l & 15) ^ (r & 15), col = kt * 128 + 8 * cg;
-    dma16(src.brow[j] + (col < src.kcols ? col : 0), &S.B[4 * (4 * w + j)][0]);
+    dma16(src.brow[j] + (FULL || col < src.kcols ? col : 0), &S.B[4 * (4 * w + j)][0]);
   }
 }
 
@@ -595,12 +595,12 @@ __device__ __forceinline__ void pf16_read(Pf16Ops<WF> &o, const Pf16Stage<WF> &S
 // dequantised weight operand feeds 4 MFMAs.  Columns past the reduction
 // length: scale 0 (weights 0) and activations 0.  SWAP: activations as the A
 // operand.
-template <int WF, bool SWAP, int S>
+template <int WF, bool SWAP, bool FULL, int S>
 __device__ __forceinline__ void pf16_mma_step(const Pf16Ops<WF> &o, bool gin, const float (&slo)[2], const float (&shi)[2],
                                               const uint32_t (&t01)[2], const uint32_t (&t23)[2], v4f (*acc)[4]) {
   v8bf bop[4];
 #pragma unroll
-  for (int cb = 0; cb < 4; cb++) bop[cb] = __builtin_bit_cast(v8bf, gin ? o.b[S][cb] : v4i{0, 0, 0, 0});
+  for (int cb = 0; cb < 4; cb++) bop[cb] = __builtin_bit_cast(v8bf, (FULL || gin) ? o.b[S][cb] : v4i{0, 0, 0, 0});
 #pragma unroll
   for (int q = 0; q < 2; q++) {
     v8bf aop;
@@ -613,10 +613,10 @@ __device__ __forceinline__ void pf16_mma_step(const Pf16Ops<WF> &o, bool gin, co
 
 // One k-tile: the scales are decoded once per row tile (NF3: its scaled
 // magnitude table).
-template <int WF, bool SWAP>
+template <int WF, bool SWAP, bool FULL>
 __device__ __forceinline__ void pf16_mma(const Pf16Ops<WF> &o, int kt, int kcols, int l, v4f (*acc)[4]) {
   const int g = l >> 4;
-  const bool gin = kt * 128 + 32 * g < kcols;
+  const bool gin = FULL || kt * 128 + 32 * g < kcols;
   float slo[2] = {0.f, 0.f}, shi[2] = {0.f, 0.f};
   uint32_t t01[2] = {0u, 0u}, t23[2] = {0u, 0u};
 #pragma unroll
@@ -631,36 +631,43 @@ __device__ __forceinline__ void pf16_mma(const Pf16Ops<WF> &o, int kt, int kcols
       t23[q] = pack_bf16x2(0.6047f * f, f);
     }
   }
-  pf16_mma_step<WF, SWAP, 0>(o, gin, slo, shi, t01, t23, acc);
-  pf16_mma_step<WF, SWAP, 1>(o, gin, slo, shi, t01, t23, acc);
-  pf16_mma_step<WF, SWAP, 2>(o, gin, slo, shi, t01, t23, acc);
-  pf16_mma_step<WF, SWAP, 3>(o, gin, slo, shi, t01, t23, acc);
+  pf16_mma_step<WF, SWAP, FULL, 0>(o, gin, slo, shi, t01, t23, acc);
+  pf16_mma_step<WF, SWAP, FULL, 1>(o, gin, slo, shi, t01, t23, acc);
+  pf16_mma_step<WF, SWAP, FULL, 2>(o, gin, slo, shi, t01, t23, acc);
+  pf16_mma_step<WF, SWAP, FULL, 3>(o, gin, slo, shi, t01, t23, acc);
 }
 
 // One k-tile of the ring: after the barrier that proves stage kt landed for
 // every wave (and that every wave is done with stage kt - 1, whose slot then
 // takes stage kt + ST - 1), stage kt is read.
 template <int WF, bool SWAP>
-__device__ __forceinline__ void pf16_step(Pf16Lds<WF> &L, const Pf16Src &src, int kt, int nkt, v4f (*acc)[4]) {
+__device__ __forceinline__ void pf16_step(Pf16Lds<WF> &L, const Pf16Src &src, int kt, int nkt, int w,
+                                          v4f (*acc)[4]) {
   constexpr int ST = kPf16Stages;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int l = threadIdx.x & 63;
   wait16_stages<WF>(min(ST - 2, nkt - 1 - kt));   // stage kt has landed
   __builtin_amdgcn_s_barrier();
-  if (kt + ST - 1 < nkt) pf16_issue<WF>(L.st[(kt + ST - 1) % ST], src, kt + ST - 1, w, l);
+  const int kn = kt + ST - 1;
+  if (kn < nkt) {
+    if ((kn + 1) * 128 <= src.kcols) pf16_issue<WF, true>(L.st[kn % ST], src, kn, w, l);
+    else pf16_issue<WF, false>(L.st[kn % ST], src, kn, w, l);
+  }
   Pf16Ops<WF> o;
   pf16_read<WF>(o, L.st[kt % ST], w, l);
-  pf16_mma<WF, SWAP>(o, kt, src.kcols, l, acc);
+  if ((kt + 1) * 128 <= src.kcols) pf16_mma<WF, SWAP, true>(o, kt, src.kcols, l, acc);
+  else pf16_mma<WF, SWAP, false>(o, kt, src.kcols, l, acc);
 }
 
+// w: the wave index, wave-uniform (scalar), so stage and weight addresses stay scalar.
 template <int WF, bool SWAP>
-__device__ __forceinline__ void pf16_kloop(Pf16Lds<WF> &L, const Pf16Src &src, v4f (*acc)[4]) {
+__device__ __forceinline__ void pf16_kloop(Pf16Lds<WF> &L, const Pf16Src &src, int w, v4f (*acc)[4]) {
   constexpr int ST = kPf16Stages;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int l = threadIdx.x & 63;
   const int nkt = (src.kcols + 127) / 128;
 #pragma unroll
   for (int s = 0; s < ST - 1; s++)
-    if (s < nkt) pf16_issue<WF>(L.st[s], src, s, w, l);
-  for (int kt = 0; kt < nkt; kt++) pf16_step<WF, SWAP>(L, src, kt, nkt, acc);
+    if (s < nkt) pf16_issue<WF, false>(L.st[s], src, s, w, l);
+  for (int kt = 0; kt < nkt; kt++) pf16_step<WF, SWAP>(L, src, kt, nkt, w, acc);
 }
 
 }  // namespace
@@ -674,6 +681,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
   const PfWork wk = pf_work(a, N / 64, true);
   if (!wk.valid) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int hb = wk.sub, groups = K / 32;
   Pf16Src src;
   src.wstep = (size_t)16 * groups * U;
@@ -692,7 +700,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
   for (int q = 0; q < 2; q++)
 #pragma unroll
     for (int cb = 0; cb < 4; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
-  pf16_kloop<WF, false>(L, src, acc);
+  pf16_kloop<WF, false>(L, src, wu, acc);
   // epilogue: row tiles 2w (up) and 2w + 1 (gate) = intermediate columns 64 hb + 16 w .. +15
   const float gs = a.g13 ? a.g13[wk.e] : 1.0f;
 #pragma unroll
@@ -722,6 +730,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
   const PfWork wk = pf_work(a, K / 128, false);
   if (!wk.valid) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int ob = wk.sub, groups = N / 32;   // output columns 128 ob .. +127 = w2 row tiles 8 ob .. +7
   Pf16Src src;
   src.wstep = (size_t)16 * groups * U;
@@ -744,7 +753,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
   for (int q = 0; q < 2; q++)
 #pragma unroll
     for (int cb = 0; cb < 4; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
-  pf16_kloop<WF, true>(L, src, acc);
+  pf16_kloop<WF, true>(L, src, wu, acc);
   __syncthreads();   // s_r / s_w visible
   // acc[q][cb][i]: route 16 cb + 4 g + i, output column 128 ob + 32 w + 16 q + c
   pf_combine<2, 4>(a, wk, acc, s_r, s_w, (size_t)128 * ob + 32 * w + c, 0, c, g);
