@@ -348,6 +348,11 @@ int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
   for (auto &t : tensors) max_exp = std::max(max_exp, (size_t)t.rows * t.groups * t.unit);
   const size_t budget = (size_t)256 << 20;
   const long batch = std::max<long>(1, std::min<long>(x->E, (long)(budget / max_exp)));
+  // NF3 codes: unpacking leaves the kernels' sign / index form before the permutation
+  if (x->wfmt == MOE_W_NF3 && !to_tiles) {
+    HIP_TRY(moe::launch_nf3_recode(x->w13, (long)x->E * 2 * x->N * (x->K / 32), 0, s));
+    HIP_TRY(moe::launch_nf3_recode(x->w2, (long)x->E * x->K * (x->N / 32), 0, s));
+  }
   uint8_t *tmp = nullptr;
   HIP_TRY(hipMalloc(&tmp, batch * max_exp));
   int rc = MOE_OK;
@@ -362,6 +367,12 @@ int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
                                 to_tiles, s);
       if (e != hipSuccess) rc = fail(MOE_EHIP, "weight permute: %s", hipGetErrorString(e));
     }
+  }
+  // NF3 codes: packing ends in the kernels' sign / index form
+  if (rc == MOE_OK && x->wfmt == MOE_W_NF3 && to_tiles) {
+    hipError_t e1 = moe::launch_nf3_recode(x->w13, (long)x->E * 2 * x->N * (x->K / 32), 1, s);
+    if (e1 == hipSuccess) e1 = moe::launch_nf3_recode(x->w2, (long)x->E * x->K * (x->N / 32), 1, s);
+    if (e1 != hipSuccess) rc = fail(MOE_EHIP, "nf3 recode: %s", hipGetErrorString(e1));
   }
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess && rc == MOE_OK) rc = fail(MOE_EHIP, "weight permute sync: %s", hipGetErrorString(e));

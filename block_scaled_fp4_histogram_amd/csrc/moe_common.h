@@ -138,6 +138,7 @@ hipError_t launch_quant_f32(const float *h, long rows, int cols, uint8_t *q, uin
 //   pair   1 for w13: row tiles interleave up and gate halves
 //   gate_up 1 when the checkpoint stacks w13 as [gate; up]
 //   to_tiles 1 = checkpoint -> tile layout, 0 = back
+hipError_t launch_nf3_recode(uint8_t *w, long units, int to_kernel, hipStream_t s);
 hipError_t launch_permute(const uint8_t *tmp, uint8_t *dst, long ne, int unit, int rows, int groups, int pair,
                           int gate_up, int to_tiles, hipStream_t s);
 

@@ -858,11 +858,11 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
           for (int st = 0; st < 4; st++)
             acc = mfma_bf16(nvfp4_step(d[st], st < 2 ? slo : shi), __builtin_bit_cast(v8bf, B[st]), acc);
         } else {
-          const float f = e4m3_f32((l & 1) ? (sc >> 8) & 0xFFu : sc & 0xFFu);
-          const uint32_t t01 = pack_bf16x2(0.1275f * f, 0.3563f * f), t23 = pack_bf16x2(0.6047f * f, f);
+          uint32_t t01, t23;
+          nf3_tables(e4m3_f32((l & 1) ? (sc >> 8) & 0xFFu : sc & 0xFFu), t01, t23);
 #pragma unroll
           for (int st = 0; st < 4; st++)
-            acc = mfma_bf16(nf3_step_lut(nf3_group(d[0], d[1], d[2], st), t01, t23), __builtin_bit_cast(v8bf, B[st]), acc);
+            acc = mfma_bf16(nf3_step_rc(st < 2 ? d[0] : d[1], d[2], st, t01, t23), __builtin_bit_cast(v8bf, B[st]), acc);
         }
         if (ic.kt == nkt - 1 || base + s + 1 == i1) {
           dec_fold_lds(a, ic.md, ic.pass * 16, c, g, acc, r >= 0 ? wr_s[r] * ic.g2 : 0.f, &yb[w][0], tok);

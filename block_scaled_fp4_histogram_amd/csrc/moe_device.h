@@ -206,50 +206,33 @@ __device__ __forceinline__ v8bf nvfp4_step(uint32_t w, float sc) {
   return __builtin_bit_cast(v8bf, r);
 }
 
-// NF3 magnitudes |codebook| ascending; code c >= 4 is +mag[c-4], c < 4 is -mag[3-c].
-__device__ __forceinline__ float nf3_val(uint32_t c, float m0, float m1, float m2, float m3) {
-  const uint32_t mi = (c & 4u) ? (c & 3u) : (3u - (c & 3u));
-  const float v = (mi & 2u) ? ((mi & 1u) ? m3 : m2) : ((mi & 1u) ? m1 : m0);
-  return (c & 4u) ? v : -v;
+// NF3 codes in tile layout.  A code c stands for +mag[c - 4] (c >= 4) or
+// -mag[3 - c] (c < 4), mag ascending {0.1275, 0.3563, 0.6047, 1}.  The
+// repacker rewrites each lane's 12 bytes (32 codes: 3 bits each, code e at bit
+// 3e) as a sign bit and a 2-bit magnitude index per code, placed so that one
+// shift and mask give a byte-permute selector and one shift gives the sign:
+//   d0 / d1: magnitude indices of codes 0..15 / 16..31; for code e = 8 s + 2 m
+//     + h (step s, pair m, half h) at bits 8 (s & 1) + 2 m + 16 h of d[s >> 1];
+//   d2: sign of code e (1 = negative) at bit 15 - (4 s + m) + 16 h.
+// The same number of bits as the packed codes, so no extra HBM traffic.
+// t01 / t23: the bf16 magnitudes times the group's scale (rounded once),
+// entries 0, 1 and 2, 3 in the low / high halves.
+__device__ __forceinline__ void nf3_tables(float f, uint32_t &t01, uint32_t &t23) {
+  t01 = pack_bf16x2(0.1275f * f, 0.3563f * f);
+  t23 = pack_bf16x2(0.6047f * f, f);
 }
 
-// 8 NF3 codes (one 24-bit group) -> 8 bf16 (codebook x scale, rounded to bf16).
-__device__ __forceinline__ v8bf nf3_step(uint32_t w24, float m0, float m1, float m2, float m3) {
+// 8 codes of step s (dsel = d0 for s < 2, else d1) -> 8 bf16: per code pair a
+// byte permute picks both magnitudes, then the two sign bits are or-ed in.
+__device__ __forceinline__ v8bf nf3_step_rc(uint32_t dsel, uint32_t d2, int s, uint32_t t01, uint32_t t23) {
   v4i r;
 #pragma unroll
   for (int m = 0; m < 4; m++) {
-    const float lo = nf3_val((w24 >> (6 * m)) & 7u, m0, m1, m2, m3);
-    const float hi = nf3_val((w24 >> (6 * m + 3)) & 7u, m0, m1, m2, m3);
-    r[m] = (int)pack_bf16x2(lo, hi);
+    const uint32_t x = (dsel >> (8 * (s & 1) + 2 * m)) & 0x00030003u;   // index of code 2m at bit 0, 2m+1 at bit 16
+    const uint32_t sel = x * 0x0202u + 0x01000100u;                      // bytes 2i, 2i + 1 of each half's entry
+    r[m] = (int)(__builtin_amdgcn_perm(t23, t01, sel) | ((d2 << (4 * s + m)) & 0x80008000u));
   }
   return __builtin_bit_cast(v8bf, r);
-}
-
-// 24-bit NF3 group (8 codes) -> 8 bf16 through a 4-entry table of the rounded
-// magnitudes (t01 = |v0| | |v1| << 16, t23 likewise): per code pair one byte
-// permute picks both magnitudes, then the sign bits are or-ed in.  A code c
-// stands for +mag[c - 4] (c >= 4) or -mag[3 - c]; the bits are worked on for
-// all eight codes at once.
-__device__ __forceinline__ v8bf nf3_step_lut(uint32_t w24, uint32_t t01, uint32_t t23) {
-  const uint32_t neg = (~w24 >> 2) & 0x249249u;             // bit 3e: code e is negative
-  const uint32_t idx = (w24 ^ (neg * 3u)) & 0x6DB6DBu;      // bits 3e, 3e + 1: magnitude index of code e
-  v4i r;
-#pragma unroll
-  for (int m = 0; m < 4; m++) {
-    const uint32_t x = ((idx >> (6 * m)) & 3u) | (((idx >> (6 * m + 3)) & 3u) << 16);
-    const uint32_t sel = ((x | (x << 8)) << 1) + 0x01000100u;
-    const uint32_t sgn = (((neg >> (6 * m)) & 1u) << 15) | (((neg >> (6 * m + 3)) & 1u) << 31);
-    r[m] = (int)(__builtin_amdgcn_perm(t23, t01, sel) | sgn);
-  }
-  return __builtin_bit_cast(v8bf, r);
-}
-
-// The 24-bit group s (codes 8 s .. 8 s + 7) of a lane's 12 NF3 bytes d0..d2.
-__device__ __forceinline__ uint32_t nf3_group(uint32_t d0, uint32_t d1, uint32_t d2, int s) {
-  return s == 0 ? (d0 & 0xFFFFFFu)
-       : s == 1 ? ((d0 >> 24) | (d1 << 8)) & 0xFFFFFFu
-       : s == 2 ? ((d1 >> 16) | (d2 << 16)) & 0xFFFFFFu
-                : d2 >> 8;
 }
 
 // Dequantised operand of one lane for k-step s (0..3) of a 128-column k-tile.
@@ -287,15 +270,9 @@ struct A16Tile {
     if (WF == W_NVFP4) {
       return nvfp4_step(d[s], e4m3_f32(s < 2 ? (sc & 0xFFu) : (sc >> 8)));
     } else {
-      const float f = e4m3_f32(sc);
-      // group s of 24 bits starts at bit 24*s of the 96-bit lane word
-      const uint64_t lo = (uint64_t)d[0] | ((uint64_t)d[1] << 32);
-      uint32_t w24;
-      if (s == 0) w24 = (uint32_t)lo & 0xFFFFFFu;
-      else if (s == 1) w24 = (uint32_t)(lo >> 24) & 0xFFFFFFu;
-      else if (s == 2) w24 = (uint32_t)((lo >> 48) | ((uint64_t)d[2] << 16)) & 0xFFFFFFu;
-      else w24 = d[2] >> 8;
-      return nf3_step(w24, 0.1275f * f, 0.3563f * f, 0.6047f * f, f);
+      uint32_t t01, t23;
+      nf3_tables(e4m3_f32(sc), t01, t23);
+      return nf3_step_rc(s < 2 ? d[0] : d[1], d[2], s, t01, t23);
     }
   }
 };

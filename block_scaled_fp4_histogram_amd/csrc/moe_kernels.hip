@@ -643,6 +643,58 @@ __global__ __launch_bounds__(256) void k_permute(const uint8_t *tmp, uint8_t *ds
   else *(Word *)(dst + ck) = *(const Word *)(tmp + o);
 }
 
+// NF3 codes between the packed form (code e of a 12-byte unit at bit 3e of its
+// 96 bits, little endian) and the kernels' sign / magnitude-index form (see
+// nf3_step_rc).  Both hold the same 96 bits of information per unit; the
+// rewrite is per unit, so it commutes with the tile permutation.
+__global__ __launch_bounds__(256) void k_nf3_recode(uint32_t *w, long units, int to_kernel) {
+  const long u = (long)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  uint32_t *p = w + 3 * u;
+  const uint32_t a0 = p[0], a1 = p[1], a2 = p[2];
+  uint32_t b0 = 0, b1 = 0, b2 = 0;
+  if (to_kernel) {
+#pragma unroll
+    for (int e = 0; e < 32; e++) {
+      const int bit = 3 * e;
+      uint32_t c;
+      if (bit + 3 <= 32) c = (a0 >> bit) & 7u;
+      else if (bit < 32) c = ((a0 >> bit) | (a1 << (32 - bit))) & 7u;
+      else if (bit + 3 <= 64) c = (a1 >> (bit - 32)) & 7u;
+      else if (bit < 64) c = ((a1 >> (bit - 32)) | (a2 << (64 - bit))) & 7u;
+      else c = (a2 >> (bit - 64)) & 7u;
+      const uint32_t neg = c < 4u ? 1u : 0u, idx = c < 4u ? 3u - c : c - 4u;
+      const int s = e >> 3, m = (e >> 1) & 3, h = e & 1;
+      const uint32_t ib = idx << (8 * (s & 1) + 2 * m + 16 * h);
+      if (s < 2) b0 |= ib;
+      else b1 |= ib;
+      b2 |= neg << (15 - (4 * s + m) + 16 * h);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; e++) {
+      const int s = e >> 3, m = (e >> 1) & 3, h = e & 1;
+      const uint32_t idx = ((s < 2 ? a0 : a1) >> (8 * (s & 1) + 2 * m + 16 * h)) & 3u;
+      const uint32_t neg = (a2 >> (15 - (4 * s + m) + 16 * h)) & 1u;
+      const uint32_t c = neg ? 3u - idx : idx + 4u;
+      const int bit = 3 * e;
+      if (bit < 32) b0 |= c << bit;
+      if (bit + 3 > 32 && bit < 64) b1 |= bit < 32 ? c >> (32 - bit) : c << (bit - 32);
+      if (bit + 3 > 64) b2 |= bit < 64 ? c >> (64 - bit) : c << (bit - 64);
+    }
+  }
+  p[0] = b0;
+  p[1] = b1;
+  p[2] = b2;
+}
+
+hipError_t launch_nf3_recode(uint8_t *w, long units, int to_kernel, hipStream_t s) {
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_nf3_recode, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, (uint32_t *)w, units,
+                     to_kernel);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const uint8_t *tmp, uint8_t *dst, long ne, int unit, int rows, int groups, int pair,
                           int gate_up, int to_tiles, hipStream_t s) {
   const long exp_bytes = (long)rows * groups * unit;

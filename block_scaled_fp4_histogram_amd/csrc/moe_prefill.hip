@@ -605,7 +605,7 @@ __device__ __forceinline__ void pf16_mma_step(const Pf16Ops<WF> &o, bool gin, co
   for (int q = 0; q < 2; q++) {
     v8bf aop;
     if constexpr (WF == W_NVFP4) aop = nvfp4_step(o.a[q][S], S < 2 ? slo[q] : shi[q]);
-    else aop = nf3_step_lut(nf3_group(o.a[q][0], o.a[q][1], o.a[q][2], S), t01[q], t23[q]);
+    else aop = nf3_step_rc(S < 2 ? o.a[q][0] : o.a[q][1], o.a[q][2], S, t01[q], t23[q]);
 #pragma unroll
     for (int cb = 0; cb < 4; cb++) acc[q][cb] = SWAP ? mfma_bf16(bop[cb], aop, acc[q][cb]) : mfma_bf16(aop, bop[cb], acc[q][cb]);
   }
@@ -626,9 +626,7 @@ __device__ __forceinline__ void pf16_mma(const Pf16Ops<WF> &o, int kt, int kcols
       slo[q] = e4m3_f32(sc & 0xFFu);
       shi[q] = e4m3_f32((sc >> 8) & 0xFFu);
     } else {
-      const float f = e4m3_f32(sc & 0xFFu);
-      t01[q] = pack_bf16x2(0.1275f * f, 0.3563f * f);
-      t23[q] = pack_bf16x2(0.6047f * f, f);
+      nf3_tables(e4m3_f32(sc & 0xFFu), t01[q], t23[q]);
     }
   }
   pf16_mma_step<WF, SWAP, FULL, 0>(o, gin, slo, shi, t01, t23, acc);
