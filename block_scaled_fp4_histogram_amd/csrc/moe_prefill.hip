@@ -414,214 +414,144 @@ hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s) {
 
 // ================================================================ W4A16 / W3A16
 //
-// The same 64-route tiles and LDS ring for NVFP4 and NF3 experts with bf16
-// activations.  A ring stage holds 8 weight row tiles of one 128-column k-tile
-// in MFMA lane order (16 / 12 bytes and 2 / 1 scale bytes per lane) and the 64
-// routes' bf16 activation slices (256 bytes each, 16-byte chunks XOR-swizzled
-// by row % 16).  Wave w owns row tiles 2w, 2w + 1 against all 64 routes, so
-// each weight element is dequantised once per tile, one 8-column step at a
-// time (E2M1 x E4M3, or NF3 codebook x E4M3, to bf16; exact for E2M1), and
-// feeds 4 bf16 MFMAs: 4 steps x 2 row tiles x 4 route blocks per k-tile.
+// The same 64-route tiles for NVFP4 and NF3 experts with bf16 activations.
+// Wave w owns weight row tiles 2w, 2w + 1 against all 64 routes, so each
+// weight element is dequantised once per tile, one 8-column step at a time
+// (E2M1 x E4M3, or NF3 codebook x E4M3, to bf16; exact for E2M1), and feeds 4
+// bf16 MFMAs: 4 steps x 2 row tiles x 4 route blocks per k-tile.  A wave's
+// weights are used by that wave only, so they skip LDS: buffer loads put each
+// k-tile's weight and scale bytes (16 / 12 and 2 / 1 per lane, MFMA lane
+// order) straight into a ring of kPf16Stages register sets.  The activations
+// are shared by the four waves and go through an LDS ring of the same depth:
+// a stage holds the 64 routes' bf16 slices of one 128-column k-tile (256 bytes
+// each, 16-byte chunks XOR-swizzled by row % 16) loaded directly to LDS.
 namespace {
 
 constexpr int kPf16Stages = 3;
+// vector-memory operations of one wave per stage: 2 weight tiles, 2 scale
+// loads, 4 activation chunks (both formats)
+constexpr int kPf16Loads = 8;
 
-// Direct-to-LDS loads of one wave per stage: NVFP4 2 weight tiles (16 bytes a
-// lane) + 1 scale chunk + 4 activation chunks; NF3 6 dword loads for 2 weight
-// tiles (768 bytes each) + 1 scale chunk + 4 activation chunks.  Loads narrower
-// than a dword are not used: they would leave 4-byte lane slots in LDS.
-template <int WF>
-struct Pf16Loads {
-  static constexpr int n = (WF == W_NVFP4) ? 7 : 11;
-};
-
-template <int WF>
 struct Pf16Stage {
-  static constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
-  uint8_t A[8][64 * U];
-  uint8_t AS[8][64 * SU];
-  uint8_t spare[256];   // NF3: landing slot of the scale loads of waves 2, 3
   uint8_t B[kPfTileRows][256];
 };
 
-template <int WF>
 struct __attribute__((aligned(16))) Pf16Lds {
-  Pf16Stage<WF> st[kPf16Stages];
+  Pf16Stage st[kPf16Stages];
 };
 
-template <int WF>
 __device__ __forceinline__ void wait16_stages(int stages) {
-  constexpr int n = Pf16Loads<WF>::n;
-  if (stages >= 2) wait_vm<2 * n>();
-  else if (stages == 1) wait_vm<n>();
+  if (stages >= 2) wait_vm<2 * kPf16Loads>();
+  else if (stages == 1) wait_vm<kPf16Loads>();
   else wait_vm<0>();
 }
 
 struct Pf16Src {
-  const uint8_t *wbase, *sbase;   // row tile rt, k-tile kt: wbase + rt * wstep + kt * 64 U (scales: 64 SU)
-  size_t wstep, sstep;
-  const uint16_t *brow[4];        // this lane's activation rows of its four B chunks
-  int kcols;                      // reduction length (columns)
+  Buf wb, sb;                  // the block's 8 weight row tiles / their scales
+  uint32_t wstep, sstep;       // bytes per row tile (data / scales)
+  const uint16_t *brow[4];     // this lane's activation rows of its four B chunks
+  int kcols;                   // reduction length (columns)
 };
 
-// The loads of wave w for k-tile kt: weight row tiles 2w, 2w+1 (NVFP4: one
-// 16-byte load each; NF3: three dword loads of 256 bytes each), one dword load
-// of scales (NVFP4: row tiles 2w, 2w+1; NF3: waves 0, 1 row tiles 4w .. 4w+3,
-// waves 2, 3 a spare slot), activation chunks 4w .. 4w+3 (1 KB each: 4 routes x
-// 256 bytes; lane l -> route 4j + l/16, LDS slot l % 16 holding global chunk
-// slot ^ route%16).  Lanes past the reduction length load from a valid address.
-template <int WF, bool FULL>
-__device__ __forceinline__ void pf16_issue(Pf16Stage<WF> &S, const Pf16Src &src, int kt, int w, int l) {
+// A wave's weight operands of one k-tile: row tiles 2w + q.  The scales come
+// as the aligned dword holding this lane's 2 (NVFP4) or 1 (NF3) bytes: a
+// narrower load would be zero-extended where the ring is carried round the
+// loop, which makes the compiler wait for every load in flight there.
+struct Pf16W {
+  uint32_t a[2][4];   // NVFP4 4 dwords, NF3 3 dwords (+1 zero)
+  uint32_t sc[2];
+};
+
+// This lane's scale bits (low 16 for NVFP4, low 8 for NF3) in its scale dword.
+template <int WF>
+__device__ __forceinline__ uint32_t pf16_scale(uint32_t dw, int l) {
+  return WF == W_NVFP4 ? dw >> (16 * (l & 1)) : dw >> (8 * (l & 3));
+}
+
+// Weight and scale loads of wave w for k-tile kt.  Lanes whose 32-column group
+// lies past the reduction length read past the buffer's range: zeros, and no
+// memory traffic.
+template <int WF>
+__device__ __forceinline__ void pf16_load_w(Pf16W &r, const Pf16Src &src, int kt, int w, int l) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
-  if constexpr (WF == W_NVFP4) {
-    const bool in = FULL || kt * 128 + 32 * (l >> 4) < src.kcols;
+  const bool in = kt * 128 + 32 * (l >> 4) < src.kcols;
+  const uint32_t vd = in ? (uint32_t)(kt * 64 * U + l * U) : 0x80000000u;
+  const uint32_t vs = in ? (uint32_t)(kt * 64 * SU + ((l * SU) & ~3)) : 0x80000000u;
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int rt = 2 * w + j;
-      dma16(src.wbase + rt * src.wstep + (in ? (size_t)kt * 64 * U + l * U : 0), &S.A[rt][0]);
-    }
-    // dword d of row tile 2w + l/32 holds the scales of MFMA lanes 2d, 2d + 1
-    const int rt = 2 * w + (l >> 5), d = l & 31;
-    const bool ins = FULL || kt * 128 + 32 * ((2 * d) >> 4) < src.kcols;
-    dma4(src.sbase + rt * src.sstep + (ins ? (size_t)kt * 64 * SU + 4 * d : 0), &S.AS[2 * w][0]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int rt = 2 * w + j;
-#pragma unroll
-      for (int m = 0; m < 3; m++) {   // bytes 256 m + 4 l of the row tile's 768-byte k-tile: MFMA lane (256 m + 4 l) / 12
-        const int lane = (256 * m + 4 * l) / 12;
-        const bool in = FULL || kt * 128 + 32 * (lane >> 4) < src.kcols;
-        dma4(src.wbase + rt * src.wstep + (in ? (size_t)kt * 64 * U + 256 * m + 4 * l : 0), &S.A[rt][256 * m]);
-      }
-    }
-    if (w < 2) {   // dword d of row tile 4w + l/16 holds the scales of MFMA lanes 4d .. 4d + 3
-      const int rt = 4 * w + (l >> 4), d = l & 15;
-      const bool ins = FULL || kt * 128 + 32 * ((4 * d) >> 4) < src.kcols;
-      dma4(src.sbase + rt * src.sstep + (ins ? (size_t)kt * 64 * SU + 4 * d : 0), &S.AS[4 * w][0]);
+  for (int q = 0; q < 2; q++) {
+    const uint32_t rt = (uint32_t)(2 * w + q);
+    if constexpr (WF == W_NVFP4) {
+      const v4i v = buf_load16(src.wb, vd, rt * src.wstep);
+      r.a[q][0] = v[0]; r.a[q][1] = v[1]; r.a[q][2] = v[2]; r.a[q][3] = v[3];
+      r.sc[q] = buf_load4(src.sb, vs, rt * src.sstep);
     } else {
-      dma4(src.sbase, &S.spare[0]);
+      const v3i v = buf_load12(src.wb, vd, rt * src.wstep);
+      r.a[q][0] = v[0]; r.a[q][1] = v[1]; r.a[q][2] = v[2]; r.a[q][3] = 0;
+      r.sc[q] = buf_load4(src.sb, vs, rt * src.sstep);
     }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int r = 4 * (4 * w + j) + (l >> 4), cg = (l & 15) ^ (r & 15), col = kt * 128 + 8 * cg;
-    dma16(src.brow[j] + (FULL || col < src.kcols ? col : 0), &S.B[4 * (4 * w + j)][0]);
   }
 }
 
-// One wave's operands of a landed stage: its 2 weight row tiles (2w, 2w + 1)
-// and all 64 routes' activation chunks (4 steps x 4 route blocks).
-template <int WF>
-struct Pf16Ops {
-  uint32_t a[2][4];   // row tile q: NVFP4 4 dwords, NF3 3 dwords (+1 unused)
-  int sc[2];
-  v4i b[4][4];        // step s, route block cb
-};
+// Activation chunks 4w .. 4w+3 of k-tile kt (1 KB each: 4 routes x 256 bytes;
+// lane l -> route 4j + l/16, LDS slot l % 16 holding global chunk slot ^
+// route%16).  Lanes past the reduction length load column 0.
+__device__ __forceinline__ void pf16_issue_b(Pf16Stage &S, const Pf16Src &src, int kt, int w, int l) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int r = 4 * (4 * w + j) + (l >> 4), cg = (l & 15) ^ (r & 15), col = kt * 128 + 8 * cg;
+    dma16(src.brow[j] + (col < src.kcols ? col : 0), &S.B[4 * (4 * w + j)][0]);
+  }
+}
 
-// LDS reads of one wave's operands (asm: invisible to the compiler's
-// direct-to-LDS bookkeeping, as for the W4A8 kernels).  The wait is part of
-// each statement: between an LDS read and its wait the compiler could copy the
-// register it loads.
-template <int WF>
-__device__ __forceinline__ void pf16_read(Pf16Ops<WF> &o, const Pf16Stage<WF> &S, int w, int l) {
-  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+// The 64 routes' activations of a landed stage, read and waited for in one
+// asm statement (invisible to the compiler's direct-to-LDS bookkeeping; a
+// wait in a later statement would let the compiler copy registers still in
+// flight).  b[s][cb]: step s, route block cb.
+__device__ __forceinline__ void pf16_read_b(v4i (&b)[4][4], const Pf16Stage &S, int l) {
   const int c = l & 15, g = l >> 4;
-  const uint32_t va = lds_addr(&S.A[2 * w][l * U]), vs = lds_addr(&S.AS[2 * w][l * SU]);
   const uint8_t *brow = &S.B[c][0];   // + 16 rows (4096 bytes) per route block
   uint32_t vb[4];
 #pragma unroll
   for (int s = 0; s < 4; s++) vb[s] = lds_addr(brow + 16 * ((4 * g + s) ^ c));
-#define PF16_READ_B                               \
-  "ds_read_b128 %0, %[b0]\n"                      \
-  "ds_read_b128 %1, %[b0] offset:4096\n"          \
-  "ds_read_b128 %2, %[b0] offset:8192\n"          \
-  "ds_read_b128 %3, %[b0] offset:12288\n"         \
-  "ds_read_b128 %4, %[b1]\n"                      \
-  "ds_read_b128 %5, %[b1] offset:4096\n"          \
-  "ds_read_b128 %6, %[b1] offset:8192\n"          \
-  "ds_read_b128 %7, %[b1] offset:12288\n"         \
-  "ds_read_b128 %8, %[b2]\n"                      \
-  "ds_read_b128 %9, %[b2] offset:4096\n"          \
-  "ds_read_b128 %10, %[b2] offset:8192\n"         \
-  "ds_read_b128 %11, %[b2] offset:12288\n"        \
-  "ds_read_b128 %12, %[b3]\n"                     \
-  "ds_read_b128 %13, %[b3] offset:4096\n"         \
-  "ds_read_b128 %14, %[b3] offset:8192\n"         \
-  "ds_read_b128 %15, %[b3] offset:12288\n"
-#define PF16_B_OUT                                                                                             \
-  "=&v"(o.b[0][0]), "=&v"(o.b[0][1]), "=&v"(o.b[0][2]), "=&v"(o.b[0][3]), "=&v"(o.b[1][0]), "=&v"(o.b[1][1]), \
-      "=&v"(o.b[1][2]), "=&v"(o.b[1][3]), "=&v"(o.b[2][0]), "=&v"(o.b[2][1]), "=&v"(o.b[2][2]),                 \
-      "=&v"(o.b[2][3]), "=&v"(o.b[3][0]), "=&v"(o.b[3][1]), "=&v"(o.b[3][2]), "=&v"(o.b[3][3])
-  if constexpr (WF == W_NVFP4) {
-    v4i a0, a1;
-    asm volatile(PF16_READ_B
-                 "ds_read_b128 %16, %[va]\n"
-                 "ds_read_b128 %17, %[va] offset:1024\n"
-                 "ds_read_u16 %18, %[vs]\n"
-                 "ds_read_u16 %19, %[vs] offset:128\n"
-                 "s_waitcnt lgkmcnt(0)"
-                 : PF16_B_OUT, "=&v"(a0), "=&v"(a1), "=&v"(o.sc[0]), "=&v"(o.sc[1])
-                 : [b0] "v"(vb[0]), [b1] "v"(vb[1]), [b2] "v"(vb[2]), [b3] "v"(vb[3]), [va] "v"(va), [vs] "v"(vs)
-                 : "memory");
-#pragma unroll
-    for (int d = 0; d < 4; d++) {
-      o.a[0][d] = (uint32_t)a0[d];
-      o.a[1][d] = (uint32_t)a1[d];
-    }
-  } else {
-    // 12-byte lanes are only 4-byte aligned: three dword reads per row tile
-    asm volatile(PF16_READ_B
-                 "ds_read_b32 %16, %[va]\n"
-                 "ds_read_b32 %17, %[va] offset:4\n"
-                 "ds_read_b32 %18, %[va] offset:8\n"
-                 "ds_read_b32 %19, %[va] offset:768\n"
-                 "ds_read_b32 %20, %[va] offset:772\n"
-                 "ds_read_b32 %21, %[va] offset:776\n"
-                 "ds_read_u8 %22, %[vs]\n"
-                 "ds_read_u8 %23, %[vs] offset:64\n"
-                 "s_waitcnt lgkmcnt(0)"
-                 : PF16_B_OUT, "=&v"(o.a[0][0]), "=&v"(o.a[0][1]), "=&v"(o.a[0][2]), "=&v"(o.a[1][0]),
-                   "=&v"(o.a[1][1]), "=&v"(o.a[1][2]), "=&v"(o.sc[0]), "=&v"(o.sc[1])
-                 : [b0] "v"(vb[0]), [b1] "v"(vb[1]), [b2] "v"(vb[2]), [b3] "v"(vb[3]), [va] "v"(va), [vs] "v"(vs)
-                 : "memory");
-    o.a[0][3] = o.a[1][3] = 0;
-  }
-#undef PF16_READ_B
-#undef PF16_B_OUT
+  asm volatile(
+      "ds_read_b128 %0, %16\n"
+      "ds_read_b128 %1, %16 offset:4096\n"
+      "ds_read_b128 %2, %16 offset:8192\n"
+      "ds_read_b128 %3, %16 offset:12288\n"
+      "ds_read_b128 %4, %17\n"
+      "ds_read_b128 %5, %17 offset:4096\n"
+      "ds_read_b128 %6, %17 offset:8192\n"
+      "ds_read_b128 %7, %17 offset:12288\n"
+      "ds_read_b128 %8, %18\n"
+      "ds_read_b128 %9, %18 offset:4096\n"
+      "ds_read_b128 %10, %18 offset:8192\n"
+      "ds_read_b128 %11, %18 offset:12288\n"
+      "ds_read_b128 %12, %19\n"
+      "ds_read_b128 %13, %19 offset:4096\n"
+      "ds_read_b128 %14, %19 offset:8192\n"
+      "ds_read_b128 %15, %19 offset:12288\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[0][2]), "=&v"(b[0][3]), "=&v"(b[1][0]), "=&v"(b[1][1]),
+        "=&v"(b[1][2]), "=&v"(b[1][3]), "=&v"(b[2][0]), "=&v"(b[2][1]), "=&v"(b[2][2]), "=&v"(b[2][3]),
+        "=&v"(b[3][0]), "=&v"(b[3][1]), "=&v"(b[3][2]), "=&v"(b[3][3])
+      : "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3])
+      : "memory");
 }
 
-// 8 bf16 MFMAs of step S of a k-tile (2 row tiles x 4 route blocks); each
-// dequantised weight operand feeds 4 MFMAs.  Columns past the reduction
-// length: scale 0 (weights 0) and activations 0.  SWAP: activations as the A
-// operand.
-template <int WF, bool SWAP, bool FULL, int S>
-__device__ __forceinline__ void pf16_mma_step(const Pf16Ops<WF> &o, bool gin, const float (&slo)[2], const float (&shi)[2],
-                                              const uint32_t (&t01)[2], const uint32_t (&t23)[2], v4f (*acc)[4]) {
-  v8bf bop[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; cb++) bop[cb] = __builtin_bit_cast(v8bf, (FULL || gin) ? o.b[S][cb] : v4i{0, 0, 0, 0});
-#pragma unroll
-  for (int q = 0; q < 2; q++) {
-    v8bf aop;
-    if constexpr (WF == W_NVFP4) aop = nvfp4_step(o.a[q][S], S < 2 ? slo[q] : shi[q]);
-    else aop = nf3_step_rc(S < 2 ? o.a[q][0] : o.a[q][1], o.a[q][2], S, t01[q], t23[q]);
-#pragma unroll
-    for (int cb = 0; cb < 4; cb++) acc[q][cb] = SWAP ? mfma_bf16(bop[cb], aop, acc[q][cb]) : mfma_bf16(aop, bop[cb], acc[q][cb]);
-  }
-}
-
-// One k-tile: the scales are decoded once per row tile (NF3: its scaled
-// magnitude table).
+// 32 bf16 MFMAs of one k-tile (4 steps x 2 row tiles x 4 route blocks); each
+// dequantised weight operand feeds 4 MFMAs.  Scales are decoded once per row
+// tile (NF3: its scaled magnitude table).  Columns past the reduction length
+// (FULL: none): the weights there are zero (their scales load as 0) and the
+// activations are zeroed.  SWAP: activations as the A operand.
 template <int WF, bool SWAP, bool FULL>
-__device__ __forceinline__ void pf16_mma(const Pf16Ops<WF> &o, int kt, int kcols, int l, v4f (*acc)[4]) {
-  const int g = l >> 4;
-  const bool gin = FULL || kt * 128 + 32 * g < kcols;
+__device__ __forceinline__ void pf16_mma(const Pf16W &wt, const v4i (&b)[4][4], int kt, int kcols, int l,
+                                         v4f (*acc)[4]) {
+  const bool gin = FULL || kt * 128 + 32 * (l >> 4) < kcols;
   float slo[2] = {0.f, 0.f}, shi[2] = {0.f, 0.f};
   uint32_t t01[2] = {0u, 0u}, t23[2] = {0u, 0u};
 #pragma unroll
   for (int q = 0; q < 2; q++) {
-    const uint32_t sc = gin ? (uint32_t)o.sc[q] : 0u;
+    const uint32_t sc = pf16_scale<WF>(wt.sc[q], l);
     if constexpr (WF == W_NVFP4) {
       slo[q] = e4m3_f32(sc & 0xFFu);
       shi[q] = e4m3_f32((sc >> 8) & 0xFFu);
@@ -629,43 +559,105 @@ __device__ __forceinline__ void pf16_mma(const Pf16Ops<WF> &o, int kt, int kcols
       nf3_tables(e4m3_f32(sc & 0xFFu), t01[q], t23[q]);
     }
   }
-  pf16_mma_step<WF, SWAP, FULL, 0>(o, gin, slo, shi, t01, t23, acc);
-  pf16_mma_step<WF, SWAP, FULL, 1>(o, gin, slo, shi, t01, t23, acc);
-  pf16_mma_step<WF, SWAP, FULL, 2>(o, gin, slo, shi, t01, t23, acc);
-  pf16_mma_step<WF, SWAP, FULL, 3>(o, gin, slo, shi, t01, t23, acc);
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    v8bf bop[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++) bop[cb] = __builtin_bit_cast(v8bf, gin ? b[s][cb] : v4i{0, 0, 0, 0});
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      v8bf aop;
+      if constexpr (WF == W_NVFP4) aop = nvfp4_step(wt.a[q][s], s < 2 ? slo[q] : shi[q]);
+      else aop = nf3_step_rc(s < 2 ? wt.a[q][0] : wt.a[q][1], wt.a[q][2], s, t01[q], t23[q]);
+#pragma unroll
+      for (int cb = 0; cb < 4; cb++)
+        acc[q][cb] = SWAP ? mfma_bf16(bop[cb], aop, acc[q][cb]) : mfma_bf16(aop, bop[cb], acc[q][cb]);
+    }
+  }
 }
 
-// One k-tile of the ring: after the barrier that proves stage kt landed for
-// every wave (and that every wave is done with stage kt - 1, whose slot then
-// takes stage kt + ST - 1), stage kt is read.
-template <int WF, bool SWAP>
-__device__ __forceinline__ void pf16_step(Pf16Lds<WF> &L, const Pf16Src &src, int kt, int nkt, int w,
-                                          v4f (*acc)[4]) {
+// One k-tile (R = kt % ST).  After the barrier that proves stage kt landed for
+// every wave (and that every wave is done with stage kt - 1), k-tile
+// kt + ST - 1 is issued: its activations into stage kt - 1's LDS slot, its
+// weights into the register set that held k-tile kt - 1.  Then stage kt is
+// read and multiplied with register set R.  WAITN: loads allowed in flight at
+// the wait (kPf16Loads when k-tile kt + 1 exists, else 0; -1: decided at run
+// time); ISSUE: whether k-tile kt + ST - 1 exists (-1: at run time).  Where
+// both are known at compile time the compiler's own bookkeeping of the ring
+// registers stays exact; at run time it falls back to full waits.
+template <int WF, bool SWAP, int R, int WAITN, int ISSUE>
+__device__ __forceinline__ void pf16_step(Pf16Lds &L, const Pf16Src &src, Pf16W (&ring)[kPf16Stages], int kt,
+                                          int nkt, int w, v4f (*acc)[4]) {
   constexpr int ST = kPf16Stages;
   const int l = threadIdx.x & 63;
-  wait16_stages<WF>(min(ST - 2, nkt - 1 - kt));   // stage kt has landed
+  if constexpr (WAITN == kPf16Loads) wait_vm<kPf16Loads>();
+  else if constexpr (WAITN == 0) wait_vm<0>();
+  else wait16_stages(min(ST - 2, nkt - 1 - kt));   // stage kt has landed
   __builtin_amdgcn_s_barrier();
   const int kn = kt + ST - 1;
-  if (kn < nkt) {
-    if ((kn + 1) * 128 <= src.kcols) pf16_issue<WF, true>(L.st[kn % ST], src, kn, w, l);
-    else pf16_issue<WF, false>(L.st[kn % ST], src, kn, w, l);
+  if (ISSUE == 1 || (ISSUE == -1 && kn < nkt)) {
+    // one branch-free load sequence: two paths of loads here would make the
+    // compiler's bookkeeping of the ring registers conservative (a full wait)
+    pf16_load_w<WF>(ring[(R + ST - 1) % ST], src, kn, w, l);
+    pf16_issue_b(L.st[kn % ST], src, kn, w, l);
   }
-  Pf16Ops<WF> o;
-  pf16_read<WF>(o, L.st[kt % ST], w, l);
-  if ((kt + 1) * 128 <= src.kcols) pf16_mma<WF, SWAP, true>(o, kt, src.kcols, l, acc);
-  else pf16_mma<WF, SWAP, false>(o, kt, src.kcols, l, acc);
+  v4i b[4][4];
+  pf16_read_b(b, L.st[kt % ST], l);
+  if ((kt + 1) * 128 <= src.kcols) pf16_mma<WF, SWAP, true>(ring[R], b, kt, src.kcols, l, acc);
+  else pf16_mma<WF, SWAP, false>(ring[R], b, kt, src.kcols, l, acc);
 }
 
-// w: the wave index, wave-uniform (scalar), so stage and weight addresses stay scalar.
-template <int WF, bool SWAP>
-__device__ __forceinline__ void pf16_kloop(Pf16Lds<WF> &L, const Pf16Src &src, int w, v4f (*acc)[4]) {
+// A k-loop of exactly NKT k-tiles (NKT <= 4), straight-line.
+template <int WF, bool SWAP, int NKT>
+__device__ __forceinline__ void pf16_kloop_fixed(Pf16Lds &L, const Pf16Src &src, Pf16W (&ring)[kPf16Stages], int w,
+                                                 v4f (*acc)[4]) {
   constexpr int ST = kPf16Stages;
+  static_assert(NKT >= 1 && NKT <= 4, "short k-loops");
+  pf16_step<WF, SWAP, 0, (1 < NKT) ? kPf16Loads : 0, (ST - 1 < NKT) ? 1 : 0>(L, src, ring, 0, NKT, w, acc);
+  if constexpr (NKT > 1)
+    pf16_step<WF, SWAP, 1, (2 < NKT) ? kPf16Loads : 0, (ST < NKT) ? 1 : 0>(L, src, ring, 1, NKT, w, acc);
+  if constexpr (NKT > 2)
+    pf16_step<WF, SWAP, 2, (3 < NKT) ? kPf16Loads : 0, (ST + 1 < NKT) ? 1 : 0>(L, src, ring, 2, NKT, w, acc);
+  if constexpr (NKT > 3)
+    pf16_step<WF, SWAP, 0, (4 < NKT) ? kPf16Loads : 0, (ST + 2 < NKT) ? 1 : 0>(L, src, ring, 3, NKT, w, acc);
+}
+
+// w: the wave index, wave-uniform (scalar), so stage and weight offsets stay
+// scalar.  Short reductions run a straight-line loop; long ones whole ring
+// turns while every step is steady, then at most ST + 1 closing steps.
+template <int WF, bool SWAP>
+__device__ __forceinline__ void pf16_kloop(Pf16Lds &L, const Pf16Src &src, int w, v4f (*acc)[4]) {
+  constexpr int ST = kPf16Stages;
+  static_assert(ST == 3, "the k-loop is unrolled by the ring depth");
   const int l = threadIdx.x & 63;
   const int nkt = (src.kcols + 127) / 128;
+  Pf16W ring[ST];
+  // stages 0 .. ST - 2 are issued even past the last k-tile (weights then load
+  // as zeros without traffic, activations from column 0): a fixed load count
+  // keeps the compiler's bookkeeping of the ring registers exact
 #pragma unroll
-  for (int s = 0; s < ST - 1; s++)
-    if (s < nkt) pf16_issue<WF, false>(L.st[s], src, s, w, l);
-  for (int kt = 0; kt < nkt; kt++) pf16_step<WF, SWAP>(L, src, kt, nkt, w, acc);
+  for (int s = 0; s < ST - 1; s++) {
+    pf16_load_w<WF>(ring[s], src, s, w, l);
+    pf16_issue_b(L.st[s], src, s, w, l);
+  }
+  if (nkt <= 4) {
+    if (nkt == 4) pf16_kloop_fixed<WF, SWAP, 4>(L, src, ring, w, acc);
+    else if (nkt == 3) pf16_kloop_fixed<WF, SWAP, 3>(L, src, ring, w, acc);
+    else if (nkt == 2) pf16_kloop_fixed<WF, SWAP, 2>(L, src, ring, w, acc);
+    else pf16_kloop_fixed<WF, SWAP, 1>(L, src, ring, w, acc);
+    return;
+  }
+  int kt = 0;
+  for (; kt + 2 * ST - 1 <= nkt; kt += ST) {   // k-tiles kt .. kt + 2 steady: kt + 2 + ST - 1 < nkt
+    pf16_step<WF, SWAP, 0, kPf16Loads, 1>(L, src, ring, kt, nkt, w, acc);
+    pf16_step<WF, SWAP, 1, kPf16Loads, 1>(L, src, ring, kt + 1, nkt, w, acc);
+    pf16_step<WF, SWAP, 2, kPf16Loads, 1>(L, src, ring, kt + 2, nkt, w, acc);
+  }
+  if (kt < nkt) pf16_step<WF, SWAP, 0, -1, -1>(L, src, ring, kt, nkt, w, acc);
+  if (kt + 1 < nkt) pf16_step<WF, SWAP, 1, -1, -1>(L, src, ring, kt + 1, nkt, w, acc);
+  if (kt + 2 < nkt) pf16_step<WF, SWAP, 2, -1, -1>(L, src, ring, kt + 2, nkt, w, acc);
+  if (kt + 3 < nkt) pf16_step<WF, SWAP, 0, -1, -1>(L, src, ring, kt + 3, nkt, w, acc);
+  if (kt + 4 < nkt) pf16_step<WF, SWAP, 1, -1, -1>(L, src, ring, kt + 4, nkt, w, acc);
 }
 
 }  // namespace
@@ -674,7 +666,7 @@ __device__ __forceinline__ void pf16_kloop(Pf16Lds<WF> &L, const Pf16Src &src, i
 template <int WF>
 __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
-  __shared__ Pf16Lds<WF> L;
+  __shared__ Pf16Lds L;
   const int K = a.K, N = a.N;
   const PfWork wk = pf_work(a, N / 64, true);
   if (!wk.valid) return;
@@ -682,10 +674,10 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int hb = wk.sub, groups = K / 32;
   Pf16Src src;
-  src.wstep = (size_t)16 * groups * U;
-  src.sstep = (size_t)16 * groups * SU;
-  src.wbase = a.w13 + (size_t)wk.e * (2 * N) * groups * U + (size_t)(8 * hb) * src.wstep;
-  src.sbase = a.s13 + (size_t)wk.e * (2 * N) * groups * SU + (size_t)(8 * hb) * src.sstep;
+  src.wstep = (uint32_t)(16 * groups * U);
+  src.sstep = (uint32_t)(16 * groups * SU);
+  src.wb = make_buf(a.w13 + (size_t)wk.e * (2 * N) * groups * U + (size_t)(8 * hb) * src.wstep, 8 * src.wstep);
+  src.sb = make_buf(a.s13 + (size_t)wk.e * (2 * N) * groups * SU + (size_t)(8 * hb) * src.sstep, 8 * src.sstep);
   src.kcols = K;
   // rows past the tile read route p0's token; their results are never stored
 #pragma unroll
@@ -721,7 +713,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
 template <int WF>
 __global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
-  __shared__ Pf16Lds<WF> L;
+  __shared__ Pf16Lds L;
   __shared__ int s_r[kPfTileRows];
   __shared__ float s_w[kPfTileRows];
   const int K = a.K, N = a.N;
@@ -731,10 +723,10 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int ob = wk.sub, groups = N / 32;   // output columns 128 ob .. +127 = w2 row tiles 8 ob .. +7
   Pf16Src src;
-  src.wstep = (size_t)16 * groups * U;
-  src.sstep = (size_t)16 * groups * SU;
-  src.wbase = a.w2 + (size_t)wk.e * K * groups * U + (size_t)(8 * ob) * src.wstep;
-  src.sbase = a.s2 + (size_t)wk.e * K * groups * SU + (size_t)(8 * ob) * src.sstep;
+  src.wstep = (uint32_t)(16 * groups * U);
+  src.sstep = (uint32_t)(16 * groups * SU);
+  src.wb = make_buf(a.w2 + (size_t)wk.e * K * groups * U + (size_t)(8 * ob) * src.wstep, 8 * src.wstep);
+  src.sb = make_buf(a.s2 + (size_t)wk.e * K * groups * SU + (size_t)(8 * ob) * src.sstep, 8 * src.sstep);
   src.kcols = N;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
