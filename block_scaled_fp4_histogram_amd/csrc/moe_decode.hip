@@ -6,18 +6,20 @@
 // (one route per lane; wave ballots group the routes of each expert in order of
 // first occurrence), and there is no separate planner, quantiser or combine:
 //
-//   k_dec_gemm1  grid (N/32 intermediate blocks, expert slots), 8 waves split K.
+//   k_dec_gemm1  grid (N/32 intermediate blocks, expert slots), 4 waves split K.
 //                The token rows of the expert's routes are quantised to MXFP8
 //                into LDS once per workgroup (W4A8) or read as bf16 (W4A16);
 //                up/gate GEMMs, clamped SwiGLU and requantisation of h, stored
-//                per route r = t*top_k + j.
-//   k_dec_gemm2  grid (K/16 output row tiles), the block's waves split the work.
-//                Each wave runs the down GEMM of its share for 16 output
-//                columns and folds the router-weighted results into per-token
-//                fp32 accumulators; the waves are summed in a fixed order and
-//                the bf16 output written.  No atomics: bit-stable run to run.
-//                W4A8 splits (expert, k-tile) items evenly over the waves and
-//                requests every item's weights up front; W4A16 splits experts.
+//                per route r = t*top_k + j.  Block (0, 0) also publishes the
+//                expert-group table the down GEMM reads.
+//   k_dec_gemm2  grid (K/16 output row tiles), 8 waves.  The block's work is
+//                the list of (expert group, 16-route pass, k-tile) items, split
+//                evenly over the waves; each wave streams its items' weights
+//                through a register ring and folds the router-weighted results
+//                into per-token fp32 accumulators; the waves are summed in a
+//                fixed order and the bf16 output written.  No atomics:
+//                bit-stable run to run.  Every route's intermediate row is
+//                staged in LDS by direct loads ahead of the ring.
 #include <type_traits>
 
 #include "moe_device.h"
@@ -36,11 +38,6 @@ __device__ __forceinline__ int dec_route_u(const DecArgs &a, int lane) {
     if (e1 >= 0 && e1 < a.tier[1].E) return a.tier[0].E + e1;
   }
   return -1;
-}
-
-__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return ((unsigned long long)hi << 32) | lo;
 }
 
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
@@ -382,35 +379,10 @@ __global__ __launch_bounds__(256, 4) void k_dec_gemm1_a16(DecArgs a) {
 //
 // Lane (token t = l % 16, group g) accumulates output columns 16*rt + 4g .. +3
 // of token t.  After the down GEMM of one expert for up to 16 of its routes
-// (MFMA columns), each route's router-weighted result moves to the lane of its
-// token by a lane shuffle; slots j of a token are visited in order.
-__device__ __forceinline__ void dec_fold(const DecArgs &a, unsigned long long md, int p0, int c, int g, const v4f &acc,
-                                         float wr, float *tok) {
-  float val[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) val[i] = acc[i] * wr;
-  for (int j = 0; j < a.topk; j++) {
-    const int rr = c * a.topk + j;   // route of token c, slot j
-    int src = 0;
-    bool take = false;
-    if (c < a.T && rr < 64 && ((md >> rr) & 1ull)) {
-      const int col = __popcll(md & ((1ull << rr) - 1ull)) - p0;
-      if (col >= 0 && col < 16) {
-        src = col;
-        take = true;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const float v = __shfl(val[i], src + 16 * g);
-      if (take) tok[i] += v;
-    }
-  }
-}
-
-// The same fold through a per-wave 16 x 16 fp32 LDS tile: lane (route column
-// c, group g) stores its router-weighted outputs, then lane (token c, group g)
-// adds the rows of its token's routes, slots in order.
+// (MFMA columns), the results move to the lanes of their tokens through a
+// per-wave 16 x 16 fp32 LDS tile: lane (route column c, group g) stores its
+// router-weighted outputs, then lane (token c, group g) adds the rows of its
+// token's routes, slots in order.
 __device__ __forceinline__ void dec_fold_lds(const DecArgs &a, unsigned long long md, int p0, int c, int g,
                                              const v4f &acc, float wr, float *yb, float *tok) {
   *(v4f *)(yb + c * 16 + 4 * g) = acc * wr;
@@ -425,156 +397,6 @@ __device__ __forceinline__ void dec_fold_lds(const DecArgs &a, unsigned long lon
         for (int i = 0; i < 4; i++) tok[i] += v[i];
       }
     }
-  }
-}
-
-// One w2 row tile of one expert: buffer resources of the expert's data and
-// scales and the row tile's wave-uniform offsets.
-struct W2Tile {
-  Buf wb, sb;
-  uint32_t w0, s0;
-  float g2;
-};
-
-// k-tiles of the down GEMM loaded in one burst: all of them when N <= 640
-// (W4A8); two at a time for W4A16, whose bf16 activations also sit in registers
-constexpr int kW2MaxTiles = 5;
-constexpr int kW2MaxTilesA16 = 2;
-constexpr int kDecG2Waves = 16;
-
-// Down GEMM of one expert for one row tile and up to 16 of its route columns:
-// every k-tile of weights (and, for W4A16, of activations) is requested before
-// the first MFMA, so one memory round trip covers the expert.
-template <bool A8, int WF>
-__device__ __forceinline__ v4f w2_expert(const DecArgs &a, const W2Tile &t, const uint8_t *hq_s, const uint8_t *hs_s,
-                                         int r, int g, uint32_t l, float *wr) {
-  constexpr uint32_t U = A8 ? 16 : FmtGeom<WF>::unit, SU = A8 ? 1 : FmtGeom<WF>::sunit;
-  typedef typename std::conditional<A8, v4i, A16Tile<WF>>::type T;
-  constexpr int NB = A8 ? kW2MaxTiles : kW2MaxTilesA16;
-  const int N = a.N, nkt = (N + 127) / 128;
-  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  *wr = r >= 0 ? a.topk_w[r] : 0.f;   // in flight with the weight burst
-  for (int kt0 = 0; kt0 < nkt; kt0 += NB) {
-    T A[NB];
-    int sa[NB];
-    v4i B[A8 ? 1 : NB][4];
-#pragma unroll
-    for (int j = 0; j < NB; j++) {
-      const int kt = kt0 + j, kb = kt * 128;
-      const bool inb = kt < nkt && kb + 32 * g < N;
-      if constexpr (A8) {
-        A[j] = v4i{0, 0, 0, 0};
-        sa[j] = 0;
-        if (inb) {
-          A[j] = buf_load16(t.wb, (uint32_t)kt * 1024u + l * 16u, t.w0);
-          sa[j] = buf_load1(t.sb, (uint32_t)kt * 64u + l, t.s0);
-        }
-      } else {
-        if (inb) A[j].load(t.wb, (uint32_t)kt * 64u * U + l * U, t.w0, t.sb, (uint32_t)kt * 64u * SU + l * SU, t.s0);
-        else A[j].zero();
-#pragma unroll
-        for (int s = 0; s < 4; s++) B[j][s] = v4i{0, 0, 0, 0};
-        if (r >= 0 && inb) {
-          const v4i *hp = (const v4i *)(a.hb + (size_t)r * N + kb + 32 * g);
-#pragma unroll
-          for (int s = 0; s < 4; s++) B[j][s] = hp[s];
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NB; j++) {
-      const int kt = kt0 + j, kb = kt * 128;
-      if (kt >= nkt) break;
-      if constexpr (A8) {
-        v4i B0 = v4i{0, 0, 0, 0}, B1 = v4i{0, 0, 0, 0};
-        int sb = 0;
-        if (r >= 0) {   // MXFP8 rows of every route are staged in LDS
-          const uint8_t *hrow = hq_s + r * (N + 16);
-          if (kb + 16 * g < N) B0 = *(const v4i *)(hrow + kb + 16 * g);
-          if (kb + 64 + 16 * g < N) B1 = *(const v4i *)(hrow + kb + 64 + 16 * g);
-          if (kb + 32 * g < N) sb = hs_s[r * hs_stride(N) + kb / 32 + g];
-        }
-        const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
-        acc = mfma_fp4_fp8(A[j], bop, acc, sa[j], sb);
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; s++) acc = mfma_bf16(A[j].step(s), __builtin_bit_cast(v8bf, B[j][s]), acc);
-      }
-    }
-  }
-  return acc;
-}
-
-// One wave's share of the experts (gi = w, w + kDecG2Waves, ...) of format WF
-// for output row tile rt.
-template <bool A8, int WF>
-__device__ __forceinline__ void dec_gemm2_wave(const DecArgs &a, const int *gu_s, const unsigned long long *gm_s,
-                                               int ng, const uint8_t *hq_s, const uint8_t *hs_s, float *tok) {
-  constexpr int U = A8 ? 16 : FmtGeom<WF>::unit, SU = A8 ? 1 : FmtGeom<WF>::sunit;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, g = l >> 4;
-  const int K = a.K, N = a.N, groups = N / 32, rt = blockIdx.x;
-  const size_t rt_bytes = (size_t)16 * groups * U, rt_scales = (size_t)16 * groups * SU;
-  for (int gi = w; gi < ng; gi += kDecG2Waves) {
-    const DecExpert X = dec_expert(a, __builtin_amdgcn_readfirstlane(gu_s[gi]));
-    if (!A8 && X.fmt != WF) continue;
-    W2Tile t;
-    t.wb = make_buf(X.w2 + (size_t)X.e * K * groups * U, (uint32_t)((size_t)K * groups * U));
-    t.sb = make_buf(X.s2 + (size_t)X.e * K * groups * SU, (uint32_t)((size_t)K * groups * SU));
-    t.w0 = (uint32_t)((size_t)rt * rt_bytes);
-    t.s0 = (uint32_t)((size_t)rt * rt_scales);
-    const unsigned long long md = uniform_u64(gm_s[gi]);
-    const int ncols = __popcll(md);
-    for (int p0 = 0; p0 < ncols; p0 += 16) {   // one pass unless the expert holds > 16 routes
-      const int r = (p0 + c < ncols) ? nth_bit(md, p0 + c) : -1;
-      float wr;
-      const v4f acc = w2_expert<A8, WF>(a, t, hq_s, hs_s, r, g, (uint32_t)l, &wr);
-      dec_fold(a, md, p0, c, g, acc, wr * X.g2, tok);
-    }
-  }
-}
-
-// W4A16 down GEMM, grid (K/16 output row tiles); the block's waves split the
-// experts (bf16 intermediate rows are read from global memory at MFMA time).
-__global__ __launch_bounds__(kDecG2Waves * 64) void k_dec_gemm2_a16(DecArgs a) {
-  __shared__ int gu_s[kDecodeMaxRoutes];
-  __shared__ unsigned long long gm_s[kDecodeMaxRoutes];
-  __shared__ int ng_s;
-  __shared__ float tred[kDecG2Waves][4][64];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
-  if (w == 0) {
-    const int u = dec_route_u(a, l);
-    const unsigned long long same = dec_same(u);
-    const int lead = same ? __ffsll(same) - 1 : -1;
-    int n = 0;
-    for (unsigned long long f = __ballot(lead == l); f; f &= f - 1, n++) {
-      const int L = __ffsll(f) - 1;
-      const unsigned long long m = __ballot(lead == L);
-      if (l == 0) {
-        gu_s[n] = __builtin_amdgcn_readlane(u, L);
-        gm_s[n] = m;
-      }
-    }
-    if (l == 0) ng_s = n;
-  }
-  __syncthreads();
-  float tok[4] = {0.f, 0.f, 0.f, 0.f};
-  dec_gemm2_wave<false, W_NVFP4>(a, gu_s, gm_s, ng_s, nullptr, nullptr, tok);
-  dec_gemm2_wave<false, W_NF3>(a, gu_s, gm_s, ng_s, nullptr, nullptr, tok);
-#pragma unroll
-  for (int i = 0; i < 4; i++) tred[w][i][l] = tok[i];
-  __syncthreads();
-  if (w == 0 && c < a.T) {
-    float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      s[i] = 0.f;
-#pragma unroll
-      for (int v = 0; v < kDecG2Waves; v++) s[i] += tred[v][i][l];
-    }
-    uint2 o;
-    o.x = pack_bf16x2(s[0], s[1]);
-    o.y = pack_bf16x2(s[2], s[3]);
-    *(uint2 *)(a.out + (size_t)c * a.K + blockIdx.x * 16 + 4 * g) = o;
   }
 }
 

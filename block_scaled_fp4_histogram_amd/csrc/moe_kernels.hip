@@ -1,6 +1,14 @@
 // gfx950 kernels of the routed MoE layer with block-scaled 4-bit expert weights.
 //
-// Data flow of one launch sequence (one chunk of T tokens, R = T * top_k routes):
+// Three launch sequences by batch size (the host picks one per chunk):
+//   * decode batches (<= 16 tokens, <= 64 routes): two kernels, see
+//     moe_decode.hip;
+//   * prefill batches (>= 128 tokens, N % 64 == 0): the route planner below,
+//     then the 64-route-tile GEMMs of moe_prefill.hip, then the combine below;
+//   * everything between: the route planner, the 16-route-tile GEMMs of this
+//     file, then the combine.
+// The planner and combine of the last two (one chunk of T tokens, R = T * top_k
+// routes):
 //   k_route      expert histogram, prefix offsets, stable route permutation and
 //                the tile table (one block when R <= kRouteChunk; otherwise
 //                count -> scan -> scatter); extra blocks quantise x to MXFP8 and

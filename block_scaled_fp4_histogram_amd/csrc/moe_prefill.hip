@@ -1,19 +1,17 @@
-// Prefill-size W4A8 GEMMs: tiles of 64 routes of one expert, operands streamed
-// into an LDS ring by direct global-to-LDS loads and shared by a 2 x 2 grid of
-// waves.
+// Prefill-size GEMMs: tiles of 64 routes of one expert.
 //
-// One ring stage holds one 128-column k-tile: 8 weight row tiles (8 x 1 KB of
-// FP4 in MFMA lane order), the 64 routes' MXFP8 activation slices (8 blocks of
-// 8 rows x 128 bytes, 16-byte chunks XOR-swizzled so that MFMA operand reads
-// spread over the LDS banks) and the scales of both (As: 8 x 64 bytes, Bs:
-// 64 x 4 bytes).  Every wave issues the same five loads per stage (two weight
-// tiles, two activation blocks, one 256-byte scale chunk), so "all but the
-// newest n stages have landed" is one s_waitcnt vmcnt(5 n) per wave followed
-// by a barrier.  Each wave reads its operands of k-tile kt+1 from LDS while its
-// MFMAs of k-tile kt run, and the ring keeps its other stages in flight.
-//
-// Wave (wr, wc) owns row tiles 4 wr .. +3 and routes 32 wc .. +31: 8 block-
-// scaled MFMAs per k-tile.
+// W4A8 (MXFP4 weights x MXFP8 activations).  A block holds 16 weight row tiles
+// (256 weight rows) against the tile's 64 routes; its operands stream through
+// a 3-stage LDS ring by direct global-to-LDS loads.  One stage holds one
+// 128-column k-tile: 16 weight row tiles (16 x 1 KB of FP4 in MFMA lane
+// order), the 64 routes' MXFP8 activation slices (8 blocks of 8 rows x 128
+// bytes, 16-byte chunks XOR-swizzled so that MFMA operand reads spread over
+// the LDS banks) and the scales of both (As: 16 x 64 bytes, Bs: 64 x 4 bytes).
+// Every wave issues the same eight loads per stage, so "all but the newest n
+// stages have landed" is one s_waitcnt vmcnt(8 n) per wave followed by a
+// barrier.  Wave (wr, wc) owns row tiles 8 wr .. +7 and routes 32 wc .. +31:
+// 16 block-scaled MFMAs per k-tile, operands read from LDS at the k-tile that
+// uses them.
 //
 // Blocks are numbered XCD-major: the hardware hands workgroup b to XCD b % 8,
 // so logical work item (b % 8) * per + b / 8 puts a contiguous run of
@@ -21,18 +19,20 @@
 // items column-block-major: all tiles of a hot expert then run at once on one
 // XCD against the same weight slab, which is read once, while the activations
 // (tens of MB, re-read once per column block) stay in the last-level cache.
-// The down GEMM orders them tile-major: the 56-odd column blocks of a tile
-// share its activation rows in L2, and one expert's w2 (2 MB) stays in L2
-// across its consecutive tiles.
+// The down GEMM orders them tile-major: the column blocks of a tile share its
+// activation rows in L2, and one expert's w2 stays in L2 across its
+// consecutive tiles.
 //
-//   k_pf_gemm1_a8  items (tile, 64-column intermediate block): up/gate GEMMs over
-//                  K, clamped SwiGLU and MXFP8 requantisation of 64 intermediate
-//                  columns of 64 routes.
-//   k_pf_gemm2_a8  items (tile, 128-column output block): down GEMM over N with
+//   k_pf_gemm1_a8  items (tile, 128-column intermediate block = 8 up and 8
+//                  gate row tiles): up/gate GEMMs over K, clamped SwiGLU and
+//                  MXFP8 requantisation of 128 intermediate columns of 64 routes.
+//   k_pf_gemm2_a8  items (tile, 256-column output block): down GEMM over N with
 //                  the activations as the MFMA's A operand, so each lane holds
 //                  16 consecutive output columns' worth of one route per
 //                  instruction; combine straight from the accumulators (fp32
 //                  atomics, or bf16 route-buffer rows).
+//
+// W4A16 / W3A16 (NVFP4 or NF3 weights x bf16 activations): see that section.
 #include "moe_device.h"
 
 namespace moe {
