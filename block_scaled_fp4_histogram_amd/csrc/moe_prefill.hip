@@ -38,14 +38,15 @@
 namespace moe {
 
 constexpr int kPfRT = 16;        // W4A8: weight row tiles per block (256 weight rows)
-constexpr int kPfQ = 8;          // W4A8: row tiles per wave
-constexpr int kPfStages = 3;     // W4A8: LDS ring depth (k-tiles)
-constexpr int kPfLoadsPerStage = 8;
+constexpr int kPfQ = 4;          // W4A8: row tiles per wave
+constexpr int kPfStages = 3;     // W4A8: ring depth (k-tiles), LDS and registers
+// vector-memory operations of one wave per stage: 4 weight tiles, 4 weight
+// scale dwords, 2 activation blocks, 1 activation scale chunk (or a spare)
+constexpr int kPfLoads = 11;
 
 struct PfStage {
-  uint8_t A[kPfRT][1024];         // weight row tiles, MFMA lane order
   uint8_t B[8][1024];             // activation rows 8b .. 8b+7 of block b, swizzled 16-byte chunks
-  uint8_t S[2048];                // As [16][64] | Bs [64][4] | 3 spare 256-byte slots
+  uint8_t S[1024];                // Bs [64][4] | 3 spare 256-byte slots
 };
 
 struct __attribute__((aligned(16))) PfLds {
@@ -54,8 +55,8 @@ struct __attribute__((aligned(16))) PfLds {
 
 // Wait until at most `stages` ring stages issued by this wave are in flight.
 __device__ __forceinline__ void wait_stages(int stages) {
-  if (stages >= 2) wait_vm<2 * kPfLoadsPerStage>();
-  else if (stages == 1) wait_vm<kPfLoadsPerStage>();
+  if (stages >= 2) wait_vm<2 * kPfLoads>();
+  else if (stages == 1) wait_vm<kPfLoads>();
   else wait_vm<0>();
 }
 
@@ -89,169 +90,187 @@ __device__ __forceinline__ PfWork pf_work(const GemmArgs &a, int nsub, bool sub_
 }
 
 struct PfSrc {
-  const uint8_t *wbase, *sbase;   // row tile rt, k-tile kt: wbase + rt * wstep + kt * 1024 (scales: 64 per k-tile)
-  size_t wstep, sstep;
-  int nrt;                        // row tiles of this block that exist (8 or 16); the rest repeat the last one
+  Buf wb, sb;                     // the block's weight row tiles / their scales (nrt tiles)
+  uint32_t wstep, sstep;          // bytes per row tile (data / scales)
+  int nrt;                        // row tiles of this block that exist (8 or 16)
   const uint8_t *brow[2];         // this lane's activation rows of its two B blocks
   const uint8_t *bsrow;           // activation scale row of route (lane)
   int kbytes;                     // reduction length (bytes of one activation row)
 };
 
-// The eight loads of wave w for k-tile kt into stage S: weight row tiles 4w ..
-// 4w+3, activation blocks 2w, 2w+1, the scales of row tiles 4w .. 4w+3, and the
-// activation scales (wave 0; waves 1-3 fill spare slots to keep the per-wave
-// load count equal).  Lanes whose data lies past the reduction length (a
-// partial last k-tile) load from a valid address instead; the MFMA step zeroes
-// those activation bytes and both scales there.
-template <bool FULL>
-__device__ __forceinline__ void pf_issue(PfStage &S, const PfSrc &src, int kt, int w, int l) {
-  const bool in = FULL || (kt * 4 + (l >> 4)) * 32 < src.kbytes;
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int rt = 4 * w + j, rs = min(rt, src.nrt - 1);
-    dma16(src.wbase + rs * src.wstep + (in ? (size_t)kt * 1024 + l * 16 : 0), &S.A[rt][0]);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; j++) {   // activation blocks 2w + j: lane l -> row l / 8, its chunk slot l
-    const int r8 = l >> 3, part = (l & 7) ^ r8, off = kt * 128 + part * 16;
-    dma16(src.brow[j] + (FULL || off < src.kbytes ? off : 0), &S.B[2 * w + j][0]);
-  }
-  {   // As row tiles 4w .. 4w+3: lane l -> row tile 4w + l / 16, dword l % 16
-    const int rs = min(4 * w + (l >> 4), src.nrt - 1), d = l & 15;
-    const bool ins = FULL || (kt * 4 + (d >> 2)) * 32 < src.kbytes;
-    dma4(src.sbase + rs * src.sstep + (ins ? (size_t)kt * 64 + 4 * d : 0), &S.S[256 * w]);
-  }
-  dma4(src.bsrow + 4 * kt, &S.S[w == 0 ? 1024 : 1024 + 256 * w]);
-}
-
-// One wave's operands of a landed stage.  The LDS reads are issued by asm the
-// compiler cannot see into: seen, each would make it wait for every direct-to-
-// LDS load in flight (it cannot tell ring stages apart), emptying the ring at
-// every k-tile.  pf_read issues them and waits for them in one statement.
-struct PfOps {
-  v4i a[kPfQ];   // weight row tiles 8 wr + q
-  v4i b[4];      // activation chunks: [cb] = columns 16 g .. of route block cb, [2 + cb] = columns 64 + 16 g ..
-  int sa[kPfQ], sb[2];
+// A wave's weight operands of one k-tile: row tiles 4w + q, and the aligned
+// scale dword holding this lane's byte (a narrower load would be zero-extended
+// where the ring is carried round the loop, which makes the compiler wait for
+// every load in flight there).
+struct PfW {
+  v4i a[kPfQ];
+  uint32_t sa[kPfQ];
 };
 
-__device__ __forceinline__ void pf_read(PfOps &o, const PfStage &S, int wr, int wc, int l) {
+// Weight and scale loads of wave w for k-tile kt.  Lanes whose 32-column group
+// lies past the reduction length, and row tiles past the block's last one,
+// read past the buffer's range: zeros, and no memory traffic.
+__device__ __forceinline__ void pf_load_w(PfW &r, const PfSrc &src, int kt, int w, int l) {
+  const bool in = (kt * 4 + (l >> 4)) * 32 < src.kbytes;
+#pragma unroll
+  for (int q = 0; q < kPfQ; q++) {
+    const int rt = 4 * w + q;
+    const bool ok = in && rt < src.nrt;
+    const uint32_t so = rt < src.nrt ? (uint32_t)rt : 0u;
+    r.a[q] = buf_load16(src.wb, ok ? (uint32_t)(kt * 1024 + l * 16) : 0x80000000u, so * src.wstep);
+    r.sa[q] = buf_load4(src.sb, ok ? (uint32_t)(kt * 64 + (l & ~3)) : 0x80000000u, so * src.sstep);
+  }
+}
+
+// The shared loads of wave w for k-tile kt into stage S: activation blocks 2w,
+// 2w+1 (lane l -> row l / 8, its chunk slot l) and the activation scales (wave
+// 0; waves 1-3 fill spare slots to keep the per-wave load count equal).  Lanes
+// past the reduction length load column 0; the MFMA step zeroes those bytes.
+__device__ __forceinline__ void pf_issue_b(PfStage &S, const PfSrc &src, int kt, int w, int l) {
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int r8 = l >> 3, part = (l & 7) ^ r8, off = kt * 128 + part * 16;
+    dma16(src.brow[j] + (off < src.kbytes ? off : 0), &S.B[2 * w + j][0]);
+  }
+  const int nkt = (src.kbytes + 127) / 128;
+  dma4(src.bsrow + 4 * min(kt, nkt - 1), &S.S[256 * w]);   // a stage past the end re-reads the last one
+}
+
+// The 64 routes' activations of a landed stage: b[cb][h] = columns 64 h +
+// 16 g .. of route 16 cb + c, sb[cb] its scale of 32-column group g.  Read
+// with asm (invisible to the compiler's direct-to-LDS bookkeeping, which would
+// otherwise wait for every ring stage in flight) and waited for in the same
+// statement (a wait in a later statement would let the compiler copy
+// registers still in flight).
+__device__ __forceinline__ void pf_read_b(v4i (&b)[4][2], int (&sb)[4], const PfStage &S, int l) {
   const int c = l & 15, g = l >> 4, r8 = c & 7;
-  const uint8_t *bblk = &S.B[4 * wc + (c >> 3)][0];
-  const uint32_t va = lds_addr(&S.A[kPfQ * wr][l * 16]), vb0 = lds_addr(bblk + pf_slot(r8, g) * 16),
-                 vb1 = lds_addr(bblk + pf_slot(r8, 4 + g) * 16), vsa = lds_addr(&S.S[kPfQ * wr * 64 + l]),
-                 vsb = lds_addr(&S.S[1024 + (32 * wc + c) * 4 + g]);
-  // the wait is part of the same statement: between an LDS read and its wait
-  // the compiler could copy the register it loads (it cannot know the value
-  // is still in flight)
+  const uint8_t *blk = &S.B[c >> 3][0];   // + 2 KB per route block
+  const uint32_t vb0 = lds_addr(blk + pf_slot(r8, g) * 16), vb1 = lds_addr(blk + pf_slot(r8, 4 + g) * 16),
+                 vsb = lds_addr(&S.S[c * 4 + g]);   // + 64 bytes per route block
   asm volatile(
-      "ds_read_b128 %8, %23\n"
-      "ds_read_b128 %9, %23 offset:2048\n"
-      "ds_read_b128 %10, %24\n"
-      "ds_read_b128 %11, %24 offset:2048\n"
-      "ds_read_u8 %20, %26\n"
-      "ds_read_u8 %21, %26 offset:64\n"
-      "ds_read_u8 %12, %25\n"
-      "ds_read_u8 %13, %25 offset:64\n"
-      "ds_read_u8 %14, %25 offset:128\n"
-      "ds_read_u8 %15, %25 offset:192\n"
-      "ds_read_u8 %16, %25 offset:256\n"
-      "ds_read_u8 %17, %25 offset:320\n"
-      "ds_read_u8 %18, %25 offset:384\n"
-      "ds_read_u8 %19, %25 offset:448\n"
-      "ds_read_b128 %0, %22\n"
-      "ds_read_b128 %1, %22 offset:1024\n"
-      "ds_read_b128 %2, %22 offset:2048\n"
-      "ds_read_b128 %3, %22 offset:3072\n"
-      "ds_read_b128 %4, %22 offset:4096\n"
-      "ds_read_b128 %5, %22 offset:5120\n"
-      "ds_read_b128 %6, %22 offset:6144\n"
-      "ds_read_b128 %7, %22 offset:7168\n"
+      "ds_read_b128 %0, %12\n"
+      "ds_read_b128 %1, %13\n"
+      "ds_read_b128 %2, %12 offset:2048\n"
+      "ds_read_b128 %3, %13 offset:2048\n"
+      "ds_read_b128 %4, %12 offset:4096\n"
+      "ds_read_b128 %5, %13 offset:4096\n"
+      "ds_read_b128 %6, %12 offset:6144\n"
+      "ds_read_b128 %7, %13 offset:6144\n"
+      "ds_read_u8 %8, %14\n"
+      "ds_read_u8 %9, %14 offset:64\n"
+      "ds_read_u8 %10, %14 offset:128\n"
+      "ds_read_u8 %11, %14 offset:192\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.a[4]), "=&v"(o.a[5]), "=&v"(o.a[6]),
-        "=&v"(o.a[7]), "=&v"(o.b[0]), "=&v"(o.b[1]), "=&v"(o.b[2]), "=&v"(o.b[3]), "=&v"(o.sa[0]), "=&v"(o.sa[1]),
-        "=&v"(o.sa[2]), "=&v"(o.sa[3]), "=&v"(o.sa[4]), "=&v"(o.sa[5]), "=&v"(o.sa[6]), "=&v"(o.sa[7]),
-        "=&v"(o.sb[0]), "=&v"(o.sb[1])
-      : "v"(va), "v"(vb0), "v"(vb1), "v"(vsa), "v"(vsb)
+      : "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[1][0]), "=&v"(b[1][1]), "=&v"(b[2][0]), "=&v"(b[2][1]),
+        "=&v"(b[3][0]), "=&v"(b[3][1]), "=&v"(sb[0]), "=&v"(sb[1]), "=&v"(sb[2]), "=&v"(sb[3])
+      : "v"(vb0), "v"(vb1), "v"(vsb)
       : "memory");
 }
 
-// 16 MFMAs of one k-tile, two per weight row tile.  Past the reduction length (a partial last k-tile; FULL: none) the activation
+// 16 block-scaled MFMAs of one k-tile (4 row tiles x 4 route blocks).  Past
+// the reduction length (a partial last k-tile; FULL: none) the activation
 // bytes are zeroed and both scales set to 2^-127, so the products there are
-// exact zeros whatever the stage held.  SWAP: activations as the A operand
-// (accumulator lane = output column, elements = 4 routes).
-template <bool SWAP, bool FULL, int Q>
-__device__ __forceinline__ void pf_mma_q(const PfOps &o, bool gin, const v8i (&bop)[2], v4f (*acc)[2]) {
-#pragma unroll
-  for (int cb = 0; cb < 2; cb++) {
-    const int sa = (FULL || gin) ? o.sa[Q] : 0, sb = (FULL || gin) ? o.sb[cb] : 0;
-    if (SWAP)
-      acc[Q][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bop[cb], fp4_operand(o.a[Q]), acc[Q][cb], 0, 4, 0,
-                                                                    sb, 0, sa);
-    else
-      acc[Q][cb] = mfma_fp4_fp8(o.a[Q], bop[cb], acc[Q][cb], sa, sb);
-  }
-}
-
+// exact zeros.  SWAP: activations as the A operand (accumulator lane = output
+// column, elements = 4 routes).
 template <bool SWAP, bool FULL>
-__device__ __forceinline__ void pf_mma(const PfOps &o, int kt, int kbytes, int l, v4f (*acc)[2]) {
+__device__ __forceinline__ void pf_mma(const PfW &wt, const v4i (&b)[4][2], const int (&sb)[4], int kt, int kbytes,
+                                       int l, v4f (*acc)[4]) {
   const int g = l >> 4;
   const bool in0 = FULL || kt * 128 + 16 * g < kbytes, in1 = FULL || kt * 128 + 64 + 16 * g < kbytes;
   const bool gin = FULL || (kt * 4 + g) * 32 < kbytes;   // 32-column group g of this k-tile exists
-  v8i bop[2];
+  v8i bop[4];
 #pragma unroll
-  for (int cb = 0; cb < 2; cb++) {
-    const v4i b0 = in0 ? o.b[cb] : v4i{0, 0, 0, 0};
-    const v4i b1 = in1 ? o.b[2 + cb] : v4i{0, 0, 0, 0};
+  for (int cb = 0; cb < 4; cb++) {
+    const v4i b0 = in0 ? b[cb][0] : v4i{0, 0, 0, 0};
+    const v4i b1 = in1 ? b[cb][1] : v4i{0, 0, 0, 0};
     bop[cb] = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
   }
-  pf_mma_q<SWAP, FULL, 0>(o, gin, bop, acc);
-  pf_mma_q<SWAP, FULL, 1>(o, gin, bop, acc);
-  pf_mma_q<SWAP, FULL, 2>(o, gin, bop, acc);
-  pf_mma_q<SWAP, FULL, 3>(o, gin, bop, acc);
-  pf_mma_q<SWAP, FULL, 4>(o, gin, bop, acc);
-  pf_mma_q<SWAP, FULL, 5>(o, gin, bop, acc);
-  pf_mma_q<SWAP, FULL, 6>(o, gin, bop, acc);
-  pf_mma_q<SWAP, FULL, 7>(o, gin, bop, acc);
+#pragma unroll
+  for (int q = 0; q < kPfQ; q++) {
+    const int sa = gin ? (int)(wt.sa[q] >> (8 * (l & 3))) : 0;   // the MFMA takes the low byte
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++) {
+      const int sbv = gin ? sb[cb] : 0;
+      if (SWAP)
+        acc[q][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bop[cb], fp4_operand(wt.a[q]), acc[q][cb], 0, 4,
+                                                                      0, sbv, 0, sa);
+      else
+        acc[q][cb] = mfma_fp4_fp8(wt.a[q], bop[cb], acc[q][cb], sa, sbv);
+    }
+  }
 }
 
-// One k-tile: wait until stage kt has landed for every wave (every wave is
-// then also done with stage kt - 1), refill stage kt - 1's slot with k-tile
-// kt + kPfStages - 1, read this wave's operands of stage kt, multiply.
-template <bool SWAP>
-__device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, int kt, int nkt, v4f (*acc)[2]) {
+// One k-tile (R = kt % ST).  After the barrier that proves stage kt landed for
+// every wave (and that every wave is done with stage kt - 1), k-tile
+// kt + ST - 1 is issued: its activations into stage kt - 1's LDS slot, its
+// weights into the register set that held k-tile kt - 1.  Then stage kt is
+// read and multiplied with register set R.  WAITN: loads allowed in flight at
+// the wait (kPfLoads when k-tile kt + 1 exists, else 0; -1: decided at run
+// time); ISSUE: whether k-tile kt + ST - 1 exists (-1: at run time).  Where
+// both are known at compile time the compiler's own bookkeeping of the ring
+// registers stays exact.  Waves without weight rows (the missing half of a
+// partial block) still load and pass the barriers, but skip the MFMAs.
+template <bool SWAP, int R, int WAITN, int ISSUE>
+__device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, PfW (&ring)[kPfStages], int kt, int nkt, int w,
+                                        bool active, v4f (*acc)[4]) {
   constexpr int ST = kPfStages;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, wr = w >> 1, wc = w & 1;
-  wait_stages(min(ST - 2, nkt - 1 - kt));   // stage kt has landed
+  const int l = threadIdx.x & 63;
+  if constexpr (WAITN == kPfLoads) wait_vm<kPfLoads>();
+  else if constexpr (WAITN == 0) wait_vm<0>();
+  else wait_stages(min(ST - 2, nkt - 1 - kt));   // stage kt has landed
   __builtin_amdgcn_s_barrier();
   const int kn = kt + ST - 1;
-  if (kn < nkt) {
-    if ((kn + 1) * 128 <= src.kbytes) pf_issue<true>(L.st[kn % ST], src, kn, w, l);
-    else pf_issue<false>(L.st[kn % ST], src, kn, w, l);
+  if (ISSUE == 1 || (ISSUE == -1 && kn < nkt)) {
+    // one branch-free load sequence keeps the compiler's waits exact
+    pf_load_w(ring[(R + ST - 1) % ST], src, kn, w, l);
+    pf_issue_b(L.st[kn % ST], src, kn, w, l);
   }
-  PfOps o;
-  pf_read(o, L.st[kt % ST], wr, wc, l);
-  if ((kt + 1) * 128 <= src.kbytes) pf_mma<SWAP, true>(o, kt, src.kbytes, l, acc);
-  else pf_mma<SWAP, false>(o, kt, src.kbytes, l, acc);
+  v4i b[4][2];
+  int sb[4];
+  pf_read_b(b, sb, L.st[kt % ST], l);
+  if (active) {
+    if ((kt + 1) * 128 <= src.kbytes) pf_mma<SWAP, true>(ring[R], b, sb, kt, src.kbytes, l, acc);
+    else pf_mma<SWAP, false>(ring[R], b, sb, kt, src.kbytes, l, acc);
+  }
 }
 
-// The k-loop of both GEMMs.
+// The k-loop of both GEMMs: whole ring turns while every step is steady, then
+// at most ST + 1 closing steps.  w: the wave index, wave-uniform (scalar).
 template <bool SWAP>
-__device__ __forceinline__ void pf_kloop(PfLds &L, const PfSrc &src, v4f (*acc)[2]) {
+__device__ __forceinline__ void pf_kloop(PfLds &L, const PfSrc &src, int w, v4f (*acc)[4]) {
   constexpr int ST = kPfStages;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  static_assert(ST == 3, "the k-loop is unrolled by the ring depth");
+  const int l = threadIdx.x & 63;
   const int nkt = (src.kbytes + 127) / 128;
+  const bool active = kPfQ * w < src.nrt;
+  PfW ring[ST];
+  // stages 0 .. ST - 2 are issued even past the last k-tile (weights then load
+  // as zeros without traffic, activations from column 0): a fixed load count
+  // keeps the compiler's bookkeeping of the ring registers exact
 #pragma unroll
-  for (int s = 0; s < ST - 1; s++)
-    if (s < nkt) pf_issue<false>(L.st[s], src, s, w, l);
-  for (int kt = 0; kt < nkt; kt++) pf_step<SWAP>(L, src, kt, nkt, acc);
+  for (int s = 0; s < ST - 1; s++) {
+    pf_load_w(ring[s], src, s, w, l);
+    pf_issue_b(L.st[s], src, s, w, l);
+  }
+  int kt = 0;
+  for (; kt + 2 * ST - 1 <= nkt; kt += ST) {   // k-tiles kt .. kt + 2 steady: kt + 2 + ST - 1 < nkt
+    pf_step<SWAP, 0, kPfLoads, 1>(L, src, ring, kt, nkt, w, active, acc);
+    pf_step<SWAP, 1, kPfLoads, 1>(L, src, ring, kt + 1, nkt, w, active, acc);
+    pf_step<SWAP, 2, kPfLoads, 1>(L, src, ring, kt + 2, nkt, w, active, acc);
+  }
+  if (kt < nkt) pf_step<SWAP, 0, -1, -1>(L, src, ring, kt, nkt, w, active, acc);
+  if (kt + 1 < nkt) pf_step<SWAP, 1, -1, -1>(L, src, ring, kt + 1, nkt, w, active, acc);
+  if (kt + 2 < nkt) pf_step<SWAP, 2, -1, -1>(L, src, ring, kt + 2, nkt, w, active, acc);
+  if (kt + 3 < nkt) pf_step<SWAP, 0, -1, -1>(L, src, ring, kt + 3, nkt, w, active, acc);
+  if (kt + 4 < nkt) pf_step<SWAP, 1, -1, -1>(L, src, ring, kt + 4, nkt, w, active, acc);
 }
 
-template <int Q>
-__device__ __forceinline__ void zero_acc(v4f (*acc)[2]) {
+template <int Q, int CB>
+__device__ __forceinline__ void zero_acc(v4f (*acc)[CB]) {
 #pragma unroll
   for (int q = 0; q < Q; q++)
 #pragma unroll
-    for (int cb = 0; cb < 2; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
 }
 
 // Down-GEMM combine from accumulators in the swapped layout: acc[q][cb][i] is
@@ -301,20 +320,23 @@ __device__ __forceinline__ void pf_combine(const GemmArgs &a, const PfWork &wk, 
 
 // ---------------------------------------------------------------- GEMM1
 // Block: 16 row tiles of w13 = up and gate of 128 intermediate columns (the
-// last block of an N % 128 == 64 layer holds 8).
-__global__ __launch_bounds__(256) void k_pf_gemm1_a8(GemmArgs a) {
+// last block of an N % 128 == 64 layer holds 8).  Wave w: row tiles 4w .. 4w+3
+// = up and gate of intermediate columns 128 hb + 32 w .. +31 (one MXFP8 group).
+__global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8(GemmArgs a) {
   __shared__ PfLds L;
   const int K = a.K, N = a.N;
   const PfWork wk = pf_work(a, (N + 127) / 128, true);
   if (!wk.valid) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int hb = wk.sub;
   PfSrc src;
-  src.wstep = (size_t)16 * (K / 2);
-  src.sstep = (size_t)16 * (K / 32);
-  src.wbase = a.w13 + (size_t)wk.e * (2 * N) * (K / 2) + (size_t)(kPfRT * hb) * src.wstep;
-  src.sbase = a.s13 + (size_t)wk.e * (2 * N) * (K / 32) + (size_t)(kPfRT * hb) * src.sstep;
+  src.wstep = (uint32_t)(16 * (K / 2));
+  src.sstep = (uint32_t)(16 * (K / 32));
   src.nrt = min(kPfRT, N / 8 - kPfRT * hb);
+  src.wb = make_buf(a.w13 + (size_t)wk.e * (2 * N) * (K / 2) + (size_t)(kPfRT * hb) * src.wstep, src.nrt * src.wstep);
+  src.sb = make_buf(a.s13 + (size_t)wk.e * (2 * N) * (K / 32) + (size_t)(kPfRT * hb) * src.sstep,
+                    src.nrt * src.sstep);
   src.kbytes = K;
   // rows past the tile read route p0's token; their results are never stored
 #pragma unroll
@@ -323,62 +345,58 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a8(GemmArgs a) {
     src.brow[j] = a.xq + (size_t)(a.perm[wk.p0 + (row < wk.rows ? row : 0)] / a.topk) * K;
   }
   src.bsrow = a.xs + (size_t)(a.perm[wk.p0 + (l < wk.rows ? l : 0)] / a.topk) * (K / 32);
-  v4f acc[kPfQ][2];
-  zero_acc<kPfQ>(acc);
-  pf_kloop<false>(L, src, acc);
-  if (kPfQ * wr >= src.nrt) return;   // the missing half of a partial block
-  // epilogue: row tiles 8 wr + q, q = 2 s + {0, 1}: up / gate of intermediate
-  // columns 128 hb + 64 wr + 16 s .. +15; MXFP8 groups of two 16-column blocks
+  v4f acc[kPfQ][4];
+  zero_acc<kPfQ, 4>(acc);
+  pf_kloop<false>(L, src, wu, acc);
+  if (kPfQ * w >= src.nrt) return;   // the missing half of a partial block
+  // epilogue: row tiles 4w + 2s (up) and 4w + 2s + 1 (gate) = intermediate
+  // columns 128 hb + 32 w + 16 s .. +15; their 32 columns form one MXFP8 group
   const int hss = hs_stride(N);
+  const size_t c0 = (size_t)128 * hb + 32 * w;
 #pragma unroll
-  for (int cb = 0; cb < 2; cb++) {
-    const int row = 32 * wc + 16 * cb + c;
+  for (int cb = 0; cb < 4; cb++) {
+    const int row = 16 * cb + c;
+    float h[8];
 #pragma unroll
-    for (int pp = 0; pp < 2; pp++) {
-      float h[8];
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) h[s * 4 + i] = silu_clamped(acc[2 * s + 1][cb][i], acc[2 * s][cb][i], a.limit, a.has_limit);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(h[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    float inv;
+    const uint32_t sbyte = mx_scale(amax, &inv);
+    if (row < wk.rows) {
+      const size_t p = (size_t)(wk.p0 + row);
 #pragma unroll
       for (int s = 0; s < 2; s++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int q = 2 * (2 * pp + s);
-          h[s * 4 + i] = silu_clamped(acc[q + 1][cb][i], acc[q][cb][i], a.limit, a.has_limit);
-        }
-      float amax = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(h[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      float inv;
-      const uint32_t sbyte = mx_scale(amax, &inv);
-      if (row < wk.rows) {
-        const size_t p = (size_t)(wk.p0 + row);
-        const size_t c0 = (size_t)128 * hb + 64 * wr + 32 * pp;
-#pragma unroll
-        for (int s = 0; s < 2; s++)
-          *(uint32_t *)(a.hq + p * N + c0 + 16 * s + 4 * g) = e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
-        if (g == 0) a.hs[p * hss + c0 / 32] = (uint8_t)sbyte;
-      }
+        *(uint32_t *)(a.hq + p * N + c0 + 16 * s + 4 * g) = e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
+      if (g == 0) a.hs[p * hss + c0 / 32] = (uint8_t)sbyte;
     }
   }
 }
 
 // ---------------------------------------------------------------- GEMM2
-// Block: 16 row tiles of w2 = 256 output columns.
-__global__ __launch_bounds__(256) void k_pf_gemm2_a8(GemmArgs a) {
+// Block: 16 row tiles of w2 = 256 output columns; wave w: output columns
+// 256 ob + 64 w .. +63 of all 64 routes.
+__global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8(GemmArgs a) {
   __shared__ PfLds L;
   __shared__ int s_r[kPfTileRows];
   __shared__ float s_w[kPfTileRows];
   const int K = a.K, N = a.N;
   const PfWork wk = pf_work(a, K / 256, false);
   if (!wk.valid) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4, wr = w >> 1, wc = w & 1;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int ob = wk.sub;
   PfSrc src;
-  src.wstep = (size_t)16 * (N / 2);
-  src.sstep = (size_t)16 * (N / 32);
-  src.wbase = a.w2 + (size_t)wk.e * K * (N / 2) + (size_t)(kPfRT * ob) * src.wstep;
-  src.sbase = a.s2 + (size_t)wk.e * K * (N / 32) + (size_t)(kPfRT * ob) * src.sstep;
+  src.wstep = (uint32_t)(16 * (N / 2));
+  src.sstep = (uint32_t)(16 * (N / 32));
   src.nrt = kPfRT;
+  src.wb = make_buf(a.w2 + (size_t)wk.e * K * (N / 2) + (size_t)(kPfRT * ob) * src.wstep, kPfRT * src.wstep);
+  src.sb = make_buf(a.s2 + (size_t)wk.e * K * (N / 32) + (size_t)(kPfRT * ob) * src.sstep, kPfRT * src.sstep);
   src.kbytes = N;
 #pragma unroll
   for (int j = 0; j < 2; j++) {
@@ -391,11 +409,12 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a8(GemmArgs a) {
     s_r[tid] = r;
     s_w[tid] = a.topk_w[r];
   }
-  v4f acc[kPfQ][2];
-  zero_acc<kPfQ>(acc);
-  pf_kloop<true>(L, src, acc);
+  v4f acc[kPfQ][4];
+  zero_acc<kPfQ, 4>(acc);
+  pf_kloop<true>(L, src, wu, acc);
   __syncthreads();   // s_r / s_w visible
-  pf_combine<kPfQ, 2>(a, wk, acc, s_r, s_w, (size_t)256 * ob + 128 * wr + c, wc, c, g);
+  // acc[q][cb][i]: route 16 cb + 4 g + i, output column 256 ob + 64 w + 16 q + c
+  pf_combine<kPfQ, 4>(a, wk, acc, s_r, s_w, (size_t)256 * ob + 64 * w + c, 0, c, g);
 }
 
 static int pf_grid(int grid_tiles, int nsub) { return (grid_tiles * nsub + 7) / 8 * 8; }
