@@ -229,8 +229,12 @@ __device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, PfW (&ring)[
   int sb[4];
   pf_read_b(b, sb, L.st[kt % ST], l);
   if (active) {
+    // raised issue priority while this wave has MFMAs ready: the arbiter then
+    // feeds the matrix core from it while the SIMD's other wave waits on memory
+    __builtin_amdgcn_s_setprio(1);
     if ((kt + 1) * 128 <= src.kbytes) pf_mma<SWAP, true>(ring[R], b, sb, kt, src.kbytes, l, acc);
     else pf_mma<SWAP, false>(ring[R], b, sb, kt, src.kbytes, l, acc);
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
@@ -381,22 +385,24 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8(GemmArgs a) {
 // ---------------------------------------------------------------- GEMM2
 // Block: 16 row tiles of w2 = 256 output columns; wave w: output columns
 // 256 ob + 64 w .. +63 of all 64 routes.
-__global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8(GemmArgs a) {
-  __shared__ PfLds L;
-  __shared__ int s_r[kPfTileRows];
-  __shared__ float s_w[kPfTileRows];
-  const int K = a.K, N = a.N;
-  const PfWork wk = pf_work(a, K / 256, false);
-  if (!wk.valid) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int ob = wk.sub;
+struct PfG2 {
   PfSrc src;
+  PfWork wk;
+  int ob;
+};
+
+__device__ __forceinline__ bool pf_g2_setup(const GemmArgs &a, PfG2 &g2, int *s_r, float *s_w) {
+  const int K = a.K, N = a.N, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  g2.wk = pf_work(a, K / 256, false);
+  if (!g2.wk.valid) return false;
+  const PfWork &wk = g2.wk;
+  g2.ob = wk.sub;
+  PfSrc &src = g2.src;
   src.wstep = (uint32_t)(16 * (N / 2));
   src.sstep = (uint32_t)(16 * (N / 32));
   src.nrt = kPfRT;
-  src.wb = make_buf(a.w2 + (size_t)wk.e * K * (N / 2) + (size_t)(kPfRT * ob) * src.wstep, kPfRT * src.wstep);
-  src.sb = make_buf(a.s2 + (size_t)wk.e * K * (N / 32) + (size_t)(kPfRT * ob) * src.sstep, kPfRT * src.sstep);
+  src.wb = make_buf(a.w2 + (size_t)wk.e * K * (N / 2) + (size_t)(kPfRT * g2.ob) * src.wstep, kPfRT * src.wstep);
+  src.sb = make_buf(a.s2 + (size_t)wk.e * K * (N / 32) + (size_t)(kPfRT * g2.ob) * src.sstep, kPfRT * src.sstep);
   src.kbytes = N;
 #pragma unroll
   for (int j = 0; j < 2; j++) {
@@ -409,12 +415,75 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8(GemmArgs a) {
     s_r[tid] = r;
     s_w[tid] = a.topk_w[r];
   }
+  return true;
+}
+
+__global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8(GemmArgs a) {
+  __shared__ PfLds L;
+  __shared__ int s_r[kPfTileRows];
+  __shared__ float s_w[kPfTileRows];
+  PfG2 g2;
+  if (!pf_g2_setup(a, g2, s_r, s_w)) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   v4f acc[kPfQ][4];
   zero_acc<kPfQ, 4>(acc);
-  pf_kloop<true>(L, src, wu, acc);
+  pf_kloop<true>(L, g2.src, wu, acc);
   __syncthreads();   // s_r / s_w visible
   // acc[q][cb][i]: route 16 cb + 4 g + i, output column 256 ob + 64 w + 16 q + c
-  pf_combine<kPfQ, 4>(a, wk, acc, s_r, s_w, (size_t)256 * ob + 64 * w + c, 0, c, g);
+  pf_combine<kPfQ, 4>(a, g2.wk, acc, s_r, s_w, (size_t)256 * g2.ob + 64 * w + c, 0, c, g);
+}
+
+// The same for a short reduction (N <= 128 NKT): every k-tile's weights and
+// activations are requested up front (one memory round trip per block instead
+// of one per ring turn), then consumed in order as each stage lands.
+template <int NKT>
+struct PfShortLds {
+  PfStage st[NKT];
+};
+
+template <int NKT>
+__global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8_short(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) PfShortLds<NKT> L;
+  __shared__ int s_r[kPfTileRows];
+  __shared__ float s_w[kPfTileRows];
+  PfG2 g2;
+  if (!pf_g2_setup(a, g2, s_r, s_w)) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const PfSrc &src = g2.src;
+  PfW wt[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; kt++) {
+    pf_load_w(wt[kt], src, kt, wu, l);
+    pf_issue_b(L.st[kt], src, kt, wu, l);
+  }
+  v4f acc[kPfQ][4];
+  zero_acc<kPfQ, 4>(acc);
+#pragma unroll
+  for (int kt = 0; kt < NKT; kt++) {
+    // stage kt has landed once the kPfLoads loads of each later stage are all
+    // that may still be in flight (loads complete in order)
+    if constexpr (true) {
+      switch (NKT - 1 - kt) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<kPfLoads>(); break;
+        case 2: wait_vm<2 * kPfLoads>(); break;
+        case 3: wait_vm<3 * kPfLoads>(); break;
+        default: wait_vm<4 * kPfLoads>(); break;
+      }
+    }
+    __builtin_amdgcn_s_barrier();
+    v4i b[4][2];
+    int sb[4];
+    pf_read_b(b, sb, L.st[kt], l);
+    __builtin_amdgcn_s_setprio(1);
+    if ((kt + 1) * 128 <= src.kbytes) pf_mma<true, true>(wt[kt], b, sb, kt, src.kbytes, l, acc);
+    else pf_mma<true, false>(wt[kt], b, sb, kt, src.kbytes, l, acc);
+    __builtin_amdgcn_s_setprio(0);
+  }
+  __syncthreads();   // s_r / s_w visible
+  pf_combine<kPfQ, 4>(a, g2.wk, acc, s_r, s_w, (size_t)256 * g2.ob + 64 * w + c, 0, c, g);
 }
 
 static int pf_grid(int grid_tiles, int nsub) { return (grid_tiles * nsub + 7) / 8 * 8; }
@@ -427,7 +496,15 @@ hipError_t launch_pf_gemm1(const GemmArgs &a, int grid_tiles, hipStream_t s) {
 
 hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pf_gemm2_a8, dim3(pf_grid(grid_tiles, a.K / 256)), dim3(256), 0, s, a);
+  const dim3 grid(pf_grid(grid_tiles, a.K / 256)), block(256);
+  switch ((a.N + 127) / 128) {
+    case 1: hipLaunchKernelGGL(k_pf_gemm2_a8_short<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_pf_gemm2_a8_short<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(k_pf_gemm2_a8_short<3>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_pf_gemm2_a8_short<4>, grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL(k_pf_gemm2_a8_short<5>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(k_pf_gemm2_a8, grid, block, 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
@@ -622,8 +699,12 @@ __device__ __forceinline__ void pf16_step(Pf16Lds &L, const Pf16Src &src, Pf16W 
   }
   v4i b[4][4];
   pf16_read_b(b, L.st[kt % ST], l);
+  // raised issue priority around the MFMAs as for the W4A8 kernels (measured:
+  // faster for the up/gate GEMM, slower for the down GEMM's short k-loops)
+  if (!SWAP) __builtin_amdgcn_s_setprio(1);
   if ((kt + 1) * 128 <= src.kcols) pf16_mma<WF, SWAP, true>(ring[R], b, kt, src.kcols, l, acc);
   else pf16_mma<WF, SWAP, false>(ring[R], b, kt, src.kcols, l, acc);
+  if (!SWAP) __builtin_amdgcn_s_setprio(0);
 }
 
 // A k-loop of exactly NKT k-tiles (NKT <= 4), straight-line.
