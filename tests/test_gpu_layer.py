@@ -70,6 +70,18 @@ SMALL = {
     "hybrid_prefill_small": lambda: I.make_problem(I.Config("hybrid_prefill_small", T=140, E=12, K=512, N=128,
                                                             topk=3, limit=None, fmt=I.FMT_NVFP4, hybrid_nvfp4=4),
                                                    seed=15),
+    # k-loop shapes of the prefill kernels: W4A8 down GEMM with 3 k-tiles (the last
+    # half) requested up front; 6 k-tiles through the register/LDS ring with an
+    # up/gate GEMM of 8 k-tiles (two whole ring turns, then closing steps); W4A16
+    # down GEMMs with 3 k-tiles (straight-line) and 5 (ring)
+    "prefill_n320": lambda: I.make_problem(I.Config("prefill_n320", T=140, E=6, K=256, N=320, topk=2, limit=7.0,
+                                                    fmt=I.FMT_MXFP4, e8m0_exp=(-6, -2), zipf_s=1.1), seed=16),
+    "prefill_n768": lambda: I.make_problem(I.Config("prefill_n768", T=128, E=4, K=1024, N=768, topk=2, limit=7.0,
+                                                    fmt=I.FMT_MXFP4, e8m0_exp=(-7, -3)), seed=17),
+    "nvfp4_prefill_n320": lambda: I.make_problem(I.Config("nvfp4_prefill_n320", T=136, E=5, K=256, N=320, topk=2,
+                                                          limit=None, fmt=I.FMT_NVFP4), seed=18),
+    "nf3_prefill_n640": lambda: I.make_problem(I.Config("nf3_prefill_n640", T=130, E=4, K=768, N=640, topk=2,
+                                                        limit=None, fmt=I.FMT_NF3), seed=19),
 }
 
 
@@ -91,7 +103,8 @@ def _sample_rows(prob, n, seed=0):
 @pytest.mark.parametrize("name", ["tiny", "mxfp4_ragged", "nvfp4_small", "nf3_small", "hybrid_small",
                                   "nvfp4_clamped", "hybrid_decode", "decode_many_routes", "nf3_decode",
                                   "prefill_small", "prefill_narrow", "nvfp4_prefill_small", "nf3_prefill_small",
-                                  "hybrid_prefill_small"])
+                                  "hybrid_prefill_small", "prefill_n320", "prefill_n768", "nvfp4_prefill_n320",
+                                  "nf3_prefill_n640"])
 @pytest.mark.parametrize("deterministic", [False, True])
 def test_small_layers_all_rows(name, deterministic):
     L = layer(name)
