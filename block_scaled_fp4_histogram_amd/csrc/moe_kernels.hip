@@ -575,20 +575,31 @@ __global__ __launch_bounds__(256) void k_cast(const float *acc, long n8, uint16_
 }
 
 // out[t] = bf16(sum over valid slots j, in slot order, of rb[t*topk + j]); 8 columns per thread.
-__global__ __launch_bounds__(256) void k_topk_sum(const uint16_t *rb, const int32_t *inv, int T, int K, int topk,
+// All TK slot rows and their validity are requested before the first add (rows
+// of invalid slots are in the buffer's range, just never written, and are
+// masked), so each thread has one memory round trip instead of TK.
+template <int TK>
+__global__ __launch_bounds__(256) void k_topk_sum(const uint16_t *rb, const int32_t *inv, int T, int K,
                                                   uint16_t *out) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   const long per_row = K / 8;
   if (i >= (long)T * per_row) return;
   const long t = i / per_row, c8 = i % per_row;
+  uint4 v[TK];
+  int ok[TK];
+#pragma unroll
+  for (int j = 0; j < TK; j++) {
+    const long r = t * TK + j;
+    ok[j] = inv[r];
+    v[j] = *(const uint4 *)(rb + r * K + c8 * 8);
+  }
   float s[8];
 #pragma unroll
   for (int m = 0; m < 8; m++) s[m] = 0.f;
-  for (int j = 0; j < topk; j++) {
-    const long r = t * topk + j;
-    if (inv[r] < 0) continue;
-    const uint4 v = *(const uint4 *)(rb + r * K + c8 * 8);
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < TK; j++) {
+    if (ok[j] < 0) continue;
+    const uint32_t wv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
     for (int m = 0; m < 4; m++) {
       s[2 * m] += bf16_to_f32(wv[m] & 0xFFFFu);
@@ -603,13 +614,28 @@ __global__ __launch_bounds__(256) void k_topk_sum(const uint16_t *rb, const int3
   *(uint4 *)(out + t * K + c8 * 8) = o;
 }
 
+template <int TK>
+static void launch_topk_sum(dim3 grid, dim3 block, hipStream_t s, const uint16_t *rb, const int32_t *inv, int T, int K,
+                            uint16_t *out) {
+  hipLaunchKernelGGL(k_topk_sum<TK>, grid, block, 0, s, rb, inv, T, K, out);
+}
+
 hipError_t launch_finalize(int deterministic, const float *out_acc, const uint16_t *rb, const int32_t *inv, int T,
                            int K, int topk, uint16_t *out, hipStream_t s) {
   const long n8 = (long)T * K / 8;
   if (n8 == 0) return hipSuccess;
   const dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
-  if (deterministic) hipLaunchKernelGGL(k_topk_sum, grid, block, 0, s, rb, inv, T, K, topk, out);
-  else hipLaunchKernelGGL(k_cast, grid, block, 0, s, out_acc, n8, out);
+  if (deterministic) {
+    typedef void (*Fn)(dim3, dim3, hipStream_t, const uint16_t *, const int32_t *, int, int, uint16_t *);
+    static const Fn fns[16] = {launch_topk_sum<1>,  launch_topk_sum<2>,  launch_topk_sum<3>,  launch_topk_sum<4>,
+                               launch_topk_sum<5>,  launch_topk_sum<6>,  launch_topk_sum<7>,  launch_topk_sum<8>,
+                               launch_topk_sum<9>,  launch_topk_sum<10>, launch_topk_sum<11>, launch_topk_sum<12>,
+                               launch_topk_sum<13>, launch_topk_sum<14>, launch_topk_sum<15>, launch_topk_sum<16>};
+    if (topk < 1 || topk > 16) return hipErrorInvalidValue;
+    fns[topk - 1](grid, block, s, rb, inv, T, K, out);
+  } else {
+    hipLaunchKernelGGL(k_cast, grid, block, 0, s, out_acc, n8, out);
+  }
   return hipGetLastError();
 }
 
