@@ -210,21 +210,27 @@ __global__ __launch_bounds__(64 * kRouteWaves) void k_route(RouteArgs a) {
 }
 
 // Multi-chunk: per-expert scan over chunks, offsets, tile table.  One thread
-// per expert; the chunk counts are read 8 at a time so the loads overlap.
+// per expert; up to 32 chunk counts are read in one batch and kept in
+// registers for the second pass (more chunks take further batches).
 __global__ __launch_bounds__(1024) void k_route_scan(RouteArgs a) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int tbeg[kMaxExperts + 1];
   const int U = a.E0 + a.E1, u = threadIdx.x;
-  constexpr int B = 8;
+  constexpr int B = 32;
+  int v[B];
   if (u < U) {
+#pragma unroll
+    for (int j = 0; j < B; j++) v[j] = j < a.G ? a.chunk_hist[j * U + u] : 0;
     int run = 0;
-    for (int b0 = 0; b0 < a.G; b0 += B) {
-      int v[B];
 #pragma unroll
-      for (int j = 0; j < B; j++) v[j] = b0 + j < a.G ? a.chunk_hist[(b0 + j) * U + u] : 0;
+    for (int j = 0; j < B; j++) run += v[j];
+    for (int b0 = B; b0 < a.G; b0 += B) {
+      int x[B];
 #pragma unroll
-      for (int j = 0; j < B; j++) run += v[j];
+      for (int j = 0; j < B; j++) x[j] = b0 + j < a.G ? a.chunk_hist[(b0 + j) * U + u] : 0;
+#pragma unroll
+      for (int j = 0; j < B; j++) run += x[j];
     }
     cnt[u] = run;
   }
@@ -233,15 +239,21 @@ __global__ __launch_bounds__(1024) void k_route_scan(RouteArgs a) {
   __syncthreads();
   if (u < U) {
     int run = off[u];
-    for (int b0 = 0; b0 < a.G; b0 += B) {
-      int v[B];
 #pragma unroll
-      for (int j = 0; j < B; j++) v[j] = b0 + j < a.G ? a.chunk_hist[(b0 + j) * U + u] : 0;
+    for (int j = 0; j < B; j++)
+      if (j < a.G) {
+        a.chunk_hist[j * U + u] = run;
+        run += v[j];
+      }
+    for (int b0 = B; b0 < a.G; b0 += B) {
+      int x[B];
+#pragma unroll
+      for (int j = 0; j < B; j++) x[j] = b0 + j < a.G ? a.chunk_hist[(b0 + j) * U + u] : 0;
 #pragma unroll
       for (int j = 0; j < B; j++)
         if (b0 + j < a.G) {
           a.chunk_hist[(b0 + j) * U + u] = run;
-          run += v[j];
+          run += x[j];
         }
     }
   }
