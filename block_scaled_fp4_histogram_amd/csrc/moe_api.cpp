@@ -285,6 +285,38 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ga.rb = (uint16_t *)(scratch + L.rb);
   ga.deterministic = deterministic;
   const int row_tiles = (R + ra.tile_rows - 1) / ra.tile_rows;
+  // prefill with two W4A16 / W3A16 tiers: one launch per GEMM covers both tiers,
+  // so their weight streams share the machine instead of running back to back
+  const bool tiers_together = prefill && n_tiers == 2 && tiers[0].experts->wfmt != MOE_W_MXFP4 &&
+                              tiers[1].experts->wfmt != MOE_W_MXFP4;
+  if (tiers_together) {
+    const moe_experts_s *xa = tiers[0].experts, *xb = tiers[1].experts;
+    ga.tier = 0;
+    ga.u_base = 0;
+    ga.w13 = xa->w13;
+    ga.s13 = xa->s13;
+    ga.w2 = xa->w2;
+    ga.s2 = xa->s2;
+    ga.g13 = xa->g13;
+    ga.g2 = xa->g2;
+    ga.fmt_a = xa->wfmt;
+    ga.w13b = xb->w13;
+    ga.s13b = xb->s13;
+    ga.w2b = xb->w2;
+    ga.s2b = xb->s2;
+    ga.g13b = xb->g13;
+    ga.g2b = xb->g2;
+    ga.fmt_b = xb->wfmt;
+    ga.u_base_b = xa->E;
+    const int grid_tiles = row_tiles + std::min(xa->E + xb->E, R);
+    HIP_TRY(moe::launch_pf16_gemm1_tiers(ga, grid_tiles, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    HIP_TRY(moe::launch_pf16_gemm2_tiers(ga, grid_tiles, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+    HIP_TRY(moe::launch_finalize(deterministic, ga.out_acc, ga.rb, I32(L.inv), T, p->K, p->topk, out, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[4], s));
+    return MOE_OK;
+  }
   int u_base = 0;
   for (int i = 0; i < n_tiers; i++) {
     const moe_experts_s *xp = tiers[i].experts;

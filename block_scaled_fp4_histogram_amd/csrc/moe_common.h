@@ -75,6 +75,11 @@ struct GemmArgs {
   uint16_t *rb;                      // bf16 [R, K] route buffer (deterministic combine)
   int deterministic;
   int T;                             // tokens of the chunk (rows of x / the accumulator)
+  // both tiers in one launch (prefill W4A16 / W3A16): the fields above are tier 0,
+  // these tier 1, whose experts follow tier 0's in the unified index (u_base_b)
+  const uint8_t *w13b, *s13b, *w2b, *s2b;
+  const float *g13b, *g2b;
+  int fmt_a, fmt_b, u_base_b;
 };
 
 // Decode-size batches (T <= kDecodeMaxT tokens, T * top_k <= 64 routes): two
@@ -126,6 +131,8 @@ hipError_t launch_pf_gemm1(const GemmArgs &a, int grid_tiles, hipStream_t s);
 hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s);
 hipError_t launch_pf16_gemm1(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s);
 hipError_t launch_pf16_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s);
+hipError_t launch_pf16_gemm1_tiers(const GemmArgs &a, int grid_tiles, hipStream_t s);
+hipError_t launch_pf16_gemm2_tiers(const GemmArgs &a, int grid_tiles, hipStream_t s);
 hipError_t launch_finalize(int deterministic, const float *out_acc, const uint16_t *rb, const int32_t *inv,
                            int T, int K, int topk, uint16_t *out, hipStream_t s);
 hipError_t launch_quant_bf16(const uint16_t *x, long rows, int cols, uint8_t *q, uint8_t *sc, hipStream_t s);

@@ -763,21 +763,57 @@ __device__ __forceinline__ void pf16_kloop(Pf16Lds &L, const Pf16Src &src, int w
 }  // namespace
 
 // ---------------------------------------------------------------- GEMM1 (A16)
+// One tier's expert tensors.
+struct PfTier {
+  const uint8_t *w13, *s13, *w2, *s2;
+  const float *g13, *g2;
+};
+
+__device__ __forceinline__ PfTier pf_tier(const GemmArgs &a, int tier) {
+  PfTier t;
+  t.w13 = tier ? a.w13b : a.w13;
+  t.s13 = tier ? a.s13b : a.s13;
+  t.w2 = tier ? a.w2b : a.w2;
+  t.s2 = tier ? a.s2b : a.s2;
+  t.g13 = tier ? a.g13b : a.g13;
+  t.g2 = tier ? a.g2b : a.g2;
+  return t;
+}
+
+// Work item of a launch that covers both tiers: tier 0's items, then tier 1's,
+// each in its own order (as pf_work), all numbered XCD-major together.
+__device__ __forceinline__ PfWork pf_work_tiers(const GemmArgs &a, int nsub, bool sub_major, int *tier) {
+  PfWork w;
+  const int n0 = a.tier_tiles[1] - a.tier_tiles[0], n1 = a.tier_tiles[3] - a.tier_tiles[2];
+  const int items0 = n0 * nsub, items = items0 + n1 * nsub, per = (items + 7) >> 3;
+  const int b = blockIdx.x, slot = b >> 3, item = (b & 7) * per + slot;
+  w.valid = slot < per && item < items;
+  if (!w.valid) return w;
+  const int t1 = item >= items0 ? 1 : 0, local = t1 ? item - items0 : item, ntiles = t1 ? n1 : n0;
+  const int tbeg = a.tier_tiles[2 * t1];
+  const int t = sub_major ? local % ntiles : local / nsub;
+  w.sub = sub_major ? local / ntiles : local - t * nsub;
+  const int u = a.tile_u[tbeg + t];
+  w.e = u - (t1 ? a.u_base_b : 0);
+  w.p0 = a.off[u] + a.tile_row0[tbeg + t];
+  w.rows = min(a.tile_rows, a.off[u + 1] - w.p0);
+  *tier = t1;
+  return w;
+}
+
+// Block: w13 row tiles 8 hb .. +7 = up and gate of intermediate columns 64 hb .. +63.
 template <int WF>
-__global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
+__device__ __forceinline__ void pf16_gemm1_body(const GemmArgs &a, const PfWork &wk, const PfTier &T, Pf16Lds &L) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
-  __shared__ Pf16Lds L;
   const int K = a.K, N = a.N;
-  const PfWork wk = pf_work(a, N / 64, true);
-  if (!wk.valid) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int hb = wk.sub, groups = K / 32;
   Pf16Src src;
   src.wstep = (uint32_t)(16 * groups * U);
   src.sstep = (uint32_t)(16 * groups * SU);
-  src.wb = make_buf(a.w13 + (size_t)wk.e * (2 * N) * groups * U + (size_t)(8 * hb) * src.wstep, 8 * src.wstep);
-  src.sb = make_buf(a.s13 + (size_t)wk.e * (2 * N) * groups * SU + (size_t)(8 * hb) * src.sstep, 8 * src.sstep);
+  src.wb = make_buf(T.w13 + (size_t)wk.e * (2 * N) * groups * U + (size_t)(8 * hb) * src.wstep, 8 * src.wstep);
+  src.sb = make_buf(T.s13 + (size_t)wk.e * (2 * N) * groups * SU + (size_t)(8 * hb) * src.sstep, 8 * src.sstep);
   src.kcols = K;
   // rows past the tile read route p0's token; their results are never stored
 #pragma unroll
@@ -792,7 +828,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
     for (int cb = 0; cb < 4; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
   pf16_kloop<WF, false>(L, src, wu, acc);
   // epilogue: row tiles 2w (up) and 2w + 1 (gate) = intermediate columns 64 hb + 16 w .. +15
-  const float gs = a.g13 ? a.g13[wk.e] : 1.0f;
+  const float gs = T.g13 ? T.g13[wk.e] : 1.0f;
 #pragma unroll
   for (int cb = 0; cb < 4; cb++) {
     const int row = 16 * cb + c;
@@ -809,24 +845,40 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- GEMM2 (A16)
 template <int WF>
-__global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
-  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+__global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
   __shared__ Pf16Lds L;
-  __shared__ int s_r[kPfTileRows];
-  __shared__ float s_w[kPfTileRows];
-  const int K = a.K, N = a.N;
-  const PfWork wk = pf_work(a, K / 128, false);
+  const PfWork wk = pf_work(a, a.N / 64, true);
   if (!wk.valid) return;
+  pf16_gemm1_body<WF>(a, wk, pf_tier(a, 0), L);
+}
+
+// Both tiers in one launch: each block runs its tier's format.
+__global__ __launch_bounds__(256) void k_pf_gemm1_a16_tiers(GemmArgs a) {
+  __shared__ Pf16Lds L;
+  int tier = 0;
+  const PfWork wk = pf_work_tiers(a, a.N / 64, true, &tier);
+  if (!wk.valid) return;
+  const PfTier T = pf_tier(a, tier);
+  if ((tier ? a.fmt_b : a.fmt_a) == W_NVFP4) pf16_gemm1_body<W_NVFP4>(a, wk, T, L);
+  else pf16_gemm1_body<W_NF3>(a, wk, T, L);
+}
+
+// ---------------------------------------------------------------- GEMM2 (A16)
+// Block: w2 row tiles 8 ob .. +7 = output columns 128 ob .. +127.
+template <int WF>
+__device__ __forceinline__ void pf16_gemm2_body(const GemmArgs &a, const PfWork &wk, const PfTier &T, Pf16Lds &L,
+                                                int *s_r, float *s_w) {
+  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  const int K = a.K, N = a.N;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int ob = wk.sub, groups = N / 32;   // output columns 128 ob .. +127 = w2 row tiles 8 ob .. +7
+  const int ob = wk.sub, groups = N / 32;
   Pf16Src src;
   src.wstep = (uint32_t)(16 * groups * U);
   src.sstep = (uint32_t)(16 * groups * SU);
-  src.wb = make_buf(a.w2 + (size_t)wk.e * K * groups * U + (size_t)(8 * ob) * src.wstep, 8 * src.wstep);
-  src.sb = make_buf(a.s2 + (size_t)wk.e * K * groups * SU + (size_t)(8 * ob) * src.sstep, 8 * src.sstep);
+  src.wb = make_buf(T.w2 + (size_t)wk.e * K * groups * U + (size_t)(8 * ob) * src.wstep, 8 * src.wstep);
+  src.sb = make_buf(T.s2 + (size_t)wk.e * K * groups * SU + (size_t)(8 * ob) * src.sstep, 8 * src.sstep);
   src.kcols = N;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
@@ -836,7 +888,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
   if (tid < wk.rows) {
     const int r = a.perm[wk.p0 + tid];
     s_r[tid] = r;
-    s_w[tid] = a.topk_w[r] * (a.g2 ? a.g2[wk.e] : 1.0f);
+    s_w[tid] = a.topk_w[r] * (T.g2 ? T.g2[wk.e] : 1.0f);
   }
   v4f acc[2][4];
 #pragma unroll
@@ -847,6 +899,28 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
   __syncthreads();   // s_r / s_w visible
   // acc[q][cb][i]: route 16 cb + 4 g + i, output column 128 ob + 32 w + 16 q + c
   pf_combine<2, 4>(a, wk, acc, s_r, s_w, (size_t)128 * ob + 32 * w + c, 0, c, g);
+}
+
+template <int WF>
+__global__ __launch_bounds__(256) void k_pf_gemm2_a16(GemmArgs a) {
+  __shared__ Pf16Lds L;
+  __shared__ int s_r[kPfTileRows];
+  __shared__ float s_w[kPfTileRows];
+  const PfWork wk = pf_work(a, a.K / 128, false);
+  if (!wk.valid) return;
+  pf16_gemm2_body<WF>(a, wk, pf_tier(a, 0), L, s_r, s_w);
+}
+
+__global__ __launch_bounds__(256) void k_pf_gemm2_a16_tiers(GemmArgs a) {
+  __shared__ Pf16Lds L;
+  __shared__ int s_r[kPfTileRows];
+  __shared__ float s_w[kPfTileRows];
+  int tier = 0;
+  const PfWork wk = pf_work_tiers(a, a.K / 128, false, &tier);
+  if (!wk.valid) return;
+  const PfTier T = pf_tier(a, tier);
+  if ((tier ? a.fmt_b : a.fmt_a) == W_NVFP4) pf16_gemm2_body<W_NVFP4>(a, wk, T, L, s_r, s_w);
+  else pf16_gemm2_body<W_NF3>(a, wk, T, L, s_r, s_w);
 }
 
 template <int WF>
@@ -864,6 +938,19 @@ hipError_t launch_pf16_gemm1(int wfmt, const GemmArgs &a, int grid_tiles, hipStr
 hipError_t launch_pf16_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
   return wfmt == W_NVFP4 ? launch_pf_a16<W_NVFP4>(a, grid_tiles, s, true) : launch_pf_a16<W_NF3>(a, grid_tiles, s, true);
+}
+
+// grid_tiles: an upper bound on both tiers' tiles together.
+hipError_t launch_pf16_gemm1_tiers(const GemmArgs &a, int grid_tiles, hipStream_t s) {
+  if (grid_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pf_gemm1_a16_tiers, dim3(pf_grid(grid_tiles, a.N / 64)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf16_gemm2_tiers(const GemmArgs &a, int grid_tiles, hipStream_t s) {
+  if (grid_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pf_gemm2_a16_tiers, dim3(pf_grid(grid_tiles, a.K / 128)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace moe
