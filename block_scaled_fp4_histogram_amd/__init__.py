@@ -76,6 +76,10 @@ class Plan:
         cap = _lib.load().moe_plan_capacity(self.handle, T, C.byref(rows))
         return cap, rows.value
 
+    def set_router_weight_on_input(self, enable: bool = True):
+        """Apply each slot's router weight to GEMM1's input instead of the GEMM2 result (bf16 plans)."""
+        _check(_lib.load().moe_plan_set_router_weight_on_input(self.handle, int(bool(enable))))
+
     def enable_stage_timing(self, max_runs: int):
         """Record HIP events between the layer's stages for the next max_runs runs."""
         _check(_lib.load().moe_plan_enable_stage_timing(self.handle, max_runs))

@@ -52,6 +52,7 @@ struct moe_plan_s {
   float limit;
   int has_limit;
   int afmt, w13_layout, max_tokens;
+  int w_on_input = 0;     // router weight applied to GEMM1's input (W4A16 / W3A16 only)
   std::vector<int> caps;  // ascending; caps.back() == chunk
   // optional stage timing: kStageEvents events per recorded run
   std::vector<hipEvent_t> events;
@@ -177,6 +178,7 @@ int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const ui
   }
   da.limit = p->limit;
   da.has_limit = p->has_limit;
+  da.w_on_input = p->w_on_input;
   da.cpass = moe::decode_cpass(p->K, p->afmt == MOE_A_MXFP8);
   da.hq = scratch + L.hq;
   da.hs = scratch + L.hs;
@@ -280,6 +282,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ga.hb = (uint16_t *)(scratch + L.hb);
   ga.limit = p->limit;
   ga.has_limit = p->has_limit;
+  ga.w_on_input = p->w_on_input;
   ga.topk_w = wts;
   ga.out_acc = (float *)(scratch + L.acc);
   ga.rb = (uint16_t *)(scratch + L.rb);
@@ -453,6 +456,14 @@ void moe_plan_destroy(moe_plan_t plan) {
     plan->magic = 0;
     delete plan;
   }
+}
+
+int moe_plan_set_router_weight_on_input(moe_plan_t plan, int enable) {
+  if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
+  if (enable && plan->afmt != MOE_A_BF16)
+    return fail(MOE_EUNSUPPORTED, "router weight on the input needs bf16 activations (W4A16 / W3A16)");
+  plan->w_on_input = enable ? 1 : 0;
+  return MOE_OK;
 }
 
 int moe_plan_enable_stage_timing(moe_plan_t plan, int max_runs) {

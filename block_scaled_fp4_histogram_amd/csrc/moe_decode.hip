@@ -295,7 +295,9 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
     __syncthreads();
     if (w == 0) {
       float h[8];
-      dec_swiglu<NW>(red, l, X.g13, a.limit, a.has_limit, h);
+      // router weight on the input (W4A16 / W3A16): GEMM1 is linear, so it scales the accumulators
+      const float gs = X.g13 * ((!A8 && a.w_on_input && have) ? a.topk_w[nth_bit(md, p0 + c)] : 1.0f);
+      dec_swiglu<NW>(red, l, gs, a.limit, a.has_limit, h);
       if (A8) {
         float amax = 0.f;
 #pragma unroll
@@ -593,7 +595,7 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   const int ng = __builtin_amdgcn_readfirstlane(G->ng), NI = __builtin_amdgcn_readfirstlane(G->nitems);
   int gu = G->gu[l], istart = G->istart[l];
   uint32_t gm_lo = (uint32_t)G->gm[l], gm_hi = (uint32_t)(G->gm[l] >> 32);
-  float wv = tid < a.R ? a.topk_w[tid] : 0.f;
+  float wv = tid < a.R ? (a.w_on_input ? 1.0f : a.topk_w[tid]) : 0.f;   // weight on the input: 1 here
   float g2v = 1.0f;   // global scale of group l's expert
   if (l < ng) {
     const bool t1 = a.n_tiers > 1 && gu >= a.tier[0].E;

@@ -401,7 +401,7 @@ __device__ __forceinline__ void combine_store(const GemmArgs &a, const TileInfo 
                                               float gscale) {
   if (c >= ti.rows) return;
   const int r = a.perm[ti.p0 + c];
-  const float wgt = a.topk_w[r] * gscale;
+  const float wgt = (a.w_on_input ? 1.0f : a.topk_w[r]) * gscale;
   if (a.deterministic) {
     uint2 v;
     v.x = pack_bf16x2(wgt * acc[0], wgt * acc[1]);
@@ -492,9 +492,10 @@ __global__ __launch_bounds__(256) void k_gemm1_a16(GemmArgs a) {
     for (int i = 0; i < 4; i++) red[w][q * 4 + i][l] = acc[q][i];
   __syncthreads();
   if (w != 0) return;
-  const float gs = a.g13 ? a.g13[ti.e] : 1.0f;
   if (c < ti.rows) {
     const size_t p = (size_t)(ti.p0 + c);
+    // router weight on the input: GEMM1 is linear, so it scales the accumulators
+    const float gs = (a.g13 ? a.g13[ti.e] : 1.0f) * (a.w_on_input ? a.topk_w[a.perm[p]] : 1.0f);
 #pragma unroll
     for (int s = 0; s < 2; s++) {
       float h[4];

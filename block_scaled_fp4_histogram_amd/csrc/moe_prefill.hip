@@ -828,12 +828,14 @@ __device__ __forceinline__ void pf16_gemm1_body(const GemmArgs &a, const PfWork 
     for (int cb = 0; cb < 4; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
   pf16_kloop<WF, false>(L, src, wu, acc);
   // epilogue: row tiles 2w (up) and 2w + 1 (gate) = intermediate columns 64 hb + 16 w .. +15
-  const float gs = T.g13 ? T.g13[wk.e] : 1.0f;
+  const float g13 = T.g13 ? T.g13[wk.e] : 1.0f;
 #pragma unroll
   for (int cb = 0; cb < 4; cb++) {
     const int row = 16 * cb + c;
     if (row < wk.rows) {
       const size_t p = (size_t)(wk.p0 + row);
+      // router weight on the input: GEMM1 is linear, so it scales the accumulators
+      const float gs = g13 * (a.w_on_input ? a.topk_w[a.perm[p]] : 1.0f);
       float h[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) h[i] = silu_clamped(acc[1][cb][i] * gs, acc[0][cb][i] * gs, a.limit, a.has_limit);
@@ -888,7 +890,7 @@ __device__ __forceinline__ void pf16_gemm2_body(const GemmArgs &a, const PfWork 
   if (tid < wk.rows) {
     const int r = a.perm[wk.p0 + tid];
     s_r[tid] = r;
-    s_w[tid] = a.topk_w[r] * (T.g2 ? T.g2[wk.e] : 1.0f);
+    s_w[tid] = (a.w_on_input ? 1.0f : a.topk_w[r]) * (T.g2 ? T.g2[wk.e] : 1.0f);
   }
   v4f acc[2][4];
 #pragma unroll

@@ -147,6 +147,15 @@ const char *moe_last_error(void);
  * capacity's tile (0 on a bad plan).  Host only; used by tests and benches. */
 int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows);
 
+/* Apply each slot's router weight to that slot's copy of the token before
+ * GEMM1 instead of to its GEMM2 result (vLLM "fused_moe/b12x" page,
+ * process_weights_after_loading: apply_router_weight_on_input, W4A16 only):
+ *     out[t] += W2[e] . act(W13[e] . (w[t,j] x_t)).
+ * GEMM1 is linear, so the kernels scale its fp32 accumulators by w.  Only for
+ * plans with MOE_A_BF16 activations: MOE_EUNSUPPORTED otherwise.  enable = 0
+ * restores the default (weight on the GEMM2 result).  Host only. */
+int moe_plan_set_router_weight_on_input(moe_plan_t plan, int enable);
+
 /* ---- instrumentation ------------------------------------------------- */
 
 /* Stage timing for benchmarks: after this call, each moe_run under `plan`

@@ -333,12 +333,17 @@ static void orc_expert(const orc_tier *tier, int e, int K, int N, double limit, 
  * limit: NaN = no clamp.  gate_up = 1 when w13 is stacked [gate; up].
  * acc [nrows, K] and out [nrows, K] are written.  Returns 0, or -1 on bad args.
  */
-int orc_moe(int E_global, int K, int N, int topk, double limit, int gate_up, int n_tiers,
-            const orc_tier *tiers, const uint16_t *x, const int32_t *ids, const float *wts, long T,
-            const int32_t *rows, long nrows, double *acc, uint16_t *out) {
+int orc_moe_ex(int E_global, int K, int N, int topk, double limit, int gate_up, int n_tiers,
+               const orc_tier *tiers, const uint16_t *x, const int32_t *ids, const float *wts, long T,
+               const int32_t *rows, long nrows, double *acc, uint16_t *out, int weight_on_input) {
   long i;
-  int bad = 0;
+  int bad = 0, tt;
   if (K % 32 || N % 32 || topk < 1 || n_tiers < 1 || n_tiers > 8) return -1;
+  /* the router weight on the input exists for the 16-bit activation path only
+     (vLLM "fused_moe/b12x" page, process_weights_after_loading) */
+  if (weight_on_input)
+    for (tt = 0; tt < n_tiers; tt++)
+      if (tiers[tt].fmt == ORC_FMT_MXFP4) return -1;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
   for (i = 0; i < nrows; i++) {
     long t = rows ? rows[i] : i;
@@ -348,7 +353,8 @@ int orc_moe(int E_global, int K, int N, int topk, double limit, int gate_up, int
     double *a = acc + i * K;
     int j, c, have_a8 = 0, have_a16 = 0;
     double *xa8 = (double *)malloc(sizeof(double) * K);
-    if (!xh || !y || !rowbuf || !h || !xa8 || t < 0 || t >= T) {
+    double *xw = (double *)malloc(sizeof(double) * K);
+    if (!xh || !y || !rowbuf || !h || !xa8 || !xw || t < 0 || t >= T) {
       bad = 1;
     } else {
       uint8_t q[32], sc;
@@ -376,14 +382,28 @@ int orc_moe(int E_global, int K, int N, int topk, double limit, int gate_up, int
           }
           xin = xh;
         }
-        orc_expert(&tiers[tt], local, K, N, limit, gate_up, xin, y, rowbuf, h);
-        for (c = 0; c < K; c++) a[c] += (double)wts[t * topk + j] * y[c];
+        if (weight_on_input) {
+          /* the slot's copy of the token is scaled before GEMM1; its result enters with weight 1 */
+          for (c = 0; c < K; c++) xw[c] = (double)wts[t * topk + j] * xin[c];
+          orc_expert(&tiers[tt], local, K, N, limit, gate_up, xw, y, rowbuf, h);
+          for (c = 0; c < K; c++) a[c] += y[c];
+        } else {
+          orc_expert(&tiers[tt], local, K, N, limit, gate_up, xin, y, rowbuf, h);
+          for (c = 0; c < K; c++) a[c] += (double)wts[t * topk + j] * y[c];
+        }
       }
       for (c = 0; c < K; c++) out[i * K + c] = orc_bf16_from_double(a[c]);
     }
-    free(xh); free(y); free(rowbuf); free(h); free(xa8);
+    free(xh); free(y); free(rowbuf); free(h); free(xa8); free(xw);
   }
   return bad ? -1 : 0;
+}
+
+int orc_moe(int E_global, int K, int N, int topk, double limit, int gate_up, int n_tiers,
+            const orc_tier *tiers, const uint16_t *x, const int32_t *ids, const float *wts, long T,
+            const int32_t *rows, long nrows, double *acc, uint16_t *out) {
+  return orc_moe_ex(E_global, K, N, topk, limit, gate_up, n_tiers, tiers, x, ids, wts, T, rows, nrows, acc, out,
+                    0);
 }
 
 /* Threads an OpenMP build will use (1 without OpenMP). */

@@ -55,8 +55,9 @@ def _bf16(v):
     return np.array([O.bf16_to_float(O.bf16_from_float(float(a))) for a in v])
 
 
-def expert_mlp(fmt, wts, e, x_bf16_row, K, N, limit, gate_up=False):
-    """One token through one expert, float64, quantisation as the format demands."""
+def expert_mlp(fmt, wts, e, x_bf16_row, K, N, limit, gate_up=False, x_scale=1.0):
+    """One token through one expert, float64, quantisation as the format demands;
+    x_scale multiplies the (16-bit) input first."""
     g13 = 1.0 if wts.get("g13") is None else float(wts["g13"][e])
     g2 = 1.0 if wts.get("g2") is None else float(wts["g2"][e])
     W13 = dequant(fmt, wts["w13"][e], wts["s13"][e], g13)
@@ -64,6 +65,7 @@ def expert_mlp(fmt, wts, e, x_bf16_row, K, N, limit, gate_up=False):
     x = (x_bf16_row.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     if fmt == O.FMT_MXFP4:
         x = _mx_fake(x.astype(np.float32))
+    x = x * x_scale
     z = W13 @ x
     up, gate = (z[N:], z[:N]) if gate_up else (z[:N], z[N:])
     if limit is not None:
@@ -77,7 +79,7 @@ def expert_mlp(fmt, wts, e, x_bf16_row, K, N, limit, gate_up=False):
     return W2 @ h
 
 
-def moe(prob, gate_up=False):
+def moe(prob, gate_up=False, weight_on_input=False):
     c = prob.cfg
     T = prob.x.shape[0]
     acc = np.zeros((T, c.K))
@@ -89,7 +91,10 @@ def moe(prob, gate_up=False):
             for tier in prob.tiers:
                 e = gid if tier.emap is None else int(tier.emap[gid])
                 if 0 <= e < tier.E:
-                    y = expert_mlp(tier.fmt, tier.weights, e, prob.x[t], c.K, c.N, c.limit, gate_up)
-                    acc[t] += float(prob.wts[t, j]) * y
+                    w = float(prob.wts[t, j])
+                    if weight_on_input:
+                        acc[t] += expert_mlp(tier.fmt, tier.weights, e, prob.x[t], c.K, c.N, c.limit, gate_up, w)
+                    else:
+                        acc[t] += w * expert_mlp(tier.fmt, tier.weights, e, prob.x[t], c.K, c.N, c.limit, gate_up)
                     break
     return acc

@@ -102,3 +102,14 @@ def test_destroy_is_safe_on_null():
     L = _lib.load()
     L.moe_plan_destroy(None)
     L.moe_experts_destroy(None)
+
+
+def test_router_weight_on_input_needs_bf16_activations():
+    a8 = M.Plan(8, 256, 128, 2, 7.0, M.A_MXFP8, max_tokens=16)
+    with pytest.raises(RuntimeError) as e:
+        a8.set_router_weight_on_input(True)
+    assert "bf16" in str(e.value)
+    a8.set_router_weight_on_input(False)   # the default stays accepted
+    a16 = M.Plan(8, 256, 128, 2, None, M.A_BF16, max_tokens=16)
+    a16.set_router_weight_on_input(True)
+    a16.set_router_weight_on_input(False)

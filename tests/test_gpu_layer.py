@@ -221,3 +221,15 @@ def test_gate_up_layout_flag():
     out = L.run()
     acc, _ = O.moe_problem(prob, gate_up=True)
     assert_rows_match(out, acc, label="gate_up")
+
+
+# Router weight on the input (W4A16 / W3A16 only), on every launch sequence: the general
+# 16-route kernels, decode, prefill, and both hybrid tiers in one prefill launch.
+@pytest.mark.parametrize("name", ["nvfp4_small", "nf3_small", "hybrid_decode", "nvfp4_prefill_small",
+                                  "hybrid_prefill_small"])
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_router_weight_on_input(name, deterministic):
+    L = layer(name, weight_on_input=True)
+    out = L.run(deterministic=deterministic)
+    acc, _ = O.moe_problem(L.prob, weight_on_input=True)
+    assert_rows_match(out, acc, label=f"{name} weight-on-input det={deterministic}")

@@ -177,3 +177,39 @@ def test_quantised_layer_envelope_vs_unquantised():
             ref += float(p.wts[r, j]) * (W2 @ (gate / (1 + np.exp(-gate)) * up))
         rel.append(np.linalg.norm(acc[r] - ref) / np.linalg.norm(ref))
     assert 0.005 < np.mean(rel) < 0.10, rel
+
+
+# Router weight on the input (vLLM "fused_moe/b12x" page, apply_router_weight_on_input,
+# 16-bit activation formats only): out[t] = sum_j W2 act(W13 (w_j x_t)).
+@pytest.mark.parametrize("name", ["nvfp4", "nf3", "hybrid"])
+def test_weight_on_input_matches_float64_bruteforce(name):
+    p = CASES[name]()
+    acc, _ = O.moe_problem(p, weight_on_input=True)
+    ref = BF.moe(p, weight_on_input=True)
+    assert np.allclose(acc, ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+    assert not np.allclose(acc, O.moe_problem(p)[0])   # the activation is not linear: it matters where w goes
+
+
+def test_weight_on_input_is_per_slot_scaled_input():
+    """With power-of-two router weights the scaled bf16 input is exact, so the layer equals
+    the sum over slots of one-slot layers with weight 1 run on w_j * x."""
+    p = CASES["nf3"]()
+    T, k = p.ids.shape
+    rng = np.random.default_rng(7)
+    p.wts[:] = 2.0 ** rng.integers(-3, 3, size=(T, k))
+    acc, _ = O.moe_problem(p, weight_on_input=True)
+    xf = (p.x.astype(np.uint32) << 16).view(np.float32)
+    total = np.zeros_like(acc)
+    for j in range(k):
+        xj = (xf * p.wts[:, j:j + 1]).astype(np.float32)
+        xb = (xj.view(np.uint32) >> 16).astype(np.uint16)   # exact: power-of-two scaling of bf16 values
+        assert np.array_equal((xb.astype(np.uint32) << 16).view(np.float32), xj)
+        q = I.Problem(dataclasses.replace(p.cfg, topk=1), xb, p.ids[:, j:j + 1].copy(),
+                      np.ones((T, 1), np.float32), p.tiers)
+        total += O.moe_problem(q)[0]
+    assert np.allclose(acc, total, rtol=1e-12, atol=1e-12 * np.abs(total).max())
+
+
+def test_weight_on_input_refused_for_mxfp8_activations():
+    with pytest.raises(ValueError):
+        O.moe_problem(CASES["mxfp4_k3"](), weight_on_input=True)
