@@ -76,6 +76,10 @@ class Plan:
         cap = _lib.load().moe_plan_capacity(self.handle, T, C.byref(rows))
         return cap, rows.value
 
+    def set_swiglu_oai(self, alpha: float, beta: float):
+        """Activation gate * sigmoid(alpha gate) * (up + beta) after the clamps (bf16 plans; 1, 0 = plain)."""
+        _check(_lib.load().moe_plan_set_swiglu_oai(self.handle, float(alpha), float(beta)))
+
     def set_router_weight_on_input(self, enable: bool = True):
         """Apply each slot's router weight to GEMM1's input instead of the GEMM2 result (bf16 plans)."""
         _check(_lib.load().moe_plan_set_router_weight_on_input(self.handle, int(bool(enable))))

@@ -25,6 +25,7 @@ SIGNATURES = {
     "moe_last_error": (C.c_char_p, []),
     "moe_plan_capacity": (_i, [_vp, _i, C.POINTER(_i)]),
     "moe_plan_set_router_weight_on_input": (_i, [_vp, _i]),
+    "moe_plan_set_swiglu_oai": (_i, [_vp, C.c_float, C.c_float]),
     "moe_plan_enable_stage_timing": (_i, [_vp, _i]),
     "moe_plan_stage_times": (_i, [_vp, C.POINTER(_f), _i, C.POINTER(_i)]),
     "moe_debug_route": (_i, [_vp, _vp, _i, _vp, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp]),

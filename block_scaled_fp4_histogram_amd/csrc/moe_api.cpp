@@ -53,6 +53,7 @@ struct moe_plan_s {
   int has_limit;
   int afmt, w13_layout, max_tokens;
   int w_on_input = 0;     // router weight applied to GEMM1's input (W4A16 / W3A16 only)
+  float alpha = 1.f, beta = 0.f;   // SwiGLU form gate * sigmoid(alpha gate) * (up + beta)
   std::vector<int> caps;  // ascending; caps.back() == chunk
   // optional stage timing: kStageEvents events per recorded run
   std::vector<hipEvent_t> events;
@@ -179,6 +180,8 @@ int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const ui
   da.limit = p->limit;
   da.has_limit = p->has_limit;
   da.w_on_input = p->w_on_input;
+  da.alpha = p->alpha;
+  da.beta = p->beta;
   da.cpass = moe::decode_cpass(p->K, p->afmt == MOE_A_MXFP8);
   da.hq = scratch + L.hq;
   da.hs = scratch + L.hs;
@@ -283,6 +286,8 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ga.limit = p->limit;
   ga.has_limit = p->has_limit;
   ga.w_on_input = p->w_on_input;
+  ga.alpha = p->alpha;
+  ga.beta = p->beta;
   ga.topk_w = wts;
   ga.out_acc = (float *)(scratch + L.acc);
   ga.rb = (uint16_t *)(scratch + L.rb);
@@ -463,6 +468,17 @@ int moe_plan_set_router_weight_on_input(moe_plan_t plan, int enable) {
   if (enable && plan->afmt != MOE_A_BF16)
     return fail(MOE_EUNSUPPORTED, "router weight on the input needs bf16 activations (W4A16 / W3A16)");
   plan->w_on_input = enable ? 1 : 0;
+  return MOE_OK;
+}
+
+int moe_plan_set_swiglu_oai(moe_plan_t plan, float alpha, float beta) {
+  if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
+  if (!std::isfinite(alpha) || !std::isfinite(beta)) return fail(MOE_EINVAL, "alpha and beta must be finite");
+  const bool plain = alpha == 1.f && beta == 0.f;
+  if (!plain && plan->afmt != MOE_A_BF16)
+    return fail(MOE_EUNSUPPORTED, "the alpha/beta SwiGLU form needs bf16 activations (W4A16 / W3A16)");
+  plan->alpha = alpha;
+  plan->beta = beta;
   return MOE_OK;
 }
 

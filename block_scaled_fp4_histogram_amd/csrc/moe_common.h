@@ -76,6 +76,7 @@ struct GemmArgs {
   int deterministic;
   int T;                             // tokens of the chunk (rows of x / the accumulator)
   int w_on_input;                    // router weight scales GEMM1 (W4A16 / W3A16), not the GEMM2 result
+  float alpha, beta;                 // SwiGLU form: gate * sigmoid(alpha gate) * (up + beta)
   // both tiers in one launch (prefill W4A16 / W3A16): the fields above are tier 0,
   // these tier 1, whose experts follow tier 0's in the unified index (u_base_b)
   const uint8_t *w13b, *s13b, *w2b, *s2b;
@@ -119,6 +120,7 @@ struct DecArgs {
   uint16_t *out;                     // bf16 [T, K]
   DecGroups *groups;                 // scratch
   int w_on_input;                    // router weight scales GEMM1 (W4A16 / W3A16), not the GEMM2 result
+  float alpha, beta;                 // SwiGLU form: gate * sigmoid(alpha gate) * (up + beta)
 };
 
 int decode_cpass(int K, int a8);

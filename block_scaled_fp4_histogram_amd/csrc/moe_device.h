@@ -42,12 +42,14 @@ __device__ __forceinline__ float e4m3_f32(uint32_t b) {
   return (b & 0x80u) ? -v : v;
 }
 
-__device__ __forceinline__ float silu_clamped(float gate, float up, float limit, int has_limit) {
+__device__ __forceinline__ float silu_clamped(float gate, float up, float limit, int has_limit, float alpha,
+                                              float beta) {
   if (has_limit) {
     gate = fminf(gate, limit);
     up = fminf(fmaxf(up, -limit), limit);
   }
-  return gate / (1.0f + __expf(-gate)) * up;
+  // alpha = 1, beta = 0: silu(gate) * up; otherwise the OAI form gate * sigmoid(alpha gate) * (up + beta)
+  return gate / (1.0f + __expf(-alpha * gate)) * (up + beta);
 }
 
 // Two fp32 -> two E4M3 (fn) codes (bits 0-7, 8-15), nearest with ties to even,

@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void k_gemm1_a8(GemmArgs a) {
       const int iu = (2 * s) * 4 + i, ig = (2 * s + 1) * 4 + i;
       const float up = red[0][iu][l] + red[1][iu][l] + red[2][iu][l] + red[3][iu][l];
       const float gate = red[0][ig][l] + red[1][ig][l] + red[2][ig][l] + red[3][ig][l];
-      h[s * 4 + i] = silu_clamped(gate, up, a.limit, a.has_limit);
+      h[s * 4 + i] = silu_clamped(gate, up, a.limit, a.has_limit, a.alpha, a.beta);
     }
   // MXFP8 block of 32 intermediate columns of route c: 8 values here x 4 lanes
   float amax = 0.f;
@@ -504,7 +504,7 @@ __global__ __launch_bounds__(256) void k_gemm1_a16(GemmArgs a) {
         const int iu = (2 * s) * 4 + i, ig = (2 * s + 1) * 4 + i;
         const float up = (red[0][iu][l] + red[1][iu][l] + red[2][iu][l] + red[3][iu][l]) * gs;
         const float gate = (red[0][ig][l] + red[1][ig][l] + red[2][ig][l] + red[3][ig][l]) * gs;
-        h[i] = silu_clamped(gate, up, a.limit, a.has_limit);
+        h[i] = silu_clamped(gate, up, a.limit, a.has_limit, a.alpha, a.beta);
       }
       uint2 v;
       v.x = pack_bf16x2(h[0], h[1]);

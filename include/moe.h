@@ -156,6 +156,14 @@ int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows);
  * restores the default (weight on the GEMM2 result).  Host only. */
 int moe_plan_set_router_weight_on_input(moe_plan_t plan, int enable);
 
+/* The SwiGLU-OAI activation form (vLLM "fused_moe/b12x" page, _swiglu_params:
+ * a limit plus alpha and beta for swigluoai): after the limit clamps,
+ *     h = gate * sigmoid(alpha * gate) * (up + beta).
+ * alpha = 1, beta = 0 (the default) is the plain clamped SwiGLU.  Other values
+ * only for MOE_A_BF16 plans (the page refuses this activation with W4A8):
+ * MOE_EUNSUPPORTED otherwise; non-finite values: MOE_EINVAL.  Host only. */
+int moe_plan_set_swiglu_oai(moe_plan_t plan, float alpha, float beta);
+
 /* ---- instrumentation ------------------------------------------------- */
 
 /* Stage timing for benchmarks: after this call, each moe_run under `plan`

@@ -61,7 +61,7 @@ def lib():
                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_long, C.c_void_p, C.c_long,
                               C.c_void_p, C.c_void_p]
         L.orc_moe_ex.restype = C.c_int
-        L.orc_moe_ex.argtypes = L.orc_moe.argtypes + [C.c_int]
+        L.orc_moe_ex.argtypes = L.orc_moe.argtypes + [C.c_int, C.c_double, C.c_double]
         L.orc_num_threads.restype = C.c_int
         _lib = L
     return _lib
@@ -177,11 +177,15 @@ def route(ids: np.ndarray, E_global: int, tiers):
 
 
 def moe(E_global: int, K: int, N: int, topk: int, limit, tiers, x: np.ndarray, ids: np.ndarray,
-        wts: np.ndarray, rows=None, gate_up: bool = False, weight_on_input: bool = False):
+        wts: np.ndarray, rows=None, gate_up: bool = False, weight_on_input: bool = False,
+        alpha: float = 1.0, beta: float = 0.0):
     """The layer for the listed token rows (all rows when None).  weight_on_input:
     each slot's router weight scales that slot's copy of the token before GEMM1 and
     its result enters the sum with weight 1 (vLLM "fused_moe/b12x" page,
-    apply_router_weight_on_input; 16-bit activation formats only).
+    apply_router_weight_on_input; 16-bit activation formats only).  alpha, beta:
+    the activation gate * sigmoid(alpha gate) * (up + beta) after the clamps
+    (swigluoai's parameters on the same page, _swiglu_params; 1, 0 is SwiGLU;
+    other values 16-bit activation formats only).
 
     Returns (acc float64 [n, K], out bf16-bits uint16 [n, K])."""
     x = _c(x, np.uint16)
@@ -195,17 +199,19 @@ def moe(E_global: int, K: int, N: int, topk: int, limit, tiers, x: np.ndarray, i
     ta = _TierArgs(tiers)
     lim = math.nan if limit is None else float(limit)
     rc = lib().orc_moe_ex(E_global, K, N, topk, lim, int(gate_up), len(tiers), C.addressof(ta.arr), _p(x),
-                          _p(ids), _p(wts), T, _p(rows_a), n, _p(acc), _p(out), int(bool(weight_on_input)))
+                          _p(ids), _p(wts), T, _p(rows_a), n, _p(acc), _p(out), int(bool(weight_on_input)),
+                          float(alpha), float(beta))
     if rc != 0:
         raise ValueError("bad layer arguments")
     return acc, out
 
 
-def moe_problem(prob, rows=None, gate_up: bool = False, weight_on_input: bool = False):
+def moe_problem(prob, rows=None, gate_up: bool = False, weight_on_input: bool = False, alpha: float = 1.0,
+                beta: float = 0.0):
     """The layer for a block_scaled_fp4_histogram_amd.inputs.Problem."""
     c = prob.cfg
     return moe(c.E, c.K, c.N, c.topk, c.limit, prob.tiers, prob.x, prob.ids, prob.wts, rows, gate_up,
-               weight_on_input)
+               weight_on_input, alpha, beta)
 
 
 def num_threads() -> int:

@@ -27,6 +27,11 @@
  *    moe_b12x_next.py, module docstring (_DIRECT_IDS).
  *  - SwiGLU limit: B12xExperts._swiglu_params (the clamp's form is not printed;
  *    this file takes gate <- min(gate, L), up <- clamp(up, -L, L)).
+ *  - SwiGLU-OAI alpha and beta: the same method returns them for the
+ *    swigluoai activation only, and _supports_activation / the W4A8 check
+ *    refuse that activation with quantised activations.  The activation's
+ *    formula is not printed; this file takes gate * sigmoid(alpha gate) *
+ *    (up + beta) after the clamps (alpha = 1, beta = 0 is the plain SwiGLU).
  *  - MXFP8 activations (E4M3 codes + E8M0 scale per 32): moe_b12x_next.py,
  *    module docstring ("in-kernel MXFP8 activations"); the scale rule is the
  *    OCP MX one, E = floor(log2 amax) - emax(E4M3 = 8), codes saturate.
@@ -273,8 +278,8 @@ long orc_route(const int32_t *ids, long T, int topk, int E_global, int n_tiers, 
 /* ---------------------------------------------------------------- layer */
 
 /* One routed token through its expert: returns y[K] (double) for activation xh[K]. */
-static void orc_expert(const orc_tier *tier, int e, int K, int N, double limit, int gate_up,
-                       const double *xh, double *y, double *rowbuf, double *h) {
+static void orc_expert(const orc_tier *tier, int e, int K, int N, double limit, double alpha, double beta,
+                       int gate_up, const double *xh, double *y, double *rowbuf, double *h) {
   int n, c, k;
   int a8 = tier->fmt == ORC_FMT_MXFP4;
   double g13 = tier->g13 ? (double)tier->g13[e] : 1.0, g2 = tier->g2 ? (double)tier->g2[e] : 1.0;
@@ -289,7 +294,7 @@ static void orc_expert(const orc_tier *tier, int e, int K, int N, double limit, 
   float hf[32];
   uint8_t q[32], sc;
 
-  /* GEMM1 + activation: h[n] = silu(gate_n) * up_n */
+  /* GEMM1 + activation: h[n] = gate_n sigmoid(alpha gate_n) (up_n + beta) */
   for (n = 0; n < N; n++) {
     double up = 0.0, gate = 0.0;
     int up_row = gate_up ? N + n : n, gate_row = gate_up ? n : N + n;
@@ -302,7 +307,7 @@ static void orc_expert(const orc_tier *tier, int e, int K, int N, double limit, 
       if (up > limit) up = limit;
       if (up < -limit) up = -limit;
     }
-    h[n] = gate / (1.0 + exp(-gate)) * up;
+    h[n] = gate / (1.0 + exp(-alpha * gate)) * (up + beta);
   }
   /* requantiser between the GEMMs: MXFP8 on fp32 h (A8), bf16 (A16) */
   if (a8) {
@@ -330,18 +335,21 @@ static void orc_expert(const orc_tier *tier, int e, int K, int N, double limit, 
  * in slot order, then out = bf16(acc).  A row with no valid slot is exactly 0.
  * Activation path follows the weight format: MXFP4 quantises x and h to MXFP8
  * (W4A8); NVFP4 and NF3 keep x in bf16 and round h to bf16 (W4A16 / W3A16).
- * limit: NaN = no clamp.  gate_up = 1 when w13 is stacked [gate; up].
+ * limit: NaN = no clamp.  alpha, beta: the activation's form (1, 0 = SwiGLU;
+ * other values 16-bit activation formats only).  gate_up = 1 when w13 is
+ * stacked [gate; up].
  * acc [nrows, K] and out [nrows, K] are written.  Returns 0, or -1 on bad args.
  */
 int orc_moe_ex(int E_global, int K, int N, int topk, double limit, int gate_up, int n_tiers,
                const orc_tier *tiers, const uint16_t *x, const int32_t *ids, const float *wts, long T,
-               const int32_t *rows, long nrows, double *acc, uint16_t *out, int weight_on_input) {
+               const int32_t *rows, long nrows, double *acc, uint16_t *out, int weight_on_input, double alpha,
+               double beta) {
   long i;
   int bad = 0, tt;
   if (K % 32 || N % 32 || topk < 1 || n_tiers < 1 || n_tiers > 8) return -1;
   /* the router weight on the input exists for the 16-bit activation path only
      (vLLM "fused_moe/b12x" page, process_weights_after_loading) */
-  if (weight_on_input)
+  if (weight_on_input || alpha != 1.0 || beta != 0.0)
     for (tt = 0; tt < n_tiers; tt++)
       if (tiers[tt].fmt == ORC_FMT_MXFP4) return -1;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
@@ -385,10 +393,10 @@ int orc_moe_ex(int E_global, int K, int N, int topk, double limit, int gate_up, 
         if (weight_on_input) {
           /* the slot's copy of the token is scaled before GEMM1; its result enters with weight 1 */
           for (c = 0; c < K; c++) xw[c] = (double)wts[t * topk + j] * xin[c];
-          orc_expert(&tiers[tt], local, K, N, limit, gate_up, xw, y, rowbuf, h);
+          orc_expert(&tiers[tt], local, K, N, limit, alpha, beta, gate_up, xw, y, rowbuf, h);
           for (c = 0; c < K; c++) a[c] += y[c];
         } else {
-          orc_expert(&tiers[tt], local, K, N, limit, gate_up, xin, y, rowbuf, h);
+          orc_expert(&tiers[tt], local, K, N, limit, alpha, beta, gate_up, xin, y, rowbuf, h);
           for (c = 0; c < K; c++) a[c] += (double)wts[t * topk + j] * y[c];
         }
       }
@@ -403,7 +411,7 @@ int orc_moe(int E_global, int K, int N, int topk, double limit, int gate_up, int
             const orc_tier *tiers, const uint16_t *x, const int32_t *ids, const float *wts, long T,
             const int32_t *rows, long nrows, double *acc, uint16_t *out) {
   return orc_moe_ex(E_global, K, N, topk, limit, gate_up, n_tiers, tiers, x, ids, wts, T, rows, nrows, acc, out,
-                    0);
+                    0, 1.0, 0.0);
 }
 
 /* Threads an OpenMP build will use (1 without OpenMP). */

@@ -55,9 +55,14 @@ def _bf16(v):
     return np.array([O.bf16_to_float(O.bf16_from_float(float(a))) for a in v])
 
 
-def expert_mlp(fmt, wts, e, x_bf16_row, K, N, limit, gate_up=False, x_scale=1.0):
+def silu_mul(gate, up):
+    return gate / (1.0 + np.exp(-gate)) * up
+
+
+def expert_mlp(fmt, wts, e, x_bf16_row, K, N, limit, gate_up=False, x_scale=1.0, act=silu_mul):
     """One token through one expert, float64, quantisation as the format demands;
-    x_scale multiplies the (16-bit) input first."""
+    x_scale multiplies the (16-bit) input first; act(gate, up) is the activation
+    applied after the clamps."""
     g13 = 1.0 if wts.get("g13") is None else float(wts["g13"][e])
     g2 = 1.0 if wts.get("g2") is None else float(wts["g2"][e])
     W13 = dequant(fmt, wts["w13"][e], wts["s13"][e], g13)
@@ -71,7 +76,7 @@ def expert_mlp(fmt, wts, e, x_bf16_row, K, N, limit, gate_up=False, x_scale=1.0)
     if limit is not None:
         gate = np.minimum(gate, limit)
         up = np.clip(up, -limit, limit)
-    h = gate / (1.0 + np.exp(-gate)) * up
+    h = act(gate, up)
     if fmt == O.FMT_MXFP4:
         h = np.concatenate([_mx_fake(h[i:i + 32].astype(np.float32)) for i in range(0, N, 32)])
     else:
@@ -79,7 +84,7 @@ def expert_mlp(fmt, wts, e, x_bf16_row, K, N, limit, gate_up=False, x_scale=1.0)
     return W2 @ h
 
 
-def moe(prob, gate_up=False, weight_on_input=False):
+def moe(prob, gate_up=False, weight_on_input=False, act=silu_mul):
     c = prob.cfg
     T = prob.x.shape[0]
     acc = np.zeros((T, c.K))
@@ -93,8 +98,10 @@ def moe(prob, gate_up=False, weight_on_input=False):
                 if 0 <= e < tier.E:
                     w = float(prob.wts[t, j])
                     if weight_on_input:
-                        acc[t] += expert_mlp(tier.fmt, tier.weights, e, prob.x[t], c.K, c.N, c.limit, gate_up, w)
+                        acc[t] += expert_mlp(tier.fmt, tier.weights, e, prob.x[t], c.K, c.N, c.limit, gate_up, w,
+                                             act)
                     else:
-                        acc[t] += w * expert_mlp(tier.fmt, tier.weights, e, prob.x[t], c.K, c.N, c.limit, gate_up)
+                        acc[t] += w * expert_mlp(tier.fmt, tier.weights, e, prob.x[t], c.K, c.N, c.limit, gate_up,
+                                                 1.0, act)
                     break
     return acc

@@ -23,13 +23,15 @@ def dev(a, dtype=None):
 class DeviceLayer:
     """Plan + prepared experts of a Problem, on cuda:0."""
 
-    def __init__(self, prob, max_tokens=None, gate_up=False, weight_on_input=False):
+    def __init__(self, prob, max_tokens=None, gate_up=False, weight_on_input=False, swiglu_oai=None):
         c = prob.cfg
         self.prob = prob
         self.plan = M.Plan(c.E, c.K, c.N, c.topk, c.limit, A_OF[prob.tiers[0].fmt],
                            M.W13_GATE_UP if gate_up else M.W13_UP_GATE, max_tokens or max(c.T, 1))
         if weight_on_input:
             self.plan.set_router_weight_on_input(True)
+        if swiglu_oai is not None:
+            self.plan.set_swiglu_oai(*swiglu_oai)
         self.tiers = []
         self.keep = []
         for t in prob.tiers:

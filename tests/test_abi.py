@@ -113,3 +113,17 @@ def test_router_weight_on_input_needs_bf16_activations():
     a16 = M.Plan(8, 256, 128, 2, None, M.A_BF16, max_tokens=16)
     a16.set_router_weight_on_input(True)
     a16.set_router_weight_on_input(False)
+
+
+def test_swiglu_oai_needs_bf16_activations():
+    a8 = M.Plan(8, 256, 128, 2, 7.0, M.A_MXFP8, max_tokens=16)
+    with pytest.raises(RuntimeError) as e:
+        a8.set_swiglu_oai(1.702, 1.0)
+    assert "bf16" in str(e.value)
+    a8.set_swiglu_oai(1.0, 0.0)   # the plain form stays accepted
+    a16 = M.Plan(8, 256, 128, 2, 7.0, M.A_BF16, max_tokens=16)
+    a16.set_swiglu_oai(1.702, 1.0)
+    with pytest.raises(RuntimeError):
+        a16.set_swiglu_oai(float("nan"), 1.0)
+    with pytest.raises(RuntimeError):
+        a16.set_swiglu_oai(1.0, float("inf"))

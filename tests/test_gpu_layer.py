@@ -233,3 +233,19 @@ def test_router_weight_on_input(name, deterministic):
     out = L.run(deterministic=deterministic)
     acc, _ = O.moe_problem(L.prob, weight_on_input=True)
     assert_rows_match(out, acc, label=f"{name} weight-on-input det={deterministic}")
+
+
+# SwiGLU-OAI activation gate * sigmoid(alpha gate) * (up + beta) (W4A16 / W3A16 only), on
+# every launch sequence, with and without the clamp.
+@pytest.mark.parametrize("name", ["nvfp4_small", "nf3_small", "nvfp4_clamped", "hybrid_decode",
+                                  "nvfp4_prefill_small", "hybrid_prefill_small"])
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_swiglu_oai(name, deterministic):
+    alpha, beta = 1.702, 1.0
+    L = layer(name, swiglu_oai=(alpha, beta))
+    out = L.run(deterministic=deterministic)
+    acc, _ = O.moe_problem(L.prob, alpha=alpha, beta=beta)
+    assert_rows_match(out, acc, label=f"{name} swiglu-oai det={deterministic}")
+    plain, _ = O.moe_problem(L.prob)
+    assert not np.allclose(acc, plain, rtol=1e-2), "the parameters must change this case"
+

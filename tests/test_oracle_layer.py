@@ -213,3 +213,48 @@ def test_weight_on_input_is_per_slot_scaled_input():
 def test_weight_on_input_refused_for_mxfp8_activations():
     with pytest.raises(ValueError):
         O.moe_problem(CASES["mxfp4_k3"](), weight_on_input=True)
+
+
+# SwiGLU-OAI (vLLM "fused_moe/b12x" page, _swiglu_params: limit, alpha and beta for the
+# swigluoai activation; refused with W4A8).  The formula is not printed there; the oracle
+# takes h = gate * sigmoid(alpha gate) * (up + beta) after the clamps.
+OAI_CASES = {
+    "nvfp4": lambda: _small(I.FMT_NVFP4, E=4, K=64, N=32, topk=2, T=5, limit=7.0, seed=13),
+    "nf3": lambda: _small(I.FMT_NF3, E=3, K=64, N=64, topk=3, T=4, limit=7.0, seed=14),
+    "hybrid": lambda: _small(I.FMT_NVFP4, E=6, K=64, N=32, topk=3, T=5, limit=7.0, seed=15, hybrid=2),
+}
+
+
+def test_swiglu_oai_alpha1_beta0_is_swiglu():
+    p = OAI_CASES["nf3"]()
+    a0, o0 = O.moe_problem(p)
+    a1, o1 = O.moe_problem(p, alpha=1.0, beta=0.0)
+    assert np.array_equal(a0, a1) and np.array_equal(o0, o1)
+
+
+@pytest.mark.parametrize("name", list(OAI_CASES))
+def test_swiglu_oai_matches_float64_bruteforce(name):
+    alpha, beta = 1.702, 1.0
+    p = OAI_CASES[name]()
+    acc, _ = O.moe_problem(p, alpha=alpha, beta=beta)
+    ref = BF.moe(p, act=lambda g, u: g * (1.0 / (1.0 + np.exp(-alpha * g))) * (u + beta))
+    assert np.allclose(acc, ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+    assert not np.allclose(acc, O.moe_problem(p)[0], rtol=1e-3)
+    # each parameter on its own moves the result
+    assert not np.allclose(acc, O.moe_problem(p, alpha=alpha)[0], rtol=1e-3)
+    assert not np.allclose(acc, O.moe_problem(p, beta=beta)[0], rtol=1e-3)
+
+
+def test_swiglu_oai_large_alpha_is_relu_gate():
+    """alpha -> inf turns the sigmoid into a step: h = relu(gate) (up + beta)."""
+    p = OAI_CASES["nvfp4"]()
+    acc, _ = O.moe_problem(p, alpha=1e4, beta=0.5)
+    ref = BF.moe(p, act=lambda g, u: np.maximum(g, 0.0) * (u + 0.5))
+    assert np.allclose(acc, ref, rtol=0, atol=2e-3 * np.abs(ref).max())
+    silu = BF.moe(p, act=lambda g, u: g / (1.0 + np.exp(-g)) * (u + 0.5))
+    assert not np.allclose(silu, ref, rtol=0, atol=2e-2 * np.abs(ref).max())
+
+
+def test_swiglu_oai_refused_for_mxfp8_activations():
+    with pytest.raises(ValueError):
+        O.moe_problem(CASES["mxfp4_k3"](), alpha=1.702, beta=1.0)
