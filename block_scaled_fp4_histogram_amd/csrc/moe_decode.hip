@@ -338,21 +338,28 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
 __device__ __forceinline__ void dec_write_groups(const DecArgs &a, int u) {
   const int l = threadIdx.x & 63, nkt2 = (a.N + 127) / 128;
   const unsigned long long same = dec_same(u);
-  const unsigned long long F = __ballot(same != 0 && __ffsll(same) - 1 == l);
-  int n = 0, items = 0;
-  for (unsigned long long f = F; f; f &= f - 1, n++) {
-    const int L = __ffsll(f) - 1;
-    const unsigned long long m = readlane_u64(same, L);
-    if (l == 0) {
-      a.groups->gu[n] = __builtin_amdgcn_readlane(u, L);
-      a.groups->gm[n] = m;
-      a.groups->istart[n] = items;
-    }
-    items += ((__popcll(m) + 15) / 16) * nkt2;
+  const bool first = same != 0 && __ffsll(same) - 1 == l;   // this lane opens a group
+  const unsigned long long F = __ballot(first);
+  // a group's index is the number of groups opened by lower lanes; its item
+  // offset is the inclusive lane scan of the item counts minus its own.  One
+  // store per table entry, all lanes at once (a store per group in a loop
+  // queues behind the weight loads of the other blocks on the CU).
+  const int n = __popcll(F & ((1ull << l) - 1ull));
+  const int mine = first ? ((__popcll(same) + 15) / 16) * nkt2 : 0;
+  int incl = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (l >= d) incl += v;
   }
-  if (l == 0) {
-    a.groups->ng = n;
-    a.groups->nitems = items;
+  if (first) {
+    a.groups->gu[n] = u;
+    a.groups->gm[n] = same;
+    a.groups->istart[n] = incl - mine;
+  }
+  if (l == 63) {
+    a.groups->ng = __popcll(F);
+    a.groups->nitems = incl;
   }
 }
 
@@ -408,10 +415,13 @@ __device__ __forceinline__ void dec_fold_lds(const DecArgs &a, unsigned long lon
 // waves take equal contiguous slices.  A wave streams its items through a ring
 // of kG2Ring register slots: the weights of the next kG2Ring items are always
 // in flight, so every wave keeps its share of HBM busy from the first
-// instruction to the last.  A wave folds its accumulator into per-token sums
-// whenever a run of one (group, pass) ends; the waves' token sums are added in
-// wave order.  The partition depends only on the ids: bit-stable run to run.
-constexpr int kG2Ring = 6;
+// instruction to the last.  Two slots are enough: with 448 blocks of 8 waves
+// a deeper ring only lengthens the memory queues (measured at K = 7168:
+// 2 slots 18.9 us, 3 19.6, 6 21.2, 12 24.2).  A wave folds its accumulator
+// into per-token sums whenever a run of one (group, pass) ends; the waves'
+// token sums are added in wave order.  The partition depends only on the ids:
+// bit-stable run to run.
+constexpr int kG2Ring = 2;
 constexpr int kDecG2WavesA8 = 8;
 
 // Position in the item list; the expert's weight streams (and format, global
@@ -584,7 +594,7 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
 // or NF3 12 + 1 bytes a lane, per the group's tier); every route's bf16
 // intermediate row is staged in LDS by direct loads.  Each item is four
 // dequantise-and-multiply steps of 8 columns (bf16 MFMA).
-constexpr int kG2RingA16 = 6;
+constexpr int kG2RingA16 = 2;   // as kG2Ring (NVFP4 at K = 6144: 2 slots 40.4 us, 6 42.3)
 
 __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a) {
   extern __shared__ __align__(16) uint8_t dsm2[];
