@@ -280,6 +280,11 @@ def main():
     stage_ms, runs = plan.stage_times()
     plan.enable_stage_timing(0)
     stage_us = {s: 1000.0 * v / max(runs, 1) for s, v in zip(STAGES, stage_ms)}
+    sequence = {0: "decode", 64: "prefill"}.get(plan.capacity(cfg.T)[1], "general")
+    if sequence == "decode":
+        # two launches, no route planner or combine kernel: the events bracketing those
+        # empty stages measure only their own overhead
+        stage_us["route"] = stage_us["combine"] = 0.0
     log("stages (us): " + ", ".join(f"{k} {v:.1f}" for k, v in stage_us.items()))
 
     dominant = max(("gemm1", "gemm2"), key=lambda s: stage_us[s])
@@ -329,7 +334,7 @@ def main():
         "config": {"workload": workload, "tokens": cfg.T, "live_tokens": alg["live"], "experts": cfg.E,
                    "hidden": cfg.K, "intermediate": cfg.N, "top_k": cfg.topk,
                    "distinct_experts": alg["distinct"], "layer_copies_cycled": args.layers,
-                   "launch": "hipGraph replay" if use_graph else "eager",
+                   "launch": "hipGraph replay" if use_graph else "eager", "sequence": sequence,
                    "us_per_layer": round(us_layer, 2),
                    "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
                    "layer_hbm_frac": round(alg["layer_bytes"] / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

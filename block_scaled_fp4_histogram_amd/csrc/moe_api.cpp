@@ -519,8 +519,14 @@ int moe_plan_stage_times(moe_plan_t plan, float *ms, int n, int *runs) {
 
 int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows) {
   if (!plan_ok(plan) || T < 0) return 0;
-  if (tile_rows) *tile_rows = moe::kTileRows;
-  return cap_for(plan, std::max(T, 1));
+  const int cap = cap_for(plan, std::max(T, 1));
+  if (tile_rows) {
+    // the sequence a chunk of that capacity takes: decode (no route tiles), prefill, general
+    const int t = std::min(std::max(T, 1), cap);
+    *tile_rows = use_decode(plan, t) ? 0 : (plan->N % 64 == 0 && t >= moe::kPrefillMinT) ? moe::kPfTileRows
+                                                                                          : moe::kTileRows;
+  }
+  return cap;
 }
 
 size_t moe_scratch_bytes(moe_plan_t plan, int tokens, int deterministic) {

@@ -143,8 +143,10 @@ int moe_run(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const void *x, 
 /* Message of the calling thread's most recent failure ("" if none). */
 const char *moe_last_error(void);
 
-/* Capacity the plan runs a batch of T tokens at, and the token rows of that
- * capacity's tile (0 on a bad plan).  Host only; used by tests and benches. */
+/* Capacity the plan runs a batch of T tokens at (0 on a bad plan), and the
+ * route rows of the tiles its launch sequence uses: 0 for the decode sequence
+ * (no route planner, no tiles), 64 for prefill, 16 for the general kernels.
+ * Host only; used by tests and benches. */
 int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows);
 
 /* Apply each slot's router weight to that slot's copy of the token before

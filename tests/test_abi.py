@@ -59,6 +59,12 @@ def test_capacity_ladder_and_scratch_sizes():
     assert p.capacity(100)[0] == 128
     assert p.capacity(4096)[0] == 4096
     assert p.capacity(10000)[0] == 4096          # chunks of the top rung
+    # route tile rows of the launch sequence: decode (T <= 16, <= 64 routes) has none
+    assert p.capacity(8)[1] == 0
+    assert p.capacity(11)[1] == 16                # 66 routes: general kernels
+    assert p.capacity(4096)[1] == 64              # prefill (N % 64 == 0)
+    q = M.Plan(8, 256, 96, 2, None, M.A_MXFP8, max_tokens=512)
+    assert q.capacity(512)[1] == 16               # N % 64 != 0: general kernels
     sizes = [p.scratch_bytes(t) for t in (1, 8, 64, 512, 4096)]
     assert sizes == sorted(sizes)
     assert p.scratch_bytes(10000) == p.scratch_bytes(4096)
