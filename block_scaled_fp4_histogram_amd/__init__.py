@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes as C
 import math
+import os
 from typing import Optional, Sequence
 
 from . import _lib
@@ -19,6 +20,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOTPREPARED, MOE_ESCRATCH, MOE_EHIP =
 W_MXFP4, W_NVFP4, W_NF3 = 1, 2, 3
 A_MXFP8, A_BF16 = 1, 2
 W13_UP_GATE, W13_GATE_UP = 0, 1
+SEQ_AUTO, SEQ_DECODE, SEQ_GENERAL, SEQ_PREFILL = 0, 1, 2, 3
 
 
 class MoeError(RuntimeError):
@@ -75,6 +77,35 @@ class Plan:
         rows = C.c_int(0)
         cap = _lib.load().moe_plan_capacity(self.handle, T, C.byref(rows))
         return cap, rows.value
+
+    def set_sequence(self, tokens: int, seq: int):
+        """Pin the rung a batch of `tokens` runs at to a launch sequence (SEQ_AUTO: the ladder's choice)."""
+        _check(_lib.load().moe_plan_set_sequence(self.handle, int(tokens), int(seq)))
+
+    def sequence(self, tokens: int) -> int:
+        """The launch sequence a batch of `tokens` runs with (SEQ_DECODE / SEQ_GENERAL / SEQ_PREFILL)."""
+        return _lib.load().moe_plan_sequence(self.handle, int(tokens))
+
+    def autotune(self, tiers, tokens, deterministic: bool = False, reps: int = 5, stream=None):
+        """Race the eligible sequences at the rung of each batch size in `tokens` on a synthetic
+        batch and pin the fastest; returns [len(tokens)][3] median microseconds of DECODE,
+        GENERAL and PREFILL (NaN where a rung cannot take one)."""
+        tok = [int(t) for t in tokens]
+        arr, keep = _tiers(tiers)
+        ta = (C.c_int * len(tok))(*tok)
+        us = (C.c_float * (3 * len(tok)))()
+        _check(_lib.load().moe_plan_autotune(self.handle, arr, len(tiers), ta, len(tok), int(bool(deterministic)),
+                                             int(reps), _stream(stream), us))
+        return [[us[3 * i + k] for k in range(3)] for i in range(len(tok))]
+
+    def save_tuning(self, path: str):
+        _check(_lib.load().moe_plan_save_tuning(self.handle, os.fsencode(path)))
+
+    def load_tuning(self, path: str) -> int:
+        """Pin the rungs the file holds for this geometry; returns how many were applied."""
+        n = _lib.load().moe_plan_load_tuning(self.handle, os.fsencode(path))
+        _check(min(n, 0))
+        return n
 
     def set_swiglu_oai(self, alpha: float, beta: float):
         """Activation gate * sigmoid(alpha gate) * (up + beta) after the clamps (bf16 plans; 1, 0 = plain)."""

@@ -24,6 +24,11 @@ SIGNATURES = {
     "moe_run": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "moe_last_error": (C.c_char_p, []),
     "moe_plan_capacity": (_i, [_vp, _i, C.POINTER(_i)]),
+    "moe_plan_set_sequence": (_i, [_vp, _i, _i]),
+    "moe_plan_sequence": (_i, [_vp, _i]),
+    "moe_plan_autotune": (_i, [_vp, _vp, _i, C.POINTER(_i), _i, _i, _i, _vp, C.POINTER(_f)]),
+    "moe_plan_save_tuning": (_i, [_vp, C.c_char_p]),
+    "moe_plan_load_tuning": (_i, [_vp, C.c_char_p]),
     "moe_plan_set_router_weight_on_input": (_i, [_vp, _i]),
     "moe_plan_set_swiglu_oai": (_i, [_vp, C.c_float, C.c_float]),
     "moe_plan_enable_stage_timing": (_i, [_vp, _i]),

@@ -55,6 +55,7 @@ struct moe_plan_s {
   int w_on_input = 0;     // router weight applied to GEMM1's input (W4A16 / W3A16 only)
   float alpha = 1.f, beta = 0.f;   // SwiGLU form gate * sigmoid(alpha gate) * (up + beta)
   std::vector<int> caps;  // ascending; caps.back() == chunk
+  std::vector<int> seq;   // per rung: the launch sequence it is pinned to (MOE_SEQ_*), 0 = the ladder's choice
   // optional stage timing: kStageEvents events per recorded run
   std::vector<hipEvent_t> events;
   int timing_runs_max = 0, timing_runs = 0;
@@ -79,6 +80,12 @@ int cap_for(const moe_plan_s *p, int T) {
   for (int c : p->caps)
     if (c >= T) return c;
   return p->caps.back();
+}
+
+int rung_of(const moe_plan_s *p, int T) {
+  for (size_t i = 0; i < p->caps.size(); i++)
+    if (p->caps[i] >= T) return (int)i;
+  return (int)p->caps.size() - 1;
 }
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -211,10 +218,31 @@ bool use_decode(const moe_plan_s *p, int T) {
   return T <= moe::kDecodeMaxT && T * p->topk <= moe::kDecodeMaxRoutes && lds_ok;
 }
 
+// Launch sequences: which ones a rung of `cap` tokens may take, the capacity
+// ladder's own choice for a chunk of T tokens, and the one a chunk runs with.
+bool seq_eligible(const moe_plan_s *p, int cap, int seq) {
+  switch (seq) {
+    case MOE_SEQ_DECODE: return use_decode(p, cap);   // then also for every chunk of <= cap tokens
+    case MOE_SEQ_GENERAL: return true;
+    case MOE_SEQ_PREFILL: return p->N % 64 == 0;
+    default: return false;
+  }
+}
+
+int ladder_seq(const moe_plan_s *p, int T) {
+  if (use_decode(p, T)) return MOE_SEQ_DECODE;
+  return p->N % 64 == 0 && T >= moe::kPrefillMinT ? MOE_SEQ_PREFILL : MOE_SEQ_GENERAL;
+}
+
+int seq_for(const moe_plan_s *p, int T) {
+  const int pinned = p->seq[rung_of(p, T)];
+  return pinned ? pinned : ladder_seq(p, T);
+}
+
 // Everything one chunk needs after validation.
 int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uint16_t *x, const int32_t *ids,
               const float *wts, uint16_t *out, int T, int deterministic, const Layout &L, uint8_t *scratch,
-              hipStream_t s, bool route_only, const hipEvent_t *ev = nullptr) {
+              hipStream_t s, bool route_only, bool prefill, const hipEvent_t *ev = nullptr) {
   if (ev) HIP_TRY(hipEventRecord(ev[0], s));
   const int R = T * p->topk;
   auto I32 = [&](size_t o) { return (int32_t *)(scratch + o); };
@@ -231,8 +259,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ra.E1 = n_tiers > 1 ? tiers[1].experts->E : 0;
   ra.G = (R + moe::kRouteChunk - 1) / moe::kRouteChunk;
   ra.max_tiles = L.max_tiles;
-  // prefill kernels (64-route tiles): N % 64 == 0, batches of a prefill rung
-  const bool prefill = p->N % 64 == 0 && T >= moe::kPrefillMinT;
+  // prefill kernels: 64-route tiles (N % 64 == 0); general kernels: 16-route tiles
   ra.tile_rows = prefill ? moe::kPfTileRows : moe::kTileRows;
   ra.ru = I32(L.ru);
   ra.lrank = I32(L.lrank);
@@ -420,6 +447,27 @@ int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
   return rc;
 }
 
+// T tokens in chunks of `cap` (the capacity the scratch layout L was carved
+// for), each chunk on its rung's launch sequence.
+int run_batch(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const void *x, const int32_t *ids,
+              const float *wts, void *out, int T, int deterministic, int cap, const Layout &L, uint8_t *scratch,
+              hipStream_t s, const hipEvent_t *ev = nullptr) {
+  for (int t0 = 0; t0 < T; t0 += cap) {
+    const int tc = std::min(cap, T - t0);
+    const uint16_t *xc = (const uint16_t *)x + (size_t)t0 * p->K;
+    const int32_t *idc = ids + (size_t)t0 * p->topk;
+    const float *wc = wts + (size_t)t0 * p->topk;
+    uint16_t *oc = (uint16_t *)out + (size_t)t0 * p->K;
+    const int seq = seq_for(p, tc);
+    const int rc = seq == MOE_SEQ_DECODE
+                       ? run_decode(p, tiers, n_tiers, xc, idc, wc, oc, tc, L, scratch, s, ev)
+                       : run_chunk(p, tiers, n_tiers, xc, idc, wc, oc, tc, deterministic, L, scratch, s, false,
+                                   seq == MOE_SEQ_PREFILL, ev);
+    if (rc != MOE_OK) return rc;
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -451,6 +499,7 @@ int moe_plan(int E, int K, int N, int top_k, float swiglu_limit, int act_format,
   for (int c : kLadder)
     if (c < max_tokens) p->caps.push_back(c);
   p->caps.push_back(max_tokens);
+  p->seq.assign(p->caps.size(), 0);
   *out = p;
   return MOE_OK;
 }
@@ -522,11 +571,210 @@ int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows) {
   const int cap = cap_for(plan, std::max(T, 1));
   if (tile_rows) {
     // the sequence a chunk of that capacity takes: decode (no route tiles), prefill, general
-    const int t = std::min(std::max(T, 1), cap);
-    *tile_rows = use_decode(plan, t) ? 0 : (plan->N % 64 == 0 && t >= moe::kPrefillMinT) ? moe::kPfTileRows
-                                                                                          : moe::kTileRows;
+    const int seq = seq_for(plan, std::min(std::max(T, 1), cap));
+    *tile_rows = seq == MOE_SEQ_DECODE ? 0 : seq == MOE_SEQ_PREFILL ? moe::kPfTileRows : moe::kTileRows;
   }
   return cap;
+}
+
+int moe_plan_set_sequence(moe_plan_t plan, int tokens, int seq) {
+  if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
+  if (tokens < 1) return fail(MOE_EINVAL, "tokens=%d", tokens);
+  const int r = rung_of(plan, tokens), cap = plan->caps[r];
+  if (seq == MOE_SEQ_AUTO) {
+    plan->seq[r] = 0;
+    return MOE_OK;
+  }
+  if (seq != MOE_SEQ_DECODE && seq != MOE_SEQ_GENERAL && seq != MOE_SEQ_PREFILL)
+    return fail(MOE_EINVAL, "sequence %d", seq);
+  if (!seq_eligible(plan, cap, seq))
+    return fail(MOE_EUNSUPPORTED, "sequence %d cannot run the %d-token capacity of this plan", seq, cap);
+  plan->seq[r] = seq;
+  return MOE_OK;
+}
+
+int moe_plan_sequence(moe_plan_t plan, int tokens) {
+  if (!plan_ok(plan) || tokens < 1) return 0;
+  return seq_for(plan, std::min(tokens, plan->caps.back()));
+}
+
+// ---------------------------------------------------------------- tuning
+
+namespace {
+
+// Seeded synthetic batch for the race (splitmix64): x ~ sum of four uniforms
+// (mean 0, variance 1/3) as bf16, each token's top_k distinct ids uniform over
+// [0, E), positive router weights summing to 1.
+uint64_t mix64(uint64_t &st) {
+  uint64_t z = (st += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+double unit01(uint64_t &st) { return (double)(mix64(st) >> 11) * (1.0 / 9007199254740992.0); }
+
+void tuning_batch(const moe_plan_s *p, int T, uint64_t seed, std::vector<uint16_t> &x, std::vector<int32_t> &ids,
+                  std::vector<float> &w) {
+  uint64_t st = seed;
+  x.resize((size_t)T * p->K);
+  for (auto &v : x) {
+    const float f = (float)(unit01(st) + unit01(st) + unit01(st) + unit01(st) - 2.0);
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    v = (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+  }
+  ids.resize((size_t)T * p->topk);
+  w.resize(ids.size());
+  const int k = std::min(p->topk, p->E);
+  for (int t = 0; t < T; t++) {
+    double sum = 0.0;
+    for (int j = 0; j < p->topk; j++) {
+      int e = -1;
+      if (j < k) {
+        bool dup = true;
+        while (dup) {
+          e = (int)(mix64(st) % (uint64_t)p->E);
+          dup = false;
+          for (int i = 0; i < j; i++) dup = dup || ids[(size_t)t * p->topk + i] == e;
+        }
+      }
+      ids[(size_t)t * p->topk + j] = e;
+      w[(size_t)t * p->topk + j] = (float)(0.05 + unit01(st));
+      sum += w[(size_t)t * p->topk + j];
+    }
+    for (int j = 0; j < p->topk; j++) w[(size_t)t * p->topk + j] = (float)(w[(size_t)t * p->topk + j] / sum);
+  }
+}
+
+// Device buffers of one race, freed on every path.
+struct TuneBuffers {
+  void *x = nullptr, *ids = nullptr, *w = nullptr, *out = nullptr, *scratch = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  ~TuneBuffers() {
+    for (void *q : {x, ids, w, out, scratch})
+      if (q) (void)hipFree(q);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+  }
+};
+
+std::string geometry_key(const moe_plan_s *p) {
+  char buf[128];
+  snprintf(buf, sizeof buf, "E=%d K=%d N=%d topk=%d afmt=%d max_tokens=%d", p->E, p->K, p->N, p->topk, p->afmt,
+           p->max_tokens);
+  return buf;
+}
+
+}  // namespace
+
+int moe_plan_autotune(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const int *tokens, int n, int deterministic,
+                      int reps, void *stream, float *us_out) {
+  if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
+  int rc = check_tiers(plan, tiers, n_tiers);
+  if (rc != MOE_OK) return rc;
+  if (!tokens || n < 1 || reps < 1) return fail(MOE_EINVAL, "tokens, n and reps must be given");
+  hipStream_t s = (hipStream_t)stream;
+  const int seqs[3] = {MOE_SEQ_DECODE, MOE_SEQ_GENERAL, MOE_SEQ_PREFILL};
+  for (int i = 0; i < n; i++) {
+    if (tokens[i] < 1) return fail(MOE_EINVAL, "tokens[%d]=%d", i, tokens[i]);
+    const int r = rung_of(plan, std::min(tokens[i], plan->caps.back())), cap = plan->caps[r];
+    const Layout L = layout(plan, cap, deterministic ? 1 : 0);
+    std::vector<uint16_t> hx;
+    std::vector<int32_t> hids;
+    std::vector<float> hw;
+    tuning_batch(plan, cap, 0x6D6F6521ull + (uint64_t)cap, hx, hids, hw);
+    TuneBuffers B;
+    HIP_TRY(hipMalloc(&B.x, hx.size() * 2));
+    HIP_TRY(hipMalloc(&B.ids, hids.size() * 4));
+    HIP_TRY(hipMalloc(&B.w, hw.size() * 4));
+    HIP_TRY(hipMalloc(&B.out, hx.size() * 2));
+    HIP_TRY(hipMalloc(&B.scratch, L.total));
+    HIP_TRY(hipMemcpy(B.x, hx.data(), hx.size() * 2, hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(B.ids, hids.data(), hids.size() * 4, hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(B.w, hw.data(), hw.size() * 4, hipMemcpyHostToDevice));
+    HIP_TRY(hipEventCreate(&B.e0));
+    HIP_TRY(hipEventCreate(&B.e1));
+    struct Restore {   // the rung's previous pin comes back if the race stops early
+      moe_plan_s *p;
+      int r, v;
+      bool armed;
+      ~Restore() {
+        if (armed) p->seq[r] = v;
+      }
+    } restore{plan, r, plan->seq[r], true};
+    int best = 0;
+    float best_us = 0.f;
+    for (int k = 0; k < 3; k++) {
+      float us = NAN;
+      if (seq_eligible(plan, cap, seqs[k])) {
+        plan->seq[r] = seqs[k];
+        std::vector<float> t;
+        for (int it = 0; it < reps + 2 && rc == MOE_OK; it++) {
+          HIP_TRY(hipEventRecord(B.e0, s));
+          rc = run_batch(plan, tiers, n_tiers, B.x, (const int32_t *)B.ids, (const float *)B.w, B.out, cap,
+                         deterministic ? 1 : 0, cap, L, (uint8_t *)B.scratch, s);
+          HIP_TRY(hipEventRecord(B.e1, s));
+          HIP_TRY(hipEventSynchronize(B.e1));
+          float ms = 0.f;
+          HIP_TRY(hipEventElapsedTime(&ms, B.e0, B.e1));
+          if (it >= 2) t.push_back(1000.f * ms);   // two warm-up runs
+        }
+        if (rc != MOE_OK) return rc;
+        std::sort(t.begin(), t.end());
+        us = t[t.size() / 2];
+        if (!best || us < best_us) {
+          best = seqs[k];
+          best_us = us;
+        }
+      }
+      if (us_out) us_out[3 * i + k] = us;
+    }
+    plan->seq[r] = best;
+    restore.armed = false;
+  }
+  return MOE_OK;
+}
+
+int moe_plan_save_tuning(moe_plan_t plan, const char *path) {
+  if (!plan_ok(plan) || !path) return fail(MOE_EINVAL, "invalid plan or path");
+  const std::string key = geometry_key(plan);
+  std::vector<std::string> keep;
+  if (FILE *f = fopen(path, "r")) {   // lines of other geometries stay
+    char line[512];
+    while (fgets(line, sizeof line, f)) {
+      std::string l(line);
+      if (l.compare(0, 4, "moe ") == 0 && l.find(" " + key + " cap=") == std::string::npos) keep.push_back(l);
+    }
+    fclose(f);
+  }
+  FILE *f = fopen(path, "w");
+  if (!f) return fail(MOE_EINVAL, "cannot write %s", path);
+  for (auto &l : keep) fputs(l.c_str(), f);
+  for (size_t r = 0; r < plan->caps.size(); r++)
+    if (plan->seq[r]) fprintf(f, "moe v1 %s cap=%d seq=%d\n", key.c_str(), plan->caps[r], plan->seq[r]);
+  const bool ok = fclose(f) == 0;
+  return ok ? MOE_OK : fail(MOE_EINVAL, "cannot write %s", path);
+}
+
+int moe_plan_load_tuning(moe_plan_t plan, const char *path) {
+  if (!plan_ok(plan) || !path) return fail(MOE_EINVAL, "invalid plan or path");
+  FILE *f = fopen(path, "r");
+  if (!f) return fail(MOE_EINVAL, "cannot read %s", path);
+  const std::string head = "moe v1 " + geometry_key(plan) + " cap=";
+  char line[512];
+  int applied = 0;
+  while (fgets(line, sizeof line, f)) {
+    if (strncmp(line, head.c_str(), head.size()) != 0) continue;
+    int cap = 0, seq = 0;
+    if (sscanf(line + head.size(), "%d seq=%d", &cap, &seq) != 2) continue;
+    const int r = rung_of(plan, cap);
+    if (plan->caps[r] != cap || !seq_eligible(plan, cap, seq)) continue;   // stale or foreign entry
+    plan->seq[r] = seq;
+    applied++;
+  }
+  fclose(f);
+  return applied;
 }
 
 size_t moe_scratch_bytes(moe_plan_t plan, int tokens, int deterministic) {
@@ -623,19 +871,7 @@ int moe_run(moe_plan_t p, const moe_tier *tiers, int n_tiers, const void *x, con
     ev = &p->events[(size_t)p->timing_runs * kStageEvents];
     p->timing_runs++;
   }
-  for (int t0 = 0; t0 < T; t0 += cap) {
-    const int tc = std::min(cap, T - t0);
-    const uint16_t *xc = (const uint16_t *)x + (size_t)t0 * p->K;
-    const int32_t *idc = ids + (size_t)t0 * p->topk;
-    const float *wc = wts + (size_t)t0 * p->topk;
-    uint16_t *oc = (uint16_t *)out + (size_t)t0 * p->K;
-    if (use_decode(p, tc))
-      rc = run_decode(p, tiers, n_tiers, xc, idc, wc, oc, tc, L, (uint8_t *)scratch, s, ev);
-    else
-      rc = run_chunk(p, tiers, n_tiers, xc, idc, wc, oc, tc, deterministic, L, (uint8_t *)scratch, s, false, ev);
-    if (rc != MOE_OK) return rc;
-  }
-  return MOE_OK;
+  return run_batch(p, tiers, n_tiers, x, ids, wts, out, T, deterministic, cap, L, (uint8_t *)scratch, s, ev);
 }
 
 int moe_debug_route(moe_plan_t p, const moe_tier *tiers, int n_tiers, const int32_t *ids, int T, void *scratch,
@@ -650,7 +886,7 @@ int moe_debug_route(moe_plan_t p, const moe_tier *tiers, int n_tiers, const int3
   const Layout L = layout(p, cap, 1);
   if (scratch_bytes < L.total) return fail(MOE_ESCRATCH, "scratch of %zu bytes; %zu needed", scratch_bytes, L.total);
   hipStream_t s = (hipStream_t)stream;
-  rc = run_chunk(p, tiers, n_tiers, nullptr, ids, nullptr, nullptr, T, 1, L, (uint8_t *)scratch, s, true);
+  rc = run_chunk(p, tiers, n_tiers, nullptr, ids, nullptr, nullptr, T, 1, L, (uint8_t *)scratch, s, true, false);
   if (rc != MOE_OK) return rc;
   int U = 0;
   for (int i = 0; i < n_tiers; i++) U += tiers[i].experts->E;

@@ -58,6 +58,11 @@ typedef enum {
 typedef enum { MOE_W_MXFP4 = 1, MOE_W_NVFP4 = 2, MOE_W_NF3 = 3 } moe_wfmt;
 typedef enum { MOE_A_MXFP8 = 1, MOE_A_BF16 = 2 } moe_afmt;
 typedef enum { MOE_W13_UP_GATE = 0, MOE_W13_GATE_UP = 1 } moe_w13_layout;
+/* Launch sequences of one chunk (the capacity ladder's choice unless a rung is
+ * pinned): DECODE = two kernels, no route planner (T <= 16, T * top_k <= 64);
+ * GENERAL = planner + 16-route-tile GEMMs + combine (any batch); PREFILL =
+ * planner + 64-route-tile GEMMs + combine (N % 64 == 0). */
+typedef enum { MOE_SEQ_AUTO = 0, MOE_SEQ_DECODE = 1, MOE_SEQ_GENERAL = 2, MOE_SEQ_PREFILL = 3 } moe_sequence;
 
 typedef struct moe_plan_s *moe_plan_t;       /* one layer geometry (host memory only) */
 typedef struct moe_experts_s *moe_experts_t; /* one layer's (or tier's) prepared weights */
@@ -148,6 +153,37 @@ const char *moe_last_error(void);
  * (no route planner, no tiles), 64 for prefill, 16 for the general kernels.
  * Host only; used by tests and benches. */
 int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows);
+
+/* Per-capacity tuning (sglang "moe_b12x_next.py", module docstring and
+ * _Geometry: each capacity of the ladder gets its own execution plan, raced
+ * once per geometry and persisted, instead of a fixed heuristic).
+ *
+ * moe_plan_set_sequence pins the rung a batch of `tokens` runs at to one
+ * launch sequence (MOE_SEQ_AUTO: back to the ladder's choice).  A sequence
+ * the rung cannot take (DECODE above 16 tokens or 64 routes, PREFILL with
+ * N % 64 != 0) is MOE_EUNSUPPORTED.  moe_plan_sequence returns the sequence a
+ * batch of `tokens` runs with now (0 on a bad plan).  Host only.
+ *
+ * moe_plan_autotune races every sequence each listed batch size's rung can
+ * take, on a seeded synthetic batch of the rung's full size with the caller's
+ * prepared experts (`reps` timed runs after two warm-up runs, median), and pins
+ * the rung to the fastest.  us_out (NULL or [n][3]) receives the median times
+ * of DECODE, GENERAL and PREFILL in microseconds, NaN where not eligible.  It
+ * allocates and synchronises (it is a tuning session, not part of the layer):
+ * call it before graph capture.
+ *
+ * moe_plan_save_tuning writes the plan's pinned rungs to a text file, one line
+ * per rung keyed by the geometry (E, K, N, top_k, act_format, max_tokens),
+ * keeping other geometries' lines already in the file.  moe_plan_load_tuning
+ * pins the rungs of the lines matching this plan's geometry and returns how
+ * many it applied (entries a rung cannot take are skipped), or MOE_EINVAL when
+ * the file cannot be read. */
+int moe_plan_set_sequence(moe_plan_t plan, int tokens, int seq);
+int moe_plan_sequence(moe_plan_t plan, int tokens);
+int moe_plan_autotune(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const int *tokens, int n, int deterministic,
+                      int reps, void *stream, float *us_out);
+int moe_plan_save_tuning(moe_plan_t plan, const char *path);
+int moe_plan_load_tuning(moe_plan_t plan, const char *path);
 
 /* Apply each slot's router weight to that slot's copy of the token before
  * GEMM1 instead of to its GEMM2 result (vLLM "fused_moe/b12x" page,

@@ -133,3 +133,42 @@ def test_swiglu_oai_needs_bf16_activations():
         a16.set_swiglu_oai(float("nan"), 1.0)
     with pytest.raises(RuntimeError):
         a16.set_swiglu_oai(1.0, float("inf"))
+
+
+def test_sequence_pins_and_tuning_file(tmp_path):
+    p = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
+    assert p.sequence(8) == M.SEQ_DECODE
+    assert p.sequence(64) == M.SEQ_GENERAL
+    assert p.sequence(4096) == M.SEQ_PREFILL
+    p.set_sequence(8, M.SEQ_GENERAL)
+    assert p.sequence(8) == M.SEQ_GENERAL and p.capacity(8)[1] == 16
+    assert p.sequence(7) == M.SEQ_DECODE              # another rung
+    p.set_sequence(64, M.SEQ_PREFILL)
+    assert p.sequence(50) == M.SEQ_PREFILL and p.capacity(64)[1] == 64
+    with pytest.raises(M.MoeError) as e:
+        p.set_sequence(24, M.SEQ_DECODE)              # 24 tokens x 6 slots > 64 routes
+    assert e.value.code == M.MOE_EUNSUPPORTED
+    with pytest.raises(M.MoeError) as e:
+        p.set_sequence(8, 7)
+    assert e.value.code == M.MOE_EINVAL
+    path = str(tmp_path / "tuning.txt")
+    other = M.Plan(8, 256, 96, 2, None, M.A_MXFP8, max_tokens=512)
+    with pytest.raises(M.MoeError) as e:
+        other.set_sequence(512, M.SEQ_PREFILL)        # N % 64 != 0
+    assert e.value.code == M.MOE_EUNSUPPORTED
+    other.set_sequence(4, M.SEQ_GENERAL)
+    other.save_tuning(path)
+    p.save_tuning(path)                               # keeps the other geometry's line
+    fresh = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
+    assert fresh.load_tuning(path) == 2
+    assert fresh.sequence(8) == M.SEQ_GENERAL and fresh.sequence(64) == M.SEQ_PREFILL
+    assert fresh.sequence(4096) == M.SEQ_PREFILL
+    o2 = M.Plan(8, 256, 96, 2, None, M.A_MXFP8, max_tokens=512)
+    assert o2.load_tuning(path) == 1 and o2.sequence(4) == M.SEQ_GENERAL
+    p.set_sequence(8, M.SEQ_AUTO)
+    assert p.sequence(8) == M.SEQ_DECODE
+    p.save_tuning(path)                               # rewrites this geometry's lines only
+    again = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
+    assert again.load_tuning(path) == 1 and again.sequence(8) == M.SEQ_DECODE
+    with pytest.raises(M.MoeError):
+        again.load_tuning(str(tmp_path / "missing.txt"))

@@ -3,6 +3,7 @@ rel-L2 <= 1e-2 and rel max-abs <= 2e-2 against the oracle's float64
 accumulator; rows with no valid slot exactly zero; deterministic mode bit-stable.
 Small configurations are compared on every row, full-size ones on sampled rows."""
 import dataclasses
+import math
 
 import numpy as np
 import pytest
@@ -249,3 +250,42 @@ def test_swiglu_oai(name, deterministic):
     plain, _ = O.moe_problem(L.prob)
     assert not np.allclose(acc, plain, rtol=1e-2), "the parameters must change this case"
 
+
+
+# Launch sequences pinned per capacity rung (moe_plan_set_sequence): batches the ladder
+# would send down another sequence must give the same layer on the pinned one.
+@pytest.mark.parametrize("name,seq", [("hybrid_decode", M.SEQ_GENERAL), ("hybrid_decode", M.SEQ_PREFILL),
+                                      ("nf3_decode", M.SEQ_GENERAL), ("nvfp4_clamped", M.SEQ_PREFILL),
+                                      ("decode_many_routes", M.SEQ_PREFILL), ("prefill_small", M.SEQ_GENERAL),
+                                      ("hybrid_small", M.SEQ_PREFILL), ("mxfp4_ragged", M.SEQ_GENERAL)])
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_pinned_sequence(name, seq, deterministic):
+    L = layer(name)
+    T = L.prob.cfg.T
+    L.plan.set_sequence(T, seq)
+    try:
+        assert L.plan.sequence(T) == seq
+        out = L.run(deterministic=deterministic)
+    finally:
+        L.plan.set_sequence(T, M.SEQ_AUTO)
+    acc, _ = O.moe_problem(L.prob)
+    assert_rows_match(out, acc, label=f"{name} sequence {seq} det={deterministic}")
+
+
+def test_autotune_pins_the_fastest_sequence():
+    L = layer("hybrid_small")          # 29 tokens x 5 slots: general or prefill; 8 tokens: all three
+    T = L.prob.cfg.T
+    try:
+        us = L.plan.autotune(L.tiers, [T, 8], reps=3)
+        assert math.isnan(us[0][0]) and us[0][1] > 0 and us[0][2] > 0
+        assert all(v > 0 for v in us[1])
+        seqs = (M.SEQ_DECODE, M.SEQ_GENERAL, M.SEQ_PREFILL)
+        for i, t in enumerate((T, 8)):
+            times = [v if not math.isnan(v) else float("inf") for v in us[i]]
+            assert L.plan.sequence(t) == seqs[times.index(min(times))]
+        out = L.run()
+    finally:
+        L.plan.set_sequence(T, M.SEQ_AUTO)
+        L.plan.set_sequence(8, M.SEQ_AUTO)
+    acc, _ = O.moe_problem(L.prob)
+    assert_rows_match(out, acc, label="hybrid_small after autotune")
