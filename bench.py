@@ -15,6 +15,7 @@ bounded sample of the same workload on this host's cores.
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -165,6 +166,11 @@ def main():
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
                     help="replay the layer from a captured HIP graph (auto: batches of <= 64 tokens, "
                          "as decode steps run in serving)")
+    ap.add_argument("--tune", default="", metavar="T1,T2,...",
+                    help="race the launch sequences at the capacity of each batch size (moe_plan_autotune) on "
+                         "the workload's geometry and print the times instead of the benchmark line")
+    ap.add_argument("--tune-reps", type=int, default=10, help="timed runs per sequence in --tune")
+    ap.add_argument("--tune-file", default="", help="with --tune: save the pinned rungs to this file")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference kernel that "
                          "scales HBM byte counters)")
@@ -202,7 +208,8 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     a8 = prob.tiers[0].fmt == I.FMT_MXFP4
-    plan = M.Plan(cfg.E, cfg.K, cfg.N, cfg.topk, cfg.limit, M.A_MXFP8 if a8 else M.A_BF16, max_tokens=cfg.T)
+    max_tokens = max([cfg.T] + [int(v) for v in args.tune.split(",") if v])
+    plan = M.Plan(cfg.E, cfg.K, cfg.N, cfg.topk, cfg.limit, M.A_MXFP8 if a8 else M.A_BF16, max_tokens=max_tokens)
 
     def upload(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -230,6 +237,18 @@ def main():
     out = torch.empty_like(x)
     scratch = M.scratch_for(plan, cfg.T, args.deterministic, dev)
     run_tiers = [[(ex, emap) for _, ex, emap in tiers] for tiers in layers]
+    if args.tune:
+        toks = [int(v) for v in args.tune.split(",")]
+        us = plan.autotune(run_tiers[0], toks, args.deterministic, reps=args.tune_reps)
+        names = ("decode", "general", "prefill")
+        rows = [{"tokens": t, "capacity": plan.capacity(t)[0],
+                 "us": {n: (None if math.isnan(v) else round(v, 2)) for n, v in zip(names, u)},
+                 "pinned": names[plan.sequence(t) - 1]} for t, u in zip(toks, us)]
+        if args.tune_file:
+            plan.save_tuning(args.tune_file)
+        print(json.dumps({"workload": cfg.name, "deterministic": args.deterministic, "layer_copies": args.layers,
+                          "tuning": rows}), flush=True)
+        return
 
     def step(i):
         M.run(plan, run_tiers[i % len(run_tiers)], x, ids, wts, out, args.deterministic, scratch)

@@ -229,6 +229,10 @@ bool seq_eligible(const moe_plan_s *p, int cap, int seq) {
   }
 }
 
+// The ladder's own choice.  The prefill threshold is where the 64-route tiles
+// overtake the 16-route ones in a race on uniform routing (one MI355X, both
+// geometries of the pages, atomic and deterministic combine): from 512 tokens
+// up for W4A16 / W3A16 and for atomic W4A8, 1024 for deterministic W4A8.
 int ladder_seq(const moe_plan_s *p, int T) {
   if (use_decode(p, T)) return MOE_SEQ_DECODE;
   return p->N % 64 == 0 && T >= moe::kPrefillMinT ? MOE_SEQ_PREFILL : MOE_SEQ_GENERAL;

@@ -29,6 +29,9 @@ def layer(name, **kw):
             prob = SMALL[name]()
         _CACHE.clear()   # keep at most one large layer resident
         _CACHE[key] = DeviceLayer(prob, **kw)
+        if name in SMALL and "prefill" in name:
+            # small batches the ladder gives the 16-route kernels: pin the 64-route ones
+            _CACHE[key].plan.set_sequence(prob.cfg.T, M.SEQ_PREFILL)
     return _CACHE[key]
 
 
@@ -52,7 +55,7 @@ SMALL = {
                                                           limit=7.0, fmt=I.FMT_MXFP4, e8m0_exp=(-9, -5)), seed=9),
     "nf3_decode": lambda: I.make_problem(I.Config("nf3_decode", T=5, E=40, K=512, N=96, topk=7, limit=None,
                                                   fmt=I.FMT_NF3), seed=10),
-    # prefill-size W4A8 batches (T >= 128, N % 64 == 0): 64-route tiles streamed through
+    # W4A8 batches on the prefill sequence (pinned in layer(); N % 64 == 0): 64-route tiles streamed through
     # the LDS ring; Zipf-skewed loads give full, ragged and single-tile experts, and
     # N % 128 == 64 leaves a half k-tile in the down GEMM
     "prefill_small": lambda: I.make_problem(I.Config("prefill_small", T=160, E=12, K=512, N=192, topk=4, limit=7.0,
@@ -253,7 +256,8 @@ def test_swiglu_oai(name, deterministic):
 
 
 # Launch sequences pinned per capacity rung (moe_plan_set_sequence): batches the ladder
-# would send down another sequence must give the same layer on the pinned one.
+# (or the pin above) would send down another sequence must give the same layer on the
+# pinned one.
 @pytest.mark.parametrize("name,seq", [("hybrid_decode", M.SEQ_GENERAL), ("hybrid_decode", M.SEQ_PREFILL),
                                       ("nf3_decode", M.SEQ_GENERAL), ("nvfp4_clamped", M.SEQ_PREFILL),
                                       ("decode_many_routes", M.SEQ_PREFILL), ("prefill_small", M.SEQ_GENERAL),
@@ -262,12 +266,13 @@ def test_swiglu_oai(name, deterministic):
 def test_pinned_sequence(name, seq, deterministic):
     L = layer(name)
     T = L.prob.cfg.T
+    before = L.plan.sequence(T)
     L.plan.set_sequence(T, seq)
     try:
         assert L.plan.sequence(T) == seq
         out = L.run(deterministic=deterministic)
     finally:
-        L.plan.set_sequence(T, M.SEQ_AUTO)
+        L.plan.set_sequence(T, before)
     acc, _ = O.moe_problem(L.prob)
     assert_rows_match(out, acc, label=f"{name} sequence {seq} det={deterministic}")
 
