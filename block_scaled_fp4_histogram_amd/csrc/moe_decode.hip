@@ -593,9 +593,12 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
 // wave slices and weight ring as the W4A8 kernel (a slot: NVFP4 16 + 2 bytes
 // or NF3 12 + 1 bytes a lane, per the group's tier); every route's bf16
 // intermediate row is staged in LDS by direct loads.  Each item is four
-// dequantise-and-multiply steps of 8 columns (bf16 MFMA).
+// dequantise-and-multiply steps of 8 columns (bf16 MFMA).  WF: the format of
+// every tier (one 16- or 12-byte load per slot), or 0 for two tiers of
+// different formats (one load shape for both, below).
 constexpr int kG2RingA16 = 2;   // as kG2Ring (NVFP4 at K = 6144: 2 slots 40.4 us, 6 42.3)
 
+template <int WF>
 __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a) {
   extern __shared__ __align__(16) uint8_t dsm2[];
   __shared__ float wr_s[kDecodeMaxRoutes];
@@ -621,7 +624,8 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   if (tid < a.R) wr_s[tid] = wv;
   const int per = (NI + kDecG2WavesA8 - 1) / kDecG2WavesA8;
   const int i0 = min(NI, w * per), i1 = min(NI, i0 + per);
-  v3i A3[kG2RingA16];   // weight bytes 0..11 of the lane
+  v4i A16[kG2RingA16];   // NVFP4: the lane's 16 weight bytes
+  v3i A3[kG2RingA16];    // otherwise: weight bytes 0..11 of the lane
   uint32_t A4[kG2RingA16], sa[kG2RingA16];
   G2Iter is;
   if (i0 < i1) g2_start(is, a, i0, istart, ng, nkt, gu, gm, g2v);
@@ -633,17 +637,22 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
     is.fmt = W_NVFP4;
     is.kt = 0;
   }
-  // one instruction shape for both formats (no branch: a loaded value copied
-  // out of a branch would have to be waited for): 12 data bytes, the 4th
-  // dword (NVFP4 only; NF3 loads out of range), and an aligned 16-bit scale
-  // load (NVFP4: the lane's two E4M3 bytes; NF3: the pair holding its byte)
+  // mixed tiers: one instruction shape for both formats (no branch: a loaded
+  // value copied out of a branch would have to be waited for): 12 data bytes,
+  // the 4th dword (NVFP4 only; NF3 loads out of range), and an aligned 16-bit
+  // scale load (NVFP4: the lane's two E4M3 bytes; NF3: the pair holding its
+  // byte).  One format: one data load of its width.
   auto issue = [&](int s) {
     const bool ok = is.item < i1 && is.kt * 128 + 32 * g < N;
-    const bool nv = is.fmt == W_NVFP4;
+    const bool nv = WF == W_NVFP4 || (WF == 0 && is.fmt == W_NVFP4);
     const uint32_t U = nv ? 16u : 12u;
     const uint32_t dv = ok ? (uint32_t)is.kt * 64u * U + (uint32_t)l * U : 0x80000000u;
-    A3[s] = buf_load12(is.wb, dv, is.w0);
-    A4[s] = buf_load4(is.wb, nv && ok ? dv + 12u : 0x80000000u, is.w0);
+    if constexpr (WF == W_NVFP4) {
+      A16[s] = buf_load16(is.wb, dv, is.w0);
+    } else {
+      A3[s] = buf_load12(is.wb, dv, is.w0);
+      if constexpr (WF == 0) A4[s] = buf_load4(is.wb, nv && ok ? dv + 12u : 0x80000000u, is.w0);
+    }
     sa[s] = buf_load2(is.sb, ok ? (nv ? (uint32_t)is.kt * 128u + (uint32_t)l * 2u : (uint32_t)is.kt * 64u + (uint32_t)(l & ~1))
                                 : 0x80000000u, is.s0);
     if (is.item < i1) g2_next(is, a, ng, nkt, gu, gm, g2v);
@@ -661,7 +670,9 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   }
 #pragma unroll
   for (int s = 0; s < kG2RingA16; s++) issue(s);
-  wait_vm<3 * kG2RingA16>();   // the staged rows have landed (the ring's 3 loads a slot may be in flight)
+  // the staged rows have landed once at most the ring's loads (3 a slot for
+  // mixed tiers, 2 for one format) are in flight
+  wait_vm<(WF == 0 ? 3 : 2) * kG2RingA16>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   float tok[4] = {0.f, 0.f, 0.f, 0.f};
@@ -686,8 +697,17 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
 #pragma unroll
           for (int st = 0; st < 4; st++) B[st] = hp[st];
         }
-        const uint32_t sc = sa[s], d[4] = {(uint32_t)A3[s][0], (uint32_t)A3[s][1], (uint32_t)A3[s][2], A4[s]};
-        if (ic.fmt == W_NVFP4) {
+        uint32_t d[4];
+        if constexpr (WF == W_NVFP4) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) d[i] = (uint32_t)A16[s][i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 3; i++) d[i] = (uint32_t)A3[s][i];
+          d[3] = WF == 0 ? A4[s] : 0u;
+        }
+        const uint32_t sc = sa[s];
+        if (WF == W_NVFP4 || (WF == 0 && ic.fmt == W_NVFP4)) {
           const float slo = e4m3_f32(sc & 0xFFu), shi = e4m3_f32((sc >> 8) & 0xFFu);
 #pragma unroll
           for (int st = 0; st < 4; st++)
@@ -753,7 +773,13 @@ hipError_t launch_decode(int a8, const DecArgs &a, hipStream_t s, hipEvent_t ev_
   }
   const size_t lds2 = a8 ? (size_t)dec2_hq_bytes(a.R, a.N) + dec2_hs_bytes(a.R, a.N) : 0;
   if (a8) hipLaunchKernelGGL(k_dec_gemm2_a8, g2, dim3(kDecG2WavesA8 * 64), lds2, s, a);
-  else hipLaunchKernelGGL(k_dec_gemm2_a16r, g2, dim3(kDecG2WavesA8 * 64), (size_t)dec2_hb_bytes(a.R, a.N), s, a);
+  else {
+    const int f0 = a.tier[0].fmt, f1 = a.n_tiers > 1 ? a.tier[1].fmt : f0;
+    const size_t lds = (size_t)dec2_hb_bytes(a.R, a.N);
+    if (f0 == W_NVFP4 && f1 == W_NVFP4) hipLaunchKernelGGL(k_dec_gemm2_a16r<W_NVFP4>, g2, dim3(kDecG2WavesA8 * 64), lds, s, a);
+    else if (f0 == W_NF3 && f1 == W_NF3) hipLaunchKernelGGL(k_dec_gemm2_a16r<W_NF3>, g2, dim3(kDecG2WavesA8 * 64), lds, s, a);
+    else hipLaunchKernelGGL(k_dec_gemm2_a16r<0>, g2, dim3(kDecG2WavesA8 * 64), lds, s, a);
+  }
   return hipGetLastError();
 }
 
