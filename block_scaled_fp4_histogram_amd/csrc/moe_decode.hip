@@ -189,13 +189,16 @@ __device__ __forceinline__ void a16w_load(A16W<WF> &st, const RowTiles &rt, uint
 template <int WF>
 __device__ __forceinline__ void a16w_mfma(const A16W<WF> &st, const uint16_t *xrow, bool have, int g, int kt,
                                           v4f *acc) {
+  typename A16Tile<WF>::Deq dq[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) dq[q] = st.A[q].prep();
 #pragma unroll
   for (int s = 0; s < 4; s++) {
     v4i b = v4i{0, 0, 0, 0};
     if (have) b = *(const v4i *)(xrow + kt * 128 + 32 * g + 8 * s);
     const v8bf bb = __builtin_bit_cast(v8bf, b);
 #pragma unroll
-    for (int q = 0; q < 4; q++) acc[q] = mfma_bf16(st.A[q].step(s), bb, acc[q]);
+    for (int q = 0; q < 4; q++) acc[q] = mfma_bf16(st.A[q].step(s, dq[q]), bb, acc[q]);
   }
 }
 

@@ -35,8 +35,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
-// E4M3 (fn) byte -> fp32 (NaN codes are out of contract).
-__device__ __forceinline__ float e4m3_f32(uint32_t b) {
+// E4M3 (fn) byte (the low byte of b) -> fp32, exact, by gfx950's FP8
+// conversion (OCP E4M3: bias 7, subnormals m * 2^-9; NaN codes are out of
+// contract).  One instruction and no branches, so a scale decoded once per
+// loaded tile stays cheap next to the dequantisation it feeds.
+__device__ __forceinline__ float e4m3_f32(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+
+// The same decode from the bit fields, with the subnormal case on a branch of
+// its own.  The prefill W4A16/W3A16 k-loops keep this form: its control flow
+// bounds the compiler's scheduling regions there, and with any branch-free
+// decode their register use rises from about 245 to 300 VGPRs (one wave per
+// SIMD instead of two), which measured 45 % slower.
+__device__ __forceinline__ float e4m3_f32_branched(uint32_t b) {
   const uint32_t e = (b >> 3) & 15u, m = b & 7u;
   const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
   return (b & 0x80u) ? -v : v;
@@ -268,14 +278,25 @@ struct A16Tile {
     }
   }
   __device__ __forceinline__ void zero() { d[0] = d[1] = d[2] = d[3] = 0; sc = 0; }
-  __device__ __forceinline__ v8bf step(int s) const {
+  // The tile's decoded scales, computed once before its four steps: NVFP4 the
+  // fp32 scales of columns 0..15 and 16..31 (as bits), NF3 the scaled
+  // magnitude tables t01, t23.
+  struct Deq {
+    uint32_t u, v;
+  };
+  __device__ __forceinline__ Deq prep() const {
+    Deq q;
     if (WF == W_NVFP4) {
-      return nvfp4_step(d[s], e4m3_f32(s < 2 ? (sc & 0xFFu) : (sc >> 8)));
+      q.u = __float_as_uint(e4m3_f32(sc & 0xFFu));
+      q.v = __float_as_uint(e4m3_f32((sc >> 8) & 0xFFu));
     } else {
-      uint32_t t01, t23;
-      nf3_tables(e4m3_f32(sc), t01, t23);
-      return nf3_step_rc(s < 2 ? d[0] : d[1], d[2], s, t01, t23);
+      nf3_tables(e4m3_f32(sc & 0xFFu), q.u, q.v);
     }
+    return q;
+  }
+  __device__ __forceinline__ v8bf step(int s, const Deq &q) const {
+    if (WF == W_NVFP4) return nvfp4_step(d[s], __uint_as_float(s < 2 ? q.u : q.v));
+    return nf3_step_rc(s < 2 ? d[0] : d[1], d[2], s, q.u, q.v);
   }
 };
 
@@ -370,11 +391,14 @@ __device__ __forceinline__ void a16g1_load(A16G1Stage<WF> &st, const uint8_t *wt
 
 template <int WF>
 __device__ __forceinline__ void a16g1_compute(const A16G1Stage<WF> &st, v4f *acc) {
+  typename A16Tile<WF>::Deq dq[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) dq[q] = st.A[q].prep();
 #pragma unroll
   for (int s = 0; s < 4; s++) {
     const v8bf b = __builtin_bit_cast(v8bf, st.B[s]);
 #pragma unroll
-    for (int q = 0; q < 4; q++) acc[q] = mfma_bf16(st.A[q].step(s), b, acc[q]);
+    for (int q = 0; q < 4; q++) acc[q] = mfma_bf16(st.A[q].step(s, dq[q]), b, acc[q]);
   }
 }
 

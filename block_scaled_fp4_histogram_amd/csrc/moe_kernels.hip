@@ -547,9 +547,11 @@ __global__ __launch_bounds__(256) void k_gemm2_a16(GemmArgs a) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < 2; j++) {
+      const typename A16Tile<WF>::Deq dq = A[j].prep();
 #pragma unroll
-      for (int s = 0; s < 4; s++) acc = mfma_bf16(A[j].step(s), __builtin_bit_cast(v8bf, B[j][s]), acc);
+      for (int s = 0; s < 4; s++) acc = mfma_bf16(A[j].step(s, dq), __builtin_bit_cast(v8bf, B[j][s]), acc);
+    }
   }
   combine_store(a, ti, c, rt * 16 + 4 * g, acc, a.g2 ? a.g2[ti.e] : 1.0f);
 }

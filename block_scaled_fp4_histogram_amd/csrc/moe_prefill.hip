@@ -649,10 +649,10 @@ __device__ __forceinline__ void pf16_mma(const Pf16W &wt, const v4i (&b)[4][4], 
   for (int q = 0; q < 2; q++) {
     const uint32_t sc = pf16_scale<WF>(wt.sc[q], l);
     if constexpr (WF == W_NVFP4) {
-      slo[q] = e4m3_f32(sc & 0xFFu);
-      shi[q] = e4m3_f32((sc >> 8) & 0xFFu);
+      slo[q] = e4m3_f32_branched(sc & 0xFFu);
+      shi[q] = e4m3_f32_branched((sc >> 8) & 0xFFu);
     } else {
-      nf3_tables(e4m3_f32(sc & 0xFFu), t01[q], t23[q]);
+      nf3_tables(e4m3_f32_branched(sc & 0xFFu), t01[q], t23[q]);
     }
   }
 #pragma unroll
