@@ -1,27 +1,28 @@
 // Prefill-size GEMMs: tiles of 64 routes of one expert.
 //
-// W4A8 (MXFP4 weights x MXFP8 activations).  A block holds 16 weight row tiles
-// (256 weight rows) against the tile's 64 routes; its operands stream through
-// a 3-stage LDS ring by direct global-to-LDS loads.  One stage holds one
-// 128-column k-tile: 16 weight row tiles (16 x 1 KB of FP4 in MFMA lane
-// order), the 64 routes' MXFP8 activation slices (8 blocks of 8 rows x 128
-// bytes, 16-byte chunks XOR-swizzled so that MFMA operand reads spread over
-// the LDS banks) and the scales of both (As: 16 x 64 bytes, Bs: 64 x 4 bytes).
-// Every wave issues the same eight loads per stage, so "all but the newest n
-// stages have landed" is one s_waitcnt vmcnt(8 n) per wave followed by a
-// barrier.  Wave (wr, wc) owns row tiles 8 wr .. +7 and routes 32 wc .. +31:
-// 16 block-scaled MFMAs per k-tile, operands read from LDS at the k-tile that
-// uses them.
+// W4A8 (MXFP4 weights x MXFP8 activations).  A block of 4 waves holds 16
+// weight row tiles (256 weight rows) against the tile's 64 routes; wave w owns
+// row tiles 4w .. 4w+3 against all 64 routes, 16 block-scaled MFMAs per
+// 128-column k-tile.  The weights and their scale dwords stream by buffer
+// loads into a 3-deep register ring of each wave (no LDS); the activations are
+// shared, so they go through a 3-stage LDS ring by direct global-to-LDS loads:
+// one stage holds the 64 routes' MXFP8 slices of one k-tile (8 blocks of 8
+// rows x 128 bytes, 16-byte chunks XOR-swizzled so that MFMA operand reads
+// spread over the LDS banks) and their scales (64 x 4 bytes); each wave loads
+// two of the blocks.  Every wave issues the same eleven loads per stage, so
+// "all but the newest n stages have landed" is one s_waitcnt vmcnt(11 n) per
+// wave followed by a barrier; the activations are read from LDS at the
+// k-tile that uses them.
 //
 // Blocks are numbered XCD-major: the hardware hands workgroup b to XCD b % 8,
-// so logical work item (b % 8) * per + b / 8 puts a contiguous run of
-// (tile, column block) items on each XCD, in order.  The up/gate GEMM orders
-// items column-block-major: all tiles of a hot expert then run at once on one
-// XCD against the same weight slab, which is read once, while the activations
-// (tens of MB, re-read once per column block) stay in the last-level cache.
-// The down GEMM orders them tile-major: the column blocks of a tile share its
-// activation rows in L2, and one expert's w2 stays in L2 across its
-// consecutive tiles.
+// so logical work item (b % 8) * per + b / 8 puts a contiguous run of items on
+// each XCD, in order.  Both W4A8 GEMMs order items tile-major: the column
+// blocks of one tile run together on one XCD and share its activation rows in
+// L2, and an expert's weights stay in L2 across its consecutive tiles.  (The
+// up/gate GEMM ran column-block-major first, all tiles of an expert against
+// one weight slab at once; its 64 resident blocks per XCD then each streamed
+// private activation rows, about 530 KB of L2 fills per k-step against about
+// 190 KB tile-major, and it measured 3 % slower.)
 //
 //   k_pf_gemm1_a8  items (tile, 128-column intermediate block = 8 up and 8
 //                  gate row tiles): up/gate GEMMs over K, clamped SwiGLU and
@@ -232,7 +233,10 @@ __device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, PfW (&ring)[
     // raised issue priority while this wave has MFMAs ready: the arbiter then
     // feeds the matrix core from it while the SIMD's other wave waits on memory
     __builtin_amdgcn_s_setprio(1);
-    if ((kt + 1) * 128 <= src.kbytes) pf_mma<SWAP, true>(ring[R], b, sb, kt, src.kbytes, l, acc);
+    // a step that issues k-tile kt + ST - 1 is not the last one, so its k-tile
+    // is whole: known at compile time, the partial-tile variant and the
+    // accumulator copies where the two variants meet drop out of the loop
+    if (ISSUE == 1 || (kt + 1) * 128 <= src.kbytes) pf_mma<SWAP, true>(ring[R], b, sb, kt, src.kbytes, l, acc);
     else pf_mma<SWAP, false>(ring[R], b, sb, kt, src.kbytes, l, acc);
     __builtin_amdgcn_s_setprio(0);
   }
@@ -329,7 +333,7 @@ __device__ __forceinline__ void pf_combine(const GemmArgs &a, const PfWork &wk, 
 __global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8(GemmArgs a) {
   __shared__ PfLds L;
   const int K = a.K, N = a.N;
-  const PfWork wk = pf_work(a, (N + 127) / 128, true);
+  const PfWork wk = pf_work(a, (N + 127) / 128, false);
   if (!wk.valid) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -702,6 +706,8 @@ __device__ __forceinline__ void pf16_step(Pf16Lds &L, const Pf16Src &src, Pf16W 
   // raised issue priority around the MFMAs as for the W4A8 kernels (measured:
   // faster for the up/gate GEMM, slower for the down GEMM's short k-loops)
   if (!SWAP) __builtin_amdgcn_s_setprio(1);
+  // (the run-time check is kept in the steady loop too: its compile-time form,
+  // as in pf_step, measured 2 % slower here)
   if ((kt + 1) * 128 <= src.kcols) pf16_mma<WF, SWAP, true>(ring[R], b, kt, src.kcols, l, acc);
   else pf16_mma<WF, SWAP, false>(ring[R], b, kt, src.kcols, l, acc);
   if (!SWAP) __builtin_amdgcn_s_setprio(0);
