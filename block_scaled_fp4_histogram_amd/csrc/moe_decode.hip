@@ -148,11 +148,13 @@ struct RowTiles {
   uint32_t w0, wstep, s0, sstep;
 };
 
-__device__ __forceinline__ void a8w_load(A8W &st, const RowTiles &rt, uint32_t l, int kt) {
+// ok false (a k-tile past the reduction): the offsets fall outside the
+// buffers' range, so the loads return zeros without memory traffic.
+__device__ __forceinline__ void a8w_load(A8W &st, const RowTiles &rt, uint32_t l, int kt, bool ok) {
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    st.A[q] = buf_load16(rt.wb, (uint32_t)kt * 1024u + l * 16u, rt.w0 + q * rt.wstep);
-    st.sa[q] = buf_load1(rt.sb, (uint32_t)kt * 64u + l, rt.s0 + q * rt.sstep);
+    st.A[q] = buf_load16(rt.wb, ok ? (uint32_t)kt * 1024u + l * 16u : 0x80000000u, rt.w0 + q * rt.wstep);
+    st.sa[q] = buf_load1(rt.sb, ok ? (uint32_t)kt * 64u + l : 0x80000000u, rt.s0 + q * rt.sstep);
   }
 }
 
@@ -177,12 +179,12 @@ struct A16W {
 };
 
 template <int WF>
-__device__ __forceinline__ void a16w_load(A16W<WF> &st, const RowTiles &rt, uint32_t l, int kt) {
+__device__ __forceinline__ void a16w_load(A16W<WF> &st, const RowTiles &rt, uint32_t l, int kt, bool ok) {
   constexpr uint32_t U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
 #pragma unroll
   for (int q = 0; q < 4; q++)
-    st.A[q].load(rt.wb, (uint32_t)kt * 64u * U + l * U, rt.w0 + q * rt.wstep, rt.sb, (uint32_t)kt * 64u * SU + l * SU,
-                 rt.s0 + q * rt.sstep);
+    st.A[q].load(rt.wb, ok ? (uint32_t)kt * 64u * U + l * U : 0x80000000u, rt.w0 + q * rt.wstep, rt.sb,
+                 ok ? (uint32_t)kt * 64u * SU + l * SU : 0x80000000u, rt.s0 + q * rt.sstep);
 }
 
 // bf16 activations of route column c (LDS row xrow) for k-tile kt.
@@ -257,13 +259,16 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
     const int ncol = min(a.cpass, ncols - p0);
     const bool have = c < ncol;
     // three k-tiles of weights in flight per wave: tiles w, w + NW, w + 2 NW, ...
+    // Every load is issued, past the last k-tile too (zeros, no traffic): with
+    // loads under branches the compiler's wait before each MFMA group drained
+    // nearly every load in flight, the newly issued k-tiles included.
     Stage s0, s1, s2;
     auto load = [&](Stage &st, int kt) {
-      if constexpr (A8) a8w_load(st, rt, lu, kt);
-      else a16w_load<WF>(st, rt, lu, kt);
+      if constexpr (A8) a8w_load(st, rt, lu, kt, kt < nkt);
+      else a16w_load<WF>(st, rt, lu, kt, kt < nkt);
     };
-    if (w < nkt) load(s0, w);
-    if (w + NW < nkt) load(s1, w + NW);
+    load(s0, w);
+    load(s1, w + NW);
     dec_stage_x<A8, NW>(a, md, p0, ncol, dsm);
     __syncthreads();
     v4f acc[4];
@@ -280,16 +285,12 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
       }
     };
     for (int kt = w; kt < nkt; kt += 3 * NW) {
-      if (kt + 2 * NW < nkt) load(s2, kt + 2 * NW);
+      load(s2, kt + 2 * NW);
       mfma(s0, kt);
-      if (kt + NW < nkt) {
-        if (kt + 3 * NW < nkt) load(s0, kt + 3 * NW);
-        mfma(s1, kt + NW);
-      }
-      if (kt + 2 * NW < nkt) {
-        if (kt + 4 * NW < nkt) load(s1, kt + 4 * NW);
-        mfma(s2, kt + 2 * NW);
-      }
+      load(s0, kt + 3 * NW);
+      if (kt + NW < nkt) mfma(s1, kt + NW);
+      load(s1, kt + 4 * NW);
+      if (kt + 2 * NW < nkt) mfma(s2, kt + 2 * NW);
     }
     __syncthreads();   // the staged rows are dead; LDS becomes the reduction buffer
 #pragma unroll
