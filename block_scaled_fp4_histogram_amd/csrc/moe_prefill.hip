@@ -482,7 +482,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8_short(GemmArgs a) {
     int sb[4];
     pf_read_b(b, sb, L.st[kt], l);
     __builtin_amdgcn_s_setprio(1);
-    if ((kt + 1) * 128 <= src.kbytes) pf_mma<true, true>(wt[kt], b, sb, kt, src.kbytes, l, acc);
+    // only the last k-tile can be partial (NKT = N / 128 rounded up)
+    if (kt < NKT - 1 || (kt + 1) * 128 <= src.kbytes) pf_mma<true, true>(wt[kt], b, sb, kt, src.kbytes, l, acc);
     else pf_mma<true, false>(wt[kt], b, sb, kt, src.kbytes, l, acc);
     __builtin_amdgcn_s_setprio(0);
   }
