@@ -93,7 +93,7 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Carving of the scratch arena for one chunk of `cap` tokens.
 struct Layout {
   size_t ru, lrank, inv, perm, cnt, off, chunk_hist, tile_u, tile_row0, tier_tiles;
-  size_t xq, xs, hq, hs, hb, acc, rb;
+  size_t xq, xs, hq, hs, hb, acc, rb, dpart, dcnt;
   size_t total;
   int R, G, max_tiles;
 };
@@ -129,6 +129,10 @@ Layout layout(const moe_plan_s *p, int cap, int deterministic) {
     L.hs = take(R * moe::hs_stride(p->N));
   } else {
     L.hb = take(2 * R * p->N);
+    if (cap <= moe::kDecodeMaxT) {   // the decode down GEMM's two halves per 16-row output tile
+      L.dpart = take((size_t)(p->K / 16) * 256 * sizeof(float));
+      L.dcnt = take(4 * (size_t)(p->K / 16));
+    }
   }
   if (deterministic) L.rb = take(2 * R * p->K);
   else L.acc = take(4 * (size_t)cap * p->K);
@@ -195,6 +199,8 @@ int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const ui
   da.hb = (uint16_t *)(scratch + L.hb);
   da.out = out;
   da.groups = (moe::DecGroups *)(scratch + L.cnt);   // the planner's count table is free on this path
+  da.dpart = L.dpart ? (float *)(scratch + L.dpart) : nullptr;
+  da.dcnt = L.dcnt ? (int *)(scratch + L.dcnt) : nullptr;
   if (ev) {
     HIP_TRY(hipEventRecord(ev[0], s));
     HIP_TRY(hipEventRecord(ev[1], s));

@@ -121,7 +121,18 @@ struct DecArgs {
   DecGroups *groups;                 // scratch
   int w_on_input;                    // router weight scales GEMM1 (W4A16 / W3A16), not the GEMM2 result
   float alpha, beta;                 // SwiGLU form: gate * sigmoid(alpha gate) * (up + beta)
+  // W4A16 / W3A16 down GEMM split over two blocks per output row tile (scratch):
+  float *dpart;                      // [K/16][16 tokens][16 columns] fp32 token sums, both halves added
+  int *dcnt;                         // [K/16] halves finished; both zeroed by the up/gate kernel
 };
+
+// The W4A16 / W3A16 decode down GEMM runs two blocks per 16-row output tile,
+// one per half of the reduction's k-tiles, when there are two k-tiles or more.
+__host__ __device__ constexpr int dec2_a16_halves(int N) { return (N + 127) / 128 >= 2 ? 2 : 1; }
+// intermediate columns of half 0 (the wider one)
+__host__ __device__ constexpr int dec2_a16_cols0(int N) {
+  return dec2_a16_halves(N) == 1 ? N : ((((N + 127) / 128) + 1) / 2) * 128;
+}
 
 int decode_cpass(int K, int a8);
 size_t decode_gemm1_lds(int K, int cpass, int a8);

@@ -383,6 +383,14 @@ __global__ __launch_bounds__(256, 4) void k_dec_gemm1_a16(DecArgs a) {
   unsigned long long md;
   const int u = dec_route_u(a, threadIdx.x & 63);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) dec_write_groups(a, u);
+  if (dec2_a16_halves(a.N) == 2) {
+    // the down GEMM's per-tile accumulators and counters of finished halves
+    // start at zero: every block clears a slice
+    const int nb = gridDim.x * gridDim.y, b = blockIdx.y * gridDim.x + blockIdx.x;
+    const int n4 = a.K / 16 * 64;   // 256 floats per 16-row output tile, as float4
+    for (int i = b * 256 + (int)threadIdx.x; i < n4; i += nb * 256) ((v4f *)a.dpart)[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int i = b * 256 + (int)threadIdx.x; i < a.K / 16; i += nb * 256) a.dcnt[i] = 0;
+  }
   if (!dec_group(u, blockIdx.y, &ud, &md)) return;
   const DecExpert X = dec_expert(a, ud);
   if (X.fmt == W_NVFP4) dec_gemm1_body<false, W_NVFP4, 4>(a, X, md, dsm);
@@ -431,6 +439,7 @@ constexpr int kDecG2WavesA8 = 8;
 // Position in the item list; the expert's weight streams (and format, global
 // scale and this block's row-tile offsets) follow the group.
 struct G2Iter {
+  int rt;            // the block's 16-row output tile (set before g2_start)
   int item, grp, pass, kt, npass, fmt;
   float g2;
   unsigned long long md;
@@ -454,8 +463,8 @@ __device__ __forceinline__ void g2_enter_group(G2Iter &it, const DecArgs &a, int
   it.g2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2v), it.grp));
   it.wb = make_buf(T.w2 + (size_t)e * a.K * groups * U, (uint32_t)((size_t)a.K * groups * U));
   it.sb = make_buf(T.s2 + (size_t)e * a.K * groups * SU, (uint32_t)((size_t)a.K * groups * SU));
-  it.w0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 16u * (uint32_t)groups * U);
-  it.s0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 16u * (uint32_t)groups * SU);
+  it.w0 = __builtin_amdgcn_readfirstlane((uint32_t)it.rt * 16u * (uint32_t)groups * U);
+  it.s0 = __builtin_amdgcn_readfirstlane((uint32_t)it.rt * 16u * (uint32_t)groups * SU);
 }
 
 __device__ __forceinline__ void g2_start(G2Iter &it, const DecArgs &a, int item, int istart, int ng, int nkt, int gu,
@@ -507,6 +516,7 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   v4i A[kG2Ring];
   int sa[kG2Ring];
   G2Iter is;
+  is.rt = rt;
   if (i0 < i1) g2_start(is, a, i0, istart, ng, nkt, gu, gm);
   else is.item = i1;
   auto issue = [&](int s) {
@@ -544,6 +554,7 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   __builtin_amdgcn_s_barrier();
   float tok[4] = {0.f, 0.f, 0.f, 0.f};
   G2Iter ic;
+  ic.rt = rt;
   if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkt, gu, gm);
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
   int r = -1;
@@ -602,16 +613,38 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
 // different formats (one load shape for both, below).
 constexpr int kG2RingA16 = 2;   // as kG2Ring (NVFP4 at K = 6144: 2 slots 40.4 us, 6 42.3)
 
+//
+// Two blocks share each 16-row output tile when the reduction has two k-tiles
+// or more: block half h takes k-tiles [kt0, kt0 + nkh) of every (group, pass)
+// and stages only those columns of the intermediate rows, so a block needs
+// half the LDS and three fit on a CU (with all columns, 384 blocks of about
+// 66 KB at K = 6144 left half the CUs with twice the work of the others).
+// Each half adds its fp32 token sums into the tile's accumulator with device
+// atomics that return (so they have been performed once the wave has waited
+// for them), then counts itself on the tile's counter; the half that counts
+// second reads the sums back with atomics and writes the bf16 output.  No
+// fence is needed, which matters: a device-scope fence writes back and
+// invalidates the whole L2 of the XCD (measured: the down GEMM 2.3 times
+// slower with one fence pair per block).  The accumulators and counters are
+// zeroed by the up/gate kernel.  Two additions onto +0 give the same bits in
+// either order, so the result is bit-stable run to run.
 template <int WF>
 __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a) {
   extern __shared__ __align__(16) uint8_t dsm2[];
   __shared__ float wr_s[kDecodeMaxRoutes];
   __shared__ __align__(16) float yb[kDecG2WavesA8][256];   // per-wave fold tile, then its token sums
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
-  const int K = a.K, N = a.N, nkt = (N + 127) / 128, rt = blockIdx.x;
+  const int K = a.K, N = a.N, nkt = (N + 127) / 128;
+  const int halves = dec2_a16_halves(N), rt = blockIdx.x / halves, h = blockIdx.x - rt * halves;
+  const int nk0 = halves == 2 ? (nkt + 1) / 2 : nkt;   // k-tiles of half 0
+  const int kt0 = h ? nk0 : 0, nkh = h ? nkt - nk0 : nk0;
+  const int c0 = 128 * kt0, nh = min(N, 128 * (kt0 + nkh)) - c0;   // this half's intermediate columns
   const DecGroups *G = a.groups;
-  const int ng = __builtin_amdgcn_readfirstlane(G->ng), NI = __builtin_amdgcn_readfirstlane(G->nitems);
-  int gu = G->gu[l], istart = G->istart[l];
+  // every group's item count is a multiple of nkt (passes x k-tiles): the
+  // half's list keeps nkh of each pass's nkt k-tiles
+  const int ng = __builtin_amdgcn_readfirstlane(G->ng),
+            NI = __builtin_amdgcn_readfirstlane(G->nitems) / nkt * nkh;
+  int gu = G->gu[l], istart = G->istart[l] / nkt * nkh;
   uint32_t gm_lo = (uint32_t)G->gm[l], gm_hi = (uint32_t)(G->gm[l] >> 32);
   float wv = tid < a.R ? (a.w_on_input ? 1.0f : a.topk_w[tid]) : 0.f;   // weight on the input: 1 here
   float g2v = 1.0f;   // global scale of group l's expert
@@ -631,8 +664,9 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   v4i A16[kG2RingA16];   // NVFP4: the lane's 16 weight bytes
   v3i A3[kG2RingA16];    // otherwise: weight bytes 0..11 of the lane
   uint32_t A4[kG2RingA16], sa[kG2RingA16];
-  G2Iter is;
-  if (i0 < i1) g2_start(is, a, i0, istart, ng, nkt, gu, gm, g2v);
+  G2Iter is;   // its kt runs over the half's k-tiles: k-tile kt0 + kt of the reduction
+  is.rt = rt;
+  if (i0 < i1) g2_start(is, a, i0, istart, ng, nkh, gu, gm, g2v);
   else is.item = i1;
   if (i0 >= i1) {   // no items: the ring's loads still need valid descriptors
     is.wb = make_buf(a.hb, 0);
@@ -647,29 +681,30 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   // scale load (NVFP4: the lane's two E4M3 bytes; NF3: the pair holding its
   // byte).  One format: one data load of its width.
   auto issue = [&](int s) {
-    const bool ok = is.item < i1 && is.kt * 128 + 32 * g < N;
+    const int kt = kt0 + is.kt;
+    const bool ok = is.item < i1 && kt * 128 + 32 * g < N;
     const bool nv = WF == W_NVFP4 || (WF == 0 && is.fmt == W_NVFP4);
     const uint32_t U = nv ? 16u : 12u;
-    const uint32_t dv = ok ? (uint32_t)is.kt * 64u * U + (uint32_t)l * U : 0x80000000u;
+    const uint32_t dv = ok ? (uint32_t)kt * 64u * U + (uint32_t)l * U : 0x80000000u;
     if constexpr (WF == W_NVFP4) {
       A16[s] = buf_load16(is.wb, dv, is.w0);
     } else {
       A3[s] = buf_load12(is.wb, dv, is.w0);
       if constexpr (WF == 0) A4[s] = buf_load4(is.wb, nv && ok ? dv + 12u : 0x80000000u, is.w0);
     }
-    sa[s] = buf_load2(is.sb, ok ? (nv ? (uint32_t)is.kt * 128u + (uint32_t)l * 2u : (uint32_t)is.kt * 64u + (uint32_t)(l & ~1))
+    sa[s] = buf_load2(is.sb, ok ? (nv ? (uint32_t)kt * 128u + (uint32_t)l * 2u : (uint32_t)kt * 64u + (uint32_t)(l & ~1))
                                 : 0x80000000u, is.s0);
-    if (is.item < i1) g2_next(is, a, ng, nkt, gu, gm, g2v);
+    if (is.item < i1) g2_next(is, a, ng, nkh, gu, gm, g2v);
   };
-  // every route's bf16 intermediate row -> LDS (row stride N + 8 elements),
-  // 1 KB direct loads issued ahead of the ring
+  // this half's columns of every route's bf16 intermediate row -> LDS (row
+  // stride nh + 8 elements), 1 KB direct loads issued ahead of the ring
   const uint16_t *hb_s = (const uint16_t *)dsm2;
   {
-    const int rs = 2 * N + 16;
-    for (int ch = w; ch * 1024 < dec2_hb_bytes(a.R, N); ch += kDecG2WavesA8) {
+    const int rs = 2 * nh + 16;
+    const uint8_t *src0 = (const uint8_t *)a.hb + 2 * (size_t)c0;
+    for (int ch = w; ch * 1024 < dec2_hb_bytes(a.R, nh); ch += kDecG2WavesA8) {
       const int pos = ch * 1024 + l * 16, row = pos / rs, col = pos - row * rs;
-      dma16(row < a.R && col < 2 * N ? (const uint8_t *)a.hb + (size_t)row * 2 * N + col : (const uint8_t *)a.hb,
-            dsm2 + ch * 1024);
+      dma16(row < a.R && col < 2 * nh ? src0 + (size_t)row * 2 * N + col : (const uint8_t *)a.hb, dsm2 + ch * 1024);
     }
   }
 #pragma unroll
@@ -681,7 +716,8 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   __builtin_amdgcn_s_barrier();
   float tok[4] = {0.f, 0.f, 0.f, 0.f};
   G2Iter ic;
-  if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkt, gu, gm, g2v);
+  ic.rt = rt;
+  if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkh, gu, gm, g2v);
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
   int r = -1;
   for (int base = i0; base < i1; base += kG2RingA16) {
@@ -692,12 +728,12 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
           const int col = ic.pass * 16 + c;
           r = col < __popcll(ic.md) ? nth_bit(ic.md, col) : -1;
         }
-        const int kb = ic.kt * 128 + 32 * g;
+        const int kb = (kt0 + ic.kt) * 128 + 32 * g;
         v4i B[4];
 #pragma unroll
         for (int st = 0; st < 4; st++) B[st] = v4i{0, 0, 0, 0};
         if (r >= 0 && kb < N) {
-          const v4i *hp = (const v4i *)(hb_s + r * (N + 8) + kb);
+          const v4i *hp = (const v4i *)(hb_s + r * (nh + 8) + (kb - c0));
 #pragma unroll
           for (int st = 0; st < 4; st++) B[st] = hp[st];
         }
@@ -723,11 +759,11 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
           for (int st = 0; st < 4; st++)
             acc = mfma_bf16(nf3_step_rc(st < 2 ? d[0] : d[1], d[2], st, t01, t23), __builtin_bit_cast(v8bf, B[st]), acc);
         }
-        if (ic.kt == nkt - 1 || base + s + 1 == i1) {
+        if (ic.kt == nkh - 1 || base + s + 1 == i1) {
           dec_fold_lds(a, ic.md, ic.pass * 16, c, g, acc, r >= 0 ? wr_s[r] * ic.g2 : 0.f, &yb[w][0], tok);
           acc = v4f{0.f, 0.f, 0.f, 0.f};
         }
-        g2_next(ic, a, ng, nkt, gu, gm, g2v);
+        g2_next(ic, a, ng, nkh, gu, gm, g2v);
       }
       issue(s);   // the item kG2RingA16 ahead (out of range past the slice)
     }
@@ -736,14 +772,34 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
 #pragma unroll
   for (int i = 0; i < 4; i++) tw[i * 64 + l] = tok[i];
   __syncthreads();
-  if (w == 0 && c < a.T) {
-    float s4[4];
+  if (w != 0) return;
+  float s4[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      s4[i] = 0.f;
+  for (int i = 0; i < 4; i++) {
+    s4[i] = 0.f;
 #pragma unroll
-      for (int v = 0; v < kDecG2WavesA8; v++) s4[i] += yb[v][i * 64 + l];
+    for (int v = 0; v < kDecG2WavesA8; v++) s4[i] += yb[v][i * 64 + l];
+  }
+  if (halves == 2) {
+    // token c, columns 4g .. 4g + 3 of the tile
+    float *accp = a.dpart + (size_t)rt * 256 + c * 16 + 4 * g;
+    float done = 0.f;
+    if (c < a.T) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        done += __hip_atomic_fetch_add(accp + i, s4[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    asm volatile("" ::"v"(done));   // the returned values are waited for here
+    wait_vm<0>();
+    int prev = 0;
+    if (l == 0) prev = __hip_atomic_fetch_add(a.dcnt + rt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__shfl(prev, 0) == 0) return;   // the other half writes the output
+    if (c < a.T) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) s4[i] = __hip_atomic_fetch_add(accp + i, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (c < a.T) {
     uint2 o;
     o.x = pack_bf16x2(s4[0], s4[1]);
     o.y = pack_bf16x2(s4[2], s4[3]);
@@ -779,10 +835,11 @@ hipError_t launch_decode(int a8, const DecArgs &a, hipStream_t s, hipEvent_t ev_
   if (a8) hipLaunchKernelGGL(k_dec_gemm2_a8, g2, dim3(kDecG2WavesA8 * 64), lds2, s, a);
   else {
     const int f0 = a.tier[0].fmt, f1 = a.n_tiers > 1 ? a.tier[1].fmt : f0;
-    const size_t lds = (size_t)dec2_hb_bytes(a.R, a.N);
-    if (f0 == W_NVFP4 && f1 == W_NVFP4) hipLaunchKernelGGL(k_dec_gemm2_a16r<W_NVFP4>, g2, dim3(kDecG2WavesA8 * 64), lds, s, a);
-    else if (f0 == W_NF3 && f1 == W_NF3) hipLaunchKernelGGL(k_dec_gemm2_a16r<W_NF3>, g2, dim3(kDecG2WavesA8 * 64), lds, s, a);
-    else hipLaunchKernelGGL(k_dec_gemm2_a16r<0>, g2, dim3(kDecG2WavesA8 * 64), lds, s, a);
+    const dim3 g2h(a.K / 16 * dec2_a16_halves(a.N));
+    const size_t lds = (size_t)dec2_hb_bytes(a.R, min(dec2_a16_cols0(a.N), a.N));
+    if (f0 == W_NVFP4 && f1 == W_NVFP4) hipLaunchKernelGGL(k_dec_gemm2_a16r<W_NVFP4>, g2h, dim3(kDecG2WavesA8 * 64), lds, s, a);
+    else if (f0 == W_NF3 && f1 == W_NF3) hipLaunchKernelGGL(k_dec_gemm2_a16r<W_NF3>, g2h, dim3(kDecG2WavesA8 * 64), lds, s, a);
+    else hipLaunchKernelGGL(k_dec_gemm2_a16r<0>, g2h, dim3(kDecG2WavesA8 * 64), lds, s, a);
   }
   return hipGetLastError();
 }

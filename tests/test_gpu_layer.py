@@ -55,6 +55,12 @@ SMALL = {
                                                           limit=7.0, fmt=I.FMT_MXFP4, e8m0_exp=(-9, -5)), seed=9),
     "nf3_decode": lambda: I.make_problem(I.Config("nf3_decode", T=5, E=40, K=512, N=96, topk=7, limit=None,
                                                   fmt=I.FMT_NF3), seed=10),
+    # decode down GEMM split over two blocks per output tile by halves of the k-tiles: uneven halves
+    # (256 + 96 columns, 128 + 32 columns), the second ending in a partial k-tile
+    "nf3_decode_n352": lambda: I.make_problem(I.Config("nf3_decode_n352", T=6, E=24, K=512, N=352, topk=5,
+                                                       limit=None, fmt=I.FMT_NF3), seed=11),
+    "nvfp4_decode_n160": lambda: I.make_problem(I.Config("nvfp4_decode_n160", T=12, E=20, K=256, N=160, topk=3,
+                                                         limit=None, fmt=I.FMT_NVFP4), seed=12),
     # W4A8 batches on the prefill sequence (pinned in layer(); N % 64 == 0): 64-route tiles streamed through
     # the LDS ring; Zipf-skewed loads give full, ragged and single-tile experts, and
     # N % 128 == 64 leaves a half k-tile in the down GEMM
@@ -106,7 +112,7 @@ def _sample_rows(prob, n, seed=0):
 
 @pytest.mark.parametrize("name", ["tiny", "mxfp4_ragged", "nvfp4_small", "nf3_small", "hybrid_small",
                                   "nvfp4_clamped", "hybrid_decode", "decode_many_routes", "nf3_decode",
-                                  "prefill_small", "prefill_narrow", "nvfp4_prefill_small", "nf3_prefill_small",
+                                  "nf3_decode_n352", "nvfp4_decode_n160", "prefill_small", "prefill_narrow", "nvfp4_prefill_small", "nf3_prefill_small",
                                   "hybrid_prefill_small", "prefill_n320", "prefill_n768", "nvfp4_prefill_n320",
                                   "nf3_prefill_n640"])
 @pytest.mark.parametrize("deterministic", [False, True])
@@ -115,6 +121,13 @@ def test_small_layers_all_rows(name, deterministic):
     out = L.run(deterministic=deterministic)
     acc, _ = O.moe_problem(L.prob)
     assert_rows_match(out, acc, label=f"{name} det={deterministic}")
+
+
+@pytest.mark.parametrize("name", ["hybrid_decode", "nf3_decode", "nf3_decode_n352", "nvfp4_decode_n160",
+                                  "decode_many_routes"])
+def test_decode_cases_take_the_decode_sequence(name):
+    L = layer(name)
+    assert L.plan.sequence(L.prob.cfg.T) == M.SEQ_DECODE
 
 
 @pytest.mark.parametrize("deterministic", [False, True])
@@ -137,7 +150,8 @@ def test_full_size_sampled_rows(name, nrows, deterministic):
     assert_rows_match(out, acc, rows=rows, label=f"{name} det={deterministic}")
 
 
-@pytest.mark.parametrize("name", ["decode", "hybrid_small", "prefill", "hybrid_decode"])
+@pytest.mark.parametrize("name", ["decode", "hybrid_small", "prefill", "hybrid_decode", "nf3_decode_n352",
+                                  "nvfp4_decode"])
 def test_deterministic_bit_stable(name):
     L = layer(name)
     outs = [L.run(deterministic=True).view(torch.int16).clone() for _ in range(3)]
