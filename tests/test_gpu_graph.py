@@ -14,13 +14,17 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("deterministic", [True, False])
-@pytest.mark.parametrize("name", ["decode_small", "nvfp4_small"])
+@pytest.mark.parametrize("name", ["decode_small", "nvfp4_small", "nvfp4_split"])
 def test_graph_replays_match_eager(name, deterministic):
     if name == "decode_small":
         cfg = I.Config("decode_small", T=8, E=64, K=1024, N=192, topk=6, limit=7.0, fmt=I.FMT_MXFP4,
                        pad_rows=2, e8m0_exp=(-8, -4))
-    else:
+    elif name == "nvfp4_small":
         cfg = I.Config("nvfp4_small", T=8, E=32, K=512, N=128, topk=8, limit=None, fmt=I.FMT_NVFP4)
+    else:
+        # two k-tiles: the down GEMM's two blocks per output tile meet through counters and
+        # accumulators that the up/gate kernel clears on every replay
+        cfg = I.Config("nvfp4_split", T=8, E=32, K=512, N=256, topk=8, limit=None, fmt=I.FMT_NVFP4)
     prob = I.make_problem(cfg, seed=11)
     L = DeviceLayer(prob)
     x = dev(prob.x, torch.bfloat16)
