@@ -669,7 +669,7 @@ struct TuneBuffers {
   }
 };
 
-std::string geometry_key(const moe_plan_s *p) {
+extern "C++" std::string geometry_key(const moe_plan_s *p) {
   char buf[128];
   snprintf(buf, sizeof buf, "E=%d K=%d N=%d topk=%d afmt=%d max_tokens=%d", p->E, p->K, p->N, p->topk, p->afmt,
            p->max_tokens);
