@@ -53,6 +53,8 @@ struct PfStage {
 struct __attribute__((aligned(16))) PfLds {
   PfStage st[kPfStages];
 };
+// the deterministic combine stages 4 waves x 16 routes x (32 Q + 16) bytes in stage 0
+static_assert(sizeof(PfStage) >= 4 * 16 * (32 * kPfQ + 16), "combine staging fits one ring stage");
 
 // Wait until at most `stages` ring stages issued by this wave are in flight.
 __device__ __forceinline__ void wait_stages(int stages) {
@@ -284,32 +286,54 @@ __device__ __forceinline__ void zero_acc(v4f (*acc)[CB]) {
 // Down-GEMM combine from accumulators in the swapped layout: acc[q][cb][i] is
 // route 32 wc + 16 cb + 4 g + i (tile row; cb < CB), output column col + 16 q; s_r, s_w
 // hold each tile row's route and its router weight (times the expert's global
-// scale).  Deterministic mode writes bf16 route-buffer rows (lanes c, c ^ 1
-// swap one value so each stores two adjacent columns of one route); atomic mode
-// adds fp32 into the token accumulator, 4 routes x 16 consecutive columns per
-// instruction.
+// scale).  Deterministic mode writes bf16 route-buffer rows through LDS
+// (pf_store_rb; wc = 0); atomic mode adds fp32 into the token accumulator, 4
+// routes x 16 consecutive columns per instruction.
+//
+// The deterministic combine through LDS (lds: 16 x (32 Q + 16) bytes per
+// wave, free after the k-loop's last barrier): for each block of 16 routes the
+// wave stages its slice (16 Q columns, bf16, router weight applied) in its
+// own region and writes it back as 16-byte chunks, whole 32 Q-byte row
+// segments per route, in a quarter of the store instructions that writing the
+// 4-byte pairs directly takes (each of those covers eight rows 32 bytes apart).
+// A wave's LDS reads and writes are done in order, so no wait or barrier is
+// needed between the two phases or before the next block overwrites them.
+template <int Q, int CB>
+__device__ __forceinline__ void pf_store_rb(const GemmArgs &a, const PfWork &wk, v4f (*acc)[CB], const int *s_r,
+                                            const float *s_w, size_t col0, int c, int g, uint8_t *lds) {
+  constexpr int RB = 32 * Q, RS = RB + 16, CH = RB / 16;   // row bytes, LDS row stride, 16-byte chunks a row
+  const int l = threadIdx.x & 63;
+  uint8_t *lw = lds + (threadIdx.x >> 6) * 16 * RS;
+  const bool odd = c & 1;   // lanes c, c ^ 1 swap one value: each then holds two adjacent columns of one route
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) {
+#pragma unroll
+    for (int ip = 0; ip < 2; ip++) {
+      const int rl = 4 * g + 2 * ip + (odd ? 1 : 0), row = 16 * cb + rl;
+      const float wgt = row < wk.rows ? s_w[row] : 0.f;
+#pragma unroll
+      for (int q = 0; q < Q; q++) {
+        const float mine = acc[q][cb][2 * ip + (odd ? 1 : 0)], give = acc[q][cb][2 * ip + (odd ? 0 : 1)];
+        const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
+        const float lo = odd ? got : mine, hi = odd ? mine : got;
+        *(uint32_t *)(lw + rl * RS + 2 * ((c & ~1) + 16 * q)) = pack_bf16x2(wgt * lo, wgt * hi);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < Q / 2; j++) {
+      const int idx = l + 64 * j, rl = idx / CH, ch = idx - rl * CH, row = 16 * cb + rl;
+      const v4i v = *(const v4i *)(lw + rl * RS + 16 * ch);
+      if (row < wk.rows) *(v4i *)(a.rb + (size_t)s_r[row] * a.K + col0 + 8 * ch) = v;
+    }
+  }
+}
+
 template <int Q, int CB>
 __device__ __forceinline__ void pf_combine(const GemmArgs &a, const PfWork &wk, v4f (*acc)[CB], const int *s_r,
-                                           const float *s_w, size_t col, int wc, int c, int g) {
+                                           const float *s_w, size_t col, int wc, int c, int g, uint8_t *lds) {
   const int K = a.K;
   if (a.deterministic) {
-    const bool odd = c & 1;
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-      for (int ip = 0; ip < 2; ip++) {
-        const int row = 32 * wc + 16 * cb + 4 * g + 2 * ip + (odd ? 1 : 0);
-        const bool ok = row < wk.rows;
-        const int r = ok ? s_r[row] : 0;
-        const float wgt = ok ? s_w[row] : 0.f;
-#pragma unroll
-        for (int q = 0; q < Q; q++) {
-          const float mine = acc[q][cb][2 * ip + (odd ? 1 : 0)], give = acc[q][cb][2 * ip + (odd ? 0 : 1)];
-          const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
-          const float lo = odd ? got : mine, hi = odd ? mine : got;
-          if (ok) *(uint32_t *)(a.rb + (size_t)r * K + col + 16 * q - (odd ? 1 : 0)) = pack_bf16x2(wgt * lo, wgt * hi);
-        }
-      }
+    pf_store_rb<Q, CB>(a, wk, acc, s_r, s_w, col - c, c, g, lds);
   } else {
 #pragma unroll
     for (int cb = 0; cb < CB; cb++)
@@ -433,9 +457,9 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8(GemmArgs a) {
   v4f acc[kPfQ][4];
   zero_acc<kPfQ, 4>(acc);
   pf_kloop<true>(L, g2.src, wu, acc);
-  __syncthreads();   // s_r / s_w visible
+  __syncthreads();   // s_r / s_w visible; every wave is done with the ring's LDS
   // acc[q][cb][i]: route 16 cb + 4 g + i, output column 256 ob + 64 w + 16 q + c
-  pf_combine<kPfQ, 4>(a, g2.wk, acc, s_r, s_w, (size_t)256 * g2.ob + 64 * w + c, 0, c, g);
+  pf_combine<kPfQ, 4>(a, g2.wk, acc, s_r, s_w, (size_t)256 * g2.ob + 64 * w + c, 0, c, g, (uint8_t *)&L);
 }
 
 // The same for a short reduction (N <= 128 NKT): every k-tile's weights and
@@ -487,8 +511,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8_short(GemmArgs a) {
     else pf_mma<true, false>(wt[kt], b, sb, kt, src.kbytes, l, acc);
     __builtin_amdgcn_s_setprio(0);
   }
-  __syncthreads();   // s_r / s_w visible
-  pf_combine<kPfQ, 4>(a, g2.wk, acc, s_r, s_w, (size_t)256 * g2.ob + 64 * w + c, 0, c, g);
+  __syncthreads();   // s_r / s_w visible; every wave is done with the ring's LDS
+  pf_combine<kPfQ, 4>(a, g2.wk, acc, s_r, s_w, (size_t)256 * g2.ob + 64 * w + c, 0, c, g, (uint8_t *)&L);
 }
 
 static int pf_grid(int grid_tiles, int nsub) { return (grid_tiles * nsub + 7) / 8 * 8; }
@@ -905,9 +929,9 @@ __device__ __forceinline__ void pf16_gemm2_body(const GemmArgs &a, const PfWork 
 #pragma unroll
     for (int cb = 0; cb < 4; cb++) acc[q][cb] = v4f{0.f, 0.f, 0.f, 0.f};
   pf16_kloop<WF, true>(L, src, wu, acc);
-  __syncthreads();   // s_r / s_w visible
+  __syncthreads();   // s_r / s_w visible; every wave is done with the ring's LDS
   // acc[q][cb][i]: route 16 cb + 4 g + i, output column 128 ob + 32 w + 16 q + c
-  pf_combine<2, 4>(a, wk, acc, s_r, s_w, (size_t)128 * ob + 32 * w + c, 0, c, g);
+  pf_combine<2, 4>(a, wk, acc, s_r, s_w, (size_t)128 * ob + 32 * w + c, 0, c, g, (uint8_t *)&L);
 }
 
 template <int WF>
