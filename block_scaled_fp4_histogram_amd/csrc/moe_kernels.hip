@@ -108,18 +108,11 @@ __device__ void route_side_work(const RouteArgs &a, int sb) {
     const long nblk = (long)a.T * (a.K / 32);
     for (long i = i0; i < nblk; i += stride) {
       const v4i *src = (const v4i *)(a.x + i * 32);
-      float v[32];
+      v4i x4[4];
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const v4i w = src[q];
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-          v[8 * q + 2 * d] = bf16_to_f32((uint32_t)w[d] & 0xFFFFu);
-          v[8 * q + 2 * d + 1] = bf16_to_f32((uint32_t)w[d] >> 16);
-        }
-      }
+      for (int q = 0; q < 4; q++) x4[q] = src[q];
       uint32_t codes[8];
-      const uint32_t s = quant_block32(v, codes);
+      const uint32_t s = quant_block32_bf16(x4, codes);   // the decode path's quantiser, bit for bit
       v4i *dst = (v4i *)(a.xq + i * 32);
       dst[0] = v4i{(int)codes[0], (int)codes[1], (int)codes[2], (int)codes[3]};
       dst[1] = v4i{(int)codes[4], (int)codes[5], (int)codes[6], (int)codes[7]};
@@ -286,13 +279,14 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
 
 // ------------------------------------------------------------ quantisers
 
+// The MXFP8 quantiser every bf16 activation path runs (quant_block32_bf16).
 __global__ __launch_bounds__(256) void k_quant_bf16(const uint16_t *x, long nblk, uint8_t *q, uint8_t *sc) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= nblk) return;
-  float v[32];
-  for (int j = 0; j < 32; j++) v[j] = bf16_to_f32(x[i * 32 + j]);
+  v4i x4[4];
+  for (int j = 0; j < 4; j++) x4[j] = ((const v4i *)(x + i * 32))[j];
   uint32_t codes[8];
-  sc[i] = (uint8_t)quant_block32(v, codes);
+  sc[i] = (uint8_t)quant_block32_bf16(x4, codes);
   for (int j = 0; j < 8; j++) ((uint32_t *)(q + i * 32))[j] = codes[j];
 }
 

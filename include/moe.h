@@ -231,7 +231,10 @@ int moe_debug_route(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const i
                     int32_t *inv, void *stream);
 
 /* MXFP8 quantiser alone: rows x cols (cols % 32 == 0) of bf16 or fp32 ->
- * E4M3 codes u8 [rows, cols] + E8M0 scales u8 [rows, cols/32]. */
+ * E4M3 codes u8 [rows, cols] + E8M0 scales u8 [rows, cols/32].  The bf16 one
+ * runs the block quantiser every bf16-activation path of moe_run uses (x in
+ * the route launch and in the decode up/gate kernel); the fp32 one the
+ * requantiser's arithmetic on the intermediate. */
 int moe_debug_quant_mxfp8_bf16(const void *x, int rows, int cols, uint8_t *q, uint8_t *scales, void *stream);
 int moe_debug_quant_mxfp8_f32(const float *h, int rows, int cols, uint8_t *q, uint8_t *scales, void *stream);
 

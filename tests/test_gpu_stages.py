@@ -42,6 +42,19 @@ def _hard_f32(rows, cols, seed):
     return v
 
 
+def test_quant_bf16_hard_and_full_size():
+    """The bf16 quantiser (the one every bf16-activation path runs, decode included) on blocks
+    with exact E4M3 ties, saturating blocks, zeros and many binades, then on the prefill
+    workload's whole activation matrix (4096 x 7168)."""
+    hard = torch.from_numpy(_hard_f32(48, 512, seed=7)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for x in (hard, I.make_x(4096, 7168, seed=0)):
+        q, s = M.debug_quant_mxfp8(dev(x, torch.bfloat16))
+        torch.cuda.synchronize()
+        qo, so = O.mxfp8_quantize_bf16(x)
+        assert np.array_equal(s.cpu().numpy(), so)
+        assert np.array_equal(q.cpu().numpy(), qo)
+
+
 @pytest.mark.parametrize("rows,cols", [(16, 576), (64, 512), (3, 96)])
 def test_quant_f32_bitexact(rows, cols):
     v = _hard_f32(rows, cols, seed=cols)
