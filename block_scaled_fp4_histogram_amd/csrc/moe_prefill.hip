@@ -16,13 +16,14 @@
 //
 // Blocks are numbered XCD-major: the hardware hands workgroup b to XCD b % 8,
 // so logical work item (b % 8) * per + b / 8 puts a contiguous run of items on
-// each XCD, in order.  Both W4A8 GEMMs order items tile-major: the column
+// each XCD, in order.  All prefill GEMMs order items tile-major: the column
 // blocks of one tile run together on one XCD and share its activation rows in
 // L2, and an expert's weights stay in L2 across its consecutive tiles.  (The
 // up/gate GEMM ran column-block-major first, all tiles of an expert against
 // one weight slab at once; its 64 resident blocks per XCD then each streamed
 // private activation rows, about 530 KB of L2 fills per k-step against about
-// 190 KB tile-major, and it measured 3 % slower.)
+// 190 KB tile-major, and it measured 3 % slower; the W4A16 / W3A16 up/gate
+// GEMM, whose bf16 activations are twice the bytes, 1-2 % slower.)
 //
 //   k_pf_gemm1_a8  items (tile, 128-column intermediate block = 8 up and 8
 //                  gate row tiles): up/gate GEMMs over K, clamped SwiGLU and
@@ -881,7 +882,7 @@ __device__ __forceinline__ void pf16_gemm1_body(const GemmArgs &a, const PfWork 
 template <int WF>
 __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
   __shared__ Pf16Lds L;
-  const PfWork wk = pf_work(a, a.N / 64, true);
+  const PfWork wk = pf_work(a, a.N / 64, false);
   if (!wk.valid) return;
   pf16_gemm1_body<WF>(a, wk, pf_tier(a, 0), L);
 }
@@ -890,7 +891,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
 __global__ __launch_bounds__(256) void k_pf_gemm1_a16_tiers(GemmArgs a) {
   __shared__ Pf16Lds L;
   int tier = 0;
-  const PfWork wk = pf_work_tiers(a, a.N / 64, true, &tier);
+  const PfWork wk = pf_work_tiers(a, a.N / 64, false, &tier);
   if (!wk.valid) return;
   const PfTier T = pf_tier(a, tier);
   if ((tier ? a.fmt_b : a.fmt_a) == W_NVFP4) pf16_gemm1_body<W_NVFP4>(a, wk, T, L);
