@@ -201,6 +201,8 @@ int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const ui
   da.groups = (moe::DecGroups *)(scratch + L.cnt);   // the planner's count table is free on this path
   da.dpart = L.dpart ? (float *)(scratch + L.dpart) : nullptr;
   da.dcnt = L.dcnt ? (int *)(scratch + L.dcnt) : nullptr;
+  if (p->afmt != MOE_A_MXFP8 && moe::dec2_a16_halves(p->N) == 2 && (!da.dpart || !da.dcnt))
+    return fail(MOE_EINVAL, "decode down GEMM: the scratch layout lacks its per-tile accumulators (capacity %d)", T);
   if (ev) {
     HIP_TRY(hipEventRecord(ev[0], s));
     HIP_TRY(hipEventRecord(ev[1], s));

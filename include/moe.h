@@ -137,7 +137,13 @@ void moe_experts_destroy(moe_experts_t experts);
  *   deterministic   0: per-route results are added into an fp32 accumulator
  *                   with atomics (run-to-run order may vary);
  *                   1: per-slot route buffer + fixed-order top-k sum,
- *                   bit-stable run to run (moe_b12x_next.py, DETERMINISTIC)
+ *                   bit-stable run to run (moe_b12x_next.py, DETERMINISTIC).
+ *                   Decode-size batches (<= 16 tokens, <= 64 routes) run two
+ *                   kernels that fold each token's slots in slot order in
+ *                   either mode (bit-stable); with 16-bit activations the down
+ *                   GEMM adds two halves of each output tile into a zeroed
+ *                   fp32 accumulator with atomics, which is order-independent
+ *                   for two terms, so that stays bit-stable too.
  *   scratch         device buffer of >= moe_scratch_bytes(plan, T, deterministic)
  * Stream-ordered, no allocation, no synchronisation.
  */
