@@ -69,7 +69,89 @@ def row_errors(got, ref):
     return l2, mx
 
 
-def assert_rows_match(got_bf16, acc, rows=None, label=""):
+def _e4m3_grid():
+    import oracle as O
+    return np.array([O.e4m3(c) for c in range(127)])
+
+
+def _tie_flips(prob, t, fp32_ulps=1.0):
+    """Intermediate codes of token t that may round either way.
+
+    A W4A8 layer requantises each expert's SwiGLU output h to MXFP8 before the down
+    projection. The up/gate sums behind h are exact only up to rounding order (the
+    oracle sums in float64, the kernels in float32 on the matrix cores), so where
+    h * 2^-E lies within that rounding error of the midpoint between two E4M3 codes
+    both codes are correct. Returns, per such element, the change in the token's
+    output row [K] that taking the other code makes: router weight * (other code -
+    oracle code) * 2^E * the down projection's column."""
+    import oracle as O
+    c = prob.cfg
+    if len(prob.tiers) != 1 or prob.tiers[0].fmt != I.FMT_MXFP4:
+        return []
+    tier = prob.tiers[0]
+    w = tier.weights
+    grid = _e4m3_grid()
+    q, s = O.mxfp8_quantize_bf16(prob.x[t:t + 1])
+    xh = grid[q[0] & 0x7F] * np.where(q[0] & 0x80, -1.0, 1.0) * np.array(
+        [O.e8m0(int(s[0, k // 32])) for k in range(c.K)])
+    flips = []
+    for j in range(c.topk):
+        e = int(prob.ids[t, j])
+        if e < 0:
+            continue
+        w13 = O.dequant(tier.fmt, w["w13"][e], w["s13"][e], c.K)
+        up, gate = w13[:c.N] @ xh, w13[c.N:] @ xh
+        # worst-case float32 summation error of each dot product (K terms)
+        eps = fp32_ulps * c.K * 2.0 ** -24
+        dup, dgate = eps * (np.abs(w13[:c.N]) @ np.abs(xh)), eps * (np.abs(w13[c.N:]) @ np.abs(xh))
+        if c.limit is not None:
+            gate, up = np.minimum(gate, c.limit), np.clip(up, -c.limit, c.limit)
+        sig = 1.0 / (1.0 + np.exp(-gate))
+        h = gate * sig * up
+        dh = np.abs(sig * (1 + gate * (1 - sig)) * up) * dgate + np.abs(gate * sig) * dup + 1e-6 * np.abs(h)
+        w2 = None
+        for b in range(0, c.N, 32):
+            amax = np.abs(h[b:b + 32]).max()
+            if amax == 0:
+                continue
+            E = int(np.floor(np.log2(amax))) - 8
+            for n in range(b, b + 32):
+                v = abs(h[n]) * 2.0 ** -E
+                i = int(np.searchsorted(grid, v))
+                if i == 0 or i >= len(grid):
+                    continue
+                lo, hi = grid[i - 1], grid[i]
+                mid = 0.5 * (lo + hi)
+                if abs(v - mid) > dh[n] * 2.0 ** -E:
+                    continue
+                # the oracle's code is the nearest (ties to even); the other is across mid
+                took, other = (lo, hi) if (v < mid or (v == mid and (i - 1) % 2 == 0)) else (hi, lo)
+                if w2 is None:
+                    w2 = O.dequant(tier.fmt, w["w2"][e], w["s2"][e], c.N)
+                step = np.sign(h[n]) * (other - took) * 2.0 ** E
+                flips.append(float(prob.wts[t, j]) * step * w2[:, n])
+    return flips
+
+
+def _explained_by_ties(prob, t, got_row, acc_row):
+    # flips far below the row's tolerance are absorbed by it; try subsets of the rest
+    floor = 0.1 * REL_L2 * np.linalg.norm(acc_row)
+    flips = [f for f in _tie_flips(prob, t) if np.linalg.norm(f) > floor]
+    if not flips or len(flips) > 10:
+        return False
+    for mask in range(1, 1 << len(flips)):
+        ref = acc_row + sum(f for i, f in enumerate(flips) if mask >> i & 1)
+        l2, mx = row_errors(got_row[None], ref[None])
+        if l2[0] <= REL_L2 and mx[0] <= REL_MAXABS:
+            return True
+    return False
+
+
+def assert_rows_match(got_bf16, acc, rows=None, label="", prob=None):
+    """Every row within REL_L2 / REL_MAXABS of the oracle. With prob given (a W4A8
+    layer), a row outside them still passes when taking the other of two equally
+    correct intermediate codes for elements that sit on a rounding midpoint (see
+    _tie_flips) brings it inside."""
     got = bf16_to_f64(got_bf16)
     if rows is not None:
         got = got[rows]
@@ -77,6 +159,9 @@ def assert_rows_match(got_bf16, acc, rows=None, label=""):
     zero_ref = ~np.any(acc != 0, axis=1)
     assert np.all(got[zero_ref] == 0), f"{label}: rows with no valid slot must be exactly zero"
     bad = np.flatnonzero((l2 > REL_L2) | (mx > REL_MAXABS))
+    if prob is not None and bad.size:
+        toks = np.arange(prob.cfg.T) if rows is None else np.asarray(rows)
+        bad = np.array([r for r in bad if not _explained_by_ties(prob, int(toks[r]), got[r], acc[r])], dtype=int)
     assert bad.size == 0, (f"{label}: {bad.size} rows out of tolerance; worst rel-L2 {l2.max():.3e} "
                            f"rel-maxabs {mx.max():.3e}; first bad rows {bad[:8]}")
     return float(l2.max()), float(mx.max())

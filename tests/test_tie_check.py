@@ -1,0 +1,52 @@
+"""The GPU tests' row check for W4A8 layers lets a row differ from the oracle by a
+whole E4M3 step of an intermediate element only where that element sits on a
+rounding midpoint (both codes correct up to summation order). These cases pin that
+it accepts such a flip and nothing else, with the oracle alone."""
+import numpy as np
+import torch
+
+import oracle as O
+from block_scaled_fp4_histogram_amd import inputs as I
+
+from gpu_util import _tie_flips, assert_rows_match
+
+# T=520 E=20 K=512 N=128 top-4 MXFP4: token 148's first slot (expert 6) has an
+# intermediate element whose scaled value is within 1.2e-6 of the midpoint between
+# the E4M3 codes 352 and 384
+CFG = I.Config("tie", T=520, E=20, K=512, N=128, topk=4, limit=None, fmt=I.FMT_MXFP4, pad_rows=1,
+               e8m0_exp=(-7, -3))
+SEED = 38985
+ROW = 148
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def test_midpoint_flip_is_accepted_and_other_errors_are_not():
+    prob = I.make_problem(CFG, seed=SEED)
+    acc, _ = O.moe_problem(prob, rows=[ROW])
+    big = [f for f in _tie_flips(prob, ROW) if np.linalg.norm(f) > 1e-2 * np.linalg.norm(acc[0])]
+    assert len(big) == 1 and np.linalg.norm(big[0]) > 0.03 * np.linalg.norm(acc[0])
+    flipped = acc + big[0]
+    assert_rows_match(_bf16(flipped), acc, rows=None, label="flip", prob=_one_row(prob, ROW))
+    try:
+        assert_rows_match(_bf16(flipped), acc, label="flip without prob")
+    except AssertionError:
+        pass
+    else:
+        raise AssertionError("the flip alone must be outside the plain tolerance")
+    d = np.random.default_rng(0).standard_normal(acc.shape)
+    for wrong in (acc + d * np.linalg.norm(big[0]) / np.linalg.norm(d), acc * 1.04, acc - big[0]):
+        try:
+            assert_rows_match(_bf16(wrong), acc, label="planted", prob=_one_row(prob, ROW))
+        except AssertionError:
+            continue
+        raise AssertionError("an error that is not a midpoint flip passed")
+
+
+def _one_row(prob, r):
+    """The problem restricted to token r (the check maps result rows to tokens)."""
+    import dataclasses
+    cfg = dataclasses.replace(prob.cfg, T=1)
+    return dataclasses.replace(prob, cfg=cfg, x=prob.x[r:r + 1], ids=prob.ids[r:r + 1], wts=prob.wts[r:r + 1])
