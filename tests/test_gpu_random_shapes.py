@@ -4,8 +4,10 @@ Each case draws the expert count, hidden and intermediate sizes (within the plan
 constraints: K % 256 == 0, N % 32 == 0), top-k, weight format (MXFP4, NVFP4, NF3 or
 two tiers), clamp and a batch size that lands on the decode (<= 16 tokens and <= 64
 routes), 16-route or 64-route launch sequence, with and without padding rows, and
-runs both combine modes. The list is fixed by its seed, so a failure names a
-reproducible case."""
+runs both combine modes. The list is fixed by its two seeds, so a failure names a
+reproducible case. Rows are compared with the oracle under the same rule as every
+other GPU test, including its allowance for intermediate codes on a rounding
+midpoint."""
 import numpy as np
 import pytest
 
@@ -36,7 +38,7 @@ def _cases(n=24, seed=2026):
             if kind == "decode":
                 topk = min(topk, 64 // T)
         hybrid = fmt == "hybrid"
-        cfg = I.Config(f"rand{i}_{kind}", T=T, E=E, K=K, N=N, topk=topk,
+        cfg = I.Config(f"s{seed}_{i}_{kind}", T=T, E=E, K=K, N=N, topk=topk,
                        limit=[None, 7.0, 30.0][int(rng.integers(0, 3))],
                        fmt=I.FMT_NVFP4 if hybrid else fmt,
                        pad_rows=int(rng.integers(0, min(2, T - 1) + 1)) if T > 1 else 0,
@@ -46,7 +48,7 @@ def _cases(n=24, seed=2026):
     return out
 
 
-CASES = _cases()
+CASES = _cases(24, 2026) + _cases(24, 7)
 
 
 @pytest.mark.parametrize("case", range(len(CASES)), ids=[c.name for c, _ in CASES])
