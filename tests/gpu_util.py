@@ -97,8 +97,12 @@ def _tie_flips(prob, t, fp32_ulps=1.0):
     flips = []
     for j in range(c.topk):
         e = int(prob.ids[t, j])
-        if e < 0:
+        if not 0 <= e < c.E:            # ids the layer skips
             continue
+        if tier.emap is not None:
+            e = int(tier.emap[e])
+            if e < 0:
+                continue
         w13 = O.dequant(tier.fmt, w["w13"][e], w["s13"][e], c.K)
         up, gate = w13[:c.N] @ xh, w13[c.N:] @ xh
         # worst-case float32 summation error of each dot product (K terms)

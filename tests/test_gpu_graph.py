@@ -52,5 +52,5 @@ def test_graph_replays_match_eager(name, deterministic):
         torch.cuda.synchronize()
         if deterministic:
             assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
-        assert_rows_match(out, acc, label=f"{name} replay {rep} det={deterministic}")
+        assert_rows_match(out, acc, label=f"{name} replay {rep} det={deterministic}", prob=prob)
         del junk

@@ -120,7 +120,7 @@ def test_small_layers_all_rows(name, deterministic):
     L = layer(name)
     out = L.run(deterministic=deterministic)
     acc, _ = O.moe_problem(L.prob)
-    assert_rows_match(out, acc, label=f"{name} det={deterministic}")
+    assert_rows_match(out, acc, label=f"{name} det={deterministic}", prob=L.prob)
 
 
 @pytest.mark.parametrize("name", ["hybrid_decode", "nf3_decode", "nf3_decode_n352", "nvfp4_decode_n160",
@@ -135,7 +135,7 @@ def test_decode_all_rows(deterministic):
     L = layer("decode")
     out = L.run(deterministic=deterministic)
     acc, _ = O.moe_problem(L.prob)
-    assert_rows_match(out, acc, label=f"decode det={deterministic}")
+    assert_rows_match(out, acc, label=f"decode det={deterministic}", prob=L.prob)
     assert torch.all(out[6:].view(torch.int16) == 0)   # the two padding rows
 
 
@@ -147,7 +147,7 @@ def test_full_size_sampled_rows(name, nrows, deterministic):
     out = L.run(deterministic=deterministic)
     rows = _sample_rows(L.prob, nrows)
     acc, _ = O.moe_problem(L.prob, rows=rows)
-    assert_rows_match(out, acc, rows=rows, label=f"{name} det={deterministic}")
+    assert_rows_match(out, acc, rows=rows, label=f"{name} det={deterministic}", prob=L.prob)
 
 
 @pytest.mark.parametrize("name", ["decode", "hybrid_small", "prefill", "hybrid_decode", "nf3_decode_n352",
@@ -168,11 +168,11 @@ def test_chunked_batch_matches_single_launch():
     out = chunked.run(deterministic=True)
     assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
     acc, _ = O.moe_problem(prob)
-    assert_rows_match(chunked.run(deterministic=False), acc, label="chunked atomic")
+    assert_rows_match(chunked.run(deterministic=False), acc, label="chunked atomic", prob=prob)
     # chunks small enough for the decode path (8 tokens x 3 slots)
     dec = DeviceLayer(SMALL["mxfp4_ragged"](), max_tokens=8)
     for det in (False, True):
-        assert_rows_match(dec.run(deterministic=det), acc, label=f"decode-size chunks det={det}")
+        assert_rows_match(dec.run(deterministic=det), acc, label=f"decode-size chunks det={det}", prob=prob)
 
 
 @pytest.mark.parametrize("name", ["mxfp4_ragged", "decode"])
@@ -190,7 +190,7 @@ def test_invalid_ids_and_zero_weights(name):
         out = L.run(ids=dev(ids), wts=dev(wts), deterministic=det)
         q = I.Problem(p.cfg, p.x, ids, wts, p.tiers)
         acc, _ = O.moe_problem(q)
-        assert_rows_match(out, acc, label=f"{name} invalid ids det={det}")
+        assert_rows_match(out, acc, label=f"{name} invalid ids det={det}", prob=q)
         assert torch.all(out[3].view(torch.int16) == 0)
 
 
@@ -202,8 +202,9 @@ def test_duplicate_ids_in_a_row(name):
     ids[:, -1] = p.ids[:, -1]
     for det in (False, True):
         out = L.run(ids=dev(ids), deterministic=det)
-        acc, _ = O.moe_problem(I.Problem(p.cfg, p.x, ids, p.wts, p.tiers))
-        assert_rows_match(out, acc, label=f"{name} duplicate ids det={det}")
+        q = I.Problem(p.cfg, p.x, ids, p.wts, p.tiers)
+        acc, _ = O.moe_problem(q)
+        assert_rows_match(out, acc, label=f"{name} duplicate ids det={det}", prob=q)
 
 
 def test_zero_tokens_is_noop_and_all_padding_batch():
@@ -288,7 +289,7 @@ def test_pinned_sequence(name, seq, deterministic):
     finally:
         L.plan.set_sequence(T, before)
     acc, _ = O.moe_problem(L.prob)
-    assert_rows_match(out, acc, label=f"{name} sequence {seq} det={deterministic}")
+    assert_rows_match(out, acc, label=f"{name} sequence {seq} det={deterministic}", prob=L.prob)
 
 
 def test_autotune_pins_the_fastest_sequence():
