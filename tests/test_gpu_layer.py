@@ -150,6 +150,21 @@ def test_full_size_sampled_rows(name, nrows, deterministic):
     assert_rows_match(out, acc, rows=rows, label=f"{name} det={deterministic}", prob=L.prob)
 
 
+@pytest.mark.parametrize("name", ["decode", "nvfp4_decode"])
+@pytest.mark.parametrize("T", [1, 2, 3, 5])
+def test_full_size_decode_smaller_batches(name, T):
+    """The full-size decode layers on batches of their first T tokens: each batch size
+    is its own capacity rung of the plan (the layer's weights and plan are shared)."""
+    L = layer(name)
+    p = L.prob
+    q = I.Problem(p.cfg, p.x[:T].copy(), p.ids[:T].copy(), p.wts[:T].copy(), p.tiers)
+    acc, _ = O.moe_problem(q)
+    for det in (False, True):
+        out = L.run(x=dev(q.x, torch.bfloat16), ids=dev(q.ids), wts=dev(q.wts), deterministic=det)
+        assert out.shape[0] == T
+        assert_rows_match(out, acc, label=f"{name} T={T} det={det}", prob=q)
+
+
 @pytest.mark.parametrize("name", ["decode", "hybrid_small", "prefill", "hybrid_decode", "nf3_decode_n352",
                                   "nvfp4_decode"])
 def test_deterministic_bit_stable(name):
