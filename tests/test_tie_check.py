@@ -50,3 +50,21 @@ def _one_row(prob, r):
     import dataclasses
     cfg = dataclasses.replace(prob.cfg, T=1)
     return dataclasses.replace(prob, cfg=cfg, x=prob.x[r:r + 1], ids=prob.ids[r:r + 1], wts=prob.wts[r:r + 1])
+
+
+def test_no_flips_for_16_bit_layers_or_ignored_ids():
+    """16-bit activation layers round h to bf16, whose steps stay inside the row
+    tolerance: no flips are offered. Ids the layer skips offer none either."""
+    nv = I.make_problem(I.Config("nv", T=3, E=6, K=256, N=64, topk=2, limit=None, fmt=I.FMT_NVFP4), seed=1)
+    assert all(_tie_flips(nv, t) == [] for t in range(3))
+    prob = I.make_problem(CFG, seed=SEED)
+    one = _one_row(prob, ROW)
+    assert len(_tie_flips(one, 0)) > 0
+    ids = one.ids.copy()
+    ids[0, :] = [-1, CFG.E, CFG.E + 5, np.iinfo(np.int32).min]
+    assert _tie_flips(dataclasses_replace(one, ids=ids), 0) == []
+
+
+def dataclasses_replace(prob, **kw):
+    import dataclasses
+    return dataclasses.replace(prob, **kw)
