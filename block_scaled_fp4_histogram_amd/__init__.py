@@ -45,16 +45,38 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def _need(t, name, dtype, device=True):
+def _need(t, name, dtype, device=True, shape=None, numel=None):
+    """Dtype, contiguity and device of a tensor the C ABI receives as a raw pointer,
+    and its shape or element count: the library cannot check those itself."""
     import torch
     if t is None:
         raise ValueError(f"{name} is required")
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if device and t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")
+
+
+def weight_bytes(weight_format: int, num_experts: int, K: int, N: int, w13_rows: Optional[int] = None):
+    """Bytes of (w13, s13, w2, s2) in the checkpoint layout of include/moe.h for
+    num_experts experts: w13 [E, 2N, K] and w2 [E, K, N] codes with their block scales."""
+    rows13 = 2 * N if w13_rows is None else w13_rows
+    if weight_format == W_MXFP4:
+        code, sblk = (lambda n: n // 2), 32
+    elif weight_format == W_NVFP4:
+        code, sblk = (lambda n: n // 2), 16
+    elif weight_format == W_NF3:
+        code, sblk = (lambda n: n // 8 * 3), 32
+    else:
+        raise ValueError(f"unknown weight format {weight_format}")
+    E = num_experts
+    return (E * rows13 * code(K), E * rows13 * (K // sblk), E * K * code(N), E * K * (N // sblk))
 
 
 class Plan:
@@ -68,7 +90,7 @@ class Plan:
         _check(L.moe_plan(E, K, N, top_k, lim, act_format, w13_layout, max_tokens, C.byref(h)))
         self.handle = h
         self.E, self.K, self.N, self.top_k = E, K, N, top_k
-        self.act_format, self.max_tokens = act_format, max_tokens
+        self.act_format, self.w13_layout, self.max_tokens = act_format, w13_layout, max_tokens
 
     def scratch_bytes(self, T: int, deterministic: bool = False) -> int:
         return _lib.load().moe_scratch_bytes(self.handle, T, int(bool(deterministic)))
@@ -91,7 +113,7 @@ class Plan:
         batch and pin the fastest; returns [len(tokens)][3] median microseconds of DECODE,
         GENERAL and PREFILL (NaN where a rung cannot take one)."""
         tok = [int(t) for t in tokens]
-        arr, keep = _tiers(tiers)
+        arr, keep = _tiers(tiers, self)
         ta = (C.c_int * len(tok))(*tok)
         us = (C.c_float * (3 * len(tok)))()
         _check(_lib.load().moe_plan_autotune(self.handle, arr, len(tiers), ta, len(tok), int(bool(deterministic)),
@@ -146,11 +168,13 @@ class Experts:
     def __init__(self, plan: Plan, weight_format: int, num_experts: int, w13, s13, w2, s2, g13=None, g2=None,
                  stream=None):
         import torch
-        for name, t in (("w13", w13), ("s13", s13), ("w2", w2), ("s2", s2)):
-            _need(t, name, torch.uint8)
-        for name, t in (("g13", g13), ("g2", g2)):
-            if t is not None:
-                _need(t, name, torch.float32)
+        sizes = weight_bytes(weight_format, num_experts, plan.K, plan.N)
+        for device in (False, True):   # every size first, then where the tensors live
+            for name, t, n in zip(("w13", "s13", "w2", "s2"), (w13, s13, w2, s2), sizes):
+                _need(t, name, torch.uint8, device, numel=n)
+            for name, t in (("g13", g13), ("g2", g2)):
+                if t is not None:
+                    _need(t, name, torch.float32, device, numel=num_experts)
         h = C.c_void_p()
         _check(_lib.load().moe_prepare_weights(plan.handle, weight_format, num_experts, _ptr(w13), _ptr(s13),
                                                _ptr(g13), _ptr(w2), _ptr(s2), _ptr(g2), _stream(stream),
@@ -175,14 +199,14 @@ class Experts:
             pass
 
 
-def _tiers(tiers):
+def _tiers(tiers, plan=None):
     arr = (_lib.MoeTier * len(tiers))()
     keep = []
     for i, t in enumerate(tiers):
         ex, emap = (t if isinstance(t, (tuple, list)) else (t, None))
         if emap is not None:
             import torch
-            _need(emap, "expert_map", torch.int32)
+            _need(emap, "expert_map", torch.int32, numel=None if plan is None else plan.E)
         keep.append(emap)
         arr[i] = _lib.MoeTier(ex.handle.value, _ptr(emap))
     return arr, keep
@@ -198,16 +222,21 @@ def run(plan: Plan, tiers: Sequence, x, topk_ids, topk_weights, out=None, determ
         scratch=None, stream=None):
     """The layer (moe_run). tiers: Experts, or (Experts, expert_map int32 [E]) pairs."""
     import torch
-    _need(x, "x", torch.bfloat16)
-    _need(topk_ids, "topk_ids", torch.int32)
-    _need(topk_weights, "topk_weights", torch.float32)
+    if x is None or x.dim() != 2:
+        raise ValueError("x must be a [T, K] tensor")
     T = x.shape[0]
+    for device in (False, True):   # every shape first, then where the tensors live
+        _need(x, "x", torch.bfloat16, device, shape=(T, plan.K))
+        _need(topk_ids, "topk_ids", torch.int32, device, shape=(T, plan.top_k))
+        _need(topk_weights, "topk_weights", torch.float32, device, shape=(T, plan.top_k))
+        if out is not None:
+            _need(out, "out", torch.bfloat16, device, shape=(T, plan.K))
     if out is None:
         out = torch.empty_like(x)
-    _need(out, "out", torch.bfloat16)
     if scratch is None:
         scratch = scratch_for(plan, T, deterministic, x.device)
-    arr, keep = _tiers(tiers)
+    _need(scratch, "scratch", torch.uint8)
+    arr, keep = _tiers(tiers, plan)
     _check(_lib.load().moe_run(plan.handle, arr, len(tiers), _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
                                _ptr(out), T, int(bool(deterministic)), _ptr(scratch), scratch.numel(),
                                _stream(stream)))
@@ -217,6 +246,8 @@ def run(plan: Plan, tiers: Sequence, x, topk_ids, topk_weights, out=None, determ
 def debug_route(plan: Plan, tiers: Sequence, topk_ids, scratch=None, stream=None):
     """Route planner alone. Returns (cnt [U], off [U+1], perm [off[U]], inv [T*k]) device tensors."""
     import torch
+    if topk_ids is None or topk_ids.dim() != 2 or topk_ids.shape[1] != plan.top_k:
+        raise ValueError(f"topk_ids must be a [T, {plan.top_k}] tensor")
     _need(topk_ids, "topk_ids", torch.int32)
     T, k = topk_ids.shape
     U = sum((t[0] if isinstance(t, (tuple, list)) else t).num_experts for t in tiers)
@@ -227,7 +258,7 @@ def debug_route(plan: Plan, tiers: Sequence, topk_ids, scratch=None, stream=None
     off = torch.empty(U + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
-    arr, keep = _tiers(tiers)
+    arr, keep = _tiers(tiers, plan)
     _check(_lib.load().moe_debug_route(plan.handle, arr, len(tiers), _ptr(topk_ids), T, _ptr(scratch),
                                        scratch.numel(), _ptr(cnt), _ptr(off), _ptr(perm), _ptr(inv),
                                        _stream(stream)))

@@ -129,10 +129,11 @@ Layout layout(const moe_plan_s *p, int cap, int deterministic) {
     L.hs = take(R * moe::hs_stride(p->N));
   } else {
     L.hb = take(2 * R * p->N);
-    if (cap <= moe::kDecodeMaxT) {   // the decode down GEMM's two halves per 16-row output tile
-      L.dpart = take((size_t)(p->K / 16) * 256 * sizeof(float));
-      L.dcnt = take(4 * (size_t)(p->K / 16));
-    }
+    // the decode down GEMM's two halves per 16-row output tile meet here: carved at
+    // every capacity, since the last chunk of a batch above the top capacity can be
+    // decode-sized whatever the capacity the arena was sized for
+    L.dpart = take((size_t)(p->K / 16) * 256 * sizeof(float));
+    L.dcnt = take(4 * (size_t)(p->K / 16));
   }
   if (deterministic) L.rb = take(2 * R * p->K);
   else L.acc = take(4 * (size_t)cap * p->K);

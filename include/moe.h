@@ -69,9 +69,10 @@ typedef struct moe_experts_s *moe_experts_t; /* one layer's (or tier's) prepared
 
 /* One group of experts taking part in a moe_run.  expert_map (device, int32
  * [E], may be NULL = identity) maps a global expert id to this tier's local
- * id, or -1 when the id belongs elsewhere (hybrid_loader.py: per-tier expert
- * maps, "translates global->local + drops -1").  A global id is served by the
- * first tier whose map accepts it. */
+ * id, or -1 when the id belongs elsewhere (hybrid_loader.py, the per-tier
+ * expert maps of the hybrid runtime: each tier sees only its own experts, under
+ * local ids, and skips the rest).  A global id is served by the first tier
+ * whose map accepts it. */
 typedef struct {
   moe_experts_t experts;
   const int32_t *expert_map;

@@ -17,6 +17,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 FMT_MXFP4, FMT_NVFP4, FMT_NF3 = 1, 2, 3
+# activation forms (orc_act): SwiGLU (limit clamps, OAI alpha / beta), SiTU, ReLU^2 without the gate multiply
+ACT_SWIGLU, ACT_SITU, ACT_RELU2_NO_MUL = 0, 1, 2
 
 
 class _Tier(C.Structure):
@@ -62,6 +64,13 @@ def lib():
                               C.c_void_p, C.c_void_p]
         L.orc_moe_ex.restype = C.c_int
         L.orc_moe_ex.argtypes = L.orc_moe.argtypes + [C.c_int, C.c_double, C.c_double]
+        L.orc_moe_act.restype = C.c_int
+        L.orc_moe_act.argtypes = L.orc_moe_ex.argtypes + [C.c_int]
+        L.orc_act.restype = C.c_double
+        L.orc_act.argtypes = [C.c_int, C.c_double, C.c_double, C.c_double, C.c_double, C.c_double]
+        L.orc_ep_remap.restype = C.c_int
+        L.orc_ep_remap.argtypes = [C.c_void_p, C.c_void_p, C.c_long, C.c_int, C.c_long, C.c_long,
+                                   C.c_void_p, C.c_void_p]
         L.orc_num_threads.restype = C.c_int
         _lib = L
     return _lib
@@ -102,6 +111,25 @@ def bf16_to_float(h: int) -> float:
 
 def bf16_from_float(d: float) -> int:
     return lib().orc_bf16_from_double(float(d))
+
+
+def act(kind: int, gate: float, up: float, limit=None, alpha: float = 1.0, beta: float = 0.0) -> float:
+    """The activation the layer applies to one (gate, up) pair (orc_act; ReLU^2 reads up only)."""
+    lim = math.nan if limit is None else float(limit)
+    return lib().orc_act(int(kind), float(gate), float(up), lim, float(alpha), float(beta))
+
+
+def ep_remap(ids: np.ndarray, w: np.ndarray, offset: int, num_local: int):
+    """Expert-parallel id remap of [T, k] ids / weights (sglang moe_b12x_next.py, ep_remap_reference):
+    returns (local ids int32 [T, k], weights float32 [T, k])."""
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float32)
+    T, k = ids.shape
+    oi = np.empty((T, k), np.int32)
+    ow = np.empty((T, k), np.float32)
+    if lib().orc_ep_remap(_p(ids), _p(w), T, k, int(offset), int(num_local), _p(oi), _p(ow)) != 0:
+        raise ValueError("bad remap arguments")
+    return oi, ow
 
 
 # ------------------------------------------------------------------ arrays
@@ -178,14 +206,16 @@ def route(ids: np.ndarray, E_global: int, tiers):
 
 def moe(E_global: int, K: int, N: int, topk: int, limit, tiers, x: np.ndarray, ids: np.ndarray,
         wts: np.ndarray, rows=None, gate_up: bool = False, weight_on_input: bool = False,
-        alpha: float = 1.0, beta: float = 0.0):
+        alpha: float = 1.0, beta: float = 0.0, act_kind: int = ACT_SWIGLU):
     """The layer for the listed token rows (all rows when None).  weight_on_input:
     each slot's router weight scales that slot's copy of the token before GEMM1 and
     its result enters the sum with weight 1 (vLLM "fused_moe/b12x" page,
     apply_router_weight_on_input; 16-bit activation formats only).  alpha, beta:
     the activation gate * sigmoid(alpha gate) * (up + beta) after the clamps
     (swigluoai's parameters on the same page, _swiglu_params; 1, 0 is SwiGLU;
-    other values 16-bit activation formats only).
+    other values 16-bit activation formats only).  act_kind: ACT_SITU or
+    ACT_RELU2_NO_MUL instead of the SwiGLU (no limit, alpha or beta; ReLU^2 reads a
+    w13 of N rows and runs with 16-bit activation formats only).
 
     Returns (acc float64 [n, K], out bf16-bits uint16 [n, K])."""
     x = _c(x, np.uint16)
@@ -198,20 +228,21 @@ def moe(E_global: int, K: int, N: int, topk: int, limit, tiers, x: np.ndarray, i
     out = np.empty((n, K), np.uint16)
     ta = _TierArgs(tiers)
     lim = math.nan if limit is None else float(limit)
-    rc = lib().orc_moe_ex(E_global, K, N, topk, lim, int(gate_up), len(tiers), C.addressof(ta.arr), _p(x),
-                          _p(ids), _p(wts), T, _p(rows_a), n, _p(acc), _p(out), int(bool(weight_on_input)),
-                          float(alpha), float(beta))
+    rc = lib().orc_moe_act(E_global, K, N, topk, lim, int(gate_up), len(tiers), C.addressof(ta.arr), _p(x),
+                           _p(ids), _p(wts), T, _p(rows_a), n, _p(acc), _p(out), int(bool(weight_on_input)),
+                           float(alpha), float(beta), int(act_kind))
     if rc != 0:
         raise ValueError("bad layer arguments")
     return acc, out
 
 
 def moe_problem(prob, rows=None, gate_up: bool = False, weight_on_input: bool = False, alpha: float = 1.0,
-                beta: float = 0.0):
+                beta: float = 0.0, act_kind: int = ACT_SWIGLU):
     """The layer for a block_scaled_fp4_histogram_amd.inputs.Problem."""
     c = prob.cfg
-    return moe(c.E, c.K, c.N, c.topk, c.limit, prob.tiers, prob.x, prob.ids, prob.wts, rows, gate_up,
-               weight_on_input, alpha, beta)
+    limit = c.limit if act_kind == ACT_SWIGLU else None
+    return moe(c.E, c.K, c.N, c.topk, limit, prob.tiers, prob.x, prob.ids, prob.wts, rows, gate_up,
+               weight_on_input, alpha, beta, act_kind)
 
 
 def num_threads() -> int:

@@ -32,6 +32,18 @@
  *    refuse that activation with quantised activations.  The activation's
  *    formula is not printed; this file takes gate * sigmoid(alpha gate) *
  *    (up + beta) after the clamps (alpha = 1, beta = 0 is the plain SwiGLU).
+ *  - SiTU and ReLU^2 without the gate multiply: the same page lists them among
+ *    the supported activations (_supports_activation; the W4A8 check allows
+ *    SiLU and SiTU only; the support check takes SiTU with beta 4 and linear
+ *    beta 25 only; _swiglu_params gives neither a limit).  Their formulas are
+ *    not printed.  This file takes SiTU as the SwiGLU with both branches
+ *    softly capped by tanh, silu(b tanh(gate / b)) * (bl tanh(up / bl)) with
+ *    b = 4, bl = 25, and ReLU^2 without the multiply as relu(z)^2 on a w13 of
+ *    N rows (no gate half).
+ *  - EP id remap (moe_b12x_next.py, ep_remap / ep_remap_reference): local id
+ *    = global id - offset when that lies in [0, num_local); every other slot
+ *    takes weight 0 and the row's lowest local id (else the batch's lowest,
+ *    else 0).
  *  - MXFP8 activations (E4M3 codes + E8M0 scale per 32): moe_b12x_next.py,
  *    module docstring ("in-kernel MXFP8 activations"); the scale rule is the
  *    OCP MX one, E = floor(log2 amax) - emax(E4M3 = 8), codes saturate.
@@ -275,11 +287,68 @@ long orc_route(const int32_t *ids, long T, int topk, int E_global, int n_tiers, 
   return nvalid;
 }
 
+/* ------------------------------------------------------------ activation */
+
+#define ORC_ACT_SWIGLU 0      /* silu(gate) * up after the limit clamps; alpha / beta: OAI form */
+#define ORC_ACT_SITU 1        /* silu(4 tanh(gate/4)) * 25 tanh(up/25) */
+#define ORC_ACT_RELU2_NO_MUL 2 /* relu(z)^2 on a w13 of N rows */
+
+/* The activation of one intermediate column.  SwiGLU: when limit is not NaN,
+   gate <- min(gate, limit) and up <- clamp(up, -limit, limit) first, then
+   gate * sigmoid(alpha gate) * (up + beta) (alpha = 1, beta = 0: silu(gate) * up).
+   SiTU: both branches softly capped, silu(4 tanh(gate/4)) * (25 tanh(up/25)).
+   ReLU^2 without the multiply: relu(up)^2 (gate unused). */
+double orc_act(int act, double gate, double up, double limit, double alpha, double beta) {
+  if (act == ORC_ACT_RELU2_NO_MUL) return up > 0.0 ? up * up : 0.0;
+  if (act == ORC_ACT_SITU) {
+    double g = 4.0 * tanh(gate / 4.0), u = 25.0 * tanh(up / 25.0);
+    return g / (1.0 + exp(-g)) * u;
+  }
+  if (!isnan(limit)) {
+    if (gate > limit) gate = limit;
+    if (up > limit) up = limit;
+    if (up < -limit) up = -limit;
+  }
+  return gate / (1.0 + exp(-alpha * gate)) * (up + beta);
+}
+
+/* ------------------------------------------------------------- EP remap */
+
+/* Expert-parallel id remap of one batch [T, k]: lid = id - offset.  A slot whose
+   lid lies in [0, num_local) keeps lid and its weight; every other slot (another
+   rank's expert, padding) gets weight 0 and a fill id: the lowest valid lid of
+   its row, else the lowest valid lid of the batch, else 0.  Ids are compared in
+   64-bit so that id - offset cannot wrap. */
+int orc_ep_remap(const int32_t *ids, const float *w, long T, int topk, long offset, long num_local,
+                 int32_t *out_ids, float *out_w) {
+  long t, j, best = -1;
+  if (T < 0 || topk < 1 || num_local < 1) return -1;
+  for (t = 0; t < T * topk; t++) {
+    long lid = (long)ids[t] - offset;
+    if (lid >= 0 && lid < num_local && (best < 0 || lid < best)) best = lid;
+  }
+  for (t = 0; t < T; t++) {
+    long row_min = -1, fill;
+    for (j = 0; j < topk; j++) {
+      long lid = (long)ids[t * topk + j] - offset;
+      if (lid >= 0 && lid < num_local && (row_min < 0 || lid < row_min)) row_min = lid;
+    }
+    fill = row_min >= 0 ? row_min : (best >= 0 ? best : 0);
+    for (j = 0; j < topk; j++) {
+      long lid = (long)ids[t * topk + j] - offset;
+      int ok = lid >= 0 && lid < num_local;
+      out_ids[t * topk + j] = (int32_t)(ok ? lid : fill);
+      out_w[t * topk + j] = ok ? w[t * topk + j] : 0.0f;
+    }
+  }
+  return 0;
+}
+
 /* ---------------------------------------------------------------- layer */
 
 /* One routed token through its expert: returns y[K] (double) for activation xh[K]. */
-static void orc_expert(const orc_tier *tier, int e, int K, int N, double limit, double alpha, double beta,
-                       int gate_up, const double *xh, double *y, double *rowbuf, double *h) {
+static void orc_expert(const orc_tier *tier, int e, int K, int N, int act, double limit, double alpha,
+                       double beta, int gate_up, const double *xh, double *y, double *rowbuf, double *h) {
   int n, c, k;
   int a8 = tier->fmt == ORC_FMT_MXFP4;
   double g13 = tier->g13 ? (double)tier->g13[e] : 1.0, g2 = tier->g2 ? (double)tier->g2[e] : 1.0;
@@ -287,27 +356,26 @@ static void orc_expert(const orc_tier *tier, int e, int K, int N, double limit, 
   long s13_row_bytes = (tier->fmt == ORC_FMT_NVFP4) ? (long)K / 16 : (long)K / 32;
   long w2_row_bytes = (tier->fmt == ORC_FMT_NF3) ? (long)N / 8 * 3 : (long)N / 2;
   long s2_row_bytes = (tier->fmt == ORC_FMT_NVFP4) ? (long)N / 16 : (long)N / 32;
-  const uint8_t *w13 = tier->w13 + (size_t)e * 2 * N * w13_row_bytes;
-  const uint8_t *s13 = tier->s13 + (size_t)e * 2 * N * s13_row_bytes;
+  /* w13 holds 2N rows ([up; gate] or [gate; up]), N rows for ReLU^2 without the multiply */
+  int w13_rows = (act == ORC_ACT_RELU2_NO_MUL) ? N : 2 * N;
+  const uint8_t *w13 = tier->w13 + (size_t)e * w13_rows * w13_row_bytes;
+  const uint8_t *s13 = tier->s13 + (size_t)e * w13_rows * s13_row_bytes;
   const uint8_t *w2 = tier->w2 + (size_t)e * K * w2_row_bytes;
   const uint8_t *s2 = tier->s2 + (size_t)e * K * s2_row_bytes;
   float hf[32];
   uint8_t q[32], sc;
 
-  /* GEMM1 + activation: h[n] = gate_n sigmoid(alpha gate_n) (up_n + beta) */
+  /* GEMM1 + activation (orc_act); ReLU^2 without the multiply has no gate row */
   for (n = 0; n < N; n++) {
     double up = 0.0, gate = 0.0;
-    int up_row = gate_up ? N + n : n, gate_row = gate_up ? n : N + n;
+    int up_row = (act == ORC_ACT_RELU2_NO_MUL) ? n : (gate_up ? N + n : n), gate_row = gate_up ? n : N + n;
     orc_decode_row(tier->fmt, w13, s13, g13, up_row, K, rowbuf);
     for (k = 0; k < K; k++) up += rowbuf[k] * xh[k];
-    orc_decode_row(tier->fmt, w13, s13, g13, gate_row, K, rowbuf);
-    for (k = 0; k < K; k++) gate += rowbuf[k] * xh[k];
-    if (!isnan(limit)) {
-      if (gate > limit) gate = limit;
-      if (up > limit) up = limit;
-      if (up < -limit) up = -limit;
+    if (act != ORC_ACT_RELU2_NO_MUL) {
+      orc_decode_row(tier->fmt, w13, s13, g13, gate_row, K, rowbuf);
+      for (k = 0; k < K; k++) gate += rowbuf[k] * xh[k];
     }
-    h[n] = gate / (1.0 + exp(-alpha * gate)) * (up + beta);
+    h[n] = orc_act(act, gate, up, limit, alpha, beta);
   }
   /* requantiser between the GEMMs: MXFP8 on fp32 h (A8), bf16 (A16) */
   if (a8) {
@@ -340,16 +408,19 @@ static void orc_expert(const orc_tier *tier, int e, int K, int N, double limit, 
  * stacked [gate; up].
  * acc [nrows, K] and out [nrows, K] are written.  Returns 0, or -1 on bad args.
  */
-int orc_moe_ex(int E_global, int K, int N, int topk, double limit, int gate_up, int n_tiers,
-               const orc_tier *tiers, const uint16_t *x, const int32_t *ids, const float *wts, long T,
-               const int32_t *rows, long nrows, double *acc, uint16_t *out, int weight_on_input, double alpha,
-               double beta) {
+int orc_moe_act(int E_global, int K, int N, int topk, double limit, int gate_up, int n_tiers,
+                const orc_tier *tiers, const uint16_t *x, const int32_t *ids, const float *wts, long T,
+                const int32_t *rows, long nrows, double *acc, uint16_t *out, int weight_on_input, double alpha,
+                double beta, int act) {
   long i;
   int bad = 0, tt;
   if (K % 32 || N % 32 || topk < 1 || n_tiers < 1 || n_tiers > 8) return -1;
-  /* the router weight on the input exists for the 16-bit activation path only
-     (vLLM "fused_moe/b12x" page, process_weights_after_loading) */
-  if (weight_on_input || alpha != 1.0 || beta != 0.0)
+  if (act < ORC_ACT_SWIGLU || act > ORC_ACT_RELU2_NO_MUL) return -1;
+  /* SiTU and ReLU^2 take no limit, alpha or beta (vLLM "fused_moe/b12x" page, _swiglu_params) */
+  if (act != ORC_ACT_SWIGLU && (!isnan(limit) || alpha != 1.0 || beta != 0.0)) return -1;
+  /* the router weight on the input, the OAI form and ReLU^2 exist for the 16-bit activation
+     path only (same page: process_weights_after_loading, the W4A8 activation check) */
+  if (weight_on_input || alpha != 1.0 || beta != 0.0 || act == ORC_ACT_RELU2_NO_MUL)
     for (tt = 0; tt < n_tiers; tt++)
       if (tiers[tt].fmt == ORC_FMT_MXFP4) return -1;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
@@ -393,10 +464,10 @@ int orc_moe_ex(int E_global, int K, int N, int topk, double limit, int gate_up, 
         if (weight_on_input) {
           /* the slot's copy of the token is scaled before GEMM1; its result enters with weight 1 */
           for (c = 0; c < K; c++) xw[c] = (double)wts[t * topk + j] * xin[c];
-          orc_expert(&tiers[tt], local, K, N, limit, alpha, beta, gate_up, xw, y, rowbuf, h);
+          orc_expert(&tiers[tt], local, K, N, act, limit, alpha, beta, gate_up, xw, y, rowbuf, h);
           for (c = 0; c < K; c++) a[c] += y[c];
         } else {
-          orc_expert(&tiers[tt], local, K, N, limit, alpha, beta, gate_up, xin, y, rowbuf, h);
+          orc_expert(&tiers[tt], local, K, N, act, limit, alpha, beta, gate_up, xin, y, rowbuf, h);
           for (c = 0; c < K; c++) a[c] += (double)wts[t * topk + j] * y[c];
         }
       }
@@ -405,6 +476,14 @@ int orc_moe_ex(int E_global, int K, int N, int topk, double limit, int gate_up, 
     free(xh); free(y); free(rowbuf); free(h); free(xa8); free(xw);
   }
   return bad ? -1 : 0;
+}
+
+int orc_moe_ex(int E_global, int K, int N, int topk, double limit, int gate_up, int n_tiers,
+               const orc_tier *tiers, const uint16_t *x, const int32_t *ids, const float *wts, long T,
+               const int32_t *rows, long nrows, double *acc, uint16_t *out, int weight_on_input, double alpha,
+               double beta) {
+  return orc_moe_act(E_global, K, N, topk, limit, gate_up, n_tiers, tiers, x, ids, wts, T, rows, nrows, acc, out,
+                     weight_on_input, alpha, beta, ORC_ACT_SWIGLU);
 }
 
 int orc_moe(int E_global, int K, int N, int topk, double limit, int gate_up, int n_tiers,

@@ -74,16 +74,20 @@ def _e4m3_grid():
     return np.array([O.e4m3(c) for c in range(127)])
 
 
-def _tie_flips(prob, t, fp32_ulps=1.0):
+def _tie_flips(prob, t, gate_up=False, act_kind=0):
     """Intermediate codes of token t that may round either way.
 
-    A W4A8 layer requantises each expert's SwiGLU output h to MXFP8 before the down
-    projection. The up/gate sums behind h are exact only up to rounding order (the
-    oracle sums in float64, the kernels in float32 on the matrix cores), so where
-    h * 2^-E lies within that rounding error of the midpoint between two E4M3 codes
-    both codes are correct. Returns, per such element, the change in the token's
-    output row [K] that taking the other code makes: router weight * (other code -
-    oracle code) * 2^E * the down projection's column."""
+    A W4A8 layer requantises each expert's activation output h to MXFP8 before the
+    down projection. The up/gate sums behind h are exact only up to rounding order
+    (the oracle sums in float64, the kernels in float32 on the matrix cores), so
+    where h * 2^-E lies within that rounding error of the midpoint between two E4M3
+    codes both codes are correct. The window is a worst-case bound for the kernels'
+    order: a K-term dot product formed by block-scaled MFMAs over 128-term k-tiles
+    (at most four fp32 roundings each) and fp32 accumulation across k-tiles is off
+    by at most (K / 32) * 2^-24 * sum |w x|. Returns, per such element, the change in
+    the token's output row [K] that taking the other code makes: router weight *
+    (other code - oracle code) * 2^E * the down projection's column. gate_up: w13
+    stacked [gate; up]; act_kind: the oracle's activation form."""
     import oracle as O
     c = prob.cfg
     if len(prob.tiers) != 1 or prob.tiers[0].fmt != I.FMT_MXFP4:
@@ -104,15 +108,19 @@ def _tie_flips(prob, t, fp32_ulps=1.0):
             if e < 0:
                 continue
         w13 = O.dequant(tier.fmt, w["w13"][e], w["s13"][e], c.K)
-        up, gate = w13[:c.N] @ xh, w13[c.N:] @ xh
-        # worst-case float32 summation error of each dot product (K terms)
-        eps = fp32_ulps * c.K * 2.0 ** -24
-        dup, dgate = eps * (np.abs(w13[:c.N]) @ np.abs(xh)), eps * (np.abs(w13[c.N:]) @ np.abs(xh))
-        if c.limit is not None:
-            gate, up = np.minimum(gate, c.limit), np.clip(up, -c.limit, c.limit)
-        sig = 1.0 / (1.0 + np.exp(-gate))
-        h = gate * sig * up
-        dh = np.abs(sig * (1 + gate * (1 - sig)) * up) * dgate + np.abs(gate * sig) * dup + 1e-6 * np.abs(h)
+        wu, wg = (w13[c.N:], w13[:c.N]) if gate_up else (w13[:c.N], w13[c.N:])
+        up, gate = wu @ xh, wg @ xh
+        # worst-case float32 error of each dot product in the kernels' summation order
+        eps = (c.K / 32) * 2.0 ** -24
+        dup, dgate = eps * (np.abs(wu) @ np.abs(xh)), eps * (np.abs(wg) @ np.abs(xh))
+        lim = c.limit if act_kind == 0 else None
+        h = np.array([O.act(act_kind, g, u, lim) for g, u in zip(gate, up)])
+        # |dh| <= |dh/dgate| dgate + |dh/dup| dup, slopes from the oracle's own activation
+        sg = np.array([O.act(act_kind, g + d, u, lim) - O.act(act_kind, g - d, u, lim)
+                       for g, u, d in zip(gate, up, dgate)])
+        su = np.array([O.act(act_kind, g, u + d, lim) - O.act(act_kind, g, u - d, lim)
+                       for g, u, d in zip(gate, up, dup)])
+        dh = 0.5 * (np.abs(sg) + np.abs(su)) + 1e-6 * np.abs(h)
         w2 = None
         for b in range(0, c.N, 32):
             amax = np.abs(h[b:b + 32]).max()
@@ -137,10 +145,10 @@ def _tie_flips(prob, t, fp32_ulps=1.0):
     return flips
 
 
-def _explained_by_ties(prob, t, got_row, acc_row):
+def _explained_by_ties(prob, t, got_row, acc_row, gate_up=False, act_kind=0):
     # flips far below the row's tolerance are absorbed by it; try subsets of the rest
     floor = 0.1 * REL_L2 * np.linalg.norm(acc_row)
-    flips = [f for f in _tie_flips(prob, t) if np.linalg.norm(f) > floor]
+    flips = [f for f in _tie_flips(prob, t, gate_up, act_kind) if np.linalg.norm(f) > floor]
     if not flips or len(flips) > 10:
         return False
     for mask in range(1, 1 << len(flips)):
@@ -151,11 +159,16 @@ def _explained_by_ties(prob, t, got_row, acc_row):
     return False
 
 
-def assert_rows_match(got_bf16, acc, rows=None, label="", prob=None):
+# rows of one comparison that may pass only through midpoint flips: one, or 1 % of the rows
+TIE_ROWS_MAX_FRAC = 0.01
+
+
+def assert_rows_match(got_bf16, acc, rows=None, label="", prob=None, gate_up=False, act_kind=0):
     """Every row within REL_L2 / REL_MAXABS of the oracle. With prob given (a W4A8
     layer), a row outside them still passes when taking the other of two equally
     correct intermediate codes for elements that sit on a rounding midpoint (see
-    _tie_flips) brings it inside."""
+    _tie_flips) brings it inside; at most max(1, 1 % of the compared rows) rows may
+    pass that way, and their count is printed."""
     got = bf16_to_f64(got_bf16)
     if rows is not None:
         got = got[rows]
@@ -163,9 +176,16 @@ def assert_rows_match(got_bf16, acc, rows=None, label="", prob=None):
     zero_ref = ~np.any(acc != 0, axis=1)
     assert np.all(got[zero_ref] == 0), f"{label}: rows with no valid slot must be exactly zero"
     bad = np.flatnonzero((l2 > REL_L2) | (mx > REL_MAXABS))
+    tied = 0
     if prob is not None and bad.size:
         toks = np.arange(prob.cfg.T) if rows is None else np.asarray(rows)
-        bad = np.array([r for r in bad if not _explained_by_ties(prob, int(toks[r]), got[r], acc[r])], dtype=int)
+        keep = [r for r in bad if not _explained_by_ties(prob, int(toks[r]), got[r], acc[r], gate_up, act_kind)]
+        tied = bad.size - len(keep)
+        bad = np.array(keep, dtype=int)
+    if prob is not None:
+        print(f"[tie-allowance] {label}: {tied} of {got.shape[0]} rows passed through midpoint flips", flush=True)
     assert bad.size == 0, (f"{label}: {bad.size} rows out of tolerance; worst rel-L2 {l2.max():.3e} "
                            f"rel-maxabs {mx.max():.3e}; first bad rows {bad[:8]}")
+    limit = max(1, int(TIE_ROWS_MAX_FRAC * got.shape[0]))
+    assert tied <= limit, f"{label}: {tied} rows needed midpoint flips (at most {limit} allowed)"
     return float(l2.max()), float(mx.max())

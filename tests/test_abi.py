@@ -172,3 +172,37 @@ def test_sequence_pins_and_tuning_file(tmp_path):
     assert again.load_tuning(path) == 1 and again.sequence(8) == M.SEQ_DECODE
     with pytest.raises(M.MoeError):
         again.load_tuning(str(tmp_path / "missing.txt"))
+
+
+def test_wrapper_refuses_mis_shaped_tensors_before_the_library_sees_them():
+    """The C ABI takes raw pointers and cannot check sizes: the Python wrapper checks
+    every tensor against the plan's geometry first (CPU tensors: refused at the shape
+    check, before the device check)."""
+    import torch
+    p = M.Plan(8, 256, 128, 2, 7.0, M.A_MXFP8, max_tokens=16)
+    w13, s13, w2, s2 = (torch.zeros(n, dtype=torch.uint8) for n in M.weight_bytes(M.W_MXFP4, 8, 256, 128))
+    assert (w13.numel(), s13.numel(), w2.numel(), s2.numel()) == (8 * 256 * 128, 8 * 256 * 8, 8 * 256 * 64,
+                                                                   8 * 256 * 4)
+    short = torch.zeros(w13.numel() - 1, dtype=torch.uint8)
+    for args in ((short, s13, w2, s2), (w13, s13[:-4], w2, s2), (w13, s13, w2, s2[1:])):
+        with pytest.raises(ValueError, match="elements"):
+            M.Experts(p, M.W_MXFP4, 8, *args)
+    with pytest.raises(ValueError, match="elements"):   # globals must hold one value per expert
+        M.Experts(p, M.W_MXFP4, 8, w13, s13, w2, s2, g13=torch.ones(7))
+    nv = M.weight_bytes(M.W_NVFP4, 3, 512, 64)
+    assert nv == (3 * 128 * 256, 3 * 128 * 32, 3 * 512 * 32, 3 * 512 * 4)
+    nf = M.weight_bytes(M.W_NF3, 3, 512, 64)
+    assert nf == (3 * 128 * 192, 3 * 128 * 16, 3 * 512 * 24, 3 * 512 * 2)
+
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    ids = torch.zeros(4, 2, dtype=torch.int32)
+    wts = torch.zeros(4, 2, dtype=torch.float32)
+    cases = [(torch.zeros(4, 255, dtype=torch.bfloat16), ids, wts, None, "x"),
+             (x, torch.zeros(4, 3, dtype=torch.int32), wts, None, "topk_ids"),
+             (x, ids, torch.zeros(5, 2, dtype=torch.float32), None, "topk_weights"),
+             (x, ids, wts, torch.zeros(3, 256, dtype=torch.bfloat16), "out")]
+    for xx, ii, ww, oo, name in cases:
+        with pytest.raises(ValueError, match=name):
+            M.run(p, [], xx, ii, ww, out=oo, scratch=torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="expert_map"):
+        M._tiers([(type("E", (), {"handle": C.c_void_p(1)})(), torch.zeros(7, dtype=torch.int32))], p)

@@ -324,3 +324,79 @@ def test_autotune_pins_the_fastest_sequence():
         L.plan.set_sequence(8, M.SEQ_AUTO)
     acc, _ = O.moe_problem(L.prob)
     assert_rows_match(out, acc, label="hybrid_small after autotune")
+
+
+# ---- production rungs at full geometry -------------------------------------------------
+# Batches of 11..511 tokens run the 16-route general kernels; at the pages' geometries
+# their k-loops are 56 (K = 7168) and 48 (K = 6144) k-tiles long.
+
+def _batch(name, T):
+    """The named workload's weights with a batch of T tokens of its own routing recipe."""
+    return I.make_problem(name, T=T)
+
+
+@pytest.mark.parametrize("name,batches", [("decode", ((40, 12), (200, 12))), ("nvfp4_decode", ((40, 10),)),
+                                          ("hybrid", ((40, 10),))])
+def test_general_sequence_at_full_geometry(name, batches):
+    L = layer(name, max_tokens=256)
+    for T, nrows in batches:
+        q = _batch(name, T)
+        assert L.plan.sequence(T) == M.SEQ_GENERAL
+        rows = _sample_rows(q, nrows, seed=T)
+        acc, _ = O.moe_problem(q, rows=rows)
+        for det in (False, True):
+            out = L.run(x=dev(q.x, torch.bfloat16), ids=dev(q.ids), wts=dev(q.wts), deterministic=det)
+            assert_rows_match(out, acc, rows=rows, label=f"{name} T={T} general det={det}", prob=q)
+
+
+def test_hybrid_decode_at_full_geometry():
+    """Both tiers (64 NVFP4 + 192 NF3 experts, K = 6144, N = 512, top-8) on the decode
+    sequence, every row, both combine modes."""
+    L = layer("hybrid", max_tokens=8)
+    q = _batch("hybrid", 8)
+    assert L.plan.sequence(8) == M.SEQ_DECODE
+    acc, _ = O.moe_problem(q)
+    for det in (False, True):
+        out = L.run(x=dev(q.x, torch.bfloat16), ids=dev(q.ids), wts=dev(q.wts), deterministic=det)
+        assert_rows_match(out, acc, label=f"hybrid T=8 decode det={det}")
+
+
+def _tile_rows(prob, tile=64, hottest=5):
+    """Tokens of the first route, a middle tile's route and the last route (the last,
+    ragged tile) of the most loaded experts, and of every expert holding one route."""
+    c = prob.cfg
+    cnt, off, perm, _ = O.route(prob.ids, c.E, prob.tiers)
+    rows = set()
+    for e in np.argsort(-cnt, kind="stable")[:hottest]:
+        n = int(cnt[e])
+        tiles = (n + tile - 1) // tile
+        for pos in (0, (tiles // 2) * tile + 7, n - 1):
+            rows.add(int(perm[off[e] + min(pos, n - 1)]) // c.topk)
+    for e in np.flatnonzero(cnt == 1)[:4]:
+        rows.add(int(perm[off[e]]) // c.topk)
+    return np.array(sorted(rows), dtype=np.int32)
+
+
+def test_prefill_hot_expert_tiles():
+    L = layer("prefill")
+    assert L.plan.sequence(L.prob.cfg.T) == M.SEQ_PREFILL
+    rows = _tile_rows(L.prob)
+    acc, _ = O.moe_problem(L.prob, rows=rows)
+    for det in (False, True):
+        out = L.run(deterministic=det)
+        assert_rows_match(out, acc, rows=rows, label=f"prefill hot tiles det={det}", prob=L.prob)
+
+
+@pytest.mark.parametrize("name,max_tokens", [("nvfp4_small", 17), ("nf3_small", 17), ("hybrid_small", 24)])
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_sixteen_bit_plans_with_a_decode_sized_last_chunk(name, max_tokens, deterministic):
+    """A top capacity above the decode sizes (the arena is carved for the general
+    kernels) and a decode-size last chunk (4, 2 and 5 tokens), whose down GEMM meets
+    its two halves in the arena's accumulators."""
+    prob = SMALL[name]()
+    L = DeviceLayer(prob, max_tokens=max_tokens)
+    T = prob.cfg.T
+    assert L.plan.sequence(max_tokens) != M.SEQ_DECODE and L.plan.sequence(T % max_tokens) == M.SEQ_DECODE
+    out = L.run(deterministic=deterministic)
+    acc, _ = O.moe_problem(prob)
+    assert_rows_match(out, acc, label=f"{name} chunks of {max_tokens} det={deterministic}")

@@ -68,3 +68,31 @@ def test_no_flips_for_16_bit_layers_or_ignored_ids():
 def dataclasses_replace(prob, **kw):
     import dataclasses
     return dataclasses.replace(prob, **kw)
+
+
+def test_more_than_one_flipped_row_fails():
+    """At most max(1, 1 %) of the compared rows may pass through flips: the same
+    flipped row twice in a two-row comparison is refused."""
+    import dataclasses
+    import pytest
+    prob = I.make_problem(CFG, seed=SEED)
+    acc, _ = O.moe_problem(prob, rows=[ROW])
+    big = [f for f in _tie_flips(prob, ROW) if np.linalg.norm(f) > 1e-2 * np.linalg.norm(acc[0])]
+    two = dataclasses.replace(prob, cfg=dataclasses.replace(prob.cfg, T=2), x=prob.x[[ROW, ROW]],
+                              ids=prob.ids[[ROW, ROW]], wts=prob.wts[[ROW, ROW]])
+    acc2 = np.concatenate([acc, acc])
+    flipped2 = acc2 + big[0]
+    with pytest.raises(AssertionError, match="needed midpoint flips"):
+        assert_rows_match(_bf16(flipped2), acc2, label="two flipped rows", prob=two)
+    one_flipped = np.concatenate([acc + big[0], acc])
+    assert_rows_match(_bf16(one_flipped), acc2, label="one flipped row", prob=two)
+
+
+def test_flips_follow_the_gate_up_layout():
+    """With w13 stacked [gate; up] the halves swap: the flips offered for the swapped
+    reading of the same weights are those of the oracle run with gate_up."""
+    prob = _one_row(I.make_problem(CFG, seed=SEED), ROW)
+    a = _tie_flips(prob, 0, gate_up=False)
+    b = _tie_flips(prob, 0, gate_up=True)
+    assert len(a) > 0
+    assert len(a) != len(b) or any(not np.allclose(x, y) for x, y in zip(a, b))
