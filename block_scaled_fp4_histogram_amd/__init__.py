@@ -20,7 +20,12 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOTPREPARED, MOE_ESCRATCH, MOE_EHIP =
 W_MXFP4, W_NVFP4, W_NF3 = 1, 2, 3
 A_MXFP8, A_BF16 = 1, 2
 W13_UP_GATE, W13_GATE_UP = 0, 1
+ACT_SWIGLU, ACT_SITU = 0, 1
 SEQ_AUTO, SEQ_DECODE, SEQ_GENERAL, SEQ_PREFILL = 0, 1, 2, 3
+COMBINE_AUTO, COMBINE_ATOMIC, COMBINE_ROUTE_BUFFER = 0, 1, 2
+# race slots of the autotuner: (sequence, combine of deterministic = 0 runs)
+RACE_SLOTS = (("decode", None), ("general", "atomic"), ("general", "route_buffer"), ("prefill", "atomic"),
+              ("prefill", "route_buffer"))
 
 
 class MoeError(RuntimeError):
@@ -108,17 +113,42 @@ class Plan:
         """The launch sequence a batch of `tokens` runs with (SEQ_DECODE / SEQ_GENERAL / SEQ_PREFILL)."""
         return _lib.load().moe_plan_sequence(self.handle, int(tokens))
 
+    def set_combine(self, tokens: int, combine: int):
+        """Pin the combine of deterministic = 0 runs at the rung of `tokens` (COMBINE_*)."""
+        _check(_lib.load().moe_plan_set_combine(self.handle, int(tokens), int(combine)))
+
+    def combine(self, tokens: int) -> int:
+        """COMBINE_ATOMIC or COMBINE_ROUTE_BUFFER: how a deterministic = 0 batch of `tokens` combines."""
+        return _lib.load().moe_plan_combine(self.handle, int(tokens))
+
     def autotune(self, tiers, tokens, deterministic: bool = False, reps: int = 5, stream=None):
-        """Race the eligible sequences at the rung of each batch size in `tokens` on a synthetic
-        batch and pin the fastest; returns [len(tokens)][3] median microseconds of DECODE,
-        GENERAL and PREFILL (NaN where a rung cannot take one)."""
+        """Race, at the rung of each batch size in `tokens`, the eligible (sequence, combine) pairs on a
+        synthetic batch and pin the fastest; returns [len(tokens)][5] median microseconds in RACE_SLOTS
+        order (NaN where not raced)."""
         tok = [int(t) for t in tokens]
         arr, keep = _tiers(tiers, self)
         ta = (C.c_int * len(tok))(*tok)
-        us = (C.c_float * (3 * len(tok)))()
+        us = (C.c_float * (5 * len(tok)))()
         _check(_lib.load().moe_plan_autotune(self.handle, arr, len(tiers), ta, len(tok), int(bool(deterministic)),
                                              int(reps), _stream(stream), us))
-        return [[us[3 * i + k] for k in range(3)] for i in range(len(tok))]
+        return [[us[5 * i + k] for k in range(5)] for i in range(len(tok))]
+
+    def autotune_batch(self, tiers, x, topk_ids, topk_weights, deterministic: bool = False, reps: int = 5,
+                       stream=None):
+        """The same race at the rung of x's batch, on this batch itself (its own routing); returns the
+        5 median times in RACE_SLOTS order."""
+        import torch
+        T = x.shape[0]
+        for device in (False, True):
+            _need(x, "x", torch.bfloat16, device, shape=(T, self.K))
+            _need(topk_ids, "topk_ids", torch.int32, device, shape=(T, self.top_k))
+            _need(topk_weights, "topk_weights", torch.float32, device, shape=(T, self.top_k))
+        arr, keep = _tiers(tiers, self)
+        us = (C.c_float * 5)()
+        _check(_lib.load().moe_plan_autotune_batch(self.handle, arr, len(tiers), _ptr(x), _ptr(topk_ids),
+                                                   _ptr(topk_weights), T, int(bool(deterministic)), int(reps),
+                                                   _stream(stream), us))
+        return [us[k] for k in range(5)]
 
     def save_tuning(self, path: str):
         _check(_lib.load().moe_plan_save_tuning(self.handle, os.fsencode(path)))
@@ -132,6 +162,10 @@ class Plan:
     def set_swiglu_oai(self, alpha: float, beta: float):
         """Activation gate * sigmoid(alpha gate) * (up + beta) after the clamps (bf16 plans; 1, 0 = plain)."""
         _check(_lib.load().moe_plan_set_swiglu_oai(self.handle, float(alpha), float(beta)))
+
+    def set_activation(self, act: int):
+        """ACT_SWIGLU (default) or ACT_SITU: silu(4 tanh(gate/4)) * 25 tanh(up/25), plans without a limit."""
+        _check(_lib.load().moe_plan_set_activation(self.handle, int(act)))
 
     def set_router_weight_on_input(self, enable: bool = True):
         """Apply each slot's router weight to GEMM1's input instead of the GEMM2 result (bf16 plans)."""
@@ -241,6 +275,28 @@ def run(plan: Plan, tiers: Sequence, x, topk_ids, topk_weights, out=None, determ
                                _ptr(out), T, int(bool(deterministic)), _ptr(scratch), scratch.numel(),
                                _stream(stream)))
     return out
+
+
+def ep_remap(topk_ids, topk_weights, offset: int, num_local: int, out_ids=None, out_weights=None, stream=None):
+    """Expert-parallel id remap (moe_ep_remap): global top-k ids of [T, k] -> this rank's
+    local ids for experts [offset, offset + num_local); other slots get weight 0 and an
+    expert the batch already reads. Returns (out_ids int32, out_weights fp32)."""
+    import torch
+    if topk_ids is None or topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be a [T, k] tensor")
+    T, k = topk_ids.shape
+    if out_ids is None:
+        out_ids = torch.empty_like(topk_ids)
+    if out_weights is None:
+        out_weights = torch.empty((T, k), dtype=torch.float32, device=topk_ids.device)
+    for device in (False, True):
+        _need(topk_ids, "topk_ids", torch.int32, device, shape=(T, k))
+        _need(topk_weights, "topk_weights", torch.float32, device, shape=(T, k))
+        _need(out_ids, "out_ids", torch.int32, device, shape=(T, k))
+        _need(out_weights, "out_weights", torch.float32, device, shape=(T, k))
+    _check(_lib.load().moe_ep_remap(_ptr(topk_ids), _ptr(topk_weights), T, k, int(offset), int(num_local),
+                                    _ptr(out_ids), _ptr(out_weights), _stream(stream)))
+    return out_ids, out_weights
 
 
 def debug_route(plan: Plan, tiers: Sequence, topk_ids, scratch=None, stream=None):

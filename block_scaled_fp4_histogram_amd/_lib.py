@@ -27,12 +27,17 @@ SIGNATURES = {
     "moe_plan_set_sequence": (_i, [_vp, _i, _i]),
     "moe_plan_sequence": (_i, [_vp, _i]),
     "moe_plan_autotune": (_i, [_vp, _vp, _i, C.POINTER(_i), _i, _i, _i, _vp, C.POINTER(_f)]),
+    "moe_plan_autotune_batch": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, C.POINTER(_f)]),
+    "moe_plan_set_combine": (_i, [_vp, _i, _i]),
+    "moe_plan_combine": (_i, [_vp, _i]),
     "moe_plan_save_tuning": (_i, [_vp, C.c_char_p]),
     "moe_plan_load_tuning": (_i, [_vp, C.c_char_p]),
     "moe_plan_set_router_weight_on_input": (_i, [_vp, _i]),
     "moe_plan_set_swiglu_oai": (_i, [_vp, C.c_float, C.c_float]),
+    "moe_plan_set_activation": (_i, [_vp, _i]),
     "moe_plan_enable_stage_timing": (_i, [_vp, _i]),
     "moe_plan_stage_times": (_i, [_vp, C.POINTER(_f), _i, C.POINTER(_i)]),
+    "moe_ep_remap": (_i, [_vp, _vp, _i, _i, C.c_longlong, _i, _vp, _vp, _vp]),
     "moe_debug_route": (_i, [_vp, _vp, _i, _vp, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp]),
     "moe_debug_quant_mxfp8_bf16": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "moe_debug_quant_mxfp8_f32": (_i, [_vp, _i, _i, _vp, _vp, _vp]),

@@ -27,6 +27,15 @@ int fail(int code, const char *fmt, ...) {
   return code;
 }
 
+}  // namespace
+
+namespace moe {
+// The calling thread's error message, for entry points in other source files.
+int set_error(int code, const char *msg) { return fail(code, "%s", msg); }
+}  // namespace moe
+
+namespace {
+
 #define HIP_TRY(expr)                                                                  \
   do {                                                                                 \
     hipError_t e_ = (expr);                                                            \
@@ -54,8 +63,10 @@ struct moe_plan_s {
   int afmt, w13_layout, max_tokens;
   int w_on_input = 0;     // router weight applied to GEMM1's input (W4A16 / W3A16 only)
   float alpha = 1.f, beta = 0.f;   // SwiGLU form gate * sigmoid(alpha gate) * (up + beta)
+  int act = MOE_ACT_SWIGLU;        // activation form of the GEMM1 epilogue
   std::vector<int> caps;  // ascending; caps.back() == chunk
   std::vector<int> seq;   // per rung: the launch sequence it is pinned to (MOE_SEQ_*), 0 = the ladder's choice
+  std::vector<int> comb;  // per rung: the combine of deterministic = 0 runs (MOE_COMBINE_*), 0 = the ladder's
   // optional stage timing: kStageEvents events per recorded run
   std::vector<hipEvent_t> events;
   int timing_runs_max = 0, timing_runs = 0;
@@ -89,6 +100,22 @@ int rung_of(const moe_plan_s *p, int T) {
 }
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int seq_for(const moe_plan_s *p, int T);
+
+// Whether runs at the rung of `cap` tokens combine through the per-slot route
+// buffer and the top-k sum (always in deterministic mode) rather than fp32
+// atomics into an accumulator.  The ladder's choice for deterministic = 0: the
+// route buffer with the 64-route prefill kernels, whose atomic adds all execute
+// memory-side on this GPU (a 4096-token W4A8 prefill layer measured 903 us with
+// atomics against 602 us through the route buffer), atomics otherwise.  A chunked
+// batch's chunks all follow the rung of its first chunk.
+bool route_buffer(const moe_plan_s *p, int cap, int deterministic) {
+  if (deterministic) return true;
+  const int pinned = p->comb[rung_of(p, cap)];
+  if (pinned) return pinned == MOE_COMBINE_ROUTE_BUFFER;
+  return seq_for(p, cap) == MOE_SEQ_PREFILL;
+}
 
 // Carving of the scratch arena for one chunk of `cap` tokens.
 struct Layout {
@@ -135,7 +162,7 @@ Layout layout(const moe_plan_s *p, int cap, int deterministic) {
     L.dpart = take((size_t)(p->K / 16) * 256 * sizeof(float));
     L.dcnt = take(4 * (size_t)(p->K / 16));
   }
-  if (deterministic) L.rb = take(2 * R * p->K);
+  if (route_buffer(p, cap, deterministic)) L.rb = take(2 * R * p->K);
   else L.acc = take(4 * (size_t)cap * p->K);
   L.total = o;
   return L;
@@ -194,6 +221,7 @@ int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const ui
   da.w_on_input = p->w_on_input;
   da.alpha = p->alpha;
   da.beta = p->beta;
+  da.act = p->act;
   da.cpass = moe::decode_cpass(p->K, p->afmt == MOE_A_MXFP8);
   da.hq = scratch + L.hq;
   da.hs = scratch + L.hs;
@@ -252,7 +280,8 @@ int seq_for(const moe_plan_s *p, int T) {
   return pinned ? pinned : ladder_seq(p, T);
 }
 
-// Everything one chunk needs after validation.
+// Everything one chunk needs after validation.  deterministic: combine through
+// the route buffer and the top-k sum (1) or fp32 atomics (0).
 int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uint16_t *x, const int32_t *ids,
               const float *wts, uint16_t *out, int T, int deterministic, const Layout &L, uint8_t *scratch,
               hipStream_t s, bool route_only, bool prefill, const hipEvent_t *ev = nullptr) {
@@ -328,6 +357,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ga.w_on_input = p->w_on_input;
   ga.alpha = p->alpha;
   ga.beta = p->beta;
+  ga.act = p->act;
   ga.topk_w = wts;
   ga.out_acc = (float *)(scratch + L.acc);
   ga.rb = (uint16_t *)(scratch + L.rb);
@@ -472,9 +502,10 @@ int run_batch(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const voi
     const float *wc = wts + (size_t)t0 * p->topk;
     uint16_t *oc = (uint16_t *)out + (size_t)t0 * p->K;
     const int seq = seq_for(p, tc);
+    const int rb = route_buffer(p, cap, deterministic) ? 1 : 0;   // the combine the arena was carved for
     const int rc = seq == MOE_SEQ_DECODE
                        ? run_decode(p, tiers, n_tiers, xc, idc, wc, oc, tc, L, scratch, s, ev)
-                       : run_chunk(p, tiers, n_tiers, xc, idc, wc, oc, tc, deterministic, L, scratch, s, false,
+                       : run_chunk(p, tiers, n_tiers, xc, idc, wc, oc, tc, rb, L, scratch, s, false,
                                    seq == MOE_SEQ_PREFILL, ev);
     if (rc != MOE_OK) return rc;
   }
@@ -513,6 +544,7 @@ int moe_plan(int E, int K, int N, int top_k, float swiglu_limit, int act_format,
     if (c < max_tokens) p->caps.push_back(c);
   p->caps.push_back(max_tokens);
   p->seq.assign(p->caps.size(), 0);
+  p->comb.assign(p->caps.size(), 0);
   *out = p;
   return MOE_OK;
 }
@@ -539,8 +571,18 @@ int moe_plan_set_swiglu_oai(moe_plan_t plan, float alpha, float beta) {
   const bool plain = alpha == 1.f && beta == 0.f;
   if (!plain && plan->afmt != MOE_A_BF16)
     return fail(MOE_EUNSUPPORTED, "the alpha/beta SwiGLU form needs bf16 activations (W4A16 / W3A16)");
+  if (!plain && plan->act != MOE_ACT_SWIGLU) return fail(MOE_EUNSUPPORTED, "alpha and beta belong to the SwiGLU");
   plan->alpha = alpha;
   plan->beta = beta;
+  return MOE_OK;
+}
+
+int moe_plan_set_activation(moe_plan_t plan, int act) {
+  if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
+  if (act != MOE_ACT_SWIGLU && act != MOE_ACT_SITU) return fail(MOE_EUNSUPPORTED, "activation %d", act);
+  if (act == MOE_ACT_SITU && (plan->has_limit || plan->alpha != 1.f || plan->beta != 0.f))
+    return fail(MOE_EUNSUPPORTED, "SiTU takes no swiglu limit, alpha or beta");
+  plan->act = act;
   return MOE_OK;
 }
 
@@ -604,6 +646,21 @@ int moe_plan_set_sequence(moe_plan_t plan, int tokens, int seq) {
     return fail(MOE_EUNSUPPORTED, "sequence %d cannot run the %d-token capacity of this plan", seq, cap);
   plan->seq[r] = seq;
   return MOE_OK;
+}
+
+int moe_plan_set_combine(moe_plan_t plan, int tokens, int combine) {
+  if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
+  if (tokens < 1) return fail(MOE_EINVAL, "tokens=%d", tokens);
+  if (combine != MOE_COMBINE_AUTO && combine != MOE_COMBINE_ATOMIC && combine != MOE_COMBINE_ROUTE_BUFFER)
+    return fail(MOE_EINVAL, "combine %d", combine);
+  plan->comb[rung_of(plan, tokens)] = combine;
+  return MOE_OK;
+}
+
+int moe_plan_combine(moe_plan_t plan, int tokens) {
+  if (!plan_ok(plan) || tokens < 1) return 0;
+  const int cap = cap_for(plan, std::min(tokens, plan->caps.back()));
+  return route_buffer(plan, cap, 0) ? MOE_COMBINE_ROUTE_BUFFER : MOE_COMBINE_ATOMIC;
 }
 
 int moe_plan_sequence(moe_plan_t plan, int tokens) {
@@ -681,6 +738,102 @@ extern "C++" std::string geometry_key(const moe_plan_s *p) {
 
 }  // namespace
 
+static int check_run_args(moe_plan_t p, const moe_tier *tiers, int n_tiers, const void *x, const int32_t *ids,
+                          const float *wts, void *out, int T, void *scratch) {
+  if (!plan_ok(p)) return fail(MOE_EINVAL, "invalid plan");
+  if (T < 0) return fail(MOE_EINVAL, "T=%d", T);
+  int rc = check_tiers(p, tiers, n_tiers);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !ids || !wts || !out || !scratch) return fail(MOE_EINVAL, "null tensor pointer");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ids, 4) || !aligned(wts, 4) || !aligned(scratch, 256))
+    return fail(MOE_EINVAL, "x/out need 16-byte, ids/weights 4-byte, scratch 256-byte alignment");
+  return MOE_OK;
+}
+
+namespace {
+
+// One race at the rung of `cap` tokens on a batch of T tokens already on the device:
+// every launch sequence the rung can take, and for deterministic = 0 both combines
+// of the planner-based sequences; pins the fastest.  us_out[kRaceSlots]: median
+// microseconds of DECODE, GENERAL-atomic, GENERAL-route buffer, PREFILL-atomic,
+// PREFILL-route buffer (NaN where not raced; deterministic runs fill the
+// route-buffer slots).
+constexpr int kRaceSlots = 5;
+
+int race_rung(moe_plan_s *plan, const moe_tier *tiers, int n_tiers, const void *x, const int32_t *ids,
+              const float *wts, int T, int deterministic, int reps, hipStream_t s, float *us_out) {
+  const int r = rung_of(plan, T), cap = plan->caps[r];
+  struct Cand {
+    int seq, comb;
+  };
+  const Cand cands[kRaceSlots] = {{MOE_SEQ_DECODE, 0},
+                                  {MOE_SEQ_GENERAL, MOE_COMBINE_ATOMIC},
+                                  {MOE_SEQ_GENERAL, MOE_COMBINE_ROUTE_BUFFER},
+                                  {MOE_SEQ_PREFILL, MOE_COMBINE_ATOMIC},
+                                  {MOE_SEQ_PREFILL, MOE_COMBINE_ROUTE_BUFFER}};
+  struct Restore {   // the rung's previous pins come back if the race stops early
+    moe_plan_s *p;
+    int r, seq, comb;
+    bool armed;
+    ~Restore() {
+      if (armed) {
+        p->seq[r] = seq;
+        p->comb[r] = comb;
+      }
+    }
+  } restore{plan, r, plan->seq[r], plan->comb[r], true};
+  // one arena large enough for either combine
+  plan->comb[r] = MOE_COMBINE_ROUTE_BUFFER;
+  const size_t bytes_rb = layout(plan, cap, deterministic).total;
+  plan->comb[r] = MOE_COMBINE_ATOMIC;
+  const size_t bytes_at = layout(plan, cap, deterministic).total;
+  TuneBuffers B;
+  HIP_TRY(hipMalloc(&B.out, (size_t)T * plan->K * 2));
+  HIP_TRY(hipMalloc(&B.scratch, std::max(bytes_rb, bytes_at)));
+  HIP_TRY(hipEventCreate(&B.e0));
+  HIP_TRY(hipEventCreate(&B.e1));
+  int best = -1;
+  float best_us = 0.f;
+  for (int k = 0; k < kRaceSlots; k++) {
+    float us = NAN;
+    const Cand c = cands[k];
+    const bool combine_matters = c.seq != MOE_SEQ_DECODE && !deterministic;
+    const bool eligible = seq_eligible(plan, cap, c.seq) &&
+                          (combine_matters || c.comb == 0 || c.comb == MOE_COMBINE_ROUTE_BUFFER);
+    if (eligible) {
+      plan->seq[r] = c.seq;
+      plan->comb[r] = combine_matters ? c.comb : 0;
+      const Layout L = layout(plan, cap, deterministic);
+      std::vector<float> t;
+      int rc = MOE_OK;
+      for (int it = 0; it < reps + 2 && rc == MOE_OK; it++) {
+        HIP_TRY(hipEventRecord(B.e0, s));
+        rc = run_batch(plan, tiers, n_tiers, x, ids, wts, B.out, T, deterministic, cap, L, (uint8_t *)B.scratch, s);
+        HIP_TRY(hipEventRecord(B.e1, s));
+        HIP_TRY(hipEventSynchronize(B.e1));
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, B.e0, B.e1));
+        if (it >= 2) t.push_back(1000.f * ms);   // two warm-up runs
+      }
+      if (rc != MOE_OK) return rc;
+      std::sort(t.begin(), t.end());
+      us = t[t.size() / 2];
+      if (best < 0 || us < best_us) {
+        best = k;
+        best_us = us;
+      }
+    }
+    if (us_out) us_out[k] = us;
+  }
+  plan->seq[r] = cands[best].seq;
+  plan->comb[r] = (cands[best].seq != MOE_SEQ_DECODE && !deterministic) ? cands[best].comb : restore.comb;
+  restore.armed = false;
+  return MOE_OK;
+}
+
+}  // namespace
+
 int moe_plan_autotune(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const int *tokens, int n, int deterministic,
                       int reps, void *stream, float *us_out) {
   if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
@@ -688,11 +841,9 @@ int moe_plan_autotune(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const
   if (rc != MOE_OK) return rc;
   if (!tokens || n < 1 || reps < 1) return fail(MOE_EINVAL, "tokens, n and reps must be given");
   hipStream_t s = (hipStream_t)stream;
-  const int seqs[3] = {MOE_SEQ_DECODE, MOE_SEQ_GENERAL, MOE_SEQ_PREFILL};
   for (int i = 0; i < n; i++) {
     if (tokens[i] < 1) return fail(MOE_EINVAL, "tokens[%d]=%d", i, tokens[i]);
-    const int r = rung_of(plan, std::min(tokens[i], plan->caps.back())), cap = plan->caps[r];
-    const Layout L = layout(plan, cap, deterministic ? 1 : 0);
+    const int cap = plan->caps[rung_of(plan, std::min(tokens[i], plan->caps.back()))];
     std::vector<uint16_t> hx;
     std::vector<int32_t> hids;
     std::vector<float> hw;
@@ -701,52 +852,29 @@ int moe_plan_autotune(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const
     HIP_TRY(hipMalloc(&B.x, hx.size() * 2));
     HIP_TRY(hipMalloc(&B.ids, hids.size() * 4));
     HIP_TRY(hipMalloc(&B.w, hw.size() * 4));
-    HIP_TRY(hipMalloc(&B.out, hx.size() * 2));
-    HIP_TRY(hipMalloc(&B.scratch, L.total));
     HIP_TRY(hipMemcpy(B.x, hx.data(), hx.size() * 2, hipMemcpyHostToDevice));
     HIP_TRY(hipMemcpy(B.ids, hids.data(), hids.size() * 4, hipMemcpyHostToDevice));
     HIP_TRY(hipMemcpy(B.w, hw.data(), hw.size() * 4, hipMemcpyHostToDevice));
-    HIP_TRY(hipEventCreate(&B.e0));
-    HIP_TRY(hipEventCreate(&B.e1));
-    struct Restore {   // the rung's previous pin comes back if the race stops early
-      moe_plan_s *p;
-      int r, v;
-      bool armed;
-      ~Restore() {
-        if (armed) p->seq[r] = v;
-      }
-    } restore{plan, r, plan->seq[r], true};
-    int best = 0;
-    float best_us = 0.f;
-    for (int k = 0; k < 3; k++) {
-      float us = NAN;
-      if (seq_eligible(plan, cap, seqs[k])) {
-        plan->seq[r] = seqs[k];
-        std::vector<float> t;
-        for (int it = 0; it < reps + 2 && rc == MOE_OK; it++) {
-          HIP_TRY(hipEventRecord(B.e0, s));
-          rc = run_batch(plan, tiers, n_tiers, B.x, (const int32_t *)B.ids, (const float *)B.w, B.out, cap,
-                         deterministic ? 1 : 0, cap, L, (uint8_t *)B.scratch, s);
-          HIP_TRY(hipEventRecord(B.e1, s));
-          HIP_TRY(hipEventSynchronize(B.e1));
-          float ms = 0.f;
-          HIP_TRY(hipEventElapsedTime(&ms, B.e0, B.e1));
-          if (it >= 2) t.push_back(1000.f * ms);   // two warm-up runs
-        }
-        if (rc != MOE_OK) return rc;
-        std::sort(t.begin(), t.end());
-        us = t[t.size() / 2];
-        if (!best || us < best_us) {
-          best = seqs[k];
-          best_us = us;
-        }
-      }
-      if (us_out) us_out[3 * i + k] = us;
-    }
-    plan->seq[r] = best;
-    restore.armed = false;
+    rc = race_rung(plan, tiers, n_tiers, B.x, (const int32_t *)B.ids, (const float *)B.w, cap,
+                   deterministic ? 1 : 0, reps, s, us_out ? us_out + (size_t)kRaceSlots * i : nullptr);
+    if (rc != MOE_OK) return rc;
   }
   return MOE_OK;
+}
+
+int moe_plan_autotune_batch(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const void *x,
+                            const int32_t *topk_ids, const float *topk_weights, int T, int deterministic, int reps,
+                            void *stream, float *us_out) {
+  if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
+  const int rc = check_tiers(plan, tiers, n_tiers);
+  if (rc != MOE_OK) return rc;
+  if (!x || !topk_ids || !topk_weights) return fail(MOE_EINVAL, "null tensor pointer");
+  if (!aligned(x, 16) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_EINVAL, "x needs 16-byte, ids/weights 4-byte alignment");
+  if (T < 1 || T > plan->max_tokens) return fail(MOE_EINVAL, "T=%d outside [1, max_tokens=%d]", T, plan->max_tokens);
+  if (reps < 1) return fail(MOE_EINVAL, "reps=%d", reps);
+  return race_rung(plan, tiers, n_tiers, x, topk_ids, topk_weights, T, deterministic ? 1 : 0, reps,
+                   (hipStream_t)stream, us_out);
 }
 
 int moe_plan_save_tuning(moe_plan_t plan, const char *path) {
@@ -765,7 +893,8 @@ int moe_plan_save_tuning(moe_plan_t plan, const char *path) {
   if (!f) return fail(MOE_EINVAL, "cannot write %s", path);
   for (auto &l : keep) fputs(l.c_str(), f);
   for (size_t r = 0; r < plan->caps.size(); r++)
-    if (plan->seq[r]) fprintf(f, "moe v1 %s cap=%d seq=%d\n", key.c_str(), plan->caps[r], plan->seq[r]);
+    if (plan->seq[r] || plan->comb[r])
+      fprintf(f, "moe v2 %s cap=%d seq=%d comb=%d\n", key.c_str(), plan->caps[r], plan->seq[r], plan->comb[r]);
   const bool ok = fclose(f) == 0;
   return ok ? MOE_OK : fail(MOE_EINVAL, "cannot write %s", path);
 }
@@ -774,16 +903,25 @@ int moe_plan_load_tuning(moe_plan_t plan, const char *path) {
   if (!plan_ok(plan) || !path) return fail(MOE_EINVAL, "invalid plan or path");
   FILE *f = fopen(path, "r");
   if (!f) return fail(MOE_EINVAL, "cannot read %s", path);
-  const std::string head = "moe v1 " + geometry_key(plan) + " cap=";
+  const std::string key = geometry_key(plan) + " cap=";
+  const std::string v1 = "moe v1 " + key, v2 = "moe v2 " + key;
   char line[512];
   int applied = 0;
   while (fgets(line, sizeof line, f)) {
-    if (strncmp(line, head.c_str(), head.size()) != 0) continue;
-    int cap = 0, seq = 0;
-    if (sscanf(line + head.size(), "%d seq=%d", &cap, &seq) != 2) continue;
+    int cap = 0, seq = 0, comb = 0;
+    if (strncmp(line, v2.c_str(), v2.size()) == 0) {
+      if (sscanf(line + v2.size(), "%d seq=%d comb=%d", &cap, &seq, &comb) != 3) continue;
+    } else if (strncmp(line, v1.c_str(), v1.size()) == 0) {   // sequence pins only
+      if (sscanf(line + v1.size(), "%d seq=%d", &cap, &seq) != 2) continue;
+    } else {
+      continue;
+    }
     const int r = rung_of(plan, cap);
-    if (plan->caps[r] != cap || !seq_eligible(plan, cap, seq)) continue;   // stale or foreign entry
+    if (plan->caps[r] != cap || (seq && !seq_eligible(plan, cap, seq)) || comb < 0 ||
+        comb > MOE_COMBINE_ROUTE_BUFFER)
+      continue;   // stale or foreign entry
     plan->seq[r] = seq;
+    plan->comb[r] = comb;
     applied++;
   }
   fclose(f);
@@ -853,19 +991,6 @@ void moe_experts_destroy(moe_experts_t x) {
   }
 }
 
-static int check_run_args(moe_plan_t p, const moe_tier *tiers, int n_tiers, const void *x, const int32_t *ids,
-                          const float *wts, void *out, int T, void *scratch) {
-  if (!plan_ok(p)) return fail(MOE_EINVAL, "invalid plan");
-  if (T < 0) return fail(MOE_EINVAL, "T=%d", T);
-  int rc = check_tiers(p, tiers, n_tiers);
-  if (rc != MOE_OK) return rc;
-  if (T == 0) return MOE_OK;
-  if (!x || !ids || !wts || !out || !scratch) return fail(MOE_EINVAL, "null tensor pointer");
-  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ids, 4) || !aligned(wts, 4) || !aligned(scratch, 256))
-    return fail(MOE_EINVAL, "x/out need 16-byte, ids/weights 4-byte, scratch 256-byte alignment");
-  return MOE_OK;
-}
-
 int moe_run(moe_plan_t p, const moe_tier *tiers, int n_tiers, const void *x, const int32_t *ids,
             const float *wts, void *out, int T, int deterministic, void *scratch, size_t scratch_bytes,
             void *stream) {
@@ -909,6 +1034,20 @@ int moe_debug_route(moe_plan_t p, const moe_tier *tiers, int n_tiers, const int3
   HIP_TRY(hipMemcpyAsync(off, sc + L.off, 4 * (size_t)(U + 1), hipMemcpyDeviceToDevice, s));
   HIP_TRY(hipMemcpyAsync(perm, sc + L.perm, 4 * R, hipMemcpyDeviceToDevice, s));
   HIP_TRY(hipMemcpyAsync(inv, sc + L.inv, 4 * R, hipMemcpyDeviceToDevice, s));
+  return MOE_OK;
+}
+
+int moe_ep_remap(const int32_t *topk_ids, const float *topk_weights, int T, int top_k, long long offset,
+                 int num_local, int32_t *out_ids, float *out_weights, void *stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T=%d", T);
+  if (top_k < 1 || top_k > 64) return fail(MOE_EINVAL, "top_k=%d outside [1, 64]", top_k);
+  if (num_local < 1) return fail(MOE_EINVAL, "num_local=%d", num_local);
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !topk_weights || !out_ids || !out_weights) return fail(MOE_EINVAL, "null pointer");
+  if (!aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(out_ids, 4) || !aligned(out_weights, 4))
+    return fail(MOE_EINVAL, "ids and weights need 4-byte alignment");
+  HIP_TRY(moe::launch_ep_remap(topk_ids, topk_weights, T, top_k, (long)offset, num_local, out_ids, out_weights,
+                               (hipStream_t)stream));
   return MOE_OK;
 }
 

@@ -15,6 +15,8 @@ constexpr int kMaxExperts = 1024;    // experts of all tiers together (LDS histo
 constexpr int kMaxTiers = 2;
 
 enum WFmt { W_MXFP4 = 1, W_NVFP4 = 2, W_NF3 = 3 };
+// activation forms of the GEMM1 epilogue (MOE_ACT_* of the C ABI)
+enum Act { ACT_SWIGLU = 0, ACT_SITU = 1 };
 
 // Bytes per row of the MXFP8 intermediate's scales: N/32 rounded up to a
 // multiple of 4, so every row starts 4-byte aligned.
@@ -77,6 +79,7 @@ struct GemmArgs {
   int T;                             // tokens of the chunk (rows of x / the accumulator)
   int w_on_input;                    // router weight scales GEMM1 (W4A16 / W3A16), not the GEMM2 result
   float alpha, beta;                 // SwiGLU form: gate * sigmoid(alpha gate) * (up + beta)
+  int act;                           // Act: SwiGLU (limit, alpha, beta) or SiTU
   // both tiers in one launch (prefill W4A16 / W3A16): the fields above are tier 0,
   // these tier 1, whose experts follow tier 0's in the unified index (u_base_b)
   const uint8_t *w13b, *s13b, *w2b, *s2b;
@@ -121,6 +124,7 @@ struct DecArgs {
   DecGroups *groups;                 // scratch
   int w_on_input;                    // router weight scales GEMM1 (W4A16 / W3A16), not the GEMM2 result
   float alpha, beta;                 // SwiGLU form: gate * sigmoid(alpha gate) * (up + beta)
+  int act;                           // Act: SwiGLU (limit, alpha, beta) or SiTU
   // W4A16 / W3A16 down GEMM split over two blocks per output row tile (scratch):
   float *dpart;                      // [K/16][16 tokens][16 columns] fp32 token sums, both halves added
   int *dcnt;                         // [K/16] halves finished; both zeroed by the up/gate kernel
@@ -133,6 +137,9 @@ __host__ __device__ constexpr int dec2_a16_halves(int N) { return (N + 127) / 12
 __host__ __device__ constexpr int dec2_a16_cols0(int N) {
   return dec2_a16_halves(N) == 1 ? N : ((((N + 127) / 128) + 1) / 2) * 128;
 }
+
+// Sets the calling thread's moe_last_error message; returns code.
+int set_error(int code, const char *msg);
 
 int decode_cpass(int K, int a8);
 size_t decode_gemm1_lds(int K, int cpass, int a8);
@@ -150,6 +157,8 @@ hipError_t launch_pf16_gemm1_tiers(const GemmArgs &a, int grid_tiles, hipStream_
 hipError_t launch_pf16_gemm2_tiers(const GemmArgs &a, int grid_tiles, hipStream_t s);
 hipError_t launch_finalize(int deterministic, const float *out_acc, const uint16_t *rb, const int32_t *inv,
                            int T, int K, int topk, uint16_t *out, hipStream_t s);
+hipError_t launch_ep_remap(const int32_t *ids, const float *w, long T, int topk, long offset, long num_local,
+                           int32_t *out_ids, float *out_w, hipStream_t s);
 hipError_t launch_quant_bf16(const uint16_t *x, long rows, int cols, uint8_t *q, uint8_t *sc, hipStream_t s);
 hipError_t launch_quant_f32(const float *h, long rows, int cols, uint8_t *q, uint8_t *sc, hipStream_t s);
 

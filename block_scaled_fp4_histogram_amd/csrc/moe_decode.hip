@@ -114,7 +114,7 @@ __device__ __forceinline__ DecExpert dec_expert(const DecArgs &a, int u) {
 // columns 32*hb + 16*s + 4*g + i for s, i.
 template <int NW>
 __device__ __forceinline__ void dec_swiglu(const float *red, int l, float gs, float limit, int has_limit, float alpha,
-                                           float beta, float *h) {
+                                           float beta, int act, float *h) {
 #pragma unroll
   for (int s = 0; s < 2; s++)
 #pragma unroll
@@ -126,7 +126,7 @@ __device__ __forceinline__ void dec_swiglu(const float *red, int l, float gs, fl
         up += red[(w * 16 + iu) * 64 + l];
         gate += red[(w * 16 + ig) * 64 + l];
       }
-      h[s * 4 + i] = silu_clamped(gate * gs, up * gs, limit, has_limit, alpha, beta);
+      h[s * 4 + i] = silu_clamped(gate * gs, up * gs, limit, has_limit, alpha, beta, act);
     }
 }
 
@@ -302,7 +302,7 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
       float h[8];
       // router weight on the input (W4A16 / W3A16): GEMM1 is linear, so it scales the accumulators
       const float gs = X.g13 * ((!A8 && a.w_on_input && have) ? a.topk_w[nth_bit(md, p0 + c)] : 1.0f);
-      dec_swiglu<NW>(red, l, gs, a.limit, a.has_limit, a.alpha, a.beta, h);
+      dec_swiglu<NW>(red, l, gs, a.limit, a.has_limit, a.alpha, a.beta, a.act, h);
       if (A8) {
         float amax = 0.f;
 #pragma unroll

@@ -52,8 +52,16 @@ __device__ __forceinline__ float e4m3_f32_branched(uint32_t b) {
   return (b & 0x80u) ? -v : v;
 }
 
+// Activation of one intermediate column from its GEMM1 pair.  act == ACT_SITU:
+// both branches softly capped by tanh, silu(4 tanh(gate / 4)) * 25 tanh(up / 25)
+// (vLLM "fused_moe/b12x" page: SiTU with beta 4 and linear beta 25, no limit).
+// Otherwise the SwiGLU, with the limit clamps and the OAI alpha / beta.
 __device__ __forceinline__ float silu_clamped(float gate, float up, float limit, int has_limit, float alpha,
-                                              float beta) {
+                                              float beta, int act = ACT_SWIGLU) {
+  if (act == ACT_SITU) {
+    const float g = 4.0f * tanhf(0.25f * gate), u = 25.0f * tanhf(0.04f * up);
+    return g / (1.0f + __expf(-g)) * u;
+  }
   if (has_limit) {
     gate = fminf(gate, limit);
     up = fminf(fmaxf(up, -limit), limit);

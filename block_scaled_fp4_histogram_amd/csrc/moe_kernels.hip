@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void k_gemm1_a8(GemmArgs a) {
       const int iu = (2 * s) * 4 + i, ig = (2 * s + 1) * 4 + i;
       const float up = red[0][iu][l] + red[1][iu][l] + red[2][iu][l] + red[3][iu][l];
       const float gate = red[0][ig][l] + red[1][ig][l] + red[2][ig][l] + red[3][ig][l];
-      h[s * 4 + i] = silu_clamped(gate, up, a.limit, a.has_limit, a.alpha, a.beta);
+      h[s * 4 + i] = silu_clamped(gate, up, a.limit, a.has_limit, a.alpha, a.beta, a.act);
     }
   // MXFP8 block of 32 intermediate columns of route c: 8 values here x 4 lanes
   float amax = 0.f;
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256) void k_gemm1_a16(GemmArgs a) {
         const int iu = (2 * s) * 4 + i, ig = (2 * s + 1) * 4 + i;
         const float up = (red[0][iu][l] + red[1][iu][l] + red[2][iu][l] + red[3][iu][l]) * gs;
         const float gate = (red[0][ig][l] + red[1][ig][l] + red[2][ig][l] + red[3][ig][l]) * gs;
-        h[i] = silu_clamped(gate, up, a.limit, a.has_limit, a.alpha, a.beta);
+        h[i] = silu_clamped(gate, up, a.limit, a.has_limit, a.alpha, a.beta, a.act);
       }
       uint2 v;
       v.x = pack_bf16x2(h[0], h[1]);
@@ -645,6 +645,66 @@ hipError_t launch_finalize(int deterministic, const float *out_acc, const uint16
   } else {
     hipLaunchKernelGGL(k_cast, grid, block, 0, s, out_acc, n8, out);
   }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ EP id remap
+//
+// One expert-parallel rank's view of the router output (sglang moe_b12x_next.py,
+// ep_remap / ep_remap_reference): lid = id - offset; a slot with lid in
+// [0, num_local) keeps lid and its weight; every other slot (another rank's
+// expert, padding) gets weight 0 and the lowest valid lid of its row, else of
+// the batch, else 0, so that every slot names an expert the batch already
+// streams.  One workgroup: a batch-wide minimum (wave reductions, then LDS
+// across the waves), then one thread per row.  Ids are compared in 64 bits so
+// that id - offset cannot wrap.
+constexpr int kRemapThreads = 1024;
+
+__device__ __forceinline__ bool remap_ok(int32_t id, long offset, long num_local, long *lid) {
+  *lid = (long)id - offset;
+  return *lid >= 0 && *lid < num_local;
+}
+
+__global__ __launch_bounds__(kRemapThreads) void k_ep_remap(const int32_t *ids, const float *w, long T, int topk,
+                                                            long offset, long num_local, int32_t *out_ids,
+                                                            float *out_w) {
+  __shared__ int s_min[kRemapThreads / 64];
+  const long R = T * topk;
+  int best = INT32_MAX;
+  for (long r = threadIdx.x; r < R; r += kRemapThreads) {
+    long lid;
+    if (remap_ok(ids[r], offset, num_local, &lid)) best = min(best, (int)lid);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) best = min(best, __shfl_xor(best, d));
+  if ((threadIdx.x & 63) == 0) s_min[threadIdx.x >> 6] = best;
+  __syncthreads();
+  best = INT32_MAX;
+#pragma unroll
+  for (int i = 0; i < kRemapThreads / 64; i++) best = min(best, s_min[i]);
+  const int fb = best < num_local ? best : 0;   // no local slot in the batch: expert 0
+  for (long t = threadIdx.x; t < T; t += kRemapThreads) {
+    const int32_t *row = ids + t * topk;
+    int row_min = INT32_MAX;
+    for (int j = 0; j < topk; j++) {
+      long lid;
+      if (remap_ok(row[j], offset, num_local, &lid)) row_min = min(row_min, (int)lid);
+    }
+    const int fill = row_min < num_local ? row_min : fb;
+    for (int j = 0; j < topk; j++) {
+      long lid;
+      const bool ok = remap_ok(row[j], offset, num_local, &lid);
+      out_ids[t * topk + j] = ok ? (int32_t)lid : fill;
+      out_w[t * topk + j] = ok ? w[t * topk + j] : 0.0f;
+    }
+  }
+}
+
+hipError_t launch_ep_remap(const int32_t *ids, const float *w, long T, int topk, long offset, long num_local,
+                           int32_t *out_ids, float *out_w, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_ep_remap, dim3(1), dim3(kRemapThreads), 0, s, ids, w, T, topk, offset, num_local, out_ids,
+                     out_w);
   return hipGetLastError();
 }
 

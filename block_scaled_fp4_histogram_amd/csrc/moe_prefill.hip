@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; s++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) h[s * 4 + i] = silu_clamped(acc[2 * s + 1][cb][i], acc[2 * s][cb][i], a.limit, a.has_limit, a.alpha, a.beta);
+      for (int i = 0; i < 4; i++) h[s * 4 + i] = silu_clamped(acc[2 * s + 1][cb][i], acc[2 * s][cb][i], a.limit, a.has_limit, a.alpha, a.beta, a.act);
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(h[i]));
@@ -870,7 +870,7 @@ __device__ __forceinline__ void pf16_gemm1_body(const GemmArgs &a, const PfWork 
       const float gs = g13 * (a.w_on_input ? a.topk_w[a.perm[p]] : 1.0f);
       float h[4];
 #pragma unroll
-      for (int i = 0; i < 4; i++) h[i] = silu_clamped(acc[1][cb][i] * gs, acc[0][cb][i] * gs, a.limit, a.has_limit, a.alpha, a.beta);
+      for (int i = 0; i < 4; i++) h[i] = silu_clamped(acc[1][cb][i] * gs, acc[0][cb][i] * gs, a.limit, a.has_limit, a.alpha, a.beta, a.act);
       uint2 v;
       v.x = pack_bf16x2(h[0], h[1]);
       v.y = pack_bf16x2(h[2], h[3]);

@@ -58,11 +58,23 @@ typedef enum {
 typedef enum { MOE_W_MXFP4 = 1, MOE_W_NVFP4 = 2, MOE_W_NF3 = 3 } moe_wfmt;
 typedef enum { MOE_A_MXFP8 = 1, MOE_A_BF16 = 2 } moe_afmt;
 typedef enum { MOE_W13_UP_GATE = 0, MOE_W13_GATE_UP = 1 } moe_w13_layout;
+/* Activation forms of the GEMM1 epilogue (vLLM "fused_moe/b12x" page,
+ * _supports_activation and _swiglu_params): the SwiGLU (with the plan's limit
+ * and the optional OAI alpha / beta) and SiTU (beta 4, linear beta 25, no
+ * limit). */
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SITU = 1 } moe_activation;
 /* Launch sequences of one chunk (the capacity ladder's choice unless a rung is
  * pinned): DECODE = two kernels, no route planner (T <= 16, T * top_k <= 64);
  * GENERAL = planner + 16-route-tile GEMMs + combine (any batch); PREFILL =
  * planner + 64-route-tile GEMMs + combine (N % 64 == 0). */
 typedef enum { MOE_SEQ_AUTO = 0, MOE_SEQ_DECODE = 1, MOE_SEQ_GENERAL = 2, MOE_SEQ_PREFILL = 3 } moe_sequence;
+/* How runs with deterministic = 0 combine the k slots of a token (the
+ * GENERAL and PREFILL sequences; DECODE folds them in its down GEMM either
+ * way): ATOMIC = fp32 atomic adds into an accumulator, then one bf16 cast;
+ * ROUTE_BUFFER = the deterministic combine (per-slot bf16 route buffer and a
+ * slot-order top-k sum).  AUTO = the capacity ladder's choice: ROUTE_BUFFER on
+ * the PREFILL sequence, ATOMIC on GENERAL. */
+typedef enum { MOE_COMBINE_AUTO = 0, MOE_COMBINE_ATOMIC = 1, MOE_COMBINE_ROUTE_BUFFER = 2 } moe_combine;
 
 typedef struct moe_plan_s *moe_plan_t;       /* one layer geometry (host memory only) */
 typedef struct moe_experts_s *moe_experts_t; /* one layer's (or tier's) prepared weights */
@@ -139,6 +151,9 @@ void moe_experts_destroy(moe_experts_t experts);
  *                   with atomics (run-to-run order may vary);
  *                   1: per-slot route buffer + fixed-order top-k sum,
  *                   bit-stable run to run (moe_b12x_next.py, DETERMINISTIC).
+ *                   With 0, a rung whose combine is ROUTE_BUFFER (the
+ *                   ladder's choice on the PREFILL sequence; see
+ *                   moe_plan_set_combine) combines as 1 does.
  *                   Decode-size batches (<= 16 tokens, <= 64 routes) run two
  *                   kernels that fold each token's slots in slot order in
  *                   either mode (bit-stable); with 16-bit activations the down
@@ -171,13 +186,25 @@ int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows);
  * N % 64 != 0) is MOE_EUNSUPPORTED.  moe_plan_sequence returns the sequence a
  * batch of `tokens` runs with now (0 on a bad plan).  Host only.
  *
- * moe_plan_autotune races every sequence each listed batch size's rung can
- * take, on a seeded synthetic batch of the rung's full size with the caller's
- * prepared experts (`reps` timed runs after two warm-up runs, median), and pins
- * the rung to the fastest.  us_out (NULL or [n][3]) receives the median times
- * of DECODE, GENERAL and PREFILL in microseconds, NaN where not eligible.  It
- * allocates and synchronises (it is a tuning session, not part of the layer):
- * call it before graph capture.
+ * moe_plan_set_combine pins the combine of deterministic = 0 runs at the rung
+ * of `tokens` (moe_combine; AUTO: back to the ladder's choice);
+ * moe_plan_combine returns the one such a batch uses now (ATOMIC or
+ * ROUTE_BUFFER; 0 on a bad plan).  The scratch a run needs follows the pin
+ * (moe_scratch_bytes), so pin before sizing the arena.  Host only.
+ *
+ * moe_plan_autotune races, at the rung of each listed batch size, every launch
+ * sequence the rung can take and, for deterministic = 0, both combines of the
+ * GENERAL and PREFILL sequences, on a seeded synthetic batch of the rung's
+ * full size with the caller's prepared experts (`reps` timed runs after two
+ * warm-up runs, median), and pins the rung's sequence and combine to the
+ * fastest.  us_out (NULL or [n][5]) receives the median microseconds of
+ * DECODE, GENERAL-atomic, GENERAL-route buffer, PREFILL-atomic and
+ * PREFILL-route buffer, NaN where not raced (deterministic races fill the
+ * route-buffer entries).  moe_plan_autotune_batch races the rung of T on the
+ * caller's own batch instead (device x [T, K] bf16, topk_ids, topk_weights;
+ * T <= max_tokens; us_out NULL or [5]): the workload's routing, e.g. skewed
+ * expert loads, decides.  Both allocate and synchronise (a tuning session,
+ * not part of the layer): call them before graph capture.
  *
  * moe_plan_save_tuning writes the plan's pinned rungs to a text file, one line
  * per rung keyed by the geometry (E, K, N, top_k, act_format, max_tokens),
@@ -187,8 +214,13 @@ int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows);
  * the file cannot be read. */
 int moe_plan_set_sequence(moe_plan_t plan, int tokens, int seq);
 int moe_plan_sequence(moe_plan_t plan, int tokens);
+int moe_plan_set_combine(moe_plan_t plan, int tokens, int combine);
+int moe_plan_combine(moe_plan_t plan, int tokens);
 int moe_plan_autotune(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const int *tokens, int n, int deterministic,
                       int reps, void *stream, float *us_out);
+int moe_plan_autotune_batch(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const void *x,
+                            const int32_t *topk_ids, const float *topk_weights, int T, int deterministic, int reps,
+                            void *stream, float *us_out);
 int moe_plan_save_tuning(moe_plan_t plan, const char *path);
 int moe_plan_load_tuning(moe_plan_t plan, const char *path);
 
@@ -208,6 +240,40 @@ int moe_plan_set_router_weight_on_input(moe_plan_t plan, int enable);
  * only for MOE_A_BF16 plans (the page refuses this activation with W4A8):
  * MOE_EUNSUPPORTED otherwise; non-finite values: MOE_EINVAL.  Host only. */
 int moe_plan_set_swiglu_oai(moe_plan_t plan, float alpha, float beta);
+
+/*
+ * moe_ep_remap -- one expert-parallel rank's view of the router output
+ * (sglang "moe_b12x_next.py", ep_remap / ep_remap_reference: the step before
+ * the layer when the experts are sharded over ranks).  For each slot,
+ * lid = topk_ids[t,j] - offset (computed in 64 bits, so no id wraps):
+ *   lid in [0, num_local)  -> out_ids = lid, out_weights = topk_weights[t,j];
+ *   otherwise (an expert of another rank, padding)
+ *                          -> out_weights = 0 and out_ids = the lowest valid
+ *                             lid of row t, else the lowest of the batch,
+ *                             else 0,
+ * so every slot names an expert whose weights the batch already streams and a
+ * zero weight makes the slot add nothing.
+ *   topk_ids      device int32 [T, top_k], contiguous (global ids)
+ *   topk_weights  device fp32 [T, top_k], contiguous
+ *   out_ids       device int32 [T, top_k] (local ids, for a plan with E = num_local)
+ *   out_weights   device fp32 [T, top_k]; may not alias the inputs
+ *   top_k 1 .. 64, num_local >= 1; T = 0 is a no-op.
+ * One kernel on `stream`, no allocation, no synchronisation (graph-capturable).
+ * Returns MOE_EINVAL for bad sizes or null / misaligned pointers, MOE_EHIP if
+ * the launch fails.  The caller owns every buffer.
+ */
+int moe_ep_remap(const int32_t *topk_ids, const float *topk_weights, int T, int top_k, long long offset,
+                 int num_local, int32_t *out_ids, float *out_weights, void *stream);
+
+/* The activation form of the plan (moe_activation).  MOE_ACT_SITU: both
+ * branches softly capped by tanh,
+ *     h = silu(4 tanh(gate / 4)) * 25 tanh(up / 25)
+ * (vLLM "fused_moe/b12x" page: SiTU is taken only with beta 4 and linear beta
+ * 25, without a limit, and is one of the two activations W4A8 runs; the page
+ * does not print the formula, this is the reading taken).  Valid for every
+ * activation format; MOE_EUNSUPPORTED on a plan with a swiglu limit or OAI
+ * alpha / beta, or for an unknown form.  Host only. */
+int moe_plan_set_activation(moe_plan_t plan, int act);
 
 /* ---- instrumentation ------------------------------------------------- */
 

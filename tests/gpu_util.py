@@ -23,11 +23,14 @@ def dev(a, dtype=None):
 class DeviceLayer:
     """Plan + prepared experts of a Problem, on cuda:0."""
 
-    def __init__(self, prob, max_tokens=None, gate_up=False, weight_on_input=False, swiglu_oai=None):
+    def __init__(self, prob, max_tokens=None, gate_up=False, weight_on_input=False, swiglu_oai=None, act=None):
         c = prob.cfg
         self.prob = prob
-        self.plan = M.Plan(c.E, c.K, c.N, c.topk, c.limit, A_OF[prob.tiers[0].fmt],
+        limit = c.limit if act in (None, M.ACT_SWIGLU) else None   # SiTU takes no limit
+        self.plan = M.Plan(c.E, c.K, c.N, c.topk, limit, A_OF[prob.tiers[0].fmt],
                            M.W13_GATE_UP if gate_up else M.W13_UP_GATE, max_tokens or max(c.T, 1))
+        if act is not None:
+            self.plan.set_activation(act)
         if weight_on_input:
             self.plan.set_router_weight_on_input(True)
         if swiglu_oai is not None:

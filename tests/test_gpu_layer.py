@@ -307,23 +307,81 @@ def test_pinned_sequence(name, seq, deterministic):
     assert_rows_match(out, acc, label=f"{name} sequence {seq} det={deterministic}", prob=L.prob)
 
 
-def test_autotune_pins_the_fastest_sequence():
+_SLOT_SEQ = (M.SEQ_DECODE, M.SEQ_GENERAL, M.SEQ_GENERAL, M.SEQ_PREFILL, M.SEQ_PREFILL)
+_SLOT_COMB = (None, M.COMBINE_ATOMIC, M.COMBINE_ROUTE_BUFFER, M.COMBINE_ATOMIC, M.COMBINE_ROUTE_BUFFER)
+
+
+def _check_pins(plan, t, us, deterministic):
+    times = [v if not math.isnan(v) else float("inf") for v in us]
+    k = times.index(min(times))
+    assert plan.sequence(t) == _SLOT_SEQ[k]
+    if not deterministic and _SLOT_COMB[k] is not None:
+        assert plan.combine(t) == _SLOT_COMB[k]
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_autotune_pins_the_fastest_sequence_and_combine(deterministic):
     L = layer("hybrid_small")          # 29 tokens x 5 slots: general or prefill; 8 tokens: all three
     T = L.prob.cfg.T
     try:
-        us = L.plan.autotune(L.tiers, [T, 8], reps=3)
-        assert math.isnan(us[0][0]) and us[0][1] > 0 and us[0][2] > 0
-        assert all(v > 0 for v in us[1])
-        seqs = (M.SEQ_DECODE, M.SEQ_GENERAL, M.SEQ_PREFILL)
+        us = L.plan.autotune(L.tiers, [T, 8], deterministic=deterministic, reps=3)
+        assert math.isnan(us[0][0]) and all(v > 0 for v in us[0][2::2])
+        assert us[1][0] > 0 and us[1][2] > 0 and us[1][4] > 0
+        if deterministic:
+            assert all(math.isnan(v) for v in (us[0][1], us[0][3], us[1][1], us[1][3]))
+        else:
+            assert us[0][1] > 0 and us[0][3] > 0
         for i, t in enumerate((T, 8)):
-            times = [v if not math.isnan(v) else float("inf") for v in us[i]]
-            assert L.plan.sequence(t) == seqs[times.index(min(times))]
-        out = L.run()
+            _check_pins(L.plan, t, us[i], deterministic)
+        out = L.run(deterministic=deterministic)
     finally:
-        L.plan.set_sequence(T, M.SEQ_AUTO)
-        L.plan.set_sequence(8, M.SEQ_AUTO)
+        for t in (T, 8):
+            L.plan.set_sequence(t, M.SEQ_AUTO)
+            L.plan.set_combine(t, M.COMBINE_AUTO)
     acc, _ = O.moe_problem(L.prob)
     assert_rows_match(out, acc, label="hybrid_small after autotune")
+
+
+@pytest.mark.parametrize("name", ["prefill_small", "nvfp4_prefill_small"])
+def test_autotune_on_the_workload_s_own_batch(name):
+    """The race at the rung of the caller's batch (Zipf-skewed loads in prefill_small)
+    on that batch; the pinned (sequence, combine) runs the layer within tolerance."""
+    L = layer(name)
+    p = L.prob
+    T = p.cfg.T
+    x, ids, wts = dev(p.x, torch.bfloat16), dev(p.ids), dev(p.wts)
+    before = L.plan.sequence(T)
+    try:
+        us = L.plan.autotune_batch(L.tiers, x, ids, wts, reps=3)
+        assert all(v > 0 for v in us[1:])
+        _check_pins(L.plan, T, us, False)
+        out = L.run(deterministic=False)
+    finally:
+        L.plan.set_sequence(T, before)
+        L.plan.set_combine(T, M.COMBINE_AUTO)
+    acc, _ = O.moe_problem(p)
+    a8 = p.tiers[0].fmt == I.FMT_MXFP4
+    assert_rows_match(out, acc, label=f"{name} after autotune_batch", prob=p if a8 else None)
+
+
+@pytest.mark.parametrize("name,T", [("prefill_small", 160), ("mxfp4_ragged", 37), ("nvfp4_prefill_small", 150)])
+def test_combine_pins_give_the_same_layer(name, T):
+    """deterministic = 0 with the route-buffer combine equals the deterministic run bit for
+    bit; with atomics it is within tolerance; both on the pinned or ladder sequence."""
+    L = layer(name)
+    p = L.prob
+    acc, _ = O.moe_problem(p)
+    a8 = p.tiers[0].fmt == I.FMT_MXFP4
+    det = L.run(deterministic=True)
+    try:
+        L.plan.set_combine(T, M.COMBINE_ROUTE_BUFFER)
+        rb = L.run(deterministic=False)
+        assert torch.equal(rb.view(torch.int16), det.view(torch.int16))
+        L.plan.set_combine(T, M.COMBINE_ATOMIC)
+        at = L.run(deterministic=False)
+        assert_rows_match(at, acc, label=f"{name} atomic combine", prob=p if a8 else None)
+    finally:
+        L.plan.set_combine(T, M.COMBINE_AUTO)
 
 
 # ---- production rungs at full geometry -------------------------------------------------
@@ -400,3 +458,21 @@ def test_sixteen_bit_plans_with_a_decode_sized_last_chunk(name, max_tokens, dete
     out = L.run(deterministic=deterministic)
     acc, _ = O.moe_problem(prob)
     assert_rows_match(out, acc, label=f"{name} chunks of {max_tokens} det={deterministic}")
+
+
+# SiTU, silu(4 tanh(gate/4)) * 25 tanh(up/25), on every launch sequence and both
+# activation formats (W4A8 too: the page runs SiTU there): decode (tiny, hybrid_decode),
+# general (mxfp4_ragged, nvfp4_small) and prefill (prefill_small, nvfp4_prefill_small,
+# hybrid_prefill_small).
+@pytest.mark.parametrize("name", ["tiny", "mxfp4_ragged", "prefill_small", "nvfp4_small", "hybrid_decode",
+                                  "nvfp4_prefill_small", "hybrid_prefill_small"])
+def test_situ(name):
+    L = layer(name, act=M.ACT_SITU)
+    acc, _ = O.moe_problem(L.prob, act_kind=O.ACT_SITU)
+    a8 = L.prob.tiers[0].fmt == I.FMT_MXFP4
+    for det in (False, True):
+        out = L.run(deterministic=det)
+        assert_rows_match(out, acc, label=f"{name} situ det={det}", prob=L.prob if a8 else None,
+                          act_kind=O.ACT_SITU)
+    plain, _ = O.moe_problem(L.prob)
+    assert not np.allclose(acc, plain, rtol=1e-2), "SiTU must change this case"
