@@ -277,6 +277,25 @@ def run(plan: Plan, tiers: Sequence, x, topk_ids, topk_weights, out=None, determ
     return out
 
 
+def run_noalloc(plan: Plan, tiers: Sequence, x, topk_ids, topk_weights, out, deterministic: bool = False,
+                stream=None):
+    """The layer with the library's static 64 MiB device arena as scratch (moe_run_noalloc):
+    no device allocation by the library or here (out must be given)."""
+    import torch
+    if x is None or x.dim() != 2:
+        raise ValueError("x must be a [T, K] tensor")
+    T = x.shape[0]
+    for device in (False, True):
+        _need(x, "x", torch.bfloat16, device, shape=(T, plan.K))
+        _need(topk_ids, "topk_ids", torch.int32, device, shape=(T, plan.top_k))
+        _need(topk_weights, "topk_weights", torch.float32, device, shape=(T, plan.top_k))
+        _need(out, "out", torch.bfloat16, device, shape=(T, plan.K))
+    arr, keep = _tiers(tiers, plan)
+    _check(_lib.load().moe_run_noalloc(plan.handle, arr, len(tiers), _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
+                                       _ptr(out), T, int(bool(deterministic)), _stream(stream)))
+    return out
+
+
 def ep_remap(topk_ids, topk_weights, offset: int, num_local: int, out_ids=None, out_weights=None, stream=None):
     """Expert-parallel id remap (moe_ep_remap): global top-k ids of [T, k] -> this rank's
     local ids for experts [offset, offset + num_local); other slots get weight 0 and an

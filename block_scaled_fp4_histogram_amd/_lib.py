@@ -22,6 +22,7 @@ SIGNATURES = {
     "moe_unpack_weights": (_i, [_vp, _vp]),
     "moe_experts_destroy": (None, [_vp]),
     "moe_run": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]),
+    "moe_run_noalloc": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _vp]),
     "moe_last_error": (C.c_char_p, []),
     "moe_plan_capacity": (_i, [_vp, _i, C.POINTER(_i)]),
     "moe_plan_set_sequence": (_i, [_vp, _i, _i]),

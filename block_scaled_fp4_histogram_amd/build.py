@@ -8,7 +8,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_gfx950.so")
 SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_decode.hip"),
-           os.path.join(CSRC, "moe_prefill.hip"), os.path.join(CSRC, "moe_api.cpp")]
+           os.path.join(CSRC, "moe_prefill.hip"), os.path.join(CSRC, "moe_static.hip"),
+           os.path.join(CSRC, "moe_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

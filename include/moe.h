@@ -167,6 +167,25 @@ int moe_run(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const void *x, 
             const float *topk_weights, void *out, int T, int deterministic, void *scratch,
             size_t scratch_bytes, void *stream);
 
+/*
+ * moe_run_noalloc -- moe_run with the scratch arena taken from a static device
+ * array of the library instead of a caller buffer.  For callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *   Arguments as moe_run, without scratch / scratch_bytes.
+ *   The array holds 64 MiB per GPU (held from the library's load until the
+ *   process ends); a batch whose moe_scratch_bytes(plan, T, deterministic)
+ *   exceeds it is refused with MOE_ESCRATCH (e.g. 4096 tokens at K = 7168;
+ *   the 8-token decode batch needs about 0.3 MiB).
+ *   The first call on each device looks up that device's copy of the array
+ *   (make it outside graph capture, e.g. with T = 0); later calls allocate,
+ *   free and synchronise nothing.  Nothing in the array needs to start at zero.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ *   (two streams or two host threads) race.
+ */
+int moe_run_noalloc(moe_plan_t plan, const moe_tier *tiers, int n_tiers, const void *x, const int32_t *topk_ids,
+                    const float *topk_weights, void *out, int T, int deterministic, void *stream);
+
 /* Message of the calling thread's most recent failure ("" if none). */
 const char *moe_last_error(void);
 
