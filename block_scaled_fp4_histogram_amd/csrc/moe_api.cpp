@@ -119,10 +119,10 @@ bool route_buffer(const moe_plan_s *p, int cap, int deterministic) {
 
 // Carving of the scratch arena for one chunk of `cap` tokens.
 struct Layout {
-  size_t ru, lrank, inv, perm, cnt, off, chunk_hist, tile_u, tile_row0, tier_tiles;
+  size_t ru, lrank, inv, perm, cnt, off, chunk_hist, tile_u, tile_row0, tier_tiles, tile_u2, tile_row02, tier_tiles2;
   size_t xq, xs, hq, hs, hb, acc, rb, dpart, dcnt;
   size_t total;
-  int R, G, max_tiles;
+  int R, G, max_tiles, max_tiles2;
 };
 
 Layout layout(const moe_plan_s *p, int cap, int deterministic) {
@@ -150,6 +150,11 @@ Layout layout(const moe_plan_s *p, int cap, int deterministic) {
   L.tile_row0 = take(4 * (size_t)L.max_tiles);
   L.tier_tiles = take(4 * 2 * moe::kMaxTiers);
   if (p->afmt == MOE_A_MXFP8) {
+    // the prefill up/gate GEMM's table of 128-route tiles
+    L.max_tiles2 = (int)((R + moe::kPfWideRows - 1) / moe::kPfWideRows + std::min<size_t>(U, R));
+    L.tile_u2 = take(4 * (size_t)L.max_tiles2);
+    L.tile_row02 = take(4 * (size_t)L.max_tiles2);
+    L.tier_tiles2 = take(4 * 2 * moe::kMaxTiers);
     L.xq = take((size_t)cap * p->K);
     L.xs = take((size_t)cap * (p->K / 32));
     L.hq = take(R * p->N);
@@ -313,6 +318,14 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ra.tile_u = I32(L.tile_u);
   ra.tile_row0 = I32(L.tile_row0);
   ra.tier_tiles = I32(L.tier_tiles);
+  // 128-route tiles for the up/gate GEMM (its activation offsets are 32-bit)
+  const bool wide = prefill && p->afmt == MOE_A_MXFP8 && (uint64_t)T * p->K < (1ull << 32);
+  if (wide) {
+    ra.tile_rows2 = moe::kPfWideRows;
+    ra.tile_u2 = I32(L.tile_u2);
+    ra.tile_row02 = I32(L.tile_row02);
+    ra.tier_tiles2 = I32(L.tier_tiles2);
+  }
   ra.x = x;
   ra.T = T;
   ra.K = p->K;
@@ -407,7 +420,14 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     ga.g13 = xp->g13;
     ga.g2 = xp->g2;
     const int grid_tiles = row_tiles + std::min(xp->E, R);
-    if (prefill && xp->wfmt == MOE_W_MXFP4) HIP_TRY(moe::launch_pf_gemm1(ga, grid_tiles, s));
+    if (wide && xp->wfmt == MOE_W_MXFP4) {
+      moe::GemmArgs gw = ga;
+      gw.tile_rows = moe::kPfWideRows;
+      gw.tile_u = I32(L.tile_u2);
+      gw.tile_row0 = I32(L.tile_row02);
+      gw.tier_tiles = I32(L.tier_tiles2);
+      HIP_TRY(moe::launch_pf_gemm1(gw, (R + moe::kPfWideRows - 1) / moe::kPfWideRows + std::min(xp->E, R), s));
+    } else if (prefill && xp->wfmt == MOE_W_MXFP4) HIP_TRY(moe::launch_pf_gemm1(ga, grid_tiles, s));
     else if (prefill) HIP_TRY(moe::launch_pf16_gemm1(xp->wfmt, ga, grid_tiles, s));
     else HIP_TRY(moe::launch_gemm1(xp->wfmt, ga, grid_tiles, s));
     u_base += xp->E;

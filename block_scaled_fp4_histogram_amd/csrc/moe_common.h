@@ -9,6 +9,7 @@ namespace moe {
 
 constexpr int kTileRows = 16;        // routes of one tile of the general GEMM kernels
 constexpr int kPfTileRows = 64;      // routes of one tile of the prefill kernels
+constexpr int kPfWideRows = 128;     // routes of one tile of the prefill W4A8 up/gate kernel
 constexpr int kPrefillMinT = 512;    // smallest batch the ladder runs with the prefill kernels
 constexpr int kRouteChunk = 1024;    // routes handled by one route-planner block
 constexpr int kMaxExperts = 1024;    // experts of all tiers together (LDS histogram size)
@@ -49,6 +50,9 @@ struct RouteArgs {
   int32_t *ru, *lrank, *chunk_hist;  // per-route expert / in-chunk rank; [G][U] counts
   int32_t *cnt, *off, *perm, *inv;
   int32_t *tile_u, *tile_row0, *tier_tiles;
+  // optional second tile table of tile_rows2 routes per tile (NULL: none)
+  int tile_rows2;
+  int32_t *tile_u2, *tile_row02, *tier_tiles2;
   // work fused into the same launch by extra blocks
   const uint16_t *x;                 // bf16 [T, K] (MXFP8 quantisation when xq != NULL)
   int T, K;

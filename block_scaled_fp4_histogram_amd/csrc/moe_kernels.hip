@@ -46,56 +46,83 @@ __device__ __forceinline__ int resolve_u(int id, const RouteArgs &a) {
   return -1;
 }
 
-// Offsets and tile table from per-expert counts held in LDS cnt[U].  Wave 0
-// scans (each lane owns a run of consecutive experts, runs combined with a
-// wave prefix sum); leaves the exclusive offsets in LDS off[U+1].
+// Tile table of `rows` routes per tile from the per-expert counts: wave 1
+// scans the tile counts (each lane owns a run of consecutive experts, runs
+// combined with a wave prefix sum) into LDS tbeg[U+1]; after the barrier each
+// thread writes whole tiles, finding a tile's expert by binary search over
+// tbeg (one thread per expert would write a hot expert's ~60 tiles alone).
+__device__ void write_tiles(const RouteArgs &a, int U, const int *cnt, int *tbeg, int rows, int32_t *tile_u,
+                            int32_t *tile_row0, int32_t *tier_tiles) {
+  const int tid = threadIdx.x;
+  if (tid >= 64 && tid < 128) {
+    const int lane = tid - 64, per = (U + 63) / 64, b = lane * per;
+    int nt = 0;
+    for (int i = 0; i < per; i++)
+      if (b + i < U) nt += (cnt[b + i] + rows - 1) / rows;
+    int it = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int vt = __shfl_up(it, d);
+      if (lane >= d) it += vt;
+    }
+    int rt = it - nt;
+    for (int i = 0; i < per; i++)
+      if (b + i < U) {
+        tbeg[b + i] = rt;
+        rt += (cnt[b + i] + rows - 1) / rows;
+      }
+    if (lane == 63) tbeg[U] = it;
+  }
+  __syncthreads();
+  const int ntiles = tbeg[U];
+  for (int t = tid; t < ntiles; t += blockDim.x) {
+    int lo = 0, hi = U - 1;   // the last u with tbeg[u] <= t (experts without routes have empty ranges)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tbeg[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    tile_u[t] = lo;
+    tile_row0[t] = (t - tbeg[lo]) * rows;
+  }
+  if (tid == 0) {
+    tier_tiles[0] = 0;
+    tier_tiles[1] = tbeg[a.E0];
+    tier_tiles[2] = tbeg[a.E0];
+    tier_tiles[3] = tbeg[U];
+  }
+}
+
+// Offsets and tile table(s) from per-expert counts held in LDS cnt[U].  Wave 0
+// scans the counts (each lane owns a run of consecutive experts, runs combined
+// with a wave prefix sum); leaves the exclusive offsets in LDS off[U+1].
 __device__ void finish_plan(const RouteArgs &a, int U, const int *cnt, int *off, int *tbeg) {
   const int tid = threadIdx.x;
   if (tid < 64) {
     const int per = (U + 63) / 64, b = tid * per;
-    int s = 0, nt = 0;
+    int s = 0;
     for (int i = 0; i < per; i++)
-      if (b + i < U) {
-        s += cnt[b + i];
-        nt += (cnt[b + i] + a.tile_rows - 1) / a.tile_rows;
-      }
-    int is = s, it = nt;
+      if (b + i < U) s += cnt[b + i];
+    int is = s;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int vs = __shfl_up(is, d), vt = __shfl_up(it, d);
-      if (tid >= d) {
-        is += vs;
-        it += vt;
-      }
+      const int vs = __shfl_up(is, d);
+      if (tid >= d) is += vs;
     }
-    int rs = is - s, rt = it - nt;
+    int rs = is - s;
     for (int i = 0; i < per; i++)
       if (b + i < U) {
         off[b + i] = rs;
-        tbeg[b + i] = rt;
         rs += cnt[b + i];
-        rt += (cnt[b + i] + a.tile_rows - 1) / a.tile_rows;
       }
-    if (tid == 63) {
-      off[U] = is;
-      tbeg[U] = it;
-    }
+    if (tid == 63) off[U] = is;
   }
-  __syncthreads();
+  write_tiles(a, U, cnt, tbeg, a.tile_rows, a.tile_u, a.tile_row0, a.tier_tiles);
   for (int u = tid; u <= U; u += blockDim.x) a.off[u] = off[u];
-  for (int u = tid; u < U; u += blockDim.x) {
-    a.cnt[u] = cnt[u];
-    const int tb = tbeg[u];
-    for (int i = 0; i * a.tile_rows < cnt[u]; i++) {
-      a.tile_u[tb + i] = u;
-      a.tile_row0[tb + i] = i * a.tile_rows;
-    }
-  }
-  if (tid == 0) {
-    a.tier_tiles[0] = 0;
-    a.tier_tiles[1] = tbeg[a.E0];
-    a.tier_tiles[2] = tbeg[a.E0];
-    a.tier_tiles[3] = tbeg[U];
+  for (int u = tid; u < U; u += blockDim.x) a.cnt[u] = cnt[u];
+  if (a.tile_u2) {
+    __syncthreads();   // tbeg is reused
+    write_tiles(a, U, cnt, tbeg, a.tile_rows2, a.tile_u2, a.tile_row02, a.tier_tiles2);
   }
 }
 

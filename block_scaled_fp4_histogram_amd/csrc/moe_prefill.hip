@@ -100,6 +100,7 @@ struct PfSrc {
   const uint8_t *brow[2];         // this lane's activation rows of its two B blocks
   const uint8_t *bsrow;           // activation scale row of route (lane)
   int kbytes;                     // reduction length (bytes of one activation row)
+  int nrb;                        // 16-route blocks holding routes of the tile (the rest are padding)
 };
 
 // A wave's weight operands of one k-tile: row tiles 4w + q, and the aligned
@@ -146,11 +147,14 @@ __device__ __forceinline__ void pf_issue_b(PfStage &S, const PfSrc &src, int kt,
 // otherwise wait for every ring stage in flight) and waited for in the same
 // statement (a wait in a later statement would let the compiler copy
 // registers still in flight).
-__device__ __forceinline__ void pf_read_b(v4i (&b)[4][2], int (&sb)[4], const PfStage &S, int l) {
+// B0: the first of the 8 activation blocks (8 rows each) of the 64 routes read;
+// S0: their scales, 4 bytes a route.
+__device__ __forceinline__ void pf_read_b_at(v4i (&b)[4][2], int (&sb)[4], const uint8_t (*B0)[1024],
+                                             const uint8_t *S0, int l) {
   const int c = l & 15, g = l >> 4, r8 = c & 7;
-  const uint8_t *blk = &S.B[c >> 3][0];   // + 2 KB per route block
+  const uint8_t *blk = &B0[c >> 3][0];   // + 2 KB per route block
   const uint32_t vb0 = lds_addr(blk + pf_slot(r8, g) * 16), vb1 = lds_addr(blk + pf_slot(r8, 4 + g) * 16),
-                 vsb = lds_addr(&S.S[c * 4 + g]);   // + 64 bytes per route block
+                 vsb = lds_addr(&S0[c * 4 + g]);   // + 64 bytes per route block
   asm volatile(
       "ds_read_b128 %0, %12\n"
       "ds_read_b128 %1, %13\n"
@@ -171,6 +175,10 @@ __device__ __forceinline__ void pf_read_b(v4i (&b)[4][2], int (&sb)[4], const Pf
       : "memory");
 }
 
+__device__ __forceinline__ void pf_read_b(v4i (&b)[4][2], int (&sb)[4], const PfStage &S, int l) {
+  pf_read_b_at(b, sb, S.B, S.S, l);
+}
+
 // 16 block-scaled MFMAs of one k-tile (4 row tiles x 4 route blocks).  Past
 // the reduction length (a partial last k-tile; FULL: none) the activation
 // bytes are zeroed and both scales set to 2^-127, so the products there are
@@ -178,7 +186,7 @@ __device__ __forceinline__ void pf_read_b(v4i (&b)[4][2], int (&sb)[4], const Pf
 // column, elements = 4 routes).
 template <bool SWAP, bool FULL>
 __device__ __forceinline__ void pf_mma(const PfW &wt, const v4i (&b)[4][2], const int (&sb)[4], int kt, int kbytes,
-                                       int l, v4f (*acc)[4]) {
+                                       int nrb, int l, v4f (*acc)[4]) {
   const int g = l >> 4;
   const bool in0 = FULL || kt * 128 + 16 * g < kbytes, in1 = FULL || kt * 128 + 64 + 16 * g < kbytes;
   const bool gin = FULL || (kt * 4 + g) * 32 < kbytes;   // 32-column group g of this k-tile exists
@@ -189,17 +197,20 @@ __device__ __forceinline__ void pf_mma(const PfW &wt, const v4i (&b)[4][2], cons
     const v4i b1 = in1 ? b[cb][1] : v4i{0, 0, 0, 0};
     bop[cb] = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
   }
+  // route blocks past the tile's last route hold padding: their MFMAs are skipped
 #pragma unroll
   for (int q = 0; q < kPfQ; q++) {
     const int sa = gin ? (int)(wt.sa[q] >> (8 * (l & 3))) : 0;   // the MFMA takes the low byte
 #pragma unroll
     for (int cb = 0; cb < 4; cb++) {
-      const int sbv = gin ? sb[cb] : 0;
-      if (SWAP)
-        acc[q][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bop[cb], fp4_operand(wt.a[q]), acc[q][cb], 0, 4,
-                                                                      0, sbv, 0, sa);
-      else
-        acc[q][cb] = mfma_fp4_fp8(wt.a[q], bop[cb], acc[q][cb], sa, sbv);
+      if (cb < nrb) {
+        const int sbv = gin ? sb[cb] : 0;
+        if (SWAP)
+          acc[q][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bop[cb], fp4_operand(wt.a[q]), acc[q][cb], 0,
+                                                                        4, 0, sbv, 0, sa);
+        else
+          acc[q][cb] = mfma_fp4_fp8(wt.a[q], bop[cb], acc[q][cb], sa, sbv);
+      }
     }
   }
 }
@@ -239,8 +250,8 @@ __device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, PfW (&ring)[
     // a step that issues k-tile kt + ST - 1 is not the last one, so its k-tile
     // is whole: known at compile time, the partial-tile variant and the
     // accumulator copies where the two variants meet drop out of the loop
-    if (ISSUE == 1 || (kt + 1) * 128 <= src.kbytes) pf_mma<SWAP, true>(ring[R], b, sb, kt, src.kbytes, l, acc);
-    else pf_mma<SWAP, false>(ring[R], b, sb, kt, src.kbytes, l, acc);
+    if (ISSUE == 1 || (kt + 1) * 128 <= src.kbytes) pf_mma<SWAP, true>(ring[R], b, sb, kt, src.kbytes, src.nrb, l, acc);
+    else pf_mma<SWAP, false>(ring[R], b, sb, kt, src.kbytes, src.nrb, l, acc);
     __builtin_amdgcn_s_setprio(0);
   }
 }
@@ -378,6 +389,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8(GemmArgs a) {
     src.brow[j] = a.xq + (size_t)(a.perm[wk.p0 + (row < wk.rows ? row : 0)] / a.topk) * K;
   }
   src.bsrow = a.xs + (size_t)(a.perm[wk.p0 + (l < wk.rows ? l : 0)] / a.topk) * (K / 32);
+  src.nrb = 4;   // every route block (skipping padding here costs registers this kernel does not have)
   v4f acc[kPfQ][4];
   zero_acc<kPfQ, 4>(acc);
   pf_kloop<false>(L, src, wu, acc);
@@ -394,6 +406,175 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8(GemmArgs a) {
     for (int s = 0; s < 2; s++)
 #pragma unroll
       for (int i = 0; i < 4; i++) h[s * 4 + i] = silu_clamped(acc[2 * s + 1][cb][i], acc[2 * s][cb][i], a.limit, a.has_limit, a.alpha, a.beta, a.act);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(h[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    float inv;
+    const uint32_t sbyte = mx_scale(amax, &inv);
+    if (row < wk.rows) {
+      const size_t p = (size_t)(wk.p0 + row);
+#pragma unroll
+      for (int s = 0; s < 2; s++)
+        *(uint32_t *)(a.hq + p * N + c0 + 16 * s + 4 * g) = e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
+      if (g == 0) a.hs[p * hss + c0 / 32] = (uint8_t)sbyte;
+    }
+  }
+}
+
+// ------------------------------------------------ GEMM1, 128-route tiles
+// The same block of 16 weight row tiles (256 weight rows) against a tile of 128
+// routes: each wave owns row tiles 4w .. 4w+3 against all 128 routes, 32
+// block-scaled MFMAs per k-tile between two barriers, and each weight row tile
+// streamed from L2 serves twice the routes of a 64-route tile (at the 4096-token
+// prefill with Zipf-skewed loads, 299 weight passes instead of 485).  The
+// activations of a k-tile (16 blocks of 8 routes, 16.5 KB) go through a 2-deep
+// LDS ring, the weights through a 2-deep register ring: one k-tile of 32 MFMAs
+// per wave covers the next one's loads.  The routes are read from LDS in two
+// halves of 64 (the second skipped in tiles of at most 64 routes), and the MFMAs
+// of 16-route blocks past the tile's last route are skipped.
+constexpr int kPwStages = 2;
+// vector-memory operations of one wave per stage: 4 weight tiles, 4 weight
+// scale dwords, 4 activation blocks, 1 activation scale chunk (or a spare)
+constexpr int kPwLoads = 13;
+
+struct PwStage {
+  uint8_t B[16][1024];            // activation rows 8b .. 8b+7 of block b, swizzled 16-byte chunks
+  uint8_t S[1024];                // Bs [128][4] | 2 spare 256-byte slots
+};
+
+struct __attribute__((aligned(16))) PwLds {
+  PwStage st[kPwStages];
+};
+
+struct PwSrc {
+  PfSrc w;                        // weights (wb, sb, wstep, sstep, nrt, kbytes)
+  const uint8_t *xq, *xs;         // MXFP8 activations and their scales (uniform bases)
+  uint32_t brow[4];               // byte offsets of this lane's activation rows of its four B blocks
+  uint32_t bsrow;                 // byte offset of the scale row of route 64 (w & 1) + lane
+};
+
+// Activation blocks 4w .. 4w+3 of k-tile kt into stage S (lane l -> row l / 8
+// of its block, chunk slot l), and the scales of routes 64 (w & 1) .. +63 (waves
+// 0, 1; waves 2, 3 fill spare slots to keep the per-wave load count equal).  The
+// reduction is whole k-tiles (K % 256 == 0).
+__device__ __forceinline__ void pw_issue_b(PwStage &S, const PwSrc &src, int kt, int w, int l) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int r8 = l >> 3, part = (l & 7) ^ r8;
+    dma16(src.xq + (src.brow[j] + (uint32_t)(kt * 128 + part * 16)), &S.B[4 * w + j][0]);
+  }
+  dma4(src.xs + (src.bsrow + (uint32_t)(4 * kt)), &S.S[256 * w]);
+}
+
+// 16 MFMAs of one half (routes 64 h .. 64 h + 63) of a k-tile: the half's
+// 16-route blocks cb with 4 h + cb < nrb.
+template <int H>
+__device__ __forceinline__ void pw_mma(const PfW &wt, const v4i (&b)[4][2], const int (&sb)[4], int nrb, int l,
+                                       v4f (*acc)[8]) {
+#pragma unroll
+  for (int cb = 0; cb < 4; cb++) {
+    if (4 * H + cb < nrb) {
+      const v8i bop = v8i{b[cb][0][0], b[cb][0][1], b[cb][0][2], b[cb][0][3],
+                          b[cb][1][0], b[cb][1][1], b[cb][1][2], b[cb][1][3]};
+#pragma unroll
+      for (int q = 0; q < kPfQ; q++)
+        acc[q][4 * H + cb] = mfma_fp4_fp8(wt.a[q], bop, acc[q][4 * H + cb], (int)(wt.sa[q] >> (8 * (l & 3))), sb[cb]);
+    }
+  }
+}
+
+// One k-tile (R = kt % 2): wait for stage kt (the only one in flight), barrier
+// (every wave is also done with stage kt - 1), issue k-tile kt + 1 into the
+// slots kt - 1 held (ISSUE), then both halves of stage kt.
+template <int R, bool ISSUE>
+__device__ __forceinline__ void pw_step(PwLds &L, const PwSrc &src, PfW (&ring)[kPwStages], int kt, int w,
+                                        bool active, int nrb, v4f (*acc)[8]) {
+  const int l = threadIdx.x & 63;
+  wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  if (ISSUE) {
+    pf_load_w(ring[R ^ 1], src.w, kt + 1, w, l);
+    pw_issue_b(L.st[R ^ 1], src, kt + 1, w, l);
+  }
+  if (active) {
+    v4i b[4][2];
+    int sb[4];
+    pf_read_b_at(b, sb, &L.st[R].B[0], &L.st[R].S[0], l);
+    __builtin_amdgcn_s_setprio(1);
+    pw_mma<0>(ring[R], b, sb, nrb, l, acc);
+    __builtin_amdgcn_s_setprio(0);
+    if (nrb > 4) {
+      pf_read_b_at(b, sb, &L.st[R].B[8], &L.st[R].S[256], l);
+      __builtin_amdgcn_s_setprio(1);
+      pw_mma<1>(ring[R], b, sb, nrb, l, acc);
+      __builtin_amdgcn_s_setprio(0);
+    }
+  }
+}
+
+// Block: 16 row tiles of w13 = up and gate of 128 intermediate columns (8 in
+// the last block of an N % 128 == 64 layer) against a tile of up to 128 routes.
+__global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8w(GemmArgs a) {
+  __shared__ PwLds L;
+  const int K = a.K, N = a.N;
+  const PfWork wk = pf_work(a, (N + 127) / 128, false);
+  if (!wk.valid) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int hb = wk.sub;
+  PwSrc src;
+  src.w.wstep = (uint32_t)(16 * (K / 2));
+  src.w.sstep = (uint32_t)(16 * (K / 32));
+  src.w.nrt = min(kPfRT, N / 8 - kPfRT * hb);
+  src.w.wb = make_buf(a.w13 + (size_t)wk.e * (2 * N) * (K / 2) + (size_t)(kPfRT * hb) * src.w.wstep,
+                      src.w.nrt * src.w.wstep);
+  src.w.sb = make_buf(a.s13 + (size_t)wk.e * (2 * N) * (K / 32) + (size_t)(kPfRT * hb) * src.w.sstep,
+                      src.w.nrt * src.w.sstep);
+  src.w.kbytes = K;
+  // rows past the tile read route p0's token; their results are never stored
+  // 32-bit byte offsets: the host runs this kernel only for chunks with T * K < 2^32
+  src.xq = a.xq;
+  src.xs = a.xs;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int row = 8 * (4 * w + j) + (l >> 3);
+    src.brow[j] = (uint32_t)(a.perm[wk.p0 + (row < wk.rows ? row : 0)] / a.topk) * (uint32_t)K;
+  }
+  const int srow = 64 * (w & 1) + l;
+  src.bsrow = (uint32_t)(a.perm[wk.p0 + (srow < wk.rows ? srow : 0)] / a.topk) * (uint32_t)(K / 32);
+  const int nrb = __builtin_amdgcn_readfirstlane((wk.rows + 15) / 16);
+  const bool active = kPfQ * w < src.w.nrt;
+  v4f acc[kPfQ][8];
+  zero_acc<kPfQ, 8>(acc);
+  const int nkt = K / 128;   // even: K % 256 == 0
+  PfW ring[kPwStages];
+  pf_load_w(ring[0], src.w, 0, wu, l);
+  pw_issue_b(L.st[0], src, 0, wu, l);
+  int kt = 0;
+  for (; kt + 2 < nkt; kt += 2) {
+    pw_step<0, true>(L, src, ring, kt, wu, active, nrb, acc);
+    pw_step<1, true>(L, src, ring, kt + 1, wu, active, nrb, acc);
+  }
+  pw_step<0, true>(L, src, ring, kt, wu, active, nrb, acc);
+  pw_step<1, false>(L, src, ring, kt + 1, wu, active, nrb, acc);
+  if (!active) return;   // the missing half of a partial block
+  // epilogue: row tiles 4w + 2s (up) and 4w + 2s + 1 (gate) = intermediate
+  // columns 128 hb + 32 w + 16 s .. +15; their 32 columns form one MXFP8 group
+  const int hss = hs_stride(N);
+  const size_t c0 = (size_t)128 * hb + 32 * w;
+#pragma unroll
+  for (int cb = 0; cb < 8; cb++) {
+    if (cb >= nrb) break;
+    const int row = 16 * cb + c;
+    float h[8];
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        h[s * 4 + i] = silu_clamped(acc[2 * s + 1][cb][i], acc[2 * s][cb][i], a.limit, a.has_limit, a.alpha, a.beta,
+                                    a.act);
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(h[i]));
@@ -439,6 +620,7 @@ __device__ __forceinline__ bool pf_g2_setup(const GemmArgs &a, PfG2 &g2, int *s_
     src.brow[j] = a.hq + (size_t)(wk.p0 + (row < wk.rows ? row : 0)) * N;
   }
   src.bsrow = a.hs + (size_t)(wk.p0 + (l < wk.rows ? l : 0)) * hs_stride(N);
+  src.nrb = __builtin_amdgcn_readfirstlane((wk.rows + 15) / 16);
   if (tid < wk.rows) {
     const int r = a.perm[wk.p0 + tid];
     s_r[tid] = r;
@@ -508,8 +690,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8_short(GemmArgs a) {
     pf_read_b(b, sb, L.st[kt], l);
     __builtin_amdgcn_s_setprio(1);
     // only the last k-tile can be partial (NKT = N / 128 rounded up)
-    if (kt < NKT - 1 || (kt + 1) * 128 <= src.kbytes) pf_mma<true, true>(wt[kt], b, sb, kt, src.kbytes, l, acc);
-    else pf_mma<true, false>(wt[kt], b, sb, kt, src.kbytes, l, acc);
+    if (kt < NKT - 1 || (kt + 1) * 128 <= src.kbytes) pf_mma<true, true>(wt[kt], b, sb, kt, src.kbytes, src.nrb, l, acc);
+    else pf_mma<true, false>(wt[kt], b, sb, kt, src.kbytes, src.nrb, l, acc);
     __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();   // s_r / s_w visible; every wave is done with the ring's LDS
@@ -520,7 +702,10 @@ static int pf_grid(int grid_tiles, int nsub) { return (grid_tiles * nsub + 7) / 
 
 hipError_t launch_pf_gemm1(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pf_gemm1_a8, dim3(pf_grid(grid_tiles, (a.N + 127) / 128)), dim3(256), 0, s, a);
+  if (a.tile_rows == kPfWideRows)
+    hipLaunchKernelGGL(k_pf_gemm1_a8w, dim3(pf_grid(grid_tiles, (a.N + 127) / 128)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_pf_gemm1_a8, dim3(pf_grid(grid_tiles, (a.N + 127) / 128)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
