@@ -20,7 +20,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOTPREPARED, MOE_ESCRATCH, MOE_EHIP =
 W_MXFP4, W_NVFP4, W_NF3 = 1, 2, 3
 A_MXFP8, A_BF16 = 1, 2
 W13_UP_GATE, W13_GATE_UP = 0, 1
-ACT_SWIGLU, ACT_SITU = 0, 1
+ACT_SWIGLU, ACT_SITU, ACT_RELU2_NO_MUL = 0, 1, 2
 SEQ_AUTO, SEQ_DECODE, SEQ_GENERAL, SEQ_PREFILL = 0, 1, 2, 3
 COMBINE_AUTO, COMBINE_ATOMIC, COMBINE_ROUTE_BUFFER = 0, 1, 2
 # race slots of the autotuner: (sequence, combine of deterministic = 0 runs)
@@ -96,6 +96,7 @@ class Plan:
         self.handle = h
         self.E, self.K, self.N, self.top_k = E, K, N, top_k
         self.act_format, self.w13_layout, self.max_tokens = act_format, w13_layout, max_tokens
+        self.act = ACT_SWIGLU
 
     def scratch_bytes(self, T: int, deterministic: bool = False) -> int:
         return _lib.load().moe_scratch_bytes(self.handle, T, int(bool(deterministic)))
@@ -164,8 +165,11 @@ class Plan:
         _check(_lib.load().moe_plan_set_swiglu_oai(self.handle, float(alpha), float(beta)))
 
     def set_activation(self, act: int):
-        """ACT_SWIGLU (default) or ACT_SITU: silu(4 tanh(gate/4)) * 25 tanh(up/25), plans without a limit."""
+        """ACT_SWIGLU (default), ACT_SITU (silu(4 tanh(gate/4)) * 25 tanh(up/25)) or ACT_RELU2_NO_MUL
+        (relu(z)^2 of a w13 with N rows; bf16 plans); SiTU and ReLU^2 on plans without a limit.
+        Set before preparing experts for the plan."""
         _check(_lib.load().moe_plan_set_activation(self.handle, int(act)))
+        self.act = int(act)
 
     def set_router_weight_on_input(self, enable: bool = True):
         """Apply each slot's router weight to GEMM1's input instead of the GEMM2 result (bf16 plans)."""
@@ -202,7 +206,8 @@ class Experts:
     def __init__(self, plan: Plan, weight_format: int, num_experts: int, w13, s13, w2, s2, g13=None, g2=None,
                  stream=None):
         import torch
-        sizes = weight_bytes(weight_format, num_experts, plan.K, plan.N)
+        sizes = weight_bytes(weight_format, num_experts, plan.K, plan.N,
+                             plan.N if plan.act == ACT_RELU2_NO_MUL else None)
         for device in (False, True):   # every size first, then where the tensors live
             for name, t, n in zip(("w13", "s13", "w2", "s2"), (w13, s13, w2, s2), sizes):
                 _need(t, name, torch.uint8, device, numel=n)

@@ -75,6 +75,7 @@ struct moe_plan_s {
 struct moe_experts_s {
   uint32_t magic;
   int K, N, w13_layout;   // geometry the buffers were prepared for
+  int w13_rows;           // 2N, or N for ReLU^2 without the multiply
   int wfmt, E;
   uint8_t *w13, *s13, *w2, *s2;
   const float *g13, *g2;
@@ -86,6 +87,12 @@ namespace {
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool plan_ok(const moe_plan_s *p) { return p && p->magic == kPlanMagic; }
+
+// Rows of w13 and column pairs of GEMM1 under the plan's activation: ReLU^2
+// without the multiply has a w13 of N rows, run as an [up; gate] w13 of N / 2
+// pairs whose two halves give h columns n and N / 2 + n.
+int w13_rows(const moe_plan_s *p) { return p->act == MOE_ACT_RELU2_NO_MUL ? p->N : 2 * p->N; }
+int gemm1_pairs(const moe_plan_s *p) { return p->act == MOE_ACT_RELU2_NO_MUL ? p->N / 2 : p->N; }
 
 int cap_for(const moe_plan_s *p, int T) {
   for (int c : p->caps)
@@ -180,9 +187,11 @@ int check_tiers(const moe_plan_s *p, const moe_tier *tiers, int n_tiers) {
     const moe_experts_s *x = tiers[i].experts;
     if (!x || x->magic != kExpertsMagic) return fail(MOE_EINVAL, "tier %d: null or invalid experts handle", i);
     if (!x->prepared) return fail(MOE_ENOTPREPARED, "tier %d: experts are not prepared (checkpoint layout)", i);
-    if (x->K != p->K || x->N != p->N || x->w13_layout != p->w13_layout)
-      return fail(MOE_ENOTPREPARED, "tier %d: experts prepared for K=%d N=%d layout=%d, plan has K=%d N=%d layout=%d",
-                  i, x->K, x->N, x->w13_layout, p->K, p->N, p->w13_layout);
+    if (x->K != p->K || x->N != p->N || x->w13_layout != p->w13_layout || x->w13_rows != w13_rows(p))
+      return fail(MOE_ENOTPREPARED,
+                  "tier %d: experts prepared for K=%d N=%d layout=%d w13 rows=%d, plan has K=%d N=%d layout=%d w13 "
+                  "rows=%d",
+                  i, x->K, x->N, x->w13_layout, x->w13_rows, p->K, p->N, p->w13_layout, w13_rows(p));
     const int want_a = (x->wfmt == MOE_W_MXFP4) ? MOE_A_MXFP8 : MOE_A_BF16;
     if (want_a != p->afmt) return fail(MOE_EUNSUPPORTED, "tier %d: weight format %d does not run with activation format %d", i, x->wfmt, p->afmt);
     if (tiers[i].expert_map && !aligned(tiers[i].expert_map, 4)) return fail(MOE_EINVAL, "tier %d: misaligned expert_map", i);
@@ -227,6 +236,7 @@ int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const ui
   da.alpha = p->alpha;
   da.beta = p->beta;
   da.act = p->act;
+  da.N1 = gemm1_pairs(p);
   da.cpass = moe::decode_cpass(p->K, p->afmt == MOE_A_MXFP8);
   da.hq = scratch + L.hq;
   da.hs = scratch + L.hs;
@@ -266,7 +276,7 @@ bool seq_eligible(const moe_plan_s *p, int cap, int seq) {
   switch (seq) {
     case MOE_SEQ_DECODE: return use_decode(p, cap);   // then also for every chunk of <= cap tokens
     case MOE_SEQ_GENERAL: return true;
-    case MOE_SEQ_PREFILL: return p->N % 64 == 0;
+    case MOE_SEQ_PREFILL: return gemm1_pairs(p) % 64 == 0 && p->N % 64 == 0;
     default: return false;
   }
 }
@@ -277,7 +287,7 @@ bool seq_eligible(const moe_plan_s *p, int cap, int seq) {
 // up for W4A16 / W3A16 and for atomic W4A8, 1024 for deterministic W4A8.
 int ladder_seq(const moe_plan_s *p, int T) {
   if (use_decode(p, T)) return MOE_SEQ_DECODE;
-  return p->N % 64 == 0 && T >= moe::kPrefillMinT ? MOE_SEQ_PREFILL : MOE_SEQ_GENERAL;
+  return seq_eligible(p, T, MOE_SEQ_PREFILL) && T >= moe::kPrefillMinT ? MOE_SEQ_PREFILL : MOE_SEQ_GENERAL;
 }
 
 int seq_for(const moe_plan_s *p, int T) {
@@ -371,6 +381,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ga.alpha = p->alpha;
   ga.beta = p->beta;
   ga.act = p->act;
+  ga.N1 = gemm1_pairs(p);
   ga.topk_w = wts;
   ga.out_acc = (float *)(scratch + L.acc);
   ga.rb = (uint16_t *)(scratch + L.rb);
@@ -470,8 +481,8 @@ int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
   struct T {
     uint8_t *buf;
     int unit, rows, groups, pair;
-  } tensors[4] = {{x->w13, unit, 2 * x->N, x->K / 32, 1},
-                  {x->s13, sunit, 2 * x->N, x->K / 32, 1},
+  } tensors[4] = {{x->w13, unit, x->w13_rows, x->K / 32, 1},
+                  {x->s13, sunit, x->w13_rows, x->K / 32, 1},
                   {x->w2, unit, x->K, x->N / 32, 0},
                   {x->s2, sunit, x->K, x->N / 32, 0}};
   size_t max_exp = 0;
@@ -480,7 +491,7 @@ int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
   const long batch = std::max<long>(1, std::min<long>(x->E, (long)(budget / max_exp)));
   // NF3 codes: unpacking leaves the kernels' sign / index form before the permutation
   if (x->wfmt == MOE_W_NF3 && !to_tiles) {
-    HIP_TRY(moe::launch_nf3_recode(x->w13, (long)x->E * 2 * x->N * (x->K / 32), 0, s));
+    HIP_TRY(moe::launch_nf3_recode(x->w13, (long)x->E * x->w13_rows * (x->K / 32), 0, s));
     HIP_TRY(moe::launch_nf3_recode(x->w2, (long)x->E * x->K * (x->N / 32), 0, s));
   }
   uint8_t *tmp = nullptr;
@@ -500,7 +511,7 @@ int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
   }
   // NF3 codes: packing ends in the kernels' sign / index form
   if (rc == MOE_OK && x->wfmt == MOE_W_NF3 && to_tiles) {
-    hipError_t e1 = moe::launch_nf3_recode(x->w13, (long)x->E * 2 * x->N * (x->K / 32), 1, s);
+    hipError_t e1 = moe::launch_nf3_recode(x->w13, (long)x->E * x->w13_rows * (x->K / 32), 1, s);
     if (e1 == hipSuccess) e1 = moe::launch_nf3_recode(x->w2, (long)x->E * x->K * (x->N / 32), 1, s);
     if (e1 != hipSuccess) rc = fail(MOE_EHIP, "nf3 recode: %s", hipGetErrorString(e1));
   }
@@ -599,10 +610,21 @@ int moe_plan_set_swiglu_oai(moe_plan_t plan, float alpha, float beta) {
 
 int moe_plan_set_activation(moe_plan_t plan, int act) {
   if (!plan_ok(plan)) return fail(MOE_EINVAL, "invalid plan");
-  if (act != MOE_ACT_SWIGLU && act != MOE_ACT_SITU) return fail(MOE_EUNSUPPORTED, "activation %d", act);
-  if (act == MOE_ACT_SITU && (plan->has_limit || plan->alpha != 1.f || plan->beta != 0.f))
-    return fail(MOE_EUNSUPPORTED, "SiTU takes no swiglu limit, alpha or beta");
+  if (act != MOE_ACT_SWIGLU && act != MOE_ACT_SITU && act != MOE_ACT_RELU2_NO_MUL)
+    return fail(MOE_EUNSUPPORTED, "activation %d", act);
+  if (act != MOE_ACT_SWIGLU && (plan->has_limit || plan->alpha != 1.f || plan->beta != 0.f))
+    return fail(MOE_EUNSUPPORTED, "SiTU and ReLU^2 take no swiglu limit, alpha or beta");
+  if (act == MOE_ACT_RELU2_NO_MUL) {
+    if (plan->afmt != MOE_A_BF16)
+      return fail(MOE_EUNSUPPORTED, "ReLU^2 without the multiply needs bf16 activations (W4A16 / W3A16)");
+    if (plan->N % 64) return fail(MOE_EUNSUPPORTED, "ReLU^2 without the multiply needs N %% 64 == 0");
+    if (plan->w13_layout != MOE_W13_UP_GATE)
+      return fail(MOE_EUNSUPPORTED, "ReLU^2 without the multiply has no gate half: w13 layout must be the default");
+  }
   plan->act = act;
+  // pins a rung can no longer take go back to the ladder's choice
+  for (size_t r = 0; r < plan->caps.size(); r++)
+    if (plan->seq[r] && !seq_eligible(plan, plan->caps[r], plan->seq[r])) plan->seq[r] = 0;
   return MOE_OK;
 }
 
@@ -976,6 +998,7 @@ int moe_prepare_weights(moe_plan_t plan, int weight_format, int num_experts, voi
   x->K = plan->K;
   x->N = plan->N;
   x->w13_layout = plan->w13_layout;
+  x->w13_rows = w13_rows(plan);
   x->wfmt = weight_format;
   x->E = num_experts;
   x->w13 = (uint8_t *)w13;

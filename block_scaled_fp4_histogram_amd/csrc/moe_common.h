@@ -17,7 +17,7 @@ constexpr int kMaxTiers = 2;
 
 enum WFmt { W_MXFP4 = 1, W_NVFP4 = 2, W_NF3 = 3 };
 // activation forms of the GEMM1 epilogue (MOE_ACT_* of the C ABI)
-enum Act { ACT_SWIGLU = 0, ACT_SITU = 1 };
+enum Act { ACT_SWIGLU = 0, ACT_SITU = 1, ACT_RELU2 = 2 };
 
 // Bytes per row of the MXFP8 intermediate's scales: N/32 rounded up to a
 // multiple of 4, so every row starts 4-byte aligned.
@@ -83,7 +83,10 @@ struct GemmArgs {
   int T;                             // tokens of the chunk (rows of x / the accumulator)
   int w_on_input;                    // router weight scales GEMM1 (W4A16 / W3A16), not the GEMM2 result
   float alpha, beta;                 // SwiGLU form: gate * sigmoid(alpha gate) * (up + beta)
-  int act;                           // Act: SwiGLU (limit, alpha, beta) or SiTU
+  int act;                           // Act: SwiGLU (limit, alpha, beta), SiTU or ReLU^2 without the multiply
+  // column pairs of GEMM1: N, or N / 2 for ReLU^2 without the multiply, whose w13
+  // of N rows runs as an [up; gate] w13 of N / 2 pairs (h columns n and N / 2 + n)
+  int N1;
   // both tiers in one launch (prefill W4A16 / W3A16): the fields above are tier 0,
   // these tier 1, whose experts follow tier 0's in the unified index (u_base_b)
   const uint8_t *w13b, *s13b, *w2b, *s2b;
@@ -128,7 +131,8 @@ struct DecArgs {
   DecGroups *groups;                 // scratch
   int w_on_input;                    // router weight scales GEMM1 (W4A16 / W3A16), not the GEMM2 result
   float alpha, beta;                 // SwiGLU form: gate * sigmoid(alpha gate) * (up + beta)
-  int act;                           // Act: SwiGLU (limit, alpha, beta) or SiTU
+  int act;                           // Act: SwiGLU (limit, alpha, beta), SiTU or ReLU^2 without the multiply
+  int N1;                            // column pairs of GEMM1 (as GemmArgs::N1)
   // W4A16 / W3A16 down GEMM split over two blocks per output row tile (scratch):
   float *dpart;                      // [K/16][16 tokens][16 columns] fp32 token sums, both halves added
   int *dcnt;                         // [K/16] halves finished; both zeroed by the up/gate kernel

@@ -243,11 +243,11 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
   constexpr int U = A8 ? 16 : FmtGeom<WF>::unit, SU = A8 ? 1 : FmtGeom<WF>::sunit;
   typedef typename std::conditional<A8, A8W, A16W<WF>>::type Stage;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
-  const int K = a.K, N = a.N, nkt = K / 128, groups = K / 32, hb = blockIdx.x;
+  const int K = a.K, N = a.N, N1 = a.N1, nkt = K / 128, groups = K / 32, hb = blockIdx.x;
   const size_t rt_bytes = (size_t)16 * groups * U, rt_scales = (size_t)16 * groups * SU;
   RowTiles rt;
-  rt.wb = make_buf(X.w13 + (size_t)X.e * (2 * N) * groups * U, (uint32_t)((size_t)(2 * N) * groups * U));
-  rt.sb = make_buf(X.s13 + (size_t)X.e * (2 * N) * groups * SU, (uint32_t)((size_t)(2 * N) * groups * SU));
+  rt.wb = make_buf(X.w13 + (size_t)X.e * (2 * N1) * groups * U, (uint32_t)((size_t)(2 * N1) * groups * U));
+  rt.sb = make_buf(X.s13 + (size_t)X.e * (2 * N1) * groups * SU, (uint32_t)((size_t)(2 * N1) * groups * SU));
   rt.w0 = (uint32_t)((size_t)(4 * hb) * rt_bytes);
   rt.wstep = (uint32_t)rt_bytes;
   rt.s0 = (uint32_t)((size_t)(4 * hb) * rt_scales);
@@ -298,7 +298,31 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
 #pragma unroll
       for (int i = 0; i < 4; i++) red[(w * 16 + q * 4 + i) * 64 + l] = acc[q][i];
     __syncthreads();
-    if (w == 0) {
+    if (!A8 && a.act == ACT_RELU2) {
+      // ReLU^2 without the multiply: both halves' rows give their own columns
+      if (w == 0 && have) {
+        const float gs = X.g13 * (a.w_on_input ? a.topk_w[nth_bit(md, p0 + c)] : 1.0f);
+        const size_t r = (size_t)nth_bit(md, p0 + c);
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+#pragma unroll
+          for (int half = 0; half < 2; half++) {
+            float z[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int ir = (2 * s + half) * 4 + i;
+              float v = 0.f;
+#pragma unroll 2
+              for (int ww = 0; ww < NW; ww++) v += red[(ww * 16 + ir) * 64 + l];
+              z[i] = relu2(v * gs);
+            }
+            uint2 o;
+            o.x = pack_bf16x2(z[0], z[1]);
+            o.y = pack_bf16x2(z[2], z[3]);
+            *(uint2 *)(a.hb + r * N + half * N1 + hb * 32 + 16 * s + 4 * g) = o;
+          }
+      }
+    } else if (w == 0) {
       float h[8];
       // router weight on the input (W4A16 / W3A16): GEMM1 is linear, so it scales the accumulators
       const float gs = X.g13 * ((!A8 && a.w_on_input && have) ? a.topk_w[nth_bit(md, p0 + c)] : 1.0f);
@@ -821,7 +845,7 @@ size_t decode_gemm1_lds(int K, int cpass, int a8) {
 hipError_t launch_decode(int a8, const DecArgs &a, hipStream_t s, hipEvent_t ev_mid) {
   if (a.R == 0) return hipSuccess;
   int U = a.tier[0].E + (a.n_tiers > 1 ? a.tier[1].E : 0);
-  const dim3 g1(a.N / 32, (unsigned)min(a.R, U)), g2(a.K / 16);
+  const dim3 g1(a.N1 / 32, (unsigned)min(a.R, U)), g2(a.K / 16);
   const size_t lds1 = decode_gemm1_lds(a.K, a.cpass, a8);
   if (a8) hipLaunchKernelGGL(k_dec_gemm1_a8, g1, dim3(256), lds1, s, a);
   else hipLaunchKernelGGL(k_dec_gemm1_a16, g1, dim3(256), lds1, s, a);

@@ -70,6 +70,10 @@ __device__ __forceinline__ float silu_clamped(float gate, float up, float limit,
   return gate / (1.0f + __expf(-alpha * gate)) * (up + beta);
 }
 
+// ReLU^2 without the gate multiply (vLLM "fused_moe/b12x" page, RELU2_NO_MUL):
+// each GEMM1 output z gives its own intermediate column relu(z)^2.
+__device__ __forceinline__ float relu2(float z) { return z > 0.f ? z * z : 0.f; }
+
 // Two fp32 -> two E4M3 (fn) codes (bits 0-7, 8-15), nearest with ties to even,
 // magnitudes above 448 saturating to 448.  The hardware conversion rounds to
 // nearest even (subnormals included) but turns magnitudes above 464 into NaN,

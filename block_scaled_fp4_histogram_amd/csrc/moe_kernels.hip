@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256) void k_gemm1_a16(GemmArgs a) {
   if (!ti.valid) return;
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, g = l >> 4;
-  const int K = a.K, N = a.N, nkt = K / 128, groups = K / 32;
+  const int K = a.K, N = a.N, N1 = a.N1, nkt = K / 128, groups = K / 32;
   const int hb = blockIdx.x;
   int t = -1;
   if (c < ti.rows) t = a.perm[ti.p0 + c] / a.topk;
@@ -493,8 +493,8 @@ __global__ __launch_bounds__(256) void k_gemm1_a16(GemmArgs a) {
   const uint16_t *xrow = a.xb + (size_t)(have ? t : 0) * K;
   const size_t rt_bytes = (size_t)16 * groups * U;
   const size_t rt_scales = (size_t)16 * groups * SU;
-  const uint8_t *wt = a.w13 + (size_t)ti.e * (2 * N) * groups * U + (size_t)(4 * hb) * rt_bytes + l * U;
-  const uint8_t *st = a.s13 + (size_t)ti.e * (2 * N) * groups * SU + (size_t)(4 * hb) * rt_scales + l * SU;
+  const uint8_t *wt = a.w13 + (size_t)ti.e * (2 * N1) * groups * U + (size_t)(4 * hb) * rt_bytes + l * U;
+  const uint8_t *st = a.s13 + (size_t)ti.e * (2 * N1) * groups * SU + (size_t)(4 * hb) * rt_scales + l * SU;
   v4f acc[4];
 #pragma unroll
   for (int q = 0; q < 4; q++) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -519,18 +519,28 @@ __global__ __launch_bounds__(256) void k_gemm1_a16(GemmArgs a) {
     const float gs = (a.g13 ? a.g13[ti.e] : 1.0f) * (a.w_on_input ? a.topk_w[a.perm[p]] : 1.0f);
 #pragma unroll
     for (int s = 0; s < 2; s++) {
-      float h[4];
+      float h[4], h2[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int iu = (2 * s) * 4 + i, ig = (2 * s + 1) * 4 + i;
         const float up = (red[0][iu][l] + red[1][iu][l] + red[2][iu][l] + red[3][iu][l]) * gs;
         const float gate = (red[0][ig][l] + red[1][ig][l] + red[2][ig][l] + red[3][ig][l]) * gs;
-        h[i] = silu_clamped(gate, up, a.limit, a.has_limit, a.alpha, a.beta, a.act);
+        if (a.act == ACT_RELU2) {
+          h[i] = relu2(up);
+          h2[i] = relu2(gate);
+        } else {
+          h[i] = silu_clamped(gate, up, a.limit, a.has_limit, a.alpha, a.beta, a.act);
+        }
       }
       uint2 v;
       v.x = pack_bf16x2(h[0], h[1]);
       v.y = pack_bf16x2(h[2], h[3]);
       *(uint2 *)(a.hb + p * N + hb * 32 + 16 * s + 4 * g) = v;
+      if (a.act == ACT_RELU2) {   // the second half's rows: columns N1 + ...
+        v.x = pack_bf16x2(h2[0], h2[1]);
+        v.y = pack_bf16x2(h2[2], h2[3]);
+        *(uint2 *)(a.hb + p * N + N1 + hb * 32 + 16 * s + 4 * g) = v;
+      }
     }
   }
 }
@@ -579,7 +589,7 @@ __global__ __launch_bounds__(256) void k_gemm2_a16(GemmArgs a) {
 
 hipError_t launch_gemm1(int wfmt, const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  const dim3 grid(a.N / 32, grid_tiles), block(256);
+  const dim3 grid(a.N1 / 32, grid_tiles), block(256);
   if (wfmt == W_MXFP4) hipLaunchKernelGGL(k_gemm1_a8, grid, block, 0, s, a);
   else if (wfmt == W_NVFP4) hipLaunchKernelGGL(k_gemm1_a16<W_NVFP4>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(k_gemm1_a16<W_NF3>, grid, block, 0, s, a);

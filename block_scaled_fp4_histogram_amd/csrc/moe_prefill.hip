@@ -1022,15 +1022,15 @@ __device__ __forceinline__ PfWork pf_work_tiers(const GemmArgs &a, int nsub, boo
 template <int WF>
 __device__ __forceinline__ void pf16_gemm1_body(const GemmArgs &a, const PfWork &wk, const PfTier &T, Pf16Lds &L) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
-  const int K = a.K, N = a.N;
+  const int K = a.K, N = a.N, N1 = a.N1;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int hb = wk.sub, groups = K / 32;
   Pf16Src src;
   src.wstep = (uint32_t)(16 * groups * U);
   src.sstep = (uint32_t)(16 * groups * SU);
-  src.wb = make_buf(T.w13 + (size_t)wk.e * (2 * N) * groups * U + (size_t)(8 * hb) * src.wstep, 8 * src.wstep);
-  src.sb = make_buf(T.s13 + (size_t)wk.e * (2 * N) * groups * SU + (size_t)(8 * hb) * src.sstep, 8 * src.sstep);
+  src.wb = make_buf(T.w13 + (size_t)wk.e * (2 * N1) * groups * U + (size_t)(8 * hb) * src.wstep, 8 * src.wstep);
+  src.sb = make_buf(T.s13 + (size_t)wk.e * (2 * N1) * groups * SU + (size_t)(8 * hb) * src.sstep, 8 * src.sstep);
   src.kcols = K;
   // rows past the tile read route p0's token; their results are never stored
 #pragma unroll
@@ -1053,10 +1053,20 @@ __device__ __forceinline__ void pf16_gemm1_body(const GemmArgs &a, const PfWork 
       const size_t p = (size_t)(wk.p0 + row);
       // router weight on the input: GEMM1 is linear, so it scales the accumulators
       const float gs = g13 * (a.w_on_input ? a.topk_w[a.perm[p]] : 1.0f);
+      uint2 v;
+      if (a.act == ACT_RELU2) {
+        // ReLU^2 without the multiply: the up and gate halves' rows give columns n and N1 + n
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+          v.x = pack_bf16x2(relu2(acc[half][cb][0] * gs), relu2(acc[half][cb][1] * gs));
+          v.y = pack_bf16x2(relu2(acc[half][cb][2] * gs), relu2(acc[half][cb][3] * gs));
+          *(uint2 *)(a.hb + p * N + half * N1 + 64 * hb + 16 * w + 4 * g) = v;
+        }
+        continue;
+      }
       float h[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) h[i] = silu_clamped(acc[1][cb][i] * gs, acc[0][cb][i] * gs, a.limit, a.has_limit, a.alpha, a.beta, a.act);
-      uint2 v;
       v.x = pack_bf16x2(h[0], h[1]);
       v.y = pack_bf16x2(h[2], h[3]);
       *(uint2 *)(a.hb + p * N + 64 * hb + 16 * w + 4 * g) = v;
@@ -1067,7 +1077,7 @@ __device__ __forceinline__ void pf16_gemm1_body(const GemmArgs &a, const PfWork 
 template <int WF>
 __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
   __shared__ Pf16Lds L;
-  const PfWork wk = pf_work(a, a.N / 64, false);
+  const PfWork wk = pf_work(a, a.N1 / 64, false);
   if (!wk.valid) return;
   pf16_gemm1_body<WF>(a, wk, pf_tier(a, 0), L);
 }
@@ -1076,7 +1086,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16(GemmArgs a) {
 __global__ __launch_bounds__(256) void k_pf_gemm1_a16_tiers(GemmArgs a) {
   __shared__ Pf16Lds L;
   int tier = 0;
-  const PfWork wk = pf_work_tiers(a, a.N / 64, false, &tier);
+  const PfWork wk = pf_work_tiers(a, a.N1 / 64, false, &tier);
   if (!wk.valid) return;
   const PfTier T = pf_tier(a, tier);
   if ((tier ? a.fmt_b : a.fmt_a) == W_NVFP4) pf16_gemm1_body<W_NVFP4>(a, wk, T, L);
@@ -1145,7 +1155,7 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16_tiers(GemmArgs a) {
 template <int WF>
 static hipError_t launch_pf_a16(const GemmArgs &a, int grid_tiles, hipStream_t s, bool second) {
   if (second) hipLaunchKernelGGL(k_pf_gemm2_a16<WF>, dim3(pf_grid(grid_tiles, a.K / 128)), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_pf_gemm1_a16<WF>, dim3(pf_grid(grid_tiles, a.N / 64)), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_pf_gemm1_a16<WF>, dim3(pf_grid(grid_tiles, a.N1 / 64)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1162,7 +1172,7 @@ hipError_t launch_pf16_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStr
 // grid_tiles: an upper bound on both tiers' tiles together.
 hipError_t launch_pf16_gemm1_tiers(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pf_gemm1_a16_tiers, dim3(pf_grid(grid_tiles, a.N / 64)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_pf_gemm1_a16_tiers, dim3(pf_grid(grid_tiles, a.N1 / 64)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -60,9 +60,9 @@ typedef enum { MOE_A_MXFP8 = 1, MOE_A_BF16 = 2 } moe_afmt;
 typedef enum { MOE_W13_UP_GATE = 0, MOE_W13_GATE_UP = 1 } moe_w13_layout;
 /* Activation forms of the GEMM1 epilogue (vLLM "fused_moe/b12x" page,
  * _supports_activation and _swiglu_params): the SwiGLU (with the plan's limit
- * and the optional OAI alpha / beta) and SiTU (beta 4, linear beta 25, no
- * limit). */
-typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SITU = 1 } moe_activation;
+ * and the optional OAI alpha / beta), SiTU (beta 4, linear beta 25, no limit)
+ * and ReLU^2 without the gate multiply (no limit; w13 holds N rows, not 2N). */
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SITU = 1, MOE_ACT_RELU2_NO_MUL = 2 } moe_activation;
 /* Launch sequences of one chunk (the capacity ladder's choice unless a rung is
  * pinned): DECODE = two kernels, no route planner (T <= 16, T * top_k <= 64);
  * GENERAL = planner + 16-route-tile GEMMs + combine (any batch); PREFILL =
@@ -284,14 +284,21 @@ int moe_plan_set_swiglu_oai(moe_plan_t plan, float alpha, float beta);
 int moe_ep_remap(const int32_t *topk_ids, const float *topk_weights, int T, int top_k, long long offset,
                  int num_local, int32_t *out_ids, float *out_weights, void *stream);
 
-/* The activation form of the plan (moe_activation).  MOE_ACT_SITU: both
- * branches softly capped by tanh,
+/* The activation form of the plan (moe_activation); set it before preparing
+ * experts for the plan (the w13 row count follows it).
+ *   MOE_ACT_SITU: both branches softly capped by tanh,
  *     h = silu(4 tanh(gate / 4)) * 25 tanh(up / 25)
- * (vLLM "fused_moe/b12x" page: SiTU is taken only with beta 4 and linear beta
- * 25, without a limit, and is one of the two activations W4A8 runs; the page
- * does not print the formula, this is the reading taken).  Valid for every
- * activation format; MOE_EUNSUPPORTED on a plan with a swiglu limit or OAI
- * alpha / beta, or for an unknown form.  Host only. */
+ *   (vLLM "fused_moe/b12x" page: SiTU is taken only with beta 4 and linear beta
+ *   25, without a limit, and is one of the two activations W4A8 runs; the page
+ *   does not print the formula, this is the reading taken).  Any activation
+ *   format.
+ *   MOE_ACT_RELU2_NO_MUL: h[n] = relu(z[n])^2 for z = W13 . x with a w13 of N
+ *   rows ([E, N, K] codes and scales in the checkpoint layout; the same page
+ *   lists RELU2_NO_MUL and runs it without a gate multiply).  bf16 activations
+ *   only (the page refuses it with W4A8), N % 64 == 0, the default w13 layout;
+ *   the PREFILL sequence needs N % 128 == 0.
+ * MOE_EUNSUPPORTED on a plan with a swiglu limit or OAI alpha / beta for the
+ * other forms, for the cases above, or for an unknown form.  Host only. */
 int moe_plan_set_activation(moe_plan_t plan, int act);
 
 /* ---- instrumentation ------------------------------------------------- */

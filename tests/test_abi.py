@@ -240,3 +240,37 @@ def test_combine_pins_follow_the_ladder_scratch_and_tuning_file(tmp_path):
     open(v1, "w").write(f"moe v1 {key} cap=8 seq=2\n")
     r = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
     assert r.load_tuning(v1) == 1 and r.sequence(8) == M.SEQ_GENERAL and r.combine(8) == M.COMBINE_ATOMIC
+
+
+def test_activation_forms_are_validated_on_the_host():
+    a8 = M.Plan(8, 256, 128, 2, None, M.A_MXFP8, max_tokens=16)
+    a8.set_activation(M.ACT_SITU)                                  # SiTU runs with W4A8
+    for plan, code in ((M.Plan(8, 256, 128, 2, None, M.A_MXFP8, max_tokens=16), M.MOE_EUNSUPPORTED),   # W4A8
+                       (M.Plan(8, 256, 160, 2, None, M.A_BF16, max_tokens=16), M.MOE_EUNSUPPORTED),    # N % 64
+                       (M.Plan(8, 256, 128, 2, 7.0, M.A_BF16, max_tokens=16), M.MOE_EUNSUPPORTED),     # a limit
+                       (M.Plan(8, 256, 128, 2, None, M.A_BF16, M.W13_GATE_UP, 16), M.MOE_EUNSUPPORTED)):
+        with pytest.raises(M.MoeError) as e:
+            plan.set_activation(M.ACT_RELU2_NO_MUL)
+        assert e.value.code == code
+    with pytest.raises(M.MoeError):
+        M.Plan(8, 256, 128, 2, 7.0, M.A_BF16, max_tokens=16).set_activation(M.ACT_SITU)
+    with pytest.raises(M.MoeError):
+        a8.set_activation(9)
+    p = M.Plan(8, 256, 192, 2, None, M.A_BF16, max_tokens=1024)
+    p.set_sequence(1024, M.SEQ_PREFILL)
+    p.set_activation(M.ACT_RELU2_NO_MUL)               # N = 192: 96 pairs, no prefill kernel
+    assert p.sequence(1024) == M.SEQ_GENERAL           # the pin it can no longer take is dropped
+    with pytest.raises(M.MoeError):
+        p.set_sequence(1024, M.SEQ_PREFILL)
+    q = M.Plan(8, 256, 256, 2, None, M.A_BF16, max_tokens=1024)
+    q.set_activation(M.ACT_RELU2_NO_MUL)
+    q.set_sequence(1024, M.SEQ_PREFILL)
+    # the wrapper sizes w13 as N rows under ReLU^2
+    import torch
+    w13, s13, w2, s2 = (torch.zeros(n, dtype=torch.uint8) for n in M.weight_bytes(M.W_NVFP4, 8, 256, 256, 256))
+    assert w13.numel() == 8 * 256 * 128
+    with pytest.raises(ValueError, match="device"):    # sizes accepted, then refused for living on the CPU
+        M.Experts(q, M.W_NVFP4, 8, w13, s13, w2, s2)
+    big = torch.zeros(8 * 512 * 128, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="elements"):
+        M.Experts(q, M.W_NVFP4, 8, big, s13, w2, s2)

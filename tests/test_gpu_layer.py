@@ -476,3 +476,62 @@ def test_situ(name):
                           act_kind=O.ACT_SITU)
     plain, _ = O.moe_problem(L.prob)
     assert not np.allclose(acc, plain, rtol=1e-2), "SiTU must change this case"
+
+
+# ReLU^2 without the gate multiply (16-bit activations): w13 of N rows; every launch
+# sequence; NVFP4, NF3 and two tiers.
+def _relu2_problem(cfg, seed):
+    """A problem whose w13 keeps the first N of its 2N rows (the checkpoint of a
+    ReLU^2 layer has N rows)."""
+    import dataclasses
+    prob = I.make_problem(cfg, seed=seed)
+    N = cfg.N
+    tiers = []
+    for t in prob.tiers:
+        w = dict(t.weights)
+        w["w13"] = np.ascontiguousarray(w["w13"][:, :N])
+        w["s13"] = np.ascontiguousarray(w["s13"][:, :N])
+        tiers.append(dataclasses.replace(t, weights=w))
+    return dataclasses.replace(prob, tiers=tiers)
+
+
+RELU2 = {
+    "r2_general": (I.Config("r2_general", T=21, E=16, K=256, N=128, topk=4, limit=None, fmt=I.FMT_NVFP4), 31,
+                   None),
+    "r2_decode_nf3": (I.Config("r2_decode_nf3", T=6, E=20, K=512, N=192, topk=3, limit=None, fmt=I.FMT_NF3), 32,
+                      None),
+    "r2_prefill": (I.Config("r2_prefill", T=150, E=8, K=256, N=256, topk=4, limit=None, fmt=I.FMT_NVFP4,
+                            pad_rows=2), 33, M.SEQ_PREFILL),
+    "r2_hybrid_prefill": (I.Config("r2_hybrid_prefill", T=140, E=12, K=512, N=128, topk=3, limit=None,
+                                   fmt=I.FMT_NVFP4, hybrid_nvfp4=4), 34, M.SEQ_PREFILL),
+    "r2_hybrid_decode": (I.Config("r2_hybrid_decode", T=8, E=256, K=1024, N=512, topk=8, limit=None,
+                                  fmt=I.FMT_NVFP4, hybrid_nvfp4=64), 35, None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RELU2))
+def test_relu2_no_mul(name):
+    cfg, seed, pin = RELU2[name]
+    prob = _relu2_problem(cfg, seed)
+    L = DeviceLayer(prob, act=M.ACT_RELU2_NO_MUL)
+    if pin is not None:
+        L.plan.set_sequence(cfg.T, pin)
+    assert L.plan.sequence(cfg.T) == (pin or (M.SEQ_DECODE if "decode" in name else M.SEQ_GENERAL))
+    acc, _ = O.moe_problem(prob, act_kind=O.ACT_RELU2_NO_MUL)
+    for det in (False, True):
+        out = L.run(deterministic=det)
+        assert_rows_match(out, acc, label=f"{name} relu2 det={det}")
+
+
+def test_relu2_repack_round_trip():
+    cfg, seed, _ = RELU2["r2_decode_nf3"]
+    prob = _relu2_problem(cfg, seed)
+    L = DeviceLayer(prob, act=M.ACT_RELU2_NO_MUL)
+    ex, _ = L.tiers[0]
+    before = [t.cpu().clone() for t in L.keep[:4]]
+    ex.unpack()
+    torch.cuda.synchronize()
+    w = prob.tiers[0].weights
+    for t, k in zip(L.keep[:4], ("w13", "s13", "w2", "s2")):
+        assert np.array_equal(t.cpu().numpy(), w[k]), k
+    assert not torch.equal(before[0], L.keep[0].cpu())   # the tile layout differs from the checkpoint
