@@ -269,7 +269,7 @@ def measure(M, prob, copies, deterministic, args, dev):
     stage_ms, runs = plan.stage_times()
     plan.enable_stage_timing(0)
     stage_us = {s: 1000.0 * v / max(runs, 1) for s, v in zip(STAGES, stage_ms)}
-    sequence = {0: "decode", 64: "prefill"}.get(plan.capacity(cfg.T)[1], "general")
+    sequence = ("decode", "general", "prefill", "prefill_narrow")[plan.sequence(cfg.T) - 1]
     if sequence == "decode":
         # two launches, no route planner or combine kernel: the events bracketing those
         # empty stages measure only their own overhead
@@ -377,16 +377,23 @@ def main():
         copies = LayerCopies(M, prob, plan, args.layers, dev)
         us = plan.autotune(copies.run_tiers[0], toks, args.deterministic, reps=args.tune_reps)
         names = [s if c is None else f"{s}/{c}" for s, c in M.RACE_SLOTS]
-        seqs = ("decode", "general", "prefill")
+        seqs = ("decode", "general", "prefill", "prefill_narrow")
         combs = {M.COMBINE_ATOMIC: "atomic", M.COMBINE_ROUTE_BUFFER: "route_buffer"}
         rows = [{"tokens": t, "capacity": plan.capacity(t)[0],
                  "us": {n: (None if math.isnan(v) else round(v, 2)) for n, v in zip(names, u)},
                  "pinned": seqs[plan.sequence(t) - 1],
                  "combine": combs.get(plan.combine(t))} for t, u in zip(toks, us)]
+        # the same race at the workload's own batch (its routing, e.g. Zipf-skewed loads)
+        x = torch.from_numpy(prob.x).to(dev).view(torch.bfloat16)
+        own = plan.autotune_batch(copies.run_tiers[0], x, torch.from_numpy(prob.ids).to(dev),
+                                  torch.from_numpy(prob.wts).to(dev), args.deterministic, reps=args.tune_reps)
+        own_row = {"tokens": cfg.T, "capacity": plan.capacity(cfg.T)[0],
+                   "us": {n: (None if math.isnan(v) else round(v, 2)) for n, v in zip(names, own)},
+                   "pinned": seqs[plan.sequence(cfg.T) - 1], "combine": combs.get(plan.combine(cfg.T))}
         if args.tune_file:
             plan.save_tuning(args.tune_file)
         print(json.dumps({"workload": cfg.name, "deterministic": args.deterministic, "layer_copies": args.layers,
-                          "tuning": rows}), flush=True)
+                          "tuning": rows, "own_batch": own_row}), flush=True)
         return
 
     # the copies are prepared under a plan of the same geometry; experts run under any

@@ -21,11 +21,12 @@ W_MXFP4, W_NVFP4, W_NF3 = 1, 2, 3
 A_MXFP8, A_BF16 = 1, 2
 W13_UP_GATE, W13_GATE_UP = 0, 1
 ACT_SWIGLU, ACT_SITU, ACT_RELU2_NO_MUL = 0, 1, 2
-SEQ_AUTO, SEQ_DECODE, SEQ_GENERAL, SEQ_PREFILL = 0, 1, 2, 3
+SEQ_AUTO, SEQ_DECODE, SEQ_GENERAL, SEQ_PREFILL, SEQ_PREFILL_NARROW = 0, 1, 2, 3, 4
 COMBINE_AUTO, COMBINE_ATOMIC, COMBINE_ROUTE_BUFFER = 0, 1, 2
 # race slots of the autotuner: (sequence, combine of deterministic = 0 runs)
 RACE_SLOTS = (("decode", None), ("general", "atomic"), ("general", "route_buffer"), ("prefill", "atomic"),
-              ("prefill", "route_buffer"))
+              ("prefill", "route_buffer"), ("prefill_narrow", "atomic"), ("prefill_narrow", "route_buffer"))
+NSLOTS = len(RACE_SLOTS)
 
 
 class MoeError(RuntimeError):
@@ -111,7 +112,8 @@ class Plan:
         _check(_lib.load().moe_plan_set_sequence(self.handle, int(tokens), int(seq)))
 
     def sequence(self, tokens: int) -> int:
-        """The launch sequence a batch of `tokens` runs with (SEQ_DECODE / SEQ_GENERAL / SEQ_PREFILL)."""
+        """The launch sequence a batch of `tokens` runs with (SEQ_DECODE / SEQ_GENERAL / SEQ_PREFILL /
+        SEQ_PREFILL_NARROW)."""
         return _lib.load().moe_plan_sequence(self.handle, int(tokens))
 
     def set_combine(self, tokens: int, combine: int):
@@ -124,20 +126,20 @@ class Plan:
 
     def autotune(self, tiers, tokens, deterministic: bool = False, reps: int = 5, stream=None):
         """Race, at the rung of each batch size in `tokens`, the eligible (sequence, combine) pairs on a
-        synthetic batch and pin the fastest; returns [len(tokens)][5] median microseconds in RACE_SLOTS
+        synthetic batch and pin the fastest; returns [len(tokens)][7] median microseconds in RACE_SLOTS
         order (NaN where not raced)."""
         tok = [int(t) for t in tokens]
         arr, keep = _tiers(tiers, self)
         ta = (C.c_int * len(tok))(*tok)
-        us = (C.c_float * (5 * len(tok)))()
+        us = (C.c_float * (NSLOTS * len(tok)))()
         _check(_lib.load().moe_plan_autotune(self.handle, arr, len(tiers), ta, len(tok), int(bool(deterministic)),
                                              int(reps), _stream(stream), us))
-        return [[us[5 * i + k] for k in range(5)] for i in range(len(tok))]
+        return [[us[NSLOTS * i + k] for k in range(NSLOTS)] for i in range(len(tok))]
 
     def autotune_batch(self, tiers, x, topk_ids, topk_weights, deterministic: bool = False, reps: int = 5,
                        stream=None):
         """The same race at the rung of x's batch, on this batch itself (its own routing); returns the
-        5 median times in RACE_SLOTS order."""
+        7 median times in RACE_SLOTS order."""
         import torch
         T = x.shape[0]
         for device in (False, True):
@@ -145,11 +147,11 @@ class Plan:
             _need(topk_ids, "topk_ids", torch.int32, device, shape=(T, self.top_k))
             _need(topk_weights, "topk_weights", torch.float32, device, shape=(T, self.top_k))
         arr, keep = _tiers(tiers, self)
-        us = (C.c_float * 5)()
+        us = (C.c_float * NSLOTS)()
         _check(_lib.load().moe_plan_autotune_batch(self.handle, arr, len(tiers), _ptr(x), _ptr(topk_ids),
                                                    _ptr(topk_weights), T, int(bool(deterministic)), int(reps),
                                                    _stream(stream), us))
-        return [us[k] for k in range(5)]
+        return [us[k] for k in range(NSLOTS)]
 
     def save_tuning(self, path: str):
         _check(_lib.load().moe_plan_save_tuning(self.handle, os.fsencode(path)))

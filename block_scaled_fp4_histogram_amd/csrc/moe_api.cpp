@@ -121,7 +121,8 @@ bool route_buffer(const moe_plan_s *p, int cap, int deterministic) {
   if (deterministic) return true;
   const int pinned = p->comb[rung_of(p, cap)];
   if (pinned) return pinned == MOE_COMBINE_ROUTE_BUFFER;
-  return seq_for(p, cap) == MOE_SEQ_PREFILL;
+  const int seq = seq_for(p, cap);
+  return seq == MOE_SEQ_PREFILL || seq == MOE_SEQ_PREFILL_NARROW;
 }
 
 // Carving of the scratch arena for one chunk of `cap` tokens.
@@ -277,6 +278,8 @@ bool seq_eligible(const moe_plan_s *p, int cap, int seq) {
     case MOE_SEQ_DECODE: return use_decode(p, cap);   // then also for every chunk of <= cap tokens
     case MOE_SEQ_GENERAL: return true;
     case MOE_SEQ_PREFILL: return gemm1_pairs(p) % 64 == 0 && p->N % 64 == 0;
+    // 64-route up/gate tiles: a variant only where PREFILL runs 128-route ones (W4A8)
+    case MOE_SEQ_PREFILL_NARROW: return p->afmt == MOE_A_MXFP8 && p->N % 64 == 0;
     default: return false;
   }
 }
@@ -299,7 +302,8 @@ int seq_for(const moe_plan_s *p, int T) {
 // the route buffer and the top-k sum (1) or fp32 atomics (0).
 int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uint16_t *x, const int32_t *ids,
               const float *wts, uint16_t *out, int T, int deterministic, const Layout &L, uint8_t *scratch,
-              hipStream_t s, bool route_only, bool prefill, const hipEvent_t *ev = nullptr) {
+              hipStream_t s, bool route_only, bool prefill, const hipEvent_t *ev = nullptr,
+              bool narrow = false) {
   if (ev) HIP_TRY(hipEventRecord(ev[0], s));
   const int R = T * p->topk;
   auto I32 = [&](size_t o) { return (int32_t *)(scratch + o); };
@@ -329,7 +333,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ra.tile_row0 = I32(L.tile_row0);
   ra.tier_tiles = I32(L.tier_tiles);
   // 128-route tiles for the up/gate GEMM (its activation offsets are 32-bit)
-  const bool wide = prefill && p->afmt == MOE_A_MXFP8 && (uint64_t)T * p->K < (1ull << 32);
+  const bool wide = prefill && !narrow && p->afmt == MOE_A_MXFP8 && (uint64_t)T * p->K < (1ull << 32);
   if (wide) {
     ra.tile_rows2 = moe::kPfWideRows;
     ra.tile_u2 = I32(L.tile_u2);
@@ -534,10 +538,11 @@ int run_batch(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const voi
     uint16_t *oc = (uint16_t *)out + (size_t)t0 * p->K;
     const int seq = seq_for(p, tc);
     const int rb = route_buffer(p, cap, deterministic) ? 1 : 0;   // the combine the arena was carved for
+    const bool prefill = seq == MOE_SEQ_PREFILL || seq == MOE_SEQ_PREFILL_NARROW;
     const int rc = seq == MOE_SEQ_DECODE
                        ? run_decode(p, tiers, n_tiers, xc, idc, wc, oc, tc, L, scratch, s, ev)
-                       : run_chunk(p, tiers, n_tiers, xc, idc, wc, oc, tc, rb, L, scratch, s, false,
-                                   seq == MOE_SEQ_PREFILL, ev);
+                       : run_chunk(p, tiers, n_tiers, xc, idc, wc, oc, tc, rb, L, scratch, s, false, prefill, ev,
+                                   seq == MOE_SEQ_PREFILL_NARROW);
     if (rc != MOE_OK) return rc;
   }
   return MOE_OK;
@@ -669,7 +674,9 @@ int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows) {
   if (tile_rows) {
     // the sequence a chunk of that capacity takes: decode (no route tiles), prefill, general
     const int seq = seq_for(plan, std::min(std::max(T, 1), cap));
-    *tile_rows = seq == MOE_SEQ_DECODE ? 0 : seq == MOE_SEQ_PREFILL ? moe::kPfTileRows : moe::kTileRows;
+    *tile_rows = seq == MOE_SEQ_DECODE                                           ? 0
+                 : seq == MOE_SEQ_PREFILL || seq == MOE_SEQ_PREFILL_NARROW ? moe::kPfTileRows
+                                                                           : moe::kTileRows;
   }
   return cap;
 }
@@ -682,7 +689,7 @@ int moe_plan_set_sequence(moe_plan_t plan, int tokens, int seq) {
     plan->seq[r] = 0;
     return MOE_OK;
   }
-  if (seq != MOE_SEQ_DECODE && seq != MOE_SEQ_GENERAL && seq != MOE_SEQ_PREFILL)
+  if (seq != MOE_SEQ_DECODE && seq != MOE_SEQ_GENERAL && seq != MOE_SEQ_PREFILL && seq != MOE_SEQ_PREFILL_NARROW)
     return fail(MOE_EINVAL, "sequence %d", seq);
   if (!seq_eligible(plan, cap, seq))
     return fail(MOE_EUNSUPPORTED, "sequence %d cannot run the %d-token capacity of this plan", seq, cap);
@@ -799,9 +806,9 @@ namespace {
 // every launch sequence the rung can take, and for deterministic = 0 both combines
 // of the planner-based sequences; pins the fastest.  us_out[kRaceSlots]: median
 // microseconds of DECODE, GENERAL-atomic, GENERAL-route buffer, PREFILL-atomic,
-// PREFILL-route buffer (NaN where not raced; deterministic runs fill the
-// route-buffer slots).
-constexpr int kRaceSlots = 5;
+// PREFILL-route buffer, PREFILL_NARROW-atomic, PREFILL_NARROW-route buffer (NaN
+// where not raced; deterministic runs fill the route-buffer slots).
+constexpr int kRaceSlots = 7;
 
 int race_rung(moe_plan_s *plan, const moe_tier *tiers, int n_tiers, const void *x, const int32_t *ids,
               const float *wts, int T, int deterministic, int reps, hipStream_t s, float *us_out) {
@@ -813,7 +820,9 @@ int race_rung(moe_plan_s *plan, const moe_tier *tiers, int n_tiers, const void *
                                   {MOE_SEQ_GENERAL, MOE_COMBINE_ATOMIC},
                                   {MOE_SEQ_GENERAL, MOE_COMBINE_ROUTE_BUFFER},
                                   {MOE_SEQ_PREFILL, MOE_COMBINE_ATOMIC},
-                                  {MOE_SEQ_PREFILL, MOE_COMBINE_ROUTE_BUFFER}};
+                                  {MOE_SEQ_PREFILL, MOE_COMBINE_ROUTE_BUFFER},
+                                  {MOE_SEQ_PREFILL_NARROW, MOE_COMBINE_ATOMIC},
+                                  {MOE_SEQ_PREFILL_NARROW, MOE_COMBINE_ROUTE_BUFFER}};
   struct Restore {   // the rung's previous pins come back if the race stops early
     moe_plan_s *p;
     int r, seq, comb;

@@ -66,8 +66,16 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SITU = 1, MOE_ACT_RELU2_NO_MUL = 2 } 
 /* Launch sequences of one chunk (the capacity ladder's choice unless a rung is
  * pinned): DECODE = two kernels, no route planner (T <= 16, T * top_k <= 64);
  * GENERAL = planner + 16-route-tile GEMMs + combine (any batch); PREFILL =
- * planner + 64-route-tile GEMMs + combine (N % 64 == 0). */
-typedef enum { MOE_SEQ_AUTO = 0, MOE_SEQ_DECODE = 1, MOE_SEQ_GENERAL = 2, MOE_SEQ_PREFILL = 3 } moe_sequence;
+ * planner + 64-route-tile GEMMs + combine (N % 64 == 0), the W4A8 up/gate GEMM
+ * on 128-route tiles; PREFILL_NARROW = PREFILL with 64-route up/gate tiles
+ * (W4A8 only: a tile height for the race). */
+typedef enum {
+  MOE_SEQ_AUTO = 0,
+  MOE_SEQ_DECODE = 1,
+  MOE_SEQ_GENERAL = 2,
+  MOE_SEQ_PREFILL = 3,
+  MOE_SEQ_PREFILL_NARROW = 4
+} moe_sequence;
 /* How runs with deterministic = 0 combine the k slots of a token (the
  * GENERAL and PREFILL sequences; DECODE folds them in its down GEMM either
  * way): ATOMIC = fp32 atomic adds into an accumulator, then one bf16 cast;
@@ -212,17 +220,19 @@ int moe_plan_capacity(moe_plan_t plan, int T, int *tile_rows);
  * (moe_scratch_bytes), so pin before sizing the arena.  Host only.
  *
  * moe_plan_autotune races, at the rung of each listed batch size, every launch
- * sequence the rung can take and, for deterministic = 0, both combines of the
- * GENERAL and PREFILL sequences, on a seeded synthetic batch of the rung's
- * full size with the caller's prepared experts (`reps` timed runs after two
- * warm-up runs, median), and pins the rung's sequence and combine to the
- * fastest.  us_out (NULL or [n][5]) receives the median microseconds of
- * DECODE, GENERAL-atomic, GENERAL-route buffer, PREFILL-atomic and
- * PREFILL-route buffer, NaN where not raced (deterministic races fill the
- * route-buffer entries).  moe_plan_autotune_batch races the rung of T on the
- * caller's own batch instead (device x [T, K] bf16, topk_ids, topk_weights;
- * T <= max_tokens; us_out NULL or [5]): the workload's routing, e.g. skewed
- * expert loads, decides.  Both allocate and synchronise (a tuning session,
+ * sequence the rung can take (so the route-tile height: 16 GENERAL, 64 / 128
+ * PREFILL, 64 PREFILL_NARROW) and, for deterministic = 0, both combines of the
+ * planner-based sequences, on a seeded synthetic batch of the rung's full
+ * size with the caller's prepared experts (`reps` timed runs after two warm-up
+ * runs, median), and pins the rung's sequence and combine to the fastest.
+ * us_out (NULL or [n][7]) receives the median microseconds of DECODE,
+ * GENERAL-atomic, GENERAL-route buffer, PREFILL-atomic, PREFILL-route buffer,
+ * PREFILL_NARROW-atomic and PREFILL_NARROW-route buffer, NaN where not raced
+ * (deterministic races fill the route-buffer entries).
+ * moe_plan_autotune_batch races the rung of T on the caller's own batch
+ * instead (device x [T, K] bf16, topk_ids, topk_weights; T <= max_tokens;
+ * us_out NULL or [7]): the workload's routing, e.g. skewed expert loads,
+ * decides.  Both allocate and synchronise (a tuning session,
  * not part of the layer): call them before graph capture.
  *
  * moe_plan_save_tuning writes the plan's pinned rungs to a text file, one line

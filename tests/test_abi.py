@@ -274,3 +274,18 @@ def test_activation_forms_are_validated_on_the_host():
     big = torch.zeros(8 * 512 * 128, dtype=torch.uint8)
     with pytest.raises(ValueError, match="elements"):
         M.Experts(q, M.W_NVFP4, 8, big, s13, w2, s2)
+
+
+def test_narrow_prefill_sequence_is_a_w4a8_variant(tmp_path):
+    p = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
+    p.set_sequence(4096, M.SEQ_PREFILL_NARROW)
+    assert p.sequence(4096) == M.SEQ_PREFILL_NARROW and p.capacity(4096)[1] == 64
+    assert p.combine(4096) == M.COMBINE_ROUTE_BUFFER          # a prefill sequence: the ladder's combine
+    path = str(tmp_path / "n.txt")
+    p.save_tuning(path)
+    q = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
+    assert q.load_tuning(path) == 1 and q.sequence(4096) == M.SEQ_PREFILL_NARROW
+    a16 = M.Plan(256, 6144, 512, 8, None, M.A_BF16, max_tokens=2048)
+    with pytest.raises(M.MoeError) as e:
+        a16.set_sequence(2048, M.SEQ_PREFILL_NARROW)           # only W4A8 runs 128-route up/gate tiles
+    assert e.value.code == M.MOE_EUNSUPPORTED

@@ -288,7 +288,8 @@ def test_swiglu_oai(name, deterministic):
 # Launch sequences pinned per capacity rung (moe_plan_set_sequence): batches the ladder
 # (or the pin above) would send down another sequence must give the same layer on the
 # pinned one.
-@pytest.mark.parametrize("name,seq", [("hybrid_decode", M.SEQ_GENERAL), ("hybrid_decode", M.SEQ_PREFILL),
+@pytest.mark.parametrize("name,seq", [("prefill_small", M.SEQ_PREFILL_NARROW), ("prefill_n768", M.SEQ_PREFILL_NARROW),
+                                      ("hybrid_decode", M.SEQ_GENERAL), ("hybrid_decode", M.SEQ_PREFILL),
                                       ("nf3_decode", M.SEQ_GENERAL), ("nvfp4_clamped", M.SEQ_PREFILL),
                                       ("decode_many_routes", M.SEQ_PREFILL), ("prefill_small", M.SEQ_GENERAL),
                                       ("hybrid_small", M.SEQ_PREFILL), ("mxfp4_ragged", M.SEQ_GENERAL)])
@@ -307,8 +308,10 @@ def test_pinned_sequence(name, seq, deterministic):
     assert_rows_match(out, acc, label=f"{name} sequence {seq} det={deterministic}", prob=L.prob)
 
 
-_SLOT_SEQ = (M.SEQ_DECODE, M.SEQ_GENERAL, M.SEQ_GENERAL, M.SEQ_PREFILL, M.SEQ_PREFILL)
-_SLOT_COMB = (None, M.COMBINE_ATOMIC, M.COMBINE_ROUTE_BUFFER, M.COMBINE_ATOMIC, M.COMBINE_ROUTE_BUFFER)
+_SLOT_SEQ = (M.SEQ_DECODE, M.SEQ_GENERAL, M.SEQ_GENERAL, M.SEQ_PREFILL, M.SEQ_PREFILL, M.SEQ_PREFILL_NARROW,
+             M.SEQ_PREFILL_NARROW)
+_SLOT_COMB = (None, M.COMBINE_ATOMIC, M.COMBINE_ROUTE_BUFFER, M.COMBINE_ATOMIC, M.COMBINE_ROUTE_BUFFER,
+              M.COMBINE_ATOMIC, M.COMBINE_ROUTE_BUFFER)
 
 
 def _check_pins(plan, t, us, deterministic):
@@ -325,7 +328,8 @@ def test_autotune_pins_the_fastest_sequence_and_combine(deterministic):
     T = L.prob.cfg.T
     try:
         us = L.plan.autotune(L.tiers, [T, 8], deterministic=deterministic, reps=3)
-        assert math.isnan(us[0][0]) and all(v > 0 for v in us[0][2::2])
+        # hybrid_small is NVFP4 / NF3: no PREFILL_NARROW slots
+        assert math.isnan(us[0][0]) and us[0][2] > 0 and us[0][4] > 0 and all(math.isnan(v) for v in us[0][5:])
         assert us[1][0] > 0 and us[1][2] > 0 and us[1][4] > 0
         if deterministic:
             assert all(math.isnan(v) for v in (us[0][1], us[0][3], us[1][1], us[1][3]))
@@ -353,14 +357,15 @@ def test_autotune_on_the_workload_s_own_batch(name):
     before = L.plan.sequence(T)
     try:
         us = L.plan.autotune_batch(L.tiers, x, ids, wts, reps=3)
-        assert all(v > 0 for v in us[1:])
+        a8 = p.tiers[0].fmt == I.FMT_MXFP4
+        assert all(v > 0 for v in us[1:5])
+        assert all((v > 0) if a8 else math.isnan(v) for v in us[5:])   # the 64-route up/gate variant: W4A8
         _check_pins(L.plan, T, us, False)
         out = L.run(deterministic=False)
     finally:
         L.plan.set_sequence(T, before)
         L.plan.set_combine(T, M.COMBINE_AUTO)
     acc, _ = O.moe_problem(p)
-    a8 = p.tiers[0].fmt == I.FMT_MXFP4
     assert_rows_match(out, acc, label=f"{name} after autotune_batch", prob=p if a8 else None)
 
 
