@@ -333,7 +333,9 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ra.tile_row0 = I32(L.tile_row0);
   ra.tier_tiles = I32(L.tier_tiles);
   // 128-route tiles for the up/gate GEMM (its activation offsets are 32-bit)
-  const bool wide = prefill && !narrow && p->afmt == MOE_A_MXFP8 && (uint64_t)T * p->K < (1ull << 32);
+  // (and it stages every route's whole scale row in LDS: K <= 8704)
+  const bool wide = prefill && !narrow && p->afmt == MOE_A_MXFP8 && (uint64_t)T * p->K < (1ull << 32) &&
+                    p->K <= moe::kPfWideMaxK;
   if (wide) {
     ra.tile_rows2 = moe::kPfWideRows;
     ra.tile_u2 = I32(L.tile_u2);

@@ -10,6 +10,7 @@ namespace moe {
 constexpr int kTileRows = 16;        // routes of one tile of the general GEMM kernels
 constexpr int kPfTileRows = 64;      // routes of one tile of the prefill kernels
 constexpr int kPfWideRows = 128;     // routes of one tile of the prefill W4A8 up/gate kernel
+constexpr int kPfWideMaxK = 8704;    // largest K it takes (it stages the tile's activation scale rows in LDS)
 constexpr int kPrefillMinT = 512;    // smallest batch the ladder runs with the prefill kernels
 constexpr int kRouteChunk = 1024;    // routes handled by one route-planner block
 constexpr int kMaxExperts = 1024;    // experts of all tiers together (LDS histogram size)

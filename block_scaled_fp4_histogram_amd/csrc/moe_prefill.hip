@@ -435,37 +435,80 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8(GemmArgs a) {
 // halves of 64 (the second skipped in tiles of at most 64 routes), and the MFMAs
 // of 16-route blocks past the tile's last route are skipped.
 constexpr int kPwStages = 2;
-// vector-memory operations of one wave per stage: 4 weight tiles, 4 weight
-// scale dwords, 4 activation blocks, 1 activation scale chunk (or a spare)
-constexpr int kPwLoads = 13;
+// Activation scales: every route's whole scale row (K / 32 bytes) is staged in
+// LDS once per block, rows kPwXsRow bytes apart (68 dwords: the 16 routes a
+// read touches fall in 16 different banks).  Per-k-tile scale loads would each
+// touch one 128-byte line per route, a third of the lines a step requests.
+constexpr int kPwXsRow = 272;
+constexpr int kPwMaxK = kPwXsRow * 32;   // largest reduction the staged rows hold
 
 struct PwStage {
   uint8_t B[16][1024];            // activation rows 8b .. 8b+7 of block b, swizzled 16-byte chunks
-  uint8_t S[1024];                // Bs [128][4] | 2 spare 256-byte slots
 };
 
 struct __attribute__((aligned(16))) PwLds {
   PwStage st[kPwStages];
+  uint8_t XS[kPfWideRows * kPwXsRow];   // the tile's 128 activation scale rows
 };
 
 struct PwSrc {
   PfSrc w;                        // weights (wb, sb, wstep, sstep, nrt, kbytes)
-  const uint8_t *xq, *xs;         // MXFP8 activations and their scales (uniform bases)
+  const uint8_t *xq;              // MXFP8 activations (uniform base)
   uint32_t brow[4];               // byte offsets of this lane's activation rows of its four B blocks
-  uint32_t bsrow;                 // byte offset of the scale row of route 64 (w & 1) + lane
 };
 
 // Activation blocks 4w .. 4w+3 of k-tile kt into stage S (lane l -> row l / 8
-// of its block, chunk slot l), and the scales of routes 64 (w & 1) .. +63 (waves
-// 0, 1; waves 2, 3 fill spare slots to keep the per-wave load count equal).  The
-// reduction is whole k-tiles (K % 256 == 0).
+// of its block, chunk slot l).  The reduction is whole k-tiles (K % 256 == 0).
 __device__ __forceinline__ void pw_issue_b(PwStage &S, const PwSrc &src, int kt, int w, int l) {
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int r8 = l >> 3, part = (l & 7) ^ r8;
     dma16(src.xq + (src.brow[j] + (uint32_t)(kt * 128 + part * 16)), &S.B[4 * w + j][0]);
   }
-  dma4(src.xs + (src.bsrow + (uint32_t)(4 * kt)), &S.S[256 * w]);
+}
+
+// Every route's scale row into XS by direct 16-byte loads: wave w fills the
+// 1 KB chunks w, w + 4, ... (chunk q of the flat XS holds part q % 17 of row
+// q / 17; parts past the row's K / 32 bytes re-read part 0, padding nothing
+// reads).  Rows past the tile read route p0's token.
+__device__ __forceinline__ void pw_stage_scales(PwLds &L, const GemmArgs &a, const PfWork &wk, int w, int l) {
+  constexpr int kParts = kPwXsRow / 16, kChunks = kPfWideRows * kParts / 64;
+  const int row_bytes = a.K / 32;
+  for (int i = w; i < kChunks; i += 4) {
+    const int q = i * 64 + l, r = q / kParts, part = q - r * kParts;
+    const int tok = a.perm[wk.p0 + (r < wk.rows ? r : 0)] / a.topk;
+    dma16(a.xs + (size_t)tok * row_bytes + (part * 16 < row_bytes ? part * 16 : 0), &L.XS[i * 1024]);
+  }
+}
+
+// The 64 routes of half H of a landed stage (as pf_read_b_at) and their scales
+// of k-tile kt from XS: vxs = XS + c * kPwXsRow + g, offsets per 16-route block.
+template <int H>
+__device__ __forceinline__ void pw_read_b(v4i (&b)[4][2], int (&sb)[4], const PwStage &S, uint32_t vxs, int kt,
+                                          int l) {
+  const int c = l & 15, g = l >> 4, r8 = c & 7;
+  const uint8_t *blk = &S.B[8 * H + (c >> 3)][0];   // + 2 KB per route block
+  const uint32_t vb0 = lds_addr(blk + pf_slot(r8, g) * 16), vb1 = lds_addr(blk + pf_slot(r8, 4 + g) * 16),
+                 vsb = vxs + (uint32_t)(4 * kt);
+  constexpr int R16 = 16 * kPwXsRow, O = 64 * H * kPwXsRow;   // bytes per 16 routes; half H's first route
+  asm volatile(
+      "ds_read_b128 %0, %12\n"
+      "ds_read_b128 %1, %13\n"
+      "ds_read_b128 %2, %12 offset:2048\n"
+      "ds_read_b128 %3, %13 offset:2048\n"
+      "ds_read_b128 %4, %12 offset:4096\n"
+      "ds_read_b128 %5, %13 offset:4096\n"
+      "ds_read_b128 %6, %12 offset:6144\n"
+      "ds_read_b128 %7, %13 offset:6144\n"
+      "ds_read_u8 %8, %14 offset:%c15\n"
+      "ds_read_u8 %9, %14 offset:%c16\n"
+      "ds_read_u8 %10, %14 offset:%c17\n"
+      "ds_read_u8 %11, %14 offset:%c18\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[1][0]), "=&v"(b[1][1]), "=&v"(b[2][0]), "=&v"(b[2][1]),
+        "=&v"(b[3][0]), "=&v"(b[3][1]), "=&v"(sb[0]), "=&v"(sb[1]), "=&v"(sb[2]), "=&v"(sb[3])
+      : "v"(vb0), "v"(vb1), "v"(vsb), "i"(O), "i"(O + R16), "i"(O + 2 * R16), "i"(O + 3 * R16)
+      : "memory");
 }
 
 // 16 MFMAs of one half (routes 64 h .. 64 h + 63) of a k-tile: the half's
@@ -490,7 +533,7 @@ __device__ __forceinline__ void pw_mma(const PfW &wt, const v4i (&b)[4][2], cons
 // slots kt - 1 held (ISSUE), then both halves of stage kt.
 template <int R, bool ISSUE>
 __device__ __forceinline__ void pw_step(PwLds &L, const PwSrc &src, PfW (&ring)[kPwStages], int kt, int w,
-                                        bool active, int nrb, v4f (*acc)[8]) {
+                                        bool active, int nrb, uint32_t vxs, v4f (*acc)[8]) {
   const int l = threadIdx.x & 63;
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
@@ -501,12 +544,12 @@ __device__ __forceinline__ void pw_step(PwLds &L, const PwSrc &src, PfW (&ring)[
   if (active) {
     v4i b[4][2];
     int sb[4];
-    pf_read_b_at(b, sb, &L.st[R].B[0], &L.st[R].S[0], l);
+    pw_read_b<0>(b, sb, L.st[R], vxs, kt, l);
     __builtin_amdgcn_s_setprio(1);
     pw_mma<0>(ring[R], b, sb, nrb, l, acc);
     __builtin_amdgcn_s_setprio(0);
     if (nrb > 4) {
-      pf_read_b_at(b, sb, &L.st[R].B[8], &L.st[R].S[256], l);
+      pw_read_b<1>(b, sb, L.st[R], vxs, kt, l);
       __builtin_amdgcn_s_setprio(1);
       pw_mma<1>(ring[R], b, sb, nrb, l, acc);
       __builtin_amdgcn_s_setprio(0);
@@ -536,29 +579,28 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8w(GemmArgs a) {
   // rows past the tile read route p0's token; their results are never stored
   // 32-bit byte offsets: the host runs this kernel only for chunks with T * K < 2^32
   src.xq = a.xq;
-  src.xs = a.xs;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int row = 8 * (4 * w + j) + (l >> 3);
     src.brow[j] = (uint32_t)(a.perm[wk.p0 + (row < wk.rows ? row : 0)] / a.topk) * (uint32_t)K;
   }
-  const int srow = 64 * (w & 1) + l;
-  src.bsrow = (uint32_t)(a.perm[wk.p0 + (srow < wk.rows ? srow : 0)] / a.topk) * (uint32_t)(K / 32);
   const int nrb = __builtin_amdgcn_readfirstlane((wk.rows + 15) / 16);
   const bool active = kPfQ * w < src.w.nrt;
   v4f acc[kPfQ][8];
   zero_acc<kPfQ, 8>(acc);
   const int nkt = K / 128;   // even: K % 256 == 0
   PfW ring[kPwStages];
+  pw_stage_scales(L, a, wk, wu, l);   // landed by the first step's wait
   pf_load_w(ring[0], src.w, 0, wu, l);
   pw_issue_b(L.st[0], src, 0, wu, l);
+  const uint32_t vxs = lds_addr(&L.XS[c * kPwXsRow + g]);
   int kt = 0;
   for (; kt + 2 < nkt; kt += 2) {
-    pw_step<0, true>(L, src, ring, kt, wu, active, nrb, acc);
-    pw_step<1, true>(L, src, ring, kt + 1, wu, active, nrb, acc);
+    pw_step<0, true>(L, src, ring, kt, wu, active, nrb, vxs, acc);
+    pw_step<1, true>(L, src, ring, kt + 1, wu, active, nrb, vxs, acc);
   }
-  pw_step<0, true>(L, src, ring, kt, wu, active, nrb, acc);
-  pw_step<1, false>(L, src, ring, kt + 1, wu, active, nrb, acc);
+  pw_step<0, true>(L, src, ring, kt, wu, active, nrb, vxs, acc);
+  pw_step<1, false>(L, src, ring, kt + 1, wu, active, nrb, vxs, acc);
   if (!active) return;   // the missing half of a partial block
   // epilogue: row tiles 4w + 2s (up) and 4w + 2s + 1 (gate) = intermediate
   // columns 128 hb + 32 w + 16 s .. +15; their 32 columns form one MXFP8 group
