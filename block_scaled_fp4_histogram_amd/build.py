@@ -14,6 +14,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # an entry point that references a missing definition fails here, not at load time
+    "-Wl,--no-undefined",
     "-munsafe-fp-atomics",
     # MFMA accumulators in VGPRs: in-place accumulation, no AGPR copies in pipelined loops
     "-mllvm", "-amdgpu-mfma-vgpr-form",

@@ -11,6 +11,7 @@ constexpr int kTileRows = 16;        // routes of one tile of the general GEMM k
 constexpr int kPfTileRows = 64;      // routes of one tile of the prefill kernels
 constexpr int kPfWideRows = 128;     // routes of one tile of the prefill W4A8 up/gate kernel
 constexpr int kPfWideMaxK = 8704;    // largest K it takes (it stages the tile's activation scale rows in LDS)
+constexpr int kPfResSlots = 512;     // resident blocks of the prefill W4A8 down GEMM (2 per CU)
 constexpr int kPrefillMinT = 512;    // smallest batch the ladder runs with the prefill kernels
 constexpr int kRouteChunk = 1024;    // routes handled by one route-planner block
 constexpr int kMaxExperts = 1024;    // experts of all tiers together (LDS histogram size)
@@ -93,6 +94,8 @@ struct GemmArgs {
   const uint8_t *w13b, *s13b, *w2b, *s2b;
   const float *g13b, *g2b;
   int fmt_a, fmt_b, u_base_b;
+  // prefill W4A8 down GEMM with the route-buffer combine: 256-column output blocks per block (0: one)
+  int obg;
 };
 
 // Decode-size batches (T <= kDecodeMaxT tokens, T * top_k <= 64 routes): two

@@ -197,19 +197,22 @@ __device__ __forceinline__ void pf_mma(const PfW &wt, const v4i (&b)[4][2], cons
     const v4i b1 = in1 ? b[cb][1] : v4i{0, 0, 0, 0};
     bop[cb] = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
   }
-  // route blocks past the tile's last route hold padding: their MFMAs are skipped
+  // route blocks past the tile's last route hold padding: their MFMAs are skipped,
+  // one branch per route block (4 MFMAs)
+  int sa[kPfQ];
 #pragma unroll
-  for (int q = 0; q < kPfQ; q++) {
-    const int sa = gin ? (int)(wt.sa[q] >> (8 * (l & 3))) : 0;   // the MFMA takes the low byte
+  for (int q = 0; q < kPfQ; q++) sa[q] = gin ? (int)(wt.sa[q] >> (8 * (l & 3))) : 0;   // the MFMA takes the low byte
 #pragma unroll
-    for (int cb = 0; cb < 4; cb++) {
-      if (cb < nrb) {
-        const int sbv = gin ? sb[cb] : 0;
+  for (int cb = 0; cb < 4; cb++) {
+    if (cb < nrb) {
+      const int sbv = gin ? sb[cb] : 0;
+#pragma unroll
+      for (int q = 0; q < kPfQ; q++) {
         if (SWAP)
           acc[q][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bop[cb], fp4_operand(wt.a[q]), acc[q][cb], 0,
-                                                                        4, 0, sbv, 0, sa);
+                                                                        4, 0, sbv, 0, sa[q]);
         else
-          acc[q][cb] = mfma_fp4_fp8(wt.a[q], bop[cb], acc[q][cb], sa, sbv);
+          acc[q][cb] = mfma_fp4_fp8(wt.a[q], bop[cb], acc[q][cb], sa[q], sbv);
       }
     }
   }
@@ -740,6 +743,125 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8_short(GemmArgs a) {
   pf_combine<kPfQ, 4>(a, g2.wk, acc, s_r, s_w, (size_t)256 * g2.ob + 64 * w + c, 0, c, g, (uint8_t *)&L);
 }
 
+// ------------------------------------ GEMM2, resident intermediate rows
+// The down GEMM of the route-buffer combine as blocks of (64-route tile, run
+// of a.obg 256-column output blocks).  The tile's MXFP8 intermediate rows and
+// scales (all NKT k-tiles of N <= 128 NKT) go into LDS once per block, in the
+// stage layout of the other W4A8 kernels; each wave then streams its weights
+// through a register ring of NKT k-tiles that runs on across the output
+// blocks of the run, so the next block's weights are in flight while the
+// current one is multiplied and its route-buffer rows are stored.  A block of
+// one output block paid the intermediate rows' load, the perm lookups and the
+// ring's first round trip for five k-tiles of MFMAs; here it pays them once
+// per run.  The LDS rows are read-only after the first barrier and the
+// combine stages through per-wave regions, so the loop has no barrier.
+template <int NKT>
+struct PfResLds {
+  PfStage st[NKT];
+  uint8_t rb[4 * 16 * (32 * kPfQ + 16)];   // per-wave route-buffer staging (pf_store_rb)
+};
+
+// Weight and scale loads of row tiles rt0 .. rt0 + 3 (wave-uniform) for
+// k-tile kt.  vd / vs: the lane's byte offsets inside a k-tile's data / scales
+// (l * 16 and l & ~3), or past the buffer's range (zeros without memory
+// traffic) for loads past the run or lanes past the reduction length; the
+// k-tile's own offset goes into the scalar offset, so one lane offset serves
+// every k-tile.
+__device__ __forceinline__ void pf_load_w_rt(PfW &r, const PfSrc &src, uint32_t rt0, int kt, uint32_t vd,
+                                             uint32_t vs) {
+#pragma unroll
+  for (int q = 0; q < kPfQ; q++) {
+    r.a[q] = buf_load16(src.wb, vd, (rt0 + q) * src.wstep + (uint32_t)kt * 1024u);
+    r.sa[q] = buf_load4(src.sb, vs, (rt0 + q) * src.sstep + (uint32_t)kt * 64u);
+  }
+}
+
+// One block's work.
+template <int NKT, bool LASTFULL>
+__device__ __forceinline__ void pf_res_body(PfResLds<NKT> &L, const GemmArgs &a, const PfWork &wk, int *s_r,
+                                            float *s_w) {
+  const int K = a.K, N = a.N, nob = K / 256, obg = a.obg;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int ob0 = wk.sub * obg, ob1 = min(nob, ob0 + obg);
+  PfSrc src;
+  src.wstep = (uint32_t)(16 * (N / 2));
+  src.sstep = (uint32_t)(16 * (N / 32));
+  src.nrt = kPfRT;
+  src.wb = make_buf(a.w2 + (size_t)wk.e * K * (N / 2), (uint32_t)((size_t)K * (N / 2)));
+  src.sb = make_buf(a.s2 + (size_t)wk.e * K * (N / 32), (uint32_t)((size_t)K * (N / 32)));
+  src.kbytes = N;
+  src.nrb = __builtin_amdgcn_readfirstlane((wk.rows + 15) / 16);
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int row = 8 * (2 * w + j) + (l >> 3);
+    src.brow[j] = a.hq + (size_t)(wk.p0 + (row < wk.rows ? row : 0)) * N;
+  }
+  src.bsrow = a.hs + (size_t)(wk.p0 + (l < wk.rows ? l : 0)) * hs_stride(N);
+  if (tid < wk.rows) {
+    const int r = a.perm[wk.p0 + tid];
+    s_r[tid] = r;
+    s_w[tid] = a.topk_w[r];
+  }
+  // the tile's intermediate rows (every k-tile), then the first output block's weights
+#pragma unroll
+  for (int kt = 0; kt < NKT; kt++) pf_issue_b(L.st[kt], src, kt, wu, l);
+  // lane offsets inside a k-tile.  The lanes of a partial last k-tile past N
+  // load the next row tile's bytes (or zeros past the expert): E2M1 codes are
+  // finite, and the MFMA step zeroes their activations and scales.
+  const uint32_t kOut = 0x80000000u, vd = (uint32_t)(l * 16), vs = (uint32_t)(l & ~3);
+  PfW ring[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; kt++) pf_load_w_rt(ring[kt], src, (uint32_t)(16 * ob0 + 4 * wu), kt, vd, vs);
+  // the rows have landed once only the weight loads may be in flight; then
+  // every wave's share (and s_r / s_w) is visible
+  wait_vm<2 * kPfQ * NKT>();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  for (int ob = ob0; ob < ob1; ob++) {
+    // the epilogue's route rows and weights are re-read from LDS in each pass: hoisted out
+    // of the loop as addresses, they would stay live in registers next to the ring and spill
+    asm volatile("" ::: "memory");
+    const bool next = ob + 1 < ob1;
+    const uint32_t rtn = (uint32_t)(16 * (next ? ob + 1 : ob) + 4 * wu);
+    const uint32_t nd = next ? vd : kOut, ns = next ? vs : kOut;
+    v4f acc[kPfQ][4];
+    zero_acc<kPfQ, 4>(acc);
+#pragma unroll
+    for (int kt = 0; kt < NKT; kt++) {
+      // slot kt holds this block's k-tile kt once at most the NKT - 1 slots
+      // issued after it are in flight (stores in between only add to the count)
+      wait_vm<2 * kPfQ * (NKT - 1)>();
+      v4i b[4][2];
+      int sb[4];
+      pf_read_b(b, sb, L.st[kt], l);
+      __builtin_amdgcn_s_setprio(1);
+      if (kt < NKT - 1 || LASTFULL) pf_mma<true, true>(ring[kt], b, sb, kt, N, src.nrb, l, acc);
+      else pf_mma<true, false>(ring[kt], b, sb, kt, N, src.nrb, l, acc);
+      __builtin_amdgcn_s_setprio(0);
+      // the next output block's k-tile kt into the slot the MFMAs above read; issued after
+      // them (hoisted above, the loads would need a second register set and spill), and no
+      // step is interleaved with the next for the same reason
+      __builtin_amdgcn_sched_barrier(0);
+      pf_load_w_rt(ring[kt], src, rtn, kt, nd, ns);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // acc[q][cb][i]: route 16 cb + 4 g + i, output column 256 ob + 64 w + 16 q + c
+    pf_store_rb<kPfQ, 4>(a, wk, acc, s_r, s_w, (size_t)256 * ob + 64 * w, c, g, L.rb);
+  }
+}
+
+template <int NKT, bool LASTFULL>
+__global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8_res(GemmArgs a) {
+  __shared__ PfResLds<NKT> L;
+  __shared__ int s_r[kPfTileRows];
+  __shared__ float s_w[kPfTileRows];
+  const int nob = a.K / 256;
+  const PfWork wk = pf_work(a, (nob + a.obg - 1) / a.obg, false);
+  if (!wk.valid) return;
+  pf_res_body<NKT, LASTFULL>(L, a, wk, s_r, s_w);
+}
+
 static int pf_grid(int grid_tiles, int nsub) { return (grid_tiles * nsub + 7) / 8 * 8; }
 
 hipError_t launch_pf_gemm1(const GemmArgs &a, int grid_tiles, hipStream_t s) {
@@ -751,8 +873,26 @@ hipError_t launch_pf_gemm1(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NKT>
+static void launch_pf_gemm2_res(const GemmArgs &a, dim3 grid, hipStream_t s) {
+  if (a.N == 128 * NKT) hipLaunchKernelGGL((k_pf_gemm2_a8_res<NKT, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_pf_gemm2_a8_res<NKT, false>), grid, dim3(256), 0, s, a);
+}
+
 hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
+  const int nkt = (a.N + 127) / 128;
+  if (a.deterministic && a.obg > 0 && nkt <= 5) {   // the route-buffer combine: resident intermediate rows
+    const dim3 grid(pf_grid(grid_tiles, (a.K / 256 + a.obg - 1) / a.obg));
+    switch (nkt) {
+      case 1: launch_pf_gemm2_res<1>(a, grid, s); break;
+      case 2: launch_pf_gemm2_res<2>(a, grid, s); break;
+      case 3: launch_pf_gemm2_res<3>(a, grid, s); break;
+      case 4: launch_pf_gemm2_res<4>(a, grid, s); break;
+      default: launch_pf_gemm2_res<5>(a, grid, s); break;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid(pf_grid(grid_tiles, a.K / 256)), block(256);
   switch ((a.N + 127) / 128) {
     case 1: hipLaunchKernelGGL(k_pf_gemm2_a8_short<1>, grid, block, 0, s, a); break;
