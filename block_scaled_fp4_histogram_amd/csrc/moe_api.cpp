@@ -399,7 +399,8 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   // 182 us; runs of 10, 7, 4, 2: 187, 185, 189, 200 us; one run of 28 leaves
   // CUs idle: 187 us)
   {
-    const int nob = p->K / 256, tiles = std::max(1, R / moe::kPfTileRows);
+    // output blocks of 256 columns (W4A8) or 128 (16-bit activations)
+    const int nob = p->afmt == MOE_A_MXFP8 ? p->K / 256 : p->K / 128, tiles = std::max(1, R / moe::kPfTileRows);
     const int runs = std::min(nob, std::max(2, (moe::kPfResSlots + tiles - 1) / tiles));
     ga.obg = (nob + runs - 1) / runs;
   }

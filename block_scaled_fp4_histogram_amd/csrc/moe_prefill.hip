@@ -1334,8 +1334,159 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16_tiers(GemmArgs a) {
   else pf16_gemm2_body<W_NF3>(a, wk, T, L, s_r, s_w);
 }
 
+// ------------------------ GEMM2 (A16), resident intermediate rows
+// The route-buffer combine's down GEMM as blocks of (64-route tile, run of
+// a.obg 128-column output blocks), as the W4A8 one: the tile's bf16
+// intermediate rows (all NKT k-tiles of N <= 128 NKT, 16 KB each) go into LDS
+// once, and each wave streams its two weight row tiles of every output block
+// of the run through a register ring of NKT k-tiles, so the next block's
+// weights are in flight while the current one is multiplied and stored.  (One
+// block per output block paid the rows' load, the perm lookups and the ring's
+// first round trip for four k-tiles at N = 512.)
+template <int NKT>
+struct Pf16ResLds {
+  Pf16Stage st[NKT];
+  uint8_t rb[4 * 16 * (32 * 2 + 16)];   // per-wave route-buffer staging (pf_store_rb)
+};
+
+// Weight and scale loads of row tiles rt0, rt0 + 1 (wave-uniform) for k-tile
+// kt; vd / vs: the lane's offsets inside a k-tile's data / scales, or past the
+// buffer's range (zeros, no traffic).  The k-tile's own offset is scalar.
+template <int WF>
+__device__ __forceinline__ void pf16_load_w_rt(Pf16W &r, const Pf16Src &src, uint32_t rt0, int kt, uint32_t vd,
+                                               uint32_t vs) {
+  constexpr uint32_t U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const uint32_t so = (rt0 + q) * src.wstep + (uint32_t)kt * 64u * U, ss = (rt0 + q) * src.sstep + (uint32_t)kt * 64u * SU;
+    if constexpr (WF == W_NVFP4) {
+      const v4i v = buf_load16(src.wb, vd, so);
+      r.a[q][0] = v[0]; r.a[q][1] = v[1]; r.a[q][2] = v[2]; r.a[q][3] = v[3];
+    } else {
+      const v3i v = buf_load12(src.wb, vd, so);
+      r.a[q][0] = v[0]; r.a[q][1] = v[1]; r.a[q][2] = v[2]; r.a[q][3] = 0;
+    }
+    r.sc[q] = buf_load4(src.sb, vs, ss);
+  }
+}
+
+template <int WF, int NKT, bool LASTFULL>
+__device__ __forceinline__ void pf16_gemm2_res_body(const GemmArgs &a, const PfWork &wk, const PfTier &T,
+                                                    Pf16ResLds<NKT> &L, int *s_r, float *s_w) {
+  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  const int K = a.K, N = a.N, nob = K / 128, groups = N / 32;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int ob0 = wk.sub * a.obg, ob1 = min(nob, ob0 + a.obg);
+  Pf16Src src;
+  src.wstep = (uint32_t)(16 * groups * U);
+  src.sstep = (uint32_t)(16 * groups * SU);
+  src.wb = make_buf(T.w2 + (size_t)wk.e * K * groups * U, (uint32_t)((size_t)K * groups * U));
+  src.sb = make_buf(T.s2 + (size_t)wk.e * K * groups * SU, (uint32_t)((size_t)K * groups * SU));
+  src.kcols = N;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int row = 4 * (4 * w + j) + (l >> 4);
+    src.brow[j] = a.hb + (size_t)(wk.p0 + (row < wk.rows ? row : 0)) * N;
+  }
+  if (tid < wk.rows) {
+    const int r = a.perm[wk.p0 + tid];
+    s_r[tid] = r;
+    s_w[tid] = (a.w_on_input ? 1.0f : a.topk_w[r]) * (T.g2 ? T.g2[wk.e] : 1.0f);
+  }
+  // the tile's intermediate rows (every k-tile), then the first output block's weights
+#pragma unroll
+  for (int kt = 0; kt < NKT; kt++) pf16_issue_b(L.st[kt], src, kt, wu, l);
+  // lane offsets: a whole k-tile, and the partial last one (lanes past N load
+  // zeros: their scales then decode to 0, so no garbage code meets a zeroed input)
+  const uint32_t kOut = 0x80000000u, vd = (uint32_t)(l * U), vs = (uint32_t)((l * SU) & ~3);
+  const bool lin = LASTFULL || (NKT - 1) * 128 + 32 * g < N;
+  const uint32_t vdl = lin ? vd : kOut, vsl = lin ? vs : kOut;
+  Pf16W ring[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; kt++)
+    pf16_load_w_rt<WF>(ring[kt], src, (uint32_t)(8 * ob0 + 2 * wu), kt, kt < NKT - 1 ? vd : vdl, kt < NKT - 1 ? vs : vsl);
+  // the rows have landed once only the weight loads may be in flight; then
+  // every wave's share (and s_r / s_w) is visible
+  wait_vm<4 * NKT>();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  for (int ob = ob0; ob < ob1; ob++) {
+    asm volatile("" ::: "memory");   // keep the epilogue's LDS reads in the epilogue
+    const bool next = ob + 1 < ob1;
+    const uint32_t rtn = (uint32_t)(8 * (next ? ob + 1 : ob) + 2 * wu);
+    const uint32_t nd = next ? vd : kOut, ns = next ? vs : kOut, ndl = next ? vdl : kOut, nsl = next ? vsl : kOut;
+    v4f acc[2][4];
+    zero_acc<2, 4>(acc);
+#pragma unroll
+    for (int kt = 0; kt < NKT; kt++) {
+      wait_vm<4 * (NKT - 1)>();   // slot kt has landed (the NKT - 1 later slots may be in flight)
+      v4i b[4][4];
+      pf16_read_b(b, L.st[kt], l);
+      if (kt < NKT - 1 || LASTFULL) pf16_mma<WF, true, true>(ring[kt], b, kt, N, l, acc);
+      else pf16_mma<WF, true, false>(ring[kt], b, kt, N, l, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      pf16_load_w_rt<WF>(ring[kt], src, rtn, kt, kt < NKT - 1 ? nd : ndl, kt < NKT - 1 ? ns : nsl);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // acc[q][cb][i]: route 16 cb + 4 g + i, output column 128 ob + 32 w + 16 q + c
+    pf_store_rb<2, 4>(a, wk, acc, s_r, s_w, (size_t)128 * ob + 32 * w, c, g, L.rb);
+  }
+}
+
+template <int WF, int NKT, bool LASTFULL>
+__global__ __launch_bounds__(256, 2) void k_pf_gemm2_a16_res(GemmArgs a) {
+  __shared__ Pf16ResLds<NKT> L;
+  __shared__ int s_r[kPfTileRows];
+  __shared__ float s_w[kPfTileRows];
+  const PfWork wk = pf_work(a, (a.K / 128 + a.obg - 1) / a.obg, false);
+  if (!wk.valid) return;
+  pf16_gemm2_res_body<WF, NKT, LASTFULL>(a, wk, pf_tier(a, 0), L, s_r, s_w);
+}
+
+template <int NKT, bool LASTFULL>
+__global__ __launch_bounds__(256, 2) void k_pf_gemm2_a16_res_tiers(GemmArgs a) {
+  __shared__ Pf16ResLds<NKT> L;
+  __shared__ int s_r[kPfTileRows];
+  __shared__ float s_w[kPfTileRows];
+  int tier = 0;
+  const PfWork wk = pf_work_tiers(a, (a.K / 128 + a.obg - 1) / a.obg, false, &tier);
+  if (!wk.valid) return;
+  const PfTier T = pf_tier(a, tier);
+  if ((tier ? a.fmt_b : a.fmt_a) == W_NVFP4) pf16_gemm2_res_body<W_NVFP4, NKT, LASTFULL>(a, wk, T, L, s_r, s_w);
+  else pf16_gemm2_res_body<W_NF3, NKT, LASTFULL>(a, wk, T, L, s_r, s_w);
+}
+
+// The resident down GEMM for the route-buffer combine at N <= 512 (NKT <= 4);
+// false where it does not apply.
+template <int WF, int NKT>
+static void launch_pf16_res_n(const GemmArgs &a, dim3 grid, hipStream_t s, bool tiers) {
+  if (tiers) {
+    if (a.N == 128 * NKT) hipLaunchKernelGGL((k_pf_gemm2_a16_res_tiers<NKT, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_pf_gemm2_a16_res_tiers<NKT, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.N == 128 * NKT) hipLaunchKernelGGL((k_pf_gemm2_a16_res<WF, NKT, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_pf_gemm2_a16_res<WF, NKT, false>), grid, dim3(256), 0, s, a);
+  }
+}
+
+template <int WF>
+static bool launch_pf16_res(const GemmArgs &a, int grid_tiles, hipStream_t s, bool tiers) {
+  const int nkt = (a.N + 127) / 128;
+  if (!a.deterministic || a.obg <= 0 || nkt > 4) return false;
+  const dim3 grid(pf_grid(grid_tiles, (a.K / 128 + a.obg - 1) / a.obg));
+  switch (nkt) {
+    case 1: launch_pf16_res_n<WF, 1>(a, grid, s, tiers); break;
+    case 2: launch_pf16_res_n<WF, 2>(a, grid, s, tiers); break;
+    case 3: launch_pf16_res_n<WF, 3>(a, grid, s, tiers); break;
+    default: launch_pf16_res_n<WF, 4>(a, grid, s, tiers); break;
+  }
+  return true;
+}
+
 template <int WF>
 static hipError_t launch_pf_a16(const GemmArgs &a, int grid_tiles, hipStream_t s, bool second) {
+  if (second && launch_pf16_res<WF>(a, grid_tiles, s, false)) return hipGetLastError();
   if (second) hipLaunchKernelGGL(k_pf_gemm2_a16<WF>, dim3(pf_grid(grid_tiles, a.K / 128)), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_pf_gemm1_a16<WF>, dim3(pf_grid(grid_tiles, a.N1 / 64)), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -1360,6 +1511,7 @@ hipError_t launch_pf16_gemm1_tiers(const GemmArgs &a, int grid_tiles, hipStream_
 
 hipError_t launch_pf16_gemm2_tiers(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
+  if (launch_pf16_res<W_NVFP4>(a, grid_tiles, s, true)) return hipGetLastError();
   hipLaunchKernelGGL(k_pf_gemm2_a16_tiers, dim3(pf_grid(grid_tiles, a.K / 128)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
