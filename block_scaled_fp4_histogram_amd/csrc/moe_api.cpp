@@ -157,12 +157,12 @@ Layout layout(const moe_plan_s *p, int cap, int deterministic) {
   L.tile_u = take(4 * (size_t)L.max_tiles);
   L.tile_row0 = take(4 * (size_t)L.max_tiles);
   L.tier_tiles = take(4 * 2 * moe::kMaxTiers);
+  // the prefill up/gate GEMM's table of 128-route tiles
+  L.max_tiles2 = (int)((R + moe::kPfWideRows - 1) / moe::kPfWideRows + std::min<size_t>(U, R));
+  L.tile_u2 = take(4 * (size_t)L.max_tiles2);
+  L.tile_row02 = take(4 * (size_t)L.max_tiles2);
+  L.tier_tiles2 = take(4 * 2 * moe::kMaxTiers);
   if (p->afmt == MOE_A_MXFP8) {
-    // the prefill up/gate GEMM's table of 128-route tiles
-    L.max_tiles2 = (int)((R + moe::kPfWideRows - 1) / moe::kPfWideRows + std::min<size_t>(U, R));
-    L.tile_u2 = take(4 * (size_t)L.max_tiles2);
-    L.tile_row02 = take(4 * (size_t)L.max_tiles2);
-    L.tier_tiles2 = take(4 * 2 * moe::kMaxTiers);
     L.xq = take((size_t)cap * p->K);
     L.xs = take((size_t)cap * (p->K / 32));
     L.hq = take(R * p->N);
@@ -277,9 +277,9 @@ bool seq_eligible(const moe_plan_s *p, int cap, int seq) {
   switch (seq) {
     case MOE_SEQ_DECODE: return use_decode(p, cap);   // then also for every chunk of <= cap tokens
     case MOE_SEQ_GENERAL: return true;
-    case MOE_SEQ_PREFILL: return gemm1_pairs(p) % 64 == 0 && p->N % 64 == 0;
-    // 64-route up/gate tiles: a variant only where PREFILL runs 128-route ones (W4A8)
-    case MOE_SEQ_PREFILL_NARROW: return p->afmt == MOE_A_MXFP8 && p->N % 64 == 0;
+    // PREFILL_NARROW: PREFILL with the up/gate GEMM on 64-route tiles as well
+    case MOE_SEQ_PREFILL:
+    case MOE_SEQ_PREFILL_NARROW: return gemm1_pairs(p) % 64 == 0 && p->N % 64 == 0;
     default: return false;
   }
 }
@@ -332,10 +332,11 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
   ra.tile_u = I32(L.tile_u);
   ra.tile_row0 = I32(L.tile_row0);
   ra.tier_tiles = I32(L.tier_tiles);
-  // 128-route tiles for the up/gate GEMM (its activation offsets are 32-bit)
-  // (and it stages every route's whole scale row in LDS: K <= 8704)
-  const bool wide = prefill && !narrow && p->afmt == MOE_A_MXFP8 && (uint64_t)T * p->K < (1ull << 32) &&
-                    p->K <= moe::kPfWideMaxK;
+  // 128-route tiles for the up/gate GEMM: its activation offsets are 32-bit, and
+  // the W4A8 one stages every route's whole scale row in LDS (K <= 8704)
+  const bool wide = prefill && !narrow &&
+                    (p->afmt == MOE_A_MXFP8 ? (uint64_t)T * p->K < (1ull << 32) && p->K <= moe::kPfWideMaxK
+                                            : (uint64_t)2 * T * p->K < (1ull << 32));
   if (wide) {
     ra.tile_rows2 = moe::kPfWideRows;
     ra.tile_u2 = I32(L.tile_u2);
@@ -428,7 +429,17 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     ga.fmt_b = xb->wfmt;
     ga.u_base_b = xa->E;
     const int grid_tiles = row_tiles + std::min(xa->E + xb->E, R);
-    HIP_TRY(moe::launch_pf16_gemm1_tiers(ga, grid_tiles, s));
+    if (wide) {
+      moe::GemmArgs gw = ga;
+      gw.tile_rows = moe::kPfWideRows;
+      gw.tile_u = I32(L.tile_u2);
+      gw.tile_row0 = I32(L.tile_row02);
+      gw.tier_tiles = I32(L.tier_tiles2);
+      HIP_TRY(moe::launch_pf16_gemm1_tiers(
+          gw, (R + moe::kPfWideRows - 1) / moe::kPfWideRows + std::min(xa->E + xb->E, R), s));
+    } else {
+      HIP_TRY(moe::launch_pf16_gemm1_tiers(ga, grid_tiles, s));
+    }
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));
     HIP_TRY(moe::launch_pf16_gemm2_tiers(ga, grid_tiles, s));
     if (ev) HIP_TRY(hipEventRecord(ev[3], s));
@@ -448,13 +459,15 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     ga.g13 = xp->g13;
     ga.g2 = xp->g2;
     const int grid_tiles = row_tiles + std::min(xp->E, R);
-    if (wide && xp->wfmt == MOE_W_MXFP4) {
+    if (wide) {
       moe::GemmArgs gw = ga;
       gw.tile_rows = moe::kPfWideRows;
       gw.tile_u = I32(L.tile_u2);
       gw.tile_row0 = I32(L.tile_row02);
       gw.tier_tiles = I32(L.tier_tiles2);
-      HIP_TRY(moe::launch_pf_gemm1(gw, (R + moe::kPfWideRows - 1) / moe::kPfWideRows + std::min(xp->E, R), s));
+      const int wtiles = (R + moe::kPfWideRows - 1) / moe::kPfWideRows + std::min(xp->E, R);
+      if (xp->wfmt == MOE_W_MXFP4) HIP_TRY(moe::launch_pf_gemm1(gw, wtiles, s));
+      else HIP_TRY(moe::launch_pf16_gemm1(xp->wfmt, gw, wtiles, s));
     } else if (prefill && xp->wfmt == MOE_W_MXFP4) HIP_TRY(moe::launch_pf_gemm1(ga, grid_tiles, s));
     else if (prefill) HIP_TRY(moe::launch_pf16_gemm1(xp->wfmt, ga, grid_tiles, s));
     else HIP_TRY(moe::launch_gemm1(xp->wfmt, ga, grid_tiles, s));

@@ -1275,6 +1275,198 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16_tiers(GemmArgs a) {
   else pf16_gemm1_body<W_NF3>(a, wk, T, L);
 }
 
+// ------------------------------------------ GEMM1 (A16), 128-route tiles
+// The W4A16 / W3A16 up/gate GEMM on the up/gate table of 128-route tiles: the
+// same block of 8 weight row tiles (up and gate of 64 intermediate columns,
+// row tiles 2w, 2w + 1 for wave w) against up to 128 routes.  Each wave
+// dequantises its two row tiles' k-tile once and feeds the operands to the
+// MFMAs of both 64-route halves, half the dequantisation per MFMA of 64-route
+// tiles; where every expert's routes fit one tile (the 2048-token NVFP4
+// prefill: at most 95 routes an expert) each expert's weights are streamed
+// once instead of once per 64-route tile, and the MFMAs of 16-route blocks
+// holding only padding are skipped.  Activations: a 2-stage LDS ring of 32 KB
+// stages (128 routes x 256 bytes of a bf16 k-tile, 16-byte chunks XOR-swizzled
+// by route % 16 as on 64-route tiles); weights: a 2-deep register ring; one
+// k-tile of lookahead (two blocks per CU).  K % 256 == 0 (every plan's).
+constexpr int kPw16Stages = 2;
+
+struct Pw16Stage {
+  uint8_t B[kPfWideRows][256];
+};
+
+struct __attribute__((aligned(16))) Pw16Lds {
+  Pw16Stage st[kPw16Stages];
+};
+
+struct Pw16Src {
+  Pf16Src w;                      // the block's weight row tiles (wb, sb, wstep, sstep, kcols)
+  const uint8_t *xb;              // bf16 activations (uniform base)
+  uint32_t brow[8];               // byte offsets of this lane's activation rows of its 8 chunks
+};
+
+// Activation chunks 8w .. 8w+7 of k-tile kt (1 KB each: 4 routes x 256 bytes;
+// lane l -> route 4 (8w + j) + l / 16, LDS slot l % 16 holding global chunk
+// slot ^ route % 16).
+__device__ __forceinline__ void pw16_issue_b(Pw16Stage &S, const Pw16Src &src, int kt, int w, int l) {
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int r = 4 * (8 * w + j) + (l >> 4), cg = (l & 15) ^ (r & 15);
+    dma16(src.xb + (src.brow[j] + (uint32_t)(kt * 256 + 16 * cg)), &S.B[4 * (8 * w + j)][0]);
+  }
+}
+
+// The wave's two row tiles of one k-tile as bf16 MFMA operands: aop[q][s] =
+// 8 columns of step s (scales decoded once per row tile).
+template <int WF>
+__device__ __forceinline__ void pw16_deq(const Pf16W &wt, int l, v8bf (&aop)[2][4]) {
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const uint32_t sc = pf16_scale<WF>(wt.sc[q], l);
+    if constexpr (WF == W_NVFP4) {
+      const float slo = e4m3_f32_branched(sc & 0xFFu), shi = e4m3_f32_branched((sc >> 8) & 0xFFu);
+#pragma unroll
+      for (int st = 0; st < 4; st++) aop[q][st] = nvfp4_step(wt.a[q][st], st < 2 ? slo : shi);
+    } else {
+      uint32_t t01, t23;
+      nf3_tables(e4m3_f32_branched(sc & 0xFFu), t01, t23);
+#pragma unroll
+      for (int st = 0; st < 4; st++) aop[q][st] = nf3_step_rc(st < 2 ? wt.a[q][0] : wt.a[q][1], wt.a[q][2], st, t01, t23);
+    }
+  }
+}
+
+// The MFMAs of half H (routes 64 H .. 64 H + 63) of a k-tile; route blocks
+// past the tile's last route are skipped, one branch per block (8 MFMAs).
+template <int H>
+__device__ __forceinline__ void pw16_mma(const v8bf (&aop)[2][4], const v4i (&b)[4][4], int nrb, v4f (*acc)[8]) {
+#pragma unroll
+  for (int cb = 0; cb < 4; cb++) {
+    if (4 * H + cb < nrb) {
+#pragma unroll
+      for (int st = 0; st < 4; st++) {
+        const v8bf bop = __builtin_bit_cast(v8bf, b[st][cb]);
+#pragma unroll
+        for (int q = 0; q < 2; q++) acc[q][4 * H + cb] = mfma_bf16(aop[q][st], bop, acc[q][4 * H + cb]);
+      }
+    }
+  }
+}
+
+// One k-tile (R = kt % 2): wait for stage kt (the only one in flight), barrier
+// (every wave is also done with stage kt - 1), issue k-tile kt + 1 into the
+// slots kt - 1 held (ISSUE), dequantise, then both halves of stage kt.
+template <int WF, int R, bool ISSUE>
+__device__ __forceinline__ void pw16_step(Pw16Lds &L, const Pw16Src &src, Pf16W (&ring)[kPw16Stages], int kt, int w,
+                                          int nrb, v4f (*acc)[8]) {
+  const int l = threadIdx.x & 63;
+  wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  if (ISSUE) {
+    pf16_load_w<WF>(ring[R ^ 1], src.w, kt + 1, w, l);
+    pw16_issue_b(L.st[R ^ 1], src, kt + 1, w, l);
+  }
+  v8bf aop[2][4];
+  pw16_deq<WF>(ring[R], l, aop);
+  v4i b[4][4];
+  pf16_read_b(b, *(const Pf16Stage *)&L.st[R].B[0][0], l);
+  __builtin_amdgcn_s_setprio(1);
+  pw16_mma<0>(aop, b, nrb, acc);
+  __builtin_amdgcn_s_setprio(0);
+  if (nrb > 4) {
+    pf16_read_b(b, *(const Pf16Stage *)&L.st[R].B[64][0], l);
+    __builtin_amdgcn_s_setprio(1);
+    pw16_mma<1>(aop, b, nrb, acc);
+    __builtin_amdgcn_s_setprio(0);
+  }
+}
+
+template <int WF>
+__device__ __forceinline__ void pw16_gemm1_body(const GemmArgs &a, const PfWork &wk, const PfTier &T, Pw16Lds &L) {
+  constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  const int K = a.K, N = a.N, N1 = a.N1;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int hb = wk.sub, groups = K / 32;
+  Pw16Src src;
+  src.w.wstep = (uint32_t)(16 * groups * U);
+  src.w.sstep = (uint32_t)(16 * groups * SU);
+  src.w.wb = make_buf(T.w13 + (size_t)wk.e * (2 * N1) * groups * U + (size_t)(8 * hb) * src.w.wstep, 8 * src.w.wstep);
+  src.w.sb = make_buf(T.s13 + (size_t)wk.e * (2 * N1) * groups * SU + (size_t)(8 * hb) * src.w.sstep, 8 * src.w.sstep);
+  src.w.kcols = K;
+  src.xb = (const uint8_t *)a.xb;
+  // rows past the tile read route p0's token; their results are never stored.
+  // 32-bit byte offsets: the host runs this kernel only for chunks with 2 T K < 2^32
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int row = 4 * (8 * w + j) + (l >> 4);
+    src.brow[j] = (uint32_t)(a.perm[wk.p0 + (row < wk.rows ? row : 0)] / a.topk) * (uint32_t)(2 * K);
+  }
+  const int nrb = __builtin_amdgcn_readfirstlane((wk.rows + 15) / 16);
+  v4f acc[2][8];
+  zero_acc<2, 8>(acc);
+  const int nkt = K / 128;
+  Pf16W ring[kPw16Stages];
+  pf16_load_w<WF>(ring[0], src.w, 0, wu, l);
+  pw16_issue_b(L.st[0], src, 0, wu, l);
+  // an even number of k-tiles: K % 256 == 0
+  int kt = 0;
+  for (; kt + 2 < nkt; kt += 2) {
+    pw16_step<WF, 0, true>(L, src, ring, kt, wu, nrb, acc);
+    pw16_step<WF, 1, true>(L, src, ring, kt + 1, wu, nrb, acc);
+  }
+  pw16_step<WF, 0, true>(L, src, ring, kt, wu, nrb, acc);
+  pw16_step<WF, 1, false>(L, src, ring, kt + 1, wu, nrb, acc);
+  // epilogue: row tiles 2w (up) and 2w + 1 (gate) = intermediate columns 64 hb + 16 w .. +15;
+  // acc[q][cb][i]: route 16 cb + c, column 16 w + 4 g + i
+  const float g13 = T.g13 ? T.g13[wk.e] : 1.0f;
+#pragma unroll
+  for (int cb = 0; cb < 8; cb++) {
+    if (cb >= nrb) break;
+    const int row = 16 * cb + c;
+    if (row < wk.rows) {
+      const size_t p = (size_t)(wk.p0 + row);
+      // router weight on the input: GEMM1 is linear, so it scales the accumulators
+      const float gs = g13 * (a.w_on_input ? a.topk_w[a.perm[p]] : 1.0f);
+      uint2 v;
+      if (a.act == ACT_RELU2) {
+        // ReLU^2 without the multiply: the up and gate halves' rows give columns n and N1 + n
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+          v.x = pack_bf16x2(relu2(acc[half][cb][0] * gs), relu2(acc[half][cb][1] * gs));
+          v.y = pack_bf16x2(relu2(acc[half][cb][2] * gs), relu2(acc[half][cb][3] * gs));
+          *(uint2 *)(a.hb + p * N + half * N1 + 64 * hb + 16 * w + 4 * g) = v;
+        }
+        continue;
+      }
+      float h[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        h[i] = silu_clamped(acc[1][cb][i] * gs, acc[0][cb][i] * gs, a.limit, a.has_limit, a.alpha, a.beta, a.act);
+      v.x = pack_bf16x2(h[0], h[1]);
+      v.y = pack_bf16x2(h[2], h[3]);
+      *(uint2 *)(a.hb + p * N + 64 * hb + 16 * w + 4 * g) = v;
+    }
+  }
+}
+
+template <int WF>
+__global__ __launch_bounds__(256, 2) void k_pf_gemm1_a16w(GemmArgs a) {
+  __shared__ Pw16Lds L;
+  const PfWork wk = pf_work(a, a.N1 / 64, false);
+  if (!wk.valid) return;
+  pw16_gemm1_body<WF>(a, wk, pf_tier(a, 0), L);
+}
+
+__global__ __launch_bounds__(256, 2) void k_pf_gemm1_a16w_tiers(GemmArgs a) {
+  __shared__ Pw16Lds L;
+  int tier = 0;
+  const PfWork wk = pf_work_tiers(a, a.N1 / 64, false, &tier);
+  if (!wk.valid) return;
+  const PfTier T = pf_tier(a, tier);
+  if ((tier ? a.fmt_b : a.fmt_a) == W_NVFP4) pw16_gemm1_body<W_NVFP4>(a, wk, T, L);
+  else pw16_gemm1_body<W_NF3>(a, wk, T, L);
+}
+
 // ---------------------------------------------------------------- GEMM2 (A16)
 // Block: w2 row tiles 8 ob .. +7 = output columns 128 ob .. +127.
 template <int WF>
@@ -1488,6 +1680,8 @@ template <int WF>
 static hipError_t launch_pf_a16(const GemmArgs &a, int grid_tiles, hipStream_t s, bool second) {
   if (second && launch_pf16_res<WF>(a, grid_tiles, s, false)) return hipGetLastError();
   if (second) hipLaunchKernelGGL(k_pf_gemm2_a16<WF>, dim3(pf_grid(grid_tiles, a.K / 128)), dim3(256), 0, s, a);
+  else if (a.tile_rows == kPfWideRows)
+    hipLaunchKernelGGL(k_pf_gemm1_a16w<WF>, dim3(pf_grid(grid_tiles, a.N1 / 64)), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_pf_gemm1_a16<WF>, dim3(pf_grid(grid_tiles, a.N1 / 64)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -1505,7 +1699,9 @@ hipError_t launch_pf16_gemm2(int wfmt, const GemmArgs &a, int grid_tiles, hipStr
 // grid_tiles: an upper bound on both tiers' tiles together.
 hipError_t launch_pf16_gemm1_tiers(const GemmArgs &a, int grid_tiles, hipStream_t s) {
   if (grid_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pf_gemm1_a16_tiers, dim3(pf_grid(grid_tiles, a.N1 / 64)), dim3(256), 0, s, a);
+  if (a.tile_rows == kPfWideRows)
+    hipLaunchKernelGGL(k_pf_gemm1_a16w_tiers, dim3(pf_grid(grid_tiles, a.N1 / 64)), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_pf_gemm1_a16_tiers, dim3(pf_grid(grid_tiles, a.N1 / 64)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -66,9 +66,9 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SITU = 1, MOE_ACT_RELU2_NO_MUL = 2 } 
 /* Launch sequences of one chunk (the capacity ladder's choice unless a rung is
  * pinned): DECODE = two kernels, no route planner (T <= 16, T * top_k <= 64);
  * GENERAL = planner + 16-route-tile GEMMs + combine (any batch); PREFILL =
- * planner + 64-route-tile GEMMs + combine (N % 64 == 0), the W4A8 up/gate GEMM
- * on 128-route tiles; PREFILL_NARROW = PREFILL with 64-route up/gate tiles
- * (W4A8 only: a tile height for the race). */
+ * planner + 64-route-tile GEMMs + combine (N % 64 == 0), the up/gate GEMM on
+ * 128-route tiles; PREFILL_NARROW = PREFILL with 64-route up/gate tiles (a tile
+ * height for the race). */
 typedef enum {
   MOE_SEQ_AUTO = 0,
   MOE_SEQ_DECODE = 1,

@@ -286,6 +286,9 @@ def test_narrow_prefill_sequence_is_a_w4a8_variant(tmp_path):
     q = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
     assert q.load_tuning(path) == 1 and q.sequence(4096) == M.SEQ_PREFILL_NARROW
     a16 = M.Plan(256, 6144, 512, 8, None, M.A_BF16, max_tokens=2048)
+    a16.set_sequence(2048, M.SEQ_PREFILL_NARROW)               # 16-bit plans run 128-route up/gate tiles too
+    assert a16.sequence(2048) == M.SEQ_PREFILL_NARROW
+    odd = M.Plan(256, 6144, 544, 8, None, M.A_BF16, max_tokens=2048)
     with pytest.raises(M.MoeError) as e:
-        a16.set_sequence(2048, M.SEQ_PREFILL_NARROW)           # only W4A8 runs 128-route up/gate tiles
+        odd.set_sequence(2048, M.SEQ_PREFILL_NARROW)           # as PREFILL: N % 64 == 0 only
     assert e.value.code == M.MOE_EUNSUPPORTED
