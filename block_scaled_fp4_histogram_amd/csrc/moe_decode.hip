@@ -258,17 +258,19 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
   for (int p0 = 0; p0 < ncols; p0 += a.cpass) {
     const int ncol = min(a.cpass, ncols - p0);
     const bool have = c < ncol;
-    // three k-tiles of weights in flight per wave: tiles w, w + NW, w + 2 NW, ...
-    // Every load is issued, past the last k-tile too (zeros, no traffic): with
-    // loads under branches the compiler's wait before each MFMA group drained
-    // nearly every load in flight, the newly issued k-tiles included.
-    Stage s0, s1, s2;
+    // two k-tiles of weights in flight per wave: tiles w, w + NW, ... (three
+    // measured 1.4 us slower for the NVFP4 up/gate GEMM at K = 6144 and level
+    // for MXFP4: with every block resident, more requests only lengthen the
+    // memory queues).  Every load is issued, past the last k-tile too (zeros,
+    // no traffic): with loads under branches the compiler's wait before each
+    // MFMA group drained nearly every load in flight, the newly issued k-tiles
+    // included.
+    Stage s0, s1;
     auto load = [&](Stage &st, int kt) {
       if constexpr (A8) a8w_load(st, rt, lu, kt, kt < nkt);
       else a16w_load<WF>(st, rt, lu, kt, kt < nkt);
     };
     load(s0, w);
-    load(s1, w + NW);
     dec_stage_x<A8, NW>(a, md, p0, ncol, dsm);
     __syncthreads();
     v4f acc[4];
@@ -284,13 +286,11 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
         a16w_mfma<WF>(st, (const uint16_t *)dsm + cc * (K + 8), have, g, kt, acc);
       }
     };
-    for (int kt = w; kt < nkt; kt += 3 * NW) {
-      load(s2, kt + 2 * NW);
+    for (int kt = w; kt < nkt; kt += 2 * NW) {
+      load(s1, kt + NW);
       mfma(s0, kt);
-      load(s0, kt + 3 * NW);
+      load(s0, kt + 2 * NW);
       if (kt + NW < nkt) mfma(s1, kt + NW);
-      load(s1, kt + 4 * NW);
-      if (kt + 2 * NW < nkt) mfma(s2, kt + 2 * NW);
     }
     __syncthreads();   // the staged rows are dead; LDS becomes the reduction buffer
 #pragma unroll
