@@ -917,7 +917,7 @@ hipError_t launch_pf_gemm2(const GemmArgs &a, int grid_tiles, hipStream_t s) {
 // order) straight into a ring of kPf16Stages register sets.  The activations
 // are shared by the four waves and go through an LDS ring of the same depth:
 // a stage holds the 64 routes' bf16 slices of one 128-column k-tile (256 bytes
-// each, 16-byte chunks XOR-swizzled by row % 16) loaded directly to LDS.
+// each, 16-byte chunks XOR-swizzled by route (pf16_slot)) loaded directly to LDS.
 namespace {
 
 constexpr int kPf16Stages = 3;
@@ -985,13 +985,26 @@ __device__ __forceinline__ void pf16_load_w(Pf16W &r, const Pf16Src &src, int kt
   }
 }
 
+// LDS slot of 16-byte chunk k (8 bf16 columns) of a route row (256 bytes, one
+// k-tile), and its inverse: XOR-swizzled by route % 16 so that the 16 routes a
+// read touches spread over the banks, and bit 3 flipped for chunks 4..7 and
+// 12..15, so that the two 16-lane quarters of a read (chunk groups g and g ^ 1)
+// fall in different halves of the row.  (Swizzled by the route alone, the
+// 16-bit up/gate GEMM's reads took 3.8e7 bank-conflict cycles at the 2048-token
+// NVFP4 prefill, about 4 a read; with the bit flipped, none.)
+__device__ __forceinline__ int pf16_slot(int k, int r) { return (k ^ (r & 15)) ^ (((k >> 2) & 1) << 3); }
+__device__ __forceinline__ int pf16_chunk(int slot, int r) {
+  const int y = slot ^ (r & 15);
+  return y ^ (((y >> 2) & 1) << 3);
+}
+
 // Activation chunks 4w .. 4w+3 of k-tile kt (1 KB each: 4 routes x 256 bytes;
-// lane l -> route 4j + l/16, LDS slot l % 16 holding global chunk slot ^
-// route%16).  Lanes past the reduction length load column 0.
+// lane l -> route 4j + l/16, LDS slot l % 16 holding the chunk pf16_chunk
+// gives).  Lanes past the reduction length load column 0.
 __device__ __forceinline__ void pf16_issue_b(Pf16Stage &S, const Pf16Src &src, int kt, int w, int l) {
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    const int r = 4 * (4 * w + j) + (l >> 4), cg = (l & 15) ^ (r & 15), col = kt * 128 + 8 * cg;
+    const int r = 4 * (4 * w + j) + (l >> 4), cg = pf16_chunk(l & 15, r), col = kt * 128 + 8 * cg;
     dma16(src.brow[j] + (col < src.kcols ? col : 0), &S.B[4 * (4 * w + j)][0]);
   }
 }
@@ -1005,7 +1018,7 @@ __device__ __forceinline__ void pf16_read_b(v4i (&b)[4][4], const Pf16Stage &S, 
   const uint8_t *brow = &S.B[c][0];   // + 16 rows (4096 bytes) per route block
   uint32_t vb[4];
 #pragma unroll
-  for (int s = 0; s < 4; s++) vb[s] = lds_addr(brow + 16 * ((4 * g + s) ^ c));
+  for (int s = 0; s < 4; s++) vb[s] = lds_addr(brow + 16 * pf16_slot(4 * g + s, c));
   asm volatile(
       "ds_read_b128 %0, %16\n"
       "ds_read_b128 %1, %16 offset:4096\n"
@@ -1305,12 +1318,12 @@ struct Pw16Src {
 };
 
 // Activation chunks 8w .. 8w+7 of k-tile kt (1 KB each: 4 routes x 256 bytes;
-// lane l -> route 4 (8w + j) + l / 16, LDS slot l % 16 holding global chunk
-// slot ^ route % 16).
+// lane l -> route 4 (8w + j) + l / 16, LDS slot l % 16 holding the chunk
+// pf16_chunk gives).
 __device__ __forceinline__ void pw16_issue_b(Pw16Stage &S, const Pw16Src &src, int kt, int w, int l) {
 #pragma unroll
   for (int j = 0; j < 8; j++) {
-    const int r = 4 * (8 * w + j) + (l >> 4), cg = (l & 15) ^ (r & 15);
+    const int r = 4 * (8 * w + j) + (l >> 4), cg = pf16_chunk(l & 15, r);
     dma16(src.xb + (src.brow[j] + (uint32_t)(kt * 256 + 16 * cg)), &S.B[4 * (8 * w + j)][0]);
   }
 }
