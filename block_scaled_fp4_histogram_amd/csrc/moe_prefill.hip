@@ -1049,7 +1049,10 @@ __device__ __forceinline__ void pf16_read_b(v4i (&b)[4][4], const Pf16Stage &S, 
 // tile (NF3: its scaled magnitude table).  Columns past the reduction length
 // (FULL: none): the weights there are zero (their scales load as 0) and the
 // activations are zeroed.  SWAP: activations as the A operand.
-template <int WF, bool SWAP, bool FULL>
+// CVT: decode the scales with the one-instruction E4M3 convert (kernels with
+// the registers for it; in the 64-route ring kernels it raised the schedule to
+// about 300 VGPRs).
+template <int WF, bool SWAP, bool FULL, bool CVT = false>
 __device__ __forceinline__ void pf16_mma(const Pf16W &wt, const v4i (&b)[4][4], int kt, int kcols, int l,
                                          v4f (*acc)[4]) {
   const bool gin = FULL || kt * 128 + 32 * (l >> 4) < kcols;
@@ -1059,10 +1062,10 @@ __device__ __forceinline__ void pf16_mma(const Pf16W &wt, const v4i (&b)[4][4], 
   for (int q = 0; q < 2; q++) {
     const uint32_t sc = pf16_scale<WF>(wt.sc[q], l);
     if constexpr (WF == W_NVFP4) {
-      slo[q] = e4m3_f32_branched(sc & 0xFFu);
-      shi[q] = e4m3_f32_branched((sc >> 8) & 0xFFu);
+      slo[q] = CVT ? e4m3_f32(sc & 0xFFu) : e4m3_f32_branched(sc & 0xFFu);
+      shi[q] = CVT ? e4m3_f32((sc >> 8) & 0xFFu) : e4m3_f32_branched((sc >> 8) & 0xFFu);
     } else {
-      nf3_tables(e4m3_f32_branched(sc & 0xFFu), t01[q], t23[q]);
+      nf3_tables(CVT ? e4m3_f32(sc & 0xFFu) : e4m3_f32_branched(sc & 0xFFu), t01[q], t23[q]);
     }
   }
 #pragma unroll
@@ -1298,8 +1301,8 @@ __global__ __launch_bounds__(256) void k_pf_gemm1_a16_tiers(GemmArgs a) {
 // prefill: at most 95 routes an expert) each expert's weights are streamed
 // once instead of once per 64-route tile, and the MFMAs of 16-route blocks
 // holding only padding are skipped.  Activations: a 2-stage LDS ring of 32 KB
-// stages (128 routes x 256 bytes of a bf16 k-tile, 16-byte chunks XOR-swizzled
-// by route % 16 as on 64-route tiles); weights: a 2-deep register ring; one
+// stages (128 routes x 256 bytes of a bf16 k-tile, 16-byte chunks swizzled by
+// route as on 64-route tiles); weights: a 2-deep register ring; one
 // k-tile of lookahead (two blocks per CU).  K % 256 == 0 (every plan's).
 constexpr int kPw16Stages = 2;
 
@@ -1336,12 +1339,12 @@ __device__ __forceinline__ void pw16_deq(const Pf16W &wt, int l, v8bf (&aop)[2][
   for (int q = 0; q < 2; q++) {
     const uint32_t sc = pf16_scale<WF>(wt.sc[q], l);
     if constexpr (WF == W_NVFP4) {
-      const float slo = e4m3_f32_branched(sc & 0xFFu), shi = e4m3_f32_branched((sc >> 8) & 0xFFu);
+      const float slo = e4m3_f32(sc & 0xFFu), shi = e4m3_f32((sc >> 8) & 0xFFu);
 #pragma unroll
       for (int st = 0; st < 4; st++) aop[q][st] = nvfp4_step(wt.a[q][st], st < 2 ? slo : shi);
     } else {
       uint32_t t01, t23;
-      nf3_tables(e4m3_f32_branched(sc & 0xFFu), t01, t23);
+      nf3_tables(e4m3_f32(sc & 0xFFu), t01, t23);
 #pragma unroll
       for (int st = 0; st < 4; st++) aop[q][st] = nf3_step_rc(st < 2 ? wt.a[q][0] : wt.a[q][1], wt.a[q][2], st, t01, t23);
     }
@@ -1628,8 +1631,8 @@ __device__ __forceinline__ void pf16_gemm2_res_body(const GemmArgs &a, const PfW
       wait_vm<4 * (NKT - 1)>();   // slot kt has landed (the NKT - 1 later slots may be in flight)
       v4i b[4][4];
       pf16_read_b(b, L.st[kt], l);
-      if (kt < NKT - 1 || LASTFULL) pf16_mma<WF, true, true>(ring[kt], b, kt, N, l, acc);
-      else pf16_mma<WF, true, false>(ring[kt], b, kt, N, l, acc);
+      if (kt < NKT - 1 || LASTFULL) pf16_mma<WF, true, true, true>(ring[kt], b, kt, N, l, acc);
+      else pf16_mma<WF, true, false, true>(ring[kt], b, kt, N, l, acc);
       __builtin_amdgcn_sched_barrier(0);
       pf16_load_w_rt<WF>(ring[kt], src, rtn, kt, kt < NKT - 1 ? nd : ndl, kt < NKT - 1 ? ns : nsl);
       __builtin_amdgcn_sched_barrier(0);
