@@ -68,7 +68,7 @@ def test_capacity_ladder_and_scratch_sizes():
     sizes = [p.scratch_bytes(t) for t in (1, 8, 64, 512, 4096)]
     assert sizes == sorted(sizes)
     assert p.scratch_bytes(10000) == p.scratch_bytes(4096)
-    assert p.scratch_bytes(256, True) > p.scratch_bytes(256, False)     # route buffer vs accumulator (general)
+    assert p.scratch_bytes(128, True) > p.scratch_bytes(128, False)     # route buffer vs accumulator (general)
     # the prefill sequence combines through the route buffer in both modes (the ladder's choice)
     assert p.scratch_bytes(4096, True) == p.scratch_bytes(4096, False)
     assert p.scratch_bytes(8) % 256 == 0
@@ -216,13 +216,13 @@ def test_combine_pins_follow_the_ladder_scratch_and_tuning_file(tmp_path):
     combine (route buffer 2 R K bytes, accumulator 4 T K); pins persist (v2 lines) and
     sequence-only v1 lines still load."""
     p = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
-    assert p.combine(4096) == M.COMBINE_ROUTE_BUFFER and p.combine(200) == M.COMBINE_ATOMIC
+    assert p.combine(4096) == M.COMBINE_ROUTE_BUFFER and p.combine(100) == M.COMBINE_ATOMIC
     assert p.scratch_bytes(4096, False) == p.scratch_bytes(4096, True)
-    atomic_200 = p.scratch_bytes(200, False)
-    p.set_combine(200, M.COMBINE_ROUTE_BUFFER)
-    assert p.combine(200) == M.COMBINE_ROUTE_BUFFER
-    rb_200 = p.scratch_bytes(200, False)
-    assert rb_200 - atomic_200 >= 2 * 256 * 6 * 7168 - 4 * 256 * 7168 - 4096
+    atomic_100 = p.scratch_bytes(100, False)
+    p.set_combine(100, M.COMBINE_ROUTE_BUFFER)
+    assert p.combine(100) == M.COMBINE_ROUTE_BUFFER
+    rb_100 = p.scratch_bytes(100, False)
+    assert rb_100 - atomic_100 >= 2 * 128 * 6 * 7168 - 4 * 128 * 7168 - 4096
     p.set_combine(4096, M.COMBINE_ATOMIC)
     assert p.combine(4096) == M.COMBINE_ATOMIC and p.scratch_bytes(4096, False) < p.scratch_bytes(4096, True)
     with pytest.raises(M.MoeError) as e:
@@ -234,7 +234,7 @@ def test_combine_pins_follow_the_ladder_scratch_and_tuning_file(tmp_path):
     assert "moe v2" in text and "comb=2" in text and "comb=1" in text
     q = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
     assert q.load_tuning(path) == 2
-    assert q.combine(200) == M.COMBINE_ROUTE_BUFFER and q.combine(4096) == M.COMBINE_ATOMIC
+    assert q.combine(100) == M.COMBINE_ROUTE_BUFFER and q.combine(4096) == M.COMBINE_ATOMIC
     v1 = str(tmp_path / "v1.txt")
     key = "E=384 K=7168 N=576 topk=6 afmt=1 max_tokens=4096"
     open(v1, "w").write(f"moe v1 {key} cap=8 seq=2\n")

@@ -406,7 +406,7 @@ def _batch(name, T):
     return I.make_problem(name, T=T)
 
 
-@pytest.mark.parametrize("name,batches", [("decode", ((40, 12), (200, 12))), ("nvfp4_decode", ((40, 10),)),
+@pytest.mark.parametrize("name,batches", [("decode", ((40, 12), (120, 12))), ("nvfp4_decode", ((40, 10),)),
                                           ("hybrid", ((40, 10),))])
 def test_general_sequence_at_full_geometry(name, batches):
     L = layer(name, max_tokens=256)
