@@ -420,6 +420,24 @@ def test_general_sequence_at_full_geometry(name, batches):
             assert_rows_match(out, acc, rows=rows, label=f"{name} T={T} general det={det}", prob=q)
 
 
+# The rungs the ladder sends to the prefill kernels below the benchmark's batch, at the
+# production geometries: 64-route up/gate tiles while experts average under 32 routes
+# (W4A8 at 512 tokens: 8 an expert; NVFP4 at 512: 16), 128-route ones from there (NVFP4
+# and the hybrid at 1024: 32).
+@pytest.mark.parametrize("name,T,seq", [("prefill", 512, M.SEQ_PREFILL_NARROW),
+                                        ("nvfp4_prefill", 512, M.SEQ_PREFILL_NARROW),
+                                        ("nvfp4_prefill", 1024, M.SEQ_PREFILL), ("hybrid", 1024, M.SEQ_PREFILL)])
+def test_ladder_prefill_rungs_at_full_geometry(name, T, seq):
+    L = layer(name, max_tokens=T)
+    q = _batch(name, T)
+    assert L.plan.sequence(T) == seq
+    rows = _sample_rows(q, 10, seed=T)
+    acc, _ = O.moe_problem(q, rows=rows)
+    for det in (False, True):
+        out = L.run(x=dev(q.x, torch.bfloat16), ids=dev(q.ids), wts=dev(q.wts), deterministic=det)
+        assert_rows_match(out, acc, rows=rows, label=f"{name} T={T} seq={seq} det={det}", prob=q)
+
+
 def test_hybrid_decode_at_full_geometry():
     """Both tiers (64 NVFP4 + 192 NF3 experts, K = 6144, N = 512, top-8) on the decode
     sequence, every row, both combine modes."""
