@@ -287,15 +287,19 @@ bool seq_eligible(const moe_plan_s *p, int cap, int seq) {
 // The ladder's own choice, from the per-rung race on uniform routing (one
 // MI355X, both geometries of the pages, atomic and deterministic combine): the
 // 64-route-tile kernels overtake the 16-route ones from 256 tokens for W4A8
-// (deterministic: 486 vs 511 us) and from 512 for W4A16 / W3A16; the up/gate
-// GEMM's 128-route tiles overtake its 64-route ones once an expert averages 32
-// routes (below that they are mostly padding: at 1024 tokens, 16 routes an
-// expert at E = 384, top-6, the 64-route tiles lead by 2 %, at 2048 the
-// 128-route ones by 1.5 %, at the Zipf-skewed 4096-token batch by 3 %).
+// (deterministic: 485 vs 512 us) and from 512 for W4A16 / W3A16 (421 vs 569).
+// The W4A8 up/gate GEMM's 128-route tiles overtake its 64-route ones once an
+// expert averages 32 routes (below that they are mostly padding: at 1024
+// tokens, 16 routes an expert at E = 384, top-6, the 64-route tiles lead by
+// 2 %, at 2048 the 128-route ones by 1.5 %, at the Zipf-skewed 4096-token
+// batch by 4 %); the 16-bit one, whose 128-route tiles also halve its
+// dequantisation per MFMA, leads from 512 tokens (16 routes an expert).
 int ladder_seq(const moe_plan_s *p, int T) {
   if (use_decode(p, T)) return MOE_SEQ_DECODE;
-  const int min_t = p->afmt == MOE_A_MXFP8 ? moe::kPrefillMinTA8 : moe::kPrefillMinT;
-  if (T < min_t || !seq_eligible(p, T, MOE_SEQ_PREFILL)) return MOE_SEQ_GENERAL;
+  const bool a8 = p->afmt == MOE_A_MXFP8;
+  if (T < (a8 ? moe::kPrefillMinTA8 : moe::kPrefillMinT) || !seq_eligible(p, T, MOE_SEQ_PREFILL))
+    return MOE_SEQ_GENERAL;
+  if (!a8) return MOE_SEQ_PREFILL;
   return (long)T * p->topk >= (long)moe::kWideMinRoutes * p->E ? MOE_SEQ_PREFILL : MOE_SEQ_PREFILL_NARROW;
 }
 

@@ -297,14 +297,14 @@ def test_narrow_prefill_sequence_is_a_w4a8_variant(tmp_path):
 def test_ladder_default_sequences():
     """The ladder's own choice per batch size (no pins): decode up to 64 routes, the
     16-route kernels below 256 tokens (W4A8) or 512 (16-bit activations), then the prefill
-    kernels with 64-route up/gate tiles until experts average 32 routes, 128-route ones
-    from there."""
+    kernels: for W4A8 with 64-route up/gate tiles until experts average 32 routes and
+    128-route ones from there, for 16-bit activations with 128-route ones throughout."""
     a8 = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=16384)
     want = {8: M.SEQ_DECODE, 12: M.SEQ_GENERAL, 200: M.SEQ_GENERAL, 256: M.SEQ_PREFILL_NARROW,
             1024: M.SEQ_PREFILL_NARROW, 2048: M.SEQ_PREFILL, 4096: M.SEQ_PREFILL, 16384: M.SEQ_PREFILL}
     assert {t: a8.sequence(t) for t in want} == want
     a16 = M.Plan(256, 6144, 512, 8, None, M.A_BF16, max_tokens=4096)
-    want = {8: M.SEQ_DECODE, 256: M.SEQ_GENERAL, 511: M.SEQ_GENERAL, 512: M.SEQ_PREFILL_NARROW,
+    want = {8: M.SEQ_DECODE, 256: M.SEQ_GENERAL, 511: M.SEQ_GENERAL, 512: M.SEQ_PREFILL,
             1024: M.SEQ_PREFILL, 2048: M.SEQ_PREFILL}
     assert {t: a16.sequence(t) for t in want} == want
     odd = M.Plan(64, 512, 96, 4, None, M.A_BF16, max_tokens=4096)   # N % 64 != 0: no prefill kernels
