@@ -243,6 +243,7 @@ int run_decode(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const ui
   da.hs = scratch + L.hs;
   da.hb = (uint16_t *)(scratch + L.hb);
   da.out = out;
+  static_assert(sizeof(moe::DecGroups) <= 4 * moe::kMaxExperts, "the group table fits the planner's count table");
   da.groups = (moe::DecGroups *)(scratch + L.cnt);   // the planner's count table is free on this path
   da.dpart = L.dpart ? (float *)(scratch + L.dpart) : nullptr;
   da.dcnt = L.dcnt ? (int *)(scratch + L.dcnt) : nullptr;

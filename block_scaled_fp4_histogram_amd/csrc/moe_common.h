@@ -113,12 +113,14 @@ struct DecTier {
 };
 
 // Expert groups of a decode batch (routes sharing an expert, in order of first
-// occurrence) with the first item of each in the W4A8 down GEMM's item list;
+// occurrence) with their pass counts (the most slots one token has on the
+// group's expert) and the first item of each in the down GEMM's item list;
 // written by the up/gate kernel, read by the down kernel.
 struct DecGroups {
   int ng, nitems;
   int gu[kDecodeMaxRoutes];
   int istart[kDecodeMaxRoutes];
+  int np[kDecodeMaxRoutes];
   unsigned long long gm[kDecodeMaxRoutes];
 };
 

@@ -88,6 +88,15 @@ __device__ __forceinline__ int nth_bit(unsigned long long m, int n) {
   return m ? __ffsll(m) - 1 : -1;
 }
 
+// Route of token t in pass p of a group with route mask md: the token's p-th
+// slot on the group's expert, or -1.
+__device__ __forceinline__ int dec_token_route(unsigned long long md, int p, int t, int T, int topk) {
+  if (t >= T) return -1;
+  const unsigned long long tm = topk >= 64 ? md : (md >> (t * topk)) & ((1ull << topk) - 1ull);
+  const int j = nth_bit(tm, p);
+  return j < 0 ? -1 : t * topk + j;
+}
+
 struct DecExpert {
   const uint8_t *w13, *s13, *w2, *s2;
   float g13, g2;
@@ -371,9 +380,16 @@ __device__ __forceinline__ void dec_write_groups(const DecArgs &a, int u) {
   // a group's index is the number of groups opened by lower lanes; its item
   // offset is the inclusive lane scan of the item counts minus its own.  One
   // store per table entry, all lanes at once (a store per group in a loop
-  // queues behind the weight loads of the other blocks on the CU).
+  // queues behind the weight loads of the other blocks on the CU).  A group
+  // runs one pass per slot a token has on its expert (the down GEMM's MFMA
+  // columns are the batch's tokens), mostly one.
   const int n = __popcll(F & ((1ull << l) - 1ull));
-  const int mine = first ? ((__popcll(same) + 15) / 16) * nkt2 : 0;
+  int np = 0;
+  if (first) {
+    const unsigned long long tmask = a.topk >= 64 ? ~0ull : (1ull << a.topk) - 1ull;
+    for (int t = 0; t < a.T; t++) np = max(np, __popcll((same >> (t * a.topk)) & tmask));
+  }
+  const int mine = np * nkt2;
   int incl = mine;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -383,6 +399,7 @@ __device__ __forceinline__ void dec_write_groups(const DecArgs &a, int u) {
   if (first) {
     a.groups->gu[n] = u;
     a.groups->gm[n] = same;
+    a.groups->np[n] = np;
     a.groups->istart[n] = incl - mine;
   }
   if (l == 63) {
@@ -424,27 +441,11 @@ __global__ __launch_bounds__(256, 4) void k_dec_gemm1_a16(DecArgs a) {
 // ---------------------------------------------------------------- GEMM2
 //
 // Lane (token t = l % 16, group g) accumulates output columns 16*rt + 4g .. +3
-// of token t.  After the down GEMM of one expert for up to 16 of its routes
-// (MFMA columns), the results move to the lanes of their tokens through a
-// per-wave 16 x 16 fp32 LDS tile: lane (route column c, group g) stores its
-// router-weighted outputs, then lane (token c, group g) adds the rows of its
-// token's routes, slots in order.
-__device__ __forceinline__ void dec_fold_lds(const DecArgs &a, unsigned long long md, int p0, int c, int g,
-                                             const v4f &acc, float wr, float *yb, float *tok) {
-  *(v4f *)(yb + c * 16 + 4 * g) = acc * wr;
-  if (c >= a.T) return;
-  for (int j = 0; j < a.topk; j++) {
-    const int rr = c * a.topk + j;
-    if (rr < 64 && ((md >> rr) & 1ull)) {
-      const int col = __popcll(md & ((1ull << rr) - 1ull)) - p0;
-      if (col >= 0 && col < 16) {
-        const v4f v = *(const v4f *)(yb + col * 16 + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; i++) tok[i] += v[i];
-      }
-    }
-  }
-}
+// of token t.  The MFMA columns are the batch's tokens (at most 16): in pass p
+// of an expert group, column t multiplies the intermediate row of token t's
+// p-th slot on that expert (zero where it has none), so at the end of a run of
+// one (group, pass) the lane adds its router-weighted accumulator to its
+// token sums directly; the group order fixes the order of each token's terms.
 
 // W4A8 down GEMM, grid (K/16 output row tiles).  The block's work is the list
 // of items (expert group, 16-route pass, k-tile of N) in group-major order; its
@@ -471,12 +472,19 @@ struct G2Iter {
   uint32_t w0, s0;   // this block's output row tile within the expert's data / scales
 };
 
-// g2v: the groups' global scales, one per lane (loaded up front: a load here
-// would be waited for behind the weight ring).
-__device__ __forceinline__ void g2_enter_group(G2Iter &it, const DecArgs &a, int gu, unsigned long long gm,
-                                               float g2v = 1.0f) {
-  it.md = readlane_u64(gm, it.grp);
-  it.npass = (__popcll(it.md) + 15) / 16;
+// The group table, one group per lane (loaded up front: a load here would be
+// waited for behind the weight ring); g2v: the groups' global scales.
+struct G2Tab {
+  int gu, np;
+  unsigned long long gm;
+  float g2v;
+};
+
+__device__ __forceinline__ void g2_enter_group(G2Iter &it, const DecArgs &a, const G2Tab &tb) {
+  const int gu = tb.gu;
+  const float g2v = tb.g2v;
+  it.md = readlane_u64(tb.gm, it.grp);
+  it.npass = __builtin_amdgcn_readlane(tb.np, it.grp);
   const int u = __builtin_amdgcn_readlane(gu, it.grp);
   const bool t1 = a.n_tiers > 1 && u >= a.tier[0].E;
   const DecTier &T = t1 ? a.tier[1] : a.tier[0];
@@ -491,32 +499,30 @@ __device__ __forceinline__ void g2_enter_group(G2Iter &it, const DecArgs &a, int
   it.s0 = __builtin_amdgcn_readfirstlane((uint32_t)it.rt * 16u * (uint32_t)groups * SU);
 }
 
-__device__ __forceinline__ void g2_start(G2Iter &it, const DecArgs &a, int item, int istart, int ng, int nkt, int gu,
-                                         unsigned long long gm, float g2v = 1.0f) {
+__device__ __forceinline__ void g2_start(G2Iter &it, const DecArgs &a, int item, int istart, int ng, int nkt,
+                                         const G2Tab &tb) {
   const int l = threadIdx.x & 63;
   it.item = item;
   it.grp = max(0, __popcll(__ballot(l < ng && istart <= item)) - 1);
   const int rel = item - __builtin_amdgcn_readlane(istart, it.grp);
   it.pass = rel / nkt;
   it.kt = rel - it.pass * nkt;
-  g2_enter_group(it, a, gu, gm, g2v);
+  g2_enter_group(it, a, tb);
 }
 
-__device__ __forceinline__ void g2_next(G2Iter &it, const DecArgs &a, int ng, int nkt, int gu, unsigned long long gm,
-                                        float g2v = 1.0f) {
+__device__ __forceinline__ void g2_next(G2Iter &it, const DecArgs &a, int ng, int nkt, const G2Tab &tb) {
   it.item++;
   if (++it.kt < nkt) return;
   it.kt = 0;
   if (++it.pass < it.npass) return;
   it.pass = 0;
-  if (++it.grp < ng) g2_enter_group(it, a, gu, gm, g2v);
+  if (++it.grp < ng) g2_enter_group(it, a, tb);
 }
 
 __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) {
   extern __shared__ __align__(16) uint8_t dsm2[];
   __shared__ float tred[kDecG2WavesA8][4][64];
   __shared__ float wr_s[kDecodeMaxRoutes];
-  __shared__ __align__(16) float yb[kDecG2WavesA8][256];
   // wave-uniform values are pinned to scalar registers: derived from them, the
   // item bounds and weight descriptors stay scalar through the ring's branches
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
@@ -524,14 +530,18 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   // expert groups (one per lane) and item offsets, from the up/gate kernel
   const DecGroups *G = a.groups;
   const int ng = __builtin_amdgcn_readfirstlane(G->ng), NI = __builtin_amdgcn_readfirstlane(G->nitems);
-  int gu = G->gu[l], istart = G->istart[l];
+  int gu = G->gu[l], istart = G->istart[l], gnp = G->np[l];
   uint32_t gm_lo = (uint32_t)G->gm[l], gm_hi = (uint32_t)(G->gm[l] >> 32);
   float wv = tid < a.R ? a.topk_w[tid] : 0.f;
   // the table and router weights are complete here; re-defined by an empty
   // asm, their registers carry no pending load, so nothing after waits on them
   wait_vm<0>();
-  asm volatile("" : "+v"(gu), "+v"(istart), "+v"(gm_lo), "+v"(gm_hi), "+v"(wv));
-  const unsigned long long gm = ((unsigned long long)gm_hi << 32) | gm_lo;
+  asm volatile("" : "+v"(gu), "+v"(istart), "+v"(gnp), "+v"(gm_lo), "+v"(gm_hi), "+v"(wv));
+  G2Tab tb;
+  tb.gu = gu;
+  tb.np = gnp;
+  tb.gm = ((unsigned long long)gm_hi << 32) | gm_lo;
+  tb.g2v = 1.0f;
   if (tid < a.R) wr_s[tid] = wv;
   const int per = (NI + kDecG2WavesA8 - 1) / kDecG2WavesA8;
   const int i0 = min(NI, w * per), i1 = min(NI, i0 + per);
@@ -541,13 +551,13 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   int sa[kG2Ring];
   G2Iter is;
   is.rt = rt;
-  if (i0 < i1) g2_start(is, a, i0, istart, ng, nkt, gu, gm);
+  if (i0 < i1) g2_start(is, a, i0, istart, ng, nkt, tb);
   else is.item = i1;
   auto issue = [&](int s) {
     const bool ok = is.item < i1 && is.kt * 128 + 32 * g < N;
     A[s] = buf_load16(is.wb, ok ? (uint32_t)is.kt * 1024u + (uint32_t)l * 16u : 0x80000000u, is.w0);
     sa[s] = buf_load1(is.sb, ok ? (uint32_t)is.kt * 64u + (uint32_t)l : 0x80000000u, is.s0);
-    if (is.item < i1) g2_next(is, a, ng, nkt, gu, gm);
+    if (is.item < i1) g2_next(is, a, ng, nkt, tb);
   };
   if (i0 >= i1) {   // no items: the ring's loads still need valid descriptors
     is.wb = make_buf(a.hq, 0);
@@ -579,17 +589,15 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   float tok[4] = {0.f, 0.f, 0.f, 0.f};
   G2Iter ic;
   ic.rt = rt;
-  if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkt, gu, gm);
+  if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkt, tb);
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
   int r = -1;
   for (int base = i0; base < i1; base += kG2Ring) {
 #pragma unroll
     for (int s = 0; s < kG2Ring; s++) {
       if (base + s < i1) {
-        if (s == 0 || ic.kt == 0 || base + s == i0) {   // route column of this lane in the current run
-          const int col = ic.pass * 16 + c;
-          r = col < __popcll(ic.md) ? nth_bit(ic.md, col) : -1;
-        }
+        if (s == 0 || ic.kt == 0 || base + s == i0)   // route of this lane's token in the current run
+          r = dec_token_route(ic.md, ic.pass, c, a.T, a.topk);
         const int kb = ic.kt * 128;
         v4i B0 = v4i{0, 0, 0, 0}, B1 = v4i{0, 0, 0, 0};
         int sbv = 0;
@@ -602,10 +610,12 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
         const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
         acc = mfma_fp4_fp8(A[s], bop, acc, sa[s], sbv);
         if (ic.kt == nkt - 1 || base + s + 1 == i1) {
-          dec_fold_lds(a, ic.md, ic.pass * 16, c, g, acc, r >= 0 ? wr_s[r] : 0.f, &yb[w][0], tok);
+          const float wgt = r >= 0 ? wr_s[r] : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; i++) tok[i] += acc[i] * wgt;
           acc = v4f{0.f, 0.f, 0.f, 0.f};
         }
-        g2_next(ic, a, ng, nkt, gu, gm);
+        g2_next(ic, a, ng, nkt, tb);
       }
       issue(s);   // the item kG2Ring ahead (out of range past the slice)
     }
@@ -656,7 +666,7 @@ template <int WF>
 __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a) {
   extern __shared__ __align__(16) uint8_t dsm2[];
   __shared__ float wr_s[kDecodeMaxRoutes];
-  __shared__ __align__(16) float yb[kDecG2WavesA8][256];   // per-wave fold tile, then its token sums
+  __shared__ __align__(16) float yb[kDecG2WavesA8][256];   // per-wave token sums
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
   const int K = a.K, N = a.N, nkt = (N + 127) / 128;
   const int halves = dec2_a16_halves(N), rt = blockIdx.x / halves, h = blockIdx.x - rt * halves;
@@ -668,7 +678,7 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   // half's list keeps nkh of each pass's nkt k-tiles
   const int ng = __builtin_amdgcn_readfirstlane(G->ng),
             NI = __builtin_amdgcn_readfirstlane(G->nitems) / nkt * nkh;
-  int gu = G->gu[l], istart = G->istart[l] / nkt * nkh;
+  int gu = G->gu[l], istart = G->istart[l] / nkt * nkh, gnp = G->np[l];
   uint32_t gm_lo = (uint32_t)G->gm[l], gm_hi = (uint32_t)(G->gm[l] >> 32);
   float wv = tid < a.R ? (a.w_on_input ? 1.0f : a.topk_w[tid]) : 0.f;   // weight on the input: 1 here
   float g2v = 1.0f;   // global scale of group l's expert
@@ -680,8 +690,12 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   // the table, router weights and scales are complete here; re-defined by an
   // empty asm, their registers carry no pending load
   wait_vm<0>();
-  asm volatile("" : "+v"(gu), "+v"(istart), "+v"(gm_lo), "+v"(gm_hi), "+v"(wv), "+v"(g2v));
-  const unsigned long long gm = ((unsigned long long)gm_hi << 32) | gm_lo;
+  asm volatile("" : "+v"(gu), "+v"(istart), "+v"(gnp), "+v"(gm_lo), "+v"(gm_hi), "+v"(wv), "+v"(g2v));
+  G2Tab tb;
+  tb.gu = gu;
+  tb.np = gnp;
+  tb.gm = ((unsigned long long)gm_hi << 32) | gm_lo;
+  tb.g2v = g2v;
   if (tid < a.R) wr_s[tid] = wv;
   const int per = (NI + kDecG2WavesA8 - 1) / kDecG2WavesA8;
   const int i0 = min(NI, w * per), i1 = min(NI, i0 + per);
@@ -690,7 +704,7 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   uint32_t A4[kG2RingA16], sa[kG2RingA16];
   G2Iter is;   // its kt runs over the half's k-tiles: k-tile kt0 + kt of the reduction
   is.rt = rt;
-  if (i0 < i1) g2_start(is, a, i0, istart, ng, nkh, gu, gm, g2v);
+  if (i0 < i1) g2_start(is, a, i0, istart, ng, nkh, tb);
   else is.item = i1;
   if (i0 >= i1) {   // no items: the ring's loads still need valid descriptors
     is.wb = make_buf(a.hb, 0);
@@ -718,7 +732,7 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
     }
     sa[s] = buf_load2(is.sb, ok ? (nv ? (uint32_t)kt * 128u + (uint32_t)l * 2u : (uint32_t)kt * 64u + (uint32_t)(l & ~1))
                                 : 0x80000000u, is.s0);
-    if (is.item < i1) g2_next(is, a, ng, nkh, gu, gm, g2v);
+    if (is.item < i1) g2_next(is, a, ng, nkh, tb);
   };
   // this half's columns of every route's bf16 intermediate row -> LDS (row
   // stride nh + 8 elements), 1 KB direct loads issued ahead of the ring
@@ -741,17 +755,15 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   float tok[4] = {0.f, 0.f, 0.f, 0.f};
   G2Iter ic;
   ic.rt = rt;
-  if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkh, gu, gm, g2v);
+  if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkh, tb);
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
   int r = -1;
   for (int base = i0; base < i1; base += kG2RingA16) {
 #pragma unroll
     for (int s = 0; s < kG2RingA16; s++) {
       if (base + s < i1) {
-        if (s == 0 || ic.kt == 0 || base + s == i0) {   // route column of this lane in the current run
-          const int col = ic.pass * 16 + c;
-          r = col < __popcll(ic.md) ? nth_bit(ic.md, col) : -1;
-        }
+        if (s == 0 || ic.kt == 0 || base + s == i0)   // route of this lane's token in the current run
+          r = dec_token_route(ic.md, ic.pass, c, a.T, a.topk);
         const int kb = (kt0 + ic.kt) * 128 + 32 * g;
         v4i B[4];
 #pragma unroll
@@ -784,15 +796,17 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
             acc = mfma_bf16(nf3_step_rc(st < 2 ? d[0] : d[1], d[2], st, t01, t23), __builtin_bit_cast(v8bf, B[st]), acc);
         }
         if (ic.kt == nkh - 1 || base + s + 1 == i1) {
-          dec_fold_lds(a, ic.md, ic.pass * 16, c, g, acc, r >= 0 ? wr_s[r] * ic.g2 : 0.f, &yb[w][0], tok);
+          const float wgt = r >= 0 ? wr_s[r] * ic.g2 : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; i++) tok[i] += acc[i] * wgt;
           acc = v4f{0.f, 0.f, 0.f, 0.f};
         }
-        g2_next(ic, a, ng, nkh, gu, gm, g2v);
+        g2_next(ic, a, ng, nkh, tb);
       }
       issue(s);   // the item kG2RingA16 ahead (out of range past the slice)
     }
   }
-  float *tw = &yb[w][0];   // this wave's token sums [4][64], in its own fold tile
+  float *tw = &yb[w][0];   // this wave's token sums [4][64]
 #pragma unroll
   for (int i = 0; i < 4; i++) tw[i * 64 + l] = tok[i];
   __syncthreads();
