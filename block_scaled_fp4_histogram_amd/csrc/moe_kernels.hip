@@ -127,14 +127,17 @@ __device__ void finish_plan(const RouteArgs &a, int U, const int *cnt, int *off,
   }
 }
 
-// Work fused into the route launch: MXFP8 quantisation of x (one thread per
-// 32-element block) and clearing of the fp32 accumulator.
-__device__ void route_side_work(const RouteArgs &a, int sb) {
+// Work fused into the route launches: MXFP8 quantisation of x (one thread per
+// 32-element block) and clearing of the fp32 accumulator, part `part` of
+// `nparts` equal slices (a launch's side blocks sb = 0 .. side_blocks - 1 take
+// one part; with several chunks the histogram launch and the scan launch each
+// take one, beside their latency-bound route work).
+__device__ void route_side_work(const RouteArgs &a, int sb, int part, int nparts) {
   const long stride = (long)a.side_blocks * blockDim.x;
   const long i0 = (long)sb * blockDim.x + threadIdx.x;
   if (a.xq) {
-    const long nblk = (long)a.T * (a.K / 32);
-    for (long i = i0; i < nblk; i += stride) {
+    const long nall = (long)a.T * (a.K / 32), nblk = nall * (part + 1) / nparts;
+    for (long i = nall * part / nparts + i0; i < nblk; i += stride) {
       const v4i *src = (const v4i *)(a.x + i * 32);
       v4i x4[4];
 #pragma unroll
@@ -148,8 +151,8 @@ __device__ void route_side_work(const RouteArgs &a, int sb) {
     }
   }
   if (a.zero_buf) {
-    const long n4 = a.zero_n / 4;
-    for (long i = i0; i < n4; i += stride) ((v4f *)a.zero_buf)[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    const long nall = a.zero_n / 4, n4 = nall * (part + 1) / nparts;
+    for (long i = nall * part / nparts + i0; i < n4; i += stride) ((v4f *)a.zero_buf)[i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -165,7 +168,7 @@ static_assert(kRouteRounds == 1, "one 64-route round per wave");
 template <bool SINGLE>
 __global__ __launch_bounds__(64 * kRouteWaves) void k_route(RouteArgs a) {
   if ((int)blockIdx.x >= a.G) {
-    route_side_work(a, blockIdx.x - a.G);
+    route_side_work(a, blockIdx.x - a.G, 0, SINGLE ? 1 : 2);
     return;
   }
   __shared__ uint16_t whist[kRouteWaves][kMaxExperts];   // per wave: count, then exclusive prefix
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void k_route(RouteArgs a) {
 // instead of after (4096 tokens at K = 7168: planner 35 -> 25 us).
 __global__ __launch_bounds__(1024) void k_route_scan(RouteArgs a) {
   if (blockIdx.x > 0) {
-    route_side_work(a, blockIdx.x - 1);
+    route_side_work(a, blockIdx.x - 1, 1, 2);
     return;
   }
   __shared__ int cnt[kMaxExperts];
@@ -305,7 +308,7 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
   if (a.G == 1) {
     hipLaunchKernelGGL(k_route<true>, dim3(1 + a.side_blocks), dim3(64 * kRouteWaves), 0, s, a);
   } else {
-    hipLaunchKernelGGL(k_route<false>, dim3(a.G), dim3(64 * kRouteWaves), 0, s, a);
+    hipLaunchKernelGGL(k_route<false>, dim3(a.G + a.side_blocks), dim3(64 * kRouteWaves), 0, s, a);
     hipLaunchKernelGGL(k_route_scan, dim3(1 + a.side_blocks), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(k_route_scatter, dim3((a.R + 255) / 256), dim3(256), 0, s, a);
   }
