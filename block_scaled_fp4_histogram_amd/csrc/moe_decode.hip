@@ -667,7 +667,9 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   extern __shared__ __align__(16) uint8_t dsm2[];
   __shared__ float wr_s[kDecodeMaxRoutes];
   __shared__ __align__(16) float yb[kDecG2WavesA8][256];   // per-wave token sums
+  __shared__ __align__(16) uint8_t zb[64];   // zero operand bytes for absent routes and columns past N
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
+  if (tid < 16) ((uint32_t *)zb)[tid] = 0u;
   const int K = a.K, N = a.N, nkt = (N + 127) / 128;
   const int halves = dec2_a16_halves(N), rt = blockIdx.x / halves, h = blockIdx.x - rt * halves;
   const int nk0 = halves == 2 ? (nkt + 1) / 2 : nkt;   // k-tiles of half 0
@@ -718,20 +720,21 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   // the 4th dword (NVFP4 only; NF3 loads out of range), and an aligned 16-bit
   // scale load (NVFP4: the lane's two E4M3 bytes; NF3: the pair holding its
   // byte).  One format: one data load of its width.
+  // the k-tile's offset is wave-uniform, so it goes into the scalar offset
   auto issue = [&](int s) {
     const int kt = kt0 + is.kt;
     const bool ok = is.item < i1 && kt * 128 + 32 * g < N;
     const bool nv = WF == W_NVFP4 || (WF == 0 && is.fmt == W_NVFP4);
-    const uint32_t U = nv ? 16u : 12u;
-    const uint32_t dv = ok ? (uint32_t)kt * 64u * U + (uint32_t)l * U : 0x80000000u;
+    const uint32_t U = nv ? 16u : 12u, SU = nv ? 2u : 1u;
+    const uint32_t dv = ok ? (uint32_t)l * U : 0x80000000u, wo = is.w0 + (uint32_t)kt * 64u * U;
     if constexpr (WF == W_NVFP4) {
-      A16[s] = buf_load16(is.wb, dv, is.w0);
+      A16[s] = buf_load16(is.wb, dv, wo);
     } else {
-      A3[s] = buf_load12(is.wb, dv, is.w0);
-      if constexpr (WF == 0) A4[s] = buf_load4(is.wb, nv && ok ? dv + 12u : 0x80000000u, is.w0);
+      A3[s] = buf_load12(is.wb, dv, wo);
+      if constexpr (WF == 0) A4[s] = buf_load4(is.wb, nv && ok ? dv + 12u : 0x80000000u, wo);
     }
-    sa[s] = buf_load2(is.sb, ok ? (nv ? (uint32_t)kt * 128u + (uint32_t)l * 2u : (uint32_t)kt * 64u + (uint32_t)(l & ~1))
-                                : 0x80000000u, is.s0);
+    sa[s] = buf_load2(is.sb, ok ? (nv ? (uint32_t)l * 2u : (uint32_t)(l & ~1)) : 0x80000000u,
+                      is.s0 + (uint32_t)kt * 64u * SU);
     if (is.item < i1) g2_next(is, a, ng, nkh, tb);
   };
   // this half's columns of every route's bf16 intermediate row -> LDS (row
@@ -764,15 +767,12 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
       if (base + s < i1) {
         if (s == 0 || ic.kt == 0 || base + s == i0)   // route of this lane's token in the current run
           r = dec_token_route(ic.md, ic.pass, c, a.T, a.topk);
+        // absent routes and columns past N read zero bytes (zb) instead of branching
         const int kb = (kt0 + ic.kt) * 128 + 32 * g;
+        const v4i *hp = (const v4i *)(r >= 0 && kb < N ? (const uint8_t *)(hb_s + r * (nh + 8) + (kb - c0)) : zb);
         v4i B[4];
 #pragma unroll
-        for (int st = 0; st < 4; st++) B[st] = v4i{0, 0, 0, 0};
-        if (r >= 0 && kb < N) {
-          const v4i *hp = (const v4i *)(hb_s + r * (nh + 8) + (kb - c0));
-#pragma unroll
-          for (int st = 0; st < 4; st++) B[st] = hp[st];
-        }
+        for (int st = 0; st < 4; st++) B[st] = hp[st];
         uint32_t d[4];
         if constexpr (WF == W_NVFP4) {
 #pragma unroll
