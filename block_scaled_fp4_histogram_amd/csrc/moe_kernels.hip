@@ -634,7 +634,10 @@ __global__ __launch_bounds__(256) void k_cast(const float *acc, long n8, uint16_
 // out[t] = bf16(sum over valid slots j, in slot order, of rb[t*topk + j]); 8 columns per thread.
 // All TK slot rows and their validity are requested before the first add (rows
 // of invalid slots are in the buffer's range, just never written, and are
-// masked), so each thread has one memory round trip instead of TK.
+// masked), so each thread has one memory round trip instead of TK.  The route
+// buffer is read once, by non-temporal loads that keep its dead lines from
+// displacing other data in the caches (4096-token W4A8 prefill: this kernel
+// 70.4 -> 61.3 us, and the next layer's route planner 29.5 -> 27.5 us).
 template <int TK>
 __global__ __launch_bounds__(256) void k_topk_sum(const uint16_t *rb, const int32_t *inv, int T, int K,
                                                   uint16_t *out) {
@@ -648,7 +651,8 @@ __global__ __launch_bounds__(256) void k_topk_sum(const uint16_t *rb, const int3
   for (int j = 0; j < TK; j++) {
     const long r = t * TK + j;
     ok[j] = inv[r];
-    v[j] = *(const uint4 *)(rb + r * K + c8 * 8);
+    const v4i q = __builtin_nontemporal_load((const v4i *)(rb + r * K + c8 * 8));
+    v[j] = uint4{(uint32_t)q[0], (uint32_t)q[1], (uint32_t)q[2], (uint32_t)q[3]};
   }
   float s[8];
 #pragma unroll
