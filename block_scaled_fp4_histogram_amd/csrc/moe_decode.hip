@@ -162,7 +162,7 @@ struct RowTiles {
 __device__ __forceinline__ void a8w_load(A8W &st, const RowTiles &rt, uint32_t l, int kt, bool ok) {
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    st.A[q] = buf_load16(rt.wb, ok ? (uint32_t)kt * 1024u + l * 16u : 0x80000000u, rt.w0 + q * rt.wstep);
+    st.A[q] = buf_load16_nt(rt.wb, ok ? (uint32_t)kt * 1024u + l * 16u : 0x80000000u, rt.w0 + q * rt.wstep);
     st.sa[q] = buf_load1(rt.sb, ok ? (uint32_t)kt * 64u + l : 0x80000000u, rt.s0 + q * rt.sstep);
   }
 }
@@ -192,7 +192,7 @@ __device__ __forceinline__ void a16w_load(A16W<WF> &st, const RowTiles &rt, uint
   constexpr uint32_t U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
 #pragma unroll
   for (int q = 0; q < 4; q++)
-    st.A[q].load(rt.wb, ok ? (uint32_t)kt * 64u * U + l * U : 0x80000000u, rt.w0 + q * rt.wstep, rt.sb,
+    st.A[q].template load<true>(rt.wb, ok ? (uint32_t)kt * 64u * U + l * U : 0x80000000u, rt.w0 + q * rt.wstep, rt.sb,
                  ok ? (uint32_t)kt * 64u * SU + l * SU : 0x80000000u, rt.s0 + q * rt.sstep);
 }
 
@@ -267,6 +267,7 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
   for (int p0 = 0; p0 < ncols; p0 += a.cpass) {
     const int ncol = min(a.cpass, ncols - p0);
     const bool have = c < ncol;
+    // weights are read once per layer: non-temporal loads (buf_load16_nt).
     // two k-tiles of weights in flight per wave: tiles w, w + NW, ... (three
     // measured 1.4 us slower for the NVFP4 up/gate GEMM at K = 6144 and level
     // for MXFP4: with every block resident, more requests only lengthen the
@@ -555,7 +556,7 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   else is.item = i1;
   auto issue = [&](int s) {
     const bool ok = is.item < i1 && is.kt * 128 + 32 * g < N;
-    A[s] = buf_load16(is.wb, ok ? (uint32_t)is.kt * 1024u + (uint32_t)l * 16u : 0x80000000u, is.w0);
+    A[s] = buf_load16_nt(is.wb, ok ? (uint32_t)is.kt * 1024u + (uint32_t)l * 16u : 0x80000000u, is.w0);
     sa[s] = buf_load1(is.sb, ok ? (uint32_t)is.kt * 64u + (uint32_t)l : 0x80000000u, is.s0);
     if (is.item < i1) g2_next(is, a, ng, nkt, tb);
   };
@@ -728,9 +729,9 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
     const uint32_t U = nv ? 16u : 12u, SU = nv ? 2u : 1u;
     const uint32_t dv = ok ? (uint32_t)l * U : 0x80000000u, wo = is.w0 + (uint32_t)kt * 64u * U;
     if constexpr (WF == W_NVFP4) {
-      A16[s] = buf_load16(is.wb, dv, wo);
+      A16[s] = buf_load16_nt(is.wb, dv, wo);
     } else {
-      A3[s] = buf_load12(is.wb, dv, wo);
+      A3[s] = buf_load12_nt(is.wb, dv, wo);
       if constexpr (WF == 0) A4[s] = buf_load4(is.wb, nv && ok ? dv + 12u : 0x80000000u, wo);
     }
     sa[s] = buf_load2(is.sb, ok ? (nv ? (uint32_t)l * 2u : (uint32_t)(l & ~1)) : 0x80000000u,
