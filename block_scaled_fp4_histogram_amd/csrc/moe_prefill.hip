@@ -964,6 +964,9 @@ __device__ __forceinline__ uint32_t pf16_scale(uint32_t dw, int l) {
 // Weight and scale loads of wave w for k-tile kt.  Lanes whose 32-column group
 // lies past the reduction length read past the buffer's range: zeros, and no
 // memory traffic.
+// The weight data goes through non-temporal loads (hybrid prefill at 2048
+// tokens: 632.5 -> 626.6 us; level at the NVFP4 one; the W4A8 kernels, whose
+// hot experts' tiles share weight lines, measured slower with them).
 template <int WF>
 __device__ __forceinline__ void pf16_load_w(Pf16W &r, const Pf16Src &src, int kt, int w, int l) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
@@ -974,11 +977,11 @@ __device__ __forceinline__ void pf16_load_w(Pf16W &r, const Pf16Src &src, int kt
   for (int q = 0; q < 2; q++) {
     const uint32_t rt = (uint32_t)(2 * w + q);
     if constexpr (WF == W_NVFP4) {
-      const v4i v = buf_load16(src.wb, vd, rt * src.wstep);
+      const v4i v = buf_load16_nt(src.wb, vd, rt * src.wstep);
       r.a[q][0] = v[0]; r.a[q][1] = v[1]; r.a[q][2] = v[2]; r.a[q][3] = v[3];
       r.sc[q] = buf_load4(src.sb, vs, rt * src.sstep);
     } else {
-      const v3i v = buf_load12(src.wb, vd, rt * src.wstep);
+      const v3i v = buf_load12_nt(src.wb, vd, rt * src.wstep);
       r.a[q][0] = v[0]; r.a[q][1] = v[1]; r.a[q][2] = v[2]; r.a[q][3] = 0;
       r.sc[q] = buf_load4(src.sb, vs, rt * src.sstep);
     }
@@ -1568,10 +1571,10 @@ __device__ __forceinline__ void pf16_load_w_rt(Pf16W &r, const Pf16Src &src, uin
   for (int q = 0; q < 2; q++) {
     const uint32_t so = (rt0 + q) * src.wstep + (uint32_t)kt * 64u * U, ss = (rt0 + q) * src.sstep + (uint32_t)kt * 64u * SU;
     if constexpr (WF == W_NVFP4) {
-      const v4i v = buf_load16(src.wb, vd, so);
+      const v4i v = buf_load16_nt(src.wb, vd, so);
       r.a[q][0] = v[0]; r.a[q][1] = v[1]; r.a[q][2] = v[2]; r.a[q][3] = v[3];
     } else {
-      const v3i v = buf_load12(src.wb, vd, so);
+      const v3i v = buf_load12_nt(src.wb, vd, so);
       r.a[q][0] = v[0]; r.a[q][1] = v[1]; r.a[q][2] = v[2]; r.a[q][3] = 0;
     }
     r.sc[q] = buf_load4(src.sb, vs, ss);
