@@ -113,16 +113,20 @@ int seq_for(const moe_plan_s *p, int T);
 // Whether runs at the rung of `cap` tokens combine through the per-slot route
 // buffer and the top-k sum (always in deterministic mode) rather than fp32
 // atomics into an accumulator.  The ladder's choice for deterministic = 0: the
-// route buffer with the 64-route prefill kernels, whose atomic adds all execute
+// route buffer with the prefill kernels, whose atomic adds all execute
 // memory-side on this GPU (a 4096-token W4A8 prefill layer measured 903 us with
-// atomics against 602 us through the route buffer), atomics otherwise.  A chunked
-// batch's chunks all follow the rung of its first chunk.
+// atomics against 602 us through the route buffer), and with the W4A8 general
+// kernels from 256 tokens (per-rung race: 456 vs 483 us at 256 tokens, 482 vs
+// 600 us at 512; below 256 the two are within 2 %); atomics otherwise.  A
+// chunked batch's chunks all follow the rung of its first chunk.
+constexpr int kRbGeneralMinTA8 = 256;
 bool route_buffer(const moe_plan_s *p, int cap, int deterministic) {
   if (deterministic) return true;
   const int pinned = p->comb[rung_of(p, cap)];
   if (pinned) return pinned == MOE_COMBINE_ROUTE_BUFFER;
   const int seq = seq_for(p, cap);
-  return seq == MOE_SEQ_PREFILL || seq == MOE_SEQ_PREFILL_NARROW;
+  if (seq == MOE_SEQ_PREFILL || seq == MOE_SEQ_PREFILL_NARROW) return true;
+  return seq == MOE_SEQ_GENERAL && p->afmt == MOE_A_MXFP8 && cap >= kRbGeneralMinTA8;
 }
 
 // Carving of the scratch arena for one chunk of `cap` tokens.
@@ -287,8 +291,10 @@ bool seq_eligible(const moe_plan_s *p, int cap, int seq) {
 
 // The ladder's own choice, from the per-rung race on uniform routing (one
 // MI355X, both geometries of the pages, atomic and deterministic combine): the
-// 64-route-tile kernels overtake the 16-route ones from 256 tokens for W4A8
-// (deterministic: 485 vs 512 us) and from 512 for W4A16 / W3A16 (421 vs 569).
+// 64-route-tile kernels overtake the 16-route ones on the 1024-token rung for
+// W4A8 (deterministic: 547 vs 761 us; on the 512-token rung the 16-route ones,
+// whose weights stream non-temporally, still lead: 507 vs 518) and from 512
+// tokens for W4A16 / W3A16 (421 vs 569).
 // The W4A8 up/gate GEMM's 128-route tiles overtake its 64-route ones once an
 // expert averages 32 routes (below that they are mostly padding: at 1024
 // tokens, 16 routes an expert at E = 384, top-6, the 64-route tiles lead by

@@ -274,14 +274,20 @@ template <int WF>
 struct A16Tile {
   uint32_t d[4];   // NVFP4: 4 dwords of codes; NF3: 3 dwords (12 bytes)
   uint32_t sc;     // scale byte(s)
+  template <bool NT = false>   // NT: non-temporal data loads
   __device__ __forceinline__ void load(const uint8_t *data, const uint8_t *scales) {
     if (WF == W_NVFP4) {
-      const v4i v = *(const v4i *)data;
+      const v4i v = NT ? __builtin_nontemporal_load((const v4i *)data) : *(const v4i *)data;
       d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
       sc = *(const uint16_t *)scales;
     } else {
       const uint32_t *p = (const uint32_t *)data;
-      d[0] = p[0]; d[1] = p[1]; d[2] = p[2]; d[3] = 0;
+      if (NT) {
+        d[0] = __builtin_nontemporal_load(p); d[1] = __builtin_nontemporal_load(p + 1); d[2] = __builtin_nontemporal_load(p + 2);
+      } else {
+        d[0] = p[0]; d[1] = p[1]; d[2] = p[2];
+      }
+      d[3] = 0;
       sc = *scales;
     }
   }
@@ -370,7 +376,7 @@ __device__ __forceinline__ void a8g1_load(A8G1Stage &st, const uint8_t *wt, cons
                                           bool have, int g) {
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    st.A[q] = *(const v4i *)(wt + q * rt_bytes + (size_t)kt * 1024);
+    st.A[q] = __builtin_nontemporal_load((const v4i *)(wt + q * rt_bytes + (size_t)kt * 1024));   // read once
     st.sa[q] = sp[q * rt_scales + kt * 64];
   }
   if (have) {
@@ -401,7 +407,8 @@ __device__ __forceinline__ void a16g1_load(A16G1Stage<WF> &st, const uint8_t *wt
                                            size_t rt_scales, int kt, const uint16_t *xrow, bool have, int g) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
 #pragma unroll
-  for (int q = 0; q < 4; q++) st.A[q].load(wt + q * rt_bytes + (size_t)kt * 64 * U, sp + q * rt_scales + kt * 64 * SU);
+  for (int q = 0; q < 4; q++)   // weights read once at the batch sizes this serves: non-temporal
+    st.A[q].template load<true>(wt + q * rt_bytes + (size_t)kt * 64 * U, sp + q * rt_scales + kt * 64 * SU);
   if (have) {
     const v4i *xp = (const v4i *)(xrow + kt * 128 + 32 * g);
 #pragma unroll
