@@ -115,6 +115,11 @@ struct PfW {
 // Weight and scale loads of wave w for k-tile kt.  Lanes whose 32-column group
 // lies past the reduction length, and row tiles past the block's last one,
 // read past the buffer's range: zeros, and no memory traffic.
+// NT: non-temporal weight loads (the 64-route up/gate GEMM, which the ladder
+// runs where an expert mostly fills one tile, so its weights are read once:
+// 1024-token rung 546 -> 517 us; the 128-route kernel, whose hot experts'
+// tiles share weight lines, measured slower with them).
+template <bool NT = false>
 __device__ __forceinline__ void pf_load_w(PfW &r, const PfSrc &src, int kt, int w, int l) {
   const bool in = (kt * 4 + (l >> 4)) * 32 < src.kbytes;
 #pragma unroll
@@ -122,7 +127,8 @@ __device__ __forceinline__ void pf_load_w(PfW &r, const PfSrc &src, int kt, int 
     const int rt = 4 * w + q;
     const bool ok = in && rt < src.nrt;
     const uint32_t so = rt < src.nrt ? (uint32_t)rt : 0u;
-    r.a[q] = buf_load16(src.wb, ok ? (uint32_t)(kt * 1024 + l * 16) : 0x80000000u, so * src.wstep);
+    const uint32_t vo = ok ? (uint32_t)(kt * 1024 + l * 16) : 0x80000000u;
+    r.a[q] = NT ? buf_load16_nt(src.wb, vo, so * src.wstep) : buf_load16(src.wb, vo, so * src.wstep);
     r.sa[q] = buf_load4(src.sb, ok ? (uint32_t)(kt * 64 + (l & ~3)) : 0x80000000u, so * src.sstep);
   }
 }
@@ -240,7 +246,7 @@ __device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, PfW (&ring)[
   const int kn = kt + ST - 1;
   if (ISSUE == 1 || (ISSUE == -1 && kn < nkt)) {
     // one branch-free load sequence keeps the compiler's waits exact
-    pf_load_w(ring[(R + ST - 1) % ST], src, kn, w, l);
+    pf_load_w<!SWAP>(ring[(R + ST - 1) % ST], src, kn, w, l);
     pf_issue_b(L.st[kn % ST], src, kn, w, l);
   }
   v4i b[4][2];
@@ -274,7 +280,7 @@ __device__ __forceinline__ void pf_kloop(PfLds &L, const PfSrc &src, int w, v4f 
   // keeps the compiler's bookkeeping of the ring registers exact
 #pragma unroll
   for (int s = 0; s < ST - 1; s++) {
-    pf_load_w(ring[s], src, s, w, l);
+    pf_load_w<!SWAP>(ring[s], src, s, w, l);
     pf_issue_b(L.st[s], src, s, w, l);
   }
   int kt = 0;
