@@ -74,6 +74,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // One block's work item: tile of the tier's tile table and column block.
 struct PfWork {
   int valid, e, p0, rows, sub;
+  int single;   // the expert's routes fit this one tile: its weights are read once per column block
 };
 
 __device__ __forceinline__ PfWork pf_work(const GemmArgs &a, int nsub, bool sub_major) {
@@ -90,6 +91,7 @@ __device__ __forceinline__ PfWork pf_work(const GemmArgs &a, int nsub, bool sub_
   w.e = u - a.u_base;
   w.p0 = a.off[u] + a.tile_row0[tbeg + t];
   w.rows = min(a.tile_rows, a.off[u + 1] - w.p0);
+  w.single = a.off[u + 1] - a.off[u] <= a.tile_rows;
   return w;
 }
 
@@ -115,10 +117,13 @@ struct PfW {
 // Weight and scale loads of wave w for k-tile kt.  Lanes whose 32-column group
 // lies past the reduction length, and row tiles past the block's last one,
 // read past the buffer's range: zeros, and no memory traffic.
-// NT: non-temporal weight loads (the 64-route up/gate GEMM, which the ladder
-// runs where an expert mostly fills one tile, so its weights are read once:
-// 1024-token rung 546 -> 517 us; the 128-route kernel, whose hot experts'
-// tiles share weight lines, measured slower with them).
+// NT: non-temporal weight loads, for up/gate tiles whose expert's weights are
+// read once per column block (the 64-route kernel on the 1024-token rung:
+// 546 -> 517 us with them), not for the tiles of hot experts, which share
+// weight lines in L2 (with them for every tile the 128-route kernel measured
+// 268 -> 281 us at the Zipf-skewed 4096-token batch, the 64-route one
+// 577 -> 669 us).  The 128-route kernel takes them for blocks whose expert
+// fits the one tile (that batch: 271 -> 262 us), the 64-route one always.
 template <bool NT = false>
 __device__ __forceinline__ void pf_load_w(PfW &r, const PfSrc &src, int kt, int w, int l) {
   const bool in = (kt * 4 + (l >> 4)) * 32 < src.kbytes;
@@ -234,7 +239,7 @@ __device__ __forceinline__ void pf_mma(const PfW &wt, const v4i (&b)[4][2], cons
 // both are known at compile time the compiler's own bookkeeping of the ring
 // registers stays exact.  Waves without weight rows (the missing half of a
 // partial block) still load and pass the barriers, but skip the MFMAs.
-template <bool SWAP, int R, int WAITN, int ISSUE>
+template <bool SWAP, int R, int WAITN, int ISSUE, bool NT>
 __device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, PfW (&ring)[kPfStages], int kt, int nkt, int w,
                                         bool active, v4f (*acc)[4]) {
   constexpr int ST = kPfStages;
@@ -246,7 +251,7 @@ __device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, PfW (&ring)[
   const int kn = kt + ST - 1;
   if (ISSUE == 1 || (ISSUE == -1 && kn < nkt)) {
     // one branch-free load sequence keeps the compiler's waits exact
-    pf_load_w<!SWAP>(ring[(R + ST - 1) % ST], src, kn, w, l);
+    pf_load_w<NT>(ring[(R + ST - 1) % ST], src, kn, w, l);
     pf_issue_b(L.st[kn % ST], src, kn, w, l);
   }
   v4i b[4][2];
@@ -267,7 +272,7 @@ __device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, PfW (&ring)[
 
 // The k-loop of both GEMMs: whole ring turns while every step is steady, then
 // at most ST + 1 closing steps.  w: the wave index, wave-uniform (scalar).
-template <bool SWAP>
+template <bool SWAP, bool NT = false>
 __device__ __forceinline__ void pf_kloop(PfLds &L, const PfSrc &src, int w, v4f (*acc)[4]) {
   constexpr int ST = kPfStages;
   static_assert(ST == 3, "the k-loop is unrolled by the ring depth");
@@ -280,20 +285,20 @@ __device__ __forceinline__ void pf_kloop(PfLds &L, const PfSrc &src, int w, v4f 
   // keeps the compiler's bookkeeping of the ring registers exact
 #pragma unroll
   for (int s = 0; s < ST - 1; s++) {
-    pf_load_w<!SWAP>(ring[s], src, s, w, l);
+    pf_load_w<NT>(ring[s], src, s, w, l);
     pf_issue_b(L.st[s], src, s, w, l);
   }
   int kt = 0;
   for (; kt + 2 * ST - 1 <= nkt; kt += ST) {   // k-tiles kt .. kt + 2 steady: kt + 2 + ST - 1 < nkt
-    pf_step<SWAP, 0, kPfLoads, 1>(L, src, ring, kt, nkt, w, active, acc);
-    pf_step<SWAP, 1, kPfLoads, 1>(L, src, ring, kt + 1, nkt, w, active, acc);
-    pf_step<SWAP, 2, kPfLoads, 1>(L, src, ring, kt + 2, nkt, w, active, acc);
+    pf_step<SWAP, 0, kPfLoads, 1, NT>(L, src, ring, kt, nkt, w, active, acc);
+    pf_step<SWAP, 1, kPfLoads, 1, NT>(L, src, ring, kt + 1, nkt, w, active, acc);
+    pf_step<SWAP, 2, kPfLoads, 1, NT>(L, src, ring, kt + 2, nkt, w, active, acc);
   }
-  if (kt < nkt) pf_step<SWAP, 0, -1, -1>(L, src, ring, kt, nkt, w, active, acc);
-  if (kt + 1 < nkt) pf_step<SWAP, 1, -1, -1>(L, src, ring, kt + 1, nkt, w, active, acc);
-  if (kt + 2 < nkt) pf_step<SWAP, 2, -1, -1>(L, src, ring, kt + 2, nkt, w, active, acc);
-  if (kt + 3 < nkt) pf_step<SWAP, 0, -1, -1>(L, src, ring, kt + 3, nkt, w, active, acc);
-  if (kt + 4 < nkt) pf_step<SWAP, 1, -1, -1>(L, src, ring, kt + 4, nkt, w, active, acc);
+  if (kt < nkt) pf_step<SWAP, 0, -1, -1, NT>(L, src, ring, kt, nkt, w, active, acc);
+  if (kt + 1 < nkt) pf_step<SWAP, 1, -1, -1, NT>(L, src, ring, kt + 1, nkt, w, active, acc);
+  if (kt + 2 < nkt) pf_step<SWAP, 2, -1, -1, NT>(L, src, ring, kt + 2, nkt, w, active, acc);
+  if (kt + 3 < nkt) pf_step<SWAP, 0, -1, -1, NT>(L, src, ring, kt + 3, nkt, w, active, acc);
+  if (kt + 4 < nkt) pf_step<SWAP, 1, -1, -1, NT>(L, src, ring, kt + 4, nkt, w, active, acc);
 }
 
 template <int Q, int CB>
@@ -401,7 +406,11 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8(GemmArgs a) {
   src.nrb = 4;   // every route block (skipping padding here costs registers this kernel does not have)
   v4f acc[kPfQ][4];
   zero_acc<kPfQ, 4>(acc);
-  pf_kloop<false>(L, src, wu, acc);
+  // non-temporal weights for every tile: the ladder runs this kernel where experts
+  // average under 32 routes, mostly one tile each (choosing per block, as the
+  // 128-route kernel does, makes this kernel spill and measured slower: 1024-token
+  // rung 568 vs 516 us)
+  pf_kloop<false, true>(L, src, wu, acc);
   if (kPfQ * w >= src.nrt) return;   // the missing half of a partial block
   // epilogue: row tiles 4w + 2s (up) and 4w + 2s + 1 (gate) = intermediate
   // columns 128 hb + 32 w + 16 s .. +15; their 32 columns form one MXFP8 group
@@ -540,14 +549,14 @@ __device__ __forceinline__ void pw_mma(const PfW &wt, const v4i (&b)[4][2], cons
 // One k-tile (R = kt % 2): wait for stage kt (the only one in flight), barrier
 // (every wave is also done with stage kt - 1), issue k-tile kt + 1 into the
 // slots kt - 1 held (ISSUE), then both halves of stage kt.
-template <int R, bool ISSUE>
+template <int R, bool ISSUE, bool NT>
 __device__ __forceinline__ void pw_step(PwLds &L, const PwSrc &src, PfW (&ring)[kPwStages], int kt, int w,
                                         bool active, int nrb, uint32_t vxs, v4f (*acc)[8]) {
   const int l = threadIdx.x & 63;
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
   if (ISSUE) {
-    pf_load_w(ring[R ^ 1], src.w, kt + 1, w, l);
+    pf_load_w<NT>(ring[R ^ 1], src.w, kt + 1, w, l);
     pw_issue_b(L.st[R ^ 1], src, kt + 1, w, l);
   }
   if (active) {
@@ -564,6 +573,23 @@ __device__ __forceinline__ void pw_step(PwLds &L, const PwSrc &src, PfW (&ring)[
       __builtin_amdgcn_s_setprio(0);
     }
   }
+}
+
+// The k-loop; NT: non-temporal weight loads.
+template <bool NT>
+__device__ __forceinline__ void pw_kloop(PwLds &L, const PwSrc &src, int nkt, int wu, bool active, int nrb,
+                                         uint32_t vxs, v4f (*acc)[8]) {
+  const int l = threadIdx.x & 63;
+  PfW ring[kPwStages];
+  pf_load_w<NT>(ring[0], src.w, 0, wu, l);
+  pw_issue_b(L.st[0], src, 0, wu, l);
+  int kt = 0;
+  for (; kt + 2 < nkt; kt += 2) {
+    pw_step<0, true, NT>(L, src, ring, kt, wu, active, nrb, vxs, acc);
+    pw_step<1, true, NT>(L, src, ring, kt + 1, wu, active, nrb, vxs, acc);
+  }
+  pw_step<0, true, NT>(L, src, ring, kt, wu, active, nrb, vxs, acc);
+  pw_step<1, false, NT>(L, src, ring, kt + 1, wu, active, nrb, vxs, acc);
 }
 
 // Block: 16 row tiles of w13 = up and gate of 128 intermediate columns (8 in
@@ -598,18 +624,10 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm1_a8w(GemmArgs a) {
   v4f acc[kPfQ][8];
   zero_acc<kPfQ, 8>(acc);
   const int nkt = K / 128;   // even: K % 256 == 0
-  PfW ring[kPwStages];
   pw_stage_scales(L, a, wk, wu, l);   // landed by the first step's wait
-  pf_load_w(ring[0], src.w, 0, wu, l);
-  pw_issue_b(L.st[0], src, 0, wu, l);
   const uint32_t vxs = lds_addr(&L.XS[c * kPwXsRow + g]);
-  int kt = 0;
-  for (; kt + 2 < nkt; kt += 2) {
-    pw_step<0, true>(L, src, ring, kt, wu, active, nrb, vxs, acc);
-    pw_step<1, true>(L, src, ring, kt + 1, wu, active, nrb, vxs, acc);
-  }
-  pw_step<0, true>(L, src, ring, kt, wu, active, nrb, vxs, acc);
-  pw_step<1, false>(L, src, ring, kt + 1, wu, active, nrb, vxs, acc);
+  if (wk.single) pw_kloop<true>(L, src, nkt, wu, active, nrb, vxs, acc);
+  else pw_kloop<false>(L, src, nkt, wu, active, nrb, vxs, acc);
   if (!active) return;   // the missing half of a partial block
   // epilogue: row tiles 4w + 2s (up) and 4w + 2s + 1 (gate) = intermediate
   // columns 128 hb + 32 w + 16 s .. +15; their 32 columns form one MXFP8 group
@@ -1221,6 +1239,7 @@ __device__ __forceinline__ PfWork pf_work_tiers(const GemmArgs &a, int nsub, boo
   w.e = u - (t1 ? a.u_base_b : 0);
   w.p0 = a.off[u] + a.tile_row0[tbeg + t];
   w.rows = min(a.tile_rows, a.off[u + 1] - w.p0);
+  w.single = a.off[u + 1] - a.off[u] <= a.tile_rows;
   *tier = t1;
   return w;
 }
