@@ -791,17 +791,22 @@ struct PfResLds {
 // traffic) for loads past the run or lanes past the reduction length; the
 // k-tile's own offset goes into the scalar offset, so one lane offset serves
 // every k-tile.
+template <bool NT = false>   // NT: non-temporal weight loads
 __device__ __forceinline__ void pf_load_w_rt(PfW &r, const PfSrc &src, uint32_t rt0, int kt, uint32_t vd,
                                              uint32_t vs) {
 #pragma unroll
   for (int q = 0; q < kPfQ; q++) {
-    r.a[q] = buf_load16(src.wb, vd, (rt0 + q) * src.wstep + (uint32_t)kt * 1024u);
+    const uint32_t so = (rt0 + q) * src.wstep + (uint32_t)kt * 1024u;
+    r.a[q] = NT ? buf_load16_nt(src.wb, vd, so) : buf_load16(src.wb, vd, so);
     r.sa[q] = buf_load4(src.sb, vs, (rt0 + q) * src.sstep + (uint32_t)kt * 64u);
   }
 }
 
 // One block's work.
-template <int NKT, bool LASTFULL>
+// NT: non-temporal weight loads, for blocks whose expert fits its one 64-route
+// tile (its weights are then read once; every tile non-temporal measured
+// 198 -> 211 us at the Zipf-skewed 4096-token batch, this choice 189.5 -> 185.0).
+template <int NKT, bool LASTFULL, bool NT>
 __device__ __forceinline__ void pf_res_body(PfResLds<NKT> &L, const GemmArgs &a, const PfWork &wk, int *s_r,
                                             float *s_w) {
   const int K = a.K, N = a.N, nob = K / 256, obg = a.obg;
@@ -836,7 +841,7 @@ __device__ __forceinline__ void pf_res_body(PfResLds<NKT> &L, const GemmArgs &a,
   const uint32_t kOut = 0x80000000u, vd = (uint32_t)(l * 16), vs = (uint32_t)(l & ~3);
   PfW ring[NKT];
 #pragma unroll
-  for (int kt = 0; kt < NKT; kt++) pf_load_w_rt(ring[kt], src, (uint32_t)(16 * ob0 + 4 * wu), kt, vd, vs);
+  for (int kt = 0; kt < NKT; kt++) pf_load_w_rt<NT>(ring[kt], src, (uint32_t)(16 * ob0 + 4 * wu), kt, vd, vs);
   // the rows have landed once only the weight loads may be in flight; then
   // every wave's share (and s_r / s_w) is visible
   wait_vm<2 * kPfQ * NKT>();
@@ -867,7 +872,7 @@ __device__ __forceinline__ void pf_res_body(PfResLds<NKT> &L, const GemmArgs &a,
       // them (hoisted above, the loads would need a second register set and spill), and no
       // step is interleaved with the next for the same reason
       __builtin_amdgcn_sched_barrier(0);
-      pf_load_w_rt(ring[kt], src, rtn, kt, nd, ns);
+      pf_load_w_rt<NT>(ring[kt], src, rtn, kt, nd, ns);
       __builtin_amdgcn_sched_barrier(0);
     }
     // acc[q][cb][i]: route 16 cb + 4 g + i, output column 256 ob + 64 w + 16 q + c
@@ -883,7 +888,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8_res(GemmArgs a) {
   const int nob = a.K / 256;
   const PfWork wk = pf_work(a, (nob + a.obg - 1) / a.obg, false);
   if (!wk.valid) return;
-  pf_res_body<NKT, LASTFULL>(L, a, wk, s_r, s_w);
+  if (wk.single) pf_res_body<NKT, LASTFULL, true>(L, a, wk, s_r, s_w);
+  else pf_res_body<NKT, LASTFULL, false>(L, a, wk, s_r, s_w);
 }
 
 static int pf_grid(int grid_tiles, int nsub) { return (grid_tiles * nsub + 7) / 8 * 8; }
