@@ -291,10 +291,8 @@ bool seq_eligible(const moe_plan_s *p, int cap, int seq) {
 
 // The ladder's own choice, from the per-rung race on uniform routing (one
 // MI355X, both geometries of the pages, atomic and deterministic combine): the
-// 64-route-tile kernels overtake the 16-route ones on the 1024-token rung for
-// W4A8 (deterministic: 547 vs 761 us; on the 512-token rung the 16-route ones,
-// whose weights stream non-temporally, still lead: 507 vs 518) and from 512
-// tokens for W4A16 / W3A16 (421 vs 569).
+// 64-route-tile kernels overtake the 16-route ones from 256 tokens for W4A8
+// (deterministic: 448 vs 465 us) and from 512 for W4A16 / W3A16 (421 vs 569).
 // The W4A8 up/gate GEMM's 128-route tiles overtake its 64-route ones once an
 // expert averages 32 routes (below that they are mostly padding: at 1024
 // tokens, 16 routes an expert at E = 384, top-6, the 64-route tiles lead by

@@ -13,7 +13,7 @@ constexpr int kPfWideRows = 128;     // routes of one tile of the prefill W4A8 u
 constexpr int kPfWideMaxK = 8704;    // largest K it takes (it stages the tile's activation scale rows in LDS)
 constexpr int kPfResSlots = 512;     // resident blocks of the prefill W4A8 down GEMM (2 per CU)
 constexpr int kPrefillMinT = 512;    // smallest batch the ladder runs with the prefill kernels (16-bit activations)
-constexpr int kPrefillMinTA8 = 513;  // the same for W4A8
+constexpr int kPrefillMinTA8 = 256;  // the same for W4A8
 constexpr int kWideMinRoutes = 32;   // routes an expert averages from which the ladder takes 128-route up/gate tiles
 constexpr int kRouteChunk = 1024;    // routes handled by one route-planner block
 constexpr int kMaxExperts = 1024;    // experts of all tiers together (LDS histogram size)

@@ -160,8 +160,8 @@ void moe_experts_destroy(moe_experts_t experts);
  *                   1: per-slot route buffer + fixed-order top-k sum,
  *                   bit-stable run to run (moe_b12x_next.py, DETERMINISTIC).
  *                   With 0, a rung whose combine is ROUTE_BUFFER (the
- *                   ladder's choice on the PREFILL sequences and on W4A8
- *                   GENERAL rungs from 256 tokens; see
+ *                   ladder's choice on the PREFILL sequences, and on W4A8
+ *                   GENERAL rungs from 256 tokens when pinned there; see
  *                   moe_plan_set_combine) combines as 1 does.
  *                   Decode-size batches (<= 16 tokens, <= 64 routes) run two
  *                   kernels that fold each token's slots in slot order in

@@ -212,12 +212,13 @@ def test_wrapper_refuses_mis_shaped_tensors_before_the_library_sees_them():
 
 def test_combine_pins_follow_the_ladder_scratch_and_tuning_file(tmp_path):
     """deterministic = 0 combines through the route buffer on the prefill sequences and on
-    the W4A8 general one from 256 tokens, with atomics below unless a rung is pinned; the
-    scratch follows the combine (route buffer 2 R K bytes, accumulator 4 T K); pins persist
-    (v2 lines) and sequence-only v1 lines still load."""
+    the W4A8 general one from 256 tokens (where a pin puts it), with atomics on the general
+    one below unless a rung is pinned; the scratch follows the combine (route buffer 2 R K
+    bytes, accumulator 4 T K); pins persist (v2 lines) and sequence-only v1 lines still load."""
     p = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
     assert p.combine(4096) == M.COMBINE_ROUTE_BUFFER and p.combine(100) == M.COMBINE_ATOMIC
-    assert p.sequence(256) == M.SEQ_GENERAL and p.combine(256) == M.COMBINE_ROUTE_BUFFER
+    p.set_sequence(256, M.SEQ_GENERAL)
+    assert p.combine(256) == M.COMBINE_ROUTE_BUFFER
     assert M.Plan(256, 6144, 512, 8, None, M.A_BF16, max_tokens=4096).combine(256) == M.COMBINE_ATOMIC
     assert p.scratch_bytes(4096, False) == p.scratch_bytes(4096, True)
     atomic_100 = p.scratch_bytes(100, False)
@@ -298,12 +299,12 @@ def test_narrow_prefill_sequence_is_a_w4a8_variant(tmp_path):
 
 def test_ladder_default_sequences():
     """The ladder's own choice per batch size (no pins): decode up to 64 routes, the
-    16-route kernels up to 512 tokens (W4A8) or below 512 (16-bit activations), then the
-    prefill kernels: for W4A8 with 64-route up/gate tiles until experts average 32 routes
-    and 128-route ones from there, for 16-bit activations with 128-route ones throughout."""
+    16-route kernels below 256 tokens (W4A8) or 512 (16-bit activations), then the prefill
+    kernels: for W4A8 with 64-route up/gate tiles until experts average 32 routes and
+    128-route ones from there, for 16-bit activations with 128-route ones throughout."""
     a8 = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=16384)
-    want = {8: M.SEQ_DECODE, 12: M.SEQ_GENERAL, 200: M.SEQ_GENERAL, 256: M.SEQ_GENERAL, 512: M.SEQ_GENERAL,
-            513: M.SEQ_PREFILL_NARROW, 1024: M.SEQ_PREFILL_NARROW, 2048: M.SEQ_PREFILL, 4096: M.SEQ_PREFILL,
+    want = {8: M.SEQ_DECODE, 12: M.SEQ_GENERAL, 200: M.SEQ_GENERAL, 255: M.SEQ_GENERAL, 256: M.SEQ_PREFILL_NARROW,
+            512: M.SEQ_PREFILL_NARROW, 1024: M.SEQ_PREFILL_NARROW, 2048: M.SEQ_PREFILL, 4096: M.SEQ_PREFILL,
             16384: M.SEQ_PREFILL}
     assert {t: a8.sequence(t) for t in want} == want
     a16 = M.Plan(256, 6144, 512, 8, None, M.A_BF16, max_tokens=4096)

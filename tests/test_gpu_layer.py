@@ -422,9 +422,10 @@ def test_general_sequence_at_full_geometry(name, batches):
 
 # The rungs the ladder sends to the prefill kernels below the benchmark's batch, at the
 # production geometries: W4A8 with 64-route up/gate tiles while experts average under 32
-# routes (1024 tokens: 16 an expert) and 128-route ones from there (2048: 32); 16-bit
-# activations with 128-route ones from the first prefill rung (512 tokens: 16 an expert).
-@pytest.mark.parametrize("name,T,seq", [("prefill", 1024, M.SEQ_PREFILL_NARROW), ("prefill", 2048, M.SEQ_PREFILL),
+# routes (from the first prefill rung, 256 tokens: 4 an expert) and 128-route ones from
+# there (2048: 32); 16-bit activations with 128-route ones from the first prefill rung (512
+# tokens: 16 an expert).
+@pytest.mark.parametrize("name,T,seq", [("prefill", 256, M.SEQ_PREFILL_NARROW), ("prefill", 2048, M.SEQ_PREFILL),
                                         ("nvfp4_prefill", 512, M.SEQ_PREFILL), ("hybrid", 1024, M.SEQ_PREFILL)])
 def test_ladder_prefill_rungs_at_full_geometry(name, T, seq):
     L = layer(name, max_tokens=T)
