@@ -217,8 +217,9 @@ def test_combine_pins_follow_the_ladder_scratch_and_tuning_file(tmp_path):
     bytes, accumulator 4 T K); pins persist (v2 lines) and sequence-only v1 lines still load."""
     p = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
     assert p.combine(4096) == M.COMBINE_ROUTE_BUFFER and p.combine(100) == M.COMBINE_ATOMIC
-    p.set_sequence(256, M.SEQ_GENERAL)
-    assert p.combine(256) == M.COMBINE_ROUTE_BUFFER
+    g = M.Plan(384, 7168, 576, 6, 7.0, M.A_MXFP8, max_tokens=4096)
+    g.set_sequence(256, M.SEQ_GENERAL)
+    assert g.combine(256) == M.COMBINE_ROUTE_BUFFER and g.combine(128) == M.COMBINE_ATOMIC
     assert M.Plan(256, 6144, 512, 8, None, M.A_BF16, max_tokens=4096).combine(256) == M.COMBINE_ATOMIC
     assert p.scratch_bytes(4096, False) == p.scratch_bytes(4096, True)
     atomic_100 = p.scratch_bytes(100, False)
