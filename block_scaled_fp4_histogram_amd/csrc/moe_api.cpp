@@ -173,6 +173,9 @@ Layout layout(const moe_plan_s *p, int cap, int deterministic) {
     L.hs = take(R * moe::hs_stride(p->N));
   } else {
     L.hb = take(2 * R * p->N);
+    // per route and 32-column slice of hb, the exponent byte of its largest
+    // magnitude: the decode down GEMM's fp16 row scale
+    L.hs = take(R * moe::hs_stride(p->N));
     // the decode down GEMM's two halves per 16-row output tile meet here: carved at
     // every capacity, since the last chunk of a batch above the top capacity can be
     // decode-sized whatever the capacity the arena was sized for

@@ -133,8 +133,10 @@ struct DecArgs {
   float limit;
   int has_limit;
   int cpass;                         // token rows per LDS staging pass (MXFP8 x)
-  uint8_t *hq, *hs;                  // MXFP8 intermediate per route r: [R, N], [R, N/32]
-  uint16_t *hb;                      // bf16 intermediate per route r: [R, N]
+  uint8_t *hq, *hs;                  // MXFP8 intermediate per route r: [R, N], [R, N/32]; W4A16: hs the
+                                     // exponent byte of each 32-column slice of hb
+  uint16_t *hb;                      // W4A16 intermediate per route r: [R, N], each 32-column slice the
+                                     // bf16-rounded values in fp16 times 2^-e of its own (from its byte)
   uint16_t *out;                     // bf16 [T, K]
   DecGroups *groups;                 // scratch
   int w_on_input;                    // router weight scales GEMM1 (W4A16 / W3A16), not the GEMM2 result

@@ -118,12 +118,13 @@ __device__ __forceinline__ DecExpert dec_expert(const DecArgs &a, int u) {
   return x;
 }
 
-// Fixed-order sum over the NW waves of the 16 GEMM1 accumulators, clamped
-// SwiGLU; returns the 8 intermediate values of lane (route column c, group g):
-// columns 32*hb + 16*s + 4*g + i for s, i.
+// Fixed-order sum over the NW waves of the 16 GEMM1 accumulators, times 2^ex
+// (the route's fp16 activation exponent; 0 for MXFP8), clamped SwiGLU; returns
+// the 8 intermediate values of lane (route column c, group g): columns
+// 32*hb + 16*s + 4*g + i for s, i.
 template <int NW>
 __device__ __forceinline__ void dec_swiglu(const float *red, int l, float gs, float limit, int has_limit, float alpha,
-                                           float beta, int act, float *h) {
+                                           float beta, int act, int ex, float *h) {
 #pragma unroll
   for (int s = 0; s < 2; s++)
 #pragma unroll
@@ -135,6 +136,9 @@ __device__ __forceinline__ void dec_swiglu(const float *red, int l, float gs, fl
         up += red[(w * 16 + iu) * 64 + l];
         gate += red[(w * 16 + ig) * 64 + l];
       }
+      // sums of fp16 activations scaled by 2^-ex (0 for MXFP8) back to scale, then the global scale
+      up = __builtin_amdgcn_ldexpf(up, ex);
+      gate = __builtin_amdgcn_ldexpf(gate, ex);
       h[s * 4 + i] = silu_clamped(gate * gs, up * gs, limit, has_limit, alpha, beta, act);
     }
 }
@@ -196,25 +200,28 @@ __device__ __forceinline__ void a16w_load(A16W<WF> &st, const RowTiles &rt, uint
                  ok ? (uint32_t)kt * 64u * SU + l * SU : 0x80000000u, rt.s0 + q * rt.sstep);
 }
 
-// bf16 activations of route column c (LDS row xrow) for k-tile kt.
+// fp16 activations of route column c (LDS row xrow, scaled by its row's
+// power of two) for k-tile kt; the weights are dequantised to fp16.
 template <int WF>
 __device__ __forceinline__ void a16w_mfma(const A16W<WF> &st, const uint16_t *xrow, bool have, int g, int kt,
                                           v4f *acc) {
   typename A16Tile<WF>::Deq dq[4];
 #pragma unroll
-  for (int q = 0; q < 4; q++) dq[q] = st.A[q].prep();
+  for (int q = 0; q < 4; q++) dq[q] = st.A[q].prep_h();
 #pragma unroll
   for (int s = 0; s < 4; s++) {
     v4i b = v4i{0, 0, 0, 0};
     if (have) b = *(const v4i *)(xrow + kt * 128 + 32 * g + 8 * s);
-    const v8bf bb = __builtin_bit_cast(v8bf, b);
+    const v8h bb = __builtin_bit_cast(v8h, b);
 #pragma unroll
-    for (int q = 0; q < 4; q++) acc[q] = mfma_bf16(st.A[q].step(s, dq[q]), bb, acc[q]);
+    for (int q = 0; q < 4; q++) acc[q] = mfma_f16(st.A[q].step_h(s, dq[q]), bb, acc[q]);
   }
 }
 
 // Stage the activation rows of the pass's route columns into LDS: MXFP8 codes
-// and scales (W4A8), or the bf16 rows as they are (W4A16).
+// and scales (W4A8), or (W4A16) the bf16 rows, then each row in place as fp16
+// times 2^-e with its exponent e (h_row_exp of the row's largest magnitude)
+// after the rows.
 template <bool A8, int NW>
 __device__ __forceinline__ void dec_stage_x(const DecArgs &a, unsigned long long md, int p0, int ncol, uint8_t *dsm) {
   const int K = a.K, kb32 = K / 32, tid = threadIdx.x;
@@ -236,12 +243,26 @@ __device__ __forceinline__ void dec_stage_x(const DecArgs &a, unsigned long long
       dst[1] = v4i{(int)codes[4], (int)codes[5], (int)codes[6], (int)codes[7]};
     }
   } else {
-    const int xstride = K + 8;   // bf16 elements
+    const int xstride = K + 8, n8 = K / 8;   // bf16 / fp16 elements, 8-element chunks per row
     uint16_t *xb = (uint16_t *)dsm;
-    for (int i = tid; i < ncol * (K / 8); i += NW * 64) {
-      const int col = i / (K / 8), c8 = i - col * (K / 8);
+    uint32_t *xm = (uint32_t *)(dsm + (size_t)a.cpass * 2 * xstride);   // per-row largest magnitude
+    if (tid < ncol) xm[tid] = 0u;
+    __syncthreads();
+    // 16 consecutive chunks (n8 is a multiple of 16) lie in one row: their
+    // largest is reduced across the 16-lane row by DPP, then one LDS atomic
+    for (int i = tid; i < ncol * n8; i += NW * 64) {
+      const int col = i / n8, c8 = i - col * n8;
       const int t = nth_bit(md, p0 + col) / a.topk;
-      *(v4i *)(xb + col * xstride + c8 * 8) = *(const v4i *)(a.x + (size_t)t * K + c8 * 8);
+      const v4i v = *(const v4i *)(a.x + (size_t)t * K + c8 * 8);
+      *(v4i *)(xb + col * xstride + c8 * 8) = v;
+      const uint32_t m = row16_max(bf16x8_amax(v));
+      if ((tid & 15) == 0) atomicMax(&xm[col], m);
+    }
+    __syncthreads();
+    for (int i = tid; i < ncol * n8; i += NW * 64) {
+      const int col = i / n8;
+      v4i *q = (v4i *)(xb + col * xstride + (i - col * n8) * 8);
+      *q = bf16x8_to_h(*q, h_row_exp(xm[col]));
     }
   }
 }
@@ -283,6 +304,8 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
     load(s0, w);
     dec_stage_x<A8, NW>(a, md, p0, ncol, dsm);
     __syncthreads();
+    // the column's activation exponent (fp16 rows only), read before LDS is reused
+    const int ex = (!A8 && have) ? h_row_exp(((const uint32_t *)(dsm + (size_t)a.cpass * 2 * (K + 8)))[c]) : 0;
     v4f acc[4];
 #pragma unroll
     for (int q = 0; q < 4; q++) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -309,10 +332,12 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
       for (int i = 0; i < 4; i++) red[(w * 16 + q * 4 + i) * 64 + l] = acc[q][i];
     __syncthreads();
     if (!A8 && a.act == ACT_RELU2) {
-      // ReLU^2 without the multiply: both halves' rows give their own columns
-      if (w == 0 && have) {
-        const float gs = X.g13 * (a.w_on_input ? a.topk_w[nth_bit(md, p0 + c)] : 1.0f);
-        const size_t r = (size_t)nth_bit(md, p0 + c);
+      // ReLU^2 without the multiply: both halves' rows give their own columns,
+      // each 32-column slice in fp16 with its exponent byte (as below)
+      if (w == 0) {
+        uint32_t mh[2] = {0u, 0u};
+        uint2 o[2][2];   // [s][half], bf16
+        const float gs = X.g13 * ((a.w_on_input && have) ? a.topk_w[nth_bit(md, p0 + c)] : 1.0f);
 #pragma unroll
         for (int s = 0; s < 2; s++)
 #pragma unroll
@@ -324,19 +349,32 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
               float v = 0.f;
 #pragma unroll 2
               for (int ww = 0; ww < NW; ww++) v += red[(ww * 16 + ir) * 64 + l];
-              z[i] = relu2(v * gs);
+              z[i] = relu2(__builtin_amdgcn_ldexpf(v, ex) * gs);
             }
-            uint2 o;
-            o.x = pack_bf16x2(z[0], z[1]);
-            o.y = pack_bf16x2(z[2], z[3]);
-            *(uint2 *)(a.hb + r * N + half * N1 + hb * 32 + 16 * s + 4 * g) = o;
+            o[s][half].x = pack_bf16x2(z[0], z[1]);
+            o[s][half].y = pack_bf16x2(z[2], z[3]);
+            mh[half] = max(mh[half], bf16x8_amax(v4i{(int)o[s][half].x, (int)o[s][half].y, 0, 0}));
           }
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+          uint32_t m = max(mh[half], (uint32_t)__shfl_xor((int)mh[half], 16));
+          m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+          if (have) {
+            const size_t r = (size_t)nth_bit(md, p0 + c);
+            const int e = h_row_exp(m);
+#pragma unroll
+            for (int s = 0; s < 2; s++)
+              *(uint2 *)(a.hb + r * N + half * N1 + hb * 32 + 16 * s + 4 * g) =
+                  uint2{bf16x2_to_h(o[s][half].x, e), bf16x2_to_h(o[s][half].y, e)};
+            if (g == 0) a.hs[r * hs_stride(N) + half * (N1 / 32) + hb] = (uint8_t)(m >> 23);
+          }
+        }
       }
     } else if (w == 0) {
       float h[8];
       // router weight on the input (W4A16 / W3A16): GEMM1 is linear, so it scales the accumulators
       const float gs = X.g13 * ((!A8 && a.w_on_input && have) ? a.topk_w[nth_bit(md, p0 + c)] : 1.0f);
-      dec_swiglu<NW>(red, l, gs, a.limit, a.has_limit, a.alpha, a.beta, a.act, h);
+      dec_swiglu<NW>(red, l, gs, a.limit, a.has_limit, a.alpha, a.beta, a.act, ex, h);
       if (A8) {
         float amax = 0.f;
 #pragma unroll
@@ -353,14 +391,27 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
                 e4m3x4(h[s * 4], h[s * 4 + 1], h[s * 4 + 2], h[s * 4 + 3], inv);
           if (g == 0) a.hs[r * hs_stride(N) + hb] = (uint8_t)sbyte;
         }
-      } else if (have) {
-        const size_t r = (size_t)nth_bit(md, p0 + c);
+      } else {
+        // the bf16-rounded values of each 32-column slice as fp16 times 2^-e,
+        // e from the slice's largest magnitude, whose exponent byte is stored
+        // for the down GEMM (which brings the slices of a row to one scale)
+        uint2 v[2];
+        uint32_t m = 0;
 #pragma unroll
         for (int s = 0; s < 2; s++) {
-          uint2 v;
-          v.x = pack_bf16x2(h[s * 4], h[s * 4 + 1]);
-          v.y = pack_bf16x2(h[s * 4 + 2], h[s * 4 + 3]);
-          *(uint2 *)(a.hb + r * N + hb * 32 + 16 * s + 4 * g) = v;
+          v[s].x = pack_bf16x2(h[s * 4], h[s * 4 + 1]);
+          v[s].y = pack_bf16x2(h[s * 4 + 2], h[s * 4 + 3]);
+          m = max(m, bf16x8_amax(v4i{(int)v[s].x, (int)v[s].y, 0, 0}));
+        }
+        m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+        if (have) {
+          const size_t r = (size_t)nth_bit(md, p0 + c);
+          const int e = h_row_exp(m);
+#pragma unroll
+          for (int s = 0; s < 2; s++)
+            *(uint2 *)(a.hb + r * N + hb * 32 + 16 * s + 4 * g) = uint2{bf16x2_to_h(v[s].x, e), bf16x2_to_h(v[s].y, e)};
+          if (g == 0) a.hs[r * hs_stride(N) + hb] = (uint8_t)(m >> 23);
         }
       }
     }
@@ -642,8 +693,9 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
 // W4A16 / W3A16 down GEMM, grid (K/16 output row tiles): the same item list,
 // wave slices and weight ring as the W4A8 kernel (a slot: NVFP4 16 + 2 bytes
 // or NF3 12 + 1 bytes a lane, per the group's tier); every route's bf16
-// intermediate row is staged in LDS by direct loads.  Each item is four
-// dequantise-and-multiply steps of 8 columns (bf16 MFMA).  WF: the format of
+// intermediate row is staged in LDS by direct loads and converted there to
+// fp16 times a power of two per row.  Each item is four dequantise-and-multiply
+// steps of 8 columns (fp16 MFMA).  WF: the format of
 // every tier (one 16- or 12-byte load per slot), or 0 for two tiers of
 // different formats (one load shape for both, below).
 constexpr int kG2RingA16 = 2;   // as kG2Ring (NVFP4 at K = 6144: 2 slots 40.4 us, 6 42.3)
@@ -669,8 +721,10 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   __shared__ float wr_s[kDecodeMaxRoutes];
   __shared__ __align__(16) float yb[kDecG2WavesA8][256];   // per-wave token sums
   __shared__ __align__(16) uint8_t zb[64];   // zero operand bytes for absent routes and columns past N
+  __shared__ uint32_t rexb[kDecodeMaxRoutes];  // per route the largest exponent byte of its slices in this half
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
   if (tid < 16) ((uint32_t *)zb)[tid] = 0u;
+  if (tid < kDecodeMaxRoutes) rexb[tid] = 0u;
   const int K = a.K, N = a.N, nkt = (N + 127) / 128;
   const int halves = dec2_a16_halves(N), rt = blockIdx.x / halves, h = blockIdx.x - rt * halves;
   const int nk0 = halves == 2 ? (nkt + 1) / 2 : nkt;   // k-tiles of half 0
@@ -684,6 +738,17 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   int gu = G->gu[l], istart = G->istart[l] / nkt * nkh, gnp = G->np[l];
   uint32_t gm_lo = (uint32_t)G->gm[l], gm_hi = (uint32_t)(G->gm[l] >> 32);
   float wv = tid < a.R ? (a.w_on_input ? 1.0f : a.topk_w[tid]) : 0.f;   // weight on the input: 1 here
+  // the exponent bytes of the routes' 32-column slices in this half (written
+  // by the up/gate kernel), one a thread; their maximum per route is the
+  // exponent of its fp16 row here
+  const int nsl = nh / 32, nsr = a.R * nsl;
+  const float rsl = 1.0f / (float)nsl;   // route of slice entry i: exact for the sizes here
+  int sr = 0;
+  uint32_t sb8 = 0;
+  if (tid < nsr) {
+    sr = (int)(((float)tid + 0.5f) * rsl);
+    sb8 = a.hs[(size_t)sr * hs_stride(N) + c0 / 32 + (tid - sr * nsl)];
+  }
   float g2v = 1.0f;   // global scale of group l's expert
   if (l < ng) {
     const bool t1 = a.n_tiers > 1 && gu >= a.tier[0].E;
@@ -693,13 +758,20 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   // the table, router weights and scales are complete here; re-defined by an
   // empty asm, their registers carry no pending load
   wait_vm<0>();
-  asm volatile("" : "+v"(gu), "+v"(istart), "+v"(gnp), "+v"(gm_lo), "+v"(gm_hi), "+v"(wv), "+v"(g2v));
+  asm volatile("" : "+v"(gu), "+v"(istart), "+v"(gnp), "+v"(gm_lo), "+v"(gm_hi), "+v"(wv), "+v"(g2v), "+v"(sb8));
   G2Tab tb;
   tb.gu = gu;
   tb.np = gnp;
   tb.gm = ((unsigned long long)gm_hi << 32) | gm_lo;
   tb.g2v = g2v;
   if (tid < a.R) wr_s[tid] = wv;
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();   // rexb is zero
+  if (tid < nsr) atomicMax(&rexb[sr], sb8);
+  for (int i = tid + kDecG2WavesA8 * 64; i < nsr; i += kDecG2WavesA8 * 64) {
+    const int r = (int)(((float)i + 0.5f) * rsl);
+    atomicMax(&rexb[r], (uint32_t)a.hs[(size_t)r * hs_stride(N) + c0 / 32 + (i - r * nsl)]);
+  }
   const int per = (NI + kDecG2WavesA8 - 1) / kDecG2WavesA8;
   const int i0 = min(NI, w * per), i1 = min(NI, i0 + per);
   v4i A16[kG2RingA16];   // NVFP4: the lane's 16 weight bytes
@@ -738,22 +810,57 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
                       is.s0 + (uint32_t)kt * 64u * SU);
     if (is.item < i1) g2_next(is, a, ng, nkh, tb);
   };
-  // this half's columns of every route's bf16 intermediate row -> LDS (row
-  // stride nh + 8 elements), 1 KB direct loads issued ahead of the ring
-  const uint16_t *hb_s = (const uint16_t *)dsm2;
+  // this half's columns of every route's intermediate row -> LDS (row stride
+  // nh + 8 elements) at one scale per row.  The up/gate kernel wrote each
+  // 32-column slice in fp16 times 2^-e_s of its own; each 8-column chunk is
+  // loaded into registers ahead of the ring (with its slice's exponent byte),
+  // multiplied by 2^(e_s - e) for its row's exponent e (the largest e_s of the
+  // row in this half, so the factor is at most 1) and stored.  Chunks past the
+  // rows load out of range (zeros, no traffic), so every round issues the same
+  // loads.
+  uint16_t *hb_s = (uint16_t *)dsm2;
   {
-    const int rs = 2 * nh + 16;
-    const uint8_t *src0 = (const uint8_t *)a.hb + 2 * (size_t)c0;
-    for (int ch = w; ch * 1024 < dec2_hb_bytes(a.R, nh); ch += kDecG2WavesA8) {
-      const int pos = ch * 1024 + l * 16, row = pos / rs, col = pos - row * rs;
-      dma16(row < a.R && col < 2 * nh ? src0 + (size_t)row * 2 * N + col : (const uint8_t *)a.hb, dsm2 + ch * 1024);
+    constexpr int kCh = 4, NT = kDecG2WavesA8 * 64;
+    const int n8 = nh / 8, nch = a.R * n8;
+    const float rn = 1.0f / (float)n8;   // row of chunk i: exact for the sizes here
+    const Buf hbuf = make_buf(a.hb, (uint32_t)((size_t)a.R * N * 2)), sbuf = make_buf(a.hs, (uint32_t)(a.R * hs_stride(N)));
+    for (int base = 0; base < nch; base += kCh * NT) {
+      v4i v[kCh];
+      uint32_t eb[kCh];
+#pragma unroll
+      for (int j = 0; j < kCh; j++) {
+        const int i = base + tid + j * NT, r = (int)(((float)i + 0.5f) * rn), c8 = i - r * n8;
+        const bool ok = i < nch;
+        v[j] = buf_load16(hbuf, ok ? (uint32_t)(r * N + c0 + 8 * c8) * 2u : 0x80000000u, 0);
+        eb[j] = buf_load1(sbuf, ok ? (uint32_t)(r * hs_stride(N) + (c0 + 8 * c8) / 32) : 0x80000000u, 0);
+      }
+      if (base == 0) {
+#pragma unroll
+        for (int q = 0; q < kG2RingA16; q++) issue(q);
+        // the routes' exponent bytes (rexb) are complete for every wave
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+      }
+#pragma unroll
+      for (int j = 0; j < kCh; j++) {
+        const int i = base + tid + j * NT, r = (int)(((float)i + 0.5f) * rn), c8 = i - r * n8;
+        if (i < nch) {
+          const v2h f = pow2_h2((int)(eb[j] & 0xFFu) - (int)rexb[r]);
+          v4i o;
+#pragma unroll
+          for (int d = 0; d < 4; d++) {
+            const uint32_t u = (uint32_t)v[j][d];   // a copy: bit_cast reads objects, not vector elements
+            o[d] = __builtin_bit_cast(int, __builtin_bit_cast(v2h, u) * f);
+          }
+          *(v4i *)(hb_s + r * (nh + 8) + 8 * c8) = o;
+        }
+      }
+    }
+    if (nch == 0) {
+#pragma unroll
+      for (int q = 0; q < kG2RingA16; q++) issue(q);
     }
   }
-#pragma unroll
-  for (int s = 0; s < kG2RingA16; s++) issue(s);
-  // the staged rows have landed once at most the ring's loads (3 a slot for
-  // mixed tiers, 2 for one format) are in flight
-  wait_vm<(WF == 0 ? 3 : 2) * kG2RingA16>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   float tok[4] = {0.f, 0.f, 0.f, 0.f};
@@ -761,13 +868,15 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
   ic.rt = rt;
   if (i0 < i1) g2_start(ic, a, i0, istart, ng, nkh, tb);
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  int r = -1;
+  int r = -1, er = 0;
   for (int base = i0; base < i1; base += kG2RingA16) {
 #pragma unroll
     for (int s = 0; s < kG2RingA16; s++) {
       if (base + s < i1) {
-        if (s == 0 || ic.kt == 0 || base + s == i0)   // route of this lane's token in the current run
+        if (s == 0 || ic.kt == 0 || base + s == i0) {   // route of this lane's token in the current run
           r = dec_token_route(ic.md, ic.pass, c, a.T, a.topk);
+          er = r >= 0 ? (int)rexb[r] - 141 : 0;   // the row's exponent, h_row_exp of its byte
+        }
         // absent routes and columns past N read zero bytes (zb) instead of branching
         const int kb = (kt0 + ic.kt) * 128 + 32 * g;
         const v4i *hp = (const v4i *)(r >= 0 && kb < N ? (const uint8_t *)(hb_s + r * (nh + 8) + (kb - c0)) : zb);
@@ -785,21 +894,21 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
         }
         const uint32_t sc = sa[s];
         if (WF == W_NVFP4 || (WF == 0 && ic.fmt == W_NVFP4)) {
-          const float slo = e4m3_f32(sc & 0xFFu), shi = e4m3_f32((sc >> 8) & 0xFFu);
+          const v2h sp = e4m3x2_h(sc);
 #pragma unroll
           for (int st = 0; st < 4; st++)
-            acc = mfma_bf16(nvfp4_step(d[st], st < 2 ? slo : shi), __builtin_bit_cast(v8bf, B[st]), acc);
+            acc = mfma_f16(nvfp4_step_h(d[st], st < 2 ? sp.x : sp.y), __builtin_bit_cast(v8h, B[st]), acc);
         } else {
           uint32_t t01, t23;
-          nf3_tables(e4m3_f32((l & 1) ? (sc >> 8) & 0xFFu : sc & 0xFFu), t01, t23);
+          nf3_tables_h(e4m3_f32((l & 1) ? (sc >> 8) & 0xFFu : sc & 0xFFu), t01, t23);
 #pragma unroll
           for (int st = 0; st < 4; st++)
-            acc = mfma_bf16(nf3_step_rc(st < 2 ? d[0] : d[1], d[2], st, t01, t23), __builtin_bit_cast(v8bf, B[st]), acc);
+            acc = mfma_f16(nf3_step_h(st < 2 ? d[0] : d[1], d[2], st, t01, t23), __builtin_bit_cast(v8h, B[st]), acc);
         }
         if (ic.kt == nkh - 1 || base + s + 1 == i1) {
           const float wgt = r >= 0 ? wr_s[r] * ic.g2 : 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; i++) tok[i] += acc[i] * wgt;
+          for (int i = 0; i < 4; i++) tok[i] += __builtin_amdgcn_ldexpf(acc[i], er) * wgt;
           acc = v4f{0.f, 0.f, 0.f, 0.f};
         }
         g2_next(ic, a, ng, nkh, tb);
@@ -847,12 +956,12 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
 }
 
 int decode_cpass(int K, int a8) {
-  const int row = a8 ? K + 16 + K / 32 : 2 * (K + 8);
+  const int row = a8 ? K + 16 + K / 32 : 2 * (K + 8) + 4;   // W4A16: fp16 row + its exponent
   return max(1, min(kDecodeMaxT, kDecStageBytes / row));
 }
 
 size_t decode_gemm1_lds(int K, int cpass, int a8) {
-  const size_t stage = a8 ? (size_t)cpass * (K + 16) + (size_t)cpass * (K / 32) : (size_t)cpass * 2 * (K + 8);
+  const size_t stage = a8 ? (size_t)cpass * (K + 16) + (size_t)cpass * (K / 32) : (size_t)cpass * (2 * (K + 8) + 4);
   const size_t red = (size_t)4 * 16 * 64 * sizeof(float);
   return ((stage > red ? stage : red) + 15) & ~(size_t)15;
 }

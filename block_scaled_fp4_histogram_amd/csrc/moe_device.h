@@ -269,6 +269,113 @@ __device__ __forceinline__ v8bf nf3_step_rc(uint32_t dsel, uint32_t d2, int s, u
   return __builtin_bit_cast(v8bf, r);
 }
 
+// ------------------------------------------- the same operands in fp16
+//
+// An NVFP4 weight value (E2M1 code times E4M3 scale: at most five significant
+// bits, magnitudes 2^-10 .. 2688) and a scaled NF3 table entry (a bf16 value
+// between about 2^-12 and 448) are exact in fp16 as they are in bf16.  In fp16
+// the scale goes onto two values at once: v_cvt_scalef32_pk_f16_fp4 decodes a
+// byte's two codes and one packed 16-bit multiply scales them, one instruction
+// a value against two for bf16, for which gfx950 has no packed multiply.  The
+// activations must then be fp16 too: a bf16 row is multiplied by the power of
+// two 2^-e that puts its largest magnitude in [2^14, 2^15) and converted, which
+// is exact for every element above 2^-28 of that maximum (bf16's 8 significant
+// bits fit fp16's 11 wherever the scaled value is an fp16 normal); the sums are
+// multiplied back by 2^e.  fp16 x fp16 products are exact in the MFMA's fp32 as
+// bf16 products are, so only elements below 2^-28 of their row's largest
+// round differently from the bf16 form.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v4f mfma_f16(v8h a, v8h b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// The two E4M3 scales in the low 16 bits of b as an fp16 pair (exact).
+__device__ __forceinline__ v2h e4m3x2_h(uint32_t b) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false); }
+
+// 8 fp4 codes (as for nvfp4_step) x scale sc -> 8 fp16, exact.
+__device__ __forceinline__ v8h nvfp4_step_h(uint32_t w, _Float16 sc) {
+  const v2h s2 = v2h{sc, sc};
+  v4i r;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    v2h f;
+    if (m == 0) f = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    else if (m == 1) f = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    else if (m == 2) f = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    else f = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+    r[m] = __builtin_bit_cast(int, f * s2);
+  }
+  return __builtin_bit_cast(v8h, r);
+}
+
+// Two bf16 (low, high half) -> the same two values as fp16 where they are
+// fp16 normals (the NF3 tables' entries are).
+__device__ __forceinline__ uint32_t bf16x2_to_h2(uint32_t u) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)));
+}
+
+// nf3_tables with fp16 entries holding the same bf16-rounded products.
+__device__ __forceinline__ void nf3_tables_h(float f, uint32_t &t01, uint32_t &t23) {
+  nf3_tables(f, t01, t23);
+  t01 = bf16x2_to_h2(t01);
+  t23 = bf16x2_to_h2(t23);
+}
+
+// nf3_step_rc selects whole 16-bit entries and ORs in bit 15, the sign bit of
+// fp16 as of bf16, so fp16 tables give the fp16 operand.
+__device__ __forceinline__ v8h nf3_step_h(uint32_t dsel, uint32_t d2, int s, uint32_t t01, uint32_t t23) {
+  return __builtin_bit_cast(v8h, nf3_step_rc(dsel, d2, s, t01, t23));
+}
+
+// Largest magnitude of eight bf16 (one 16-byte chunk), as fp32 bits.
+__device__ __forceinline__ uint32_t bf16x8_amax(v4i x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t u = (uint32_t)x[i] & 0x7FFF7FFFu;
+    m = max(m, max(u & 0xFFFFu, u >> 16));
+  }
+  return m << 16;
+}
+
+// Maximum over the 16 lanes of each row of the wave (every lane gets it):
+// rotations within the row by DPP, no LDS round trip.  All 16 lanes active.
+__device__ __forceinline__ uint32_t row16_max(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false));   // row_ror:8
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x124, 0xF, 0xF, false));   // row_ror:4
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x122, 0xF, 0xF, false));   // row_ror:2
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x121, 0xF, 0xF, false));   // row_ror:1
+  return m;
+}
+
+// The exponent e of a row whose largest magnitude has fp32 bits amax: the row
+// is converted as values * 2^-e, its largest then in [2^14, 2^15) (for a zero
+// or subnormal maximum, e = -141 keeps every value below 2^15).
+__device__ __forceinline__ int h_row_exp(uint32_t amax) { return (int)((amax >> 23) & 0xFFu) - 141; }
+
+// Two bf16 -> two fp16 of the values times 2^-e.
+__device__ __forceinline__ uint32_t bf16x2_to_h(uint32_t u, int e) {
+  const float lo = __builtin_amdgcn_ldexpf(__uint_as_float(u << 16), -e);
+  const float hi = __builtin_amdgcn_ldexpf(__uint_as_float(u & 0xFFFF0000u), -e);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// Eight bf16 -> eight fp16 of the values times 2^-e.
+__device__ __forceinline__ v4i bf16x8_to_h(v4i x, int e) {
+  v4i r;
+#pragma unroll
+  for (int i = 0; i < 4; i++) r[i] = (int)bf16x2_to_h((uint32_t)x[i], e);
+  return r;
+}
+
+// 2^d as an fp16 pair, for -24 <= d <= 0 (subnormal below 2^-14); 0 for d < -24.
+__device__ __forceinline__ v2h pow2_h2(int d) {
+  const uint32_t b = d >= -14 ? (uint32_t)(d + 15) << 10 : d >= -24 ? 1u << (d + 24) : 0u;
+  return __builtin_bit_cast(v2h, b | (b << 16));
+}
+
 // Dequantised operand of one lane for k-step s (0..3) of a 128-column k-tile.
 template <int WF>
 struct A16Tile {
@@ -326,6 +433,24 @@ struct A16Tile {
   __device__ __forceinline__ v8bf step(int s, const Deq &q) const {
     if (WF == W_NVFP4) return nvfp4_step(d[s], __uint_as_float(s < 2 ? q.u : q.v));
     return nf3_step_rc(s < 2 ? d[0] : d[1], d[2], s, q.u, q.v);
+  }
+  // fp16 forms: NVFP4 u = both scales as an fp16 pair; NF3 fp16 tables
+  __device__ __forceinline__ Deq prep_h() const {
+    Deq q;
+    if (WF == W_NVFP4) {
+      q.u = __builtin_bit_cast(uint32_t, e4m3x2_h(sc));
+      q.v = 0;
+    } else {
+      nf3_tables_h(e4m3_f32(sc & 0xFFu), q.u, q.v);
+    }
+    return q;
+  }
+  __device__ __forceinline__ v8h step_h(int s, const Deq &q) const {
+    if (WF == W_NVFP4) {
+      const v2h p = __builtin_bit_cast(v2h, q.u);
+      return nvfp4_step_h(d[s], s < 2 ? p.x : p.y);
+    }
+    return nf3_step_h(s < 2 ? d[0] : d[1], d[2], s, q.u, q.v);
   }
 };
 
