@@ -118,13 +118,13 @@ __device__ __forceinline__ DecExpert dec_expert(const DecArgs &a, int u) {
   return x;
 }
 
-// Fixed-order sum over the NW waves of the 16 GEMM1 accumulators, times 2^ex
-// (the route's fp16 activation exponent; 0 for MXFP8), clamped SwiGLU; returns
-// the 8 intermediate values of lane (route column c, group g): columns
-// 32*hb + 16*s + 4*g + i for s, i.
+// Fixed-order sum over the NW waves of the 16 GEMM1 accumulators, wave w's
+// times 2^ex[w] (its fp16 activation exponent for the lane's route; 0 for
+// MXFP8), clamped SwiGLU; returns the 8 intermediate values of lane (route
+// column c, group g): columns 32*hb + 16*s + 4*g + i for s, i.
 template <int NW>
 __device__ __forceinline__ void dec_swiglu(const float *red, int l, float gs, float limit, int has_limit, float alpha,
-                                           float beta, int act, int ex, float *h) {
+                                           float beta, int act, const int *ex, float *h) {
 #pragma unroll
   for (int s = 0; s < 2; s++)
 #pragma unroll
@@ -133,12 +133,9 @@ __device__ __forceinline__ void dec_swiglu(const float *red, int l, float gs, fl
       float up = 0.f, gate = 0.f;
 #pragma unroll 2
       for (int w = 0; w < NW; w++) {
-        up += red[(w * 16 + iu) * 64 + l];
-        gate += red[(w * 16 + ig) * 64 + l];
+        up += __builtin_amdgcn_ldexpf(red[(w * 16 + iu) * 64 + l], ex[w]);
+        gate += __builtin_amdgcn_ldexpf(red[(w * 16 + ig) * 64 + l], ex[w]);
       }
-      // sums of fp16 activations scaled by 2^-ex (0 for MXFP8) back to scale, then the global scale
-      up = __builtin_amdgcn_ldexpf(up, ex);
-      gate = __builtin_amdgcn_ldexpf(gate, ex);
       h[s * 4 + i] = silu_clamped(gate * gs, up * gs, limit, has_limit, alpha, beta, act);
     }
 }
@@ -219,11 +216,13 @@ __device__ __forceinline__ void a16w_mfma(const A16W<WF> &st, const uint16_t *xr
 }
 
 // Stage the activation rows of the pass's route columns into LDS: MXFP8 codes
-// and scales (W4A8), or (W4A16) the bf16 rows, then each row in place as fp16
-// times 2^-e with its exponent e (h_row_exp of the row's largest magnitude)
-// after the rows.
+// and scales (W4A8, the block's threads together), or (W4A16) fp16 rows.
+// W4A16: wave w stages only the columns of its own k-tiles (w, w + NW, ...),
+// the only ones it reads, as fp16 times 2^-e with e = h_row_exp of their
+// largest magnitude (xe[w][col]), so no wave waits for another.
 template <bool A8, int NW>
-__device__ __forceinline__ void dec_stage_x(const DecArgs &a, unsigned long long md, int p0, int ncol, uint8_t *dsm) {
+__device__ __forceinline__ void dec_stage_x(const DecArgs &a, unsigned long long md, int p0, int ncol, uint8_t *dsm,
+                                            int (*xe)[kDecodeMaxT]) {
   const int K = a.K, kb32 = K / 32, tid = threadIdx.x;
   if (A8) {
     const int xstride = K + 16;
@@ -243,26 +242,38 @@ __device__ __forceinline__ void dec_stage_x(const DecArgs &a, unsigned long long
       dst[1] = v4i{(int)codes[4], (int)codes[5], (int)codes[6], (int)codes[7]};
     }
   } else {
-    const int xstride = K + 8, n8 = K / 8;   // bf16 / fp16 elements, 8-element chunks per row
+    constexpr int kB = 4;   // chunks of 8 loaded per lane at once
+    const int w = tid >> 6, l = tid & 63, xstride = K + 8, nkt = K / 128;
+    const int nq = ((nkt - w + NW - 1) / NW) * 16;   // 16-byte chunks of this wave's k-tiles in a row
     uint16_t *xb = (uint16_t *)dsm;
-    uint32_t *xm = (uint32_t *)(dsm + (size_t)a.cpass * 2 * xstride);   // per-row largest magnitude
-    if (tid < ncol) xm[tid] = 0u;
-    __syncthreads();
-    // 16 consecutive chunks (n8 is a multiple of 16) lie in one row: their
-    // largest is reduced across the 16-lane row by DPP, then one LDS atomic
-    for (int i = tid; i < ncol * n8; i += NW * 64) {
-      const int col = i / n8, c8 = i - col * n8;
+    for (int col = 0; col < ncol; col++) {
       const int t = nth_bit(md, p0 + col) / a.topk;
-      const v4i v = *(const v4i *)(a.x + (size_t)t * K + c8 * 8);
-      *(v4i *)(xb + col * xstride + c8 * 8) = v;
-      const uint32_t m = row16_max(bf16x8_amax(v));
-      if ((tid & 15) == 0) atomicMax(&xm[col], m);
-    }
-    __syncthreads();
-    for (int i = tid; i < ncol * n8; i += NW * 64) {
-      const int col = i / n8;
-      v4i *q = (v4i *)(xb + col * xstride + (i - col * n8) * 8);
-      *q = bf16x8_to_h(*q, h_row_exp(xm[col]));
+      const uint16_t *src = a.x + (size_t)t * K;
+      uint16_t *dst = xb + col * xstride;
+      uint32_t m = 0;
+      for (int q0 = 0; q0 < nq; q0 += 64 * kB) {
+        v4i v[kB];
+#pragma unroll
+        for (int j = 0; j < kB; j++) {   // chunk q: k-tile w + NW * (q / 16), chunk q % 16 of it
+          const int q = q0 + l + 64 * j, e8 = ((q >> 4) * NW + w) * 128 + (q & 15) * 8;
+          v[j] = q < nq ? *(const v4i *)(src + e8) : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < kB; j++) {
+          const int q = q0 + l + 64 * j, e8 = ((q >> 4) * NW + w) * 128 + (q & 15) * 8;
+          if (q < nq) *(v4i *)(dst + e8) = v[j];
+          m = max(m, bf16x8_amax(v[j]));
+        }
+      }
+      m = row16_max(m);
+      m = max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
+              max((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
+      const int e = h_row_exp(m);
+      for (int q = l; q < nq; q += 64) {
+        v4i *p = (v4i *)(dst + ((q >> 4) * NW + w) * 128 + (q & 15) * 8);
+        *p = bf16x8_to_h(*p, e);
+      }
+      if (l == 0) xe[w][col] = e;
     }
   }
 }
@@ -284,6 +295,7 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
   rt.sstep = (uint32_t)rt_scales;
   const uint32_t lu = (uint32_t)l;
   float *red = (float *)dsm;   // after the k-loop: [NW waves][16][64]
+  __shared__ int xe[NW][kDecodeMaxT];   // W4A16: exponent of each wave's fp16 activation columns per route
   const int ncols = __popcll(md);
   for (int p0 = 0; p0 < ncols; p0 += a.cpass) {
     const int ncol = min(a.cpass, ncols - p0);
@@ -302,10 +314,8 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
       else a16w_load<WF>(st, rt, lu, kt, kt < nkt);
     };
     load(s0, w);
-    dec_stage_x<A8, NW>(a, md, p0, ncol, dsm);
-    __syncthreads();
-    // the column's activation exponent (fp16 rows only), read before LDS is reused
-    const int ex = (!A8 && have) ? h_row_exp(((const uint32_t *)(dsm + (size_t)a.cpass * 2 * (K + 8)))[c]) : 0;
+    dec_stage_x<A8, NW>(a, md, p0, ncol, dsm, xe);
+    if (A8) __syncthreads();   // W4A16: each wave reads only what it staged
     v4f acc[4];
 #pragma unroll
     for (int q = 0; q < 4; q++) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -331,6 +341,9 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
 #pragma unroll
       for (int i = 0; i < 4; i++) red[(w * 16 + q * 4 + i) * 64 + l] = acc[q][i];
     __syncthreads();
+    int ex[NW];   // the waves' activation exponents for the lane's column (fp16 rows only)
+#pragma unroll
+    for (int ww = 0; ww < NW; ww++) ex[ww] = (!A8 && have) ? xe[ww][c] : 0;
     if (!A8 && a.act == ACT_RELU2) {
       // ReLU^2 without the multiply: both halves' rows give their own columns,
       // each 32-column slice in fp16 with its exponent byte (as below)
@@ -348,8 +361,8 @@ __device__ __forceinline__ void dec_gemm1_body(const DecArgs &a, const DecExpert
               const int ir = (2 * s + half) * 4 + i;
               float v = 0.f;
 #pragma unroll 2
-              for (int ww = 0; ww < NW; ww++) v += red[(ww * 16 + ir) * 64 + l];
-              z[i] = relu2(__builtin_amdgcn_ldexpf(v, ex) * gs);
+              for (int ww = 0; ww < NW; ww++) v += __builtin_amdgcn_ldexpf(red[(ww * 16 + ir) * 64 + l], ex[ww]);
+              z[i] = relu2(v * gs);
             }
             o[s][half].x = pack_bf16x2(z[0], z[1]);
             o[s][half].y = pack_bf16x2(z[2], z[3]);
@@ -956,12 +969,12 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a16r(DecArgs a
 }
 
 int decode_cpass(int K, int a8) {
-  const int row = a8 ? K + 16 + K / 32 : 2 * (K + 8) + 4;   // W4A16: fp16 row + its exponent
+  const int row = a8 ? K + 16 + K / 32 : 2 * (K + 8);
   return max(1, min(kDecodeMaxT, kDecStageBytes / row));
 }
 
 size_t decode_gemm1_lds(int K, int cpass, int a8) {
-  const size_t stage = a8 ? (size_t)cpass * (K + 16) + (size_t)cpass * (K / 32) : (size_t)cpass * (2 * (K + 8) + 4);
+  const size_t stage = a8 ? (size_t)cpass * (K + 16) + (size_t)cpass * (K / 32) : (size_t)cpass * 2 * (K + 8);
   const size_t red = (size_t)4 * 16 * 64 * sizeof(float);
   return ((stage > red ? stage : red) + 15) & ~(size_t)15;
 }
