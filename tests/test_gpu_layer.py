@@ -566,3 +566,54 @@ def test_relu2_repack_round_trip():
     for t, k in zip(L.keep[:4], ("w13", "s13", "w2", "s2")):
         assert np.array_equal(t.cpu().numpy(), w[k]), k
     assert not torch.equal(before[0], L.keep[0].cpu())   # the tile layout differs from the checkpoint
+
+
+def _scale_bf16(x, e):
+    """bf16 bits times 2^e elementwise (e broadcast to x's shape); exact while the values stay bf16 normals."""
+    f = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64) * np.exp2(e)
+    b = f.astype(np.float32).view(np.uint32)
+    assert np.all(b & 0xFFFF == 0)
+    return (b >> 16).astype(np.uint16)
+
+
+# E4M3 scale bytes 448, 1, 2^-3 and 2^-6, one per 32-column slice of the intermediate in turn
+_SLICE_SCALES = np.array([0x7E, 0x38, 0x20, 0x08], dtype=np.uint8)
+
+
+def _wide_range_problem(name):
+    """A decode-size 16-bit layer whose token rows span 2^-16 .. 2^16 times the generator's values, with the
+    four k-tile classes of a row (k-tile index mod 4) a further 2^-8 .. 2^10 apart, and whose w13 scales put
+    the intermediate's 32-column slices up to about 2^30 apart within one row."""
+    p = SMALL[name]()
+    T, K, N = p.cfg.T, p.cfg.K, p.cfg.N
+    row_e = np.round(np.linspace(-16, 16, T))[:, None]
+    col_e = np.array([-8, -2, 4, 10])[(np.arange(K) // 128) % 4][None, :]
+    x = _scale_bf16(p.x, row_e + col_e)
+    tiers = []
+    for t in p.tiers:
+        w = dict(t.weights)
+        s13 = w["s13"].copy()
+        cls = _SLICE_SCALES[(np.arange(N) // 32) % 4]
+        s13[:, :N, :] = cls[None, :, None]   # up rows ([up; gate] stacking)
+        s13[:, N:, :] = cls[None, :, None]   # gate rows
+        w["s13"] = s13
+        tiers.append(dataclasses.replace(t, weights=w))
+    return I.Problem(p.cfg, x, p.ids, p.wts, tiers)
+
+
+@pytest.mark.parametrize("name", ["nvfp4_decode_n160", "nf3_decode_n352", "hybrid_decode"])
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_decode_fp16_operands_over_wide_ranges(name, deterministic):
+    """The 16-bit decode kernels multiply in fp16 on operands scaled by powers of two (per route row and
+    wave for the activations, per 32-column slice then per route row for the intermediate): rows far
+    outside fp16's range, waves of one row with different exponents, and intermediate slices from equal
+    to more than 24 binades apart all stay within the row tolerance of the oracle."""
+    prob = _wide_range_problem(name)
+    L = DeviceLayer(prob)
+    assert L.plan.sequence(prob.cfg.T) == M.SEQ_DECODE
+    out = L.run(deterministic=deterministic)
+    acc, _ = O.moe_problem(prob)
+    assert np.all(np.isfinite(acc))
+    mags = np.abs(acc).max(axis=1)
+    assert mags.max() / mags[mags > 0].min() > 2.0 ** 40   # the rows really span a wide range
+    assert_rows_match(out, acc, label=f"{name} wide det={deterministic}", prob=prob)
