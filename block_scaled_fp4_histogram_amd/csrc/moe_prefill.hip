@@ -324,9 +324,12 @@ __device__ __forceinline__ void zero_acc(v4f (*acc)[CB]) {
 // 4-byte pairs directly takes (each of those covers eight rows 32 bytes apart).
 // A wave's LDS reads and writes are done in order, so no wait or barrier is
 // needed between the two phases or before the next block overwrites them.
-template <int Q, int CB>
+// SE: the sums are of fp16 rows scaled by 2^-s_e[route]; they are multiplied
+// back by 2^s_e before the router weight.
+template <int Q, int CB, bool SE = false>
 __device__ __forceinline__ void pf_store_rb(const GemmArgs &a, const PfWork &wk, v4f (*acc)[CB], const int *s_r,
-                                            const float *s_w, size_t col0, int c, int g, uint8_t *lds) {
+                                            const float *s_w, size_t col0, int c, int g, uint8_t *lds,
+                                            const int *s_e = nullptr) {
   constexpr int RB = 32 * Q, RS = RB + 16, CH = RB / 16;   // row bytes, LDS row stride, 16-byte chunks a row
   const int l = threadIdx.x & 63;
   uint8_t *lw = lds + (threadIdx.x >> 6) * 16 * RS;
@@ -337,11 +340,16 @@ __device__ __forceinline__ void pf_store_rb(const GemmArgs &a, const PfWork &wk,
     for (int ip = 0; ip < 2; ip++) {
       const int rl = 4 * g + 2 * ip + (odd ? 1 : 0), row = 16 * cb + rl;
       const float wgt = row < wk.rows ? s_w[row] : 0.f;
+      const int er = (SE && row < wk.rows) ? s_e[row] : 0;
 #pragma unroll
       for (int q = 0; q < Q; q++) {
         const float mine = acc[q][cb][2 * ip + (odd ? 1 : 0)], give = acc[q][cb][2 * ip + (odd ? 0 : 1)];
         const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
-        const float lo = odd ? got : mine, hi = odd ? mine : got;
+        float lo = odd ? got : mine, hi = odd ? mine : got;
+        if constexpr (SE) {
+          lo = __builtin_amdgcn_ldexpf(lo, er);
+          hi = __builtin_amdgcn_ldexpf(hi, er);
+        }
         *(uint32_t *)(lw + rl * RS + 2 * ((c & ~1) + 16 * q)) = pack_bf16x2(wgt * lo, wgt * hi);
       }
     }
@@ -1084,11 +1092,37 @@ __device__ __forceinline__ void pf16_read_b(v4i (&b)[4][4], const Pf16Stage &S, 
 // activations are zeroed.  SWAP: activations as the A operand.
 // CVT: decode the scales with the one-instruction E4M3 convert (kernels with
 // the registers for it; in the 64-route ring kernels it raised the schedule to
-// about 300 VGPRs).
-template <int WF, bool SWAP, bool FULL, bool CVT = false>
+// about 300 VGPRs).  H: fp16 activations and fp16 weight operands (fp16 MFMA).
+template <int WF, bool SWAP, bool FULL, bool CVT = false, bool H = false>
 __device__ __forceinline__ void pf16_mma(const Pf16W &wt, const v4i (&b)[4][4], int kt, int kcols, int l,
                                          v4f (*acc)[4]) {
   const bool gin = FULL || kt * 128 + 32 * (l >> 4) < kcols;
+  if constexpr (H) {
+    v2h sp[2];
+    uint32_t t01[2] = {0u, 0u}, t23[2] = {0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const uint32_t sc = pf16_scale<WF>(wt.sc[q], l);
+      if constexpr (WF == W_NVFP4) sp[q] = e4m3x2_h(sc & 0xFFFFu);
+      else nf3_tables_h(e4m3_f32(sc & 0xFFu), t01[q], t23[q]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      v8h bop[4];
+#pragma unroll
+      for (int cb = 0; cb < 4; cb++) bop[cb] = __builtin_bit_cast(v8h, gin ? b[s][cb] : v4i{0, 0, 0, 0});
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        v8h aop;
+        if constexpr (WF == W_NVFP4) aop = nvfp4_step_h(wt.a[q][s], s < 2 ? sp[q].x : sp[q].y);
+        else aop = nf3_step_h(s < 2 ? wt.a[q][0] : wt.a[q][1], wt.a[q][2], s, t01[q], t23[q]);
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++)
+          acc[q][cb] = SWAP ? mfma_f16(bop[cb], aop, acc[q][cb]) : mfma_f16(aop, bop[cb], acc[q][cb]);
+      }
+    }
+    return;
+  }
   float slo[2] = {0.f, 0.f}, shi[2] = {0.f, 0.f};
   uint32_t t01[2] = {0u, 0u}, t23[2] = {0u, 0u};
 #pragma unroll
@@ -1580,7 +1614,8 @@ __global__ __launch_bounds__(256) void k_pf_gemm2_a16_tiers(GemmArgs a) {
 // The route-buffer combine's down GEMM as blocks of (64-route tile, run of
 // a.obg 128-column output blocks), as the W4A8 one: the tile's bf16
 // intermediate rows (all NKT k-tiles of N <= 128 NKT, 16 KB each) go into LDS
-// once, and each wave streams its two weight row tiles of every output block
+// once (NVFP4 tiles then convert them to fp16, below, and multiply in fp16:
+// NVFP4 prefill at 2048 tokens, down GEMM 211 -> 196 us), and each wave streams its two weight row tiles of every output block
 // of the run through a register ring of NKT k-tiles, so the next block's
 // weights are in flight while the current one is multiplied and stored.  (One
 // block per output block paid the rows' load, the perm lookups and the ring's
@@ -1589,6 +1624,7 @@ template <int NKT>
 struct Pf16ResLds {
   Pf16Stage st[NKT];
   uint8_t rb[4 * 16 * (32 * 2 + 16)];   // per-wave route-buffer staging (pf_store_rb)
+  int re[kPfTileRows];                   // each route's fp16 row exponent
 };
 
 // Weight and scale loads of row tiles rt0, rt0 + 1 (wave-uniform) for k-tile
@@ -1616,6 +1652,7 @@ template <int WF, int NKT, bool LASTFULL>
 __device__ __forceinline__ void pf16_gemm2_res_body(const GemmArgs &a, const PfWork &wk, const PfTier &T,
                                                     Pf16ResLds<NKT> &L, int *s_r, float *s_w) {
   constexpr int U = FmtGeom<WF>::unit, SU = FmtGeom<WF>::sunit;
+  constexpr bool H = WF == W_NVFP4;   // fp16 operands (one packed multiply a value pair in the decode)
   const int K = a.K, N = a.N, nob = K / 128, groups = N / 32;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -1653,6 +1690,34 @@ __device__ __forceinline__ void pf16_gemm2_res_body(const GemmArgs &a, const PfW
   wait_vm<4 * NKT>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
+  // NVFP4 (H): the staged bf16 rows in place as fp16 times 2^-e, e from each
+  // route's largest magnitude (h_row_exp; L.re for the epilogue).  Threads
+  // 4r .. 4r + 3 take route r's chunks, a quarter of every k-tile's 16 slots
+  // each, and meet by DPP; the slot order is rotated by r so that the 16 lanes
+  // of a read cover all 16 slots (no bank conflicts).  Chunks past N hold a
+  // copy of the row's first columns (harmless).  NF3 tiles stay bf16: their
+  // table decode costs the same in either type.
+  if constexpr (H) {
+    const int r = tid >> 2, qq = tid & 3;
+    uint32_t m = 0;
+#pragma unroll
+    for (int kt = 0; kt < NKT; kt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) m = max(m, bf16x8_amax(*(const v4i *)&L.st[kt].B[r][16 * (4 * qq + ((j + r) & 3))]));
+    m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    const int e = h_row_exp(m);
+#pragma unroll
+    for (int kt = 0; kt < NKT; kt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        v4i *p = (v4i *)&L.st[kt].B[r][16 * (4 * qq + ((j + r) & 3))];
+        *p = bf16x8_to_h(*p, e);
+      }
+    if (qq == 0) L.re[r] = e;
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  }
   for (int ob = ob0; ob < ob1; ob++) {
     asm volatile("" ::: "memory");   // keep the epilogue's LDS reads in the epilogue
     const bool next = ob + 1 < ob1;
@@ -1665,14 +1730,14 @@ __device__ __forceinline__ void pf16_gemm2_res_body(const GemmArgs &a, const PfW
       wait_vm<4 * (NKT - 1)>();   // slot kt has landed (the NKT - 1 later slots may be in flight)
       v4i b[4][4];
       pf16_read_b(b, L.st[kt], l);
-      if (kt < NKT - 1 || LASTFULL) pf16_mma<WF, true, true, true>(ring[kt], b, kt, N, l, acc);
-      else pf16_mma<WF, true, false, true>(ring[kt], b, kt, N, l, acc);
+      if (kt < NKT - 1 || LASTFULL) pf16_mma<WF, true, true, true, H>(ring[kt], b, kt, N, l, acc);
+      else pf16_mma<WF, true, false, true, H>(ring[kt], b, kt, N, l, acc);
       __builtin_amdgcn_sched_barrier(0);
       pf16_load_w_rt<WF>(ring[kt], src, rtn, kt, kt < NKT - 1 ? nd : ndl, kt < NKT - 1 ? ns : nsl);
       __builtin_amdgcn_sched_barrier(0);
     }
     // acc[q][cb][i]: route 16 cb + 4 g + i, output column 128 ob + 32 w + 16 q + c
-    pf_store_rb<2, 4>(a, wk, acc, s_r, s_w, (size_t)128 * ob + 32 * w, c, g, L.rb);
+    pf_store_rb<2, 4, H>(a, wk, acc, s_r, s_w, (size_t)128 * ob + 32 * w, c, g, L.rb, L.re);
   }
 }
 
