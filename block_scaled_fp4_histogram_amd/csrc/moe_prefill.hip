@@ -343,9 +343,13 @@ __device__ __forceinline__ void pf_store_rb(const GemmArgs &a, const PfWork &wk,
       const int er = (SE && row < wk.rows) ? s_e[row] : 0;
 #pragma unroll
       for (int q = 0; q < Q; q++) {
-        const float mine = acc[q][cb][2 * ip + (odd ? 1 : 0)], give = acc[q][cb][2 * ip + (odd ? 0 : 1)];
+        // even lane: lo = its a0, hi = the odd partner's a0; odd lane: lo = the
+        // even partner's a1, hi = its a1 (selects on two named elements: an
+        // element index that depends on the lane compiles to a 4-way chain)
+        const float a0 = acc[q][cb][2 * ip], a1 = acc[q][cb][2 * ip + 1];
+        const float give = odd ? a0 : a1;
         const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
-        float lo = odd ? got : mine, hi = odd ? mine : got;
+        float lo = odd ? got : a0, hi = odd ? a1 : got;
         if constexpr (SE) {
           lo = __builtin_amdgcn_ldexpf(lo, er);
           hi = __builtin_amdgcn_ldexpf(hi, er);
