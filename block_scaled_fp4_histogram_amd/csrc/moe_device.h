@@ -64,16 +64,19 @@ __device__ __forceinline__ float e4m3_f32_branched(uint32_t b) {
 // Otherwise the SwiGLU, with the limit clamps and the OAI alpha / beta.
 __device__ __forceinline__ float silu_clamped(float gate, float up, float limit, int has_limit, float alpha,
                                               float beta, int act = ACT_SWIGLU) {
+  // the sigmoid's reciprocal by v_rcp_f32 (1 ulp), not a correctly rounded
+  // division (about ten instructions): the prefill epilogues run it for every
+  // intermediate value
   if (act == ACT_SITU) {
     const float g = 4.0f * tanhf(0.25f * gate), u = 25.0f * tanhf(0.04f * up);
-    return g / (1.0f + __expf(-g)) * u;
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
   }
   if (has_limit) {
     gate = fminf(gate, limit);
     up = fminf(fmaxf(up, -limit), limit);
   }
   // alpha = 1, beta = 0: silu(gate) * up; otherwise the OAI form gate * sigmoid(alpha gate) * (up + beta)
-  return gate / (1.0f + __expf(-alpha * gate)) * (up + beta);
+  return gate * __builtin_amdgcn_rcpf(1.0f + __expf(-alpha * gate)) * (up + beta);
 }
 
 // ReLU^2 without the gate multiply (vLLM "fused_moe/b12x" page, RELU2_NO_MUL):
