@@ -306,7 +306,9 @@ def measure(M, prob, copies, deterministic, args, dev):
         "layer_mfma_frac": round(alg["layer_flops"] / (med * 1e-6) / 1e12 / mfma_peak, 4),
         "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
-        "dtype": "mxfp4*mxfp8->f32" if a8 else "bf16(dequant nvfp4/nf3)*bf16->f32",
+        "dtype": "mxfp4*mxfp8->f32" if a8 else (
+            "f16(dequant nvfp4/nf3)*f16(bf16 rows scaled by 2^-e)->f32" if sequence == "decode" else
+            "bf16(dequant nvfp4/nf3)*bf16->f32 (NVFP4 route-buffer down GEMM in f16)"),
     }
 
 
