@@ -149,8 +149,12 @@ void moe_experts_destroy(moe_experts_t experts);
 /*
  * moe_run -- the layer.
  *   tiers, n_tiers  1 or 2 groups of prepared experts (2 = hybrid: NVFP4 and
- *                   NF3 tiers, both through the bf16 path)
- *   x               bf16 [T, K] row-major
+ *                   NF3 tiers, both through the 16-bit-activation path)
+ *   x               bf16 [T, K] row-major.  16-bit-activation layers multiply
+ *                   in bf16, except the decode-size launches and the NVFP4
+ *                   route-buffer down GEMM, which multiply in fp16 on rows
+ *                   scaled by a power of two each (exact for every element at
+ *                   or above 2^-28 of its row's largest magnitude)
  *   topk_ids        int32 [T, top_k]; ids outside [0, E) are skipped
  *   topk_weights    fp32 [T, top_k]
  *   out             bf16 [T, K], fully overwritten
