@@ -617,3 +617,20 @@ def test_decode_fp16_operands_over_wide_ranges(name, deterministic):
     mags = np.abs(acc).max(axis=1)
     assert mags.max() / mags[mags > 0].min() > 2.0 ** 40   # the rows really span a wide range
     assert_rows_match(out, acc, label=f"{name} wide det={deterministic}", prob=prob)
+
+
+@pytest.mark.parametrize("name", ["nvfp4_prefill_small", "hybrid_prefill_small", "nvfp4_prefill_zipf"])
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_prefill_fp16_down_gemm_over_wide_ranges(name, deterministic):
+    """The NVFP4 route-buffer down GEMM converts each tile's intermediate rows to fp16 times a power of two
+    per route: token rows from 2^-16 to 2^16 times the generator's values (the intermediate then spans
+    about 2^64) stay within the row tolerance on the prefill sequence, NF3 tiles (bf16) alongside."""
+    prob = _wide_range_problem(name)
+    L = DeviceLayer(prob)
+    L.plan.set_sequence(prob.cfg.T, M.SEQ_PREFILL)
+    out = L.run(deterministic=deterministic)
+    acc, _ = O.moe_problem(prob)
+    assert np.all(np.isfinite(acc))
+    mags = np.abs(acc).max(axis=1)
+    assert mags.max() / mags[mags > 0].min() > 2.0 ** 40
+    assert_rows_match(out, acc, label=f"{name} wide det={deterministic}", prob=prob)
