@@ -26,16 +26,11 @@ __device__ __forceinline__ uint32_t mx_scale(float amax, float *inv_scale) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// fp32 -> bf16, nearest with ties to even: (u + 0x7FFF + bit 16 of u) >> 16
-// on the bits.  gfx950's v_cvt_pk_bf16_f32 gives exactly that for every
-// finite input, denormals and overflow to infinity included (compared over
-// all 2^32 bit patterns on the GPU), and converts two values in one
-// instruction, so the pair form uses it.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
+// Two fp32 -> two bf16 (low, high half), nearest with ties to even, i.e.
+// (u + 0x7FFF + bit 16 of u) >> 16 on each value's bits.  gfx950's
+// v_cvt_pk_bf16_f32 gives exactly that for every finite input, denormals and
+// overflow to infinity included (compared over all 2^32 bit patterns on the
+// GPU), in one instruction for the pair.
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{lo, hi}, v2bf));
