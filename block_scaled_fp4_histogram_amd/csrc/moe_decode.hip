@@ -588,9 +588,11 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
   extern __shared__ __align__(16) uint8_t dsm2[];
   __shared__ float tred[kDecG2WavesA8][4][64];
   __shared__ float wr_s[kDecodeMaxRoutes];
+  __shared__ __align__(16) uint8_t zb[64];   // zero operand bytes for absent routes and columns past N
   // wave-uniform values are pinned to scalar registers: derived from them, the
   // item bounds and weight descriptors stay scalar through the ring's branches
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, c = l & 15, g = l >> 4;
+  if (tid < 16) ((uint32_t *)zb)[tid] = 0u;
   const int K = a.K, N = a.N, nkt = (N + 127) / 128, rt = blockIdx.x;
   // expert groups (one per lane) and item offsets, from the up/gate kernel
   const DecGroups *G = a.groups;
@@ -663,15 +665,12 @@ __global__ __launch_bounds__(kDecG2WavesA8 * 64) void k_dec_gemm2_a8(DecArgs a) 
       if (base + s < i1) {
         if (s == 0 || ic.kt == 0 || base + s == i0)   // route of this lane's token in the current run
           r = dec_token_route(ic.md, ic.pass, c, a.T, a.topk);
+        // absent routes and columns past N read zero bytes (zb) instead of branching
         const int kb = ic.kt * 128;
-        v4i B0 = v4i{0, 0, 0, 0}, B1 = v4i{0, 0, 0, 0};
-        int sbv = 0;
-        if (r >= 0) {
-          const uint8_t *hrow = hq_s + r * (N + 16);
-          if (kb + 16 * g < N) B0 = *(const v4i *)(hrow + kb + 16 * g);
-          if (kb + 64 + 16 * g < N) B1 = *(const v4i *)(hrow + kb + 64 + 16 * g);
-          if (kb + 32 * g < N) sbv = hs_s[r * hs_stride(N) + kb / 32 + g];
-        }
+        const uint8_t *hrow = hq_s + (r >= 0 ? r : 0) * (N + 16);
+        const v4i B0 = *(const v4i *)(r >= 0 && kb + 16 * g < N ? hrow + kb + 16 * g : zb);
+        const v4i B1 = *(const v4i *)(r >= 0 && kb + 64 + 16 * g < N ? hrow + kb + 64 + 16 * g : zb);
+        const int sbv = *(r >= 0 && kb + 32 * g < N ? hs_s + (r >= 0 ? r : 0) * hs_stride(N) + kb / 32 + g : zb);
         const v8i bop = v8i{B0[0], B0[1], B0[2], B0[3], B1[0], B1[1], B1[2], B1[3]};
         acc = mfma_fp4_fp8(A[s], bop, acc, sa[s], sbv);
         if (ic.kt == nkt - 1 || base + s + 1 == i1) {
