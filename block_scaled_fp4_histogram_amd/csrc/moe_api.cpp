@@ -78,6 +78,7 @@ struct moe_experts_s {
   int w13_rows;           // 2N, or N for ReLU^2 without the multiply
   int wfmt, E;
   uint8_t *w13, *s13, *w2, *s2;
+  uint8_t *s2g;   // MXFP4, prepared: w2 scales in mx_soff's order for the prefill down GEMMs (owned)
   const float *g13, *g2;
   int prepared;
 };
@@ -500,7 +501,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     ga.w13 = xp->w13;
     ga.s13 = xp->s13;
     ga.w2 = xp->w2;
-    ga.s2 = xp->s2;
+    ga.s2 = prefill && xp->wfmt == MOE_W_MXFP4 ? xp->s2g : xp->s2;
     ga.g13 = xp->g13;
     ga.g2 = xp->g2;
     const int grid_tiles = row_tiles + std::min(xp->E, R);
@@ -522,17 +523,24 @@ void fmt_units(int wfmt, int *unit, int *sunit) {
 }
 
 // Rewrite the four tensors between checkpoint and tile layout, a batch of
-// experts at a time through a temporary device buffer.
+// experts at a time through a temporary device buffer.  Packing MXFP4 experts
+// also writes the prefill copy of the w2 scales (x->s2g, allocated here; its
+// entry comes before s2's, which it reads in checkpoint layout); unpacking
+// frees it.
 int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
   int unit, sunit;
   fmt_units(x->wfmt, &unit, &sunit);
+  const bool mx = x->wfmt == MOE_W_MXFP4 && to_tiles;
+  const size_t s2_bytes = (size_t)x->E * x->K * (x->N / 32);
+  if (mx && !x->s2g) HIP_TRY(hipMalloc(&x->s2g, s2_bytes));
   struct T {
-    uint8_t *buf;
-    int unit, rows, groups, pair;
-  } tensors[4] = {{x->w13, unit, x->w13_rows, x->K / 32, 1},
-                  {x->s13, sunit, x->w13_rows, x->K / 32, 1},
-                  {x->w2, unit, x->K, x->N / 32, 0},
-                  {x->s2, sunit, x->K, x->N / 32, 0}};
+    uint8_t *buf, *dst;   // dst: where the permuted bytes go (null: back into buf)
+    int unit, rows, groups, pair, mxs;
+  } tensors[5] = {{x->w13, nullptr, unit, x->w13_rows, x->K / 32, 1, 0},
+                  {x->s13, nullptr, sunit, x->w13_rows, x->K / 32, 1, 0},
+                  {x->w2, nullptr, unit, x->K, x->N / 32, 0, 0},
+                  {x->s2, mx ? x->s2g : nullptr, sunit, x->K, x->N / 32, 0, 1},
+                  {x->s2, nullptr, sunit, x->K, x->N / 32, 0, 0}};
   size_t max_exp = 0;
   for (auto &t : tensors) max_exp = std::max(max_exp, (size_t)t.rows * t.groups * t.unit);
   const size_t budget = (size_t)256 << 20;
@@ -546,14 +554,15 @@ int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
   HIP_TRY(hipMalloc(&tmp, batch * max_exp));
   int rc = MOE_OK;
   for (auto &t : tensors) {
+    if (t.mxs && !t.dst) continue;   // no prefill copy (not MXFP4, or unpacking)
     const size_t exp_bytes = (size_t)t.rows * t.groups * t.unit;
     for (long e0 = 0; e0 < x->E && rc == MOE_OK; e0 += batch) {
       const long ne = std::min<long>(batch, x->E - e0);
       uint8_t *base = t.buf + e0 * exp_bytes;
       hipError_t e = hipMemcpyAsync(tmp, base, ne * exp_bytes, hipMemcpyDeviceToDevice, s);
       if (e == hipSuccess)
-        e = moe::launch_permute(tmp, base, ne, t.unit, t.rows, t.groups, t.pair, x->w13_layout == MOE_W13_GATE_UP,
-                                to_tiles, s);
+        e = moe::launch_permute(tmp, t.dst ? t.dst + e0 * exp_bytes : base, ne, t.unit, t.rows, t.groups, t.pair,
+                                x->w13_layout == MOE_W13_GATE_UP, to_tiles, t.mxs, s);
       if (e != hipSuccess) rc = fail(MOE_EHIP, "weight permute: %s", hipGetErrorString(e));
     }
   }
@@ -566,6 +575,10 @@ int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess && rc == MOE_OK) rc = fail(MOE_EHIP, "weight permute sync: %s", hipGetErrorString(e));
   (void)hipFree(tmp);
+  if ((rc != MOE_OK || !to_tiles) && x->s2g) {
+    (void)hipFree(x->s2g);
+    x->s2g = nullptr;
+  }
   return rc;
 }
 
@@ -1058,12 +1071,14 @@ int moe_prepare_weights(moe_plan_t plan, int weight_format, int num_experts, voi
   x->s13 = (uint8_t *)s13;
   x->w2 = (uint8_t *)w2;
   x->s2 = (uint8_t *)s2;
+  x->s2g = nullptr;
   x->g13 = g13;
   x->g2 = g2;
   x->prepared = 0;
   const int rc = permute_all(x, 1, (hipStream_t)stream);
   if (rc != MOE_OK) {
     x->magic = 0;
+    if (x->s2g) (void)hipFree(x->s2g);
     delete x;
     return rc;
   }
@@ -1083,6 +1098,7 @@ int moe_unpack_weights(moe_experts_t x, void *stream) {
 void moe_experts_destroy(moe_experts_t x) {
   if (x && x->magic == kExpertsMagic) {
     x->magic = 0;
+    if (x->s2g) (void)hipFree(x->s2g);
     delete x;
   }
 }

@@ -27,6 +27,19 @@ enum Act { ACT_SWIGLU = 0, ACT_SITU = 1, ACT_RELU2 = 2 };
 // multiple of 4, so every row starts 4-byte aligned.
 __host__ __device__ constexpr int hs_stride(int N) { return (N / 32 + 3) & ~3; }
 
+// Prefill copy of the MXFP4 w2 scales: the bytes of one 16-row tile (E8M0, one per lane and k-tile; nkf =
+// the whole 128-column k-tiles of the reduction, a partial last one after
+// them): whole k-tiles in runs of four with each lane's four bytes in one
+// dword (lane-major), so that a wave loads the scales of four consecutive
+// k-tiles at once; whole k-tiles after the last run lane-major with as many
+// bytes a lane as there are of them; a partial last k-tile a byte a lane (its
+// first 16 * (32-column groups) lanes).  Byte offset of lane l of k-tile kt:
+__host__ __device__ constexpr uint32_t mx_soff(int kt, int l, int nkf) {
+  return kt < (nkf & ~3) ? (uint32_t)((kt >> 2) * 256 + l * 4 + (kt & 3))
+         : kt < nkf      ? (uint32_t)((nkf & ~3) * 64 + l * (nkf & 3) + (kt & 3))
+                         : (uint32_t)(nkf * 64 + l);
+}
+
 // LDS budget of the decode up/gate GEMM's staged token rows: six MXFP8 rows
 // at K = 7168 (one pass for every expert of an 8-token batch at top-6), and
 // three blocks per CU.
@@ -187,8 +200,9 @@ hipError_t launch_quant_f32(const float *h, long rows, int cols, uint8_t *q, uin
 //   pair   1 for w13: row tiles interleave up and gate halves
 //   gate_up 1 when the checkpoint stacks w13 as [gate; up]
 //   to_tiles 1 = checkpoint -> tile layout, 0 = back
+//   mxs    1: the k-tiles of a row tile in mx_soff's order (the prefill copy of MXFP4 w2 scales)
 hipError_t launch_nf3_recode(uint8_t *w, long units, int to_kernel, hipStream_t s);
 hipError_t launch_permute(const uint8_t *tmp, uint8_t *dst, long ne, int unit, int rows, int groups, int pair,
-                          int gate_up, int to_tiles, hipStream_t s);
+                          int gate_up, int to_tiles, int mxs, hipStream_t s);
 
 }  // namespace moe

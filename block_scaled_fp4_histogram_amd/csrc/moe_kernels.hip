@@ -361,8 +361,11 @@ hipError_t launch_quant_f32(const float *h, long rows, int cols, uint8_t *q, uin
 // (lane l = row + 16*q holds the 32 columns 128*kt + 32*q .. +31 of its row),
 // 16 bytes per lane for FP4.  The last k-tile of a row tile may hold fewer
 // 32-column groups (only its first 16*nq lanes exist).  Scales likewise, one
-// byte per lane.  w13 row tiles interleave up and gate: tile 2j = up rows
-// 16j..16j+15, tile 2j+1 = gate rows 16j..16j+15.
+// byte per lane.  MXFP4 experts also keep a second copy of the w2 scales, for
+// the prefill down GEMMs, with the k-tiles of a row tile in mx_soff's order (a
+// lane's bytes of four consecutive k-tiles in one dword).
+// w13 row tiles interleave up and gate: tile 2j = up rows 16j..16j+15, tile
+// 2j+1 = gate rows 16j..16j+15.
 
 // grid: x = N/32 (intermediate column blocks), y = tiles; 4 waves split K
 // (wave w takes k-tiles w, w+4, ...), loads double-buffered in registers.  At
@@ -766,14 +769,35 @@ hipError_t launch_ep_remap(const int32_t *ids, const float *w, long T, int topk,
 // ------------------------------------------------------------ repacker
 
 // Position, in the checkpoint layout, of byte `o` of the tile layout (both
-// within one expert).  See the weight tile layout above.
-__device__ __forceinline__ long ckpt_offset(long o, int unit, int rows, int groups, int pair, int gate_up) {
+// within one expert).  See the weight tile layout above; mxs: MXFP4 scales,
+// whose k-tiles are in mx_soff's order (one byte a lane).
+__device__ __forceinline__ long ckpt_offset(long o, int unit, int rows, int groups, int pair, int gate_up, int mxs) {
   const long rt_size = (long)16 * groups * unit;
   const long rt = o / rt_size;
   const long in_rt = o % rt_size;
-  const long kt = in_rt / (64L * unit);
-  const long rem = in_rt % (64L * unit);
-  const int lane = (int)(rem / unit), b = (int)(rem % unit);
+  long kt;
+  int lane, b;
+  if (mxs) {
+    // the inverse of mx_soff (unit 1)
+    const long nkf = groups / 4, g4 = nkf & ~3L;
+    b = 0;
+    if (in_rt < g4 * 64) {
+      kt = 4 * (in_rt / 256) + (in_rt & 3);
+      lane = (int)((in_rt & 255) >> 2);
+    } else if (in_rt < nkf * 64) {
+      const long r = nkf & 3, x = in_rt - g4 * 64;
+      kt = g4 + x % r;
+      lane = (int)(x / r);
+    } else {
+      kt = nkf;
+      lane = (int)(in_rt - nkf * 64);
+    }
+  } else {
+    kt = in_rt / (64L * unit);
+    const long rem = in_rt % (64L * unit);
+    lane = (int)(rem / unit);
+    b = (int)(rem % unit);
+  }
   const int r = lane & 15, q = lane >> 4;
   long row;
   if (pair) {
@@ -791,12 +815,12 @@ __device__ __forceinline__ long ckpt_offset(long o, int unit, int rows, int grou
 template <typename Word>
 __global__ __launch_bounds__(256) void k_permute(const uint8_t *tmp, uint8_t *dst, long total_words, long exp_bytes,
                                                  int unit, int rows, int groups, int pair, int gate_up,
-                                                 int to_tiles) {
+                                                 int to_tiles, int mxs) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= total_words) return;
   const long o = i * (long)sizeof(Word);
   const long e = o / exp_bytes, in_e = o % exp_bytes;
-  const long ck = e * exp_bytes + ckpt_offset(in_e, unit, rows, groups, pair, gate_up);
+  const long ck = e * exp_bytes + ckpt_offset(in_e, unit, rows, groups, pair, gate_up, mxs);
   if (to_tiles) *(Word *)(dst + o) = *(const Word *)(tmp + ck);
   else *(Word *)(dst + ck) = *(const Word *)(tmp + o);
 }
@@ -854,17 +878,17 @@ hipError_t launch_nf3_recode(uint8_t *w, long units, int to_kernel, hipStream_t 
 }
 
 hipError_t launch_permute(const uint8_t *tmp, uint8_t *dst, long ne, int unit, int rows, int groups, int pair,
-                          int gate_up, int to_tiles, hipStream_t s) {
+                          int gate_up, int to_tiles, int mxs, hipStream_t s) {
   const long exp_bytes = (long)rows * groups * unit;
   const long bytes = ne * exp_bytes;
   if (bytes == 0) return hipSuccess;
   if (unit % 4 == 0) {
     const long words = bytes / 4;
     hipLaunchKernelGGL(k_permute<uint32_t>, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, tmp, dst, words,
-                       exp_bytes, unit, rows, groups, pair, gate_up, to_tiles);
+                       exp_bytes, unit, rows, groups, pair, gate_up, to_tiles, mxs);
   } else {
     hipLaunchKernelGGL(k_permute<uint8_t>, dim3((unsigned)((bytes + 255) / 256)), dim3(256), 0, s, tmp, dst, bytes,
-                       exp_bytes, unit, rows, groups, pair, gate_up, to_tiles);
+                       exp_bytes, unit, rows, groups, pair, gate_up, to_tiles, mxs);
   }
   return hipGetLastError();
 }

@@ -108,7 +108,9 @@ struct PfSrc {
 // A wave's weight operands of one k-tile: row tiles 4w + q, and the aligned
 // scale dword holding this lane's byte (a narrower load would be zero-extended
 // where the ring is carried round the loop, which makes the compiler wait for
-// every load in flight there).
+// every load in flight there).  w2 scales are in mx_soff's order: within a
+// run of four whole k-tiles that dword holds the lane's bytes of all four, at
+// bit 8 * (kt % 4) (pf_scale_shift).
 struct PfW {
   v4i a[kPfQ];
   uint32_t sa[kPfQ];
@@ -124,9 +126,11 @@ struct PfW {
 // 268 -> 281 us at the Zipf-skewed 4096-token batch, the 64-route one
 // 577 -> 669 us).  The 128-route kernel takes them for blocks whose expert
 // fits the one tile (that batch: 271 -> 262 us), the 64-route one always.
-template <bool NT = false>
+// MX: w2 scales (mx_soff's order), else w13 (k-tile-major).
+template <bool NT = false, bool MX = false>
 __device__ __forceinline__ void pf_load_w(PfW &r, const PfSrc &src, int kt, int w, int l) {
   const bool in = (kt * 4 + (l >> 4)) * 32 < src.kbytes;
+  const uint32_t sv = MX ? mx_soff(kt, l, src.kbytes >> 7) & ~3u : (uint32_t)(kt * 64 + (l & ~3));
 #pragma unroll
   for (int q = 0; q < kPfQ; q++) {
     const int rt = 4 * w + q;
@@ -134,8 +138,13 @@ __device__ __forceinline__ void pf_load_w(PfW &r, const PfSrc &src, int kt, int 
     const uint32_t so = rt < src.nrt ? (uint32_t)rt : 0u;
     const uint32_t vo = ok ? (uint32_t)(kt * 1024 + l * 16) : 0x80000000u;
     r.a[q] = NT ? buf_load16_nt(src.wb, vo, so * src.wstep) : buf_load16(src.wb, vo, so * src.wstep);
-    r.sa[q] = buf_load4(src.sb, ok ? (uint32_t)(kt * 64 + (l & ~3)) : 0x80000000u, so * src.sstep);
+    r.sa[q] = buf_load4(src.sb, ok ? sv : 0x80000000u, so * src.sstep);
   }
+}
+
+// Bit position of lane l's w2 scale byte of k-tile kt in its slot's dword.
+__device__ __forceinline__ int pf_scale_shift(int kt, int l, int kbytes) {
+  return 8 * (int)(mx_soff(kt, l, kbytes >> 7) & 3u);
 }
 
 // The shared loads of wave w for k-tile kt into stage S: activation blocks 2w,
@@ -197,7 +206,7 @@ __device__ __forceinline__ void pf_read_b(v4i (&b)[4][2], int (&sb)[4], const Pf
 // column, elements = 4 routes).
 template <bool SWAP, bool FULL>
 __device__ __forceinline__ void pf_mma(const PfW &wt, const v4i (&b)[4][2], const int (&sb)[4], int kt, int kbytes,
-                                       int nrb, int l, v4f (*acc)[4]) {
+                                       int nrb, int l, v4f (*acc)[4], const uint32_t *sa_src = nullptr) {
   const int g = l >> 4;
   const bool in0 = FULL || kt * 128 + 16 * g < kbytes, in1 = FULL || kt * 128 + 64 + 16 * g < kbytes;
   const bool gin = FULL || (kt * 4 + g) * 32 < kbytes;   // 32-column group g of this k-tile exists
@@ -211,8 +220,10 @@ __device__ __forceinline__ void pf_mma(const PfW &wt, const v4i (&b)[4][2], cons
   // route blocks past the tile's last route hold padding: their MFMAs are skipped,
   // one branch per route block (4 MFMAs)
   int sa[kPfQ];
+  const uint32_t *sap = sa_src ? sa_src : wt.sa;
+  const int sh = SWAP ? pf_scale_shift(kt, l, kbytes) : 8 * (l & 3);   // SWAP: the down GEMM (w2 scales)
 #pragma unroll
-  for (int q = 0; q < kPfQ; q++) sa[q] = gin ? (int)(wt.sa[q] >> (8 * (l & 3))) : 0;   // the MFMA takes the low byte
+  for (int q = 0; q < kPfQ; q++) sa[q] = gin ? (int)(sap[q] >> sh) : 0;   // the MFMA takes the low byte
 #pragma unroll
   for (int cb = 0; cb < 4; cb++) {
     if (cb < nrb) {
@@ -251,7 +262,7 @@ __device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, PfW (&ring)[
   const int kn = kt + ST - 1;
   if (ISSUE == 1 || (ISSUE == -1 && kn < nkt)) {
     // one branch-free load sequence keeps the compiler's waits exact
-    pf_load_w<NT>(ring[(R + ST - 1) % ST], src, kn, w, l);
+    pf_load_w<NT, SWAP>(ring[(R + ST - 1) % ST], src, kn, w, l);
     pf_issue_b(L.st[kn % ST], src, kn, w, l);
   }
   v4i b[4][2];
@@ -285,7 +296,7 @@ __device__ __forceinline__ void pf_kloop(PfLds &L, const PfSrc &src, int w, v4f 
   // keeps the compiler's bookkeeping of the ring registers exact
 #pragma unroll
   for (int s = 0; s < ST - 1; s++) {
-    pf_load_w<NT>(ring[s], src, s, w, l);
+    pf_load_w<NT, SWAP>(ring[s], src, s, w, l);
     pf_issue_b(L.st[s], src, s, w, l);
   }
   int kt = 0;
@@ -747,7 +758,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8_short(GemmArgs a) {
   PfW wt[NKT];
 #pragma unroll
   for (int kt = 0; kt < NKT; kt++) {
-    pf_load_w(wt[kt], src, kt, wu, l);
+    pf_load_w<false, true>(wt[kt], src, kt, wu, l);
     pf_issue_b(L.st[kt], src, kt, wu, l);
   }
   v4f acc[kPfQ][4];
@@ -803,15 +814,29 @@ struct PfResLds {
 // traffic) for loads past the run or lanes past the reduction length; the
 // k-tile's own offset goes into the scalar offset, so one lane offset serves
 // every k-tile.
+// son: the scale loads are in range.  skip: this k-tile's scale bytes are in
+// the dword of its run's first k-tile, which the caller keeps: no scale load
+// (pf_res_loads counts the loads of a slot).
 template <bool NT = false>   // NT: non-temporal weight loads
-__device__ __forceinline__ void pf_load_w_rt(PfW &r, const PfSrc &src, uint32_t rt0, int kt, uint32_t vd,
-                                             uint32_t vs) {
+__device__ __forceinline__ void pf_load_w_rt(PfW &r, const PfSrc &src, uint32_t rt0, int kt, uint32_t vd, bool son,
+                                             bool skip, int l) {
+  const uint32_t vs = son ? (mx_soff(kt, l, src.kbytes >> 7) & ~3u) : 0x80000000u;
 #pragma unroll
   for (int q = 0; q < kPfQ; q++) {
     const uint32_t so = (rt0 + q) * src.wstep + (uint32_t)kt * 1024u;
     r.a[q] = NT ? buf_load16_nt(src.wb, vd, so) : buf_load16(src.wb, vd, so);
-    r.sa[q] = buf_load4(src.sb, vs, (rt0 + q) * src.sstep + (uint32_t)kt * 64u);
+    if (!skip) r.sa[q] = buf_load4(src.sb, vs, (rt0 + q) * src.sstep);
   }
+}
+
+// Loads of ring slot kt (kt < 0: of every slot) for a reduction of NKF whole
+// k-tiles in NKT: the weights, and the scales outside a run's later k-tiles.
+template <int NKT, int NKF>
+__host__ __device__ constexpr int pf_res_loads(int kt) {
+  if (kt >= 0) return kPfQ * ((kt < (NKF & ~3) && (kt & 3) != 0) ? 1 : 2);
+  int n = 0;
+  for (int k = 0; k < NKT; k++) n += pf_res_loads<NKT, NKF>(k);
+  return n;
 }
 
 // One block's work.
@@ -850,13 +875,17 @@ __device__ __forceinline__ void pf_res_body(PfResLds<NKT> &L, const GemmArgs &a,
   // lane offsets inside a k-tile.  The lanes of a partial last k-tile past N
   // load the next row tile's bytes (or zeros past the expert): E2M1 codes are
   // finite, and the MFMA step zeroes their activations and scales.
-  const uint32_t kOut = 0x80000000u, vd = (uint32_t)(l * 16), vs = (uint32_t)(l & ~3);
+  const uint32_t kOut = 0x80000000u, vd = (uint32_t)(l * 16);
+  // whole k-tiles of the reduction; those in runs of four (scale bytes of a
+  // run in one dword a lane: loaded with the run's first k-tile)
+  constexpr int NKF = LASTFULL ? NKT : NKT - 1, G4 = NKF & ~3;
   PfW ring[NKT];
 #pragma unroll
-  for (int kt = 0; kt < NKT; kt++) pf_load_w_rt<NT>(ring[kt], src, (uint32_t)(16 * ob0 + 4 * wu), kt, vd, vs);
+  for (int kt = 0; kt < NKT; kt++)
+    pf_load_w_rt<NT>(ring[kt], src, (uint32_t)(16 * ob0 + 4 * wu), kt, vd, true, kt < G4 && (kt & 3) != 0, l);
   // the rows have landed once only the weight loads may be in flight; then
   // every wave's share (and s_r / s_w) is visible
-  wait_vm<2 * kPfQ * NKT>();
+  wait_vm<pf_res_loads<NKT, NKF>(-1)>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   for (int ob = ob0; ob < ob1; ob++) {
@@ -865,26 +894,34 @@ __device__ __forceinline__ void pf_res_body(PfResLds<NKT> &L, const GemmArgs &a,
     asm volatile("" ::: "memory");
     const bool next = ob + 1 < ob1;
     const uint32_t rtn = (uint32_t)(16 * (next ? ob + 1 : ob) + 4 * wu);
-    const uint32_t nd = next ? vd : kOut, ns = next ? vs : kOut;
+    const uint32_t nd = next ? vd : kOut;
     v4f acc[kPfQ][4];
     zero_acc<kPfQ, 4>(acc);
+    uint32_t srun[kPfQ];   // this output block's scale dwords of the current run of four k-tiles
 #pragma unroll
     for (int kt = 0; kt < NKT; kt++) {
-      // slot kt holds this block's k-tile kt once at most the NKT - 1 slots
-      // issued after it are in flight (stores in between only add to the count)
-      wait_vm<2 * kPfQ * (NKT - 1)>();
+      // slot kt holds this block's k-tile kt once at most the loads of the NKT - 1
+      // slots issued after it are in flight (stores in between only add to the count)
+      constexpr int TOT = pf_res_loads<NKT, NKF>(-1);
+      if (kt < G4 && (kt & 3) != 0) wait_vm<TOT - kPfQ>();
+      else wait_vm<TOT - 2 * kPfQ>();
       v4i b[4][2];
       int sb[4];
       pf_read_b(b, sb, L.st[kt], l);
+      const bool run = kt < G4;
+      if (run && (kt & 3) == 0) {
+#pragma unroll
+        for (int q = 0; q < kPfQ; q++) srun[q] = ring[kt].sa[q];   // kept past the slot's reload
+      }
       __builtin_amdgcn_s_setprio(1);
-      if (kt < NKT - 1 || LASTFULL) pf_mma<true, true>(ring[kt], b, sb, kt, N, src.nrb, l, acc);
-      else pf_mma<true, false>(ring[kt], b, sb, kt, N, src.nrb, l, acc);
+      if (kt < NKT - 1 || LASTFULL) pf_mma<true, true>(ring[kt], b, sb, kt, N, src.nrb, l, acc, run ? srun : nullptr);
+      else pf_mma<true, false>(ring[kt], b, sb, kt, N, src.nrb, l, acc, run ? srun : nullptr);
       __builtin_amdgcn_s_setprio(0);
       // the next output block's k-tile kt into the slot the MFMAs above read; issued after
       // them (hoisted above, the loads would need a second register set and spill), and no
       // step is interleaved with the next for the same reason
       __builtin_amdgcn_sched_barrier(0);
-      pf_load_w_rt<NT>(ring[kt], src, rtn, kt, nd, ns);
+      pf_load_w_rt<NT>(ring[kt], src, rtn, kt, nd, next, run && (kt & 3) != 0, l);
       __builtin_amdgcn_sched_barrier(0);
     }
     // acc[q][cb][i]: route 16 cb + 4 g + i, output column 256 ob + 64 w + 16 q + c

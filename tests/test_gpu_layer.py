@@ -634,3 +634,23 @@ def test_prefill_fp16_down_gemm_over_wide_ranges(name, deterministic):
     mags = np.abs(acc).max(axis=1)
     assert mags.max() / mags[mags > 0].min() > 2.0 ** 40
     assert_rows_match(out, acc, label=f"{name} wide det={deterministic}", prob=prob)
+
+
+# MXFP4 w2 scales are stored per row tile in runs of four whole k-tiles (a lane's four
+# bytes in one dword), then the whole k-tiles after the last run, then a partial last
+# k-tile: down-projection widths with two runs and a partial k-tile (1088), a run and a
+# tail of three (896), and two runs, a tail of two and a partial k-tile (1344), through
+# every launch sequence.
+@pytest.mark.parametrize("N", [896, 1088, 1344])
+@pytest.mark.parametrize("seq", [M.SEQ_DECODE, M.SEQ_GENERAL, M.SEQ_PREFILL, M.SEQ_PREFILL_NARROW])
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_mxfp4_down_scale_runs(N, seq, deterministic):
+    T = 6 if seq == M.SEQ_DECODE else 96
+    prob = I.make_problem(I.Config(f"mxfp4_n{N}", T=T, E=4, K=256, N=N, topk=2, limit=7.0, fmt=I.FMT_MXFP4,
+                                   e8m0_exp=(-7, -3)), seed=N + T)
+    L = DeviceLayer(prob)
+    L.plan.set_sequence(T, seq)
+    assert L.plan.sequence(T) == seq
+    out = L.run(deterministic=deterministic)
+    acc, _ = O.moe_problem(prob)
+    assert_rows_match(out, acc, label=f"mxfp4 N={N} sequence {seq} det={deterministic}", prob=prob)

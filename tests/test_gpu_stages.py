@@ -121,7 +121,8 @@ def test_route_bitexact(name):
 
 @pytest.mark.parametrize("fmt,gate_up", [(I.FMT_MXFP4, False), (I.FMT_MXFP4, True), (I.FMT_NVFP4, False),
                                          (I.FMT_NF3, False)])
-@pytest.mark.parametrize("geom", [(8, 256, 128), (3, 512, 96), (2, 7168, 576)])
+# (E, K, N); N = 896 / 1344: MXFP4 w2 scales with a tail of whole k-tiles after the runs of four
+@pytest.mark.parametrize("geom", [(8, 256, 128), (3, 512, 96), (2, 7168, 576), (2, 256, 896), (2, 256, 1344)])
 def test_repack_roundtrip_bitexact(fmt, gate_up, geom):
     E, K, N = geom
     w = I.make_weights(fmt, E, K, N, seed=E + K)
