@@ -78,7 +78,7 @@ struct moe_experts_s {
   int w13_rows;           // 2N, or N for ReLU^2 without the multiply
   int wfmt, E;
   uint8_t *w13, *s13, *w2, *s2;
-  uint8_t *s2g;   // MXFP4, prepared: w2 scales in mx_soff's order for the prefill down GEMMs (owned)
+  uint8_t *s13g, *s2g;   // MXFP4, prepared: the scales in mx_soff's order for the prefill GEMMs (owned)
   const float *g13, *g2;
   int prepared;
 };
@@ -472,7 +472,7 @@ int run_chunk(const moe_plan_s *p, const moe_tier *tiers, int n_tiers, const uin
     ga.tier = i;
     ga.u_base = u_base;
     ga.w13 = xp->w13;
-    ga.s13 = xp->s13;
+    ga.s13 = prefill && xp->wfmt == MOE_W_MXFP4 ? xp->s13g : xp->s13;
     ga.w2 = xp->w2;
     ga.s2 = xp->s2;
     ga.g13 = xp->g13;
@@ -522,21 +522,29 @@ void fmt_units(int wfmt, int *unit, int *sunit) {
   *sunit = (wfmt == MOE_W_NVFP4) ? 2 : 1;
 }
 
+void free_prefill_scales(moe_experts_s *x) {
+  for (uint8_t **p : {&x->s13g, &x->s2g}) {
+    if (*p) (void)hipFree(*p);
+    *p = nullptr;
+  }
+}
+
 // Rewrite the four tensors between checkpoint and tile layout, a batch of
 // experts at a time through a temporary device buffer.  Packing MXFP4 experts
-// also writes the prefill copy of the w2 scales (x->s2g, allocated here; its
-// entry comes before s2's, which it reads in checkpoint layout); unpacking
-// frees it.
+// also writes the prefill copies of the scales (x->s13g, x->s2g, allocated
+// here; their entries come before those that repack the scales themselves,
+// so they read the checkpoint layout); unpacking frees them.
 int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
   int unit, sunit;
   fmt_units(x->wfmt, &unit, &sunit);
   const bool mx = x->wfmt == MOE_W_MXFP4 && to_tiles;
-  const size_t s2_bytes = (size_t)x->E * x->K * (x->N / 32);
-  if (mx && !x->s2g) HIP_TRY(hipMalloc(&x->s2g, s2_bytes));
+  if (mx && !x->s13g) HIP_TRY(hipMalloc(&x->s13g, (size_t)x->E * x->w13_rows * (x->K / 32)));
+  if (mx && !x->s2g) HIP_TRY(hipMalloc(&x->s2g, (size_t)x->E * x->K * (x->N / 32)));
   struct T {
     uint8_t *buf, *dst;   // dst: where the permuted bytes go (null: back into buf)
     int unit, rows, groups, pair, mxs;
-  } tensors[5] = {{x->w13, nullptr, unit, x->w13_rows, x->K / 32, 1, 0},
+  } tensors[6] = {{x->w13, nullptr, unit, x->w13_rows, x->K / 32, 1, 0},
+                  {x->s13, mx ? x->s13g : nullptr, sunit, x->w13_rows, x->K / 32, 1, 1},
                   {x->s13, nullptr, sunit, x->w13_rows, x->K / 32, 1, 0},
                   {x->w2, nullptr, unit, x->K, x->N / 32, 0, 0},
                   {x->s2, mx ? x->s2g : nullptr, sunit, x->K, x->N / 32, 0, 1},
@@ -575,10 +583,7 @@ int permute_all(moe_experts_s *x, int to_tiles, hipStream_t s) {
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess && rc == MOE_OK) rc = fail(MOE_EHIP, "weight permute sync: %s", hipGetErrorString(e));
   (void)hipFree(tmp);
-  if ((rc != MOE_OK || !to_tiles) && x->s2g) {
-    (void)hipFree(x->s2g);
-    x->s2g = nullptr;
-  }
+  if (rc != MOE_OK || !to_tiles) free_prefill_scales(x);
   return rc;
 }
 
@@ -1071,14 +1076,14 @@ int moe_prepare_weights(moe_plan_t plan, int weight_format, int num_experts, voi
   x->s13 = (uint8_t *)s13;
   x->w2 = (uint8_t *)w2;
   x->s2 = (uint8_t *)s2;
-  x->s2g = nullptr;
+  x->s13g = x->s2g = nullptr;
   x->g13 = g13;
   x->g2 = g2;
   x->prepared = 0;
   const int rc = permute_all(x, 1, (hipStream_t)stream);
   if (rc != MOE_OK) {
     x->magic = 0;
-    if (x->s2g) (void)hipFree(x->s2g);
+    free_prefill_scales(x);
     delete x;
     return rc;
   }
@@ -1098,7 +1103,7 @@ int moe_unpack_weights(moe_experts_t x, void *stream) {
 void moe_experts_destroy(moe_experts_t x) {
   if (x && x->magic == kExpertsMagic) {
     x->magic = 0;
-    if (x->s2g) (void)hipFree(x->s2g);
+    free_prefill_scales(x);
     delete x;
   }
 }

@@ -27,7 +27,7 @@ enum Act { ACT_SWIGLU = 0, ACT_SITU = 1, ACT_RELU2 = 2 };
 // multiple of 4, so every row starts 4-byte aligned.
 __host__ __device__ constexpr int hs_stride(int N) { return (N / 32 + 3) & ~3; }
 
-// Prefill copy of the MXFP4 w2 scales: the bytes of one 16-row tile (E8M0, one per lane and k-tile; nkf =
+// Prefill copies of the MXFP4 scales: the bytes of one 16-row tile (E8M0, one per lane and k-tile; nkf =
 // the whole 128-column k-tiles of the reduction, a partial last one after
 // them): whole k-tiles in runs of four with each lane's four bytes in one
 // dword (lane-major), so that a wave loads the scales of four consecutive
@@ -200,7 +200,7 @@ hipError_t launch_quant_f32(const float *h, long rows, int cols, uint8_t *q, uin
 //   pair   1 for w13: row tiles interleave up and gate halves
 //   gate_up 1 when the checkpoint stacks w13 as [gate; up]
 //   to_tiles 1 = checkpoint -> tile layout, 0 = back
-//   mxs    1: the k-tiles of a row tile in mx_soff's order (the prefill copy of MXFP4 w2 scales)
+//   mxs    1: the k-tiles of a row tile in mx_soff's order (the prefill copies of MXFP4 scales)
 hipError_t launch_nf3_recode(uint8_t *w, long units, int to_kernel, hipStream_t s);
 hipError_t launch_permute(const uint8_t *tmp, uint8_t *dst, long ne, int unit, int rows, int groups, int pair,
                           int gate_up, int to_tiles, int mxs, hipStream_t s);

@@ -361,8 +361,8 @@ hipError_t launch_quant_f32(const float *h, long rows, int cols, uint8_t *q, uin
 // (lane l = row + 16*q holds the 32 columns 128*kt + 32*q .. +31 of its row),
 // 16 bytes per lane for FP4.  The last k-tile of a row tile may hold fewer
 // 32-column groups (only its first 16*nq lanes exist).  Scales likewise, one
-// byte per lane.  MXFP4 experts also keep a second copy of the w2 scales, for
-// the prefill down GEMMs, with the k-tiles of a row tile in mx_soff's order (a
+// byte per lane.  MXFP4 experts also keep second copies of the scales, for
+// the prefill GEMMs, with the k-tiles of a row tile in mx_soff's order (a
 // lane's bytes of four consecutive k-tiles in one dword).
 // w13 row tiles interleave up and gate: tile 2j = up rows 16j..16j+15, tile
 // 2j+1 = gate rows 16j..16j+15.

@@ -108,9 +108,9 @@ struct PfSrc {
 // A wave's weight operands of one k-tile: row tiles 4w + q, and the aligned
 // scale dword holding this lane's byte (a narrower load would be zero-extended
 // where the ring is carried round the loop, which makes the compiler wait for
-// every load in flight there).  w2 scales are in mx_soff's order: within a
-// run of four whole k-tiles that dword holds the lane's bytes of all four, at
-// bit 8 * (kt % 4) (pf_scale_shift).
+// every load in flight there).  The scales are the prefill copies, in
+// mx_soff's order: within a run of four whole k-tiles that dword holds the
+// lane's bytes of all four, at bit 8 * (kt % 4) (pf_scale_shift).
 struct PfW {
   v4i a[kPfQ];
   uint32_t sa[kPfQ];
@@ -126,11 +126,14 @@ struct PfW {
 // 268 -> 281 us at the Zipf-skewed 4096-token batch, the 64-route one
 // 577 -> 669 us).  The 128-route kernel takes them for blocks whose expert
 // fits the one tile (that batch: 271 -> 262 us), the 64-route one always.
-// MX: w2 scales (mx_soff's order), else w13 (k-tile-major).
-template <bool NT = false, bool MX = false>
-__device__ __forceinline__ void pf_load_w(PfW &r, const PfSrc &src, int kt, int w, int l) {
+// REUSE: kt lies inside a run of four whole k-tiles, past its first, and prev
+// is the landed slot of k-tile kt - 1, whose scale dword holds this k-tile's
+// bytes too: it is copied and no scale load is issued (for callers that wait
+// for every load).
+template <bool NT = false, bool REUSE = false>
+__device__ __forceinline__ void pf_load_w(PfW &r, const PfSrc &src, int kt, int w, int l, const PfW *prev = nullptr) {
   const bool in = (kt * 4 + (l >> 4)) * 32 < src.kbytes;
-  const uint32_t sv = MX ? mx_soff(kt, l, src.kbytes >> 7) & ~3u : (uint32_t)(kt * 64 + (l & ~3));
+  const uint32_t sv = mx_soff(kt, l, src.kbytes >> 7) & ~3u;
 #pragma unroll
   for (int q = 0; q < kPfQ; q++) {
     const int rt = 4 * w + q;
@@ -138,11 +141,12 @@ __device__ __forceinline__ void pf_load_w(PfW &r, const PfSrc &src, int kt, int 
     const uint32_t so = rt < src.nrt ? (uint32_t)rt : 0u;
     const uint32_t vo = ok ? (uint32_t)(kt * 1024 + l * 16) : 0x80000000u;
     r.a[q] = NT ? buf_load16_nt(src.wb, vo, so * src.wstep) : buf_load16(src.wb, vo, so * src.wstep);
-    r.sa[q] = buf_load4(src.sb, ok ? sv : 0x80000000u, so * src.sstep);
+    if constexpr (REUSE) r.sa[q] = prev->sa[q];
+    else r.sa[q] = buf_load4(src.sb, ok ? sv : 0x80000000u, so * src.sstep);
   }
 }
 
-// Bit position of lane l's w2 scale byte of k-tile kt in its slot's dword.
+// Bit position of lane l's scale byte of k-tile kt in its slot's dword.
 __device__ __forceinline__ int pf_scale_shift(int kt, int l, int kbytes) {
   return 8 * (int)(mx_soff(kt, l, kbytes >> 7) & 3u);
 }
@@ -221,7 +225,7 @@ __device__ __forceinline__ void pf_mma(const PfW &wt, const v4i (&b)[4][2], cons
   // one branch per route block (4 MFMAs)
   int sa[kPfQ];
   const uint32_t *sap = sa_src ? sa_src : wt.sa;
-  const int sh = SWAP ? pf_scale_shift(kt, l, kbytes) : 8 * (l & 3);   // SWAP: the down GEMM (w2 scales)
+  const int sh = pf_scale_shift(kt, l, kbytes);
 #pragma unroll
   for (int q = 0; q < kPfQ; q++) sa[q] = gin ? (int)(sap[q] >> sh) : 0;   // the MFMA takes the low byte
 #pragma unroll
@@ -262,7 +266,7 @@ __device__ __forceinline__ void pf_step(PfLds &L, const PfSrc &src, PfW (&ring)[
   const int kn = kt + ST - 1;
   if (ISSUE == 1 || (ISSUE == -1 && kn < nkt)) {
     // one branch-free load sequence keeps the compiler's waits exact
-    pf_load_w<NT, SWAP>(ring[(R + ST - 1) % ST], src, kn, w, l);
+    pf_load_w<NT>(ring[(R + ST - 1) % ST], src, kn, w, l);
     pf_issue_b(L.st[kn % ST], src, kn, w, l);
   }
   v4i b[4][2];
@@ -296,7 +300,7 @@ __device__ __forceinline__ void pf_kloop(PfLds &L, const PfSrc &src, int w, v4f 
   // keeps the compiler's bookkeeping of the ring registers exact
 #pragma unroll
   for (int s = 0; s < ST - 1; s++) {
-    pf_load_w<NT, SWAP>(ring[s], src, s, w, l);
+    pf_load_w<NT>(ring[s], src, s, w, l);
     pf_issue_b(L.st[s], src, s, w, l);
   }
   int kt = 0;
@@ -555,7 +559,7 @@ __device__ __forceinline__ void pw_read_b(v4i (&b)[4][2], int (&sb)[4], const Pw
 // 16 MFMAs of one half (routes 64 h .. 64 h + 63) of a k-tile: the half's
 // 16-route blocks cb with 4 h + cb < nrb.
 template <int H>
-__device__ __forceinline__ void pw_mma(const PfW &wt, const v4i (&b)[4][2], const int (&sb)[4], int nrb, int l,
+__device__ __forceinline__ void pw_mma(const PfW &wt, const v4i (&b)[4][2], const int (&sb)[4], int nrb, int sh,
                                        v4f (*acc)[8]) {
 #pragma unroll
   for (int cb = 0; cb < 4; cb++) {
@@ -564,7 +568,7 @@ __device__ __forceinline__ void pw_mma(const PfW &wt, const v4i (&b)[4][2], cons
                           b[cb][1][0], b[cb][1][1], b[cb][1][2], b[cb][1][3]};
 #pragma unroll
       for (int q = 0; q < kPfQ; q++)
-        acc[q][4 * H + cb] = mfma_fp4_fp8(wt.a[q], bop, acc[q][4 * H + cb], (int)(wt.sa[q] >> (8 * (l & 3))), sb[cb]);
+        acc[q][4 * H + cb] = mfma_fp4_fp8(wt.a[q], bop, acc[q][4 * H + cb], (int)(wt.sa[q] >> sh), sb[cb]);
     }
   }
 }
@@ -572,27 +576,29 @@ __device__ __forceinline__ void pw_mma(const PfW &wt, const v4i (&b)[4][2], cons
 // One k-tile (R = kt % 2): wait for stage kt (the only one in flight), barrier
 // (every wave is also done with stage kt - 1), issue k-tile kt + 1 into the
 // slots kt - 1 held (ISSUE), then both halves of stage kt.
-template <int R, bool ISSUE, bool NT>
+// REUSE: k-tile kt + 1 lies inside a run of four whole k-tiles, past its first.
+template <int R, bool ISSUE, bool NT, bool REUSE = false>
 __device__ __forceinline__ void pw_step(PwLds &L, const PwSrc &src, PfW (&ring)[kPwStages], int kt, int w,
                                         bool active, int nrb, uint32_t vxs, v4f (*acc)[8]) {
   const int l = threadIdx.x & 63;
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
   if (ISSUE) {
-    pf_load_w<NT>(ring[R ^ 1], src.w, kt + 1, w, l);
+    pf_load_w<NT, REUSE>(ring[R ^ 1], src.w, kt + 1, w, l, &ring[R]);
     pw_issue_b(L.st[R ^ 1], src, kt + 1, w, l);
   }
   if (active) {
     v4i b[4][2];
     int sb[4];
+    const int sh = pf_scale_shift(kt, l, src.w.kbytes);
     pw_read_b<0>(b, sb, L.st[R], vxs, kt, l);
     __builtin_amdgcn_s_setprio(1);
-    pw_mma<0>(ring[R], b, sb, nrb, l, acc);
+    pw_mma<0>(ring[R], b, sb, nrb, sh, acc);
     __builtin_amdgcn_s_setprio(0);
     if (nrb > 4) {
       pw_read_b<1>(b, sb, L.st[R], vxs, kt, l);
       __builtin_amdgcn_s_setprio(1);
-      pw_mma<1>(ring[R], b, sb, nrb, l, acc);
+      pw_mma<1>(ring[R], b, sb, nrb, sh, acc);
       __builtin_amdgcn_s_setprio(0);
     }
   }
@@ -607,6 +613,13 @@ __device__ __forceinline__ void pw_kloop(PwLds &L, const PwSrc &src, int nkt, in
   pf_load_w<NT>(ring[0], src.w, 0, wu, l);
   pw_issue_b(L.st[0], src, 0, wu, l);
   int kt = 0;
+  // runs of four k-tiles: one scale load each
+  for (; kt + 4 < nkt; kt += 4) {
+    pw_step<0, true, NT, true>(L, src, ring, kt, wu, active, nrb, vxs, acc);
+    pw_step<1, true, NT, true>(L, src, ring, kt + 1, wu, active, nrb, vxs, acc);
+    pw_step<0, true, NT, true>(L, src, ring, kt + 2, wu, active, nrb, vxs, acc);
+    pw_step<1, true, NT>(L, src, ring, kt + 3, wu, active, nrb, vxs, acc);
+  }
   for (; kt + 2 < nkt; kt += 2) {
     pw_step<0, true, NT>(L, src, ring, kt, wu, active, nrb, vxs, acc);
     pw_step<1, true, NT>(L, src, ring, kt + 1, wu, active, nrb, vxs, acc);
@@ -758,7 +771,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm2_a8_short(GemmArgs a) {
   PfW wt[NKT];
 #pragma unroll
   for (int kt = 0; kt < NKT; kt++) {
-    pf_load_w<false, true>(wt[kt], src, kt, wu, l);
+    pf_load_w(wt[kt], src, kt, wu, l);
     pf_issue_b(L.st[kt], src, kt, wu, l);
   }
   v4f acc[kPfQ][4];

@@ -134,13 +134,13 @@ size_t moe_scratch_bytes(moe_plan_t plan, int tokens, int deterministic);
  *                  rewritten in place and afterwards hold the tile layout
  *   g13, g2        device fp32 [num_experts] globals (NVFP4; NULL = 1.0)
  * The returned handle borrows the buffers (the caller keeps ownership and must
- * keep them alive).  For MXFP4 experts the handle also owns one device buffer
- * of num_experts * K * N / 32 bytes (1/16 of w2): a second copy of the w2
- * scales, ordered for the prefill down GEMMs, which read a lane's scales of
- * four k-tiles in one load; moe_unpack_weights and moe_experts_destroy free
- * it.  moe_experts_destroy releases the handle and that copy, never the
- * caller's buffers.  Prepare allocates a temporary device buffer and
- * synchronises `stream`; it is not for graph capture.
+ * keep them alive).  For MXFP4 experts the handle also owns second copies of
+ * s13 and s2 (device buffers of their sizes, 1/16 of w13 and w2), ordered for
+ * the prefill GEMMs, which read a lane's scales of four k-tiles in one load;
+ * moe_unpack_weights and moe_experts_destroy free them.  moe_experts_destroy
+ * releases the handle and those copies, never the caller's buffers.  Prepare
+ * allocates a temporary device buffer and synchronises `stream`; it is not
+ * for graph capture.
  */
 int moe_prepare_weights(moe_plan_t plan, int weight_format, int num_experts, void *w13, void *s13,
                         const float *g13, void *w2, void *s2, const float *g2, void *stream,
