@@ -638,20 +638,24 @@ def test_prefill_fp16_down_gemm_over_wide_ranges(name, deterministic):
 
 # The prefill GEMMs read copies of the MXFP4 scales stored per row tile in runs of four
 # whole k-tiles (a lane's four bytes in one dword), then the whole k-tiles after the
-# last run, then a partial last k-tile.  Down-projection widths with two runs and a
-# partial k-tile (1088), a run and a tail of three (896), and two runs, a tail of two
-# and a partial k-tile (1344); hidden sizes with two runs and a tail of two (1280), one
-# run and a tail of two (768) and a tail of two alone (256); every launch sequence.
+# last run, then a partial last k-tile; NVFP4 layers of the same shapes alongside (their
+# two-byte scales keep the tile layout, with odd and partial k-tile counts).  Widths
+# with two runs and a partial k-tile (1088), a run and a tail of three (896), and two
+# runs, a tail of two and a partial k-tile (1344); hidden sizes with two runs and a tail
+# of two (1280), one run and a tail of two (768) and a tail of two alone (256); every
+# launch sequence.
+@pytest.mark.parametrize("fmt", [I.FMT_MXFP4, I.FMT_NVFP4])
 @pytest.mark.parametrize("N,K", [(896, 1280), (1088, 256), (1344, 768)])
 @pytest.mark.parametrize("seq", [M.SEQ_DECODE, M.SEQ_GENERAL, M.SEQ_PREFILL, M.SEQ_PREFILL_NARROW])
 @pytest.mark.parametrize("deterministic", [False, True])
-def test_mxfp4_scale_runs(N, K, seq, deterministic):
+def test_scale_runs(fmt, N, K, seq, deterministic):
     T = 6 if seq == M.SEQ_DECODE else 96
-    prob = I.make_problem(I.Config(f"mxfp4_n{N}_k{K}", T=T, E=4, K=K, N=N, topk=2, limit=7.0, fmt=I.FMT_MXFP4,
-                                   e8m0_exp=(-7, -3)), seed=N + K + T)
+    extra = {"e8m0_exp": (-7, -3)} if fmt == I.FMT_MXFP4 else {}
+    prob = I.make_problem(I.Config(f"scale_runs_{fmt}_n{N}_k{K}", T=T, E=4, K=K, N=N, topk=2, limit=7.0, fmt=fmt,
+                                   **extra), seed=N + K + T + fmt)
     L = DeviceLayer(prob)
     L.plan.set_sequence(T, seq)
     assert L.plan.sequence(T) == seq
     out = L.run(deterministic=deterministic)
     acc, _ = O.moe_problem(prob)
-    assert_rows_match(out, acc, label=f"mxfp4 N={N} sequence {seq} det={deterministic}", prob=prob)
+    assert_rows_match(out, acc, label=f"fmt {fmt} N={N} sequence {seq} det={deterministic}", prob=prob)
