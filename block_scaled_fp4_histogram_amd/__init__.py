@@ -203,7 +203,9 @@ class Plan:
 class Experts:
     """One layer's (or tier's) experts, repacked in place (moe_prepare_weights).
 
-    The tensors are borrowed: they hold the tile layout until unpack()."""
+    The tensors are borrowed: they hold the tile layout until unpack().  For MXFP4 the
+    handle also owns device copies of s13 and s2 in the prefill GEMMs' order, freed by
+    unpack() or when the handle is destroyed."""
 
     def __init__(self, plan: Plan, weight_format: int, num_experts: int, w13, s13, w2, s2, g13=None, g2=None,
                  stream=None):
